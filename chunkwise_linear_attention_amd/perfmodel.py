@@ -1,0 +1,96 @@
+"""Algorithmic work of the hot path: bytes and FLOPs per unit, and rooflines.
+
+These are the counts the throughput and roofline figures are priced against.
+They count what the method itself must move or compute, not what a given
+kernel happens to move.
+
+Citations (page title, then section):
+  ZTF = "Parallel scan" (zerotofrontier.app, ssm/parallel-scan)
+"""
+
+from __future__ import annotations
+
+import math
+
+# MI355X published peaks (dense; no sparsity).
+PEAK_HBM_GBS = 8000.0          # GB/s
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
+PEAK_FP32_VALU_TFLOPS = 157.3  # fp32 vector
+
+
+# --------------------------------------------------------------------------
+# chunk-size arithmetic: ZTF "How big should a chunk be"
+# --------------------------------------------------------------------------
+
+
+def chunk_flops(Tc: int, dk: int, dv: int) -> int:
+    """Matrix-product FLOPs of one full chunk of the forward: intra scores
+    2 Tc^2 dk, their product with V 2 Tc^2 dv, inter read 2 Tc dk dv, state
+    update 2 Tc dk dv (an m x k by k x n product costs 2 m k n)."""
+    return 2 * Tc * Tc * dk + 2 * Tc * Tc * dv + 4 * Tc * dk * dv
+
+
+def sequence_flops(T: int, Tc: int, dk: int, dv: int) -> int:
+    """Forward FLOPs over a sequence of T tokens in ceil(T / Tc) chunks (the
+    last one shorter)."""
+    full, rem = divmod(T, Tc)
+    return full * chunk_flops(Tc, dk, dv) + (chunk_flops(rem, dk, dv) if rem else 0)
+
+
+def balance_chunk(dk: int, dv: int) -> float:
+    """Chunk length at which the quadratic and linear parts cost the same:
+    2 Tc^2 (dk + dv) = 4 Tc dk dv  ->  Tc* = 2 dk dv / (dk + dv)."""
+    return 2.0 * dk * dv / (dk + dv)
+
+
+def onchip_bytes(Tc: int, d: int) -> dict:
+    """Bytes one chunk keeps on chip: bf16 Q, K, V; fp32 scores; fp32 state."""
+    return {"inputs_bf16": 3 * Tc * d * 2, "scores_f32": Tc * Tc * 4,
+            "state_f32": d * d * 4}
+
+
+# --------------------------------------------------------------------------
+# per-unit algorithmic bytes / FLOPs of the two regimes
+# --------------------------------------------------------------------------
+
+
+def scan_bytes_per_elem(direction: str = "fwdbwd") -> int:
+    """Diagonal scan, fp32: forward reads a, b and writes h (12 B); backward
+    reads a, h, dh and writes da, db (20 B)."""
+    return {"fwd": 12, "bwd": 20, "fwdbwd": 32}[direction]
+
+
+def chunk_bytes_per_token_head(dk: int, dv: int, direction: str = "fwdbwd") -> int:
+    """Chunkwise, bf16 I/O, fp32 log decay: forward reads q, k, v, l and
+    writes o; backward reads q, k, v, dO, l and writes dq, dk, dv, dl."""
+    fwd = 2 * dk + 2 * dk + 2 * dv + 4 + 2 * dv
+    bwd = 2 * dk * 2 + 2 * dv + 2 * dv + 4 + 2 * dk * 2 + 2 * dv + 4
+    return {"fwd": fwd, "bwd": bwd, "fwdbwd": fwd + bwd}[direction]
+
+
+def chunk_state_bytes(dk: int, dv: int) -> int:
+    """One fp32 dk x dv state (S0, S_T, dS_T or dS0) per (batch, head)."""
+    return 4 * dk * dv
+
+
+def chunk_flops_per_token_head(Tc: int, dk: int, dv: int, direction: str = "fwdbwd") -> int:
+    """Forward 2 Tc (dk + dv) + 4 dk dv; backward 2 Tc (3 dk + 2 dv) + 10 dk dv
+    (dQ pass with the chunk-state recompute, dK/dV pass with the adjoint
+    state update).  Masked upper triangles are counted as computed."""
+    fwd = 2 * Tc * (dk + dv) + 4 * dk * dv
+    bwd = 2 * Tc * (3 * dk + 2 * dv) + 10 * dk * dv
+    return {"fwd": fwd, "bwd": bwd, "fwdbwd": fwd + bwd}[direction]
+
+
+def roofline_seconds(bytes_: float, flops: float = 0.0,
+                     peak_gbs: float = PEAK_HBM_GBS,
+                     peak_tflops: float = PEAK_BF16_TFLOPS) -> float:
+    return max(bytes_ / (peak_gbs * 1e9), flops / (peak_tflops * 1e12))
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def log2ceil(n: int) -> int:
+    return max(0, math.ceil(math.log2(n))) if n > 0 else 0

@@ -1,0 +1,237 @@
+/*
+ * Float64 CPU oracle loops -- TEST INFRASTRUCTURE ONLY.
+ *
+ * The same definitions as oracle/scan.py and oracle/attn.py, written as plain
+ * sequential loops in C so that full-size samples and the CPU baseline run in
+ * seconds.  OpenMP spreads independent units (channels, heads) over the host
+ * cores; each unit runs strictly in time order.  Nothing in the GPU library
+ * includes or links this file, and this file includes nothing of it.
+ *
+ * Inputs are the exact device inputs: fp32 values and bf16 bit patterns, upcast
+ * to double before any arithmetic.  All arithmetic and all outputs are double.
+ *
+ * Citations (page title, then section):
+ *   ZTF = "Parallel scan" (zerotofrontier.app, ssm/parallel-scan)
+ *   LA2 = "Lightning Attention-2: A Free Lunch for Handling Unlimited Sequence
+ *         Lengths in Large Language Models" (paper-graph-ui summary)
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double bf16_to_double(uint16_t bits) {
+  uint32_t u = ((uint32_t)bits) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/*
+ * Diagonal recurrence, forward.  ZTF "The scan for one number of state":
+ * h_t = a_t h_{t-1} + b_t from h_0 (zero when h0 is NULL).
+ * a, b: [B, T, D] fp32; h0: [B, D] fp32 or NULL.
+ * Computes the block of channels b in [b0, b1), d in [d0, d1):
+ * h: [b1-b0, T, d1-d0] double, hT: [b1-b0, d1-d0] double.
+ */
+void oracle_scan_fwd(const float *a, const float *b, const float *h0, double *h,
+                     double *hT, int64_t B, int64_t T, int64_t D, int64_t b0,
+                     int64_t b1, int64_t d0, int64_t d1) {
+  int64_t nb = b1 - b0, nd = d1 - d0;
+  (void)B;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t ib = 0; ib < nb; ++ib) {
+    for (int64_t id = 0; id < nd; ++id) {
+      int64_t bb = b0 + ib, dd = d0 + id;
+      double s = h0 ? (double)h0[bb * D + dd] : 0.0;
+      for (int64_t t = 0; t < T; ++t) {
+        int64_t src = (bb * T + t) * D + dd;
+        s = (double)a[src] * s + (double)b[src];
+        h[(ib * T + t) * nd + id] = s;
+      }
+      hT[ib * nd + id] = s;
+    }
+  }
+}
+
+/*
+ * Diagonal recurrence, backward.  ZTF "The backward pass is a scan in
+ * reverse": hbar_T = g_T + dh_T, hbar_t = g_t + a_{t+1} hbar_{t+1};
+ * db_t = hbar_t, da_t = hbar_t h_{t-1} (h_0 at t = 1), dh0 = a_1 hbar_1.
+ * a, h (forward output), dh: [B, T, D] fp32; h0, dhT: [B, D] fp32 or NULL.
+ * Outputs for the channel block: da, db [nb, T, nd], dh0 [nb, nd], double.
+ */
+void oracle_scan_bwd(const float *a, const float *h, const float *h0,
+                     const float *dh, const float *dhT, double *da, double *db,
+                     double *dh0, int64_t B, int64_t T, int64_t D, int64_t b0,
+                     int64_t b1, int64_t d0, int64_t d1) {
+  int64_t nb = b1 - b0, nd = d1 - d0;
+  (void)B;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t ib = 0; ib < nb; ++ib) {
+    for (int64_t id = 0; id < nd; ++id) {
+      int64_t bb = b0 + ib, dd = d0 + id;
+      double hbar = dhT ? (double)dhT[bb * D + dd] : 0.0;
+      for (int64_t t = T - 1; t >= 0; --t) {
+        int64_t src = (bb * T + t) * D + dd;
+        if (t < T - 1) hbar *= (double)a[src + D];
+        hbar += (double)dh[src];
+        double hprev = t > 0 ? (double)h[src - D] : (h0 ? (double)h0[bb * D + dd] : 0.0);
+        db[(ib * T + t) * nd + id] = hbar;
+        da[(ib * T + t) * nd + id] = hbar * hprev;
+      }
+      dh0[ib * nd + id] = T > 0 ? (double)a[(bb * T) * D + dd] * hbar : hbar;
+    }
+  }
+}
+
+/*
+ * Matrix-state recurrence, forward, for a list of heads.  ZTF "The chunkwise
+ * algorithm" (the recurrence it is derived for) and "Scans over vector and
+ * matrix states": S_t = a_t S_{t-1} + k_t v_t^T, o_t = S_t^T q_t, a_t =
+ * exp(l_t).
+ * q, k: [B, H, T, DK] bf16 bits; v: [B, H, T, DV] bf16 bits; l: [B, H, T]
+ * fp32; S0: [B, H, DK, DV] fp32 or NULL.  heads: flat indices b*H + h.
+ * Outputs: o [nheads, T, DV], ST [nheads, DK, DV], double.
+ */
+void oracle_la_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                   const float *l, const float *S0, double *o, double *ST,
+                   int64_t T, int64_t DK, int64_t DV, const int64_t *heads,
+                   int64_t nheads) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < nheads; ++i) {
+    int64_t hd = heads[i];
+    const uint16_t *qh = q + hd * T * DK, *kh = k + hd * T * DK, *vh = v + hd * T * DV;
+    const float *lh = l + hd * T;
+    double *S = (double *)malloc(sizeof(double) * DK * DV);
+    double *kt = (double *)malloc(sizeof(double) * (DK + DV + DK));
+    double *vt = kt + DK, *qt = vt + DV;
+    for (int64_t e = 0; e < DK * DV; ++e) S[e] = S0 ? (double)S0[hd * DK * DV + e] : 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      double at = exp((double)lh[t]);
+      for (int64_t x = 0; x < DK; ++x) kt[x] = bf16_to_double(kh[t * DK + x]);
+      for (int64_t x = 0; x < DK; ++x) qt[x] = bf16_to_double(qh[t * DK + x]);
+      for (int64_t y = 0; y < DV; ++y) vt[y] = bf16_to_double(vh[t * DV + y]);
+      for (int64_t x = 0; x < DK; ++x)
+        for (int64_t y = 0; y < DV; ++y) S[x * DV + y] = at * S[x * DV + y] + kt[x] * vt[y];
+      double *ot = o + (i * T + t) * DV;
+      for (int64_t y = 0; y < DV; ++y) ot[y] = 0.0;
+      for (int64_t x = 0; x < DK; ++x)
+        for (int64_t y = 0; y < DV; ++y) ot[y] += S[x * DV + y] * qt[x];
+    }
+    memcpy(ST + i * DK * DV, S, sizeof(double) * DK * DV);
+    free(kt);
+    free(S);
+  }
+}
+
+/*
+ * Matrix-state recurrence, backward, for a list of heads.  ZTF "The backward
+ * pass of linear attention": Sbar_T = q_T dO_T^T + dS_T,
+ * Sbar_t = q_t dO_t^T + a_{t+1} Sbar_{t+1}; dq_t = S_t dO_t,
+ * dk_t = Sbar_t v_t, dv_t = Sbar_t^T k_t, dl_t = a_t <Sbar_t, S_{t-1}>,
+ * dS0 = a_1 Sbar_1.  The states S_{t-1}, S_t are recomputed in the reverse
+ * sweep from checkpoints stored every CK steps of a first forward loop
+ * (ZTF "The backward pass is a scan in reverse": chunked kernels store only
+ * boundary states and recompute the rest; here it only bounds memory).
+ * dO: [B, H, T, DV] bf16 bits; dST: [B, H, DK, DV] fp32 or NULL.
+ * Outputs: dq, dk [nheads, T, DK]; dv [nheads, T, DV]; dl [nheads, T];
+ * dS0 [nheads, DK, DV]; double.
+ */
+void oracle_la_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                   const float *l, const float *S0, const uint16_t *dO,
+                   const float *dST, double *dq, double *dk, double *dv,
+                   double *dl, double *dS0, int64_t T, int64_t DK, int64_t DV,
+                   const int64_t *heads, int64_t nheads) {
+  const int64_t CK = 64;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < nheads; ++i) {
+    int64_t hd = heads[i];
+    const uint16_t *qh = q + hd * T * DK, *kh = k + hd * T * DK, *vh = v + hd * T * DV;
+    const uint16_t *doh = dO + hd * T * DV;
+    const float *lh = l + hd * T;
+    int64_t SZ = DK * DV;
+    int64_t ncp = T / CK + 1;
+    /* checkpoints: cp[c] = S_{c*CK} */
+    double *cp = (double *)malloc(sizeof(double) * SZ * ncp);
+    /* states of one block: blk[j] = S_{t0 + j}, j = 0..CK */
+    double *blk = (double *)malloc(sizeof(double) * SZ * (CK + 1));
+    double *Sb = (double *)malloc(sizeof(double) * SZ);
+    double *tmp = (double *)malloc(sizeof(double) * (2 * DK + 2 * DV));
+    double *kt = tmp, *qt = tmp + DK, *vt = tmp + 2 * DK, *dot = tmp + 2 * DK + DV;
+    double *S = blk; /* scratch for the first forward loop */
+    for (int64_t e = 0; e < SZ; ++e) S[e] = S0 ? (double)S0[hd * SZ + e] : 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      if (t % CK == 0) memcpy(cp + (t / CK) * SZ, S, sizeof(double) * SZ);
+      double at = exp((double)lh[t]);
+      for (int64_t x = 0; x < DK; ++x) kt[x] = bf16_to_double(kh[t * DK + x]);
+      for (int64_t y = 0; y < DV; ++y) vt[y] = bf16_to_double(vh[t * DV + y]);
+      for (int64_t x = 0; x < DK; ++x)
+        for (int64_t y = 0; y < DV; ++y) S[x * DV + y] = at * S[x * DV + y] + kt[x] * vt[y];
+    }
+    for (int64_t e = 0; e < SZ; ++e) Sb[e] = dST ? (double)dST[hd * SZ + e] : 0.0;
+    int64_t nblk = (T + CK - 1) / CK;
+    for (int64_t c = nblk - 1; c >= 0; --c) {
+      int64_t t0 = c * CK, n = (T - t0 < CK) ? T - t0 : CK;
+      memcpy(blk, cp + c * SZ, sizeof(double) * SZ);
+      for (int64_t j = 0; j < n; ++j) {
+        int64_t t = t0 + j;
+        double at = exp((double)lh[t]);
+        for (int64_t x = 0; x < DK; ++x) kt[x] = bf16_to_double(kh[t * DK + x]);
+        for (int64_t y = 0; y < DV; ++y) vt[y] = bf16_to_double(vh[t * DV + y]);
+        const double *Sp = blk + j * SZ;
+        double *Sn = blk + (j + 1) * SZ;
+        for (int64_t x = 0; x < DK; ++x)
+          for (int64_t y = 0; y < DV; ++y) Sn[x * DV + y] = at * Sp[x * DV + y] + kt[x] * vt[y];
+      }
+      for (int64_t j = n - 1; j >= 0; --j) {
+        int64_t t = t0 + j;
+        if (t < T - 1) {
+          double an = exp((double)lh[t + 1]);
+          for (int64_t e = 0; e < SZ; ++e) Sb[e] *= an;
+        }
+        for (int64_t x = 0; x < DK; ++x) qt[x] = bf16_to_double(qh[t * DK + x]);
+        for (int64_t x = 0; x < DK; ++x) kt[x] = bf16_to_double(kh[t * DK + x]);
+        for (int64_t y = 0; y < DV; ++y) vt[y] = bf16_to_double(vh[t * DV + y]);
+        for (int64_t y = 0; y < DV; ++y) dot[y] = bf16_to_double(doh[t * DV + y]);
+        for (int64_t x = 0; x < DK; ++x)
+          for (int64_t y = 0; y < DV; ++y) Sb[x * DV + y] += qt[x] * dot[y];
+        const double *Sprev = blk + j * SZ, *Scur = blk + (j + 1) * SZ;
+        double *gq = dq + (i * T + t) * DK, *gk = dk + (i * T + t) * DK;
+        double *gv = dv + (i * T + t) * DV;
+        for (int64_t x = 0; x < DK; ++x) {
+          double sq = 0.0, sk = 0.0;
+          for (int64_t y = 0; y < DV; ++y) {
+            sq += Scur[x * DV + y] * dot[y];
+            sk += Sb[x * DV + y] * vt[y];
+          }
+          gq[x] = sq;
+          gk[x] = sk;
+        }
+        for (int64_t y = 0; y < DV; ++y) gv[y] = 0.0;
+        for (int64_t x = 0; x < DK; ++x)
+          for (int64_t y = 0; y < DV; ++y) gv[y] += Sb[x * DV + y] * kt[x];
+        double inner = 0.0;
+        for (int64_t e = 0; e < SZ; ++e) inner += Sb[e] * Sprev[e];
+        dl[i * T + t] = exp((double)lh[t]) * inner;
+      }
+    }
+    double a1 = T > 0 ? exp((double)lh[0]) : 1.0;
+    for (int64_t e = 0; e < SZ; ++e) dS0[i * SZ + e] = a1 * Sb[e];
+    free(tmp);
+    free(Sb);
+    free(blk);
+    free(cp);
+  }
+}
