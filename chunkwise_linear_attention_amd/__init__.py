@@ -1,0 +1,24 @@
+"""MI355X-native gated linear-recurrence scans (libcla).
+
+Python binding over the C ABI in include/cla.h.  Tensors are torch tensors on
+a ROCm device; torch provides device memory and the current stream, and every
+step of the computation runs in the library's HIP kernels.
+
+    h, hT              = scan(a, b, h0=None)
+    da, db, dh0        = scan_bwd(a, h, h0, dh, dhT=None)
+    o, ST              = chunked_linear_attn(q, k, v, log_decay, S0=None)
+    dq, dk, dv, dl, dS0 = chunked_linear_attn_bwd(q, k, v, log_decay, S0, dO, dST=None)
+"""
+
+from ._lib import ClaError, lib  # noqa: F401
+from .api import (  # noqa: F401
+    chunked_linear_attn,
+    chunked_linear_attn_bwd,
+    scan,
+    scan_bwd,
+    scan_workspace_bytes,
+    chunk_workspace_bytes,
+)
+
+__all__ = ["scan", "scan_bwd", "chunked_linear_attn", "chunked_linear_attn_bwd",
+           "scan_workspace_bytes", "chunk_workspace_bytes", "ClaError"]

@@ -1,0 +1,169 @@
+"""Torch-facing wrappers with the same names as the C ABI calls.
+
+Each wrapper checks dtypes, devices and shapes, allocates the outputs and the
+workspace with torch, and calls the library on torch's current stream.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+CHUNK = 64
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _opt(t, *a):
+    if t is not None:
+        _need(t, *a)
+
+
+def _workspace(nbytes, device):
+    if nbytes == 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+# ---------------------------------------------------------------------------
+# diagonal scan
+# ---------------------------------------------------------------------------
+
+
+def scan_workspace_bytes(B: int, T: int, D: int) -> int:
+    return int(_lib.lib().cla_scan_workspace_bytes(B, T, D))
+
+
+def scan(a, b, h0=None, *, want_final=True, workspace=None):
+    """h_t = a_t h_{t-1} + b_t over dim 1 of [B, T, D] fp32 tensors.
+    Returns (h, h_T) (h_T is None when want_final is False)."""
+    if a.dim() != 3:
+        raise ValueError("a must be [B, T, D]")
+    B, T, D = a.shape
+    dev = a.device
+    _need(a, "a", torch.float32, (B, T, D), dev)
+    _need(b, "b", torch.float32, (B, T, D), dev)
+    _opt(h0, "h0", torch.float32, (B, D), dev)
+    h = torch.empty_like(a)
+    hT = torch.empty((B, D), dtype=torch.float32, device=dev) if want_final else None
+    L = _lib.lib()
+    nbytes = int(L.cla_scan_workspace_bytes(B, T, D))
+    if workspace is None:
+        ws, wsb = _workspace(nbytes, dev)
+    else:
+        ws, wsb = workspace, workspace.numel() * workspace.element_size()
+    st = L.cla_scan_fwd(_ptr(a), _ptr(b), _ptr(h0), _ptr(h), _ptr(hT), B, T, D,
+                        _ptr(ws), wsb, _stream(dev))
+    _lib.check("cla_scan_fwd", st)
+    return h, hT
+
+
+def scan_bwd(a, h, h0, dh, dhT=None, *, want_dh0=True, workspace=None):
+    """Backward of ``scan``: returns (da, db, dh0)."""
+    B, T, D = a.shape
+    dev = a.device
+    _need(a, "a", torch.float32, (B, T, D), dev)
+    _need(h, "h", torch.float32, (B, T, D), dev)
+    _opt(h0, "h0", torch.float32, (B, D), dev)
+    _need(dh, "dh", torch.float32, (B, T, D), dev)
+    _opt(dhT, "dhT", torch.float32, (B, D), dev)
+    da = torch.empty_like(a)
+    db = torch.empty_like(a)
+    dh0 = torch.empty((B, D), dtype=torch.float32, device=dev) if want_dh0 else None
+    L = _lib.lib()
+    nbytes = int(L.cla_scan_workspace_bytes(B, T, D))
+    if workspace is None:
+        ws, wsb = _workspace(nbytes, dev)
+    else:
+        ws, wsb = workspace, workspace.numel() * workspace.element_size()
+    st = L.cla_scan_bwd(_ptr(a), _ptr(h), _ptr(h0), _ptr(dh), _ptr(dhT), _ptr(da),
+                        _ptr(db), _ptr(dh0), B, T, D, _ptr(ws), wsb, _stream(dev))
+    _lib.check("cla_scan_bwd", st)
+    return da, db, dh0
+
+
+# ---------------------------------------------------------------------------
+# chunkwise linear attention
+# ---------------------------------------------------------------------------
+
+
+def chunk_workspace_bytes(B, H, T, DK, DV, backward=False, chunk=CHUNK) -> int:
+    return int(_lib.lib().cla_chunk_workspace_bytes(B, H, T, DK, DV, chunk, int(backward)))
+
+
+def chunked_linear_attn(q, k, v, log_decay, S0=None, *, want_final=True,
+                        chunk=CHUNK, workspace=None):
+    """S_t = exp(l_t) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t, chunkwise.
+    q, k: [B, H, T, DK] bf16; v: [B, H, T, DV] bf16; log_decay: [B, H, T] fp32;
+    S0: [B, H, DK, DV] fp32 or None.  Returns (o bf16, S_T fp32 or None)."""
+    B, H, T, DK = q.shape
+    DV = v.shape[-1]
+    dev = q.device
+    _need(q, "q", torch.bfloat16, (B, H, T, DK), dev)
+    _need(k, "k", torch.bfloat16, (B, H, T, DK), dev)
+    _need(v, "v", torch.bfloat16, (B, H, T, DV), dev)
+    _need(log_decay, "log_decay", torch.float32, (B, H, T), dev)
+    _opt(S0, "S0", torch.float32, (B, H, DK, DV), dev)
+    o = torch.empty((B, H, T, DV), dtype=torch.bfloat16, device=dev)
+    ST = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev) if want_final else None
+    L = _lib.lib()
+    nbytes = int(L.cla_chunk_workspace_bytes(B, H, T, DK, DV, chunk, 0))
+    if workspace is None:
+        ws, wsb = _workspace(nbytes, dev)
+    else:
+        ws, wsb = workspace, workspace.numel() * workspace.element_size()
+    st = L.cla_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(S0), _ptr(o),
+                         _ptr(ST), B, H, T, DK, DV, chunk, _ptr(ws), wsb, _stream(dev))
+    _lib.check("cla_chunk_fwd", st)
+    return o, ST
+
+
+def chunked_linear_attn_bwd(q, k, v, log_decay, S0, dO, dST=None, *, want_dS0=True,
+                            chunk=CHUNK, workspace=None):
+    """Backward of ``chunked_linear_attn``: returns (dq, dk, dv, dlog_decay, dS0)."""
+    B, H, T, DK = q.shape
+    DV = v.shape[-1]
+    dev = q.device
+    _need(q, "q", torch.bfloat16, (B, H, T, DK), dev)
+    _need(k, "k", torch.bfloat16, (B, H, T, DK), dev)
+    _need(v, "v", torch.bfloat16, (B, H, T, DV), dev)
+    _need(log_decay, "log_decay", torch.float32, (B, H, T), dev)
+    _opt(S0, "S0", torch.float32, (B, H, DK, DV), dev)
+    _need(dO, "dO", torch.bfloat16, (B, H, T, DV), dev)
+    _opt(dST, "dST", torch.float32, (B, H, DK, DV), dev)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dl = torch.empty_like(log_decay)
+    dS0 = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev) if want_dS0 else None
+    L = _lib.lib()
+    nbytes = int(L.cla_chunk_workspace_bytes(B, H, T, DK, DV, chunk, 1))
+    if workspace is None:
+        ws, wsb = _workspace(nbytes, dev)
+    else:
+        ws, wsb = workspace, workspace.numel() * workspace.element_size()
+    st = L.cla_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(S0), _ptr(dO),
+                         _ptr(dST), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dl), _ptr(dS0),
+                         B, H, T, DK, DV, chunk, _ptr(ws), wsb, _stream(dev))
+    _lib.check("cla_chunk_bwd", st)
+    return dq, dk, dv, dl, dS0

@@ -1,0 +1,183 @@
+// The C ABI of libcla (declared in include/cla.h): host-side argument
+// validation, workspace sizing and kernel launches.  Every check runs before
+// the first HIP call, so a rejected call touches no device state.
+#include <stdint.h>
+#include <string.h>
+
+#include <initializer_list>
+
+#include "../../include/cla.h"
+#include "internal.h"
+
+namespace {
+
+struct Range {
+  const void *p;
+  size_t bytes;
+};
+
+bool overlap(const Range &x, const Range &y) {
+  if (!x.p || !y.p || x.bytes == 0 || y.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(x.p), a1 = a0 + x.bytes;
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(y.p), b1 = b0 + y.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+// Every output must be disjoint from every input and from every other output.
+bool any_alias(std::initializer_list<Range> inputs,
+               std::initializer_list<Range> outputs) {
+  for (const Range &o : outputs) {
+    for (const Range &i : inputs)
+      if (overlap(o, i)) return true;
+    for (const Range &o2 : outputs)
+      if (&o2 != &o && overlap(o, o2)) return true;
+  }
+  return false;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? CLA_OK : CLA_ERR_HIP; }
+
+bool supported_head_dim(int64_t d) { return d == 64 || d == 128; }
+
+}  // namespace
+
+extern "C" {
+
+const char *cla_status_string(int status) {
+  switch (status) {
+    case CLA_OK: return "CLA_OK";
+    case CLA_ERR_NULL_ARG: return "CLA_ERR_NULL_ARG: a required pointer is NULL";
+    case CLA_ERR_BAD_SHAPE: return "CLA_ERR_BAD_SHAPE: a size is negative";
+    case CLA_ERR_UNSUPPORTED: return "CLA_ERR_UNSUPPORTED: head size or chunk length not supported";
+    case CLA_ERR_WORKSPACE: return "CLA_ERR_WORKSPACE: workspace missing or too small";
+    case CLA_ERR_ALIAS: return "CLA_ERR_ALIAS: an output overlaps an input or another output";
+    case CLA_ERR_HIP: return "CLA_ERR_HIP: a HIP launch failed";
+    default: return "CLA_ERR_UNKNOWN";
+  }
+}
+
+const char *cla_version(void) { return "cla 0.1 gfx950"; }
+
+// ---------------------------------------------------------------------------
+// diagonal scan
+// ---------------------------------------------------------------------------
+
+size_t cla_scan_workspace_bytes(int64_t B, int64_t T, int64_t D) {
+  if (B < 0 || T < 0 || D < 0) return 0;
+  return cla::plan_scan(B, T, D).ws_bytes;
+}
+
+int cla_scan_fwd(const float *a, const float *b, const float *h0, float *h,
+                 float *hT, int64_t B, int64_t T, int64_t D, void *workspace,
+                 size_t workspace_bytes, cla_stream_t stream) {
+  if (B < 0 || T < 0 || D < 0) return CLA_ERR_BAD_SHAPE;
+  if (B == 0 || D == 0) return CLA_OK;
+  const size_t full = (size_t)B * (size_t)T * (size_t)D * sizeof(float);
+  const size_t row = (size_t)B * (size_t)D * sizeof(float);
+  if (T > 0 && (!a || !b || !h)) return CLA_ERR_NULL_ARG;
+  const cla::ScanPlan plan = cla::plan_scan(B, T, D);
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+    return CLA_ERR_WORKSPACE;
+  const Range ws{plan.ws_bytes ? workspace : nullptr, plan.ws_bytes};
+  if (any_alias({{a, full}, {b, full}, {h0, row}}, {{h, full}, {hT, row}, ws}))
+    return CLA_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0) return hT ? hip_status(cla::launch_copy_or_zero(hT, h0, B * D, s)) : CLA_OK;
+  return hip_status(cla::launch_scan_fwd(a, b, h0, h, hT, B, T, D, plan, workspace, s));
+}
+
+int cla_scan_bwd(const float *a, const float *h, const float *h0,
+                 const float *dh, const float *dhT, float *da, float *db,
+                 float *dh0, int64_t B, int64_t T, int64_t D, void *workspace,
+                 size_t workspace_bytes, cla_stream_t stream) {
+  if (B < 0 || T < 0 || D < 0) return CLA_ERR_BAD_SHAPE;
+  if (B == 0 || D == 0) return CLA_OK;
+  const size_t full = (size_t)B * (size_t)T * (size_t)D * sizeof(float);
+  const size_t row = (size_t)B * (size_t)D * sizeof(float);
+  if (T > 0 && (!a || !h || !dh || !da || !db)) return CLA_ERR_NULL_ARG;
+  const cla::ScanPlan plan = cla::plan_scan(B, T, D);
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+    return CLA_ERR_WORKSPACE;
+  const Range ws{plan.ws_bytes ? workspace : nullptr, plan.ws_bytes};
+  if (any_alias({{a, full}, {h, full}, {h0, row}, {dh, full}, {dhT, row}},
+                {{da, full}, {db, full}, {dh0, row}, ws}))
+    return CLA_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0) return dh0 ? hip_status(cla::launch_copy_or_zero(dh0, dhT, B * D, s)) : CLA_OK;
+  return hip_status(
+      cla::launch_scan_bwd(a, h, h0, dh, dhT, da, db, dh0, B, T, D, plan, workspace, s));
+}
+
+// ---------------------------------------------------------------------------
+// chunkwise linear attention
+// ---------------------------------------------------------------------------
+
+size_t cla_chunk_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t DK,
+                                 int64_t DV, int64_t chunk, int backward) {
+  if (B < 0 || H < 0 || T < 0) return 0;
+  if (!supported_head_dim(DK) || !supported_head_dim(DV) || chunk != 64) return 0;
+  const cla::ChunkPlan plan = cla::plan_chunk(B, H, T, DK, DV);
+  return backward ? plan.ws_bwd : plan.ws_fwd;
+}
+
+int cla_chunk_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                  const float *log_decay, const float *S0, uint16_t *o,
+                  float *ST, int64_t B, int64_t H, int64_t T, int64_t DK,
+                  int64_t DV, int64_t chunk, void *workspace,
+                  size_t workspace_bytes, cla_stream_t stream) {
+  if (B < 0 || H < 0 || T < 0 || DK < 0 || DV < 0 || chunk < 0) return CLA_ERR_BAD_SHAPE;
+  if (!supported_head_dim(DK) || !supported_head_dim(DV) || chunk != 64)
+    return CLA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0) return CLA_OK;
+  const size_t nh = (size_t)B * (size_t)H;
+  const size_t qk = nh * (size_t)T * (size_t)DK * 2, vv = nh * (size_t)T * (size_t)DV * 2;
+  const size_t ll = nh * (size_t)T * 4, ss = nh * (size_t)DK * (size_t)DV * 4;
+  if (T > 0 && (!q || !k || !v || !log_decay || !o)) return CLA_ERR_NULL_ARG;
+  const cla::ChunkPlan plan = cla::plan_chunk(B, H, T, DK, DV);
+  if (plan.ws_fwd > 0 && (!workspace || workspace_bytes < plan.ws_fwd))
+    return CLA_ERR_WORKSPACE;
+  const Range ws{plan.ws_fwd ? workspace : nullptr, plan.ws_fwd};
+  if (any_alias({{q, qk}, {k, qk}, {v, vv}, {log_decay, ll}, {S0, ss}},
+                {{o, vv}, {ST, ss}, ws}))
+    return CLA_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0)
+    return ST ? hip_status(cla::launch_copy_or_zero(ST, S0, (int64_t)(nh * DK * DV), s))
+              : CLA_OK;
+  return hip_status(cla::launch_chunk_fwd(q, k, v, log_decay, S0, o, ST, B, H, T, DK,
+                                          DV, plan, workspace, s));
+}
+
+int cla_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                  const float *log_decay, const float *S0, const uint16_t *dO,
+                  const float *dST, uint16_t *dq, uint16_t *dk, uint16_t *dv,
+                  float *dlog_decay, float *dS0, int64_t B, int64_t H,
+                  int64_t T, int64_t DK, int64_t DV, int64_t chunk,
+                  void *workspace, size_t workspace_bytes,
+                  cla_stream_t stream) {
+  if (B < 0 || H < 0 || T < 0 || DK < 0 || DV < 0 || chunk < 0) return CLA_ERR_BAD_SHAPE;
+  if (!supported_head_dim(DK) || !supported_head_dim(DV) || chunk != 64)
+    return CLA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0) return CLA_OK;
+  const size_t nh = (size_t)B * (size_t)H;
+  const size_t qk = nh * (size_t)T * (size_t)DK * 2, vv = nh * (size_t)T * (size_t)DV * 2;
+  const size_t ll = nh * (size_t)T * 4, ss = nh * (size_t)DK * (size_t)DV * 4;
+  if (T > 0 && (!q || !k || !v || !log_decay || !dO || !dq || !dk || !dv || !dlog_decay))
+    return CLA_ERR_NULL_ARG;
+  const cla::ChunkPlan plan = cla::plan_chunk(B, H, T, DK, DV);
+  if (plan.ws_bwd > 0 && (!workspace || workspace_bytes < plan.ws_bwd))
+    return CLA_ERR_WORKSPACE;
+  const Range ws{plan.ws_bwd ? workspace : nullptr, plan.ws_bwd};
+  if (any_alias({{q, qk}, {k, qk}, {v, vv}, {log_decay, ll}, {S0, ss}, {dO, vv}, {dST, ss}},
+                {{dq, qk}, {dk, qk}, {dv, vv}, {dlog_decay, ll}, {dS0, ss}, ws}))
+    return CLA_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0)
+    return dS0 ? hip_status(cla::launch_copy_or_zero(dS0, dST, (int64_t)(nh * DK * DV), s))
+               : CLA_OK;
+  return hip_status(cla::launch_chunk_bwd(q, k, v, log_decay, S0, dO, dST, dq, dk, dv,
+                                          dlog_decay, dS0, B, H, T, DK, DV, plan,
+                                          workspace, s));
+}
+
+}  // extern "C"

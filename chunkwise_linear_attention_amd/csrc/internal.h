@@ -1,0 +1,71 @@
+// Internal declarations shared by the C-ABI layer (api.cpp) and the kernel
+// translation units.  Not part of the public interface (include/cla.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace cla {
+
+// ---------------------------------------------------------------------------
+// diagonal scan
+// ---------------------------------------------------------------------------
+
+// How a diagonal scan is split over the GPU.  Channels are grouped 64 at a
+// time (16 lanes x float4); each group sweeps the whole time axis unless the
+// batch and channel count alone give too few groups, in which case the time
+// axis is cut into P segments whose composed pairs go through the workspace.
+struct ScanPlan {
+  int64_t P = 1;         // segments along time
+  int64_t seg_len = 0;   // steps per segment (multiple of the block length)
+  size_t ws_bytes = 0;   // workspace bytes (P - 1 pairs per channel)
+};
+
+ScanPlan plan_scan(int64_t B, int64_t T, int64_t D);
+
+hipError_t launch_scan_fwd(const float *a, const float *b, const float *h0,
+                           float *h, float *hT, int64_t B, int64_t T,
+                           int64_t D, const ScanPlan &plan, void *ws,
+                           hipStream_t stream);
+
+hipError_t launch_scan_bwd(const float *a, const float *h, const float *h0,
+                           const float *dh, const float *dhT, float *da,
+                           float *db, float *dh0, int64_t B, int64_t T,
+                           int64_t D, const ScanPlan &plan, void *ws,
+                           hipStream_t stream);
+
+// dst[i] = src ? src[i] : 0 for i < n (empty-sequence final states).
+hipError_t launch_copy_or_zero(float *dst, const float *src, int64_t n,
+                               hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// chunkwise linear attention
+// ---------------------------------------------------------------------------
+
+struct ChunkPlan {
+  int64_t P = 1;          // segments along time per (batch, head)
+  int64_t seg_chunks = 0; // chunks per segment
+  size_t ws_fwd = 0;      // workspace bytes, forward
+  size_t ws_bwd = 0;      // workspace bytes, backward
+};
+
+ChunkPlan plan_chunk(int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV);
+
+hipError_t launch_chunk_fwd(const uint16_t *q, const uint16_t *k,
+                            const uint16_t *v, const float *l,
+                            const float *S0, uint16_t *o, float *ST,
+                            int64_t B, int64_t H, int64_t T, int64_t DK,
+                            int64_t DV, const ChunkPlan &plan, void *ws,
+                            hipStream_t stream);
+
+hipError_t launch_chunk_bwd(const uint16_t *q, const uint16_t *k,
+                            const uint16_t *v, const float *l,
+                            const float *S0, const uint16_t *dO,
+                            const float *dST, uint16_t *dq, uint16_t *dk,
+                            uint16_t *dv, float *dl, float *dS0, int64_t B,
+                            int64_t H, int64_t T, int64_t DK, int64_t DV,
+                            const ChunkPlan &plan, void *ws,
+                            hipStream_t stream);
+
+}  // namespace cla

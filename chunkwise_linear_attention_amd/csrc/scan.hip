@@ -1,0 +1,381 @@
+// Diagonal (per-channel) linear-recurrence scan, forward and backward, for
+// gfx950.
+//
+// Citations (page title, then section):
+//   ZTF  = "Parallel scan" (zerotofrontier.app, ssm/parallel-scan)
+//   WIKI = "Parallel Scan" (aiwiki.thehackersbrain.dev)
+//
+// The recurrence h_t = a_t h_{t-1} + b_t is a scan of affine pairs under
+// (a1, b1) . (a2, b2) = (a1 a2, a2 b1 + b2), the earlier step on the left
+// (ZTF "The scan for one number of state").  The backward is the same scan
+// run in reverse time over the pairs (a_{t+1}, dh_t) (ZTF "The backward pass
+// is a scan in reverse").  Both directions share one kernel template.
+//
+// Layout: [B, T, D] fp32, channels contiguous.  A workgroup owns 16 * VEC
+// channels of one batch row and sweeps its time range in blocks of
+// kBlock = 4 * kNW * kK steps:
+//   lane  = 16 channel lanes (VEC channels each, float4 when VEC = 4)
+//         x 4 time slots;   wave w holds slots 4w .. 4w+3;
+//   slot j of a block owns the kK consecutive steps j*kK .. j*kK + kK - 1.
+// Per block: coalesced loads (each wave instruction covers 4 rows of 64
+// channels) -> a serial compose of kK steps in registers -> a Hillis-Steele
+// scan over the 4 slots of a wave with lane shuffles (WIKI code listing; ZTF
+// "The scan for one number of state") -> wave aggregates through LDS, folded
+// onto the pair carried from the previous block (WIKI: "carry one composed
+// pair across the chunk boundary") -> each lane recomputes its kK states from
+// its incoming state and stores them.  No intermediate state reaches HBM.
+//
+// When B * D alone gives too few workgroups, the time axis is cut into P
+// segments: a first pass (AGG) writes each segment's composed pair, and the
+// main pass starts each segment from the fold of the earlier segments' pairs
+// (ZTF "Splitting one sequence across devices", done across workgroups).
+#include "internal.h"
+
+namespace cla {
+namespace {
+
+constexpr int kNW = 8;                  // waves per workgroup
+constexpr int kK = 4;                   // steps per lane per block
+constexpr int kBlock = 4 * kNW * kK;    // 128 steps per block
+constexpr int64_t kTargetGroups = 512;  // workgroups wanted to fill 256 CUs
+
+template <int VEC>
+struct Pair {
+  float A[VEC];
+  float S[VEC];
+};
+
+template <int VEC>
+__device__ __forceinline__ void ldv(const float *p, float (&x)[VEC]) {
+  if constexpr (VEC == 4) {
+    const float4 v = *reinterpret_cast<const float4 *>(p);
+    x[0] = v.x;
+    x[1] = v.y;
+    x[2] = v.z;
+    x[3] = v.w;
+  } else {
+    x[0] = *p;
+  }
+}
+
+template <int VEC>
+__device__ __forceinline__ void stv(float *p, const float (&x)[VEC]) {
+  if constexpr (VEC == 4) {
+    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  } else {
+    *p = x[0];
+  }
+}
+
+template <int VEC>
+__device__ __forceinline__ void fillv(float (&x)[VEC], float v) {
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) x[e] = v;
+}
+
+struct ScanArgs {
+  const float *a;      // [B, T, D] decays
+  const float *x;      // forward: b; backward: dh
+  const float *hprev;  // backward: forward output h (h_{t-1}); forward: unused
+  const float *init;   // forward: h0; backward: dhT (NULL = zeros)
+  const float *h0;     // backward: forward h0 for da at t = 0 (NULL = zeros)
+  float *y;            // forward: h; backward: db
+  float *y2;           // backward: da
+  float *fin;          // forward: hT; backward: dh0 (NULL = skip)
+  float2 *agg;         // [P - 1][B * D] composed pair of each segment
+  int64_t B, T, D;
+  int64_t seg_len;
+  int64_t P;
+  int64_t groups_per_batch;
+};
+
+// DIR = 0: scan position u is time t = u, pair (a_t, b_t), state h.
+// DIR = 1: scan position u is time t = T - 1 - u, pair (a_{t+1}, dh_t) with
+//          a_{T+1} = 1, state hbar; outputs db_t = hbar_t, da_t = hbar_t h_{t-1}.
+// AGG    : only compose each segment's pair (segments 0 .. P-2) into agg.
+template <int VEC, int DIR, bool AGG>
+__global__ __launch_bounds__(kNW * 64) void scan_kernel(ScanArgs p) {
+  constexpr int CG = 16 * VEC;
+  __shared__ Pair<VEC> wagg[2][kNW][16];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int cq = lane & 15;
+  const int s = lane >> 4;
+  const int slot = w * 4 + s;
+
+  const int64_t g = blockIdx.x;
+  const int64_t seg = blockIdx.y;
+  const int64_t bb = g / p.groups_per_batch;
+  const int64_t c = (g % p.groups_per_batch) * CG + cq * VEC;
+  const bool cvalid = c < p.D;  // VEC = 4 implies D % 4 == 0
+  const int64_t T = p.T, D = p.D;
+  const int64_t u_begin = seg * p.seg_len;
+  const int64_t u_end = min(T, u_begin + p.seg_len);
+  const int64_t base = bb * T * D + c;
+
+  // carry: the state entering this segment (main pass) or the composed pair
+  // of the steps seen so far (AGG pass)
+  float cA[VEC], cS[VEC];
+  fillv<VEC>(cA, 1.0f);
+  fillv<VEC>(cS, 0.0f);
+  if constexpr (!AGG) {
+    if (cvalid && p.init) ldv<VEC>(p.init + bb * D + c, cS);
+    for (int64_t q = 0; q < seg; ++q) {
+      if (cvalid) {
+        const float2 *ap = p.agg + q * p.B * D + bb * D + c;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float2 pr = ap[e];
+          cS[e] = pr.x * cS[e] + pr.y;
+        }
+      }
+    }
+  }
+
+  int it = 0;
+  for (int64_t ub = u_begin; ub < u_end; ub += kBlock, ++it) {
+    float av[kK][VEC], xv[kK][VEC], hv[kK][VEC];
+#pragma unroll
+    for (int i = 0; i < kK; ++i) {
+      const int64_t u = ub + slot * kK + i;
+      const bool ok = cvalid && u < u_end;
+      fillv<VEC>(av[i], 1.0f);
+      fillv<VEC>(xv[i], 0.0f);
+      fillv<VEC>(hv[i], 0.0f);
+      if (ok) {
+        if constexpr (DIR == 0) {
+          ldv<VEC>(p.a + base + u * D, av[i]);
+          ldv<VEC>(p.x + base + u * D, xv[i]);
+        } else {
+          const int64_t t = T - 1 - u;
+          if (t + 1 < T) ldv<VEC>(p.a + base + (t + 1) * D, av[i]);
+          ldv<VEC>(p.x + base + t * D, xv[i]);
+          if constexpr (!AGG) {
+            if (t >= 1) {
+              ldv<VEC>(p.hprev + base + (t - 1) * D, hv[i]);
+            } else if (p.h0) {
+              ldv<VEC>(p.h0 + bb * D + c, hv[i]);
+            }
+          }
+        }
+      }
+    }
+
+    // serial compose of this lane's kK steps (earlier step on the left)
+    float A[VEC], S[VEC];
+    fillv<VEC>(A, 1.0f);
+    fillv<VEC>(S, 0.0f);
+#pragma unroll
+    for (int i = 0; i < kK; ++i) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        S[e] = av[i][e] * S[e] + xv[i][e];
+        A[e] = A[e] * av[i][e];
+      }
+    }
+
+    // Hillis-Steele over the 4 slots of the wave: shifts of 1 and 2 slots
+#pragma unroll
+    for (int sh = 16; sh < 64; sh <<= 1) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float pA = __shfl_up(A[e], sh, 64);
+        const float pS = __shfl_up(S[e], sh, 64);
+        if (lane >= sh) {
+          S[e] = A[e] * pS + S[e];
+          A[e] = A[e] * pA;
+        }
+      }
+    }
+    // exclusive prefix inside the wave
+    float eA[VEC], eS[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      eA[e] = __shfl_up(A[e], 16, 64);
+      eS[e] = __shfl_up(S[e], 16, 64);
+      if (lane < 16) {
+        eA[e] = 1.0f;
+        eS[e] = 0.0f;
+      }
+    }
+    const int buf = it & 1;
+    if (s == 3) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        wagg[buf][w][cq].A[e] = A[e];
+        wagg[buf][w][cq].S[e] = S[e];
+      }
+    }
+    __syncthreads();
+
+    // fold the wave aggregates onto the carry; remember the state entering
+    // this wave
+    float hs[VEC];
+    fillv<VEC>(hs, 0.0f);
+#pragma unroll
+    for (int u = 0; u < kNW; ++u) {
+      if (u == w) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) hs[e] = cS[e];
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float wa = wagg[buf][u][cq].A[e];
+        const float ws = wagg[buf][u][cq].S[e];
+        cS[e] = wa * cS[e] + ws;
+        if constexpr (AGG) cA[e] = cA[e] * wa;
+      }
+    }
+
+    if constexpr (!AGG) {
+      float st[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) st[e] = eA[e] * hs[e] + eS[e];
+#pragma unroll
+      for (int i = 0; i < kK; ++i) {
+        const int64_t u = ub + slot * kK + i;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) st[e] = av[i][e] * st[e] + xv[i][e];
+        if (cvalid && u < u_end) {
+          const int64_t t = DIR == 0 ? u : T - 1 - u;
+          stv<VEC>(p.y + base + t * D, st);
+          if constexpr (DIR == 1) {
+            float dav[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) dav[e] = st[e] * hv[i][e];
+            stv<VEC>(p.y2 + base + t * D, dav);
+          }
+        }
+      }
+    }
+  }
+
+  if (w == 0 && s == 0 && cvalid) {
+    if constexpr (AGG) {
+      float2 *ap = p.agg + seg * p.B * D + bb * D + c;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) ap[e] = make_float2(cA[e], cS[e]);
+    } else {
+      if (seg == p.P - 1 && p.fin) {
+        if constexpr (DIR == 0) {
+          stv<VEC>(p.fin + bb * D + c, cS);
+        } else {
+          float a0[VEC];
+          ldv<VEC>(p.a + base, a0);  // a_1, the decay of the first step
+          float d0[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) d0[e] = a0[e] * cS[e];
+          stv<VEC>(p.fin + bb * D + c, d0);
+        }
+      }
+    }
+  }
+}
+
+__global__ void copy_or_zero_kernel(float *dst, const float *src, int64_t n) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src ? src[i] : 0.0f;
+}
+
+bool aligned16(const void *ptr) {
+  return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0;
+}
+
+template <int VEC, int DIR>
+hipError_t run(ScanArgs args, const ScanPlan &plan, hipStream_t stream) {
+  constexpr int CG = 16 * VEC;
+  args.groups_per_batch = (args.D + CG - 1) / CG;
+  const int64_t groups = args.B * args.groups_per_batch;
+  if (plan.P > 1) {
+    dim3 grid((unsigned)groups, (unsigned)(plan.P - 1));
+    hipLaunchKernelGGL((scan_kernel<VEC, DIR, true>), grid, dim3(kNW * 64), 0,
+                       stream, args);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid((unsigned)groups, (unsigned)plan.P);
+  hipLaunchKernelGGL((scan_kernel<VEC, DIR, false>), grid, dim3(kNW * 64), 0,
+                     stream, args);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+ScanPlan plan_scan(int64_t B, int64_t T, int64_t D) {
+  ScanPlan plan;
+  plan.seg_len = T;
+  if (B <= 0 || T <= 0 || D <= 0) return plan;
+  const int64_t groups = B * ((D + 63) / 64);
+  const int64_t nblk = (T + kBlock - 1) / kBlock;
+  int64_t P = 1;
+  if (groups < kTargetGroups) {
+    P = (kTargetGroups + groups - 1) / groups;
+    if (P > nblk) P = nblk;
+  }
+  const int64_t seg_blocks = (nblk + P - 1) / P;
+  P = (nblk + seg_blocks - 1) / seg_blocks;
+  plan.P = P;
+  plan.seg_len = seg_blocks * kBlock;
+  plan.ws_bytes = (size_t)(P - 1) * (size_t)B * (size_t)D * sizeof(float2);
+  return plan;
+}
+
+hipError_t launch_scan_fwd(const float *a, const float *b, const float *h0,
+                           float *h, float *hT, int64_t B, int64_t T,
+                           int64_t D, const ScanPlan &plan, void *ws,
+                           hipStream_t stream) {
+  ScanArgs args{};
+  args.a = a;
+  args.x = b;
+  args.init = h0;
+  args.y = h;
+  args.fin = hT;
+  args.agg = static_cast<float2 *>(ws);
+  args.B = B;
+  args.T = T;
+  args.D = D;
+  args.seg_len = plan.seg_len;
+  args.P = plan.P;
+  const bool v4 = (D % 4 == 0) && aligned16(a) && aligned16(b) && aligned16(h) &&
+                  (!h0 || aligned16(h0)) && (!hT || aligned16(hT));
+  return v4 ? run<4, 0>(args, plan, stream) : run<1, 0>(args, plan, stream);
+}
+
+hipError_t launch_scan_bwd(const float *a, const float *h, const float *h0,
+                           const float *dh, const float *dhT, float *da,
+                           float *db, float *dh0, int64_t B, int64_t T,
+                           int64_t D, const ScanPlan &plan, void *ws,
+                           hipStream_t stream) {
+  ScanArgs args{};
+  args.a = a;
+  args.x = dh;
+  args.hprev = h;
+  args.init = dhT;
+  args.h0 = h0;
+  args.y = db;
+  args.y2 = da;
+  args.fin = dh0;
+  args.agg = static_cast<float2 *>(ws);
+  args.B = B;
+  args.T = T;
+  args.D = D;
+  args.seg_len = plan.seg_len;
+  args.P = plan.P;
+  const bool v4 = (D % 4 == 0) && aligned16(a) && aligned16(h) && aligned16(dh) &&
+                  aligned16(da) && aligned16(db) && (!h0 || aligned16(h0)) &&
+                  (!dhT || aligned16(dhT)) && (!dh0 || aligned16(dh0));
+  return v4 ? run<4, 1>(args, plan, stream) : run<1, 1>(args, plan, stream);
+}
+
+hipError_t launch_copy_or_zero(float *dst, const float *src, int64_t n,
+                               hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int threads = 256;
+  const int64_t blocks = (n + threads - 1) / threads;
+  hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)blocks), dim3(threads),
+                     0, stream, dst, src, n);
+  return hipGetLastError();
+}
+
+}  // namespace cla

@@ -1,0 +1,170 @@
+/*
+ * cla.h -- C ABI of libcla, gated linear-recurrence scans for AMD MI355X
+ * (gfx950).
+ *
+ * Two regimes of the recurrence h_t = a_t h_{t-1} + b_t:
+ *
+ *   diagonal state   h_t = a_t * h_{t-1} + b_t, elementwise per channel
+ *                    ("Parallel scan", zerotofrontier.app ssm/parallel-scan,
+ *                    sections "The scan for one number of state" and "A
+ *                    vectorized scan for diagonal states"; "Parallel Scan",
+ *                    aiwiki.thehackersbrain.dev, section "Composition").
+ *
+ *   matrix state     S_t = a_t S_{t-1} + k_t v_t^T,  o_t = S_t^T q_t,
+ *                    a_t = exp(l_t), computed chunkwise ("Parallel scan",
+ *                    section "The chunkwise algorithm"; "Lightning
+ *                    Attention-2: A Free Lunch for Handling Unlimited Sequence
+ *                    Lengths in Large Language Models", Eq. 4-10 and Alg. 1).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as inputs/outputs are DEVICE pointers owned by the
+ *     caller; tensors are dense, row-major, contiguous.  The library never
+ *     allocates, frees or synchronizes: it validates the arguments on the
+ *     host, enqueues its kernels on `stream` (NULL = the default stream) and
+ *     returns.  Results are ready when the stream reaches that point.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Arguments are checked on the host before any launch, in this order:
+ *     shapes (negative -> CLA_ERR_BAD_SHAPE), unsupported sizes
+ *     (CLA_ERR_UNSUPPORTED), required pointers (NULL -> CLA_ERR_NULL_ARG),
+ *     workspace (too small -> CLA_ERR_WORKSPACE), outputs overlapping inputs
+ *     or each other (CLA_ERR_ALIAS).  A failed check launches nothing.
+ *     CLA_ERR_HIP reports a failed launch.
+ *   - A zero-sized problem (B, D, H = 0) is a no-op.  T = 0 is an empty
+ *     sequence: the final state equals the initial state (zeros if NULL) and
+ *     the initial-state gradient equals the final-state gradient.
+ *   - Results are deterministic: the same inputs give bit-identical outputs
+ *     (no atomics in any reduction).
+ *   - Calls that share a workspace must be ordered (one stream, or events).
+ */
+#ifndef CLA_H
+#define CLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A HIP stream (hipStream_t); NULL selects the default stream. */
+typedef struct ihipStream_t *cla_stream_t;
+
+enum {
+  CLA_OK = 0,
+  CLA_ERR_NULL_ARG = 1,    /* a required pointer is NULL                      */
+  CLA_ERR_BAD_SHAPE = 2,   /* a size is negative                              */
+  CLA_ERR_UNSUPPORTED = 3, /* DK/DV not in {64, 128}, chunk != 64, T too long */
+  CLA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required         */
+  CLA_ERR_ALIAS = 5,       /* an output overlaps an input or another output   */
+  CLA_ERR_HIP = 6          /* a HIP launch failed                             */
+};
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *cla_status_string(int status);
+
+/* Library version string, e.g. "cla 0.1 gfx950". */
+const char *cla_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Diagonal state                                                            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Workspace bytes that cla_scan_fwd / cla_scan_bwd need for this shape (may
+ * be 0).  When the batch and channel count alone cannot fill the GPU, the
+ * time axis is split into segments whose composed pairs (A, beta) are kept
+ * in the workspace ("Parallel scan", section "Splitting one sequence across
+ * devices": an exclusive scan of per-piece pairs, then each piece resumes
+ * from its incoming state).  Returns 0 for invalid shapes.
+ */
+size_t cla_scan_workspace_bytes(int64_t B, int64_t T, int64_t D);
+
+/*
+ * Forward scan.  "Parallel scan", sections "The scan for one number of
+ * state" (recurrence, h_0 = 0 unless given) and "Scans over vector and matrix
+ * states" (a nonzero h_0 is folded into the first step).
+ *   a, b : [B, T, D] fp32 inputs (decays and inputs; a may be 0 or 1).
+ *   h0   : [B, D] fp32 initial state, or NULL for zeros.
+ *   h    : [B, T, D] fp32 output, h[b, t, d] = state after step t.
+ *   hT   : [B, D] fp32 final state, or NULL to skip.
+ */
+int cla_scan_fwd(const float *a, const float *b, const float *h0, float *h,
+                 float *hT, int64_t B, int64_t T, int64_t D, void *workspace,
+                 size_t workspace_bytes, cla_stream_t stream);
+
+/*
+ * Backward of cla_scan_fwd.  "Parallel scan", section "The backward pass is a
+ * scan in reverse": the adjoint hbar_t = dL/dh_t satisfies
+ *   hbar_T = dh_T + dhT,  hbar_t = dh_t + a_{t+1} hbar_{t+1},
+ * and db_t = hbar_t, da_t = hbar_t h_{t-1} (h_0 at t = 1), dh0 = a_1 hbar_1.
+ *   a    : [B, T, D] fp32, the forward decays.
+ *   h    : [B, T, D] fp32, the forward output (supplies h_{t-1}).
+ *   h0   : [B, D] fp32 forward initial state, or NULL for zeros.
+ *   dh   : [B, T, D] fp32 gradient arriving at h.
+ *   dhT  : [B, D] fp32 gradient arriving at the final state, or NULL.
+ *   da, db : [B, T, D] fp32 outputs.
+ *   dh0  : [B, D] fp32 output, or NULL to skip.
+ */
+int cla_scan_bwd(const float *a, const float *h, const float *h0,
+                 const float *dh, const float *dhT, float *da, float *db,
+                 float *dh0, int64_t B, int64_t T, int64_t D, void *workspace,
+                 size_t workspace_bytes, cla_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Matrix state, chunkwise (declared here, defined in the chunk kernels)     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Workspace bytes for cla_chunk_fwd (backward = 0) or cla_chunk_bwd
+ * (backward = 1) at this shape.  Returns 0 for an invalid shape.
+ */
+size_t cla_chunk_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t DK,
+                                 int64_t DV, int64_t chunk, int backward);
+
+/*
+ * Chunkwise forward.  "Parallel scan", section "The chunkwise algorithm":
+ * chunks of `chunk` tokens (the last may be shorter); inside a chunk the
+ * decay-masked product (Q K^T (.) L) V, between chunks the carried state,
+ *   O_[j] = (Q_[j] K_[j]^T (.) L) V_[j] + diag(lambda) Q_[j] S_[j-1],
+ *   S_[j] = a_{chunk total} S_[j-1] + K_[j]^T diag(gamma) V_[j],
+ * with the decays built from in-chunk cumulative log sums (section "Long
+ * products without underflow").  Lightning Attention-2 Alg. 1 is the case of
+ * a constant decay.
+ *   q, k      : [B, H, T, DK] bf16.     v : [B, H, T, DV] bf16.
+ *   log_decay : [B, H, T] fp32, l_t = log a_t; finite (not checked).
+ *   S0        : [B, H, DK, DV] fp32 initial state, or NULL for zeros.
+ *   o         : [B, H, T, DV] bf16 output.
+ *   ST        : [B, H, DK, DV] fp32 final state, or NULL to skip.
+ *   DK, DV in {64, 128}; chunk must be 64.
+ */
+int cla_chunk_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                  const float *log_decay, const float *S0, uint16_t *o,
+                  float *ST, int64_t B, int64_t H, int64_t T, int64_t DK,
+                  int64_t DV, int64_t chunk, void *workspace,
+                  size_t workspace_bytes, cla_stream_t stream);
+
+/*
+ * Chunkwise backward.  "Parallel scan", section "The backward pass of linear
+ * attention" (adjoint state, the four gradients, the closed-form decay
+ * gradient that needs no stored states) and Lightning Attention-2 Eq. 11-20,
+ * Alg. 2 (dQ in forward chunk order, dK and dV in reverse chunk order).
+ *   q, k, v, log_decay, S0 : as in cla_chunk_fwd.
+ *   dO        : [B, H, T, DV] bf16 gradient arriving at o.
+ *   dST       : [B, H, DK, DV] fp32 gradient arriving at S_T, or NULL.
+ *   dq, dk    : [B, H, T, DK] bf16 outputs.   dv : [B, H, T, DV] bf16 output.
+ *   dlog_decay: [B, H, T] fp32 output, dL/dl_t.
+ *   dS0       : [B, H, DK, DV] fp32 output, or NULL to skip.
+ */
+int cla_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                  const float *log_decay, const float *S0, const uint16_t *dO,
+                  const float *dST, uint16_t *dq, uint16_t *dk, uint16_t *dv,
+                  float *dlog_decay, float *dS0, int64_t B, int64_t H,
+                  int64_t T, int64_t DK, int64_t DV, int64_t chunk,
+                  void *workspace, size_t workspace_bytes,
+                  cla_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CLA_H */

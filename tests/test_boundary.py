@@ -1,0 +1,103 @@
+"""The C ABI boundary on the host (CPU only, no GPU calls).
+
+The library must load, export every function include/cla.h declares, and
+reject bad arguments with the documented status codes before any launch.
+Fake non-NULL addresses are used for pointers the checks only compare; every
+call here returns before the library touches the device.
+"""
+
+import ctypes
+
+import pytest
+
+from chunkwise_linear_attention_amd import _lib
+
+OK, NULL, SHAPE, UNSUP, WS, ALIAS = 0, 1, 2, 3, 4, 5
+
+# distinct fake device addresses, far apart so that ranges never overlap
+A, B_, C, D_, E, F, G, H_, I, J, K, L = (0x10_0000_0000 * (i + 1) for i in range(12))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _lib.header_symbols()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+
+
+def test_status_strings(lib):
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.cla_status_string(code).decode().startswith(name)
+    assert b"UNKNOWN" in lib.cla_status_string(99)
+    assert lib.cla_version().startswith(b"cla")
+
+
+def test_scan_workspace_sizes(lib):
+    # a batch-and-channel count that fills the GPU needs no workspace
+    assert lib.cla_scan_workspace_bytes(8, 16384, 4096) == 0
+    # one 64-channel group is split into 32 segments of 128 steps
+    assert lib.cla_scan_workspace_bytes(1, 4096, 64) == 31 * 64 * 8
+    assert lib.cla_scan_workspace_bytes(-1, 4, 4) == 0
+    assert lib.cla_scan_workspace_bytes(1, 0, 4) == 0
+
+
+def test_scan_fwd_validation(lib):
+    f = lib.cla_scan_fwd
+    assert f(A, B_, None, C, None, -1, 4, 4, None, 0, None) == SHAPE
+    assert f(A, B_, None, C, None, 1, -4, 4, None, 0, None) == SHAPE
+    assert f(None, B_, None, C, None, 1, 4, 4, None, 0, None) == NULL
+    assert f(A, None, None, C, None, 1, 4, 4, None, 0, None) == NULL
+    assert f(A, B_, None, None, None, 1, 4, 4, None, 0, None) == NULL
+    # small B * D needs a workspace
+    assert f(A, B_, None, C, None, 1, 4096, 64, None, 0, None) == WS
+    assert f(A, B_, None, C, None, 1, 4096, 64, D_, 100, None) == WS
+    # outputs overlapping inputs or each other
+    assert f(A, B_, None, A, None, 1, 4096, 64, D_, 1 << 20, None) == ALIAS
+    assert f(A, B_, None, C, B_ + 16, 1, 4096, 64, D_, 1 << 20, None) == ALIAS
+    assert f(A, B_, None, C, None, 1, 4096, 64, C + 4, 1 << 20, None) == ALIAS
+    # empty batch / channels: no-op
+    assert f(None, None, None, None, None, 0, 4, 4, None, 0, None) == OK
+    assert f(None, None, None, None, None, 3, 4, 0, None, 0, None) == OK
+
+
+def test_scan_bwd_validation(lib):
+    f = lib.cla_scan_bwd
+    assert f(A, B_, None, C, None, D_, E, None, 1, -1, 4, None, 0, None) == SHAPE
+    for i in range(5):
+        args = [A, B_, None, C, None, D_, E, None]
+        args[[0, 1, 3, 5, 6][i]] = None
+        assert f(*args, 1, 4, 4, None, 0, None) == NULL
+    assert f(A, B_, None, C, None, D_, E, None, 1, 4096, 64, None, 0, None) == WS
+    assert f(A, B_, None, C, None, C, E, None, 1, 4096, 64, F, 1 << 20, None) == ALIAS
+    assert f(A, B_, None, C, None, D_, D_, None, 1, 4096, 64, F, 1 << 20, None) == ALIAS
+    assert f(None, None, None, None, None, None, None, None, 0, 9, 9, None, 0, None) == OK
+
+
+def test_chunk_validation(lib):
+    fw = lib.cla_chunk_fwd
+    bw = lib.cla_chunk_bwd
+    ws = lib.cla_chunk_workspace_bytes
+    assert ws(1, 1, 64, 32, 64, 64, 0) == 0          # unsupported head size
+    assert fw(A, B_, C, D_, None, E, None, -1, 1, 64, 64, 64, 64, None, 0, None) == SHAPE
+    assert fw(A, B_, C, D_, None, E, None, 1, 1, 64, 32, 64, 64, None, 0, None) == UNSUP
+    assert fw(A, B_, C, D_, None, E, None, 1, 1, 64, 64, 96, 64, None, 0, None) == UNSUP
+    assert fw(A, B_, C, D_, None, E, None, 1, 1, 64, 64, 64, 32, None, 0, None) == UNSUP
+    assert fw(None, B_, C, D_, None, E, None, 1, 1, 64, 64, 64, 64, None, 0, None) == NULL
+    assert fw(A, B_, C, D_, None, None, None, 1, 1, 64, 64, 64, 64, None, 0, None) == NULL
+    assert fw(A, B_, C, D_, None, A, None, 1, 1, 64, 64, 64, 64, F, 1 << 30, None) == ALIAS
+    assert fw(None, None, None, None, None, None, None, 0, 4, 64, 64, 64, 64, None, 0, None) == OK
+    args = [A, B_, C, D_, None, E, None, F, G, H_, I, None]
+    assert bw(*args, 1, 1, 64, 64, 128, 32, None, 0, None) == UNSUP
+    for idx in (0, 1, 2, 3, 5, 7, 8, 9, 10):
+        a2 = list(args)
+        a2[idx] = None
+        assert bw(*a2, 1, 1, 64, 64, 64, 64, None, 0, None) == NULL, idx
+    a2 = list(args)
+    a2[8] = A  # dk aliases q
+    assert bw(*a2, 1, 1, 64, 64, 64, 64, J, 1 << 30, None) == ALIAS
