@@ -39,6 +39,9 @@ int hip_status(hipError_t e) { return e == hipSuccess ? CLA_OK : CLA_ERR_HIP; }
 
 bool supported_head_dim(int64_t d) { return d == 64 || d == 128; }
 
+// bf16 tiles are moved in 16-byte pieces
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 }  // namespace
 
 extern "C" {
@@ -133,6 +136,8 @@ int cla_chunk_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   const size_t qk = nh * (size_t)T * (size_t)DK * 2, vv = nh * (size_t)T * (size_t)DV * 2;
   const size_t ll = nh * (size_t)T * 4, ss = nh * (size_t)DK * (size_t)DV * 4;
   if (T > 0 && (!q || !k || !v || !log_decay || !o)) return CLA_ERR_NULL_ARG;
+  if (T > 0 && !(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o)))
+    return CLA_ERR_UNSUPPORTED;
   const cla::ChunkPlan plan = cla::plan_chunk(B, H, T, DK, DV);
   if (plan.ws_fwd > 0 && (!workspace || workspace_bytes < plan.ws_fwd))
     return CLA_ERR_WORKSPACE;
@@ -164,6 +169,9 @@ int cla_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   const size_t ll = nh * (size_t)T * 4, ss = nh * (size_t)DK * (size_t)DV * 4;
   if (T > 0 && (!q || !k || !v || !log_decay || !dO || !dq || !dk || !dv || !dlog_decay))
     return CLA_ERR_NULL_ARG;
+  if (T > 0 && !(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(dO) &&
+                 aligned16(dq) && aligned16(dk) && aligned16(dv)))
+    return CLA_ERR_UNSUPPORTED;
   const cla::ChunkPlan plan = cla::plan_chunk(B, H, T, DK, DV);
   if (plan.ws_bwd > 0 && (!workspace || workspace_bytes < plan.ws_bwd))
     return CLA_ERR_WORKSPACE;

@@ -1,18 +1,449 @@
-// Chunkwise linear attention kernels (placeholder until the MFMA kernels land).
+// Chunkwise linear attention with a scalar decay per step, forward pass and
+// the segment machinery shared with the backward, for gfx950.
+//
+// Citations (page title, then section / equation):
+//   ZTF = "Parallel scan" (zerotofrontier.app, ssm/parallel-scan)
+//   LA2 = "Lightning Attention-2: A Free Lunch for Handling Unlimited
+//         Sequence Lengths in Large Language Models" (paper-graph-ui summary)
+//
+// Recurrence (ZTF "The chunkwise algorithm"): S_t = a_t S_{t-1} + k_t v_t^T,
+// o_t = S_t^T q_t, a_t = exp(l_t).  Chunks of TC = 64 tokens; for chunk j
+// starting after token t0, with in-chunk cumulative logs c_r = l_{t0+1} + ...
+// + l_{t0+r} (ZTF "Long products without underflow": sums of logs inside a
+// short window stay accurate; no long cumulative sums, no ratios):
+//   mask     D_rs  = exp(c_r - c_s) for r >= s (diagonal 1), else 0
+//   lambda_r       = exp(c_r)          decay from the chunk start
+//   gamma_s        = exp(c_n - c_s)    decay to the chunk end
+//   alpha          = exp(c_n)
+//   O_[j] = (Q K^T (.) D) V + diag(lambda) Q S_[j-1]      (LA2 Eq. 8)
+//   S_[j] = alpha S_[j-1] + (diag(gamma) K)^T V           (LA2 Eq. 10)
+// The mask is applied elementwise to the fp32 score tile; it is never
+// factored into exp(c_r) exp(-c_s), which overflows for strong decays.
+//
+// Workgroup = 4 waves on one (batch*head, segment).  Per chunk:
+//   stage  : Q (row-major), K (row-major and transposed), V (transposed) into
+//            LDS; wave 0 computes c, lambda, gamma, alpha.
+//   scores : wave w computes the transposed scores for queries 16w..16w+15
+//            against the key tiles at or below the diagonal, masks them in
+//            fp32 and writes P = bf16(S (.) D) to LDS.
+//   output : wave w owns value columns [w DV/4, (w+1) DV/4) and computes
+//            O^T = V^T P^T + S^T (lambda Q)^T on MFMA; its slice of the fp32
+//            state, held in MFMA accumulators, is fed back (as bf16) as the A
+//            operand of the inter-chunk product without leaving registers.
+//   update : S <- alpha S + (gamma K)^T V on MFMA into the same accumulators.
+// Inputs are bf16, the state and all accumulation fp32.
+#include "chunk_common.h"
 #include "internal.h"
 
 namespace cla {
+namespace chunk {
+namespace {
 
-ChunkPlan plan_chunk(int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV) {
-  (void)B; (void)H; (void)T; (void)DK; (void)DV;
-  return ChunkPlan{};
+constexpr int64_t kTargetWG = 512;   // 2 workgroups per CU on 256 CUs
+constexpr int64_t kMinSegChunks = 4;
+
+struct FwdArgs {
+  const uint16_t *q;       // [nh, T, DK]
+  const uint16_t *k;       // [nh, T, DK]
+  const uint16_t *v;       // [nh, T, DV]
+  const float *l;          // [nh, T]
+  const float *S0;         // [nh, DK, DV] (or [nh, DV, DK] if s0_trans); NULL = 0
+  const float *Sin;        // [P-1, nh, DK, DV] state entering segments 1..P-1
+  uint16_t *o;             // [nh, T, DV]
+  float *ST;               // [nh, DK, DV] (or transposed if st_trans); NULL = skip
+  float *Sloc;             // state-only pass: [P-1, nh, DK, DV]
+  float *aloc;             // state-only pass: [P-1, nh] total decay of the segment
+  const uint16_t *xdot;    // optional [nh, T, DV]: rdot[t] = sum_j xdot[t, j] o[t, j]
+  float *rdot;             // [nh, T]
+  int64_t nh, T, seg_chunks, P;
+  int s0_trans, st_trans;
+};
+
+// MODE 0: outputs (o, S_T, rdot).  MODE 1: segment state only (Sloc, aloc).
+template <int DK, int DV, int MODE>
+__global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
+  constexpr int NJ = DV / 64;          // 16-column tiles per wave
+  constexpr int NDT = DK / 16;         // 16-row tiles of the state
+  constexpr int QKB = 64 * DK * 2;     // bytes of a row-major [64 x DK] tile
+  constexpr int TB_K = DK * 128;       // bytes of a transposed [DK x 64] tile
+  constexpr int TB_V = DV * 128;
+  constexpr int OFF_QS = 0;
+  constexpr int OFF_KS = OFF_QS + (MODE == 0 ? QKB : 0);
+  constexpr int OFF_KT = OFF_KS + (MODE == 0 ? QKB : 0);
+  constexpr int OFF_VT = OFF_KT + TB_K;
+  constexpr int OFF_PS = OFF_VT + TB_V;
+  constexpr int OFF_C = OFF_PS + (MODE == 0 ? 64 * 128 : 0);
+  constexpr int OFF_RD = OFF_C + 3 * 64 * 4 + 16;
+  constexpr int SMEM = OFF_RD + (MODE == 0 ? NWAVE * 64 * 4 : 0);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  unsigned char *QS = smem + OFF_QS;
+  unsigned char *KS = smem + OFF_KS;
+  unsigned char *KT = smem + OFF_KT;
+  unsigned char *VT = smem + OFF_VT;
+  unsigned char *PS = smem + OFF_PS;
+  float *CS = reinterpret_cast<float *>(smem + OFF_C);
+  float *LAM = CS + 64;
+  float *GAM = CS + 128;
+  float *ALPHA = CS + 192;
+  float *RD = reinterpret_cast<float *>(smem + OFF_RD);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int64_t bh = blockIdx.x % a.nh;
+  const int64_t seg = blockIdx.x / a.nh;
+  const int64_t T = a.T;
+  const int64_t nchunks = (T + TC - 1) / TC;
+  const int64_t c_begin = seg * a.seg_chunks;
+  const int64_t c_end = min(nchunks, c_begin + a.seg_chunks);
+  const int j0 = w * (DV / 4);  // first value column of this wave
+
+  const uint16_t *qh = a.q + bh * T * DK;
+  const uint16_t *kh = a.k + bh * T * DK;
+  const uint16_t *vh = a.v + bh * T * DV;
+  const float *lh = a.l + bh * T;
+
+  // S_acc[dt][jt][i] = S[16 dt + 4 lg + i][j0 + 16 jt + li]
+  f32x4 S_acc[NDT][NJ];
+  {
+    const float *src = nullptr;
+    bool trans = false;
+    if (MODE == 0) {
+      if (seg == 0) {
+        src = a.S0 ? a.S0 + bh * DK * DV : nullptr;
+        trans = a.s0_trans;
+      } else {
+        src = a.Sin + ((seg - 1) * a.nh + bh) * DK * DV;
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = 16 * dt + 4 * lg + i, j = j0 + 16 * jt + li;
+          S_acc[dt][jt][i] = src ? src[trans ? j * DK + d : d * DV + j] : 0.f;
+        }
+  }
+  float alpha_total = 1.f;
+
+  for (int64_t ci = c_begin; ci < c_end; ++ci) {
+    const int64_t t0 = ci * TC;
+    const int n = (int)min<int64_t>(TC, T - t0);
+
+    TileRegs<DK> kr;
+    TileRegs<DV> vr;
+    TileRegs<DK> qr;
+    tile_load<DK>(kh + t0 * DK, n, tid, kr);
+    tile_load<DV>(vh + t0 * DV, n, tid, vr);
+    if (MODE == 0) tile_load<DK>(qh + t0 * DK, n, tid, qr);
+    float lv = 0.f;
+    if (w == 0 && lane < n) lv = lh[t0 + lane];
+
+    __syncthreads();  // the previous chunk's LDS reads are done
+    tile_store_cols<DK>(KT, tid, kr);
+    tile_store_cols<DV>(VT, tid, vr);
+    if (MODE == 0) {
+      tile_store_rows<DK>(KS, tid, kr);
+      tile_store_rows<DK>(QS, tid, qr);
+    }
+    if (w == 0) {
+      // inclusive in-chunk cumulative log (rows >= n add 0)
+      float c = lv;
+#pragma unroll
+      for (int sh = 1; sh < 64; sh <<= 1) {
+        const float p = __shfl_up(c, sh, 64);
+        if (lane >= sh) c += p;
+      }
+      const float cl = __shfl(c, 63, 64);
+      CS[lane] = c;
+      LAM[lane] = expf(c);
+      GAM[lane] = expf(cl - c);
+      if (lane == 0) ALPHA[0] = expf(cl);
+    }
+    __syncthreads();
+
+    if constexpr (MODE == 0) {
+      // ---- scores: P[r][s] for r in [16w, 16w+16), transposed tiles ----
+      const int r = 16 * w + li;
+      const float cr = CS[r];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        f32x4 acc = zero4();
+        if (st <= w) {
+#pragma unroll
+          for (int kk = 0; kk < DK / 32; ++kk) {
+            const bf16x8 ka = lds_frag<DK / 8>(KS, 16 * st + li, 4 * kk + lg);
+            const bf16x8 qb = lds_frag<DK / 8>(QS, r, 4 * kk + lg);
+            acc = mfma(ka, qb, acc);
+          }
+        }
+        // acc[i] = (K Q^T)[s = 16 st + 4 lg + i][r]
+        bf16x4 pv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * st + 4 * lg + i;
+          float p = 0.f;
+          if (s <= r) p = acc[i] * __expf(cr - CS[s]);
+          pv[i] = tobf(p);
+        }
+        *reinterpret_cast<bf16x4 *>(PS + swz_off<8>(r, 2 * st + (lg >> 1)) + (lg & 1) * 8) = pv;
+      }
+      __syncthreads();
+
+      // ---- output: O^T for this wave's value columns, all 64 rows ----
+      bf16x8 vfrag[NJ][2];
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          vfrag[jt][kb] = lds_frag<8>(VT, j0 + 16 * jt + li, 4 * kb + lg);
+      // the state slice as bf16 A operands: rows j, k-set
+      // {32kk + 4lg + 0..3, 32kk + 16 + 4lg + 0..3}
+      bf16x8 sfrag[DK / 32][NJ];
+#pragma unroll
+      for (int kk = 0; kk < DK / 32; ++kk)
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) sfrag[kk][jt] = cvt8(S_acc[2 * kk][jt], S_acc[2 * kk + 1][jt]);
+
+      float rd_part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int rr = 16 * rt + li;
+        const float lam = LAM[rr];
+        // (lambda Q)^T B operands for the same k permutation
+        bf16x8 qfrag[DK / 32];
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+          const bf16x4 lo = lds_half<DK / 8>(QS, rr, 32 * kk + 4 * lg);
+          const bf16x4 hi = lds_half<DK / 8>(QS, rr, 32 * kk + 16 + 4 * lg);
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[e] = tof(lo[e]) * lam;
+            x[e + 4] = tof(hi[e]) * lam;
+          }
+          qfrag[kk] = cvt8(x);
+        }
+        bf16x8 pfrag[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) pfrag[kb] = lds_frag<8>(PS, rr, 4 * kb + lg);
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            if (kb <= (rt >> 1)) acc = mfma(vfrag[jt][kb], pfrag[kb], acc);
+#pragma unroll
+          for (int kk = 0; kk < DK / 32; ++kk) acc = mfma(sfrag[kk][jt], qfrag[kk], acc);
+          // acc[i] = O[row rr][col j0 + 16 jt + 4 lg + i]
+          if (rr < n) {
+            const int jc = j0 + 16 * jt + 4 * lg;
+            bf16x4 ov;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ov[i] = tobf(acc[i]);
+            *reinterpret_cast<bf16x4 *>(a.o + (bh * T + t0 + rr) * DV + jc) = ov;
+            if (a.xdot) {
+              const bf16x4 xv =
+                  *reinterpret_cast<const bf16x4 *>(a.xdot + (bh * T + t0 + rr) * DV + jc);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) rd_part[rt] += tof(xv[i]) * acc[i];
+            }
+          }
+        }
+      }
+      if (a.xdot) {
+        // reduce over the 4 lane groups, then over the 4 waves through LDS
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          float x = rd_part[rt];
+          x += __shfl_xor(x, 16, 64);
+          x += __shfl_xor(x, 32, 64);
+          if (lg == 0) RD[w * 64 + 16 * rt + li] = x;
+        }
+        __syncthreads();
+        if (tid < 64 && tid < n) {
+          const float s = RD[tid] + RD[64 + tid] + RD[128 + tid] + RD[192 + tid];
+          a.rdot[bh * T + t0 + tid] = s;
+        }
+      }
+    }
+
+    // ---- state update: S <- alpha S + (gamma K)^T V ----
+    const float alpha = ALPHA[0];
+    alpha_total *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S_acc[dt][jt][i] *= alpha;
+    bf16x8 vb[NJ][2];
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) vb[jt][kb] = lds_frag<8>(VT, j0 + 16 * jt + li, 4 * kb + lg);
+    float gam[2][8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gam[kb][e] = GAM[32 * kb + 8 * lg + e];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kt = lds_frag<8>(KT, 16 * dt + li, 4 * kb + lg);
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = tof(kt[e]) * gam[kb][e];
+        const bf16x8 ka = cvt8(x);
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) S_acc[dt][jt] = mfma(ka, vb[jt][kb], S_acc[dt][jt]);
+      }
+    }
+  }
+
+  // ---- segment outputs ----
+  if constexpr (MODE == 0) {
+    if (seg == a.P - 1 && a.ST) {
+      float *dst = a.ST + bh * DK * DV;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d = 16 * dt + 4 * lg + i, j = j0 + 16 * jt + li;
+            dst[a.st_trans ? j * DK + d : d * DV + j] = S_acc[dt][jt][i];
+          }
+    }
+  } else {
+    float *dst = a.Sloc + (seg * a.nh + bh) * DK * DV;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = 16 * dt + 4 * lg + i, j = j0 + 16 * jt + li;
+          dst[d * DV + j] = S_acc[dt][jt][i];
+        }
+    if (tid == 0) a.aloc[seg * a.nh + bh] = alpha_total;
+  }
 }
 
-hipError_t launch_chunk_fwd(const uint16_t *, const uint16_t *, const uint16_t *,
-                            const float *, const float *, uint16_t *, float *,
-                            int64_t, int64_t, int64_t, int64_t, int64_t,
-                            const ChunkPlan &, void *, hipStream_t) {
-  return hipErrorNotSupported;
+// Incoming state of every segment from the segment pairs (alpha_p, S_p):
+// S_in(0) = S0, S_in(p+1) = alpha_p S_in(p) + S_p (ZTF "Splitting one
+// sequence across devices": an exclusive scan of per-piece pairs).  In place:
+// slot p of Sloc becomes the state entering segment p+1.  One thread per
+// state element, sequential over segments.
+__global__ void segment_scan_kernel(float *Sloc, const float *aloc, const float *S0,
+                                    int s0_trans, int64_t nh, int64_t P, int DK, int DV) {
+  const int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t per = (int64_t)DK * DV;
+  if (e >= nh * per) return;
+  const int64_t bh = e / per, x = e % per;
+  const int d = (int)(x / DV), j = (int)(x % DV);
+  float carry = S0 ? S0[bh * per + (s0_trans ? (int64_t)j * DK + d : x)] : 0.f;
+  for (int64_t p = 0; p + 1 < P; ++p) {
+    float *slot = Sloc + (p * nh + bh) * per + x;
+    carry = aloc[p * nh + bh] * carry + *slot;
+    *slot = carry;
+  }
+}
+
+template <int DK, int DV>
+hipError_t fwd_impl(FwdArgs args, hipStream_t stream) {
+  const int64_t P = args.P;
+  if (P > 1) {
+    dim3 g1((unsigned)(args.nh * (P - 1)));
+    hipLaunchKernelGGL((chunk_fwd_kernel<DK, DV, 1>), g1, dim3(NTHR), 0, stream, args);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = args.nh * DK * DV;
+    hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       stream, args.Sloc, args.aloc, args.S0, args.s0_trans, args.nh, P, DK, DV);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    args.Sin = args.Sloc;
+  }
+  dim3 g((unsigned)(args.nh * P));
+  hipLaunchKernelGGL((chunk_fwd_kernel<DK, DV, 0>), g, dim3(NTHR), 0, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t fwd_dispatch(const FwdArgs &args, int DK, int DV, hipStream_t stream) {
+  if (DK == 64 && DV == 64) return fwd_impl<64, 64>(args, stream);
+  if (DK == 64 && DV == 128) return fwd_impl<64, 128>(args, stream);
+  if (DK == 128 && DV == 64) return fwd_impl<128, 64>(args, stream);
+  if (DK == 128 && DV == 128) return fwd_impl<128, 128>(args, stream);
+  return hipErrorInvalidValue;
+}
+
+// workspace carve-up for one forward-type pass
+struct FwdWs {
+  float *Sloc;
+  float *aloc;
+  size_t bytes;
+};
+
+FwdWs fwd_ws(void *base, int64_t nh, int64_t P, int64_t DK, int64_t DV) {
+  FwdWs w{};
+  if (P <= 1) return w;
+  const size_t s_bytes = (size_t)(P - 1) * nh * DK * DV * sizeof(float);
+  const size_t a_bytes = ((size_t)(P - 1) * nh * sizeof(float) + 255) & ~(size_t)255;
+  w.Sloc = static_cast<float *>(base);
+  w.aloc = base ? reinterpret_cast<float *>(static_cast<char *>(base) + s_bytes) : nullptr;
+  w.bytes = s_bytes + a_bytes;
+  return w;
+}
+
+}  // namespace
+}  // namespace chunk
+
+ChunkPlan plan_chunk(int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV) {
+  ChunkPlan plan;
+  const int64_t nh = B * H;
+  const int64_t nchunks = (T + chunk::TC - 1) / chunk::TC;
+  plan.seg_chunks = nchunks;
+  if (nh <= 0 || nchunks <= 0) return plan;
+  int64_t P = 1;
+  if (nh < chunk::kTargetWG) {
+    P = (chunk::kTargetWG + nh - 1) / nh;
+    const int64_t maxP = (nchunks + chunk::kMinSegChunks - 1) / chunk::kMinSegChunks;
+    if (P > maxP) P = maxP;
+    if (P < 1) P = 1;
+  }
+  const int64_t segc = (nchunks + P - 1) / P;
+  P = (nchunks + segc - 1) / segc;
+  plan.P = P;
+  plan.seg_chunks = segc;
+  plan.ws_fwd = chunk::fwd_ws(nullptr, nh, P, DK, DV).bytes;
+  plan.ws_bwd = 0;
+  return plan;
+}
+
+hipError_t launch_chunk_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                            const float *l, const float *S0, uint16_t *o, float *ST,
+                            int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV,
+                            const ChunkPlan &plan, void *ws, hipStream_t stream) {
+  chunk::FwdArgs args{};
+  args.q = q;
+  args.k = k;
+  args.v = v;
+  args.l = l;
+  args.S0 = S0;
+  args.o = o;
+  args.ST = ST;
+  args.nh = B * H;
+  args.T = T;
+  args.seg_chunks = plan.seg_chunks;
+  args.P = plan.P;
+  const chunk::FwdWs w = chunk::fwd_ws(ws, args.nh, plan.P, DK, DV);
+  args.Sloc = w.Sloc;
+  args.aloc = w.aloc;
+  return chunk::fwd_dispatch(args, (int)DK, (int)DV, stream);
 }
 
 hipError_t launch_chunk_bwd(const uint16_t *, const uint16_t *, const uint16_t *,

@@ -13,7 +13,7 @@
 //
 // Layout: [B, T, D] fp32, channels contiguous.  A workgroup owns 16 * VEC
 // channels of one batch row and sweeps its time range in blocks of
-// kBlock = 4 * kNW * kK steps:
+// 4 * NW * K steps (NW waves, K steps per lane):
 //   lane  = 16 channel lanes (VEC channels each, float4 when VEC = 4)
 //         x 4 time slots;   wave w holds slots 4w .. 4w+3;
 //   slot j of a block owns the kK consecutive steps j*kK .. j*kK + kK - 1.
@@ -34,10 +34,37 @@
 namespace cla {
 namespace {
 
-constexpr int kNW = 8;                  // waves per workgroup
-constexpr int kK = 4;                   // steps per lane per block
-constexpr int kBlock = 4 * kNW * kK;    // 128 steps per block
-constexpr int64_t kTargetGroups = 512;  // workgroups wanted to fill 256 CUs
+// Tile shapes (compile-time; overridable for tuning builds).  Measured on
+// MI355X at B=8, T=16384, D=4096: the forward is fastest with 4 waves x 2
+// steps per lane, the backward (3 reads, 2 writes per element) with 2 waves
+// x 2 steps per lane.
+#ifndef CLA_SCAN_FWD_NW
+#define CLA_SCAN_FWD_NW 4
+#endif
+#ifndef CLA_SCAN_FWD_K
+#define CLA_SCAN_FWD_K 2
+#endif
+#ifndef CLA_SCAN_BWD_NW
+#define CLA_SCAN_BWD_NW 2
+#endif
+#ifndef CLA_SCAN_BWD_K
+#define CLA_SCAN_BWD_K 2
+#endif
+#ifndef CLA_SCAN_PREFETCH
+#define CLA_SCAN_PREFETCH 1
+#endif
+#ifndef CLA_SCAN_NT
+#define CLA_SCAN_NT 1
+#endif
+#ifndef CLA_SCAN_TARGET_GROUPS
+#define CLA_SCAN_TARGET_GROUPS 512
+#endif
+// Segment lengths are multiples of kPlanBlock, a multiple of both block
+// lengths 4 * NW * K.
+constexpr int kPlanBlock = 128;
+static_assert(kPlanBlock % (4 * CLA_SCAN_FWD_NW * CLA_SCAN_FWD_K) == 0, "block");
+static_assert(kPlanBlock % (4 * CLA_SCAN_BWD_NW * CLA_SCAN_BWD_K) == 0, "block");
+constexpr int64_t kTargetGroups = CLA_SCAN_TARGET_GROUPS;  // to fill 256 CUs
 
 template <int VEC>
 struct Pair {
@@ -45,25 +72,46 @@ struct Pair {
   float S[VEC];
 };
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming loads/stores: every element is touched once, so they are marked
+// non-temporal to keep them from displacing reusable lines in the caches.
 template <int VEC>
 __device__ __forceinline__ void ldv(const float *p, float (&x)[VEC]) {
   if constexpr (VEC == 4) {
-    const float4 v = *reinterpret_cast<const float4 *>(p);
+#if CLA_SCAN_NT
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+#else
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+#endif
     x[0] = v.x;
     x[1] = v.y;
     x[2] = v.z;
     x[3] = v.w;
   } else {
+#if CLA_SCAN_NT
+    x[0] = __builtin_nontemporal_load(p);
+#else
     x[0] = *p;
+#endif
   }
 }
 
 template <int VEC>
 __device__ __forceinline__ void stv(float *p, const float (&x)[VEC]) {
   if constexpr (VEC == 4) {
-    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    const f32x4 v = {x[0], x[1], x[2], x[3]};
+#if CLA_SCAN_NT
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
+#else
+    *reinterpret_cast<f32x4 *>(p) = v;
+#endif
   } else {
+#if CLA_SCAN_NT
+    __builtin_nontemporal_store(x[0], p);
+#else
     *p = x[0];
+#endif
   }
 }
 
@@ -93,9 +141,11 @@ struct ScanArgs {
 // DIR = 1: scan position u is time t = T - 1 - u, pair (a_{t+1}, dh_t) with
 //          a_{T+1} = 1, state hbar; outputs db_t = hbar_t, da_t = hbar_t h_{t-1}.
 // AGG    : only compose each segment's pair (segments 0 .. P-2) into agg.
-template <int VEC, int DIR, bool AGG>
+// kNW waves per workgroup, kK steps per lane per block.
+template <int VEC, int DIR, bool AGG, int kNW, int kK>
 __global__ __launch_bounds__(kNW * 64) void scan_kernel(ScanArgs p) {
   constexpr int CG = 16 * VEC;
+  constexpr int kBlock = 4 * kNW * kK;
   __shared__ Pair<VEC> wagg[2][kNW][16];
 
   const int lane = threadIdx.x & 63;
@@ -133,9 +183,10 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(ScanArgs p) {
     }
   }
 
-  int it = 0;
-  for (int64_t ub = u_begin; ub < u_end; ub += kBlock, ++it) {
-    float av[kK][VEC], xv[kK][VEC], hv[kK][VEC];
+  // Loads of one block of kK steps for this lane; steps outside the segment
+  // (or channels past D) load the identity pair (1, 0).
+  auto load_block = [&](int64_t ub, float (&av)[kK][VEC], float (&xv)[kK][VEC],
+                        float (&hv)[kK][VEC]) {
 #pragma unroll
     for (int i = 0; i < kK; ++i) {
       const int64_t u = ub + slot * kK + i;
@@ -161,6 +212,22 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(ScanArgs p) {
         }
       }
     }
+  };
+
+  float av[kK][VEC], xv[kK][VEC], hv[kK][VEC];
+#if CLA_SCAN_PREFETCH
+  float nav[kK][VEC], nxv[kK][VEC], nhv[kK][VEC];
+  load_block(u_begin, av, xv, hv);
+#endif
+  int it = 0;
+  for (int64_t ub = u_begin; ub < u_end; ub += kBlock, ++it) {
+#if CLA_SCAN_PREFETCH
+    // issue the next block's loads before working on this one; the LDS-only
+    // barrier below does not wait for them
+    if (ub + kBlock < u_end) load_block(ub + kBlock, nav, nxv, nhv);
+#else
+    load_block(ub, av, xv, hv);
+#endif
 
     // serial compose of this lane's kK steps (earlier step on the left)
     float A[VEC], S[VEC];
@@ -249,6 +316,17 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(ScanArgs p) {
         }
       }
     }
+#if CLA_SCAN_PREFETCH
+#pragma unroll
+    for (int i = 0; i < kK; ++i) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        av[i][e] = nav[i][e];
+        xv[i][e] = nxv[i][e];
+        hv[i][e] = nhv[i][e];
+      }
+    }
+#endif
   }
 
   if (w == 0 && s == 0 && cvalid) {
@@ -285,17 +363,19 @@ bool aligned16(const void *ptr) {
 template <int VEC, int DIR>
 hipError_t run(ScanArgs args, const ScanPlan &plan, hipStream_t stream) {
   constexpr int CG = 16 * VEC;
+  constexpr int kNW = DIR == 0 ? CLA_SCAN_FWD_NW : CLA_SCAN_BWD_NW;
+  constexpr int kK = DIR == 0 ? CLA_SCAN_FWD_K : CLA_SCAN_BWD_K;
   args.groups_per_batch = (args.D + CG - 1) / CG;
   const int64_t groups = args.B * args.groups_per_batch;
   if (plan.P > 1) {
     dim3 grid((unsigned)groups, (unsigned)(plan.P - 1));
-    hipLaunchKernelGGL((scan_kernel<VEC, DIR, true>), grid, dim3(kNW * 64), 0,
+    hipLaunchKernelGGL((scan_kernel<VEC, DIR, true, kNW, kK>), grid, dim3(kNW * 64), 0,
                        stream, args);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   dim3 grid((unsigned)groups, (unsigned)plan.P);
-  hipLaunchKernelGGL((scan_kernel<VEC, DIR, false>), grid, dim3(kNW * 64), 0,
+  hipLaunchKernelGGL((scan_kernel<VEC, DIR, false, kNW, kK>), grid, dim3(kNW * 64), 0,
                      stream, args);
   return hipGetLastError();
 }
@@ -307,7 +387,7 @@ ScanPlan plan_scan(int64_t B, int64_t T, int64_t D) {
   plan.seg_len = T;
   if (B <= 0 || T <= 0 || D <= 0) return plan;
   const int64_t groups = B * ((D + 63) / 64);
-  const int64_t nblk = (T + kBlock - 1) / kBlock;
+  const int64_t nblk = (T + kPlanBlock - 1) / kPlanBlock;
   int64_t P = 1;
   if (groups < kTargetGroups) {
     P = (kTargetGroups + groups - 1) / groups;
@@ -316,7 +396,7 @@ ScanPlan plan_scan(int64_t B, int64_t T, int64_t D) {
   const int64_t seg_blocks = (nblk + P - 1) / P;
   P = (nblk + seg_blocks - 1) / seg_blocks;
   plan.P = P;
-  plan.seg_len = seg_blocks * kBlock;
+  plan.seg_len = seg_blocks * kPlanBlock;
   plan.ws_bytes = (size_t)(P - 1) * (size_t)B * (size_t)D * sizeof(float2);
   return plan;
 }
