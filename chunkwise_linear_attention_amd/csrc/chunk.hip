@@ -33,6 +33,7 @@
 //   update : S <- alpha S + (gamma K)^T V on MFMA into the same accumulators.
 // Inputs are bf16, the state and all accumulation fp32.
 #include "chunk_common.h"
+#include "chunk_kernels.h"
 #include "internal.h"
 
 namespace cla {
@@ -41,23 +42,6 @@ namespace {
 
 constexpr int64_t kTargetWG = 512;   // 2 workgroups per CU on 256 CUs
 constexpr int64_t kMinSegChunks = 4;
-
-struct FwdArgs {
-  const uint16_t *q;       // [nh, T, DK]
-  const uint16_t *k;       // [nh, T, DK]
-  const uint16_t *v;       // [nh, T, DV]
-  const float *l;          // [nh, T]
-  const float *S0;         // [nh, DK, DV] (or [nh, DV, DK] if s0_trans); NULL = 0
-  const float *Sin;        // [P-1, nh, DK, DV] state entering segments 1..P-1
-  uint16_t *o;             // [nh, T, DV]
-  float *ST;               // [nh, DK, DV] (or transposed if st_trans); NULL = skip
-  float *Sloc;             // state-only pass: [P-1, nh, DK, DV]
-  float *aloc;             // state-only pass: [P-1, nh] total decay of the segment
-  const uint16_t *xdot;    // optional [nh, T, DV]: rdot[t] = sum_j xdot[t, j] o[t, j]
-  float *rdot;             // [nh, T]
-  int64_t nh, T, seg_chunks, P;
-  int s0_trans, st_trans;
-};
 
 // MODE 0: outputs (o, S_T, rdot).  MODE 1: segment state only (Sloc, aloc).
 template <int DK, int DV, int MODE>
@@ -339,14 +323,16 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
 // slot p of Sloc becomes the state entering segment p+1.  One thread per
 // state element, sequential over segments.
 __global__ void segment_scan_kernel(float *Sloc, const float *aloc, const float *S0,
-                                    int s0_trans, int64_t nh, int64_t P, int DK, int DV) {
+                                    int s0_trans, int reverse, int64_t nh, int64_t P, int DK,
+                                    int DV) {
   const int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   const int64_t per = (int64_t)DK * DV;
   if (e >= nh * per) return;
   const int64_t bh = e / per, x = e % per;
   const int d = (int)(x / DV), j = (int)(x % DV);
   float carry = S0 ? S0[bh * per + (s0_trans ? (int64_t)j * DK + d : x)] : 0.f;
-  for (int64_t p = 0; p + 1 < P; ++p) {
+  for (int64_t i = 0; i + 1 < P; ++i) {
+    const int64_t p = reverse ? P - 2 - i : i;
     float *slot = Sloc + (p * nh + bh) * per + x;
     carry = aloc[p * nh + bh] * carry + *slot;
     *slot = carry;
@@ -361,10 +347,8 @@ hipError_t fwd_impl(FwdArgs args, hipStream_t stream) {
     hipLaunchKernelGGL((chunk_fwd_kernel<DK, DV, 1>), g1, dim3(NTHR), 0, stream, args);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t n = args.nh * DK * DV;
-    hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                       stream, args.Sloc, args.aloc, args.S0, args.s0_trans, args.nh, P, DK, DV);
-    e = hipGetLastError();
+    e = launch_segment_scan(args.Sloc, args.aloc, args.S0, args.s0_trans, 0, args.nh, P, DK,
+                            DV, stream);
     if (e != hipSuccess) return e;
     args.Sin = args.Sloc;
   }
@@ -373,13 +357,26 @@ hipError_t fwd_impl(FwdArgs args, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t fwd_dispatch(const FwdArgs &args, int DK, int DV, hipStream_t stream) {
+}  // namespace
+
+hipError_t launch_segment_scan(float *slots, const float *aloc, const float *init,
+                               int init_trans, int reverse, int64_t nh, int64_t P, int DK,
+                               int DV, hipStream_t stream) {
+  const int64_t n = nh * DK * DV;
+  hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     stream, slots, aloc, init, init_trans, reverse, nh, P, DK, DV);
+  return hipGetLastError();
+}
+
+hipError_t fwd_dispatch(FwdArgs args, int DK, int DV, hipStream_t stream) {
   if (DK == 64 && DV == 64) return fwd_impl<64, 64>(args, stream);
   if (DK == 64 && DV == 128) return fwd_impl<64, 128>(args, stream);
   if (DK == 128 && DV == 64) return fwd_impl<128, 64>(args, stream);
   if (DK == 128 && DV == 128) return fwd_impl<128, 128>(args, stream);
   return hipErrorInvalidValue;
 }
+
+namespace {
 
 // workspace carve-up for one forward-type pass
 struct FwdWs {
@@ -396,6 +393,30 @@ FwdWs fwd_ws(void *base, int64_t nh, int64_t P, int64_t DK, int64_t DV) {
   w.Sloc = static_cast<float *>(base);
   w.aloc = base ? reinterpret_cast<float *>(static_cast<char *>(base) + s_bytes) : nullptr;
   w.bytes = s_bytes + a_bytes;
+  return w;
+}
+
+// backward workspace: the forward-type segment area (reused by the reverse
+// pass), q . dq and k . dk per token, and the final state for <S_T, dS_T>
+struct BwdWs {
+  FwdWs seg;
+  float *r1, *r2, *ST;
+  size_t bytes;
+};
+
+BwdWs bwd_ws(void *base, int64_t nh, int64_t T, int64_t P, int64_t DK, int64_t DV) {
+  BwdWs w{};
+  w.seg = fwd_ws(base, nh, P, DK, DV);
+  size_t off = w.seg.bytes;
+  auto carve = [&](size_t bytes) -> float * {
+    float *p = base ? reinterpret_cast<float *>(static_cast<char *>(base) + off) : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  };
+  w.r1 = carve((size_t)nh * T * sizeof(float));
+  w.r2 = carve((size_t)nh * T * sizeof(float));
+  w.ST = carve((size_t)nh * DK * DV * sizeof(float));
+  w.bytes = off;
   return w;
 }
 
@@ -420,7 +441,7 @@ ChunkPlan plan_chunk(int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV) {
   plan.P = P;
   plan.seg_chunks = segc;
   plan.ws_fwd = chunk::fwd_ws(nullptr, nh, P, DK, DV).bytes;
-  plan.ws_bwd = 0;
+  plan.ws_bwd = chunk::bwd_ws(nullptr, nh, T, P, DK, DV).bytes;
   return plan;
 }
 
@@ -446,12 +467,59 @@ hipError_t launch_chunk_fwd(const uint16_t *q, const uint16_t *k, const uint16_t
   return chunk::fwd_dispatch(args, (int)DK, (int)DV, stream);
 }
 
-hipError_t launch_chunk_bwd(const uint16_t *, const uint16_t *, const uint16_t *,
-                            const float *, const float *, const uint16_t *,
-                            const float *, uint16_t *, uint16_t *, uint16_t *,
-                            float *, float *, int64_t, int64_t, int64_t, int64_t,
-                            int64_t, const ChunkPlan &, void *, hipStream_t) {
-  return hipErrorNotSupported;
+hipError_t launch_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                            const float *l, const float *S0, const uint16_t *dO,
+                            const float *dST, uint16_t *dq, uint16_t *dk, uint16_t *dv,
+                            float *dl, float *dS0, int64_t B, int64_t H, int64_t T,
+                            int64_t DK, int64_t DV, const ChunkPlan &plan, void *ws,
+                            hipStream_t stream) {
+  const int64_t nh = B * H;
+  const chunk::BwdWs w = chunk::bwd_ws(ws, nh, T, plan.P, DK, DV);
+  // dQ pass (forward chunk order): the forward recurrence on the transposed
+  // state S^T with keys v and values k, read by dO:
+  //   dQ_[j] = (dO V^T (.) D) K + diag(lambda) dO S_[j-1]^T   (LA2 Eq. 15)
+  // It also yields q . dq per token and S_T for the decay gradient.
+  chunk::FwdArgs fa{};
+  fa.q = dO;
+  fa.k = v;
+  fa.v = k;
+  fa.l = l;
+  fa.S0 = S0;
+  fa.s0_trans = 1;
+  fa.o = dq;
+  fa.ST = dST ? w.ST : nullptr;
+  fa.st_trans = 1;
+  fa.xdot = q;
+  fa.rdot = w.r1;
+  fa.Sloc = w.seg.Sloc;
+  fa.aloc = w.seg.aloc;
+  fa.nh = nh;
+  fa.T = T;
+  fa.seg_chunks = plan.seg_chunks;
+  fa.P = plan.P;
+  hipError_t e = chunk::fwd_dispatch(fa, (int)DV, (int)DK, stream);
+  if (e != hipSuccess) return e;
+  // dK/dV pass (reverse chunk order)
+  chunk::BwdArgs ba{};
+  ba.q = q;
+  ba.k = k;
+  ba.v = v;
+  ba.dO = dO;
+  ba.l = l;
+  ba.dST = dST;
+  ba.dk = dk;
+  ba.dv = dv;
+  ba.r2 = w.r2;
+  ba.dS0 = dS0;
+  ba.Gloc = w.seg.Sloc;
+  ba.aloc = w.seg.aloc;
+  ba.nh = nh;
+  ba.T = T;
+  ba.seg_chunks = plan.seg_chunks;
+  ba.P = plan.P;
+  e = chunk::bwd_kv_dispatch(ba, (int)DK, (int)DV, stream);
+  if (e != hipSuccess) return e;
+  return chunk::launch_dlog(w.r1, w.r2, dST ? w.ST : nullptr, dST, dl, nh, T, DK * DV, stream);
 }
 
 }  // namespace cla

@@ -1,0 +1,509 @@
+// Chunkwise linear attention, backward pass: the reverse-order dK/dV kernel
+// and the decay-gradient kernel, for gfx950.  The dQ pass is the forward
+// kernel run on (dO, V, K) (chunk.hip).
+//
+// Citations (page title, then section / equation):
+//   ZTF = "Parallel scan" (zerotofrontier.app, ssm/parallel-scan)
+//   LA2 = "Lightning Attention-2: A Free Lunch for Handling Unlimited
+//         Sequence Lengths in Large Language Models" (paper-graph-ui summary)
+//
+// ZTF "The backward pass of linear attention": the adjoint state obeys the
+// reverse recurrence Sbar_t = q_t dO_t^T + a_{t+1} Sbar_{t+1}; keys and values
+// get kbar_t = Sbar_t v_t and vbar_t = Sbar_t^T k_t.  Chunkwise, with G the
+// gradient of the state after chunk j (LA2 Eq. 17, 19, 20 with the index
+// convention of the per-token Eq. 12):
+//   dV_[j] = (Q K^T (.) D)^T dO + diag(gamma) K G
+//   dK_[j] = (dO V^T (.) D)^T Q + diag(gamma) V G^T
+//   G     <- alpha G + (diag(lambda) Q)^T dO       (state gradient entering j)
+// with the same in-chunk decays as the forward.  Chunks run last to first.
+//
+// Workgroup = 8 waves on one (batch*head, segment).  Waves 0-3 ("dV side")
+// each own the columns [w DV/4, (w+1) DV/4) of G in fp32 MFMA accumulators;
+// waves 4-7 ("dK side") each own the columns [w' DK/4, (w'+1) DK/4) of G^T.
+// Both copies are updated every chunk from the same bf16 operands, so each
+// side feeds its state straight back as an MFMA operand without an LDS round
+// trip.  The dK side also forms r2_s = k_s . dk_s (fp32, before rounding) for
+// the decay gradient.
+//
+// Decay gradient (ZTF "The backward pass of linear attention", the closed
+// form after Yang et al. 2023 Sec. 4.3): dl_u = sum_{t >= u} (q_t . dq_t -
+// k_t . dk_t), plus <S_T, dS_T> on every u when the final state has a
+// gradient (every path into the final state crosses every step).  A reverse
+// cumulative sum per sequence, accumulated in fp64.
+#include "chunk_common.h"
+#include "chunk_kernels.h"
+#include "internal.h"
+
+namespace cla {
+namespace chunk {
+
+namespace {
+
+constexpr int BTHR = 512;
+
+// MODE 0: dK, dV, r2, dS0.  MODE 1: the G recurrence of one segment from
+// zero (segments 1..P-1), for the segment scan.
+template <int DK, int DV, int MODE>
+__global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
+  constexpr int NJ = DV / 64;   // dV side: 16-col tiles of G per wave
+  constexpr int NI = DK / 64;   // dK side: 16-col tiles of G^T per wave
+  constexpr int RK = 64 * DK * 2, RV = 64 * DV * 2;  // row-major tile bytes
+  constexpr int TK = DK * 128, TV = DV * 128;        // transposed tile bytes
+  constexpr int OFF_QT = 0;
+  constexpr int OFF_DOT = OFF_QT + TK;
+  constexpr int OFF_QS = OFF_DOT + TV;
+  constexpr int OFF_KS = OFF_QS + (MODE == 0 ? RK : 0);
+  constexpr int OFF_VS = OFF_KS + (MODE == 0 ? RK : 0);
+  constexpr int OFF_DOS = OFF_VS + (MODE == 0 ? RV : 0);
+  constexpr int OFF_P1 = OFF_DOS + (MODE == 0 ? RV : 0);
+  constexpr int OFF_P2 = OFF_P1 + (MODE == 0 ? 64 * 128 : 0);
+  constexpr int OFF_C = OFF_P2 + (MODE == 0 ? 64 * 128 : 0);
+  constexpr int OFF_R2 = OFF_C + 3 * 64 * 4 + 16;
+  constexpr int SMEM = OFF_R2 + (MODE == 0 ? 4 * 64 * 4 : 0);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  unsigned char *QT = smem + OFF_QT;
+  unsigned char *DOT = smem + OFF_DOT;
+  unsigned char *QS = smem + OFF_QS;
+  unsigned char *KS = smem + OFF_KS;
+  unsigned char *VS = smem + OFF_VS;
+  unsigned char *DOS = smem + OFF_DOS;
+  unsigned char *P1 = smem + OFF_P1;  // P1T[s][r] = D[r][s] (q_r . k_s)
+  unsigned char *P2 = smem + OFF_P2;  // P2T[s][r] = D[r][s] (dO_r . v_s)
+  float *CS = reinterpret_cast<float *>(smem + OFF_C);
+  float *LAM = CS + 64;
+  float *GAM = CS + 128;
+  float *ALPHA = CS + 192;
+  float *R2P = reinterpret_cast<float *>(smem + OFF_R2);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int side = w >> 2, wv = w & 3;   // side 0: dV / G;  side 1: dK / G^T
+  const int64_t bh = blockIdx.x % a.nh;
+  const int64_t seg = MODE == 0 ? blockIdx.x / a.nh : 1 + blockIdx.x / a.nh;
+  const int64_t T = a.T;
+  const int64_t nchunks = (T + TC - 1) / TC;
+  const int64_t c_begin = seg * a.seg_chunks;
+  const int64_t c_end = min(nchunks, c_begin + a.seg_chunks);
+  const int jw0 = wv * (DV / 4);  // side 0: first column j of this wave
+  const int dw0 = wv * (DK / 4);  // side 1: first column d of G^T
+
+  const uint16_t *qh = a.q + bh * T * DK;
+  const uint16_t *kh = a.k + bh * T * DK;
+  const uint16_t *vh = a.v + bh * T * DV;
+  const uint16_t *doh = a.dO + bh * T * DV;
+  const float *lh = a.l + bh * T;
+
+  // One register array holds either side's state (both have DK*DV/1024
+  // tiles of 16 x 16):
+  //   side 0: Gs[dt * NJ + jt][i] = G[16 dt + 4 lg + i][jw0 + 16 jt + li]
+  //   side 1: Gs[jt * NI + it][i] = G^T[16 jt + 4 lg + i][dw0 + 16 it + li]
+  constexpr int NG = DK * DV / 1024;
+  static_assert((DK / 16) * NJ == NG && (DV / 16) * NI == NG, "state tiles");
+  f32x4 Gs[NG];
+#define G0(dt, jt) Gs[(dt) * NJ + (jt)]
+#define G1(jt, it) Gs[(jt) * NI + (it)]
+  {
+    const float *src = nullptr;
+    if (MODE == 0) {
+      if (seg == a.P - 1) {
+        src = a.dST ? a.dST + bh * DK * DV : nullptr;
+      } else {
+        src = a.Gin + (seg * a.nh + bh) * DK * DV;
+      }
+    }
+    if (side == 0) {
+#pragma unroll
+      for (int dt = 0; dt < DK / 16; ++dt)
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d = 16 * dt + 4 * lg + i, j = jw0 + 16 * jt + li;
+            G0(dt, jt)[i] = src ? src[d * DV + j] : 0.f;
+          }
+    } else {
+#pragma unroll
+      for (int jt = 0; jt < DV / 16; ++jt)
+#pragma unroll
+        for (int it = 0; it < NI; ++it)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = 16 * jt + 4 * lg + i, d = dw0 + 16 * it + li;
+            G1(jt, it)[i] = (MODE == 0 && src) ? src[d * DV + j] : 0.f;
+          }
+    }
+  }
+  float alpha_total = 1.f;
+
+  for (int64_t ci = c_end - 1; ci >= c_begin; --ci) {
+    const int64_t t0 = ci * TC;
+    const int n = (int)min<int64_t>(TC, T - t0);
+
+    // stage: threads 0..255 move Q and dO, threads 256..511 move K and V
+    TileRegs<DK> qr, kr;
+    TileRegs<DV> dr, vr;
+    const int ht = tid & 255;
+    if (tid < 256) {
+      tile_load<DK>(qh + t0 * DK, n, ht, qr);
+      tile_load<DV>(doh + t0 * DV, n, ht, dr);
+    } else if (MODE == 0) {
+      tile_load<DK>(kh + t0 * DK, n, ht, kr);
+      tile_load<DV>(vh + t0 * DV, n, ht, vr);
+    }
+    float lv = 0.f;
+    if (w == 0 && lane < n) lv = lh[t0 + lane];
+
+    __syncthreads();
+    if (tid < 256) {
+      tile_store_cols<DK>(QT, ht, qr);
+      tile_store_cols<DV>(DOT, ht, dr);
+      if (MODE == 0) {
+        tile_store_rows<DK>(QS, ht, qr);
+        tile_store_rows<DV>(DOS, ht, dr);
+      }
+    } else if (MODE == 0) {
+      tile_store_rows<DK>(KS, ht, kr);
+      tile_store_rows<DV>(VS, ht, vr);
+    }
+    if (w == 0) {
+      float c = lv;
+#pragma unroll
+      for (int sh = 1; sh < 64; sh <<= 1) {
+        const float p = __shfl_up(c, sh, 64);
+        if (lane >= sh) c += p;
+      }
+      const float cl = __shfl(c, 63, 64);
+      CS[lane] = c;
+      LAM[lane] = expf(c);
+      GAM[lane] = expf(cl - c);
+      if (lane == 0) ALPHA[0] = expf(cl);
+    }
+    __syncthreads();
+
+    if constexpr (MODE == 0) {
+      // ---- masked score tiles, stored transposed: P[s][r] for key tile wv ----
+      {
+        const int st = wv;
+        const int s = 16 * st + li;
+        const float cs = CS[s];
+        unsigned char *PT = side == 0 ? P1 : P2;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          f32x4 acc = zero4();
+          if (rt >= st) {
+            if (side == 0) {
+#pragma unroll
+              for (int kk = 0; kk < DK / 32; ++kk)
+                acc = mfma(lds_frag<DK / 8>(QS, 16 * rt + li, 4 * kk + lg),
+                           lds_frag<DK / 8>(KS, s, 4 * kk + lg), acc);
+            } else {
+#pragma unroll
+              for (int kk = 0; kk < DV / 32; ++kk)
+                acc = mfma(lds_frag<DV / 8>(DOS, 16 * rt + li, 4 * kk + lg),
+                           lds_frag<DV / 8>(VS, s, 4 * kk + lg), acc);
+            }
+          }
+          // acc[i] = X[r = 16 rt + 4 lg + i][s]
+          bf16x4 pv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * rt + 4 * lg + i;
+            float p = 0.f;
+            if (r >= s) p = acc[i] * __expf(CS[r] - cs);
+            pv[i] = tobf(p);
+          }
+          *reinterpret_cast<bf16x4 *>(PT + swz_off<8>(s, 2 * rt + (lg >> 1)) + (lg & 1) * 8) = pv;
+        }
+      }
+      __syncthreads();
+
+      if (side == 0) {
+        // ---- dV^T[j][s] = dO^T P1 + G^T (gamma K)^T ----
+        bf16x8 gfrag[DK / 32][NJ];
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk)
+#pragma unroll
+          for (int jt = 0; jt < NJ; ++jt) gfrag[kk][jt] = cvt8(G0(2 * kk, jt), G0(2 * kk + 1, jt));
+        bf16x8 dfrag[NJ][2];
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) dfrag[jt][kb] = lds_frag<8>(DOT, jw0 + 16 * jt + li, 4 * kb + lg);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const int s = 16 * st + li;
+          const float gs = GAM[s];
+          bf16x8 kfrag[DK / 32];
+#pragma unroll
+          for (int kk = 0; kk < DK / 32; ++kk) {
+            const bf16x4 lo = lds_half<DK / 8>(KS, s, 32 * kk + 4 * lg);
+            const bf16x4 hi = lds_half<DK / 8>(KS, s, 32 * kk + 16 + 4 * lg);
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[e] = tof(lo[e]) * gs;
+              x[e + 4] = tof(hi[e]) * gs;
+            }
+            kfrag[kk] = cvt8(x);
+          }
+          bf16x8 pfrag[2];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) pfrag[kb] = lds_frag<8>(P1, s, 4 * kb + lg);
+#pragma unroll
+          for (int jt = 0; jt < NJ; ++jt) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+              if (2 * kb + 1 >= st) acc = mfma(dfrag[jt][kb], pfrag[kb], acc);
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) acc = mfma(gfrag[kk][jt], kfrag[kk], acc);
+            // acc[i] = dV[s][jw0 + 16 jt + 4 lg + i]
+            if (s < n) {
+              bf16x4 ov;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) ov[i] = tobf(acc[i]);
+              *reinterpret_cast<bf16x4 *>(a.dv + (bh * T + t0 + s) * DV + jw0 + 16 * jt + 4 * lg) = ov;
+            }
+          }
+        }
+      } else {
+        // ---- dK^T[d][s] = Q^T P2 + G (gamma V)^T ; r2_s = k_s . dk_s ----
+        bf16x8 gfrag[DV / 32][NI];
+#pragma unroll
+        for (int kk = 0; kk < DV / 32; ++kk)
+#pragma unroll
+          for (int it = 0; it < NI; ++it) gfrag[kk][it] = cvt8(G1(2 * kk, it), G1(2 * kk + 1, it));
+        bf16x8 qfrag[NI][2];
+#pragma unroll
+        for (int it = 0; it < NI; ++it)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) qfrag[it][kb] = lds_frag<8>(QT, dw0 + 16 * it + li, 4 * kb + lg);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const int s = 16 * st + li;
+          const float gs = GAM[s];
+          bf16x8 vfrag[DV / 32];
+#pragma unroll
+          for (int kk = 0; kk < DV / 32; ++kk) {
+            const bf16x4 lo = lds_half<DV / 8>(VS, s, 32 * kk + 4 * lg);
+            const bf16x4 hi = lds_half<DV / 8>(VS, s, 32 * kk + 16 + 4 * lg);
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[e] = tof(lo[e]) * gs;
+              x[e + 4] = tof(hi[e]) * gs;
+            }
+            vfrag[kk] = cvt8(x);
+          }
+          bf16x8 pfrag[2];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) pfrag[kb] = lds_frag<8>(P2, s, 4 * kb + lg);
+          float r2p = 0.f;
+#pragma unroll
+          for (int it = 0; it < NI; ++it) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+              if (2 * kb + 1 >= st) acc = mfma(qfrag[it][kb], pfrag[kb], acc);
+#pragma unroll
+            for (int kk = 0; kk < DV / 32; ++kk) acc = mfma(gfrag[kk][it], vfrag[kk], acc);
+            // acc[i] = dK[s][dw0 + 16 it + 4 lg + i]
+            const int dc = dw0 + 16 * it + 4 * lg;
+            const bf16x4 kv = lds_half<DK / 8>(KS, s, dc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r2p += tof(kv[i]) * acc[i];
+            if (s < n) {
+              bf16x4 ov;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) ov[i] = tobf(acc[i]);
+              *reinterpret_cast<bf16x4 *>(a.dk + (bh * T + t0 + s) * DK + dc) = ov;
+            }
+          }
+          r2p += __shfl_xor(r2p, 16, 64);
+          r2p += __shfl_xor(r2p, 32, 64);
+          if (lg == 0) R2P[wv * 64 + s] = r2p;
+        }
+      }
+    }
+
+    // ---- state-gradient update (both copies) ----
+    const float alpha = ALPHA[0];
+    alpha_total *= alpha;
+    float lam[2][8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lam[kb][e] = LAM[32 * kb + 8 * lg + e];
+    if (side == 0) {
+      // G[d][j] += sum_r (lambda Q)^T[d][r] dO[r][j]
+#pragma unroll
+      for (int dt = 0; dt < DK / 16; ++dt)
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) G0(dt, jt)[i] *= alpha;
+      bf16x8 db[NJ][2];
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) db[jt][kb] = lds_frag<8>(DOT, jw0 + 16 * jt + li, 4 * kb + lg);
+#pragma unroll
+      for (int dt = 0; dt < DK / 16; ++dt) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 qt = lds_frag<8>(QT, 16 * dt + li, 4 * kb + lg);
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = tof(qt[e]) * lam[kb][e];
+          const bf16x8 qa = cvt8(x);
+#pragma unroll
+          for (int jt = 0; jt < NJ; ++jt) G0(dt, jt) = mfma(qa, db[jt][kb], G0(dt, jt));
+        }
+      }
+    } else if (MODE == 0) {
+      // G^T[j][d] += sum_r dO^T[j][r] (lambda Q)[r][d]
+#pragma unroll
+      for (int jt = 0; jt < DV / 16; ++jt)
+#pragma unroll
+        for (int it = 0; it < NI; ++it)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) G1(jt, it)[i] *= alpha;
+      bf16x8 qb[NI][2];
+#pragma unroll
+      for (int it = 0; it < NI; ++it)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 qt = lds_frag<8>(QT, dw0 + 16 * it + li, 4 * kb + lg);
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = tof(qt[e]) * lam[kb][e];
+          qb[it][kb] = cvt8(x);
+        }
+#pragma unroll
+      for (int jt = 0; jt < DV / 16; ++jt) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 da = lds_frag<8>(DOT, 16 * jt + li, 4 * kb + lg);
+#pragma unroll
+          for (int it = 0; it < NI; ++it) G1(jt, it) = mfma(da, qb[it][kb], G1(jt, it));
+        }
+      }
+    }
+
+    if constexpr (MODE == 0) {
+      __syncthreads();  // R2P complete
+      if (tid < 64 && tid < n)
+        a.r2[bh * T + t0 + tid] = R2P[tid] + R2P[64 + tid] + R2P[128 + tid] + R2P[192 + tid];
+    }
+  }
+
+  // ---- segment outputs ----
+  if constexpr (MODE == 0) {
+    if (seg == 0 && a.dS0 && side == 0) {
+      float *dst = a.dS0 + bh * DK * DV;
+#pragma unroll
+      for (int dt = 0; dt < DK / 16; ++dt)
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            dst[(16 * dt + 4 * lg + i) * DV + jw0 + 16 * jt + li] = G0(dt, jt)[i];
+    }
+  } else {
+    if (side == 0) {
+      float *dst = a.Gloc + ((seg - 1) * a.nh + bh) * DK * DV;
+#pragma unroll
+      for (int dt = 0; dt < DK / 16; ++dt)
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            dst[(16 * dt + 4 * lg + i) * DV + jw0 + 16 * jt + li] = G0(dt, jt)[i];
+    }
+    if (tid == 0) a.aloc[(seg - 1) * a.nh + bh] = alpha_total;
+  }
+}
+
+#undef G0
+#undef G1
+
+// dl_u = sdot + sum_{t >= u} (r1_t - r2_t), sdot = <S_T, dS_T> (0 if no dS_T).
+// One workgroup per sequence; fp64 accumulation.
+__global__ __launch_bounds__(256) void dlog_kernel(const float *r1, const float *r2,
+                                                   const float *ST, const float *dST,
+                                                   float *dl, int64_t T, int64_t per) {
+  __shared__ double red[256];
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  double sd = 0.0;
+  if (ST && dST) {
+    for (int64_t e = tid; e < per; e += 256)
+      sd += (double)ST[bh * per + e] * (double)dST[bh * per + e];
+  }
+  red[tid] = sd;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  const double sdot = red[0];
+  __syncthreads();
+  const int64_t L = (T + 255) / 256;
+  const int64_t lo = min<int64_t>(T, tid * L), hi = min<int64_t>(T, lo + L);
+  const float *x1 = r1 + bh * T, *x2 = r2 + bh * T;
+  double local = 0.0;
+  for (int64_t t = lo; t < hi; ++t) local += (double)x1[t] - (double)x2[t];
+  red[tid] = local;
+  __syncthreads();
+  // suffix sums over threads (Hillis-Steele, from the right)
+  for (int o = 1; o < 256; o <<= 1) {
+    const double add = (tid + o < 256) ? red[tid + o] : 0.0;
+    __syncthreads();
+    red[tid] += add;
+    __syncthreads();
+  }
+  double acc = sdot + (tid + 1 < 256 ? red[tid + 1] : 0.0);
+  float *out = dl + bh * T;
+  for (int64_t t = hi - 1; t >= lo; --t) {
+    acc += (double)x1[t] - (double)x2[t];
+    out[t] = (float)acc;
+  }
+}
+
+template <int DK, int DV>
+hipError_t bwd_kv_impl(BwdArgs args, hipStream_t stream) {
+  const int64_t P = args.P;
+  if (P > 1) {
+    hipLaunchKernelGGL((chunk_bwd_kernel<DK, DV, 1>), dim3((unsigned)(args.nh * (P - 1))),
+                       dim3(BTHR), 0, stream, args);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_segment_scan(args.Gloc, args.aloc, args.dST, 0, 1, args.nh, P, DK, DV, stream);
+    if (e != hipSuccess) return e;
+    args.Gin = args.Gloc;
+  }
+  hipLaunchKernelGGL((chunk_bwd_kernel<DK, DV, 0>), dim3((unsigned)(args.nh * P)), dim3(BTHR), 0,
+                     stream, args);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t bwd_kv_dispatch(const BwdArgs &args, int DK, int DV, hipStream_t stream) {
+  if (DK == 64 && DV == 64) return bwd_kv_impl<64, 64>(args, stream);
+  if (DK == 64 && DV == 128) return bwd_kv_impl<64, 128>(args, stream);
+  if (DK == 128 && DV == 64) return bwd_kv_impl<128, 64>(args, stream);
+  if (DK == 128 && DV == 128) return bwd_kv_impl<128, 128>(args, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dlog(const float *r1, const float *r2, const float *ST, const float *dST,
+                       float *dl, int64_t nh, int64_t T, int64_t per, hipStream_t stream) {
+  hipLaunchKernelGGL(dlog_kernel, dim3((unsigned)nh), dim3(256), 0, stream, r1, r2, ST, dST, dl,
+                     T, per);
+  return hipGetLastError();
+}
+
+}  // namespace chunk
+}  // namespace cla

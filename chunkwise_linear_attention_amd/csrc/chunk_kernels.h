@@ -1,0 +1,61 @@
+// Argument blocks and launchers of the chunkwise kernels, shared by the
+// forward (chunk.hip) and backward (chunk_bwd.hip) translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cla {
+namespace chunk {
+
+struct FwdArgs {
+  const uint16_t *q;       // [nh, T, DK]
+  const uint16_t *k;       // [nh, T, DK]
+  const uint16_t *v;       // [nh, T, DV]
+  const float *l;          // [nh, T]
+  const float *S0;         // [nh, DK, DV] (or [nh, DV, DK] if s0_trans); NULL = 0
+  const float *Sin;        // [P-1, nh, DK, DV] state entering segments 1..P-1
+  uint16_t *o;             // [nh, T, DV]
+  float *ST;               // [nh, DK, DV] (or transposed if st_trans); NULL = skip
+  float *Sloc;             // state-only pass: [P-1, nh, DK, DV]
+  float *aloc;             // state-only pass: [P-1, nh] total decay of the segment
+  const uint16_t *xdot;    // optional [nh, T, DV]: rdot[t] = sum_j xdot[t, j] o[t, j]
+  float *rdot;             // [nh, T]
+  int64_t nh, T, seg_chunks, P;
+  int s0_trans, st_trans;
+};
+
+struct BwdArgs {
+  const uint16_t *q, *k, *v, *dO;   // [nh, T, DK|DV]
+  const float *l;                   // [nh, T]
+  const float *dST;                 // [nh, DK, DV] or NULL
+  const float *Gin;                 // [P-1, nh, DK, DV]: G at the end of segments 0..P-2
+  uint16_t *dk, *dv;                // [nh, T, DK|DV]
+  float *r2;                        // [nh, T]  k . dk
+  float *dS0;                       // [nh, DK, DV] or NULL
+  float *Gloc;                      // state-only pass: [P-1, nh, DK, DV] (segment p in slot p-1)
+  float *aloc;                      // state-only pass: [P-1, nh]
+  int64_t nh, T, seg_chunks, P;
+};
+
+// Forward-type pass (segment state pass, segment scan, main pass).
+hipError_t fwd_dispatch(FwdArgs args, int DK, int DV, hipStream_t stream);
+
+// Reverse dK/dV pass (segment state pass, reverse segment scan, main pass).
+hipError_t bwd_kv_dispatch(const BwdArgs &args, int DK, int DV, hipStream_t stream);
+
+// Exclusive scan of per-segment pairs (alpha_p, S_p) held in slots, in place.
+// Forward (reverse = 0): slot p becomes the state entering segment p + 1,
+// starting from init.  Reverse (reverse = 1): slot p (holding segment p + 1's
+// pair) becomes the state gradient at the end of segment p, starting from
+// init at the end of the sequence.
+hipError_t launch_segment_scan(float *slots, const float *aloc, const float *init,
+                               int init_trans, int reverse, int64_t nh, int64_t P,
+                               int DK, int DV, hipStream_t stream);
+
+// dl_u = <S_T, dS_T> + sum_{t >= u} (r1_t - r2_t) per sequence.
+hipError_t launch_dlog(const float *r1, const float *r2, const float *ST, const float *dST,
+                       float *dl, int64_t nh, int64_t T, int64_t per, hipStream_t stream);
+
+}  // namespace chunk
+}  // namespace cla
