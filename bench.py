@@ -190,6 +190,131 @@ def cpu_baseline_scan(inp, B, T, D):
 
 
 # ---------------------------------------------------------------------------
+# chunkwise linear attention
+# ---------------------------------------------------------------------------
+
+
+def bench_chunk(args, torch, cla, wl, steps, warmup, cpu_heads=0):
+    from chunkwise_linear_attention_amd import _lib
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    ci = wl.make()
+    log(f"[bench] inputs for {wl.name} drawn in {time.time() - t0:.1f}s")
+    B, H, T, DK, DV = (wl.shape[x] for x in ("B", "H", "T", "DK", "DV"))
+
+    def up(x):
+        if x is None:
+            return None
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    q, k, v, l, S0, dO, dST = (up(x) for x in (ci.q, ci.k, ci.v, ci.l, ci.S0, ci.dO, ci.dST))
+    o = torch.empty_like(v)
+    ST = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dl = torch.empty_like(l)
+    dS0 = torch.empty_like(ST)
+    L = cla.lib()
+    wsf = cla.chunk_workspace_bytes(B, H, T, DK, DV, False)
+    wsb = cla.chunk_workspace_bytes(B, H, T, DK, DV, True)
+    ws = torch.empty(max(wsf, wsb, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    P = lambda t: None if t is None else t.data_ptr()
+
+    def fwd():
+        st = L.cla_chunk_fwd(P(q), P(k), P(v), P(l), P(S0), P(o), P(ST), B, H, T, DK, DV, 64,
+                             P(ws), ws.numel(), stream)
+        if st:
+            raise RuntimeError(L.cla_status_string(st))
+
+    def bwd():
+        st = L.cla_chunk_bwd(P(q), P(k), P(v), P(l), P(S0), P(dO), P(dST), P(dq), P(dk), P(dv),
+                             P(dl), P(dS0), B, H, T, DK, DV, 64, P(ws), ws.numel(), stream)
+        if st:
+            raise RuntimeError(L.cla_status_string(st))
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        fwd()
+        bwd()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / steps
+    # per-kernel durations from HIP events recorded by the library itself
+    _lib.timing_enable(True)
+    for _ in range(steps):
+        fwd()
+        bwd()
+    table = _lib.timing_read()
+    _lib.timing_enable(False)
+    units = B * H * T
+    kernels = {}
+    for name, (tot, cnt) in table.items():
+        avg = tot / cnt
+        ent = {"avg_ms": round(avg, 5), "launches_per_step": cnt // steps,
+               "share": round(tot / sum(x[0] for x in table.values()), 4)}
+        if name in ("chunk_fwd", "chunk_dq", "chunk_dkdv", "chunk_dlog"):
+            # every token-head once per launch (segment passes cover a
+            # fraction and are reported by time only)
+            per = pm.chunk_kernel_bytes(name, DK, DV)
+            ent["algorithmic_bytes_per_launch"] = per * units
+            ent["GBps"] = round(per * units / (avg * 1e-3) / 1e9, 1)
+        kernels[name] = ent
+    main = {n: e for n, e in kernels.items() if "GBps" in e and not n.endswith("_segments")}
+    dom = max(main, key=lambda n: main[n]["avg_ms"] * main[n]["launches_per_step"])
+    d = kernels[dom]
+    achieved = d["GBps"]
+    path_bytes = pm.chunk_bytes_per_token_head(DK, DV, "fwdbwd") * units
+    path_flops = pm.chunk_flops_per_token_head(64, DK, DV, "fwdbwd") * units
+    t_roof = pm.roofline_seconds(path_bytes, path_flops)
+    roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": pm.PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved / pm.PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic(dom, wl.name, "chunk.hip" if dom in ("chunk_fwd", "chunk_dq") else "chunk_bwd.hip"),
+            "avg_launch_ms": d["avg_ms"],
+            "algorithmic_bytes_per_launch": d["algorithmic_bytes_per_launch"]}
+    res = {"value": B * T / (ms_step * 1e-3), "ms_per_step": ms_step, "dtype": "bf16",
+           "config": {"workload": wl.name, "B": B, "H": H, "T": T, "DK": DK, "DV": DV,
+                      "chunk": 64, "tokens_per_step": B * T},
+           "roofline": roof,
+           "extra": {"kernels": kernels,
+                     "path_algorithmic_bytes": path_bytes, "path_algorithmic_flops": path_flops,
+                     "path_roofline_frac": round(t_roof / (ms_step * 1e-3), 4),
+                     "mfma_util": round(path_flops / (ms_step * 1e-3) / (pm.PEAK_BF16_TFLOPS * 1e12), 4),
+                     "hbm_GBps_path": round(path_bytes / (ms_step * 1e-3) / 1e9, 1),
+                     "workspace_bytes": [wsf, wsb]}}
+    res["cpu_baseline"] = cpu_baseline_chunk(ci, cpu_heads) if cpu_heads else None
+    del q, k, v, l, S0, dO, dST, o, ST, dq, dk, dv, dl, dS0, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline_chunk(ci, nheads):
+    """The C oracle (float64 loops, OpenMP over heads), forward then backward,
+    on the first `nheads` (batch, head) sequences at full length."""
+    from oracle import cref
+    cref.build()
+    B, H, T, DK = ci.q.shape
+    heads = np.arange(min(nheads, B * H), dtype=np.int64)
+    t0 = time.time()
+    cref.la_fwd(ci.q, ci.k, ci.v, ci.l, ci.S0, heads=heads)
+    cref.la_bwd(ci.q, ci.k, ci.v, ci.l, ci.S0, ci.dO, ci.dST, heads=heads)
+    secs = time.time() - t0
+    frac = len(heads) / (B * H)
+    return {"value": round(B * T * frac / secs, 1), "unit": "tokens/s",
+            "cores": cref.num_threads(), "kind": "oracle",
+            "sample": f"{len(heads)} of {B * H} (batch, head) sequences at full length "
+                      f"T={T}, forward+backward, {secs:.2f} s; tokens/s scaled by the "
+                      "head fraction"}
+
+
+CHUNK_EXTRAS = ("la_const", "la_gated") + tuple(f"la_long_T{t}" for t in syn.LONG_T)
 
 
 def main():
@@ -199,6 +324,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="scan_large", choices=sorted(syn.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--no-chunk-extras", action="store_true",
+                    help="with the scan workload, skip the chunkwise measurements")
+    ap.add_argument("--cpu-heads", type=int, default=16,
+                    help="chunkwise workloads: sequences the oracle baseline runs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (the reference "
                          "kernel for scaling rocprofv3 byte counters)")
@@ -215,8 +344,24 @@ def main():
     wl = syn.WORKLOADS[args.workload]
     if wl.kind == "scan":
         res = bench_scan(args, torch, cla, wl)
+        if not args.no_chunk_extras:
+            # the matrix-state rows of the hot path, measured in the same run
+            chunk = {}
+            for name in CHUNK_EXTRAS:
+                r = bench_chunk(args, torch, cla, syn.WORKLOADS[name], max(3, args.steps // 2), 1)
+                chunk[name] = {"tokens_per_s": round(r["value"], 1),
+                               "ms_per_step": round(r["ms_per_step"], 4),
+                               "roofline": r["roofline"],
+                               "path_roofline_frac": r["extra"]["path_roofline_frac"],
+                               "mfma_util": r["extra"]["mfma_util"],
+                               "kernels": {n: e["avg_ms"] for n, e in r["extra"]["kernels"].items()}}
+                log(f"[bench] {name}: {r['ms_per_step']:.3f} ms/step")
+            longs = [chunk[f"la_long_T{t}"]["tokens_per_s"] for t in syn.LONG_T]
+            res["extra"]["chunkwise"] = chunk
+            res["extra"]["la_long_T_flatness_min_over_max"] = round(min(longs) / max(longs), 4)
     else:
-        raise SystemExit(f"workload {wl.name}: chunkwise bench not available yet")
+        res = bench_chunk(args, torch, cla, wl, args.steps, args.warmup,
+                          cpu_heads=args.cpu_heads if args.cpu_baseline else 0)
     if args.copy_probe:
         x = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
         y = torch.empty_like(x)

@@ -45,7 +45,24 @@ SIGNATURES = {
     "cla_chunk_fwd": ([p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, p, sz, p],
                       ctypes.c_int),
     "cla_chunk_bwd": ([p] * 12 + [i64] * 6 + [p, sz, p], ctypes.c_int),
+    "cla_timing_enable": ([ctypes.c_int], ctypes.c_int),
+    "cla_timing_read": ([p, p, p, ctypes.c_int], ctypes.c_int),
 }
+
+
+def timing_enable(on: bool) -> None:
+    lib().cla_timing_enable(1 if on else 0)
+
+
+def timing_read(max_kernels: int = 32) -> dict:
+    """{kernel name: (total ms, launches)} since the last read (synchronizes)."""
+    names = (ctypes.c_char_p * max_kernels)()
+    tot = (ctypes.c_double * max_kernels)()
+    cnt = (ctypes.c_int64 * max_kernels)()
+    n = lib().cla_timing_read(names, tot, cnt, max_kernels)
+    if n < 0:
+        raise ClaError("cla_timing_read", -n, "event query failed")
+    return {names[i].decode(): (tot[i], cnt[i]) for i in range(min(n, max_kernels))}
 
 
 def header_symbols() -> list[str]:

@@ -344,7 +344,8 @@ hipError_t fwd_impl(FwdArgs args, hipStream_t stream) {
   const int64_t P = args.P;
   if (P > 1) {
     dim3 g1((unsigned)(args.nh * (P - 1)));
-    hipLaunchKernelGGL((chunk_fwd_kernel<DK, DV, 1>), g1, dim3(NTHR), 0, stream, args);
+    CLA_LAUNCH(args.xdot ? "chunk_dq_segments" : "chunk_fwd_segments",
+               (chunk_fwd_kernel<DK, DV, 1>), g1, dim3(NTHR), stream, args);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_segment_scan(args.Sloc, args.aloc, args.S0, args.s0_trans, 0, args.nh, P, DK,
@@ -353,7 +354,8 @@ hipError_t fwd_impl(FwdArgs args, hipStream_t stream) {
     args.Sin = args.Sloc;
   }
   dim3 g((unsigned)(args.nh * P));
-  hipLaunchKernelGGL((chunk_fwd_kernel<DK, DV, 0>), g, dim3(NTHR), 0, stream, args);
+  CLA_LAUNCH(args.xdot ? "chunk_dq" : "chunk_fwd", (chunk_fwd_kernel<DK, DV, 0>), g,
+             dim3(NTHR), stream, args);
   return hipGetLastError();
 }
 
@@ -363,8 +365,8 @@ hipError_t launch_segment_scan(float *slots, const float *aloc, const float *ini
                                int init_trans, int reverse, int64_t nh, int64_t P, int DK,
                                int DV, hipStream_t stream) {
   const int64_t n = nh * DK * DV;
-  hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                     stream, slots, aloc, init, init_trans, reverse, nh, P, DK, DV);
+  CLA_LAUNCH("chunk_segment_scan", segment_scan_kernel, dim3((unsigned)((n + 255) / 256)),
+             dim3(256), stream, slots, aloc, init, init_trans, reverse, nh, P, DK, DV);
   return hipGetLastError();
 }
 

@@ -475,16 +475,16 @@ template <int DK, int DV>
 hipError_t bwd_kv_impl(BwdArgs args, hipStream_t stream) {
   const int64_t P = args.P;
   if (P > 1) {
-    hipLaunchKernelGGL((chunk_bwd_kernel<DK, DV, 1>), dim3((unsigned)(args.nh * (P - 1))),
-                       dim3(BTHR), 0, stream, args);
+    CLA_LAUNCH("chunk_dkdv_segments", (chunk_bwd_kernel<DK, DV, 1>),
+               dim3((unsigned)(args.nh * (P - 1))), dim3(BTHR), stream, args);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_segment_scan(args.Gloc, args.aloc, args.dST, 0, 1, args.nh, P, DK, DV, stream);
     if (e != hipSuccess) return e;
     args.Gin = args.Gloc;
   }
-  hipLaunchKernelGGL((chunk_bwd_kernel<DK, DV, 0>), dim3((unsigned)(args.nh * P)), dim3(BTHR), 0,
-                     stream, args);
+  CLA_LAUNCH("chunk_dkdv", (chunk_bwd_kernel<DK, DV, 0>), dim3((unsigned)(args.nh * P)),
+             dim3(BTHR), stream, args);
   return hipGetLastError();
 }
 
@@ -500,8 +500,8 @@ hipError_t bwd_kv_dispatch(const BwdArgs &args, int DK, int DV, hipStream_t stre
 
 hipError_t launch_dlog(const float *r1, const float *r2, const float *ST, const float *dST,
                        float *dl, int64_t nh, int64_t T, int64_t per, hipStream_t stream) {
-  hipLaunchKernelGGL(dlog_kernel, dim3((unsigned)nh), dim3(256), 0, stream, r1, r2, ST, dST, dl,
-                     T, per);
+  CLA_LAUNCH("chunk_dlog", dlog_kernel, dim3((unsigned)nh), dim3(256), stream, r1, r2, ST, dST,
+             dl, T, per);
   return hipGetLastError();
 }
 

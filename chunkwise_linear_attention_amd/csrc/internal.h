@@ -8,6 +8,20 @@
 
 namespace cla {
 
+// Kernel timing hooks (no-ops unless cla_timing_enable(1) was called).
+namespace timing {
+void before(hipStream_t stream);
+void after(hipStream_t stream, const char *name);
+}  // namespace timing
+
+// Launch a kernel between the timing hooks.
+#define CLA_LAUNCH(name, kernel, grid, block, stream, ...)                       \
+  do {                                                                           \
+    ::cla::timing::before(stream);                                               \
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, __VA_ARGS__);             \
+    ::cla::timing::after(stream, name);                                          \
+  } while (0)
+
 // ---------------------------------------------------------------------------
 // diagonal scan
 // ---------------------------------------------------------------------------

@@ -369,14 +369,14 @@ hipError_t run(ScanArgs args, const ScanPlan &plan, hipStream_t stream) {
   const int64_t groups = args.B * args.groups_per_batch;
   if (plan.P > 1) {
     dim3 grid((unsigned)groups, (unsigned)(plan.P - 1));
-    hipLaunchKernelGGL((scan_kernel<VEC, DIR, true, kNW, kK>), grid, dim3(kNW * 64), 0,
-                       stream, args);
+    CLA_LAUNCH(DIR == 0 ? "scan_fwd_segments" : "scan_bwd_segments",
+               (scan_kernel<VEC, DIR, true, kNW, kK>), grid, dim3(kNW * 64), stream, args);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   dim3 grid((unsigned)groups, (unsigned)plan.P);
-  hipLaunchKernelGGL((scan_kernel<VEC, DIR, false, kNW, kK>), grid, dim3(kNW * 64), 0,
-                     stream, args);
+  CLA_LAUNCH(DIR == 0 ? "scan_fwd" : "scan_bwd", (scan_kernel<VEC, DIR, false, kNW, kK>),
+             grid, dim3(kNW * 64), stream, args);
   return hipGetLastError();
 }
 
@@ -453,8 +453,8 @@ hipError_t launch_copy_or_zero(float *dst, const float *src, int64_t n,
   if (n <= 0) return hipSuccess;
   const int threads = 256;
   const int64_t blocks = (n + threads - 1) / threads;
-  hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)blocks), dim3(threads),
-                     0, stream, dst, src, n);
+  CLA_LAUNCH("copy_or_zero", copy_or_zero_kernel, dim3((unsigned)blocks), dim3(threads),
+             stream, dst, src, n);
   return hipGetLastError();
 }
 

@@ -164,6 +164,26 @@ int cla_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                   void *workspace, size_t workspace_bytes,
                   cla_stream_t stream);
 
+/* ------------------------------------------------------------------------ */
+/* Kernel timing (benchmark instrumentation)                                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * enable != 0: from now on every kernel the library launches is bracketed by
+ * two HIP events on its stream (a few microseconds of overhead per launch).
+ * enable == 0: stop recording.  Returns CLA_OK.
+ */
+int cla_timing_enable(int enable);
+
+/*
+ * Waits for every recorded launch, then reports per kernel name the total
+ * milliseconds and the number of launches since the last read, and clears the
+ * records.  names[k] point to static strings.  Fills at most `max` entries
+ * (any array may be NULL) and returns the number of distinct kernels, or
+ * -CLA_ERR_HIP if an event query failed.
+ */
+int cla_timing_read(const char **names, double *total_ms, int64_t *counts, int max);
+
 #ifdef __cplusplus
 }
 #endif
