@@ -42,6 +42,14 @@ namespace {
 
 constexpr int64_t kTargetWG = 512;   // 2 workgroups per CU on 256 CUs
 constexpr int64_t kMinSegChunks = 4;
+// The backward's decay gradient sums q.dq - k.dk backwards only inside one
+// segment, starting from the exact boundary term <S, G> of the two segment
+// states.  Inter-chunk paths reach q.dq through the bf16-rounded state S and
+// k.dk through the bf16-rounded gradient G, so the two sums do not cancel
+// exactly and their difference gathers rounding noise that grows with the
+// summed length; backward segments therefore hold at most 16 chunks (1024
+// tokens).
+constexpr int64_t kMaxBwdSegChunks = 16;
 
 // MODE 0: outputs (o, S_T, rdot).  MODE 1: segment state only (Sloc, aloc).
 template <int DK, int DV, int MODE>
@@ -398,10 +406,12 @@ FwdWs fwd_ws(void *base, int64_t nh, int64_t P, int64_t DK, int64_t DV) {
   return w;
 }
 
-// backward workspace: the forward-type segment area (reused by the reverse
-// pass), q . dq and k . dk per token, and the final state for <S_T, dS_T>
+// backward workspace: the segment states of the dQ pass (S^T at segment
+// ends) and of the reverse pass (G at segment ends), q . dq and k . dk per
+// token, and the final state for <S_T, dS_T>
 struct BwdWs {
-  FwdWs seg;
+  FwdWs seg;   // dQ pass: slots p = S^T at the end of segment p
+  FwdWs gseg;  // reverse pass: slots p = G at the end of segment p
   float *r1, *r2, *ST;
   size_t bytes;
 };
@@ -410,6 +420,8 @@ BwdWs bwd_ws(void *base, int64_t nh, int64_t T, int64_t P, int64_t DK, int64_t D
   BwdWs w{};
   w.seg = fwd_ws(base, nh, P, DK, DV);
   size_t off = w.seg.bytes;
+  w.gseg = fwd_ws(base ? static_cast<char *>(base) + off : nullptr, nh, P, DK, DV);
+  off += w.gseg.bytes;
   auto carve = [&](size_t bytes) -> float * {
     float *p = base ? reinterpret_cast<float *>(static_cast<char *>(base) + off) : nullptr;
     off += (bytes + 255) & ~(size_t)255;
@@ -443,7 +455,14 @@ ChunkPlan plan_chunk(int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV) {
   plan.P = P;
   plan.seg_chunks = segc;
   plan.ws_fwd = chunk::fwd_ws(nullptr, nh, P, DK, DV).bytes;
-  plan.ws_bwd = chunk::bwd_ws(nullptr, nh, T, P, DK, DV).bytes;
+  int64_t Pb = P;
+  const int64_t minPb = (nchunks + chunk::kMaxBwdSegChunks - 1) / chunk::kMaxBwdSegChunks;
+  if (Pb < minPb) Pb = minPb;
+  const int64_t segb = (nchunks + Pb - 1) / Pb;
+  Pb = (nchunks + segb - 1) / segb;
+  plan.P_b = Pb;
+  plan.seg_chunks_b = segb;
+  plan.ws_bwd = chunk::bwd_ws(nullptr, nh, T, Pb, DK, DV).bytes;
   return plan;
 }
 
@@ -476,7 +495,7 @@ hipError_t launch_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t
                             int64_t DK, int64_t DV, const ChunkPlan &plan, void *ws,
                             hipStream_t stream) {
   const int64_t nh = B * H;
-  const chunk::BwdWs w = chunk::bwd_ws(ws, nh, T, plan.P, DK, DV);
+  const chunk::BwdWs w = chunk::bwd_ws(ws, nh, T, plan.P_b, DK, DV);
   // dQ pass (forward chunk order): the forward recurrence on the transposed
   // state S^T with keys v and values k, read by dO:
   //   dQ_[j] = (dO V^T (.) D) K + diag(lambda) dO S_[j-1]^T   (LA2 Eq. 15)
@@ -497,8 +516,8 @@ hipError_t launch_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t
   fa.aloc = w.seg.aloc;
   fa.nh = nh;
   fa.T = T;
-  fa.seg_chunks = plan.seg_chunks;
-  fa.P = plan.P;
+  fa.seg_chunks = plan.seg_chunks_b;
+  fa.P = plan.P_b;
   hipError_t e = chunk::fwd_dispatch(fa, (int)DV, (int)DK, stream);
   if (e != hipSuccess) return e;
   // dK/dV pass (reverse chunk order)
@@ -513,15 +532,16 @@ hipError_t launch_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t
   ba.dv = dv;
   ba.r2 = w.r2;
   ba.dS0 = dS0;
-  ba.Gloc = w.seg.Sloc;
-  ba.aloc = w.seg.aloc;
+  ba.Gloc = w.gseg.Sloc;
+  ba.aloc = w.gseg.aloc;
   ba.nh = nh;
   ba.T = T;
-  ba.seg_chunks = plan.seg_chunks;
-  ba.P = plan.P;
+  ba.seg_chunks = plan.seg_chunks_b;
+  ba.P = plan.P_b;
   e = chunk::bwd_kv_dispatch(ba, (int)DK, (int)DV, stream);
   if (e != hipSuccess) return e;
-  return chunk::launch_dlog(w.r1, w.r2, dST ? w.ST : nullptr, dST, dl, nh, T, DK * DV, stream);
+  return chunk::launch_dlog(w.r1, w.r2, dST ? w.ST : nullptr, dST, w.seg.Sloc, w.gseg.Sloc, dl,
+                            nh, T, DK, DV, plan.seg_chunks_b * chunk::TC, plan.P_b, stream);
 }
 
 }  // namespace cla

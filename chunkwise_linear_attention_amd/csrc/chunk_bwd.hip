@@ -428,46 +428,71 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
 #undef G0
 #undef G1
 
-// dl_u = sdot + sum_{t >= u} (r1_t - r2_t), sdot = <S_T, dS_T> (0 if no dS_T).
-// One workgroup per sequence; fp64 accumulation.
-__global__ __launch_bounds__(256) void dlog_kernel(const float *r1, const float *r2,
-                                                   const float *ST, const float *dST,
-                                                   float *dl, int64_t T, int64_t per) {
-  __shared__ double red[256];
-  const int64_t bh = blockIdx.x;
+// Decay gradient of one segment of one sequence (one workgroup each):
+//   dl_u = B + sum_{t >= u, t in segment} (r1_t - r2_t),
+// B = the sum over all paths that cross the segment's end, i.e. <S, G> at
+// that boundary, computed exactly from the two stored fp32 states.  fp64
+// accumulation throughout.
+constexpr int DL_THR = 256;
+constexpr int DL_PER = 16;  // tokens per thread; segments hold <= 4096 tokens
+
+__global__ __launch_bounds__(DL_THR) void dlog_kernel(const float *r1, const float *r2,
+                                                      const float *ST, const float *dST,
+                                                      const float *Sseg, const float *Gseg,
+                                                      float *dl, int64_t nh, int64_t T, int DK,
+                                                      int DV, int64_t seg_len, int64_t P) {
+  __shared__ double red[DL_THR];
+  const int64_t bh = blockIdx.x % nh;
+  const int64_t seg = blockIdx.x / nh;
   const int tid = threadIdx.x;
+  const int64_t per = (int64_t)DK * DV;
   double sd = 0.0;
-  if (ST && dST) {
-    for (int64_t e = tid; e < per; e += 256)
-      sd += (double)ST[bh * per + e] * (double)dST[bh * per + e];
+  if (seg == P - 1) {
+    if (ST && dST)
+      for (int64_t e = tid; e < per; e += DL_THR)
+        sd += (double)ST[bh * per + e] * (double)dST[bh * per + e];
+  } else {
+    // Sseg holds S^T ([DV][DK]); Gseg holds G ([DK][DV])
+    const float *S = Sseg + (seg * nh + bh) * per;
+    const float *G = Gseg + (seg * nh + bh) * per;
+    for (int64_t e = tid; e < per; e += DL_THR) {
+      const int64_t d = e / DV, j = e % DV;
+      sd += (double)S[j * DK + d] * (double)G[e];
+    }
   }
   red[tid] = sd;
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
+  for (int o = DL_THR / 2; o > 0; o >>= 1) {
     if (tid < o) red[tid] += red[tid + o];
     __syncthreads();
   }
-  const double sdot = red[0];
+  const double B = red[0];
   __syncthreads();
-  const int64_t L = (T + 255) / 256;
-  const int64_t lo = min<int64_t>(T, tid * L), hi = min<int64_t>(T, lo + L);
+  const int64_t s0 = seg * seg_len, s1 = min(T, s0 + seg_len);
+  const int64_t lo = min(s1, s0 + (int64_t)tid * DL_PER), hi = min(s1, lo + DL_PER);
   const float *x1 = r1 + bh * T, *x2 = r2 + bh * T;
+  double x[DL_PER];
   double local = 0.0;
-  for (int64_t t = lo; t < hi; ++t) local += (double)x1[t] - (double)x2[t];
+#pragma unroll
+  for (int i = 0; i < DL_PER; ++i) {
+    x[i] = (lo + i < hi) ? (double)x1[lo + i] - (double)x2[lo + i] : 0.0;
+    local += x[i];
+  }
   red[tid] = local;
   __syncthreads();
-  // suffix sums over threads (Hillis-Steele, from the right)
-  for (int o = 1; o < 256; o <<= 1) {
-    const double add = (tid + o < 256) ? red[tid + o] : 0.0;
+  // suffix sums over threads (Hillis-Steele from the right)
+  for (int o = 1; o < DL_THR; o <<= 1) {
+    const double add = (tid + o < DL_THR) ? red[tid + o] : 0.0;
     __syncthreads();
     red[tid] += add;
     __syncthreads();
   }
-  double acc = sdot + (tid + 1 < 256 ? red[tid + 1] : 0.0);
+  double acc = B + (tid + 1 < DL_THR ? red[tid + 1] : 0.0);
   float *out = dl + bh * T;
-  for (int64_t t = hi - 1; t >= lo; --t) {
-    acc += (double)x1[t] - (double)x2[t];
-    out[t] = (float)acc;
+#pragma unroll
+  for (int i = DL_PER - 1; i >= 0; --i) {
+    acc += x[i];
+    if (lo + i < hi) out[lo + i] = (float)acc;
   }
 }
 
@@ -499,9 +524,11 @@ hipError_t bwd_kv_dispatch(const BwdArgs &args, int DK, int DV, hipStream_t stre
 }
 
 hipError_t launch_dlog(const float *r1, const float *r2, const float *ST, const float *dST,
-                       float *dl, int64_t nh, int64_t T, int64_t per, hipStream_t stream) {
-  CLA_LAUNCH("chunk_dlog", dlog_kernel, dim3((unsigned)nh), dim3(256), stream, r1, r2, ST, dST,
-             dl, T, per);
+                       const float *Sseg, const float *Gseg, float *dl, int64_t nh, int64_t T,
+                       int DK, int DV, int64_t seg_len, int64_t P, hipStream_t stream) {
+  if (seg_len > (int64_t)DL_THR * DL_PER) return hipErrorInvalidValue;
+  CLA_LAUNCH("chunk_dlog", dlog_kernel, dim3((unsigned)(nh * P)), dim3(DL_THR), stream, r1, r2,
+             ST, dST, Sseg, Gseg, dl, nh, T, DK, DV, seg_len, P);
   return hipGetLastError();
 }
 

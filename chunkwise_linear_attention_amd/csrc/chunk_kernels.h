@@ -53,9 +53,13 @@ hipError_t launch_segment_scan(float *slots, const float *aloc, const float *ini
                                int init_trans, int reverse, int64_t nh, int64_t P,
                                int DK, int DV, hipStream_t stream);
 
-// dl_u = <S_T, dS_T> + sum_{t >= u} (r1_t - r2_t) per sequence.
+// dl_u for u in segment p = B_p + sum_{t >= u, t in segment p} (r1_t - r2_t),
+// with the boundary term B_p = <S, G> at the end of segment p: <S_T, dS_T>
+// (0 without dS_T) for the last segment, <Sseg[p]^T, Gseg[p]> otherwise
+// (Sseg holds S^T, Gseg holds G, both [P-1, nh, DK*DV]).
 hipError_t launch_dlog(const float *r1, const float *r2, const float *ST, const float *dST,
-                       float *dl, int64_t nh, int64_t T, int64_t per, hipStream_t stream);
+                       const float *Sseg, const float *Gseg, float *dl, int64_t nh, int64_t T,
+                       int DK, int DV, int64_t seg_len, int64_t P, hipStream_t stream);
 
 }  // namespace chunk
 }  // namespace cla

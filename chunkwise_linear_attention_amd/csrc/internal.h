@@ -58,10 +58,12 @@ hipError_t launch_copy_or_zero(float *dst, const float *src, int64_t n,
 // ---------------------------------------------------------------------------
 
 struct ChunkPlan {
-  int64_t P = 1;          // segments along time per (batch, head)
-  int64_t seg_chunks = 0; // chunks per segment
-  size_t ws_fwd = 0;      // workspace bytes, forward
-  size_t ws_bwd = 0;      // workspace bytes, backward
+  int64_t P = 1;            // forward: segments along time per (batch, head)
+  int64_t seg_chunks = 0;   // forward: chunks per segment
+  int64_t P_b = 1;          // backward: segments (at most kMaxBwdSegChunks each)
+  int64_t seg_chunks_b = 0; // backward: chunks per segment
+  size_t ws_fwd = 0;        // workspace bytes, forward
+  size_t ws_bwd = 0;        // workspace bytes, backward
 };
 
 ChunkPlan plan_chunk(int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV);
