@@ -40,7 +40,7 @@ namespace cla {
 namespace chunk {
 namespace {
 
-constexpr int64_t kTargetWG = 512;   // 2 workgroups per CU on 256 CUs
+constexpr int64_t kTargetWG = 512;   // two workgroups per CU on 256 CUs
 constexpr int64_t kMinSegChunks = 4;
 // The backward's decay gradient sums q.dq - k.dk backwards only inside one
 // segment, starting from the exact boundary term <S, G> of the two segment
@@ -52,26 +52,27 @@ constexpr int64_t kMinSegChunks = 4;
 constexpr int64_t kMaxBwdSegChunks = 16;
 
 // MODE 0: outputs (o, S_T, rdot).  MODE 1: segment state only (Sloc, aloc).
+// Four waves; wave w owns value columns [w DV/4, (w+1) DV/4).
 template <int DK, int DV, int MODE>
 __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   constexpr int NJ = DV / 64;          // 16-column tiles per wave
   constexpr int NDT = DK / 16;         // 16-row tiles of the state
-  constexpr int QKB = 64 * DK * 2;     // bytes of a row-major [64 x DK] tile
-  constexpr int TB_K = DK * 128;       // bytes of a transposed [DK x 64] tile
-  constexpr int TB_V = DV * 128;
+  constexpr int NCK = DK / 8, NCV = DV / 8;  // 16-byte chunks per row
+  constexpr int QB = 64 * DK * 2, VB = 64 * DV * 2;
   constexpr int OFF_QS = 0;
-  constexpr int OFF_KS = OFF_QS + (MODE == 0 ? QKB : 0);
-  constexpr int OFF_KT = OFF_KS + (MODE == 0 ? QKB : 0);
-  constexpr int OFF_VT = OFF_KT + TB_K;
-  constexpr int OFF_PS = OFF_VT + TB_V;
+  constexpr int OFF_KS = OFF_QS + (MODE == 0 ? QB : 0);
+  constexpr int OFF_VS = OFF_KS + QB;
+  constexpr int OFF_PS = OFF_VS + VB;
   constexpr int OFF_C = OFF_PS + (MODE == 0 ? 64 * 128 : 0);
   constexpr int OFF_RD = OFF_C + 3 * 64 * 4 + 16;
   constexpr int SMEM = OFF_RD + (MODE == 0 ? NWAVE * 64 * 4 : 0);
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  // 1 KB DMA blocks per chunk: [Q (MODE 0) | K | V]
+  constexpr int NBQ = MODE == 0 ? DK / 8 : 0, NBK = DK / 8, NBV = DV / 8;
+  constexpr int NBLK = NBQ + NBK + NBV;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
   unsigned char *QS = smem + OFF_QS;
   unsigned char *KS = smem + OFF_KS;
-  unsigned char *KT = smem + OFF_KT;
-  unsigned char *VT = smem + OFF_VT;
+  unsigned char *VS = smem + OFF_VS;
   unsigned char *PS = smem + OFF_PS;
   float *CS = reinterpret_cast<float *>(smem + OFF_C);
   float *LAM = CS + 64;
@@ -124,25 +125,34 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     const int64_t t0 = ci * TC;
     const int n = (int)min<int64_t>(TC, T - t0);
 
-    TileRegs<DK> kr;
-    TileRegs<DV> vr;
-    TileRegs<DK> qr;
-    tile_load<DK>(kh + t0 * DK, n, tid, kr);
-    tile_load<DV>(vh + t0 * DV, n, tid, vr);
-    if (MODE == 0) tile_load<DK>(qh + t0 * DK, n, tid, qr);
-    float lv = 0.f;
-    if (w == 0 && lane < n) lv = lh[t0 + lane];
-
     __syncthreads();  // the previous chunk's LDS reads are done
-    tile_store_cols<DK>(KT, tid, kr);
-    tile_store_cols<DV>(VT, tid, vr);
-    if (MODE == 0) {
-      tile_store_rows<DK>(KS, tid, kr);
-      tile_store_rows<DK>(QS, tid, qr);
+    // stage Q, K, V straight into LDS
+    for (int b = w; b < NBLK; b += NWAVE) {
+      if (b < NBQ) {
+        dma_block<DK>(qh + t0 * DK, n, QS, b, lane);
+      } else if (b < NBQ + NBK) {
+        dma_block<DK>(kh + t0 * DK, n, KS, b - NBQ, lane);
+      } else {
+        dma_block<DV>(vh + t0 * DV, n, VS, b - NBQ - NBK, lane);
+      }
     }
+    bf16x4 xv[4][NJ];  // the xdot values this lane multiplies
+    if (MODE == 0 && a.xdot) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int row = min(16 * rt + li, n - 1);
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt)
+          xv[rt][jt] = *reinterpret_cast<const bf16x4 *>(a.xdot + (bh * T + t0 + row) * DV + j0 +
+                                                          16 * jt + 4 * lg);
+      }
+    }
+    float lv = 0.f;
+    if (w == 0) lv = lh[t0 + min(lane, n - 1)];
+    __builtin_amdgcn_s_waitcnt(0);
     if (w == 0) {
-      // inclusive in-chunk cumulative log (rows >= n add 0)
-      float c = lv;
+      // c, lambda, gamma (zero for rows past the chunk: they write nothing), alpha
+      float c = lane < n ? lv : 0.f;
 #pragma unroll
       for (int sh = 1; sh < 64; sh <<= 1) {
         const float p = __shfl_up(c, sh, 64);
@@ -151,84 +161,73 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
       const float cl = __shfl(c, 63, 64);
       CS[lane] = c;
       LAM[lane] = expf(c);
-      GAM[lane] = expf(cl - c);
+      GAM[lane] = lane < n ? expf(cl - c) : 0.f;
       if (lane == 0) ALPHA[0] = expf(cl);
     }
     __syncthreads();
 
     if constexpr (MODE == 0) {
-      // ---- scores: P[r][s] for r in [16w, 16w+16), transposed tiles ----
-      const int r = 16 * w + li;
-      const float cr = CS[r];
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
+      // ---- masked transposed score tiles -> P[r][s] (bf16) ----
+      for (int t = w; t < 12; t += NWAVE) {
+        const int rt = tile_rt(t), st = tile_st(t);
+        const int r = 16 * rt + li;
         f32x4 acc = zero4();
-        if (st <= w) {
+        if (st <= rt) {
 #pragma unroll
-          for (int kk = 0; kk < DK / 32; ++kk) {
-            const bf16x8 ka = lds_frag<DK / 8>(KS, 16 * st + li, 4 * kk + lg);
-            const bf16x8 qb = lds_frag<DK / 8>(QS, r, 4 * kk + lg);
-            acc = mfma(ka, qb, acc);
-          }
+          for (int kk = 0; kk < DK / 32; ++kk)
+            acc = mfma(lds_frag<NCK>(KS, 16 * st + li, 4 * kk + lg),
+                       lds_frag<NCK>(QS, r, 4 * kk + lg), acc);
         }
-        // acc[i] = (K Q^T)[s = 16 st + 4 lg + i][r]
+        // acc[i] = (K Q^T)[s = 16 st + 4 lg + i][r]; keys past the chunk are masked
+        const float cr = CS[r];
         bf16x4 pv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = 16 * st + 4 * lg + i;
           float p = 0.f;
-          if (s <= r) p = acc[i] * __expf(cr - CS[s]);
+          if (s <= r && s < n) p = acc[i] * __expf(cr - CS[s]);
           pv[i] = tobf(p);
         }
         *reinterpret_cast<bf16x4 *>(PS + swz_off<8>(r, 2 * st + (lg >> 1)) + (lg & 1) * 8) = pv;
       }
       __syncthreads();
 
-      // ---- output: O^T for this wave's value columns, all 64 rows ----
-      bf16x8 vfrag[NJ][2];
+      // ---- output: O^T[j][r] = lambda_r (S^T Q^T)[j][r] + (V^T P^T)[j][r] ----
+      bf16x8 vfrag[NJ][2];  // A operands V^T: row j, k = s
 #pragma unroll
       for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          vfrag[jt][kb] = lds_frag<8>(VT, j0 + 16 * jt + li, 4 * kb + lg);
-      // the state slice as bf16 A operands: rows j, k-set
+        for (int kb = 0; kb < 2; ++kb) vfrag[jt][kb] = tr_frag<NCV>(VS, 32 * kb, j0 + 16 * jt, li, lg);
+      // the state slice as bf16 A operands: row j, k-set
       // {32kk + 4lg + 0..3, 32kk + 16 + 4lg + 0..3}
       bf16x8 sfrag[DK / 32][NJ];
 #pragma unroll
       for (int kk = 0; kk < DK / 32; ++kk)
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt) sfrag[kk][jt] = cvt8(S_acc[2 * kk][jt], S_acc[2 * kk + 1][jt]);
-
-      float rd_part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const int rr = 16 * rt + li;
         const float lam = LAM[rr];
-        // (lambda Q)^T B operands for the same k permutation
-        bf16x8 qfrag[DK / 32];
+        bf16x8 qfrag[DK / 32];  // Q^T B operands, same k permutation
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) {
-          const bf16x4 lo = lds_half<DK / 8>(QS, rr, 32 * kk + 4 * lg);
-          const bf16x4 hi = lds_half<DK / 8>(QS, rr, 32 * kk + 16 + 4 * lg);
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[e] = tof(lo[e]) * lam;
-            x[e + 4] = tof(hi[e]) * lam;
-          }
-          qfrag[kk] = cvt8(x);
-        }
+        for (int kk = 0; kk < DK / 32; ++kk)
+          qfrag[kk] = cat8(lds_half<NCK>(QS, rr, 32 * kk + 4 * lg),
+                           lds_half<NCK>(QS, rr, 32 * kk + 16 + 4 * lg));
         bf16x8 pfrag[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) pfrag[kb] = lds_frag<8>(PS, rr, 4 * kb + lg);
+        float rdp = 0.f;
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt) {
           f32x4 acc = zero4();
 #pragma unroll
+          for (int kk = 0; kk < DK / 32; ++kk) acc = mfma(sfrag[kk][jt], qfrag[kk], acc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] *= lam;
+#pragma unroll
           for (int kb = 0; kb < 2; ++kb)
             if (kb <= (rt >> 1)) acc = mfma(vfrag[jt][kb], pfrag[kb], acc);
-#pragma unroll
-          for (int kk = 0; kk < DK / 32; ++kk) acc = mfma(sfrag[kk][jt], qfrag[kk], acc);
           // acc[i] = O[row rr][col j0 + 16 jt + 4 lg + i]
           if (rr < n) {
             const int jc = j0 + 16 * jt + 4 * lg;
@@ -237,32 +236,29 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
             for (int i = 0; i < 4; ++i) ov[i] = tobf(acc[i]);
             *reinterpret_cast<bf16x4 *>(a.o + (bh * T + t0 + rr) * DV + jc) = ov;
             if (a.xdot) {
-              const bf16x4 xv =
-                  *reinterpret_cast<const bf16x4 *>(a.xdot + (bh * T + t0 + rr) * DV + jc);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) rd_part[rt] += tof(xv[i]) * acc[i];
+              for (int i = 0; i < 4; ++i) rdp += tof(xv[rt][jt][i]) * acc[i];
             }
           }
         }
+        if (a.xdot) {
+          rdp += __shfl_xor(rdp, 16, 64);
+          rdp += __shfl_xor(rdp, 32, 64);
+          if (lg == 0) RD[w * 64 + rr] = rdp;
+        }
       }
       if (a.xdot) {
-        // reduce over the 4 lane groups, then over the 4 waves through LDS
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          float x = rd_part[rt];
-          x += __shfl_xor(x, 16, 64);
-          x += __shfl_xor(x, 32, 64);
-          if (lg == 0) RD[w * 64 + 16 * rt + li] = x;
-        }
         __syncthreads();
-        if (tid < 64 && tid < n) {
-          const float s = RD[tid] + RD[64 + tid] + RD[128 + tid] + RD[192 + tid];
+        if (tid < n) {
+          float s = 0.f;
+#pragma unroll
+          for (int u = 0; u < NWAVE; ++u) s += RD[u * 64 + tid];
           a.rdot[bh * T + t0 + tid] = s;
         }
       }
     }
 
-    // ---- state update: S <- alpha S + (gamma K)^T V ----
+    // ---- state update: S <- alpha S + K^T (gamma V) ----
     const float alpha = ALPHA[0];
     alpha_total *= alpha;
 #pragma unroll
@@ -271,27 +267,25 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
       for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) S_acc[dt][jt][i] *= alpha;
-    bf16x8 vb[NJ][2];
 #pragma unroll
-    for (int jt = 0; jt < NJ; ++jt)
+    for (int kb = 0; kb < 2; ++kb) {
+      float gam[8];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) vb[jt][kb] = lds_frag<8>(VT, j0 + 16 * jt + li, 4 * kb + lg);
-    float gam[2][8];
+      for (int e = 0; e < 8; ++e) gam[e] = GAM[32 * kb + 8 * lg + e];
+      bf16x8 vb[NJ];  // (gamma V) B operands: k = s, column j
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int jt = 0; jt < NJ; ++jt) {
+        const bf16x8 x = tr_frag<NCV>(VS, 32 * kb, j0 + 16 * jt, li, lg);
+        float y[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gam[kb][e] = GAM[32 * kb + 8 * lg + e];
+        for (int e = 0; e < 8; ++e) y[e] = tof(x[e]) * gam[e];
+        vb[jt] = cvt8(y);
+      }
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16x8 ka = tr_frag<NCK>(KS, 32 * kb, 16 * dt, li, lg);  // K^T: row d, k = s
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kt = lds_frag<8>(KT, 16 * dt + li, 4 * kb + lg);
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = tof(kt[e]) * gam[kb][e];
-        const bf16x8 ka = cvt8(x);
-#pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) S_acc[dt][jt] = mfma(ka, vb[jt][kb], S_acc[dt][jt]);
+        for (int jt = 0; jt < NJ; ++jt) S_acc[dt][jt] = mfma(ka, vb[jt], S_acc[dt][jt]);
       }
     }
   }

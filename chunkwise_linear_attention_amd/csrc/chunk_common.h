@@ -139,5 +139,144 @@ __device__ __forceinline__ void tile_store_cols(unsigned char *dst, int tid, con
   }
 }
 
+// ---------------------------------------------------------------------------
+// Item-level staging: an item is 4 token rows x 8 columns (four 16-byte
+// pieces) of a [64 x D] chunk; item ids 0 .. 2D-1, token quad sq = id % 16
+// (tokens 4sq .. 4sq+3), column chunk dc = id / 16 (columns 8dc .. 8dc+7).
+// Consecutive ids of one wave cover 16 token quads x 4 column chunks.
+// ---------------------------------------------------------------------------
+
+// Loads are unconditional (rows past the chunk's n tokens re-read row n-1,
+// which exists because n >= 1) so that no load waits on another; the stores
+// zero those rows.
+template <int D>
+__device__ __forceinline__ void item_load(const uint16_t *src, int n, int id, uint4 (&r)[4]) {
+  const int sq = id & 15, dc = id >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = min(4 * sq + i, n - 1);
+    r[i] = *reinterpret_cast<const uint4 *>(src + (int64_t)row * D + dc * 8);
+  }
+}
+
+// Same with a run-time row stride D (elements); columns 8 dc .. 8 dc + 7.
+__device__ __forceinline__ void item_load_rt(const uint16_t *src, int D, int n, int id,
+                                             uint4 (&r)[4]) {
+  const int sq = id & 15, dc = id >> 4;
+  const uint16_t *p = src + dc * 8;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = min(4 * sq + i, n - 1);
+    r[i] = *reinterpret_cast<const uint4 *>(p + (int64_t)row * D);
+  }
+}
+
+__device__ __forceinline__ void zero_tail(int sq, int n, uint4 (&r)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (4 * sq + i >= n) r[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+template <int D>
+__device__ __forceinline__ void item_store_rows(unsigned char *dst, int id, int n, uint4 (&r)[4]) {
+  const int sq = id & 15, dc = id >> 4;
+  zero_tail(sq, n, r);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<uint4 *>(dst + swz_off<D / 8>(4 * sq + i, dc)) = r[i];
+}
+
+template <int D>
+__device__ __forceinline__ void item_store_cols(unsigned char *dst, int id, int n, uint4 (&r)[4]) {
+  const int sq = id & 15, dc = id >> 4;
+  zero_tail(sq, n, r);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int d = 8 * dc + e;
+    const uint32_t lo = bf16_at(r[0], e) | (bf16_at(r[1], e) << 16);
+    const uint32_t hi = bf16_at(r[2], e) | (bf16_at(r[3], e) << 16);
+    *reinterpret_cast<uint2 *>(dst + swz_off<8>(d, sq >> 1) + (sq & 1) * 8) = make_uint2(lo, hi);
+  }
+}
+
+// The lower-triangular 16 x 16 score tiles (row tile rt >= column tile st) of
+// a 64 x 64 chunk, then the two strictly-upper tiles that the k-blocks of 32
+// read and that must hold zeros: (0, 1) and (2, 3).  Wave w of NW handles
+// tiles w, w + NW, ...
+// (Packed 2 bits per tile in an immediate, so that no table is read from
+// memory.)  rt: 0,1,1,2,2,2,3,3,3,3,0,2   st: 0,0,1,0,1,2,0,1,2,3,1,3
+__device__ __forceinline__ int tile_rt(int t) { return (0x8FFA94u >> (2 * t)) & 3; }
+__device__ __forceinline__ int tile_st(int t) { return (0xDE4910u >> (2 * t)) & 3; }
+
+// In-chunk cumulative log decay and the three decays, by one wave:
+// c_r = l_1 + .. + l_r (rows past the chunk add 0), lambda_r = exp(c_r),
+// gamma_r = exp(c_63 - c_r), alpha = exp(c_63).
+__device__ __forceinline__ void chunk_decays(float lv, int lane, float *CS, float *LAM,
+                                             float *GAM, float *ALPHA) {
+  float c = lv;
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) {
+    const float p = __shfl_up(c, sh, 64);
+    if (lane >= sh) c += p;
+  }
+  const float cl = __shfl(c, 63, 64);
+  CS[lane] = c;
+  LAM[lane] = expf(c);
+  GAM[lane] = expf(cl - c);
+  if (lane == 0) ALPHA[0] = expf(cl);
+}
+
+// ---------------------------------------------------------------------------
+// Asynchronous staging: global -> LDS copies that bypass registers
+// (global_load_lds, 16 bytes per lane; lane i of a wave writes bytes
+// 16 i .. 16 i + 15 of a 1 KB LDS block).  Block b of a row-major swizzled
+// [64 x D] tile holds rows RPB b .. RPB b + RPB - 1 (RPB = 64 / (D / 8)); lane
+// i lands at row RPB b + i / NCH, physical chunk i % NCH, so it fetches the
+// logical chunk (i % NCH) ^ (row % NCH).  Rows past the chunk's n tokens
+// re-read row n - 1 (finite data the kernels mask out).
+// ---------------------------------------------------------------------------
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D>
+__device__ __forceinline__ void dma_block(const uint16_t *chunk_src, int n, unsigned char *tile,
+                                          int block, int lane) {
+  constexpr int NCH = D / 8;
+  constexpr int RPB = 64 / NCH;
+  const int row = block * RPB + lane / NCH;
+  const int c = (lane % NCH) ^ (row & (NCH - 1));
+  const int grow = min(row, n - 1);
+  __builtin_amdgcn_global_load_lds(chunk_src + (int64_t)grow * D + c * 8,
+                                   (lds_void *)(tile + block * 1024), 16, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Transposed fragment reads (ds_read_b64_tr_b16).  Within each 16-lane group
+// the hardware returns result[i][e] = src[4 e + i / 4][i % 4], where src[j] is
+// the 4 elements at lane j's address.  Pointing lane j at row s0 + j / 4,
+// columns d0 + 4 (j % 4) .. + 3 of a row-major tile therefore gives lane i the
+// column d0 + i for rows s0 .. s0 + 3.
+// tr_frag returns, for lane (li, lg), the 8 values X[s0 + 8 lg + e][d0 + li],
+// e = 0..7: an MFMA fragment whose k index runs over rows.
+// ---------------------------------------------------------------------------
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+template <int NCH>
+__device__ __forceinline__ bf16x4 tr_read4(const unsigned char *tile, int s0, int d0, int li) {
+  const int row = s0 + (li >> 2);
+  const int col = d0 + 4 * (li & 3);
+  const unsigned char *p = tile + swz_off<NCH>(row, col >> 3) + (col & 7) * 2;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
+}
+
+template <int NCH>
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char *tile, int s0, int d0, int li,
+                                          int lg) {
+  const bf16x4 lo = tr_read4<NCH>(tile, s0 + 8 * lg, d0, li);
+  const bf16x4 hi = tr_read4<NCH>(tile, s0 + 8 * lg + 4, d0, li);
+  return cat8(lo, hi);
+}
+
 }  // namespace chunk
 }  // namespace cla
