@@ -47,28 +47,28 @@ template <int DK, int DV, int MODE>
 __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
   constexpr int NJ = DV / 64;   // dV side: 16-col tiles of G per wave
   constexpr int NI = DK / 64;   // dK side: 16-col tiles of G^T per wave
+  constexpr int NCK = DK / 8, NCV = DV / 8;
   constexpr int RK = 64 * DK * 2, RV = 64 * DV * 2;  // row-major tile bytes
-  constexpr int TK = DK * 128, TV = DV * 128;        // transposed tile bytes
-  constexpr int OFF_QT = 0;
-  constexpr int OFF_DOT = OFF_QT + TK;
-  constexpr int OFF_QS = OFF_DOT + TV;
-  constexpr int OFF_KS = OFF_QS + (MODE == 0 ? RK : 0);
+  constexpr int OFF_QS = 0;
+  constexpr int OFF_DOS = OFF_QS + RK;
+  constexpr int OFF_KS = OFF_DOS + RV;
   constexpr int OFF_VS = OFF_KS + (MODE == 0 ? RK : 0);
-  constexpr int OFF_DOS = OFF_VS + (MODE == 0 ? RV : 0);
-  constexpr int OFF_P1 = OFF_DOS + (MODE == 0 ? RV : 0);
+  constexpr int OFF_P1 = OFF_VS + (MODE == 0 ? RV : 0);
   constexpr int OFF_P2 = OFF_P1 + (MODE == 0 ? 64 * 128 : 0);
   constexpr int OFF_C = OFF_P2 + (MODE == 0 ? 64 * 128 : 0);
   constexpr int OFF_R2 = OFF_C + 3 * 64 * 4 + 16;
   constexpr int SMEM = OFF_R2 + (MODE == 0 ? 4 * 64 * 4 : 0);
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-  unsigned char *QT = smem + OFF_QT;
-  unsigned char *DOT = smem + OFF_DOT;
+  // 1 KB DMA blocks per chunk: [Q | dO | K | V] (K, V only in MODE 0)
+  constexpr int NBQ = DK / 8, NBD = DV / 8;
+  constexpr int NBK = MODE == 0 ? DK / 8 : 0, NBV = MODE == 0 ? DV / 8 : 0;
+  constexpr int NBLK = NBQ + NBD + NBK + NBV;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
   unsigned char *QS = smem + OFF_QS;
+  unsigned char *DOS = smem + OFF_DOS;
   unsigned char *KS = smem + OFF_KS;
   unsigned char *VS = smem + OFF_VS;
-  unsigned char *DOS = smem + OFF_DOS;
-  unsigned char *P1 = smem + OFF_P1;  // P1T[s][r] = D[r][s] (q_r . k_s)
-  unsigned char *P2 = smem + OFF_P2;  // P2T[s][r] = D[r][s] (dO_r . v_s)
+  unsigned char *P1 = smem + OFF_P1;  // P1[s][r] = D_rs (q_r . k_s)
+  unsigned char *P2 = smem + OFF_P2;  // P2[s][r] = D_rs (dO_r . v_s)
   float *CS = reinterpret_cast<float *>(smem + OFF_C);
   float *LAM = CS + 64;
   float *GAM = CS + 128;
@@ -135,39 +135,34 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     }
   }
   float alpha_total = 1.f;
+  int64_t r2_t0 = -1;  // chunk whose k.dk partials sit in R2P
+  int r2_n = 0;
 
   for (int64_t ci = c_end - 1; ci >= c_begin; --ci) {
     const int64_t t0 = ci * TC;
     const int n = (int)min<int64_t>(TC, T - t0);
 
-    // stage: threads 0..255 move Q and dO, threads 256..511 move K and V
-    TileRegs<DK> qr, kr;
-    TileRegs<DV> dr, vr;
-    const int ht = tid & 255;
-    if (tid < 256) {
-      tile_load<DK>(qh + t0 * DK, n, ht, qr);
-      tile_load<DV>(doh + t0 * DV, n, ht, dr);
-    } else if (MODE == 0) {
-      tile_load<DK>(kh + t0 * DK, n, ht, kr);
-      tile_load<DV>(vh + t0 * DV, n, ht, vr);
+    __syncthreads();  // the previous chunk's LDS reads are done
+    if (MODE == 0 && r2_t0 >= 0 && tid < r2_n)
+      a.r2[bh * T + r2_t0 + tid] = R2P[tid] + R2P[64 + tid] + R2P[128 + tid] + R2P[192 + tid];
+    for (int b = w; b < NBLK; b += BTHR / 64) {
+      if (b < NBQ) {
+        dma_block<DK>(qh + t0 * DK, n, QS, b, lane);
+      } else if (b < NBQ + NBD) {
+        dma_block<DV>(doh + t0 * DV, n, DOS, b - NBQ, lane);
+      } else if (b < NBQ + NBD + NBK) {
+        dma_block<DK>(kh + t0 * DK, n, KS, b - NBQ - NBD, lane);
+      } else {
+        dma_block<DV>(vh + t0 * DV, n, VS, b - NBQ - NBD - NBK, lane);
+      }
     }
     float lv = 0.f;
-    if (w == 0 && lane < n) lv = lh[t0 + lane];
-
-    __syncthreads();
-    if (tid < 256) {
-      tile_store_cols<DK>(QT, ht, qr);
-      tile_store_cols<DV>(DOT, ht, dr);
-      if (MODE == 0) {
-        tile_store_rows<DK>(QS, ht, qr);
-        tile_store_rows<DV>(DOS, ht, dr);
-      }
-    } else if (MODE == 0) {
-      tile_store_rows<DK>(KS, ht, kr);
-      tile_store_rows<DV>(VS, ht, vr);
-    }
+    if (w == 0) lv = lh[t0 + min(lane, n - 1)];
+    __builtin_amdgcn_s_waitcnt(0);
     if (w == 0) {
-      float c = lv;
+      // rows past the chunk: no decay, and lambda = 0 so that they add
+      // nothing to the state gradient
+      float c = lane < n ? lv : 0.f;
 #pragma unroll
       for (int sh = 1; sh < 64; sh <<= 1) {
         const float p = __shfl_up(c, sh, 64);
@@ -175,42 +170,41 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
       }
       const float cl = __shfl(c, 63, 64);
       CS[lane] = c;
-      LAM[lane] = expf(c);
+      LAM[lane] = lane < n ? expf(c) : 0.f;
       GAM[lane] = expf(cl - c);
       if (lane == 0) ALPHA[0] = expf(cl);
     }
     __syncthreads();
 
     if constexpr (MODE == 0) {
-      // ---- masked score tiles, stored transposed: P[s][r] for key tile wv ----
+      // ---- masked score tiles, stored transposed: P[s][r] ----
       {
-        const int st = wv;
-        const int s = 16 * st + li;
-        const float cs = CS[s];
         unsigned char *PT = side == 0 ? P1 : P2;
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
+        for (int t = wv; t < 12; t += 4) {
+          const int rt = tile_rt(t), st = tile_st(t);
+          const int s = 16 * st + li;
           f32x4 acc = zero4();
           if (rt >= st) {
             if (side == 0) {
 #pragma unroll
               for (int kk = 0; kk < DK / 32; ++kk)
-                acc = mfma(lds_frag<DK / 8>(QS, 16 * rt + li, 4 * kk + lg),
-                           lds_frag<DK / 8>(KS, s, 4 * kk + lg), acc);
+                acc = mfma(lds_frag<NCK>(QS, 16 * rt + li, 4 * kk + lg),
+                           lds_frag<NCK>(KS, s, 4 * kk + lg), acc);
             } else {
 #pragma unroll
               for (int kk = 0; kk < DV / 32; ++kk)
-                acc = mfma(lds_frag<DV / 8>(DOS, 16 * rt + li, 4 * kk + lg),
-                           lds_frag<DV / 8>(VS, s, 4 * kk + lg), acc);
+                acc = mfma(lds_frag<NCV>(DOS, 16 * rt + li, 4 * kk + lg),
+                           lds_frag<NCV>(VS, s, 4 * kk + lg), acc);
             }
           }
-          // acc[i] = X[r = 16 rt + 4 lg + i][s]
+          // acc[i] = X[r = 16 rt + 4 lg + i][s]; rows past the chunk are masked
+          const float cs = CS[s];
           bf16x4 pv;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 16 * rt + 4 * lg + i;
             float p = 0.f;
-            if (r >= s) p = acc[i] * __expf(CS[r] - cs);
+            if (r >= s && r < n) p = acc[i] * __expf(CS[r] - cs);
             pv[i] = tobf(p);
           }
           *reinterpret_cast<bf16x4 *>(PT + swz_off<8>(s, 2 * rt + (lg >> 1)) + (lg & 1) * 8) = pv;
@@ -219,34 +213,26 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
       __syncthreads();
 
       if (side == 0) {
-        // ---- dV^T[j][s] = dO^T P1 + G^T (gamma K)^T ----
+        // ---- dV^T[j][s] = gamma_s (G^T K^T)[j][s] + (dO^T P1)[j][s] ----
         bf16x8 gfrag[DK / 32][NJ];
 #pragma unroll
         for (int kk = 0; kk < DK / 32; ++kk)
 #pragma unroll
           for (int jt = 0; jt < NJ; ++jt) gfrag[kk][jt] = cvt8(G0(2 * kk, jt), G0(2 * kk + 1, jt));
-        bf16x8 dfrag[NJ][2];
+        bf16x8 dfrag[NJ][2];  // dO^T A operands: row j, k = r
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) dfrag[jt][kb] = lds_frag<8>(DOT, jw0 + 16 * jt + li, 4 * kb + lg);
+          for (int kb = 0; kb < 2; ++kb) dfrag[jt][kb] = tr_frag<NCV>(DOS, 32 * kb, jw0 + 16 * jt, li, lg);
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           const int s = 16 * st + li;
           const float gs = GAM[s];
           bf16x8 kfrag[DK / 32];
 #pragma unroll
-          for (int kk = 0; kk < DK / 32; ++kk) {
-            const bf16x4 lo = lds_half<DK / 8>(KS, s, 32 * kk + 4 * lg);
-            const bf16x4 hi = lds_half<DK / 8>(KS, s, 32 * kk + 16 + 4 * lg);
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              x[e] = tof(lo[e]) * gs;
-              x[e + 4] = tof(hi[e]) * gs;
-            }
-            kfrag[kk] = cvt8(x);
-          }
+          for (int kk = 0; kk < DK / 32; ++kk)
+            kfrag[kk] = cat8(lds_half<NCK>(KS, s, 32 * kk + 4 * lg),
+                             lds_half<NCK>(KS, s, 32 * kk + 16 + 4 * lg));
           bf16x8 pfrag[2];
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) pfrag[kb] = lds_frag<8>(P1, s, 4 * kb + lg);
@@ -254,10 +240,12 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
           for (int jt = 0; jt < NJ; ++jt) {
             f32x4 acc = zero4();
 #pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) acc = mfma(gfrag[kk][jt], kfrag[kk], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] *= gs;
+#pragma unroll
             for (int kb = 0; kb < 2; ++kb)
               if (2 * kb + 1 >= st) acc = mfma(dfrag[jt][kb], pfrag[kb], acc);
-#pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) acc = mfma(gfrag[kk][jt], kfrag[kk], acc);
             // acc[i] = dV[s][jw0 + 16 jt + 4 lg + i]
             if (s < n) {
               bf16x4 ov;
@@ -268,34 +256,26 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
           }
         }
       } else {
-        // ---- dK^T[d][s] = Q^T P2 + G (gamma V)^T ; r2_s = k_s . dk_s ----
+        // ---- dK^T[d][s] = gamma_s (G V^T)[d][s] + (Q^T P2)[d][s] ; r2_s = k_s . dk_s ----
         bf16x8 gfrag[DV / 32][NI];
 #pragma unroll
         for (int kk = 0; kk < DV / 32; ++kk)
 #pragma unroll
           for (int it = 0; it < NI; ++it) gfrag[kk][it] = cvt8(G1(2 * kk, it), G1(2 * kk + 1, it));
-        bf16x8 qfrag[NI][2];
+        bf16x8 qfrag[NI][2];  // Q^T A operands: row d, k = r
 #pragma unroll
         for (int it = 0; it < NI; ++it)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) qfrag[it][kb] = lds_frag<8>(QT, dw0 + 16 * it + li, 4 * kb + lg);
+          for (int kb = 0; kb < 2; ++kb) qfrag[it][kb] = tr_frag<NCK>(QS, 32 * kb, dw0 + 16 * it, li, lg);
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           const int s = 16 * st + li;
           const float gs = GAM[s];
           bf16x8 vfrag[DV / 32];
 #pragma unroll
-          for (int kk = 0; kk < DV / 32; ++kk) {
-            const bf16x4 lo = lds_half<DV / 8>(VS, s, 32 * kk + 4 * lg);
-            const bf16x4 hi = lds_half<DV / 8>(VS, s, 32 * kk + 16 + 4 * lg);
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              x[e] = tof(lo[e]) * gs;
-              x[e + 4] = tof(hi[e]) * gs;
-            }
-            vfrag[kk] = cvt8(x);
-          }
+          for (int kk = 0; kk < DV / 32; ++kk)
+            vfrag[kk] = cat8(lds_half<NCV>(VS, s, 32 * kk + 4 * lg),
+                             lds_half<NCV>(VS, s, 32 * kk + 16 + 4 * lg));
           bf16x8 pfrag[2];
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) pfrag[kb] = lds_frag<8>(P2, s, 4 * kb + lg);
@@ -304,13 +284,15 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
           for (int it = 0; it < NI; ++it) {
             f32x4 acc = zero4();
 #pragma unroll
+            for (int kk = 0; kk < DV / 32; ++kk) acc = mfma(gfrag[kk][it], vfrag[kk], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] *= gs;
+#pragma unroll
             for (int kb = 0; kb < 2; ++kb)
               if (2 * kb + 1 >= st) acc = mfma(qfrag[it][kb], pfrag[kb], acc);
-#pragma unroll
-            for (int kk = 0; kk < DV / 32; ++kk) acc = mfma(gfrag[kk][it], vfrag[kk], acc);
             // acc[i] = dK[s][dw0 + 16 it + 4 lg + i]
             const int dc = dw0 + 16 * it + 4 * lg;
-            const bf16x4 kv = lds_half<DK / 8>(KS, s, dc);
+            const bf16x4 kv = lds_half<NCK>(KS, s, dc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) r2p += tof(kv[i]) * acc[i];
             if (s < n) {
@@ -327,75 +309,69 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
       }
     }
 
-    // ---- state-gradient update (both copies) ----
+    // ---- state-gradient update (both copies): G <- alpha G + Q^T (lambda dO) ----
     const float alpha = ALPHA[0];
     alpha_total *= alpha;
-    float lam[2][8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int x = 0; x < NG; ++x)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) lam[kb][e] = LAM[32 * kb + 8 * lg + e];
+      for (int i = 0; i < 4; ++i) Gs[x][i] *= alpha;
     if (side == 0) {
-      // G[d][j] += sum_r (lambda Q)^T[d][r] dO[r][j]
+      // G[d][j] += sum_r Q^T[d][r] (lambda dO)[r][j]
 #pragma unroll
-      for (int dt = 0; dt < DK / 16; ++dt)
+      for (int kb = 0; kb < 2; ++kb) {
+        float lam[8];
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt)
+        for (int e = 0; e < 8; ++e) lam[e] = LAM[32 * kb + 8 * lg + e];
+        bf16x8 db[NJ];  // (lambda dO) B operands: k = r, column j
 #pragma unroll
-          for (int i = 0; i < 4; ++i) G0(dt, jt)[i] *= alpha;
-      bf16x8 db[NJ][2];
+        for (int jt = 0; jt < NJ; ++jt) {
+          const bf16x8 x = tr_frag<NCV>(DOS, 32 * kb, jw0 + 16 * jt, li, lg);
+          float y[8];
 #pragma unroll
-      for (int jt = 0; jt < NJ; ++jt)
+          for (int e = 0; e < 8; ++e) y[e] = tof(x[e]) * lam[e];
+          db[jt] = cvt8(y);
+        }
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) db[jt][kb] = lds_frag<8>(DOT, jw0 + 16 * jt + li, 4 * kb + lg);
+        for (int dt = 0; dt < DK / 16; ++dt) {
+          const bf16x8 qa = tr_frag<NCK>(QS, 32 * kb, 16 * dt, li, lg);  // Q^T: row d, k = r
 #pragma unroll
-      for (int dt = 0; dt < DK / 16; ++dt) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 qt = lds_frag<8>(QT, 16 * dt + li, 4 * kb + lg);
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = tof(qt[e]) * lam[kb][e];
-          const bf16x8 qa = cvt8(x);
-#pragma unroll
-          for (int jt = 0; jt < NJ; ++jt) G0(dt, jt) = mfma(qa, db[jt][kb], G0(dt, jt));
+          for (int jt = 0; jt < NJ; ++jt) G0(dt, jt) = mfma(qa, db[jt], G0(dt, jt));
         }
       }
     } else if (MODE == 0) {
       // G^T[j][d] += sum_r dO^T[j][r] (lambda Q)[r][d]
 #pragma unroll
-      for (int jt = 0; jt < DV / 16; ++jt)
+      for (int kb = 0; kb < 2; ++kb) {
+        float lam[8];
 #pragma unroll
-        for (int it = 0; it < NI; ++it)
+        for (int e = 0; e < 8; ++e) lam[e] = LAM[32 * kb + 8 * lg + e];
+        bf16x8 qb[NI];  // (lambda Q) B operands: k = r, column d
 #pragma unroll
-          for (int i = 0; i < 4; ++i) G1(jt, it)[i] *= alpha;
-      bf16x8 qb[NI][2];
+        for (int it = 0; it < NI; ++it) {
+          const bf16x8 x = tr_frag<NCK>(QS, 32 * kb, dw0 + 16 * it, li, lg);
+          float y[8];
 #pragma unroll
-      for (int it = 0; it < NI; ++it)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 qt = lds_frag<8>(QT, dw0 + 16 * it + li, 4 * kb + lg);
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = tof(qt[e]) * lam[kb][e];
-          qb[it][kb] = cvt8(x);
+          for (int e = 0; e < 8; ++e) y[e] = tof(x[e]) * lam[e];
+          qb[it] = cvt8(y);
         }
 #pragma unroll
-      for (int jt = 0; jt < DV / 16; ++jt) {
+        for (int jt = 0; jt < DV / 16; ++jt) {
+          const bf16x8 da = tr_frag<NCV>(DOS, 32 * kb, 16 * jt, li, lg);  // dO^T: row j, k = r
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 da = lds_frag<8>(DOT, 16 * jt + li, 4 * kb + lg);
-#pragma unroll
-          for (int it = 0; it < NI; ++it) G1(jt, it) = mfma(da, qb[it][kb], G1(jt, it));
+          for (int it = 0; it < NI; ++it) G1(jt, it) = mfma(da, qb[it], G1(jt, it));
         }
       }
     }
-
-    if constexpr (MODE == 0) {
-      __syncthreads();  // R2P complete
-      if (tid < 64 && tid < n)
-        a.r2[bh * T + t0 + tid] = R2P[tid] + R2P[64 + tid] + R2P[128 + tid] + R2P[192 + tid];
+    if (MODE == 0) {
+      r2_t0 = t0;
+      r2_n = n;
     }
+  }
+  if (MODE == 0 && r2_t0 >= 0) {
+    __syncthreads();
+    if (tid < r2_n)
+      a.r2[bh * T + r2_t0 + tid] = R2P[tid] + R2P[64 + tid] + R2P[128 + tid] + R2P[192 + tid];
   }
 
   // ---- segment outputs ----
