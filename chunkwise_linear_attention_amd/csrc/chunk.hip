@@ -40,7 +40,11 @@ namespace cla {
 namespace chunk {
 namespace {
 
-constexpr int64_t kTargetWG = 512;   // two workgroups per CU on 256 CUs
+// Concurrent workgroups: the forward-type kernel runs two per CU, the dK/dV
+// kernel one per CU, on 256 CUs.  Segment counts are chosen so that the
+// workgroups fill whole rounds of these slots.
+constexpr int64_t kFwdSlots = 512;
+constexpr int64_t kBwdSlots = 256;
 constexpr int64_t kMinSegChunks = 4;
 // The backward's decay gradient sums q.dq - k.dk backwards only inside one
 // segment, starting from the exact boundary term <S, G> of the two segment
@@ -107,6 +111,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
         trans = a.s0_trans;
       } else {
         src = a.Sin + ((seg - 1) * a.nh + bh) * DK * DV;
+        trans = a.slot_trans;
       }
     }
 #pragma unroll
@@ -313,7 +318,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int d = 16 * dt + 4 * lg + i, j = j0 + 16 * jt + li;
-          dst[d * DV + j] = S_acc[dt][jt][i];
+          dst[a.slot_trans ? j * DK + d : d * DV + j] = S_acc[dt][jt][i];
         }
     if (tid == 0) a.aloc[seg * a.nh + bh] = alpha_total;
   }
@@ -350,8 +355,10 @@ hipError_t fwd_impl(FwdArgs args, hipStream_t stream) {
                (chunk_fwd_kernel<DK, DV, 1>), g1, dim3(NTHR), stream, args);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_segment_scan(args.Sloc, args.aloc, args.S0, args.s0_trans, 0, args.nh, P, DK,
-                            DV, stream);
+    // slots and S0 are combined elementwise; S0 is read transposed only when
+    // its layout differs from the slots'
+    e = launch_segment_scan(args.Sloc, args.aloc, args.S0, args.s0_trans != args.slot_trans, 0,
+                            args.nh, P, DK, DV, stream);
     if (e != hipSuccess) return e;
     args.Sin = args.Sloc;
   }
@@ -400,13 +407,13 @@ FwdWs fwd_ws(void *base, int64_t nh, int64_t P, int64_t DK, int64_t DV) {
   return w;
 }
 
-// backward workspace: the segment states of the dQ pass (S^T at segment
-// ends) and of the reverse pass (G at segment ends), q . dq and k . dk per
-// token, and the final state for <S_T, dS_T>
+// backward workspace: the segment states of the dQ pass (S at segment ends)
+// and of the reverse pass (G at segment ends), q . dq and k . dk per token,
+// the final state S_T, and the boundary terms <S, G> per segment
 struct BwdWs {
-  FwdWs seg;   // dQ pass: slots p = S^T at the end of segment p
+  FwdWs seg;   // dQ pass: slots p = S at the end of segment p
   FwdWs gseg;  // reverse pass: slots p = G at the end of segment p
-  float *r1, *r2, *ST;
+  float *r1, *r2, *ST, *Bnd;
   size_t bytes;
 };
 
@@ -424,6 +431,7 @@ BwdWs bwd_ws(void *base, int64_t nh, int64_t T, int64_t P, int64_t DK, int64_t D
   w.r1 = carve((size_t)nh * T * sizeof(float));
   w.r2 = carve((size_t)nh * T * sizeof(float));
   w.ST = carve((size_t)nh * DK * DV * sizeof(float));
+  w.Bnd = carve((size_t)P * nh * sizeof(float));
   w.bytes = off;
   return w;
 }
@@ -437,10 +445,10 @@ ChunkPlan plan_chunk(int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV) {
   const int64_t nchunks = (T + chunk::TC - 1) / chunk::TC;
   plan.seg_chunks = nchunks;
   if (nh <= 0 || nchunks <= 0) return plan;
+  const int64_t maxP = (nchunks + chunk::kMinSegChunks - 1) / chunk::kMinSegChunks;
   int64_t P = 1;
-  if (nh < chunk::kTargetWG) {
-    P = (chunk::kTargetWG + nh - 1) / nh;
-    const int64_t maxP = (nchunks + chunk::kMinSegChunks - 1) / chunk::kMinSegChunks;
+  if (2 * nh < chunk::kFwdSlots) {
+    P = chunk::kFwdSlots / nh;  // one full round of workgroups
     if (P > maxP) P = maxP;
     if (P < 1) P = 1;
   }
@@ -449,7 +457,12 @@ ChunkPlan plan_chunk(int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV) {
   plan.P = P;
   plan.seg_chunks = segc;
   plan.ws_fwd = chunk::fwd_ws(nullptr, nh, P, DK, DV).bytes;
-  int64_t Pb = P;
+  int64_t Pb = 1;
+  if (2 * nh < chunk::kBwdSlots) {
+    Pb = chunk::kBwdSlots / nh;
+    if (Pb > maxP) Pb = maxP;
+    if (Pb < 1) Pb = 1;
+  }
   const int64_t minPb = (nchunks + chunk::kMaxBwdSegChunks - 1) / chunk::kMaxBwdSegChunks;
   if (Pb < minPb) Pb = minPb;
   const int64_t segb = (nchunks + Pb - 1) / Pb;
@@ -501,6 +514,7 @@ hipError_t launch_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t
   fa.l = l;
   fa.S0 = S0;
   fa.s0_trans = 1;
+  fa.slot_trans = 1;  // segment states kept as S (not S^T), like the G slots
   fa.o = dq;
   fa.ST = dST ? w.ST : nullptr;
   fa.st_trans = 1;
@@ -528,14 +542,17 @@ hipError_t launch_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t
   ba.dS0 = dS0;
   ba.Gloc = w.gseg.Sloc;
   ba.aloc = w.gseg.aloc;
+  ba.Sseg = w.seg.Sloc;
+  ba.STb = dST ? w.ST : nullptr;
+  ba.Bnd = w.Bnd;
   ba.nh = nh;
   ba.T = T;
   ba.seg_chunks = plan.seg_chunks_b;
   ba.P = plan.P_b;
   e = chunk::bwd_kv_dispatch(ba, (int)DK, (int)DV, stream);
   if (e != hipSuccess) return e;
-  return chunk::launch_dlog(w.r1, w.r2, dST ? w.ST : nullptr, dST, w.seg.Sloc, w.gseg.Sloc, dl,
-                            nh, T, DK, DV, plan.seg_chunks_b * chunk::TC, plan.P_b, stream);
+  return chunk::launch_dlog(w.r1, w.r2, w.Bnd, dl, nh, T, plan.seg_chunks_b * chunk::TC,
+                            plan.P_b, stream);
 }
 
 }  // namespace cla

@@ -135,6 +135,34 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     }
   }
   float alpha_total = 1.f;
+  if (MODE == 0) {
+    // Boundary term of the decay gradient: <S, G> at this segment's end,
+    // from the fp32 state the dQ pass left there and the G just loaded.
+    const float *S = seg == a.P - 1 ? (a.STb ? a.STb + bh * DK * DV : nullptr)
+                                    : a.Sseg + (seg * a.nh + bh) * DK * DV;
+    double part = 0.0;
+    if (side == 0 && S) {
+      float pf = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DK / 16; ++dt)
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            pf += G0(dt, jt)[i] * S[(16 * dt + 4 * lg + i) * DV + jw0 + 16 * jt + li];
+      part = pf;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+    __shared__ double bred[8];
+    if (lane == 0) bred[w] = part;
+    __syncthreads();
+    if (tid == 0) {
+      double b = 0.0;
+      for (int u = 0; u < 4; ++u) b += bred[u];
+      a.Bnd[seg * a.nh + bh] = (float)b;
+    }
+  }
   int64_t r2_t0 = -1;  // chunk whose k.dk partials sit in R2P
   int r2_n = 0;
 
@@ -407,43 +435,19 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
 // Decay gradient of one segment of one sequence (one workgroup each):
 //   dl_u = B + sum_{t >= u, t in segment} (r1_t - r2_t),
 // B = the sum over all paths that cross the segment's end, i.e. <S, G> at
-// that boundary, computed exactly from the two stored fp32 states.  fp64
-// accumulation throughout.
+// that boundary (computed exactly from the two fp32 states by the dK/dV
+// pass).  fp64 accumulation throughout.
 constexpr int DL_THR = 256;
 constexpr int DL_PER = 16;  // tokens per thread; segments hold <= 4096 tokens
 
 __global__ __launch_bounds__(DL_THR) void dlog_kernel(const float *r1, const float *r2,
-                                                      const float *ST, const float *dST,
-                                                      const float *Sseg, const float *Gseg,
-                                                      float *dl, int64_t nh, int64_t T, int DK,
-                                                      int DV, int64_t seg_len, int64_t P) {
+                                                      const float *Bnd, float *dl, int64_t nh,
+                                                      int64_t T, int64_t seg_len) {
   __shared__ double red[DL_THR];
   const int64_t bh = blockIdx.x % nh;
   const int64_t seg = blockIdx.x / nh;
   const int tid = threadIdx.x;
-  const int64_t per = (int64_t)DK * DV;
-  double sd = 0.0;
-  if (seg == P - 1) {
-    if (ST && dST)
-      for (int64_t e = tid; e < per; e += DL_THR)
-        sd += (double)ST[bh * per + e] * (double)dST[bh * per + e];
-  } else {
-    // Sseg holds S^T ([DV][DK]); Gseg holds G ([DK][DV])
-    const float *S = Sseg + (seg * nh + bh) * per;
-    const float *G = Gseg + (seg * nh + bh) * per;
-    for (int64_t e = tid; e < per; e += DL_THR) {
-      const int64_t d = e / DV, j = e % DV;
-      sd += (double)S[j * DK + d] * (double)G[e];
-    }
-  }
-  red[tid] = sd;
-  __syncthreads();
-  for (int o = DL_THR / 2; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
-  }
-  const double B = red[0];
-  __syncthreads();
+  const double B = (double)Bnd[seg * nh + bh];
   const int64_t s0 = seg * seg_len, s1 = min(T, s0 + seg_len);
   const int64_t lo = min(s1, s0 + (int64_t)tid * DL_PER), hi = min(s1, lo + DL_PER);
   const float *x1 = r1 + bh * T, *x2 = r2 + bh * T;
@@ -499,12 +503,11 @@ hipError_t bwd_kv_dispatch(const BwdArgs &args, int DK, int DV, hipStream_t stre
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_dlog(const float *r1, const float *r2, const float *ST, const float *dST,
-                       const float *Sseg, const float *Gseg, float *dl, int64_t nh, int64_t T,
-                       int DK, int DV, int64_t seg_len, int64_t P, hipStream_t stream) {
+hipError_t launch_dlog(const float *r1, const float *r2, const float *Bnd, float *dl, int64_t nh,
+                       int64_t T, int64_t seg_len, int64_t P, hipStream_t stream) {
   if (seg_len > (int64_t)DL_THR * DL_PER) return hipErrorInvalidValue;
   CLA_LAUNCH("chunk_dlog", dlog_kernel, dim3((unsigned)(nh * P)), dim3(DL_THR), stream, r1, r2,
-             ST, dST, Sseg, Gseg, dl, nh, T, DK, DV, seg_len, P);
+             Bnd, dl, nh, T, seg_len);
   return hipGetLastError();
 }
 

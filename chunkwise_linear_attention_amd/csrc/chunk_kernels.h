@@ -23,6 +23,7 @@ struct FwdArgs {
   float *rdot;             // [nh, T]
   int64_t nh, T, seg_chunks, P;
   int s0_trans, st_trans;
+  int slot_trans;          // segment slots (Sloc, Sin) hold this kernel's state transposed
 };
 
 struct BwdArgs {
@@ -35,6 +36,9 @@ struct BwdArgs {
   float *dS0;                       // [nh, DK, DV] or NULL
   float *Gloc;                      // state-only pass: [P-1, nh, DK, DV] (segment p in slot p-1)
   float *aloc;                      // state-only pass: [P-1, nh]
+  const float *Sseg;                // [P-1, nh, DK, DV]: S at the end of segments 0..P-2
+  const float *STb;                 // [nh, DK, DV]: S_T (NULL when there is no dS_T)
+  float *Bnd;                       // [P, nh]: <S, G> at the end of each segment
   int64_t nh, T, seg_chunks, P;
 };
 
@@ -53,13 +57,10 @@ hipError_t launch_segment_scan(float *slots, const float *aloc, const float *ini
                                int init_trans, int reverse, int64_t nh, int64_t P,
                                int DK, int DV, hipStream_t stream);
 
-// dl_u for u in segment p = B_p + sum_{t >= u, t in segment p} (r1_t - r2_t),
-// with the boundary term B_p = <S, G> at the end of segment p: <S_T, dS_T>
-// (0 without dS_T) for the last segment, <Sseg[p]^T, Gseg[p]> otherwise
-// (Sseg holds S^T, Gseg holds G, both [P-1, nh, DK*DV]).
-hipError_t launch_dlog(const float *r1, const float *r2, const float *ST, const float *dST,
-                       const float *Sseg, const float *Gseg, float *dl, int64_t nh, int64_t T,
-                       int DK, int DV, int64_t seg_len, int64_t P, hipStream_t stream);
+// dl_u for u in segment p = Bnd[p] + sum_{t >= u, t in segment p} (r1_t - r2_t),
+// with Bnd[p] = <S, G> at the end of segment p (computed by the dK/dV pass).
+hipError_t launch_dlog(const float *r1, const float *r2, const float *Bnd, float *dl, int64_t nh,
+                       int64_t T, int64_t seg_len, int64_t P, hipStream_t stream);
 
 }  // namespace chunk
 }  // namespace cla
