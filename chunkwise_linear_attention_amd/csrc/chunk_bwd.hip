@@ -49,35 +49,40 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
   constexpr int NI = DK / 64;   // dK side: 16-col tiles of G^T per wave
   constexpr int NCK = DK / 8, NCV = DV / 8;
   constexpr int RK = 64 * DK * 2, RV = 64 * DV * 2;  // row-major tile bytes
-  constexpr int OFF_QS = 0;
-  constexpr int OFF_DOS = OFF_QS + RK;
-  constexpr int OFF_KS = OFF_DOS + RV;
-  constexpr int OFF_VS = OFF_KS + (MODE == 0 ? RK : 0);
-  constexpr int OFF_P1 = OFF_VS + (MODE == 0 ? RV : 0);
-  constexpr int OFF_P2 = OFF_P1 + (MODE == 0 ? 64 * 128 : 0);
-  constexpr int OFF_C = OFF_P2 + (MODE == 0 ? 64 * 128 : 0);
-  constexpr int OFF_R2 = OFF_C + 3 * 64 * 4 + 16;
-  constexpr int SMEM = OFF_R2 + (MODE == 0 ? 4 * 64 * 4 : 0);
-  // 1 KB DMA blocks per chunk: [Q | dO | K | V] (K, V only in MODE 0)
+  // Two staging buffers, each [Q | dO | K | V | l] (K, V only in MODE 0):
+  // the next chunk streams into one by DMA while the other is being used.
+  // They are separate arrays so that the compiler can tell the DMA target
+  // from the buffer being read and does not wait for the DMA before reads.
+  constexpr int B_DOS = RK;
+  constexpr int B_KS = B_DOS + RV;
+  constexpr int B_VS = B_KS + (MODE == 0 ? RK : 0);
+  constexpr int B_L = B_VS + (MODE == 0 ? RV : 0);
+  constexpr int BUF = B_L + 64 * 4;
+  // 1 KB DMA blocks per chunk
   constexpr int NBQ = DK / 8, NBD = DV / 8;
   constexpr int NBK = MODE == 0 ? DK / 8 : 0, NBV = MODE == 0 ? DV / 8 : 0;
   constexpr int NBLK = NBQ + NBD + NBK + NBV;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
-  unsigned char *QS = smem + OFF_QS;
-  unsigned char *DOS = smem + OFF_DOS;
-  unsigned char *KS = smem + OFF_KS;
-  unsigned char *VS = smem + OFF_VS;
-  unsigned char *P1 = smem + OFF_P1;  // P1[s][r] = D_rs (q_r . k_s)
-  unsigned char *P2 = smem + OFF_P2;  // P2[s][r] = D_rs (dO_r . v_s)
-  float *CS = reinterpret_cast<float *>(smem + OFF_C);
-  float *LAM = CS + 64;
-  float *GAM = CS + 128;
-  float *ALPHA = CS + 192;
-  float *R2P = reinterpret_cast<float *>(smem + OFF_R2);
+  __shared__ __attribute__((aligned(1024))) unsigned char buf0[BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf1[BUF];
+  // P1[s][r] = D_rs (q_r . k_s), P2[s][r] = D_rs (dO_r . v_s)
+  __shared__ __attribute__((aligned(1024))) unsigned char P1[MODE == 0 ? 64 * 128 : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char P2[MODE == 0 ? 64 * 128 : 16];
+  __shared__ float R2P[MODE == 0 ? 4 * 64 : 1];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
-  const int li = lane & 15, lg = lane >> 4;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  int li = lane & 15, lg = lane >> 4;
+  // Re-derive the lane coordinates behind an empty asm at the start of each
+  // phase, so that the compiler forms LDS addresses next to their use instead
+  // of hoisting all of them out of the chunk loop (which exhausts registers).
+#define FRESH_LANE()                   \
+  do {                                 \
+    int l_ = lane;                     \
+    asm volatile("" : "+v"(l_));       \
+    li = l_ & 15;                      \
+    lg = l_ >> 4;                      \
+  } while (0)
   const int side = w >> 2, wv = w & 3;   // side 0: dV / G;  side 1: dK / G^T
   const int64_t bh = blockIdx.x % a.nh;
   const int64_t seg = MODE == 0 ? blockIdx.x / a.nh : 1 + blockIdx.x / a.nh;
@@ -112,26 +117,27 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
         src = a.Gin + (seg * a.nh + bh) * DK * DV;
       }
     }
-    if (side == 0) {
+    if (MODE == 1) src = nullptr;
 #pragma unroll
-      for (int dt = 0; dt < DK / 16; ++dt)
+    for (int x = 0; x < NG; ++x) Gs[x] = zero4();
+    if (src) {
+      if (side == 0) {
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt)
+        for (int dt = 0; dt < DK / 16; ++dt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int d = 16 * dt + 4 * lg + i, j = jw0 + 16 * jt + li;
-            G0(dt, jt)[i] = src ? src[d * DV + j] : 0.f;
-          }
-    } else {
+          for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
-      for (int jt = 0; jt < DV / 16; ++jt)
+            for (int i = 0; i < 4; ++i)
+              G0(dt, jt)[i] = src[(16 * dt + 4 * lg + i) * DV + jw0 + 16 * jt + li];
+      } else {
 #pragma unroll
-        for (int it = 0; it < NI; ++it)
+        for (int jt = 0; jt < DV / 16; ++jt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = 16 * jt + 4 * lg + i, d = dw0 + 16 * it + li;
-            G1(jt, it)[i] = (MODE == 0 && src) ? src[d * DV + j] : 0.f;
-          }
+          for (int it = 0; it < NI; ++it)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              G1(jt, it)[i] = src[(dw0 + 16 * it + li) * DV + 16 * jt + 4 * lg + i];
+      }
     }
   }
   float alpha_total = 1.f;
@@ -166,46 +172,61 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
   int64_t r2_t0 = -1;  // chunk whose k.dk partials sit in R2P
   int r2_n = 0;
 
-  for (int64_t ci = c_end - 1; ci >= c_begin; --ci) {
-    const int64_t t0 = ci * TC;
-    const int n = (int)min<int64_t>(TC, T - t0);
-
-    __syncthreads();  // the previous chunk's LDS reads are done
-    if (MODE == 0 && r2_t0 >= 0 && tid < r2_n)
-      a.r2[bh * T + r2_t0 + tid] = R2P[tid] + R2P[64 + tid] + R2P[128 + tid] + R2P[192 + tid];
+  // DMA of chunk cj into a staging buffer: 1 KB row blocks spread over the
+  // waves, the 64 log decays (rows clamped to the chunk) by wave 0.
+  auto stage = [&](int64_t cj, unsigned char *buf) __attribute__((always_inline)) {
+    const int64_t tj = cj * TC;
+    const int nj = (int)min<int64_t>(TC, T - tj);
     for (int b = w; b < NBLK; b += BTHR / 64) {
       if (b < NBQ) {
-        dma_block<DK>(qh + t0 * DK, n, QS, b, lane);
+        dma_block<DK>(qh + tj * DK, nj, buf, b, lane);
       } else if (b < NBQ + NBD) {
-        dma_block<DV>(doh + t0 * DV, n, DOS, b - NBQ, lane);
+        dma_block<DV>(doh + tj * DV, nj, buf + B_DOS, b - NBQ, lane);
       } else if (b < NBQ + NBD + NBK) {
-        dma_block<DK>(kh + t0 * DK, n, KS, b - NBQ - NBD, lane);
+        dma_block<DK>(kh + tj * DK, nj, buf + B_KS, b - NBQ - NBD, lane);
       } else {
-        dma_block<DV>(vh + t0 * DV, n, VS, b - NBQ - NBD - NBK, lane);
+        dma_block<DV>(vh + tj * DV, nj, buf + B_VS, b - NBQ - NBD - NBK, lane);
       }
     }
-    float lv = 0.f;
-    if (w == 0) lv = lh[t0 + min(lane, n - 1)];
-    __builtin_amdgcn_s_waitcnt(0);
-    if (w == 0) {
-      // rows past the chunk: no decay, and lambda = 0 so that they add
-      // nothing to the state gradient
-      float c = lane < n ? lv : 0.f;
+    if (w == 0)
+      __builtin_amdgcn_global_load_lds(lh + tj + min(lane, nj - 1), (lds_void *)(buf + B_L), 4, 0,
+                                       0);
+  };
+
+  // One chunk from staging buffer `cur`, while the chunk before it streams
+  // into `nxt` (released by the barrier that ended the previous step).
+  auto step = [&](int64_t ci, unsigned char *cur, unsigned char *nxt)
+                  __attribute__((always_inline)) {
+    const int64_t t0 = ci * TC;
+    const int n = (int)min<int64_t>(TC, T - t0);
+    unsigned char *QS = cur;
+    unsigned char *DOS = cur + B_DOS;
+    unsigned char *KS = cur + B_KS;
+    unsigned char *VS = cur + B_VS;
+    const float *LC = reinterpret_cast<const float *>(cur + B_L);
+
+    if (ci > c_begin) stage(ci - 1, nxt);
+    if (MODE == 0 && r2_t0 >= 0 && tid < r2_n) {
+      float *r2row = a.r2 + bh * T + r2_t0;
+      r2row[tid] = R2P[tid] + R2P[64 + tid] + R2P[128 + tid] + R2P[192 + tid];
+    }
+    // In-chunk decays, one token per lane, computed by every wave (lanes
+    // are then read with cross-lane shuffles).  Rows past the chunk: no
+    // decay, and lambda = 0 so that they add nothing to the state gradient.
+    float c_l = lane < n ? LC[lane] : 0.f;
 #pragma unroll
-      for (int sh = 1; sh < 64; sh <<= 1) {
-        const float p = __shfl_up(c, sh, 64);
-        if (lane >= sh) c += p;
-      }
-      const float cl = __shfl(c, 63, 64);
-      CS[lane] = c;
-      LAM[lane] = lane < n ? expf(c) : 0.f;
-      GAM[lane] = expf(cl - c);
-      if (lane == 0) ALPHA[0] = expf(cl);
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const float p = __shfl_up(c_l, sh, 64);
+      if (lane >= sh) c_l += p;
     }
-    __syncthreads();
+    const float c_last = __shfl(c_l, 63, 64);
+    const float lam_l = lane < n ? expf(c_l) : 0.f;
+    const float gam_l = expf(c_last - c_l);
+    const float alpha = expf(c_last);
 
     if constexpr (MODE == 0) {
       // ---- masked score tiles, stored transposed: P[s][r] ----
+      FRESH_LANE();
       {
         unsigned char *PT = side == 0 ? P1 : P2;
         for (int t = wv; t < 12; t += 4) {
@@ -226,22 +247,24 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
             }
           }
           // acc[i] = X[r = 16 rt + 4 lg + i][s]; rows past the chunk are masked
-          const float cs = CS[s];
+          const float cs = __shfl(c_l, s, 64);
           bf16x4 pv;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 16 * rt + 4 * lg + i;
             float p = 0.f;
-            if (r >= s && r < n) p = acc[i] * __expf(CS[r] - cs);
+            const float cr = __shfl(c_l, r, 64);
+            if (r >= s && r < n) p = acc[i] * __expf(cr - cs);
             pv[i] = tobf(p);
           }
           *reinterpret_cast<bf16x4 *>(PT + swz_off<8>(s, 2 * rt + (lg >> 1)) + (lg & 1) * 8) = pv;
         }
       }
-      __syncthreads();
+      lds_barrier();  // score tiles visible; next chunk's DMA stays in flight
 
       if (side == 0) {
         // ---- dV^T[j][s] = gamma_s (G^T K^T)[j][s] + (dO^T P1)[j][s] ----
+        FRESH_LANE();
         bf16x8 gfrag[DK / 32][NJ];
 #pragma unroll
         for (int kk = 0; kk < DK / 32; ++kk)
@@ -255,7 +278,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           const int s = 16 * st + li;
-          const float gs = GAM[s];
+          const float gs = __shfl(gam_l, s, 64);
           bf16x8 kfrag[DK / 32];
 #pragma unroll
           for (int kk = 0; kk < DK / 32; ++kk)
@@ -285,6 +308,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
         }
       } else {
         // ---- dK^T[d][s] = gamma_s (G V^T)[d][s] + (Q^T P2)[d][s] ; r2_s = k_s . dk_s ----
+        FRESH_LANE();
         bf16x8 gfrag[DV / 32][NI];
 #pragma unroll
         for (int kk = 0; kk < DV / 32; ++kk)
@@ -298,7 +322,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           const int s = 16 * st + li;
-          const float gs = GAM[s];
+          const float gs = __shfl(gam_l, s, 64);
           bf16x8 vfrag[DV / 32];
 #pragma unroll
           for (int kk = 0; kk < DV / 32; ++kk)
@@ -338,7 +362,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     }
 
     // ---- state-gradient update (both copies): G <- alpha G + Q^T (lambda dO) ----
-    const float alpha = ALPHA[0];
+    FRESH_LANE();
     alpha_total *= alpha;
 #pragma unroll
     for (int x = 0; x < NG; ++x)
@@ -350,7 +374,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
       for (int kb = 0; kb < 2; ++kb) {
         float lam[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) lam[e] = LAM[32 * kb + 8 * lg + e];
+        for (int e = 0; e < 8; ++e) lam[e] = __shfl(lam_l, 32 * kb + 8 * lg + e, 64);
         bf16x8 db[NJ];  // (lambda dO) B operands: k = r, column j
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt) {
@@ -373,7 +397,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
       for (int kb = 0; kb < 2; ++kb) {
         float lam[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) lam[e] = LAM[32 * kb + 8 * lg + e];
+        for (int e = 0; e < 8; ++e) lam[e] = __shfl(lam_l, 32 * kb + 8 * lg + e, 64);
         bf16x8 qb[NI];  // (lambda Q) B operands: k = r, column d
 #pragma unroll
         for (int it = 0; it < NI; ++it) {
@@ -395,12 +419,20 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
       r2_t0 = t0;
       r2_n = n;
     }
-  }
-  if (MODE == 0 && r2_t0 >= 0) {
+    // the next chunk has landed; this chunk's buffer is free
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid < r2_n)
-      a.r2[bh * T + r2_t0 + tid] = R2P[tid] + R2P[64 + tid] + R2P[128 + tid] + R2P[192 + tid];
+  };
+
+  stage(c_end - 1, buf0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int64_t ci = c_end - 1; ci >= c_begin; ci -= 2) {
+    step(ci, buf0, buf1);
+    if (ci - 1 >= c_begin) step(ci - 1, buf1, buf0);
   }
+  if (MODE == 0 && r2_t0 >= 0 && tid < r2_n)
+    a.r2[bh * T + r2_t0 + tid] = R2P[tid] + R2P[64 + tid] + R2P[128 + tid] + R2P[192 + tid];
 
   // ---- segment outputs ----
   if constexpr (MODE == 0) {
@@ -431,6 +463,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
 
 #undef G0
 #undef G1
+#undef FRESH_LANE
 
 // Decay gradient of one segment of one sequence (one workgroup each):
 //   dl_u = B + sum_{t >= u, t in segment} (r1_t - r2_t),

@@ -32,6 +32,14 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS
+// operations, not for its global loads, stores or LDS DMA in flight (which
+// __syncthreads() would drain through its release fence).  For exchanging
+// data written with ds_write between waves.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
