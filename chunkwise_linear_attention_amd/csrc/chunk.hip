@@ -67,9 +67,8 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   constexpr int OFF_KS = OFF_QS + (MODE == 0 ? QB : 0);
   constexpr int OFF_VS = OFF_KS + QB;
   constexpr int OFF_PS = OFF_VS + VB;
-  constexpr int OFF_C = OFF_PS + (MODE == 0 ? 64 * 128 : 0);
-  constexpr int OFF_RD = OFF_C + 3 * 64 * 4 + 16;
-  constexpr int SMEM = OFF_RD + (MODE == 0 ? NWAVE * 64 * 4 : 0);
+  constexpr int OFF_RD = OFF_PS + (MODE == 0 ? 64 * 128 : 0);
+  constexpr int SMEM = OFF_RD + (MODE == 0 ? NWAVE * 64 * 4 : 16);
   // 1 KB DMA blocks per chunk: [Q (MODE 0) | K | V]
   constexpr int NBQ = MODE == 0 ? DK / 8 : 0, NBK = DK / 8, NBV = DV / 8;
   constexpr int NBLK = NBQ + NBK + NBV;
@@ -78,15 +77,22 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   unsigned char *KS = smem + OFF_KS;
   unsigned char *VS = smem + OFF_VS;
   unsigned char *PS = smem + OFF_PS;
-  float *CS = reinterpret_cast<float *>(smem + OFF_C);
-  float *LAM = CS + 64;
-  float *GAM = CS + 128;
-  float *ALPHA = CS + 192;
-  float *RD = reinterpret_cast<float *>(smem + OFF_RD);
+  float *RD = reinterpret_cast<float *>(smem + OFF_RD);  // xdot partial sums [w][row]
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
-  const int li = lane & 15, lg = lane >> 4;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  int li = lane & 15, lg = lane >> 4;
+  // Re-derive the lane coordinates behind an empty asm at the start of each
+  // phase, so that the compiler forms LDS addresses next to their use instead
+  // of hoisting all of them out of the chunk loop (which exhausts registers).
+#define FRESH_LANE()             \
+  do {                           \
+    int l_ = lane;               \
+    asm volatile("" : "+v"(l_)); \
+    li = l_ & 15;                \
+    lg = l_ >> 4;                \
+  } while (0)
   const int64_t bh = blockIdx.x % a.nh;
   const int64_t seg = blockIdx.x / a.nh;
   const int64_t T = a.T;
@@ -125,12 +131,20 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
         }
   }
   float alpha_total = 1.f;
+  int64_t rd_t0 = -1;  // chunk whose xdot partials sit in RD
+  int rd_n = 0;
 
   for (int64_t ci = c_begin; ci < c_end; ++ci) {
     const int64_t t0 = ci * TC;
     const int n = (int)min<int64_t>(TC, T - t0);
 
-    __syncthreads();  // the previous chunk's LDS reads are done
+    lds_barrier();  // the previous chunk's LDS reads (and RD writes) are done
+    if (MODE == 0 && rd_t0 >= 0 && tid < rd_n) {
+      float s = 0.f;
+#pragma unroll
+      for (int u = 0; u < NWAVE; ++u) s += RD[u * 64 + tid];
+      a.rdot[bh * T + rd_t0 + tid] = s;
+    }
     // stage Q, K, V straight into LDS
     for (int b = w; b < NBLK; b += NWAVE) {
       if (b < NBQ) {
@@ -152,27 +166,26 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
                                                           16 * jt + 4 * lg);
       }
     }
-    float lv = 0.f;
-    if (w == 0) lv = lh[t0 + min(lane, n - 1)];
+    const float lv = lh[t0 + min(lane, n - 1)];
     __builtin_amdgcn_s_waitcnt(0);
-    if (w == 0) {
-      // c, lambda, gamma (zero for rows past the chunk: they write nothing), alpha
-      float c = lane < n ? lv : 0.f;
+    lds_barrier();  // every wave's DMA has landed
+    // In-chunk decays, one token per lane, computed by every wave and read
+    // with cross-lane shuffles.  Rows past the chunk: gamma = 0, so that they
+    // add nothing to the state.
+    float c_l = lane < n ? lv : 0.f;
 #pragma unroll
-      for (int sh = 1; sh < 64; sh <<= 1) {
-        const float p = __shfl_up(c, sh, 64);
-        if (lane >= sh) c += p;
-      }
-      const float cl = __shfl(c, 63, 64);
-      CS[lane] = c;
-      LAM[lane] = expf(c);
-      GAM[lane] = lane < n ? expf(cl - c) : 0.f;
-      if (lane == 0) ALPHA[0] = expf(cl);
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const float p = __shfl_up(c_l, sh, 64);
+      if (lane >= sh) c_l += p;
     }
-    __syncthreads();
+    const float c_last = __shfl(c_l, 63, 64);
+    const float lam_l = expf(c_l);
+    const float gam_l = lane < n ? expf(c_last - c_l) : 0.f;
+    const float alpha = expf(c_last);
 
     if constexpr (MODE == 0) {
       // ---- masked transposed score tiles -> P[r][s] (bf16) ----
+      FRESH_LANE();
       for (int t = w; t < 12; t += NWAVE) {
         const int rt = tile_rt(t), st = tile_st(t);
         const int r = 16 * rt + li;
@@ -184,20 +197,22 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
                        lds_frag<NCK>(QS, r, 4 * kk + lg), acc);
         }
         // acc[i] = (K Q^T)[s = 16 st + 4 lg + i][r]; keys past the chunk are masked
-        const float cr = CS[r];
+        const float cr = __shfl(c_l, r, 64);
         bf16x4 pv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = 16 * st + 4 * lg + i;
+          const float cs = __shfl(c_l, s, 64);
           float p = 0.f;
-          if (s <= r && s < n) p = acc[i] * __expf(cr - CS[s]);
+          if (s <= r && s < n) p = acc[i] * __expf(cr - cs);
           pv[i] = tobf(p);
         }
         *reinterpret_cast<bf16x4 *>(PS + swz_off<8>(r, 2 * st + (lg >> 1)) + (lg & 1) * 8) = pv;
       }
-      __syncthreads();
+      lds_barrier();
 
       // ---- output: O^T[j][r] = lambda_r (S^T Q^T)[j][r] + (V^T P^T)[j][r] ----
+      FRESH_LANE();
       bf16x8 vfrag[NJ][2];  // A operands V^T: row j, k = s
 #pragma unroll
       for (int jt = 0; jt < NJ; ++jt)
@@ -213,7 +228,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const int rr = 16 * rt + li;
-        const float lam = LAM[rr];
+        const float lam = __shfl(lam_l, rr, 64);
         bf16x8 qfrag[DK / 32];  // Q^T B operands, same k permutation
 #pragma unroll
         for (int kk = 0; kk < DK / 32; ++kk)
@@ -253,18 +268,13 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
         }
       }
       if (a.xdot) {
-        __syncthreads();
-        if (tid < n) {
-          float s = 0.f;
-#pragma unroll
-          for (int u = 0; u < NWAVE; ++u) s += RD[u * 64 + tid];
-          a.rdot[bh * T + t0 + tid] = s;
-        }
+        rd_t0 = t0;
+        rd_n = n;
       }
     }
 
     // ---- state update: S <- alpha S + K^T (gamma V) ----
-    const float alpha = ALPHA[0];
+    FRESH_LANE();
     alpha_total *= alpha;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -276,7 +286,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
       float gam[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gam[e] = GAM[32 * kb + 8 * lg + e];
+      for (int e = 0; e < 8; ++e) gam[e] = __shfl(gam_l, 32 * kb + 8 * lg + e, 64);
       bf16x8 vb[NJ];  // (gamma V) B operands: k = s, column j
 #pragma unroll
       for (int jt = 0; jt < NJ; ++jt) {
@@ -292,6 +302,16 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt) S_acc[dt][jt] = mfma(ka, vb[jt], S_acc[dt][jt]);
       }
+    }
+  }
+
+  if (MODE == 0 && rd_t0 >= 0) {
+    lds_barrier();
+    if (tid < rd_n) {
+      float s = 0.f;
+#pragma unroll
+      for (int u = 0; u < NWAVE; ++u) s += RD[u * 64 + tid];
+      a.rdot[bh * T + rd_t0 + tid] = s;
     }
   }
 
@@ -323,6 +343,8 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     if (tid == 0) a.aloc[seg * a.nh + bh] = alpha_total;
   }
 }
+
+#undef FRESH_LANE
 
 // Incoming state of every segment from the segment pairs (alpha_p, S_p):
 // S_in(0) = S0, S_in(p+1) = alpha_p S_in(p) + S_p (ZTF "Splitting one

@@ -206,10 +206,13 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     const float *LC = reinterpret_cast<const float *>(cur + B_L);
 
     if (ci > c_begin) stage(ci - 1, nxt);
-    if (MODE == 0 && r2_t0 >= 0 && tid < r2_n) {
-      float *r2row = a.r2 + bh * T + r2_t0;
-      r2row[tid] = R2P[tid] + R2P[64 + tid] + R2P[128 + tid] + R2P[192 + tid];
-    }
+    // the previous chunk's k.dk sums, stored at the end of this step (a store
+    // issued here would hold its data register while the DMA is in flight)
+    float r2_sum = 0.f;
+    const int64_t r2_row = r2_t0;
+    const int r2_prev_n = r2_n;
+    if (MODE == 0 && r2_t0 >= 0 && tid < r2_n)
+      r2_sum = R2P[tid] + R2P[64 + tid] + R2P[128 + tid] + R2P[192 + tid];
     // In-chunk decays, one token per lane, computed by every wave (lanes
     // are then read with cross-lane shuffles).  Rows past the chunk: no
     // decay, and lambda = 0 so that they add nothing to the state gradient.
@@ -419,6 +422,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
       r2_t0 = t0;
       r2_n = n;
     }
+    if (MODE == 0 && r2_row >= 0 && tid < r2_prev_n) a.r2[bh * T + r2_row + tid] = r2_sum;
     // the next chunk has landed; this chunk's buffer is free
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
