@@ -63,21 +63,24 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   constexpr int NDT = DK / 16;         // 16-row tiles of the state
   constexpr int NCK = DK / 8, NCV = DV / 8;  // 16-byte chunks per row
   constexpr int QB = 64 * DK * 2, VB = 64 * DV * 2;
-  constexpr int OFF_QS = 0;
-  constexpr int OFF_KS = OFF_QS + (MODE == 0 ? QB : 0);
-  constexpr int OFF_VS = OFF_KS + QB;
-  constexpr int OFF_PS = OFF_VS + VB;
-  constexpr int OFF_RD = OFF_PS + (MODE == 0 ? 64 * 128 : 0);
-  constexpr int SMEM = OFF_RD + (MODE == 0 ? NWAVE * 64 * 4 : 16);
-  // 1 KB DMA blocks per chunk: [Q (MODE 0) | K | V]
+  // Staging buffer [Q | K | V | X | l]: Q and X (the optional xdot rows) in
+  // MODE 0 only.  It is double-buffered (the next chunk streams in by DMA
+  // while this one is used) when two workgroups per CU still fit in LDS;
+  // the two buffers are separate arrays so that the compiler can tell the
+  // DMA target from the buffer being read.
+  constexpr int B_KS = MODE == 0 ? QB : 0;
+  constexpr int B_VS = B_KS + QB;
+  constexpr int B_XS = B_VS + VB;
+  constexpr int B_L = B_XS + (MODE == 0 ? VB : 0);
+  constexpr int BUF = B_L + 64 * 4;
+  constexpr int PSB = MODE == 0 ? 64 * 128 : 16;
+  constexpr int RDB = MODE == 0 ? NWAVE * 64 : 4;
+  constexpr bool DB = 2 * BUF + PSB + 4 * RDB <= 80 * 1024;
   constexpr int NBQ = MODE == 0 ? DK / 8 : 0, NBK = DK / 8, NBV = DV / 8;
-  constexpr int NBLK = NBQ + NBK + NBV;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
-  unsigned char *QS = smem + OFF_QS;
-  unsigned char *KS = smem + OFF_KS;
-  unsigned char *VS = smem + OFF_VS;
-  unsigned char *PS = smem + OFF_PS;
-  float *RD = reinterpret_cast<float *>(smem + OFF_RD);  // xdot partial sums [w][row]
+  __shared__ __attribute__((aligned(1024))) unsigned char buf0[BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf1[DB ? BUF : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char PS[PSB];
+  __shared__ float RD[RDB];  // xdot partial sums [w][row]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -100,79 +103,92 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   const int64_t c_begin = seg * a.seg_chunks;
   const int64_t c_end = min(nchunks, c_begin + a.seg_chunks);
   const int j0 = w * (DV / 4);  // first value column of this wave
+  const bool has_x = MODE == 0 && a.xdot != nullptr;
+  const int nblk = NBQ + NBK + NBV + (has_x ? NBV : 0);
 
   const uint16_t *qh = a.q + bh * T * DK;
   const uint16_t *kh = a.k + bh * T * DK;
   const uint16_t *vh = a.v + bh * T * DV;
+  const uint16_t *xh = has_x ? a.xdot + bh * T * DV : nullptr;
   const float *lh = a.l + bh * T;
 
   // S_acc[dt][jt][i] = S[16 dt + 4 lg + i][j0 + 16 jt + li]
   f32x4 S_acc[NDT][NJ];
-  {
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) S_acc[dt][jt] = zero4();
+  if (MODE == 0) {
     const float *src = nullptr;
     bool trans = false;
-    if (MODE == 0) {
-      if (seg == 0) {
-        src = a.S0 ? a.S0 + bh * DK * DV : nullptr;
-        trans = a.s0_trans;
-      } else {
-        src = a.Sin + ((seg - 1) * a.nh + bh) * DK * DV;
-        trans = a.slot_trans;
-      }
+    if (seg == 0) {
+      src = a.S0 ? a.S0 + bh * DK * DV : nullptr;
+      trans = a.s0_trans;
+    } else {
+      src = a.Sin + ((seg - 1) * a.nh + bh) * DK * DV;
+      trans = a.slot_trans;
     }
+    if (src) {
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int jt = 0; jt < NJ; ++jt)
+        for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = 16 * dt + 4 * lg + i, j = j0 + 16 * jt + li;
-          S_acc[dt][jt][i] = src ? src[trans ? j * DK + d : d * DV + j] : 0.f;
-        }
+          for (int i = 0; i < 4; ++i) {
+            const int d = 16 * dt + 4 * lg + i, j = j0 + 16 * jt + li;
+            S_acc[dt][jt][i] = src[trans ? j * DK + d : d * DV + j];
+          }
+    }
   }
   float alpha_total = 1.f;
   int64_t rd_t0 = -1;  // chunk whose xdot partials sit in RD
   int rd_n = 0;
 
-  for (int64_t ci = c_begin; ci < c_end; ++ci) {
-    const int64_t t0 = ci * TC;
-    const int n = (int)min<int64_t>(TC, T - t0);
+  // DMA of chunk cj into a staging buffer: 1 KB row blocks spread over the
+  // waves, the 64 log decays (rows clamped to the chunk) by wave 0.
+  auto stage = [&](int64_t cj, unsigned char *buf) __attribute__((always_inline)) {
+    const int64_t tj = cj * TC;
+    const int nj = (int)min<int64_t>(TC, T - tj);
+    for (int b = w; b < nblk; b += NWAVE) {
+      if (b < NBQ) {
+        dma_block<DK>(qh + tj * DK, nj, buf, b, lane);
+      } else if (b < NBQ + NBK) {
+        dma_block<DK>(kh + tj * DK, nj, buf + B_KS, b - NBQ, lane);
+      } else if (b < NBQ + NBK + NBV) {
+        dma_block<DV>(vh + tj * DV, nj, buf + B_VS, b - NBQ - NBK, lane);
+      } else {
+        dma_block<DV>(xh + tj * DV, nj, buf + B_XS, b - NBQ - NBK - NBV, lane);
+      }
+    }
+    if (w == 0)
+      __builtin_amdgcn_global_load_lds(lh + tj + min(lane, nj - 1), (lds_void *)(buf + B_L), 4, 0,
+                                       0);
+  };
 
-    lds_barrier();  // the previous chunk's LDS reads (and RD writes) are done
+  // the xdot sums of the previous chunk, from RD
+  auto rd_sum = [&]() __attribute__((always_inline)) -> float {
+    float s = 0.f;
     if (MODE == 0 && rd_t0 >= 0 && tid < rd_n) {
-      float s = 0.f;
 #pragma unroll
       for (int u = 0; u < NWAVE; ++u) s += RD[u * 64 + tid];
-      a.rdot[bh * T + rd_t0 + tid] = s;
     }
-    // stage Q, K, V straight into LDS
-    for (int b = w; b < NBLK; b += NWAVE) {
-      if (b < NBQ) {
-        dma_block<DK>(qh + t0 * DK, n, QS, b, lane);
-      } else if (b < NBQ + NBK) {
-        dma_block<DK>(kh + t0 * DK, n, KS, b - NBQ, lane);
-      } else {
-        dma_block<DV>(vh + t0 * DV, n, VS, b - NBQ - NBK, lane);
-      }
-    }
-    bf16x4 xv[4][NJ];  // the xdot values this lane multiplies
-    if (MODE == 0 && a.xdot) {
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int row = min(16 * rt + li, n - 1);
-#pragma unroll
-        for (int jt = 0; jt < NJ; ++jt)
-          xv[rt][jt] = *reinterpret_cast<const bf16x4 *>(a.xdot + (bh * T + t0 + row) * DV + j0 +
-                                                          16 * jt + 4 * lg);
-      }
-    }
-    const float lv = lh[t0 + min(lane, n - 1)];
-    __builtin_amdgcn_s_waitcnt(0);
-    lds_barrier();  // every wave's DMA has landed
+    return s;
+  };
+
+  // The work on one staged chunk.
+  auto compute = [&](int64_t ci, const unsigned char *cur) __attribute__((always_inline)) {
+    const int64_t t0 = ci * TC;
+    const int n = (int)min<int64_t>(TC, T - t0);
+    const unsigned char *QS = cur;
+    const unsigned char *KS = cur + B_KS;
+    const unsigned char *VS = cur + B_VS;
+    const unsigned char *XS = cur + B_XS;
+    const float *LC = reinterpret_cast<const float *>(cur + B_L);
+
     // In-chunk decays, one token per lane, computed by every wave and read
     // with cross-lane shuffles.  Rows past the chunk: gamma = 0, so that they
     // add nothing to the state.
-    float c_l = lane < n ? lv : 0.f;
+    float c_l = lane < n ? LC[lane] : 0.f;
 #pragma unroll
     for (int sh = 1; sh < 64; sh <<= 1) {
       const float p = __shfl_up(c_l, sh, 64);
@@ -249,25 +265,26 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
           for (int kb = 0; kb < 2; ++kb)
             if (kb <= (rt >> 1)) acc = mfma(vfrag[jt][kb], pfrag[kb], acc);
           // acc[i] = O[row rr][col j0 + 16 jt + 4 lg + i]
+          const int jc = j0 + 16 * jt + 4 * lg;
           if (rr < n) {
-            const int jc = j0 + 16 * jt + 4 * lg;
             bf16x4 ov;
 #pragma unroll
             for (int i = 0; i < 4; ++i) ov[i] = tobf(acc[i]);
             *reinterpret_cast<bf16x4 *>(a.o + (bh * T + t0 + rr) * DV + jc) = ov;
-            if (a.xdot) {
+          }
+          if (has_x) {
+            const bf16x4 xv = lds_half<NCV>(XS, rr, jc);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) rdp += tof(xv[rt][jt][i]) * acc[i];
-            }
+            for (int i = 0; i < 4; ++i) rdp += tof(xv[i]) * acc[i];
           }
         }
-        if (a.xdot) {
+        if (has_x) {
           rdp += __shfl_xor(rdp, 16, 64);
           rdp += __shfl_xor(rdp, 32, 64);
           if (lg == 0) RD[w * 64 + rr] = rdp;
         }
       }
-      if (a.xdot) {
+      if (has_x) {
         rd_t0 = t0;
         rd_n = n;
       }
@@ -303,16 +320,46 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
         for (int jt = 0; jt < NJ; ++jt) S_acc[dt][jt] = mfma(ka, vb[jt], S_acc[dt][jt]);
       }
     }
-  }
+  };
 
-  if (MODE == 0 && rd_t0 >= 0) {
-    lds_barrier();
-    if (tid < rd_n) {
-      float s = 0.f;
-#pragma unroll
-      for (int u = 0; u < NWAVE; ++u) s += RD[u * 64 + tid];
-      a.rdot[bh * T + rd_t0 + tid] = s;
+  if constexpr (DB) {
+    // one step: chunk ci from `cur` while chunk ci + 1 streams into `nxt`
+    auto step = [&](int64_t ci, unsigned char *cur, unsigned char *nxt)
+                    __attribute__((always_inline)) {
+      if (ci + 1 < c_end) stage(ci + 1, nxt);
+      // the previous chunk's xdot sums, stored at the end of the step (a
+      // store issued here would hold its data register while the DMA is in
+      // flight)
+      const float rs = rd_sum();
+      const int64_t rs_t0 = rd_t0;
+      const int rs_n = rd_n;
+      compute(ci, cur);
+      if (MODE == 0 && rs_t0 >= 0 && tid < rs_n) a.rdot[bh * T + rs_t0 + tid] = rs;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // the next chunk has landed; this chunk's buffer is free
+    };
+    stage(c_begin, buf0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int64_t ci = c_begin; ci < c_end; ci += 2) {
+      step(ci, buf0, buf1);
+      if (ci + 1 < c_end) step(ci + 1, buf1, buf0);
     }
+  } else {
+    for (int64_t ci = c_begin; ci < c_end; ++ci) {
+      lds_barrier();  // the previous chunk's LDS reads (and RD writes) are done
+      const float rs = rd_sum();
+      if (MODE == 0 && rd_t0 >= 0 && tid < rd_n) a.rdot[bh * T + rd_t0 + tid] = rs;
+      stage(ci, buf0);
+      __builtin_amdgcn_s_waitcnt(0);
+      lds_barrier();  // every wave's DMA has landed
+      compute(ci, buf0);
+    }
+    lds_barrier();
+  }
+  {
+    const float rs = rd_sum();
+    if (MODE == 0 && rd_t0 >= 0 && tid < rd_n) a.rdot[bh * T + rd_t0 + tid] = rs;
   }
 
   // ---- segment outputs ----
@@ -343,7 +390,6 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     if (tid == 0) a.aloc[seg * a.nh + bh] = alpha_total;
   }
 }
-
 #undef FRESH_LANE
 
 // Incoming state of every segment from the segment pairs (alpha_p, S_p):
@@ -433,7 +479,7 @@ FwdWs fwd_ws(void *base, int64_t nh, int64_t P, int64_t DK, int64_t DV) {
 // and of the reverse pass (G at segment ends), q . dq and k . dk per token,
 // the final state S_T, and the boundary terms <S, G> per segment
 struct BwdWs {
-  FwdWs seg;   // dQ pass: slots p = S at the end of segment p
+  FwdWs seg;   // dQ pass: slots p = S^T at the end of segment p
   FwdWs gseg;  // reverse pass: slots p = G at the end of segment p
   float *r1, *r2, *ST, *Bnd;
   size_t bytes;
@@ -536,10 +582,12 @@ hipError_t launch_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t
   fa.l = l;
   fa.S0 = S0;
   fa.s0_trans = 1;
-  fa.slot_trans = 1;  // segment states kept as S (not S^T), like the G slots
+  // segment states and S_T stay in this pass's own layout (S^T), written
+  // and read coalesced; the dK/dV pass reads them against G^T
+  fa.slot_trans = 0;
   fa.o = dq;
   fa.ST = dST ? w.ST : nullptr;
-  fa.st_trans = 1;
+  fa.st_trans = 0;
   fa.xdot = q;
   fa.rdot = w.r1;
   fa.Sloc = w.seg.Sloc;

@@ -36,8 +36,8 @@ struct BwdArgs {
   float *dS0;                       // [nh, DK, DV] or NULL
   float *Gloc;                      // state-only pass: [P-1, nh, DK, DV] (segment p in slot p-1)
   float *aloc;                      // state-only pass: [P-1, nh]
-  const float *Sseg;                // [P-1, nh, DK, DV]: S at the end of segments 0..P-2
-  const float *STb;                 // [nh, DK, DV]: S_T (NULL when there is no dS_T)
+  const float *Sseg;                // [P-1, nh, DV, DK]: S^T at the end of segments 0..P-2
+  const float *STb;                 // [nh, DV, DK]: S_T^T (NULL when there is no dS_T)
   float *Bnd;                       // [P, nh]: <S, G> at the end of each segment
   int64_t nh, T, seg_chunks, P;
 };
