@@ -219,18 +219,23 @@ def bench_chunk(args, torch, cla, wl, steps, warmup, cpu_heads=0):
     wsf = cla.chunk_workspace_bytes(B, H, T, DK, DV, False)
     wsb = cla.chunk_workspace_bytes(B, H, T, DK, DV, True)
     ws = torch.empty(max(wsf, wsb, 1), dtype=torch.uint8, device=dev)
+    # the training path: the forward saves the states the backward's
+    # segments start from (cla_chunk_fwd_saved / cla_chunk_bwd_saved)
+    nsv = int(L.cla_chunk_saved_bytes(B, H, T, DK, DV, 64))
+    saved = torch.empty(max(nsv, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     P = lambda t: None if t is None else t.data_ptr()
 
     def fwd():
-        st = L.cla_chunk_fwd(P(q), P(k), P(v), P(l), P(S0), P(o), P(ST), B, H, T, DK, DV, 64,
-                             P(ws), ws.numel(), stream)
+        st = L.cla_chunk_fwd_saved(P(q), P(k), P(v), P(l), P(S0), P(o), P(ST), P(saved),
+                                   saved.numel(), B, H, T, DK, DV, 64, P(ws), ws.numel(), stream)
         if st:
             raise RuntimeError(L.cla_status_string(st))
 
     def bwd():
-        st = L.cla_chunk_bwd(P(q), P(k), P(v), P(l), P(S0), P(dO), P(dST), P(dq), P(dk), P(dv),
-                             P(dl), P(dS0), B, H, T, DK, DV, 64, P(ws), ws.numel(), stream)
+        st = L.cla_chunk_bwd_saved(P(q), P(k), P(v), P(l), P(S0), P(dO), P(dST), P(saved),
+                                   saved.numel(), P(dq), P(dk), P(dv), P(dl), P(dS0), B, H, T,
+                                   DK, DV, 64, P(ws), ws.numel(), stream)
         if st:
             raise RuntimeError(L.cla_status_string(st))
 
@@ -288,7 +293,8 @@ def bench_chunk(args, torch, cla, wl, steps, warmup, cpu_heads=0):
                      "path_roofline_frac": round(t_roof / (ms_step * 1e-3), 4),
                      "mfma_util": round(path_flops / (ms_step * 1e-3) / (pm.PEAK_BF16_TFLOPS * 1e12), 4),
                      "hbm_GBps_path": round(path_bytes / (ms_step * 1e-3) / 1e9, 1),
-                     "workspace_bytes": [wsf, wsb]}}
+                     "workspace_bytes": [wsf, wsb], "saved_state_bytes": nsv,
+                     "path": "cla_chunk_fwd_saved + cla_chunk_bwd_saved"}}
     res["cpu_baseline"] = cpu_baseline_chunk(ci, cpu_heads) if cpu_heads else None
     del q, k, v, l, S0, dO, dST, o, ST, dq, dk, dv, dl, dS0, ws
     torch.cuda.empty_cache()

@@ -8,6 +8,10 @@ step of the computation runs in the library's HIP kernels.
     da, db, dh0        = scan_bwd(a, h, h0, dh, dhT=None)
     o, ST              = chunked_linear_attn(q, k, v, log_decay, S0=None)
     dq, dk, dv, dl, dS0 = chunked_linear_attn_bwd(q, k, v, log_decay, S0, dO, dST=None)
+
+    # training: the forward keeps the states the backward's segments start from
+    o, S_T, saved = chunked_linear_attn(q, k, v, log_decay, S0, save_states=True)
+    dq, dk, dv, dl, dS0 = chunked_linear_attn_bwd(q, k, v, log_decay, S0, dO, saved=saved)
 """
 
 from ._lib import ClaError, lib  # noqa: F401
@@ -18,7 +22,8 @@ from .api import (  # noqa: F401
     scan_bwd,
     scan_workspace_bytes,
     chunk_workspace_bytes,
+    chunk_saved_bytes,
 )
 
 __all__ = ["scan", "scan_bwd", "chunked_linear_attn", "chunked_linear_attn_bwd",
-           "scan_workspace_bytes", "chunk_workspace_bytes", "ClaError"]
+           "scan_workspace_bytes", "chunk_workspace_bytes", "chunk_saved_bytes", "ClaError"]

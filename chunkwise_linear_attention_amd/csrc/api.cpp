@@ -123,11 +123,17 @@ size_t cla_chunk_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t DK,
   return backward ? plan.ws_bwd : plan.ws_fwd;
 }
 
-int cla_chunk_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                  const float *log_decay, const float *S0, uint16_t *o,
-                  float *ST, int64_t B, int64_t H, int64_t T, int64_t DK,
-                  int64_t DV, int64_t chunk, void *workspace,
-                  size_t workspace_bytes, cla_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward with an optional saved-state output (`saved_bytes` is ignored
+// when `with_saved` is false).
+int chunk_fwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                   const float *log_decay, const float *S0, uint16_t *o, float *ST,
+                   bool with_saved, float *saved, size_t saved_bytes, int64_t B, int64_t H,
+                   int64_t T, int64_t DK, int64_t DV, int64_t chunk, void *workspace,
+                   size_t workspace_bytes, cla_stream_t stream) {
   if (B < 0 || H < 0 || T < 0 || DK < 0 || DV < 0 || chunk < 0) return CLA_ERR_BAD_SHAPE;
   if (!supported_head_dim(DK) || !supported_head_dim(DV) || chunk != 64)
     return CLA_ERR_UNSUPPORTED;
@@ -141,25 +147,26 @@ int cla_chunk_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   const cla::ChunkPlan plan = cla::plan_chunk(B, H, T, DK, DV);
   if (plan.ws_fwd > 0 && (!workspace || workspace_bytes < plan.ws_fwd))
     return CLA_ERR_WORKSPACE;
+  const size_t sv = with_saved ? plan.saved_bytes : 0;
+  if (sv > 0 && (!saved || saved_bytes < sv)) return CLA_ERR_WORKSPACE;
   const Range ws{plan.ws_fwd ? workspace : nullptr, plan.ws_fwd};
   if (any_alias({{q, qk}, {k, qk}, {v, vv}, {log_decay, ll}, {S0, ss}},
-                {{o, vv}, {ST, ss}, ws}))
+                {{o, vv}, {ST, ss}, ws, {sv ? saved : nullptr, sv}}))
     return CLA_ERR_ALIAS;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (T == 0)
     return ST ? hip_status(cla::launch_copy_or_zero(ST, S0, (int64_t)(nh * DK * DV), s))
               : CLA_OK;
-  return hip_status(cla::launch_chunk_fwd(q, k, v, log_decay, S0, o, ST, B, H, T, DK,
-                                          DV, plan, workspace, s));
+  return hip_status(cla::launch_chunk_fwd(q, k, v, log_decay, S0, o, ST, sv ? saved : nullptr,
+                                          B, H, T, DK, DV, plan, workspace, s));
 }
 
-int cla_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                  const float *log_decay, const float *S0, const uint16_t *dO,
-                  const float *dST, uint16_t *dq, uint16_t *dk, uint16_t *dv,
-                  float *dlog_decay, float *dS0, int64_t B, int64_t H,
-                  int64_t T, int64_t DK, int64_t DV, int64_t chunk,
-                  void *workspace, size_t workspace_bytes,
-                  cla_stream_t stream) {
+int chunk_bwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                   const float *log_decay, const float *S0, const uint16_t *dO,
+                   const float *dST, bool with_saved, const float *saved, size_t saved_bytes,
+                   uint16_t *dq, uint16_t *dk, uint16_t *dv, float *dlog_decay, float *dS0,
+                   int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV, int64_t chunk,
+                   void *workspace, size_t workspace_bytes, cla_stream_t stream) {
   if (B < 0 || H < 0 || T < 0 || DK < 0 || DV < 0 || chunk < 0) return CLA_ERR_BAD_SHAPE;
   if (!supported_head_dim(DK) || !supported_head_dim(DV) || chunk != 64)
     return CLA_ERR_UNSUPPORTED;
@@ -175,17 +182,72 @@ int cla_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   const cla::ChunkPlan plan = cla::plan_chunk(B, H, T, DK, DV);
   if (plan.ws_bwd > 0 && (!workspace || workspace_bytes < plan.ws_bwd))
     return CLA_ERR_WORKSPACE;
+  const size_t sv = with_saved ? plan.saved_bytes : 0;
+  if (sv > 0 && (!saved || saved_bytes < sv)) return CLA_ERR_WORKSPACE;
   const Range ws{plan.ws_bwd ? workspace : nullptr, plan.ws_bwd};
-  if (any_alias({{q, qk}, {k, qk}, {v, vv}, {log_decay, ll}, {S0, ss}, {dO, vv}, {dST, ss}},
+  if (any_alias({{q, qk}, {k, qk}, {v, vv}, {log_decay, ll}, {S0, ss}, {dO, vv}, {dST, ss},
+                 {sv ? saved : nullptr, sv}},
                 {{dq, qk}, {dk, qk}, {dv, vv}, {dlog_decay, ll}, {dS0, ss}, ws}))
     return CLA_ERR_ALIAS;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (T == 0)
     return dS0 ? hip_status(cla::launch_copy_or_zero(dS0, dST, (int64_t)(nh * DK * DV), s))
                : CLA_OK;
-  return hip_status(cla::launch_chunk_bwd(q, k, v, log_decay, S0, dO, dST, dq, dk, dv,
-                                          dlog_decay, dS0, B, H, T, DK, DV, plan,
-                                          workspace, s));
+  return hip_status(cla::launch_chunk_bwd(q, k, v, log_decay, S0, dO, dST,
+                                          sv ? saved : nullptr, dq, dk, dv, dlog_decay, dS0,
+                                          B, H, T, DK, DV, plan, workspace, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int cla_chunk_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                  const float *log_decay, const float *S0, uint16_t *o,
+                  float *ST, int64_t B, int64_t H, int64_t T, int64_t DK,
+                  int64_t DV, int64_t chunk, void *workspace,
+                  size_t workspace_bytes, cla_stream_t stream) {
+  return chunk_fwd_impl(q, k, v, log_decay, S0, o, ST, false, nullptr, 0, B, H, T, DK, DV,
+                        chunk, workspace, workspace_bytes, stream);
+}
+
+int cla_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                  const float *log_decay, const float *S0, const uint16_t *dO,
+                  const float *dST, uint16_t *dq, uint16_t *dk, uint16_t *dv,
+                  float *dlog_decay, float *dS0, int64_t B, int64_t H,
+                  int64_t T, int64_t DK, int64_t DV, int64_t chunk,
+                  void *workspace, size_t workspace_bytes,
+                  cla_stream_t stream) {
+  return chunk_bwd_impl(q, k, v, log_decay, S0, dO, dST, false, nullptr, 0, dq, dk, dv,
+                        dlog_decay, dS0, B, H, T, DK, DV, chunk, workspace, workspace_bytes,
+                        stream);
+}
+
+size_t cla_chunk_saved_bytes(int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV,
+                             int64_t chunk) {
+  if (B < 0 || H < 0 || T < 0) return 0;
+  if (!supported_head_dim(DK) || !supported_head_dim(DV) || chunk != 64) return 0;
+  return cla::plan_chunk(B, H, T, DK, DV).saved_bytes;
+}
+
+int cla_chunk_fwd_saved(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        const float *log_decay, const float *S0, uint16_t *o, float *ST,
+                        float *saved, size_t saved_bytes, int64_t B, int64_t H, int64_t T,
+                        int64_t DK, int64_t DV, int64_t chunk, void *workspace,
+                        size_t workspace_bytes, cla_stream_t stream) {
+  return chunk_fwd_impl(q, k, v, log_decay, S0, o, ST, true, saved, saved_bytes, B, H, T, DK,
+                        DV, chunk, workspace, workspace_bytes, stream);
+}
+
+int cla_chunk_bwd_saved(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        const float *log_decay, const float *S0, const uint16_t *dO,
+                        const float *dST, const float *saved, size_t saved_bytes, uint16_t *dq,
+                        uint16_t *dk, uint16_t *dv, float *dlog_decay, float *dS0, int64_t B,
+                        int64_t H, int64_t T, int64_t DK, int64_t DV, int64_t chunk,
+                        void *workspace, size_t workspace_bytes, cla_stream_t stream) {
+  return chunk_bwd_impl(q, k, v, log_decay, S0, dO, dST, true, saved, saved_bytes, dq, dk, dv,
+                        dlog_decay, dS0, B, H, T, DK, DV, chunk, workspace, workspace_bytes,
+                        stream);
 }
 
 }  // extern "C"

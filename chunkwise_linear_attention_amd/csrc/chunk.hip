@@ -320,6 +320,17 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
         for (int jt = 0; jt < NJ; ++jt) S_acc[dt][jt] = mfma(ka, vb[jt], S_acc[dt][jt]);
       }
     }
+    // the state the backward's segment ci / save_every starts from
+    if (MODE == 0 && a.saved && (ci + 1) % a.save_every == 0 && ci + 1 < nchunks) {
+      float *dst = a.saved + (((ci + 1) / a.save_every - 1) * a.nh + bh) * DK * DV;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            dst[(16 * dt + 4 * lg + i) * DV + j0 + 16 * jt + li] = S_acc[dt][jt][i];
+    }
   };
 
   if constexpr (DB) {
@@ -417,7 +428,7 @@ __global__ void segment_scan_kernel(float *Sloc, const float *aloc, const float 
 template <int DK, int DV>
 hipError_t fwd_impl(FwdArgs args, hipStream_t stream) {
   const int64_t P = args.P;
-  if (P > 1) {
+  if (P > 1 && !args.sin_given) {
     dim3 g1((unsigned)(args.nh * (P - 1)));
     CLA_LAUNCH(args.xdot ? "chunk_dq_segments" : "chunk_fwd_segments",
                (chunk_fwd_kernel<DK, DV, 1>), g1, dim3(NTHR), stream, args);
@@ -538,14 +549,19 @@ ChunkPlan plan_chunk(int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV) {
   plan.P_b = Pb;
   plan.seg_chunks_b = segb;
   plan.ws_bwd = chunk::bwd_ws(nullptr, nh, T, Pb, DK, DV).bytes;
+  plan.saved_bytes = (size_t)(Pb - 1) * nh * DK * DV * sizeof(float);
   return plan;
 }
 
 hipError_t launch_chunk_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                             const float *l, const float *S0, uint16_t *o, float *ST,
-                            int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV,
-                            const ChunkPlan &plan, void *ws, hipStream_t stream) {
+                            float *saved, int64_t B, int64_t H, int64_t T, int64_t DK,
+                            int64_t DV, const ChunkPlan &plan, void *ws, hipStream_t stream) {
   chunk::FwdArgs args{};
+  if (plan.P_b > 1) {
+    args.saved = saved;
+    args.save_every = plan.seg_chunks_b;
+  }
   args.q = q;
   args.k = k;
   args.v = v;
@@ -565,10 +581,11 @@ hipError_t launch_chunk_fwd(const uint16_t *q, const uint16_t *k, const uint16_t
 
 hipError_t launch_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                             const float *l, const float *S0, const uint16_t *dO,
-                            const float *dST, uint16_t *dq, uint16_t *dk, uint16_t *dv,
-                            float *dl, float *dS0, int64_t B, int64_t H, int64_t T,
-                            int64_t DK, int64_t DV, const ChunkPlan &plan, void *ws,
+                            const float *dST, const float *saved, uint16_t *dq, uint16_t *dk,
+                            uint16_t *dv, float *dl, float *dS0, int64_t B, int64_t H,
+                            int64_t T, int64_t DK, int64_t DV, const ChunkPlan &plan, void *ws,
                             hipStream_t stream) {
+  if (plan.P_b <= 1) saved = nullptr;
   const int64_t nh = B * H;
   const chunk::BwdWs w = chunk::bwd_ws(ws, nh, T, plan.P_b, DK, DV);
   // dQ pass (forward chunk order): the forward recurrence on the transposed
@@ -592,6 +609,12 @@ hipError_t launch_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t
   fa.rdot = w.r1;
   fa.Sloc = w.seg.Sloc;
   fa.aloc = w.seg.aloc;
+  if (saved) {
+    // segments start from the forward's saved states (S, read transposed)
+    fa.Sin = saved;
+    fa.slot_trans = 1;
+    fa.sin_given = 1;
+  }
   fa.nh = nh;
   fa.T = T;
   fa.seg_chunks = plan.seg_chunks_b;
@@ -612,7 +635,8 @@ hipError_t launch_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t
   ba.dS0 = dS0;
   ba.Gloc = w.gseg.Sloc;
   ba.aloc = w.gseg.aloc;
-  ba.Sseg = w.seg.Sloc;
+  ba.Sseg = saved ? saved : w.seg.Sloc;
+  ba.sseg_dkdv = saved ? 1 : 0;
   ba.STb = dST ? w.ST : nullptr;
   ba.Bnd = w.Bnd;
   ba.nh = nh;

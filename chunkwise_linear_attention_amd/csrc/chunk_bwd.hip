@@ -142,21 +142,35 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
   }
   float alpha_total = 1.f;
   if (MODE == 0) {
-    // Boundary term of the decay gradient: <S, G> at this segment's end,
-    // from the fp32 state S^T that the dQ pass left there and the G^T just
-    // loaded by the dK side (both read along rows: coalesced).
-    const float *St = seg == a.P - 1 ? (a.STb ? a.STb + bh * DK * DV : nullptr)
-                                     : a.Sseg + (seg * a.nh + bh) * DK * DV;
+    // Boundary term of the decay gradient: <S, G> at this segment's end, from
+    // the fp32 state left at that boundary and the G just loaded; each read
+    // runs along rows (coalesced) through the wave side whose copy of G has
+    // the state's layout: S^T from the dQ pass against G^T, S itself (saved
+    // by the forward) against G.
+    const bool last = seg == a.P - 1;
+    const float *St = last ? (a.STb ? a.STb + bh * DK * DV : nullptr)
+                           : a.Sseg + (seg * a.nh + bh) * DK * DV;
+    const bool trans = last || !a.sseg_dkdv;  // St holds S^T
     double part = 0.0;
-    if (side == 1 && St) {
+    if (St && side == (trans ? 1 : 0)) {
       float pf = 0.f;
+      if (trans) {
 #pragma unroll
-      for (int jt = 0; jt < DV / 16; ++jt)
+        for (int jt = 0; jt < DV / 16; ++jt)
 #pragma unroll
-        for (int it = 0; it < NI; ++it)
+          for (int it = 0; it < NI; ++it)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            pf += G1(jt, it)[i] * St[(16 * jt + 4 * lg + i) * DK + dw0 + 16 * it + li];
+            for (int i = 0; i < 4; ++i)
+              pf += G1(jt, it)[i] * St[(16 * jt + 4 * lg + i) * DK + dw0 + 16 * it + li];
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < DK / 16; ++dt)
+#pragma unroll
+          for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              pf += G0(dt, jt)[i] * St[(16 * dt + 4 * lg + i) * DV + jw0 + 16 * jt + li];
+      }
       part = pf;
     }
 #pragma unroll
@@ -166,7 +180,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     __syncthreads();
     if (tid == 0) {
       double b = 0.0;
-      for (int u = 4; u < 8; ++u) b += bred[u];
+      for (int u = 0; u < 8; ++u) b += bred[u];
       a.Bnd[seg * a.nh + bh] = (float)b;
     }
   }

@@ -21,9 +21,12 @@ struct FwdArgs {
   float *aloc;             // state-only pass: [P-1, nh] total decay of the segment
   const uint16_t *xdot;    // optional [nh, T, DV]: rdot[t] = sum_j xdot[t, j] o[t, j]
   float *rdot;             // [nh, T]
-  int64_t nh, T, seg_chunks, P;
+  float *saved;            // optional [nT/save_every - 1, nh, DK, DV]: the state after
+                           // every save_every chunks (MODE 0)
+  int64_t nh, T, seg_chunks, P, save_every;
   int s0_trans, st_trans;
   int slot_trans;          // segment slots (Sloc, Sin) hold this kernel's state transposed
+  int sin_given;           // Sin is supplied: no segment-state pass, no segment scan
 };
 
 struct BwdArgs {
@@ -37,7 +40,9 @@ struct BwdArgs {
   float *Gloc;                      // state-only pass: [P-1, nh, DK, DV] (segment p in slot p-1)
   float *aloc;                      // state-only pass: [P-1, nh]
   const float *Sseg;                // [P-1, nh, DV, DK]: S^T at the end of segments 0..P-2
+                                    // ([P-1, nh, DK, DV], S itself, when sseg_dkdv)
   const float *STb;                 // [nh, DV, DK]: S_T^T (NULL when there is no dS_T)
+  int sseg_dkdv;
   float *Bnd;                       // [P, nh]: <S, G> at the end of each segment
   int64_t nh, T, seg_chunks, P;
 };

@@ -64,24 +64,29 @@ struct ChunkPlan {
   int64_t seg_chunks_b = 0; // backward: chunks per segment
   size_t ws_fwd = 0;        // workspace bytes, forward
   size_t ws_bwd = 0;        // workspace bytes, backward
+  size_t saved_bytes = 0;   // states at the backward's segment ends (P_b - 1 of them)
 };
 
 ChunkPlan plan_chunk(int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV);
 
+// saved (optional): receives S after every plan.seg_chunks_b chunks, the
+// states the backward's segments start from ([P_b - 1, B*H, DK, DV]).
 hipError_t launch_chunk_fwd(const uint16_t *q, const uint16_t *k,
                             const uint16_t *v, const float *l,
                             const float *S0, uint16_t *o, float *ST,
-                            int64_t B, int64_t H, int64_t T, int64_t DK,
-                            int64_t DV, const ChunkPlan &plan, void *ws,
-                            hipStream_t stream);
+                            float *saved, int64_t B, int64_t H, int64_t T,
+                            int64_t DK, int64_t DV, const ChunkPlan &plan,
+                            void *ws, hipStream_t stream);
 
+// saved (optional): the states written by launch_chunk_fwd; the dQ pass then
+// starts its segments from them instead of recomputing them.
 hipError_t launch_chunk_bwd(const uint16_t *q, const uint16_t *k,
                             const uint16_t *v, const float *l,
                             const float *S0, const uint16_t *dO,
-                            const float *dST, uint16_t *dq, uint16_t *dk,
-                            uint16_t *dv, float *dl, float *dS0, int64_t B,
-                            int64_t H, int64_t T, int64_t DK, int64_t DV,
-                            const ChunkPlan &plan, void *ws,
+                            const float *dST, const float *saved, uint16_t *dq,
+                            uint16_t *dk, uint16_t *dv, float *dl, float *dS0,
+                            int64_t B, int64_t H, int64_t T, int64_t DK,
+                            int64_t DV, const ChunkPlan &plan, void *ws,
                             hipStream_t stream);
 
 }  // namespace cla

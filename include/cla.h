@@ -164,6 +164,47 @@ int cla_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                   void *workspace, size_t workspace_bytes,
                   cla_stream_t stream);
 
+/*
+ * Training variant: the forward also saves the fp32 states the backward's
+ * segments start from, and the backward starts from them instead of
+ * recomputing them with an extra pass over K and V.  The state at a chunk
+ * boundary is the carried S_[j] of "Parallel scan", section "The chunkwise
+ * algorithm" (the forward already holds it); the backward's use of it follows
+ * Lightning Attention-2 Alg. 2, whose dQ traversal runs forward from S_[j-1].
+ * The outputs equal those of cla_chunk_fwd / cla_chunk_bwd up to rounding
+ * order.
+ *
+ * cla_chunk_saved_bytes: bytes of the saved states at this shape (0 when the
+ * backward does not split sequences, or for an invalid shape).  The buffer
+ * holds, for each of the backward's segment boundaries p = 1 .. P-1 and each
+ * (b, h), S [DK, DV] fp32 after chunk p * (segment length) - 1; its layout is
+ * private to the library (pass it from cla_chunk_fwd_saved to
+ * cla_chunk_bwd_saved unchanged, same shape).
+ * saved: device buffer of at least cla_chunk_saved_bytes bytes (may be NULL
+ * when that is 0), owned by the caller; written by cla_chunk_fwd_saved, read
+ * by cla_chunk_bwd_saved.  Too small or NULL when needed -> CLA_ERR_WORKSPACE;
+ * overlapping another argument -> CLA_ERR_ALIAS.  Every other argument and
+ * check is that of cla_chunk_fwd / cla_chunk_bwd.
+ */
+size_t cla_chunk_saved_bytes(int64_t B, int64_t H, int64_t T, int64_t DK,
+                             int64_t DV, int64_t chunk);
+
+int cla_chunk_fwd_saved(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        const float *log_decay, const float *S0, uint16_t *o,
+                        float *ST, float *saved, size_t saved_bytes, int64_t B,
+                        int64_t H, int64_t T, int64_t DK, int64_t DV,
+                        int64_t chunk, void *workspace, size_t workspace_bytes,
+                        cla_stream_t stream);
+
+int cla_chunk_bwd_saved(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        const float *log_decay, const float *S0,
+                        const uint16_t *dO, const float *dST,
+                        const float *saved, size_t saved_bytes, uint16_t *dq,
+                        uint16_t *dk, uint16_t *dv, float *dlog_decay,
+                        float *dS0, int64_t B, int64_t H, int64_t T,
+                        int64_t DK, int64_t DV, int64_t chunk, void *workspace,
+                        size_t workspace_bytes, cla_stream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Kernel timing (benchmark instrumentation)                                 */
 /* ------------------------------------------------------------------------ */

@@ -101,3 +101,30 @@ def test_chunk_validation(lib):
     a2 = list(args)
     a2[8] = A  # dk aliases q
     assert bw(*a2, 1, 1, 64, 64, 64, 64, J, 1 << 30, None) == ALIAS
+
+
+def test_chunk_saved_validation(lib):
+    # 16 heads of 98304 tokens: 96 backward segments of 16 chunks
+    nb = lib.cla_chunk_saved_bytes(1, 16, 98304, 128, 128, 64)
+    assert nb == 95 * 16 * 128 * 128 * 4
+    # enough heads to fill the GPU without splitting: nothing to save
+    assert lib.cla_chunk_saved_bytes(96, 16, 1024, 128, 128, 64) == 0
+    assert lib.cla_chunk_saved_bytes(1, 16, 98304, 96, 128, 64) == 0
+    assert lib.cla_chunk_saved_bytes(-1, 16, 98304, 128, 128, 64) == 0
+    ws = lib.cla_chunk_workspace_bytes(1, 16, 98304, 128, 128, 64, 1)
+    f = lib.cla_chunk_fwd_saved
+    args = (1, 16, 98304, 128, 128, 64)
+    # saved missing or too small
+    assert f(A, B_, C, D_, None, E, None, None, 0, *args, F, ws, None) == WS
+    assert f(A, B_, C, D_, None, E, None, G, nb - 4, *args, F, ws, None) == WS
+    # saved overlapping an input or the output
+    assert f(A, B_, C, D_, None, E, None, A, nb, *args, F, ws, None) == ALIAS
+    assert f(A, B_, C, D_, None, E, None, E + 64, nb, *args, F, ws, None) == ALIAS
+    b = lib.cla_chunk_bwd_saved
+    out = (H_, I, J, K, None)
+    assert b(A, B_, C, D_, None, E, None, None, 0, *out, *args, F, ws, None) == WS
+    assert b(A, B_, C, D_, None, E, None, G, nb - 1, *out, *args, F, ws, None) == WS
+    # saved states are an input of the backward: an output may not overlap them
+    assert b(A, B_, C, D_, None, E, None, H_, nb, *out, *args, F, ws, None) == ALIAS
+    assert b(A, B_, C, D_, None, E, None, G, nb, *out, 1, 16, 98304, 96, 128, 64,
+             F, ws, None) == UNSUP

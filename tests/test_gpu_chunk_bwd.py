@@ -59,6 +59,36 @@ def test_chunk_bwd_parity(coracle, B, H, T, DK, DV, decay, S0, dST, seed):
     _check_bwd(ci, _bwd(ci), coracle)
 
 
+SAVED_CASES = [
+    # sequences split into backward segments (few heads), ragged ends
+    (1, 2, 2500, 64, 64, "softplus", True, True, 21),
+    (1, 1, 3001, 128, 128, "mix", True, False, 22),
+    (2, 1, 1100, 128, 64, "softplus", False, True, 23),
+    (1, 1, 700, 64, 128, "head_const", True, True, 24),
+    (1, 4, 100, 64, 64, "softplus", True, True, 25),   # one segment: nothing saved
+]
+
+
+@pytest.mark.parametrize("B,H,T,DK,DV,decay,S0,dST,seed", SAVED_CASES)
+def test_chunk_saved_states_parity(coracle, B, H, T, DK, DV, decay, S0, dST, seed):
+    """cla_chunk_fwd_saved then cla_chunk_bwd_saved: the backward starts its
+    segments from the forward's states; every output against the oracle."""
+    import chunkwise_linear_attention_amd as cla
+    from gpu_util import rel_l2, say, to_dev, to_np
+    say(f"[chunk saved] B={B} H={H} T={T} DK={DK} DV={DV} decay={decay} S0={S0} dST={dST}")
+    ci = syn.chunk_inputs(B, H, T, DK, DV, seed, qk_scale=1 / math.sqrt(DK), decay=decay,
+                          S0_scale=0.1 if S0 else None, dST_scale=0.1 if dST else None)
+    q, k, v, l, S0d, dO, dSTd = (to_dev(x) for x in (ci.q, ci.k, ci.v, ci.l, ci.S0, ci.dO, ci.dST))
+    o, ST, saved = cla.chunked_linear_attn(q, k, v, l, S0d, save_states=True)
+    assert saved.numel() == max(1, cla.chunk_saved_bytes(B, H, T, DK, DV))
+    o_r, ST_r = coracle.la_fwd(ci.q, ci.k, ci.v, ci.l, ci.S0)
+    assert rel_l2(to_np(o).reshape(o_r.shape), o_r) <= TOL
+    assert rel_l2(to_np(ST).reshape(ST_r.shape), ST_r) <= TOL
+    got = cla.chunked_linear_attn_bwd(q, k, v, l, S0d, dO, dSTd, saved=saved)
+    errs = _check_bwd(ci, got, coracle)
+    say(f"[chunk saved] rel-L2 " + ", ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()))
+
+
 def test_chunk_bwd_empty_sequence():
     import torch
     import chunkwise_linear_attention_amd as cla

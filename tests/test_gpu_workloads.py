@@ -4,7 +4,9 @@ computed one by one, plus properties that hold at any size (GPU).
 
 Workloads: la_const (B=4, H=16, T=8192, dk=dv=64, per-head constant decay),
 la_gated (B=2, H=32, T=32768, dk=128, dv=64, S0 and dS_T given) and the
-long-T sweep la_long_T* (H=16, dk=dv=128, B*T = 98304, decays -1e-5 or -5).
+long-T sweep la_long_T* (H=16, dk=dv=128, B*T = 98304, decays -1e-5 or -5);
+each through the saved-state training path (cla_chunk_fwd_saved /
+cla_chunk_bwd_saved, what the bench times) and through the plain calls.
 """
 
 import numpy as np
@@ -17,13 +19,18 @@ TOL = 2e-2
 NAMES = ("o", "ST", "dq", "dk", "dv", "dl", "dS0")
 
 
-def _run_full(ci):
+def _run_full(ci, saved):
     import torch
     import chunkwise_linear_attention_amd as cla
     from gpu_util import to_dev
     q, k, v, l, S0, dO, dST = (to_dev(x) for x in (ci.q, ci.k, ci.v, ci.l, ci.S0, ci.dO, ci.dST))
-    o, ST = cla.chunked_linear_attn(q, k, v, l, S0)
-    g = cla.chunked_linear_attn_bwd(q, k, v, l, S0, dO, dST)
+    if saved:
+        # the training path the bench times: forward saves the segment states
+        o, ST, sv = cla.chunked_linear_attn(q, k, v, l, S0, save_states=True)
+        g = cla.chunked_linear_attn_bwd(q, k, v, l, S0, dO, dST, saved=sv)
+    else:
+        o, ST = cla.chunked_linear_attn(q, k, v, l, S0)
+        g = cla.chunked_linear_attn_bwd(q, k, v, l, S0, dO, dST)
     torch.cuda.synchronize()
     return (o, ST) + tuple(g)
 
@@ -49,8 +56,9 @@ def _check_sampled(ci, out, coracle, heads):
     return errs
 
 
+@pytest.mark.parametrize("saved", [True, False], ids=["saved", "recomputed"])
 @pytest.mark.parametrize("name", ["la_const", "la_gated_dST"] + [f"la_long_T{t}" for t in syn.LONG_T])
-def test_workload_sampled_heads(coracle, name):
+def test_workload_sampled_heads(coracle, name, saved):
     from gpu_util import say
     if name == "la_gated_dST":
         ci = syn._la_gated(dST=True)
@@ -58,7 +66,7 @@ def test_workload_sampled_heads(coracle, name):
         ci = syn.WORKLOADS[name].make()
     B, H = ci.q.shape[:2]
     heads = sorted({0, (B * H) // 2 + 1, B * H - 1})
-    say(f"[workload] {name} shape={ci.q.shape} dv={ci.v.shape[-1]} heads={heads}")
-    out = _run_full(ci)
+    say(f"[workload] {name} saved={saved} shape={ci.q.shape} dv={ci.v.shape[-1]} heads={heads}")
+    out = _run_full(ci, saved)
     errs = _check_sampled(ci, out, coracle, heads)
-    say(f"[workload] {name} rel-L2: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    say(f"[workload] {name} saved={saved} rel-L2: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
