@@ -417,11 +417,29 @@ __global__ void segment_scan_kernel(float *Sloc, const float *aloc, const float 
   const int64_t bh = e / per, x = e % per;
   const int d = (int)(x / DV), j = (int)(x % DV);
   float carry = S0 ? S0[bh * per + (s0_trans ? (int64_t)j * DK + d : x)] : 0.f;
-  for (int64_t i = 0; i + 1 < P; ++i) {
-    const int64_t p = reverse ? P - 2 - i : i;
-    float *slot = Sloc + (p * nh + bh) * per + x;
-    carry = aloc[p * nh + bh] * carry + *slot;
-    *slot = carry;
+  // Only the carry is sequential: the slots and decays of U segments are
+  // loaded together, then folded in order.
+  constexpr int U = 8;
+  for (int64_t i0 = 0; i0 + 1 < P; i0 += U) {
+    float sv[U], av[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + u;
+      if (i + 1 < P) {
+        const int64_t p = reverse ? P - 2 - i : i;
+        sv[u] = Sloc[(p * nh + bh) * per + x];
+        av[u] = aloc[p * nh + bh];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + u;
+      if (i + 1 < P) {
+        const int64_t p = reverse ? P - 2 - i : i;
+        carry = av[u] * carry + sv[u];
+        Sloc[(p * nh + bh) * per + x] = carry;
+      }
+    }
   }
 }
 

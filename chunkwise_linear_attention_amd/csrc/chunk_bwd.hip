@@ -42,7 +42,8 @@ namespace {
 constexpr int BTHR = 512;
 
 // MODE 0: dK, dV, r2, dS0.  MODE 1: the G recurrence of one segment from
-// zero (segments 1..P-1), for the segment scan.
+// zero (segments 1..P-1), for the segment scan; its rows are split between
+// the two wave sides (one copy of G, half the registers per wave).
 template <int DK, int DV, int MODE>
 __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
   constexpr int NJ = DV / 64;   // dV side: 16-col tiles of G per wave
@@ -380,13 +381,14 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     }
 
     // ---- state-gradient update (both copies): G <- alpha G + Q^T (lambda dO) ----
+    // (MODE 1 keeps one copy, its rows split between the two sides.)
     FRESH_LANE();
     alpha_total *= alpha;
 #pragma unroll
-    for (int x = 0; x < NG; ++x)
+    for (int x = 0; x < (MODE == 0 ? NG : NG / 2); ++x)
 #pragma unroll
       for (int i = 0; i < 4; ++i) Gs[x][i] *= alpha;
-    if (side == 0) {
+    if (side == 0 || MODE == 1) {
       // G[d][j] += sum_r Q^T[d][r] (lambda dO)[r][j]
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -403,8 +405,10 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
           db[jt] = cvt8(y);
         }
 #pragma unroll
-        for (int dt = 0; dt < DK / 16; ++dt) {
-          const bf16x8 qa = tr_frag<NCK>(QS, 32 * kb, 16 * dt, li, lg);  // Q^T: row d, k = r
+        for (int dt = 0; dt < (MODE == 0 ? DK / 16 : DK / 32); ++dt) {
+          // Q^T: row d, k = r (MODE 1: this side's rows)
+          const int d0 = MODE == 0 ? 16 * dt : side * (DK / 2) + 16 * dt;
+          const bf16x8 qa = tr_frag<NCK>(QS, 32 * kb, d0, li, lg);
 #pragma unroll
           for (int jt = 0; jt < NJ; ++jt) G0(dt, jt) = mfma(qa, db[jt], G0(dt, jt));
         }
@@ -466,16 +470,15 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
             dst[(16 * dt + 4 * lg + i) * DV + jw0 + 16 * jt + li] = G0(dt, jt)[i];
     }
   } else {
-    if (side == 0) {
-      float *dst = a.Gloc + ((seg - 1) * a.nh + bh) * DK * DV;
+    // each side holds the rows [side DK/2, (side+1) DK/2) of its columns
+    float *dst = a.Gloc + ((seg - 1) * a.nh + bh) * DK * DV;
 #pragma unroll
-      for (int dt = 0; dt < DK / 16; ++dt)
+    for (int dt = 0; dt < DK / 32; ++dt)
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt)
+      for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            dst[(16 * dt + 4 * lg + i) * DV + jw0 + 16 * jt + li] = G0(dt, jt)[i];
-    }
+        for (int i = 0; i < 4; ++i)
+          dst[(side * (DK / 2) + 16 * dt + 4 * lg + i) * DV + jw0 + 16 * jt + li] = G0(dt, jt)[i];
     if (tid == 0) a.aloc[(seg - 1) * a.nh + bh] = alpha_total;
   }
 }
