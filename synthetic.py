@@ -159,7 +159,10 @@ def chunk_inputs(B, H, T, DK, DV, seed, qk_scale=1.0, v_scale=1.0,
     """decay: 'softplus' -> l = -softplus(N(0,1)) * 0.1;
     'head_const' -> l[b,h,t] = fp32(log(1 - 2^-(5 + 8h/H)));
     'mix' -> l = -1e-5 or -5 with probability 1/2 each;
-    'zero' -> l = 0 (no decay); ('const', x) -> l = x everywhere."""
+    'zero' -> l = 0 (no decay); ('const', x) -> l = x everywhere;
+    ('resets', p) -> the softplus decays with each step replaced, with
+    probability p, by l = -inf (a_t = 0: the state is cleared before the
+    step's write)."""
     ss = np.random.SeedSequence(seed).spawn(7)
     q = _normal_bf16(ss[0], (B, H, T, DK), qk_scale)
     k = _normal_bf16(ss[1], (B, H, T, DK), qk_scale)
@@ -178,6 +181,11 @@ def chunk_inputs(B, H, T, DK, DV, seed, qk_scale=1.0, v_scale=1.0,
         l = np.zeros((B, H, T), dtype=np.float32)
     elif isinstance(decay, tuple) and decay[0] == "const":
         l = np.full((B, H, T), decay[1], dtype=np.float32)
+    elif isinstance(decay, tuple) and decay[0] == "resets":
+        x = _draw(ss[3], B * H * T, "normal32").astype(np.float64)
+        l = (-np.logaddexp(0.0, x) * 0.1).astype(np.float32).reshape(B, H, T)
+        u = _draw(ss[3].spawn(1)[0], B * H * T, "uniform64", (0.0, 1.0)).reshape(B, H, T)
+        l[u < decay[1]] = -np.inf
     else:
         raise ValueError(f"unknown decay kind {decay!r}")
     S0 = None if S0_scale is None else _normal_f32(ss[4], (B, H, DK, DV), S0_scale)

@@ -240,3 +240,89 @@ def test_c_oracle_matches_numpy(coracle, T, dk, dv):
     o, _ = coracle.la_fwd(q, k, v, l, None, heads=[3, 1])
     np.testing.assert_allclose(o[0], o_ref[1, 1], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(o[1], o_ref[0, 1], rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# exact resets: l_t = -inf (a_t = 0) clears the state before step t's write
+# --------------------------------------------------------------------------
+
+
+def _with_resets(T, seed, at):
+    q, k, v, l, S = _rand(T, 5, 4, seed)
+    l = l.copy()
+    l[list(at)] = -np.inf
+    return q, k, v, l, S
+
+
+@pytest.mark.parametrize("at", [(0,), (9,), (9, 10), (17, 40, 63), (5, 64, 65, 90)])
+def test_reset_splits_the_sequence(at):
+    """A reset at u makes steps u.. a fresh sequence from a zero state (the
+    write at u itself survives): the whole run equals the run on steps u..
+    alone, for the recurrence, the T x T matrix mode and the chunkwise form."""
+    T = 100
+    q, k, v, l, S = _with_resets(T, 40 + len(at), at)
+    u = max(at)
+    o_tail, S_tail = oa.la_loop(q[u:], k[u:], v[u:], l[u:], None)
+    for fn in (oa.la_loop, oa.la_matrix_mode,
+               lambda *x: oa.la_chunkwise(*x, Tc=16), lambda *x: oa.la_chunkwise(*x, Tc=64)):
+        o, ST = fn(q, k, v, l, S)
+        assert np.isfinite(o).all() and np.isfinite(ST).all()
+        np.testing.assert_allclose(o[u:], o_tail, rtol=1e-11, atol=1e-11)
+        np.testing.assert_allclose(ST, S_tail, rtol=1e-11, atol=1e-11)
+    # before the first reset nothing changes
+    u0 = min(at)
+    if u0 > 0:
+        o_head, _ = oa.la_loop(q[:u0], k[:u0], v[:u0], l[:u0], S)
+        o, _ = oa.la_loop(q, k, v, l, S)
+        np.testing.assert_allclose(o[:u0], o_head, rtol=1e-12, atol=1e-12)
+
+
+def test_reset_backward():
+    """With resets: the adjoint loop gives zero gradient to the log decay of a
+    reset step (a_u = 0 scales every path through it); nothing after the
+    first reset reaches the steps before it or the initial state; and the
+    closed-form decay gradient still equals the direct one."""
+    T = 90
+    at = (30, 31, 70)
+    q, k, v, l, S0 = _with_resets(T, 7, at)
+    rng = np.random.default_rng(8)
+    dO = rng.normal(size=(T, 4))
+    dST = rng.normal(size=(5, 4))
+    dq, dk, dv, dl, dS0 = oa.la_bwd_loop(q, k, v, l, S0, dO, dST)
+    for x in (dq, dk, dv, dl, dS0):
+        assert np.isfinite(x).all()
+    assert all(dl[u] == 0.0 for u in at)
+    # the first piece alone, with no gradient arriving after it
+    dq1, dk1, dv1, _, dS01 = oa.la_bwd_loop(q[:30], k[:30], v[:30], l[:30], S0, dO[:30], None)
+    np.testing.assert_allclose(dS0, dS01, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(dq[:30], dq1, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(dk[:30], dk1, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(dv[:30], dv1, rtol=1e-11, atol=1e-11)
+    _, ST = oa.la_loop(q, k, v, l, S0)
+    np.testing.assert_allclose(oa.dlog_closed_form(q, k, dq, dk, ST, dST), dl,
+                               rtol=1e-9, atol=1e-9)
+
+
+def test_c_oracle_resets(coracle):
+    from synthetic import bf16_bits_to_f64
+    rng = np.random.default_rng(5)
+    B, H, T, dk, dv = 1, 2, 130, 8, 8
+    q = _bf16(rng.normal(size=(B, H, T, dk)) * 0.3)
+    k = _bf16(rng.normal(size=(B, H, T, dk)) * 0.3)
+    v = _bf16(rng.normal(size=(B, H, T, dv)))
+    l = rng.uniform(-0.5, 0, (B, H, T)).astype(np.float32)
+    l[0, 0, [0, 64, 65]] = -np.inf
+    l[0, 1, [63, 100]] = -np.inf
+    S0 = rng.normal(size=(B, H, dk, dv)).astype(np.float32)
+    dO = _bf16(rng.normal(size=(B, H, T, dv)))
+    dST = rng.normal(size=(B, H, dk, dv)).astype(np.float32)
+    Q, K, V, DO = (bf16_bits_to_f64(x) for x in (q, k, v, dO))
+    o_ref, ST_ref = oa.la_fwd_batched(Q, K, V, l, S0)
+    o, ST = coracle.la_fwd(q, k, v, l, S0)
+    np.testing.assert_allclose(o.reshape(o_ref.shape), o_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ST.reshape(ST_ref.shape), ST_ref, rtol=1e-12, atol=1e-12)
+    ref = oa.la_bwd_batched(Q, K, V, l, S0, DO, dST)
+    got = coracle.la_bwd(q, k, v, l, S0, dO, dST)
+    for g, r in zip(got, ref):
+        assert np.isfinite(g).all()
+        np.testing.assert_allclose(g.reshape(r.shape), r, rtol=1e-11, atol=1e-11)
