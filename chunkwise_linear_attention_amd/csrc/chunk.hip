@@ -18,7 +18,9 @@
 //   O_[j] = (Q K^T (.) D) V + diag(lambda) Q S_[j-1]      (LA2 Eq. 8)
 //   S_[j] = alpha S_[j-1] + (diag(gamma) K)^T V           (LA2 Eq. 10)
 // The mask is applied elementwise to the fp32 score tile; it is never
-// factored into exp(c_r) exp(-c_s), which overflows for strong decays.
+// factored into exp(c_r) exp(-c_s), which overflows for strong decays.  A
+// step with l = -inf (a = 0) is an exact reset: the sums keep only finite
+// parts and a count of resets decides which products vanish (chunk_decay).
 //
 // Workgroup = 4 waves on one (batch*head, segment).  Per chunk:
 //   stage  : Q (row-major), K (row-major and transposed), V (transposed) into
@@ -188,16 +190,11 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     // In-chunk decays, one token per lane, computed by every wave and read
     // with cross-lane shuffles.  Rows past the chunk: gamma = 0, so that they
     // add nothing to the state.
-    float c_l = lane < n ? LC[lane] : 0.f;
-#pragma unroll
-    for (int sh = 1; sh < 64; sh <<= 1) {
-      const float p = __shfl_up(c_l, sh, 64);
-      if (lane >= sh) c_l += p;
-    }
-    const float c_last = __shfl(c_l, 63, 64);
-    const float lam_l = expf(c_l);
-    const float gam_l = lane < n ? expf(c_last - c_l) : 0.f;
-    const float alpha = expf(c_last);
+    const ChunkDecay dc = chunk_decay(lane < n ? LC[lane] : 0.f, lane);
+    const float c_l = dc.c;
+    const float lam_l = dc.k == 0 ? expf(c_l) : 0.f;
+    const float gam_l = lane < n && dc.k == dc.k_last ? expf(dc.c_last - c_l) : 0.f;
+    const float alpha = dc.k_last == 0 ? expf(dc.c_last) : 0.f;
 
     if constexpr (MODE == 0) {
       // ---- masked transposed score tiles -> P[r][s] (bf16) ----
@@ -214,13 +211,15 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
         }
         // acc[i] = (K Q^T)[s = 16 st + 4 lg + i][r]; keys past the chunk are masked
         const float cr = __shfl(c_l, r, 64);
+        const int kr = dc.any ? __shfl(dc.k, r, 64) : 0;
         bf16x4 pv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = 16 * st + 4 * lg + i;
           const float cs = __shfl(c_l, s, 64);
+          const bool sep = dc.any && __shfl(dc.k, s, 64) != kr;  // a reset in (s, r]
           float p = 0.f;
-          if (s <= r && s < n) p = acc[i] * __expf(cr - cs);
+          if (s <= r && s < n && !sep) p = acc[i] * __expf(cr - cs);
           pv[i] = tobf(p);
         }
         *reinterpret_cast<bf16x4 *>(PS + swz_off<8>(r, 2 * st + (lg >> 1)) + (lg & 1) * 8) = pv;

@@ -232,16 +232,11 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     // In-chunk decays, one token per lane, computed by every wave (lanes
     // are then read with cross-lane shuffles).  Rows past the chunk: no
     // decay, and lambda = 0 so that they add nothing to the state gradient.
-    float c_l = lane < n ? LC[lane] : 0.f;
-#pragma unroll
-    for (int sh = 1; sh < 64; sh <<= 1) {
-      const float p = __shfl_up(c_l, sh, 64);
-      if (lane >= sh) c_l += p;
-    }
-    const float c_last = __shfl(c_l, 63, 64);
-    const float lam_l = lane < n ? expf(c_l) : 0.f;
-    const float gam_l = expf(c_last - c_l);
-    const float alpha = expf(c_last);
+    const ChunkDecay dc = chunk_decay(lane < n ? LC[lane] : 0.f, lane);
+    const float c_l = dc.c;
+    const float lam_l = lane < n && dc.k == 0 ? expf(c_l) : 0.f;
+    const float gam_l = dc.k == dc.k_last ? expf(dc.c_last - c_l) : 0.f;
+    const float alpha = dc.k_last == 0 ? expf(dc.c_last) : 0.f;
 
     if constexpr (MODE == 0) {
       // ---- masked score tiles, stored transposed: P[s][r] ----
@@ -267,13 +262,15 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
           }
           // acc[i] = X[r = 16 rt + 4 lg + i][s]; rows past the chunk are masked
           const float cs = __shfl(c_l, s, 64);
+          const int ks = dc.any ? __shfl(dc.k, s, 64) : 0;
           bf16x4 pv;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 16 * rt + 4 * lg + i;
             float p = 0.f;
             const float cr = __shfl(c_l, r, 64);
-            if (r >= s && r < n) p = acc[i] * __expf(cr - cs);
+            const bool sep = dc.any && __shfl(dc.k, r, 64) != ks;  // a reset in (s, r]
+            if (r >= s && r < n && !sep) p = acc[i] * __expf(cr - cs);
             pv[i] = tobf(p);
           }
           *reinterpret_cast<bf16x4 *>(PT + swz_off<8>(s, 2 * rt + (lg >> 1)) + (lg & 1) * 8) = pv;

@@ -98,6 +98,46 @@ __device__ __forceinline__ bf16x4 lds_half(const unsigned char *base, int row, i
   return *reinterpret_cast<const bf16x4 *>(base + swz_off<NCH>(row, col >> 3) + (col & 7) * 2);
 }
 
+// In-chunk decays of one chunk, one token per lane; every wave computes them
+// for itself and reads other tokens' values with cross-lane shuffles.  A step
+// with l = -inf (a = 0, an exact reset) clears the state before its write:
+// its log enters the sums as 0, and the count of resets so far tells which
+// tokens it separates, so no -inf is ever formed, added or subtracted.
+//   c = finite part of l_1 + .. + l_r (this lane's token r; lanes past the
+//       chunk read l = 0), k = resets among steps 1..r
+// A segment product a_{r:s} = prod_{s < u <= r} a_u is exp(c_r - c_s) when
+// k_r == k_s and 0 otherwise.
+struct ChunkDecay {
+  float c, c_last;  // this lane's and the chunk's last cumulative log
+  int k, k_last;    // this lane's and the chunk's reset count
+  bool any;         // the chunk holds a reset (wave-uniform)
+};
+
+__device__ __forceinline__ ChunkDecay chunk_decay(float l, int lane) {
+  ChunkDecay d;
+  const bool rst = l < -3.0e38f;  // -inf
+  d.any = __ballot(rst) != 0;
+  float c = rst ? 0.f : l;
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) {
+    const float p = __shfl_up(c, sh, 64);
+    if (lane >= sh) c += p;
+  }
+  int k = rst ? 1 : 0;
+  if (d.any) {
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const int p = __shfl_up(k, sh, 64);
+      if (lane >= sh) k += p;
+    }
+  }
+  d.c = c;
+  d.k = k;
+  d.c_last = __shfl(c, 63, 64);
+  d.k_last = d.any ? __shfl(k, 63, 64) : 0;
+  return d;
+}
+
 // The lower-triangular 16 x 16 score tiles (row tile rt >= column tile st) of
 // a 64 x 64 chunk, then the two strictly-upper tiles that the k-blocks of 32
 // read and that must hold zeros: (0, 1) and (2, 3).  Wave w of NW handles

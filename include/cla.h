@@ -131,7 +131,12 @@ size_t cla_chunk_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t DK,
  * products without underflow").  Lightning Attention-2 Alg. 1 is the case of
  * a constant decay.
  *   q, k      : [B, H, T, DK] bf16.     v : [B, H, T, DV] bf16.
- *   log_decay : [B, H, T] fp32, l_t = log a_t; finite (not checked).
+ *   log_decay : [B, H, T] fp32, l_t = log a_t: finite, or -inf for a_t = 0,
+ *               an exact reset (the state is cleared before step t's write;
+ *               the in-chunk decays are formed from finite partial sums and
+ *               a count of resets, the additions-only segment sums of
+ *               "Parallel scan", section "Long products without underflow").
+ *               NaN and +inf are not allowed (not checked).
  *   S0        : [B, H, DK, DV] fp32 initial state, or NULL for zeros.
  *   o         : [B, H, T, DV] bf16 output.
  *   ST        : [B, H, DK, DV] fp32 final state, or NULL to skip.

@@ -47,6 +47,11 @@ CASES = [
     (1, 2, 3000, 128, 128, "mix", False, True, 7),          # strong/weak decays, segments
     (3, 5, 700, 128, 64, "head_const", True, False, 8),
     (2, 2, 200, 64, 64, "zero", True, True, 9),
+    # exact resets (l = -inf)
+    (1, 2, 300, 64, 64, ("resets", 0.02), True, True, 10),
+    (2, 1, 1000, 128, 128, ("resets", 0.05), True, True, 11),
+    (1, 1, 4096, 64, 128, ("resets", 0.003), True, False, 12),
+    (1, 2, 200, 128, 64, ("resets", 0.5), False, True, 13),
 ]
 
 
@@ -66,6 +71,7 @@ SAVED_CASES = [
     (2, 1, 1100, 128, 64, "softplus", False, True, 23),
     (1, 1, 700, 64, 128, "head_const", True, True, 24),
     (1, 4, 100, 64, 64, "softplus", True, True, 25),   # one segment: nothing saved
+    (1, 1, 2600, 128, 128, ("resets", 0.01), True, True, 26),
 ]
 
 

@@ -51,6 +51,11 @@ CASES = [
     (1, 2, 3000, 128, 128, "mix", False, 7),        # strong/weak decay mix, segments
     (3, 5, 700, 128, 64, "head_const", True, 8),
     (2, 2, 200, 64, 64, "zero", True, 9),           # no decay
+    # exact resets (l = -inf): sparse, dense, and across segments
+    (1, 2, 300, 64, 64, ("resets", 0.02), True, 10),
+    (2, 1, 1000, 128, 128, ("resets", 0.05), True, 11),
+    (1, 1, 4096, 64, 128, ("resets", 0.003), True, 12),
+    (1, 2, 200, 128, 64, ("resets", 0.5), False, 13),
 ]
 
 
@@ -92,3 +97,14 @@ def test_chunk_fwd_deterministic():
     o1, S1 = _fwd(ci)
     o2, S2 = _fwd(ci)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_chunk_fwd_resets_at_chunk_edges(coracle):
+    """Resets on the first token, on the last token of a chunk and on the
+    first of the next, and on two neighbours."""
+    from gpu_util import say
+    say("[chunk fwd] resets at chunk edges")
+    ci = syn.chunk_inputs(1, 2, 260, 64, 64, 31, qk_scale=1 / 8, S0_scale=0.1)
+    ci.l[0, 0, [0, 63, 64, 127, 128]] = -np.inf
+    ci.l[0, 1, [191, 192, 259]] = -np.inf
+    _check_fwd(ci, _fwd(ci), coracle)
