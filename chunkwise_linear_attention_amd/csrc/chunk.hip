@@ -130,7 +130,15 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
       src = a.Sin + ((seg - 1) * a.nh + bh) * DK * DV;
       trans = a.slot_trans;
     }
-    if (src) {
+    if (src && trans && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+      // stored transposed: this lane's four rows d are contiguous (16 bytes)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt)
+          S_acc[dt][jt] = *reinterpret_cast<const f32x4 *>(src + (j0 + 16 * jt + li) * DK +
+                                                            16 * dt + 4 * lg);
+    } else if (src) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll

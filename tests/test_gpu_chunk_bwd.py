@@ -140,3 +140,28 @@ def test_chunk_bwd_deterministic():
     b = _bwd(ci)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_chunk_unaligned_state_pointers(coracle):
+    """fp32 state tensors need only 4-byte alignment: S0 and dS_T at an odd
+    float offset, read directly and transposed (dQ pass), segments present."""
+    import torch
+    import chunkwise_linear_attention_amd as cla
+    from gpu_util import dev, say, to_dev
+    say("[chunk bwd] unaligned S0 / dST")
+    B, H, T, DK, DV = 1, 2, 1500, 128, 64
+    ci = syn.chunk_inputs(B, H, T, DK, DV, 41, qk_scale=1 / math.sqrt(DK), S0_scale=0.1,
+                          dST_scale=0.1)
+    n = B * H * DK * DV
+
+    def odd(x):
+        buf = torch.zeros(n + 1, dtype=torch.float32, device=dev())
+        buf[1:] = torch.from_numpy(x.reshape(-1)).to(dev())
+        return buf[1:].view(B, H, DK, DV)
+
+    q, k, v, l, dO = (to_dev(x) for x in (ci.q, ci.k, ci.v, ci.l, ci.dO))
+    S0, dST = odd(ci.S0), odd(ci.dST)
+    assert S0.data_ptr() % 16 == 4
+    o, ST, saved = cla.chunked_linear_attn(q, k, v, l, S0, save_states=True)
+    _check_bwd(ci, cla.chunked_linear_attn_bwd(q, k, v, l, S0, dO, dST), coracle)
+    _check_bwd(ci, cla.chunked_linear_attn_bwd(q, k, v, l, S0, dO, dST, saved=saved), coracle)
