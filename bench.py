@@ -327,7 +327,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # the GPU's clocks settle only after some tens of milliseconds of work
+    # (measured: about 15 fwd+bwd steps of 2 ms), so the default warmup is
+    # long enough to time the settled rate
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="scan_large", choices=sorted(syn.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--no-chunk-extras", action="store_true",
@@ -354,7 +357,8 @@ def main():
             # the matrix-state rows of the hot path, measured in the same run
             chunk = {}
             for name in CHUNK_EXTRAS:
-                r = bench_chunk(args, torch, cla, syn.WORKLOADS[name], max(3, args.steps // 2), 1)
+                r = bench_chunk(args, torch, cla, syn.WORKLOADS[name], max(3, args.steps // 2),
+                                args.warmup)
                 chunk[name] = {"tokens_per_s": round(r["value"], 1),
                                "ms_per_step": round(r["ms_per_step"], 4),
                                "roofline": r["roofline"],

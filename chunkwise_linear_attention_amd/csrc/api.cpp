@@ -145,6 +145,7 @@ int chunk_fwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   if (T > 0 && !(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o)))
     return CLA_ERR_UNSUPPORTED;
   const cla::ChunkPlan plan = cla::plan_chunk(B, H, T, DK, DV);
+  if (!cla::chunk_plan_launchable(plan, B * H)) return CLA_ERR_UNSUPPORTED;
   if (plan.ws_fwd > 0 && (!workspace || workspace_bytes < plan.ws_fwd))
     return CLA_ERR_WORKSPACE;
   const size_t sv = with_saved ? plan.saved_bytes : 0;
@@ -180,6 +181,7 @@ int chunk_bwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                  aligned16(dq) && aligned16(dk) && aligned16(dv)))
     return CLA_ERR_UNSUPPORTED;
   const cla::ChunkPlan plan = cla::plan_chunk(B, H, T, DK, DV);
+  if (!cla::chunk_plan_launchable(plan, B * H)) return CLA_ERR_UNSUPPORTED;
   if (plan.ws_bwd > 0 && (!workspace || workspace_bytes < plan.ws_bwd))
     return CLA_ERR_WORKSPACE;
   const size_t sv = with_saved ? plan.saved_bytes : 0;

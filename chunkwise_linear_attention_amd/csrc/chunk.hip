@@ -58,6 +58,13 @@ constexpr int64_t kMinSegChunks = 4;
 constexpr int64_t kMaxBwdSegChunks = 16;
 
 // MODE 0: outputs (o, S_T, rdot).  MODE 1: segment state only (Sloc, aloc).
+// MODE 2: MODE 0 plus, in segments after the first, the segment-local sum
+// Q^T diag(A) X over the segment (gloc, galoc), A_t the decay from the
+// segment start through token t.  Run as the backward's dQ pass (Q = dO,
+// X = q) this is the local G state of the segment: the gradient of the
+// state entering it from the segment's own outputs, G_start = sum_t A_t
+// q_t dO_t^T, a plain sum that needs no reverse sweep (ZTF "The chunkwise
+// algorithm", the inter-chunk term read backwards).
 // Four waves; wave w owns value columns [w DV/4, (w+1) DV/4).
 template <int DK, int DV, int MODE>
 __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
@@ -70,15 +77,16 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   // while this one is used) when two workgroups per CU still fit in LDS;
   // the two buffers are separate arrays so that the compiler can tell the
   // DMA target from the buffer being read.
-  constexpr int B_KS = MODE == 0 ? QB : 0;
+  constexpr bool OUT = MODE != 1;      // outputs, not just the segment state
+  constexpr int B_KS = OUT ? QB : 0;
   constexpr int B_VS = B_KS + QB;
   constexpr int B_XS = B_VS + VB;
-  constexpr int B_L = B_XS + (MODE == 0 ? VB : 0);
+  constexpr int B_L = B_XS + (OUT ? VB : 0);
   constexpr int BUF = B_L + 64 * 4;
-  constexpr int PSB = MODE == 0 ? 64 * 128 : 16;
-  constexpr int RDB = MODE == 0 ? NWAVE * 64 : 4;
+  constexpr int PSB = OUT ? 64 * 128 : 16;
+  constexpr int RDB = OUT ? NWAVE * 64 : 4;
   constexpr bool DB = 2 * BUF + PSB + 4 * RDB <= 80 * 1024;
-  constexpr int NBQ = MODE == 0 ? DK / 8 : 0, NBK = DK / 8, NBV = DV / 8;
+  constexpr int NBQ = OUT ? DK / 8 : 0, NBK = DK / 8, NBV = DV / 8;
   __shared__ __attribute__((aligned(1024))) unsigned char buf0[BUF];
   __shared__ __attribute__((aligned(1024))) unsigned char buf1[DB ? BUF : 16];
   __shared__ __attribute__((aligned(1024))) unsigned char PS[PSB];
@@ -98,14 +106,23 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     li = l_ & 15;                \
     lg = l_ >> 4;                \
   } while (0)
-  const int64_t bh = blockIdx.x % a.nh;
-  const int64_t seg = blockIdx.x / a.nh;
+  // a lane-dependent value re-derived behind an empty asm, like FRESH_LANE,
+  // so that addresses built from it are not kept live across the chunk loop
+  auto fresh = [](int x) __attribute__((always_inline)) {
+    asm volatile("" : "+v"(x));
+    return x;
+  };
+  // grid (nh, segments): both indices are workgroup ids, held in scalar
+  // registers, so every pointer derived from them stays wave-uniform
+  const int64_t bh = blockIdx.x;
+  const int64_t seg = blockIdx.y;
   const int64_t T = a.T;
   const int64_t nchunks = (T + TC - 1) / TC;
   const int64_t c_begin = seg * a.seg_chunks;
   const int64_t c_end = min(nchunks, c_begin + a.seg_chunks);
   const int j0 = w * (DV / 4);  // first value column of this wave
-  const bool has_x = MODE == 0 && a.xdot != nullptr;
+  const bool has_x = OUT && a.xdot != nullptr;
+  const bool do_g = MODE == 2 && seg > 0;  // wave-uniform
   const int nblk = NBQ + NBK + NBV + (has_x ? NBV : 0);
 
   const uint16_t *qh = a.q + bh * T * DK;
@@ -114,13 +131,20 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   const uint16_t *xh = has_x ? a.xdot + bh * T * DV : nullptr;
   const float *lh = a.l + bh * T;
 
-  // S_acc[dt][jt][i] = S[16 dt + 4 lg + i][j0 + 16 jt + li]
+  // S_acc[dt][jt][i] = S[16 dt + 4 lg + i][j0 + 16 jt + li]; G_acc alike
   f32x4 S_acc[NDT][NJ];
+  f32x4 G_acc[MODE == 2 ? NDT : 1][NJ];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) S_acc[dt][jt] = zero4();
-  if (MODE == 0) {
+  if constexpr (MODE == 2) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt) G_acc[dt][jt] = zero4();
+  }
+  if (OUT) {
     const float *src = nullptr;
     bool trans = false;
     if (seg == 0) {
@@ -178,7 +202,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   // the xdot sums of the previous chunk, from RD
   auto rd_sum = [&]() __attribute__((always_inline)) -> float {
     float s = 0.f;
-    if (MODE == 0 && rd_t0 >= 0 && tid < rd_n) {
+    if (OUT && rd_t0 >= 0 && tid < rd_n) {
 #pragma unroll
       for (int u = 0; u < NWAVE; ++u) s += RD[u * 64 + tid];
     }
@@ -198,13 +222,14 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     // In-chunk decays, one token per lane, computed by every wave and read
     // with cross-lane shuffles.  Rows past the chunk: gamma = 0, so that they
     // add nothing to the state.
-    const ChunkDecay dc = chunk_decay(lane < n ? LC[lane] : 0.f, lane);
+    const int fl = fresh(lane);
+    const ChunkDecay dc = chunk_decay(fl < n ? LC[fl] : 0.f, fl);
     const float c_l = dc.c;
     const float lam_l = dc.k == 0 ? expf(c_l) : 0.f;
     const float gam_l = lane < n && dc.k == dc.k_last ? expf(dc.c_last - c_l) : 0.f;
     const float alpha = dc.k_last == 0 ? expf(dc.c_last) : 0.f;
 
-    if constexpr (MODE == 0) {
+    if constexpr (OUT) {
       // ---- masked transposed score tiles -> P[r][s] (bf16) ----
       FRESH_LANE();
       for (int t = w; t < 12; t += NWAVE) {
@@ -297,6 +322,33 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
       }
     }
 
+    // ---- segment-local sum: G += Q^T diag(A) X, A_r = alpha_total lambda_r ----
+    if (MODE == 2 && do_g) {
+      FRESH_LANE();
+      const float wg_l = lane < n ? alpha_total * lam_l : 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float wg[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wg[e] = __shfl(wg_l, 32 * kb + 8 * lg + e, 64);
+        bf16x8 xb[NJ];  // (A X) B operands: k = s, column j
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) {
+          const bf16x8 x = tr_frag<NCV>(XS, 32 * kb, j0 + 16 * jt, li, lg);
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = tof(x[e]) * wg[e];
+          xb[jt] = cvt8(y);
+        }
+#pragma unroll
+        for (int dt = 0; dt < (MODE == 2 ? NDT : 0); ++dt) {
+          const bf16x8 qa = tr_frag<NCK>(QS, 32 * kb, 16 * dt, li, lg);  // Q^T: row d, k = s
+#pragma unroll
+          for (int jt = 0; jt < NJ; ++jt) G_acc[dt][jt] = mfma(qa, xb[jt], G_acc[dt][jt]);
+        }
+      }
+    }
+
     // ---- state update: S <- alpha S + K^T (gamma V) ----
     FRESH_LANE();
     alpha_total *= alpha;
@@ -352,7 +404,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
       const int64_t rs_t0 = rd_t0;
       const int rs_n = rd_n;
       compute(ci, cur);
-      if (MODE == 0 && rs_t0 >= 0 && tid < rs_n) a.rdot[bh * T + rs_t0 + tid] = rs;
+      if (OUT && rs_t0 >= 0 && tid < rs_n) a.rdot[bh * T + rs_t0 + fresh(tid)] = rs;
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // the next chunk has landed; this chunk's buffer is free
     };
@@ -367,7 +419,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     for (int64_t ci = c_begin; ci < c_end; ++ci) {
       lds_barrier();  // the previous chunk's LDS reads (and RD writes) are done
       const float rs = rd_sum();
-      if (MODE == 0 && rd_t0 >= 0 && tid < rd_n) a.rdot[bh * T + rd_t0 + tid] = rs;
+      if (OUT && rd_t0 >= 0 && tid < rd_n) a.rdot[bh * T + rd_t0 + fresh(tid)] = rs;
       stage(ci, buf0);
       __builtin_amdgcn_s_waitcnt(0);
       lds_barrier();  // every wave's DMA has landed
@@ -377,11 +429,22 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   }
   {
     const float rs = rd_sum();
-    if (MODE == 0 && rd_t0 >= 0 && tid < rd_n) a.rdot[bh * T + rd_t0 + tid] = rs;
+    if (OUT && rd_t0 >= 0 && tid < rd_n) a.rdot[bh * T + rd_t0 + tid] = rs;
   }
 
   // ---- segment outputs ----
-  if constexpr (MODE == 0) {
+  if constexpr (OUT) {
+    if (MODE == 2 && do_g) {
+      // stored transposed (row j, then d): as the dK/dV pass's G in the dQ pass
+      float *dst = a.gloc + ((seg - 1) * a.nh + bh) * DK * DV;
+#pragma unroll
+      for (int dt = 0; dt < (MODE == 2 ? NDT : 0); ++dt)
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt)
+          *reinterpret_cast<f32x4 *>(dst + (j0 + 16 * jt + li) * DK + 16 * dt + 4 * lg) =
+              G_acc[dt][jt];
+      if (tid == 0) a.galoc[(seg - 1) * a.nh + bh] = alpha_total;
+    }
     if (seg == a.P - 1 && a.ST) {
       float *dst = a.ST + bh * DK * DV;
 #pragma unroll
@@ -454,7 +517,7 @@ template <int DK, int DV>
 hipError_t fwd_impl(FwdArgs args, hipStream_t stream) {
   const int64_t P = args.P;
   if (P > 1 && !args.sin_given) {
-    dim3 g1((unsigned)(args.nh * (P - 1)));
+    dim3 g1((unsigned)args.nh, (unsigned)(P - 1));
     CLA_LAUNCH(args.xdot ? "chunk_dq_segments" : "chunk_fwd_segments",
                (chunk_fwd_kernel<DK, DV, 1>), g1, dim3(NTHR), stream, args);
     hipError_t e = hipGetLastError();
@@ -466,9 +529,13 @@ hipError_t fwd_impl(FwdArgs args, hipStream_t stream) {
     if (e != hipSuccess) return e;
     args.Sin = args.Sloc;
   }
-  dim3 g((unsigned)(args.nh * P));
-  CLA_LAUNCH(args.xdot ? "chunk_dq" : "chunk_fwd", (chunk_fwd_kernel<DK, DV, 0>), g,
-             dim3(NTHR), stream, args);
+  dim3 g((unsigned)args.nh, (unsigned)P);
+  if (args.gloc && P > 1) {
+    CLA_LAUNCH("chunk_dq", (chunk_fwd_kernel<DK, DV, 2>), g, dim3(NTHR), stream, args);
+  } else {
+    CLA_LAUNCH(args.xdot ? "chunk_dq" : "chunk_fwd", (chunk_fwd_kernel<DK, DV, 0>), g,
+               dim3(NTHR), stream, args);
+  }
   return hipGetLastError();
 }
 
@@ -639,6 +706,12 @@ hipError_t launch_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t
     fa.Sin = saved;
     fa.slot_trans = 1;
     fa.sin_given = 1;
+  }
+  if (plan.P_b > 1) {
+    // the dK/dV pass's segment-local G states, from the dO and q rows this
+    // pass already stages
+    fa.gloc = w.gseg.Sloc;
+    fa.galoc = w.gseg.aloc;
   }
   fa.nh = nh;
   fa.T = T;

@@ -41,34 +41,33 @@ namespace {
 
 constexpr int BTHR = 512;
 
-// MODE 0: dK, dV, r2, dS0.  MODE 1: the G recurrence of one segment from
-// zero (segments 1..P-1), for the segment scan; its rows are split between
-// the two wave sides (one copy of G, half the registers per wave).
-template <int DK, int DV, int MODE>
+// dK, dV, r2 and dS0 of one segment, starting from the G at its end (dS_T
+// for the last segment; the segment-local G states come from the dQ pass).
+template <int DK, int DV>
 __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
   constexpr int NJ = DV / 64;   // dV side: 16-col tiles of G per wave
   constexpr int NI = DK / 64;   // dK side: 16-col tiles of G^T per wave
   constexpr int NCK = DK / 8, NCV = DV / 8;
   constexpr int RK = 64 * DK * 2, RV = 64 * DV * 2;  // row-major tile bytes
-  // Two staging buffers, each [Q | dO | K | V | l] (K, V only in MODE 0):
+  // Two staging buffers, each [Q | dO | K | V | l]:
   // the next chunk streams into one by DMA while the other is being used.
   // They are separate arrays so that the compiler can tell the DMA target
   // from the buffer being read and does not wait for the DMA before reads.
   constexpr int B_DOS = RK;
   constexpr int B_KS = B_DOS + RV;
-  constexpr int B_VS = B_KS + (MODE == 0 ? RK : 0);
-  constexpr int B_L = B_VS + (MODE == 0 ? RV : 0);
+  constexpr int B_VS = B_KS + RK;
+  constexpr int B_L = B_VS + RV;
   constexpr int BUF = B_L + 64 * 4;
   // 1 KB DMA blocks per chunk
   constexpr int NBQ = DK / 8, NBD = DV / 8;
-  constexpr int NBK = MODE == 0 ? DK / 8 : 0, NBV = MODE == 0 ? DV / 8 : 0;
+  constexpr int NBK = DK / 8, NBV = DV / 8;
   constexpr int NBLK = NBQ + NBD + NBK + NBV;
   __shared__ __attribute__((aligned(1024))) unsigned char buf0[BUF];
   __shared__ __attribute__((aligned(1024))) unsigned char buf1[BUF];
   // P1[s][r] = D_rs (q_r . k_s), P2[s][r] = D_rs (dO_r . v_s)
-  __shared__ __attribute__((aligned(1024))) unsigned char P1[MODE == 0 ? 64 * 128 : 16];
-  __shared__ __attribute__((aligned(1024))) unsigned char P2[MODE == 0 ? 64 * 128 : 16];
-  __shared__ float R2P[MODE == 0 ? 4 * 64 : 1];
+  __shared__ __attribute__((aligned(1024))) unsigned char P1[64 * 128];
+  __shared__ __attribute__((aligned(1024))) unsigned char P2[64 * 128];
+  __shared__ float R2P[4 * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -85,8 +84,10 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     lg = l_ >> 4;                      \
   } while (0)
   const int side = w >> 2, wv = w & 3;   // side 0: dV / G;  side 1: dK / G^T
-  const int64_t bh = blockIdx.x % a.nh;
-  const int64_t seg = MODE == 0 ? blockIdx.x / a.nh : 1 + blockIdx.x / a.nh;
+  // grid (nh, segments): both indices are workgroup ids, held in scalar
+  // registers, so every pointer derived from them stays wave-uniform
+  const int64_t bh = blockIdx.x;
+  const int64_t seg = blockIdx.y;
   const int64_t T = a.T;
   const int64_t nchunks = (T + TC - 1) / TC;
   const int64_t c_begin = seg * a.seg_chunks;
@@ -111,14 +112,11 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
 #define G1(jt, it) Gs[(jt) * NI + (it)]
   {
     const float *src = nullptr;
-    if (MODE == 0) {
-      if (seg == a.P - 1) {
-        src = a.dST ? a.dST + bh * DK * DV : nullptr;
-      } else {
-        src = a.Gin + (seg * a.nh + bh) * DK * DV;
-      }
+    if (seg == a.P - 1) {
+      src = a.dST ? a.dST + bh * DK * DV : nullptr;
+    } else {
+      src = a.Gin + (seg * a.nh + bh) * DK * DV;
     }
-    if (MODE == 1) src = nullptr;
 #pragma unroll
     for (int x = 0; x < NG; ++x) Gs[x] = zero4();
     if (src) {
@@ -141,8 +139,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
       }
     }
   }
-  float alpha_total = 1.f;
-  if (MODE == 0) {
+  {
     // Boundary term of the decay gradient: <S, G> at this segment's end, from
     // the fp32 state left at that boundary and the G just loaded; each read
     // runs along rows (coalesced) through the wave side whose copy of G has
@@ -227,7 +224,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     float r2_sum = 0.f;
     const int64_t r2_row = r2_t0;
     const int r2_prev_n = r2_n;
-    if (MODE == 0 && r2_t0 >= 0 && tid < r2_n)
+    if (r2_t0 >= 0 && tid < r2_n)
       r2_sum = R2P[tid] + R2P[64 + tid] + R2P[128 + tid] + R2P[192 + tid];
     // In-chunk decays, one token per lane, computed by every wave (lanes
     // are then read with cross-lane shuffles).  Rows past the chunk: no
@@ -238,7 +235,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     const float gam_l = dc.k == dc.k_last ? expf(dc.c_last - c_l) : 0.f;
     const float alpha = dc.k_last == 0 ? expf(dc.c_last) : 0.f;
 
-    if constexpr (MODE == 0) {
+    {
       // ---- masked score tiles, stored transposed: P[s][r] ----
       FRESH_LANE();
       {
@@ -378,14 +375,12 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     }
 
     // ---- state-gradient update (both copies): G <- alpha G + Q^T (lambda dO) ----
-    // (MODE 1 keeps one copy, its rows split between the two sides.)
     FRESH_LANE();
-    alpha_total *= alpha;
 #pragma unroll
-    for (int x = 0; x < (MODE == 0 ? NG : NG / 2); ++x)
+    for (int x = 0; x < NG; ++x)
 #pragma unroll
       for (int i = 0; i < 4; ++i) Gs[x][i] *= alpha;
-    if (side == 0 || MODE == 1) {
+    if (side == 0) {
       // G[d][j] += sum_r Q^T[d][r] (lambda dO)[r][j]
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -402,15 +397,13 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
           db[jt] = cvt8(y);
         }
 #pragma unroll
-        for (int dt = 0; dt < (MODE == 0 ? DK / 16 : DK / 32); ++dt) {
-          // Q^T: row d, k = r (MODE 1: this side's rows)
-          const int d0 = MODE == 0 ? 16 * dt : side * (DK / 2) + 16 * dt;
-          const bf16x8 qa = tr_frag<NCK>(QS, 32 * kb, d0, li, lg);
+        for (int dt = 0; dt < DK / 16; ++dt) {
+          const bf16x8 qa = tr_frag<NCK>(QS, 32 * kb, 16 * dt, li, lg);  // Q^T: row d, k = r
 #pragma unroll
           for (int jt = 0; jt < NJ; ++jt) G0(dt, jt) = mfma(qa, db[jt], G0(dt, jt));
         }
       }
-    } else if (MODE == 0) {
+    } else {
       // G^T[j][d] += sum_r dO^T[j][r] (lambda Q)[r][d]
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -434,11 +427,9 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
         }
       }
     }
-    if (MODE == 0) {
-      r2_t0 = t0;
-      r2_n = n;
-    }
-    if (MODE == 0 && r2_row >= 0 && tid < r2_prev_n) a.r2[bh * T + r2_row + tid] = r2_sum;
+    r2_t0 = t0;
+    r2_n = n;
+    if (r2_row >= 0 && tid < r2_prev_n) a.r2[bh * T + r2_row + tid] = r2_sum;
     // the next chunk has landed; this chunk's buffer is free
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -451,32 +442,19 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     step(ci, buf0, buf1);
     if (ci - 1 >= c_begin) step(ci - 1, buf1, buf0);
   }
-  if (MODE == 0 && r2_t0 >= 0 && tid < r2_n)
+  if (r2_t0 >= 0 && tid < r2_n)
     a.r2[bh * T + r2_t0 + tid] = R2P[tid] + R2P[64 + tid] + R2P[128 + tid] + R2P[192 + tid];
 
   // ---- segment outputs ----
-  if constexpr (MODE == 0) {
-    if (seg == 0 && a.dS0 && side == 0) {
-      float *dst = a.dS0 + bh * DK * DV;
+  if (seg == 0 && a.dS0 && side == 0) {
+    float *dst = a.dS0 + bh * DK * DV;
 #pragma unroll
-      for (int dt = 0; dt < DK / 16; ++dt)
-#pragma unroll
-        for (int jt = 0; jt < NJ; ++jt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            dst[(16 * dt + 4 * lg + i) * DV + jw0 + 16 * jt + li] = G0(dt, jt)[i];
-    }
-  } else {
-    // each side holds the rows [side DK/2, (side+1) DK/2) of its columns
-    float *dst = a.Gloc + ((seg - 1) * a.nh + bh) * DK * DV;
-#pragma unroll
-    for (int dt = 0; dt < DK / 32; ++dt)
+    for (int dt = 0; dt < DK / 16; ++dt)
 #pragma unroll
       for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          dst[(side * (DK / 2) + 16 * dt + 4 * lg + i) * DV + jw0 + 16 * jt + li] = G0(dt, jt)[i];
-    if (tid == 0) a.aloc[(seg - 1) * a.nh + bh] = alpha_total;
+          dst[(16 * dt + 4 * lg + i) * DV + jw0 + 16 * jt + li] = G0(dt, jt)[i];
   }
 }
 
@@ -532,15 +510,15 @@ template <int DK, int DV>
 hipError_t bwd_kv_impl(BwdArgs args, hipStream_t stream) {
   const int64_t P = args.P;
   if (P > 1) {
-    CLA_LAUNCH("chunk_dkdv_segments", (chunk_bwd_kernel<DK, DV, 1>),
-               dim3((unsigned)(args.nh * (P - 1))), dim3(BTHR), stream, args);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    e = launch_segment_scan(args.Gloc, args.aloc, args.dST, 0, 1, args.nh, P, DK, DV, stream);
+    // Gloc/aloc hold each later segment's local G state and total decay (from
+    // the dQ pass); the reverse scan turns slot p into the G at the end of
+    // segment p
+    hipError_t e =
+        launch_segment_scan(args.Gloc, args.aloc, args.dST, 0, 1, args.nh, P, DK, DV, stream);
     if (e != hipSuccess) return e;
     args.Gin = args.Gloc;
   }
-  CLA_LAUNCH("chunk_dkdv", (chunk_bwd_kernel<DK, DV, 0>), dim3((unsigned)(args.nh * P)),
+  CLA_LAUNCH("chunk_dkdv", (chunk_bwd_kernel<DK, DV>), dim3((unsigned)args.nh, (unsigned)P),
              dim3(BTHR), stream, args);
   return hipGetLastError();
 }

@@ -23,6 +23,12 @@ struct FwdArgs {
   float *rdot;             // [nh, T]
   float *saved;            // optional [nT/save_every - 1, nh, DK, DV]: the state after
                            // every save_every chunks (MODE 0)
+  float *gloc;             // optional [P-1, nh, DV, DK] (segment p in slot p-1): the
+                           // segment-local sum  sum_t A_t v_t x_t^T  over the
+                           // segment's tokens, A_t = the decay from the segment
+                           // start through t (needs xdot); in the dQ pass this is
+                           // the dK/dV pass's local G state, stored as G
+  float *galoc;            // with gloc: [P-1, nh] total decay of the segment
   int64_t nh, T, seg_chunks, P, save_every;
   int s0_trans, st_trans;
   int slot_trans;          // segment slots (Sloc, Sin) hold this kernel's state transposed
@@ -37,8 +43,10 @@ struct BwdArgs {
   uint16_t *dk, *dv;                // [nh, T, DK|DV]
   float *r2;                        // [nh, T]  k . dk
   float *dS0;                       // [nh, DK, DV] or NULL
-  float *Gloc;                      // state-only pass: [P-1, nh, DK, DV] (segment p in slot p-1)
-  float *aloc;                      // state-only pass: [P-1, nh]
+  float *Gloc;                      // [P-1, nh, DK, DV]: segment p's local G state in slot
+                                    // p-1 (written by the dQ pass); the reverse segment
+                                    // scan turns it into Gin
+  float *aloc;                      // [P-1, nh]: total decay of segment p in slot p-1
   const float *Sseg;                // [P-1, nh, DV, DK]: S^T at the end of segments 0..P-2
                                     // ([P-1, nh, DK, DV], S itself, when sseg_dkdv)
   const float *STb;                 // [nh, DV, DK]: S_T^T (NULL when there is no dS_T)
@@ -50,7 +58,7 @@ struct BwdArgs {
 // Forward-type pass (segment state pass, segment scan, main pass).
 hipError_t fwd_dispatch(FwdArgs args, int DK, int DV, hipStream_t stream);
 
-// Reverse dK/dV pass (segment state pass, reverse segment scan, main pass).
+// Reverse dK/dV pass (reverse segment scan of Gloc, main pass).
 hipError_t bwd_kv_dispatch(const BwdArgs &args, int DK, int DV, hipStream_t stream);
 
 // Exclusive scan of per-segment pairs (alpha_p, S_p) held in slots, in place.

@@ -69,6 +69,12 @@ struct ChunkPlan {
 
 ChunkPlan plan_chunk(int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV);
 
+// The chunk kernels run on a grid (B*H, segments): at most 2^31 - 1
+// sequence-heads and 65535 segments (T up to 16 * 65535 chunks of 64 tokens).
+inline bool chunk_plan_launchable(const ChunkPlan &plan, int64_t nh) {
+  return nh <= 0x7fffffff && plan.P <= 65535 && plan.P_b <= 65535;
+}
+
 // saved (optional): receives S after every plan.seg_chunks_b chunks, the
 // states the backward's segments start from ([P_b - 1, B*H, DK, DV]).
 hipError_t launch_chunk_fwd(const uint16_t *q, const uint16_t *k,

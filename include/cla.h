@@ -53,7 +53,8 @@ enum {
   CLA_OK = 0,
   CLA_ERR_NULL_ARG = 1,    /* a required pointer is NULL                      */
   CLA_ERR_BAD_SHAPE = 2,   /* a size is negative                              */
-  CLA_ERR_UNSUPPORTED = 3, /* DK/DV not in {64, 128}, chunk != 64, misaligned */
+  CLA_ERR_UNSUPPORTED = 3, /* DK/DV not in {64, 128}, chunk != 64, misaligned,
+                              chunkwise T > 67,107,840 or B*H >= 2^31 */
   CLA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required         */
   CLA_ERR_ALIAS = 5,       /* an output overlaps an input or another output   */
   CLA_ERR_HIP = 6          /* a HIP launch failed                             */
@@ -141,7 +142,8 @@ size_t cla_chunk_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t DK,
  *   o         : [B, H, T, DV] bf16 output.
  *   ST        : [B, H, DK, DV] fp32 final state, or NULL to skip.
  *   DK, DV in {64, 128}; chunk must be 64; the bf16 tensors must be
- *   16-byte aligned (CLA_ERR_UNSUPPORTED otherwise).
+ *   16-byte aligned; T at most 67,107,840 (65535 segments of 16 chunks) and
+ *   B*H below 2^31 (CLA_ERR_UNSUPPORTED otherwise).
  */
 int cla_chunk_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                   const float *log_decay, const float *S0, uint16_t *o,

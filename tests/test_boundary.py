@@ -128,3 +128,20 @@ def test_chunk_saved_validation(lib):
     assert b(A, B_, C, D_, None, E, None, H_, nb, *out, *args, F, ws, None) == ALIAS
     assert b(A, B_, C, D_, None, E, None, G, nb, *out, 1, 16, 98304, 96, 128, 64,
              F, ws, None) == UNSUP
+
+
+def test_chunk_length_limit(lib):
+    # the kernels' grid holds at most 65535 segments along time; backward
+    # segments hold at most 16 chunks of 64 tokens: T <= 16 * 65535 * 64
+    tmax = 16 * 65535 * 64
+    fw = lib.cla_chunk_fwd
+    bw = lib.cla_chunk_bwd
+    big = 1 << 40  # workspace size large enough to pass the workspace check
+    for T, want in ((tmax + 1, UNSUP), (tmax + 64, UNSUP)):
+        assert fw(A, B_, C, D_, None, E, None, 1, 1, T, 64, 64, 64, F, big, None) == want
+        assert bw(A, B_, C, D_, None, E, None, G, H_, I, J, None, 1, 1, T, 64, 64, 64,
+                  K, big, None) == want
+    # at the limit the host checks pass (workspace missing is reported next)
+    assert fw(A, B_, C, D_, None, E, None, 1, 1, tmax, 64, 64, 64, None, 0, None) == WS
+    assert bw(A, B_, C, D_, None, E, None, G, H_, I, J, None, 1, 1, tmax, 64, 64, 64,
+              None, 0, None) == WS
