@@ -57,36 +57,35 @@ constexpr int64_t kMinSegChunks = 4;
 // tokens).
 constexpr int64_t kMaxBwdSegChunks = 16;
 
-// MODE 0: outputs (o, S_T, rdot).  MODE 1: segment state only (Sloc, aloc).
-// MODE 2: MODE 0 plus, in segments after the first, the segment-local sum
-// Q^T diag(A) X over the segment (gloc, galoc), A_t the decay from the
-// segment start through token t.  Run as the backward's dQ pass (Q = dO,
-// X = q) this is the local G state of the segment: the gradient of the
-// state entering it from the segment's own outputs, G_start = sum_t A_t
-// q_t dO_t^T, a plain sum that needs no reverse sweep (ZTF "The chunkwise
-// algorithm", the inter-chunk term read backwards).
+// Outputs o, S_T and the optional rdot of one segment.  With GSUM, also (in
+// segments after the first) the segment-local sum Q^T diag(A) X over the
+// segment (gloc, galoc), A_t the decay from the segment start through token
+// t.  Run as the backward's dQ pass (Q = dO, X = q) this is the local G state
+// of the segment: the gradient of the state entering it from the segment's
+// own outputs, G_start = sum_t A_t q_t dO_t^T, a plain sum that needs no
+// reverse sweep (ZTF "The chunkwise algorithm", the inter-chunk term read
+// backwards).
 // Four waves; wave w owns value columns [w DV/4, (w+1) DV/4).
-template <int DK, int DV, int MODE>
+template <int DK, int DV, bool GSUM>
 __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   constexpr int NJ = DV / 64;          // 16-column tiles per wave
   constexpr int NDT = DK / 16;         // 16-row tiles of the state
   constexpr int NCK = DK / 8, NCV = DV / 8;  // 16-byte chunks per row
   constexpr int QB = 64 * DK * 2, VB = 64 * DV * 2;
-  // Staging buffer [Q | K | V | X | l]: Q and X (the optional xdot rows) in
-  // MODE 0 only.  It is double-buffered (the next chunk streams in by DMA
-  // while this one is used) when two workgroups per CU still fit in LDS;
-  // the two buffers are separate arrays so that the compiler can tell the
-  // DMA target from the buffer being read.
-  constexpr bool OUT = MODE != 1;      // outputs, not just the segment state
-  constexpr int B_KS = OUT ? QB : 0;
+  // Staging buffer [Q | K | V | X | l] (X: the optional xdot rows).  It is
+  // double-buffered (the next chunk streams in by DMA while this one is used)
+  // when two workgroups per CU still fit in LDS; the two buffers are separate
+  // arrays so that the compiler can tell the DMA target from the buffer being
+  // read.
+  constexpr int B_KS = QB;
   constexpr int B_VS = B_KS + QB;
   constexpr int B_XS = B_VS + VB;
-  constexpr int B_L = B_XS + (OUT ? VB : 0);
+  constexpr int B_L = B_XS + VB;
   constexpr int BUF = B_L + 64 * 4;
-  constexpr int PSB = OUT ? 64 * 128 : 16;
-  constexpr int RDB = OUT ? NWAVE * 64 : 4;
+  constexpr int PSB = 64 * 128;
+  constexpr int RDB = NWAVE * 64;
   constexpr bool DB = 2 * BUF + PSB + 4 * RDB <= 80 * 1024;
-  constexpr int NBQ = OUT ? DK / 8 : 0, NBK = DK / 8, NBV = DV / 8;
+  constexpr int NBQ = DK / 8, NBK = DK / 8, NBV = DV / 8;
   __shared__ __attribute__((aligned(1024))) unsigned char buf0[BUF];
   __shared__ __attribute__((aligned(1024))) unsigned char buf1[DB ? BUF : 16];
   __shared__ __attribute__((aligned(1024))) unsigned char PS[PSB];
@@ -121,8 +120,8 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   const int64_t c_begin = seg * a.seg_chunks;
   const int64_t c_end = min(nchunks, c_begin + a.seg_chunks);
   const int j0 = w * (DV / 4);  // first value column of this wave
-  const bool has_x = OUT && a.xdot != nullptr;
-  const bool do_g = MODE == 2 && seg > 0;  // wave-uniform
+  const bool has_x = a.xdot != nullptr;
+  const bool do_g = GSUM && seg > 0;  // wave-uniform
   const int nblk = NBQ + NBK + NBV + (has_x ? NBV : 0);
 
   const uint16_t *qh = a.q + bh * T * DK;
@@ -133,18 +132,18 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
 
   // S_acc[dt][jt][i] = S[16 dt + 4 lg + i][j0 + 16 jt + li]; G_acc alike
   f32x4 S_acc[NDT][NJ];
-  f32x4 G_acc[MODE == 2 ? NDT : 1][NJ];
+  f32x4 G_acc[GSUM ? NDT : 1][NJ];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) S_acc[dt][jt] = zero4();
-  if constexpr (MODE == 2) {
+  if constexpr (GSUM) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int jt = 0; jt < NJ; ++jt) G_acc[dt][jt] = zero4();
   }
-  if (OUT) {
+  {
     const float *src = nullptr;
     bool trans = false;
     if (seg == 0) {
@@ -202,7 +201,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   // the xdot sums of the previous chunk, from RD
   auto rd_sum = [&]() __attribute__((always_inline)) -> float {
     float s = 0.f;
-    if (OUT && rd_t0 >= 0 && tid < rd_n) {
+    if (rd_t0 >= 0 && tid < rd_n) {
 #pragma unroll
       for (int u = 0; u < NWAVE; ++u) s += RD[u * 64 + tid];
     }
@@ -229,7 +228,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     const float gam_l = lane < n && dc.k == dc.k_last ? expf(dc.c_last - c_l) : 0.f;
     const float alpha = dc.k_last == 0 ? expf(dc.c_last) : 0.f;
 
-    if constexpr (OUT) {
+    {
       // ---- masked transposed score tiles -> P[r][s] (bf16) ----
       FRESH_LANE();
       for (int t = w; t < 12; t += NWAVE) {
@@ -323,7 +322,9 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     }
 
     // ---- segment-local sum: G += Q^T diag(A) X, A_r = alpha_total lambda_r ----
-    if (MODE == 2 && do_g) {
+    // (once the decay from the segment start is exactly 0, every later token
+    // adds exactly 0)
+    if (GSUM && do_g && __builtin_amdgcn_readfirstlane(alpha_total != 0.f ? 1 : 0)) {
       FRESH_LANE();
       const float wg_l = lane < n ? alpha_total * lam_l : 0.f;
 #pragma unroll
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
           xb[jt] = cvt8(y);
         }
 #pragma unroll
-        for (int dt = 0; dt < (MODE == 2 ? NDT : 0); ++dt) {
+        for (int dt = 0; dt < (GSUM ? NDT : 0); ++dt) {
           const bf16x8 qa = tr_frag<NCK>(QS, 32 * kb, 16 * dt, li, lg);  // Q^T: row d, k = s
 #pragma unroll
           for (int jt = 0; jt < NJ; ++jt) G_acc[dt][jt] = mfma(qa, xb[jt], G_acc[dt][jt]);
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
       }
     }
     // the state the backward's segment ci / save_every starts from
-    if (MODE == 0 && a.saved && (ci + 1) % a.save_every == 0 && ci + 1 < nchunks) {
+    if (!GSUM && a.saved && (ci + 1) % a.save_every == 0 && ci + 1 < nchunks) {
       float *dst = a.saved + (((ci + 1) / a.save_every - 1) * a.nh + bh) * DK * DV;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
       const int64_t rs_t0 = rd_t0;
       const int rs_n = rd_n;
       compute(ci, cur);
-      if (OUT && rs_t0 >= 0 && tid < rs_n) a.rdot[bh * T + rs_t0 + fresh(tid)] = rs;
+      if (rs_t0 >= 0 && tid < rs_n) a.rdot[bh * T + rs_t0 + fresh(tid)] = rs;
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // the next chunk has landed; this chunk's buffer is free
     };
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     for (int64_t ci = c_begin; ci < c_end; ++ci) {
       lds_barrier();  // the previous chunk's LDS reads (and RD writes) are done
       const float rs = rd_sum();
-      if (OUT && rd_t0 >= 0 && tid < rd_n) a.rdot[bh * T + rd_t0 + fresh(tid)] = rs;
+      if (rd_t0 >= 0 && tid < rd_n) a.rdot[bh * T + rd_t0 + fresh(tid)] = rs;
       stage(ci, buf0);
       __builtin_amdgcn_s_waitcnt(0);
       lds_barrier();  // every wave's DMA has landed
@@ -429,36 +430,23 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   }
   {
     const float rs = rd_sum();
-    if (OUT && rd_t0 >= 0 && tid < rd_n) a.rdot[bh * T + rd_t0 + tid] = rs;
+    if (rd_t0 >= 0 && tid < rd_n) a.rdot[bh * T + rd_t0 + tid] = rs;
   }
 
   // ---- segment outputs ----
-  if constexpr (OUT) {
-    if (MODE == 2 && do_g) {
-      // stored transposed (row j, then d): as the dK/dV pass's G in the dQ pass
-      float *dst = a.gloc + ((seg - 1) * a.nh + bh) * DK * DV;
+  if (GSUM && do_g) {
+    // stored transposed (row j, then d): as the dK/dV pass's G in the dQ pass
+    float *dst = a.gloc + ((seg - 1) * a.nh + bh) * DK * DV;
 #pragma unroll
-      for (int dt = 0; dt < (MODE == 2 ? NDT : 0); ++dt)
+    for (int dt = 0; dt < (GSUM ? NDT : 0); ++dt)
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt)
-          *reinterpret_cast<f32x4 *>(dst + (j0 + 16 * jt + li) * DK + 16 * dt + 4 * lg) =
-              G_acc[dt][jt];
-      if (tid == 0) a.galoc[(seg - 1) * a.nh + bh] = alpha_total;
-    }
-    if (seg == a.P - 1 && a.ST) {
-      float *dst = a.ST + bh * DK * DV;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int jt = 0; jt < NJ; ++jt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int d = 16 * dt + 4 * lg + i, j = j0 + 16 * jt + li;
-            dst[a.st_trans ? j * DK + d : d * DV + j] = S_acc[dt][jt][i];
-          }
-    }
-  } else {
-    float *dst = a.Sloc + (seg * a.nh + bh) * DK * DV;
+      for (int jt = 0; jt < NJ; ++jt)
+        *reinterpret_cast<f32x4 *>(dst + (j0 + 16 * jt + li) * DK + 16 * dt + 4 * lg) =
+            G_acc[dt][jt];
+    if (tid == 0) a.galoc[(seg - 1) * a.nh + bh] = alpha_total;
+  }
+  if (seg == a.P - 1 && a.ST) {
+    float *dst = a.ST + bh * DK * DV;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -466,12 +454,140 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int d = 16 * dt + 4 * lg + i, j = j0 + 16 * jt + li;
-          dst[a.slot_trans ? j * DK + d : d * DV + j] = S_acc[dt][jt][i];
+          dst[a.st_trans ? j * DK + d : d * DV + j] = S_acc[dt][jt][i];
         }
-    if (tid == 0) a.aloc[seg * a.nh + bh] = alpha_total;
   }
 }
 #undef FRESH_LANE
+
+// Segment state pass: the pair (alpha_p, S_p) of segment p = blockIdx.y from
+// a zero state (ZTF "Splitting one sequence across devices", phase one).
+// S_p is a plain sum over the segment's chunks,
+//   S_p = sum_j A_j (diag(gamma_j) K_j)^T V_j,   A_j = prod_{i > j} alpha_i,
+// the decay from chunk j's end to the segment's end, so the chunks are taken
+// last to first with A carried as a running product (no rescaling of the
+// accumulated state).  Once A is exactly 0 in fp32 (strong decays, or a reset
+// with l = -inf), every earlier chunk contributes exactly 0: the pass stops
+// there without reading them, and alpha_p = 0.  Only K, V and l are read.
+// Four waves; wave w owns columns [w DV/4, (w+1) DV/4); two staging buffers.
+template <int DK, int DV>
+__global__ __launch_bounds__(NTHR, 2) void chunk_state_kernel(FwdArgs a) {
+  constexpr int NJ = DV / 64, NDT = DK / 16;
+  constexpr int NCK = DK / 8, NCV = DV / 8;
+  constexpr int B_VS = 64 * DK * 2, B_L = B_VS + 64 * DV * 2, BUF = B_L + 64 * 4;
+  constexpr int NBK = DK / 8, NBV = DV / 8, NBLK = NBK + NBV;
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int li = lane & 15, lg = lane >> 4;
+  const int64_t bh = blockIdx.x;
+  const int64_t seg = blockIdx.y;
+  const int64_t T = a.T;
+  const int64_t nchunks = (T + TC - 1) / TC;
+  const int64_t c_begin = seg * a.seg_chunks;
+  const int64_t c_end = min(nchunks, c_begin + a.seg_chunks);
+  const int j0 = w * (DV / 4);
+  const uint16_t *kh = a.k + bh * T * DK;
+  const uint16_t *vh = a.v + bh * T * DV;
+  const float *lh = a.l + bh * T;
+
+  f32x4 S_acc[NDT][NJ];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) S_acc[dt][jt] = zero4();
+  // decay from the end of the chunk being added to the segment's end; every
+  // wave forms it from the same data with the same instructions, so it is
+  // the same in all waves
+  float A = 1.f;
+
+  auto stage = [&](int64_t cj, unsigned char *buf) __attribute__((always_inline)) {
+    const int64_t tj = cj * TC;
+    const int nj = (int)min<int64_t>(TC, T - tj);
+    for (int b = w; b < NBLK; b += NWAVE) {
+      if (b < NBK)
+        dma_block<DK>(kh + tj * DK, nj, buf, b, lane);
+      else
+        dma_block<DV>(vh + tj * DV, nj, buf + B_VS, b - NBK, lane);
+    }
+    if (w == 0)
+      __builtin_amdgcn_global_load_lds(lh + tj + min(lane, nj - 1), (lds_void *)(buf + B_L), 4, 0,
+                                       0);
+  };
+
+  auto compute = [&](int64_t ci, const unsigned char *cur) __attribute__((always_inline)) {
+    const int64_t t0 = ci * TC;
+    const int n = (int)min<int64_t>(TC, T - t0);
+    const unsigned char *KS = cur;
+    const unsigned char *VS = cur + B_VS;
+    const float *LC = reinterpret_cast<const float *>(cur + B_L);
+    int l_ = lane;
+    asm volatile("" : "+v"(l_));
+    li = l_ & 15;
+    lg = l_ >> 4;
+    const ChunkDecay dc = chunk_decay(l_ < n ? LC[l_] : 0.f, l_);
+    // weight of token s: its decay to the chunk end, times A
+    const float wt_l = l_ < n && dc.k == dc.k_last ? A * expf(dc.c_last - dc.c) : 0.f;
+    const float alpha = dc.k_last == 0 ? expf(dc.c_last) : 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float wt[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wt[e] = __shfl(wt_l, 32 * kb + 8 * lg + e, 64);
+      bf16x8 vb[NJ];  // (A gamma V) B operands: k = s, column j
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt) {
+        const bf16x8 x = tr_frag<NCV>(VS, 32 * kb, j0 + 16 * jt, li, lg);
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = tof(x[e]) * wt[e];
+        vb[jt] = cvt8(y);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16x8 ka = tr_frag<NCK>(KS, 32 * kb, 16 * dt, li, lg);  // K^T: row d, k = s
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) S_acc[dt][jt] = mfma(ka, vb[jt], S_acc[dt][jt]);
+      }
+    }
+    A *= alpha;
+  };
+
+  // Chunk ci from `cur` while chunk ci - 1 streams into `nxt`; returns false
+  // once the earlier chunks can add nothing.  Nothing is in flight on return.
+  auto step = [&](int64_t ci, const unsigned char *cur, unsigned char *nxt)
+                  __attribute__((always_inline)) -> bool {
+    if (ci > c_begin) stage(ci - 1, nxt);
+    compute(ci, cur);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // the next chunk has landed; this chunk's buffer is free
+    return __builtin_amdgcn_readfirstlane(A != 0.f ? 1 : 0) != 0;
+  };
+
+  stage(c_end - 1, st0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int64_t ci = c_end - 1; ci >= c_begin; ci -= 2) {
+    if (!step(ci, st0, st1)) break;
+    if (ci - 1 >= c_begin && !step(ci - 1, st1, st0)) break;
+  }
+
+  float *dst = a.Sloc + (seg * a.nh + bh) * DK * DV;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 16 * dt + 4 * lg + i, j = j0 + 16 * jt + li;
+        dst[a.slot_trans ? j * DK + d : d * DV + j] = S_acc[dt][jt][i];
+      }
+  // the product of every chunk decay of the segment (0 after an early stop)
+  if (tid == 0) a.aloc[seg * a.nh + bh] = A;
+}
 
 // Incoming state of every segment from the segment pairs (alpha_p, S_p):
 // S_in(0) = S0, S_in(p+1) = alpha_p S_in(p) + S_p (ZTF "Splitting one
@@ -519,7 +635,7 @@ hipError_t fwd_impl(FwdArgs args, hipStream_t stream) {
   if (P > 1 && !args.sin_given) {
     dim3 g1((unsigned)args.nh, (unsigned)(P - 1));
     CLA_LAUNCH(args.xdot ? "chunk_dq_segments" : "chunk_fwd_segments",
-               (chunk_fwd_kernel<DK, DV, 1>), g1, dim3(NTHR), stream, args);
+               (chunk_state_kernel<DK, DV>), g1, dim3(NTHR), stream, args);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // slots and S0 are combined elementwise; S0 is read transposed only when
@@ -531,9 +647,9 @@ hipError_t fwd_impl(FwdArgs args, hipStream_t stream) {
   }
   dim3 g((unsigned)args.nh, (unsigned)P);
   if (args.gloc && P > 1) {
-    CLA_LAUNCH("chunk_dq", (chunk_fwd_kernel<DK, DV, 2>), g, dim3(NTHR), stream, args);
+    CLA_LAUNCH("chunk_dq", (chunk_fwd_kernel<DK, DV, true>), g, dim3(NTHR), stream, args);
   } else {
-    CLA_LAUNCH(args.xdot ? "chunk_dq" : "chunk_fwd", (chunk_fwd_kernel<DK, DV, 0>), g,
+    CLA_LAUNCH(args.xdot ? "chunk_dq" : "chunk_fwd", (chunk_fwd_kernel<DK, DV, false>), g,
                dim3(NTHR), stream, args);
   }
   return hipGetLastError();
