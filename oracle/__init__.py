@@ -22,6 +22,9 @@ Modules:
 * ``oracle.attn``  -- matrix-state recurrence S_t = a_t S_{t-1} + k_t v_t^T,
   o_t = S_t^T q_t: per-token loop, the T x T matrix mode, the chunkwise
   algorithm in the pages' order, and the backward by the adjoint recurrence.
+* ``oracle.gla``   -- the same with one decay per key dimension (gated linear
+  attention), S_t = diag(a_t) S_{t-1} + k_t v_t^T: loop, matrix mode,
+  chunkwise form, adjoint backward and the closed-form vector decay gradient.
 * ``oracle.cref``  -- ctypes wrapper over ``oracle/ref.c``, the same loops in
   C (float64, OpenMP over independent channels / heads) for full-size samples
   and for the CPU baseline timing.
@@ -31,6 +34,6 @@ against values printed on the pages, closed forms, brute force on tiny inputs
 or finite differences; none is "parity unpinned".
 """
 
-from . import scan, attn  # noqa: F401
+from . import scan, attn, gla  # noqa: F401
 
-__all__ = ["scan", "attn"]
+__all__ = ["scan", "attn", "gla"]

@@ -44,6 +44,8 @@ def _load():
         lib.oracle_scan_bwd.argtypes = [p, p, p, p, p, p, p, p] + [i64] * 7
         lib.oracle_la_fwd.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, p, i64]
         lib.oracle_la_bwd.argtypes = [p] * 12 + [i64, i64, i64, p, i64]
+        lib.oracle_gla_fwd.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, p, i64]
+        lib.oracle_gla_bwd.argtypes = [p] * 12 + [i64, i64, i64, p, i64]
         _lib = lib
     return _lib
 
@@ -142,4 +144,43 @@ def la_bwd(q, k, v, l, S0, dO, dST=None, heads=None):
     lib.oracle_la_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(l), _ptr(S0), _ptr(dO),
                       _ptr(dST), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dl),
                       _ptr(dS0), T, DK, DV, _ptr(hs), n)
+    return dq, dk, dv, dl, dS0
+
+
+def gla_fwd(q, k, v, l, S0=None, heads=None):
+    """One decay per key dimension: l is float32 [B, H, T, DK]; the rest as
+    ``la_fwd``.  Returns (o [n, T, DV], ST [n, DK, DV]) float64."""
+    lib = _load()
+    q, k, v = _c(q, np.uint16), _c(k, np.uint16), _c(v, np.uint16)
+    l = _c(l, np.float32)
+    S0 = _c(S0, np.float32)
+    B, H, T, DK = q.shape
+    DV = v.shape[-1]
+    hs = _heads(heads, B, H)
+    o = np.empty((len(hs), T, DV))
+    ST = np.empty((len(hs), DK, DV))
+    lib.oracle_gla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(l), _ptr(S0), _ptr(o),
+                       _ptr(ST), T, DK, DV, _ptr(hs), len(hs))
+    return o, ST
+
+
+def gla_bwd(q, k, v, l, S0, dO, dST=None, heads=None):
+    """Backward of ``gla_fwd``.  Returns (dq, dk, dv, dl [n, T, DK], dS0)."""
+    lib = _load()
+    q, k, v, dO = (_c(x, np.uint16) for x in (q, k, v, dO))
+    l = _c(l, np.float32)
+    S0 = _c(S0, np.float32)
+    dST = _c(dST, np.float32)
+    B, H, T, DK = q.shape
+    DV = v.shape[-1]
+    hs = _heads(heads, B, H)
+    n = len(hs)
+    dq = np.empty((n, T, DK))
+    dk = np.empty((n, T, DK))
+    dv = np.empty((n, T, DV))
+    dl = np.empty((n, T, DK))
+    dS0 = np.empty((n, DK, DV))
+    lib.oracle_gla_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(l), _ptr(S0), _ptr(dO),
+                       _ptr(dST), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dl),
+                       _ptr(dS0), T, DK, DV, _ptr(hs), n)
     return dq, dk, dv, dl, dS0

@@ -235,3 +235,141 @@ void oracle_la_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     free(cp);
   }
 }
+
+/*
+ * Matrix-state recurrence with one decay per key dimension (gated linear
+ * attention), forward, for a list of heads.  ZTF "Scans over vector and
+ * matrix states" (the diagonal transition) and "The chunkwise algorithm" (the
+ * GLA form S_t = G_t (.) S_{t-1} + k_t^T v_t): row x of the state decays by
+ * a_t[x] = exp(l_t[x]), then o_t = S_t^T q_t.
+ * l: [B, H, T, DK] fp32.  Other arguments as oracle_la_fwd.
+ */
+void oracle_gla_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                    const float *l, const float *S0, double *o, double *ST,
+                    int64_t T, int64_t DK, int64_t DV, const int64_t *heads,
+                    int64_t nheads) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < nheads; ++i) {
+    int64_t hd = heads[i];
+    const uint16_t *qh = q + hd * T * DK, *kh = k + hd * T * DK, *vh = v + hd * T * DV;
+    const float *lh = l + hd * T * DK;
+    double *S = (double *)malloc(sizeof(double) * DK * DV);
+    double *kt = (double *)malloc(sizeof(double) * (DK + DV + DK + DK));
+    double *vt = kt + DK, *qt = vt + DV, *at = qt + DK;
+    for (int64_t e = 0; e < DK * DV; ++e) S[e] = S0 ? (double)S0[hd * DK * DV + e] : 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      for (int64_t x = 0; x < DK; ++x) at[x] = exp((double)lh[t * DK + x]);
+      for (int64_t x = 0; x < DK; ++x) kt[x] = bf16_to_double(kh[t * DK + x]);
+      for (int64_t x = 0; x < DK; ++x) qt[x] = bf16_to_double(qh[t * DK + x]);
+      for (int64_t y = 0; y < DV; ++y) vt[y] = bf16_to_double(vh[t * DV + y]);
+      for (int64_t x = 0; x < DK; ++x)
+        for (int64_t y = 0; y < DV; ++y) S[x * DV + y] = at[x] * S[x * DV + y] + kt[x] * vt[y];
+      double *ot = o + (i * T + t) * DV;
+      for (int64_t y = 0; y < DV; ++y) ot[y] = 0.0;
+      for (int64_t x = 0; x < DK; ++x)
+        for (int64_t y = 0; y < DV; ++y) ot[y] += S[x * DV + y] * qt[x];
+    }
+    memcpy(ST + i * DK * DV, S, sizeof(double) * DK * DV);
+    free(kt);
+    free(S);
+  }
+}
+
+/*
+ * The same recurrence, backward (ZTF "The backward pass of linear attention"
+ * with the diagonal decay): Sbar_T = q_T dO_T^T + dS_T,
+ * Sbar_t = q_t dO_t^T + diag(a_{t+1}) Sbar_{t+1}; dq_t = S_t dO_t,
+ * dk_t = Sbar_t v_t, dv_t = Sbar_t^T k_t,
+ * dl_t[x] = a_t[x] <Sbar_t[x, :], S_{t-1}[x, :]>, dS0 = diag(a_1) Sbar_1.
+ * States are recomputed from checkpoints every CK steps, as in oracle_la_bwd.
+ * Outputs: dq, dk, dl [nheads, T, DK]; dv [nheads, T, DV]; dS0 [nheads, DK, DV].
+ */
+void oracle_gla_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                    const float *l, const float *S0, const uint16_t *dO,
+                    const float *dST, double *dq, double *dk, double *dv,
+                    double *dl, double *dS0, int64_t T, int64_t DK, int64_t DV,
+                    const int64_t *heads, int64_t nheads) {
+  const int64_t CK = 64;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < nheads; ++i) {
+    int64_t hd = heads[i];
+    const uint16_t *qh = q + hd * T * DK, *kh = k + hd * T * DK, *vh = v + hd * T * DV;
+    const uint16_t *doh = dO + hd * T * DV;
+    const float *lh = l + hd * T * DK;
+    int64_t SZ = DK * DV;
+    int64_t ncp = T / CK + 1;
+    double *cp = (double *)malloc(sizeof(double) * SZ * ncp);
+    double *blk = (double *)malloc(sizeof(double) * SZ * (CK + 1));
+    double *Sb = (double *)malloc(sizeof(double) * SZ);
+    double *tmp = (double *)malloc(sizeof(double) * (3 * DK + 2 * DV));
+    double *kt = tmp, *qt = tmp + DK, *at = tmp + 2 * DK, *vt = tmp + 3 * DK,
+           *dot = tmp + 3 * DK + DV;
+    double *S = blk;
+    for (int64_t e = 0; e < SZ; ++e) S[e] = S0 ? (double)S0[hd * SZ + e] : 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      if (t % CK == 0) memcpy(cp + (t / CK) * SZ, S, sizeof(double) * SZ);
+      for (int64_t x = 0; x < DK; ++x) at[x] = exp((double)lh[t * DK + x]);
+      for (int64_t x = 0; x < DK; ++x) kt[x] = bf16_to_double(kh[t * DK + x]);
+      for (int64_t y = 0; y < DV; ++y) vt[y] = bf16_to_double(vh[t * DV + y]);
+      for (int64_t x = 0; x < DK; ++x)
+        for (int64_t y = 0; y < DV; ++y) S[x * DV + y] = at[x] * S[x * DV + y] + kt[x] * vt[y];
+    }
+    for (int64_t e = 0; e < SZ; ++e) Sb[e] = dST ? (double)dST[hd * SZ + e] : 0.0;
+    int64_t nblk = (T + CK - 1) / CK;
+    for (int64_t c = nblk - 1; c >= 0; --c) {
+      int64_t t0 = c * CK, n = (T - t0 < CK) ? T - t0 : CK;
+      memcpy(blk, cp + c * SZ, sizeof(double) * SZ);
+      for (int64_t j = 0; j < n; ++j) {
+        int64_t t = t0 + j;
+        for (int64_t x = 0; x < DK; ++x) at[x] = exp((double)lh[t * DK + x]);
+        for (int64_t x = 0; x < DK; ++x) kt[x] = bf16_to_double(kh[t * DK + x]);
+        for (int64_t y = 0; y < DV; ++y) vt[y] = bf16_to_double(vh[t * DV + y]);
+        const double *Sp = blk + j * SZ;
+        double *Sn = blk + (j + 1) * SZ;
+        for (int64_t x = 0; x < DK; ++x)
+          for (int64_t y = 0; y < DV; ++y)
+            Sn[x * DV + y] = at[x] * Sp[x * DV + y] + kt[x] * vt[y];
+      }
+      for (int64_t j = n - 1; j >= 0; --j) {
+        int64_t t = t0 + j;
+        if (t < T - 1) {
+          for (int64_t x = 0; x < DK; ++x) {
+            double an = exp((double)lh[(t + 1) * DK + x]);
+            for (int64_t y = 0; y < DV; ++y) Sb[x * DV + y] *= an;
+          }
+        }
+        for (int64_t x = 0; x < DK; ++x) qt[x] = bf16_to_double(qh[t * DK + x]);
+        for (int64_t x = 0; x < DK; ++x) kt[x] = bf16_to_double(kh[t * DK + x]);
+        for (int64_t y = 0; y < DV; ++y) vt[y] = bf16_to_double(vh[t * DV + y]);
+        for (int64_t y = 0; y < DV; ++y) dot[y] = bf16_to_double(doh[t * DV + y]);
+        for (int64_t x = 0; x < DK; ++x)
+          for (int64_t y = 0; y < DV; ++y) Sb[x * DV + y] += qt[x] * dot[y];
+        const double *Sprev = blk + j * SZ, *Scur = blk + (j + 1) * SZ;
+        double *gq = dq + (i * T + t) * DK, *gk = dk + (i * T + t) * DK;
+        double *gv = dv + (i * T + t) * DV, *gl = dl + (i * T + t) * DK;
+        for (int64_t x = 0; x < DK; ++x) {
+          double sq = 0.0, sk = 0.0, sl = 0.0;
+          for (int64_t y = 0; y < DV; ++y) {
+            sq += Scur[x * DV + y] * dot[y];
+            sk += Sb[x * DV + y] * vt[y];
+            sl += Sb[x * DV + y] * Sprev[x * DV + y];
+          }
+          gq[x] = sq;
+          gk[x] = sk;
+          gl[x] = exp((double)lh[t * DK + x]) * sl;
+        }
+        for (int64_t y = 0; y < DV; ++y) gv[y] = 0.0;
+        for (int64_t x = 0; x < DK; ++x)
+          for (int64_t y = 0; y < DV; ++y) gv[y] += Sb[x * DV + y] * kt[x];
+      }
+    }
+    for (int64_t x = 0; x < DK; ++x) {
+      double a1 = T > 0 ? exp((double)lh[x]) : 1.0;
+      for (int64_t y = 0; y < DV; ++y) dS0[i * SZ + x * DV + y] = a1 * Sb[x * DV + y];
+    }
+    free(tmp);
+    free(Sb);
+    free(blk);
+    free(cp);
+  }
+}

@@ -148,7 +148,7 @@ class ChunkInputs:
     q: np.ndarray            # [B, H, T, DK] uint16 (bf16 bits)
     k: np.ndarray            # [B, H, T, DK] uint16
     v: np.ndarray            # [B, H, T, DV] uint16
-    l: np.ndarray            # [B, H, T] float32 log decay
+    l: np.ndarray            # [B, H, T] float32 log decay ([B, H, T, DK]: per key dim)
     S0: np.ndarray | None    # [B, H, DK, DV] float32
     dO: np.ndarray           # [B, H, T, DV] uint16
     dST: np.ndarray | None   # [B, H, DK, DV] float32
@@ -186,6 +186,38 @@ def chunk_inputs(B, H, T, DK, DV, seed, qk_scale=1.0, v_scale=1.0,
         l = (-np.logaddexp(0.0, x) * 0.1).astype(np.float32).reshape(B, H, T)
         u = _draw(ss[3].spawn(1)[0], B * H * T, "uniform64", (0.0, 1.0)).reshape(B, H, T)
         l[u < decay[1]] = -np.inf
+    else:
+        raise ValueError(f"unknown decay kind {decay!r}")
+    S0 = None if S0_scale is None else _normal_f32(ss[4], (B, H, DK, DV), S0_scale)
+    dO = _normal_bf16(ss[5], (B, H, T, DV))
+    dST = None if dST_scale is None else _normal_f32(ss[6], (B, H, DK, DV), dST_scale)
+    return ChunkInputs(q, k, v, l, S0, dO, dST)
+
+
+def gla_inputs(B, H, T, DK, DV, seed, qk_scale=None, v_scale=1.0,
+               decay="logsigmoid", S0_scale=None, dST_scale=None) -> ChunkInputs:
+    """Inputs with one log decay per key dimension, l [B, H, T, DK] fp32.
+    q, k ~ N(0,1) * qk_scale (default 1/sqrt(DK)), v ~ N(0,1) * v_scale, dO ~
+    N(0,1), all bf16.  decay: 'logsigmoid' -> l = logsigmoid(x) / 16 with x ~
+    N(0,1) (a sigmoid gate raised to the power 1/16); ('logsigmoid', tau) ->
+    logsigmoid(x) / tau; ('const', c) -> l = c everywhere; ('uniform', lo, hi)
+    -> l ~ U(lo, hi)."""
+    if qk_scale is None:
+        qk_scale = 1.0 / math.sqrt(DK)
+    ss = np.random.SeedSequence(seed).spawn(7)
+    q = _normal_bf16(ss[0], (B, H, T, DK), qk_scale)
+    k = _normal_bf16(ss[1], (B, H, T, DK), qk_scale)
+    v = _normal_bf16(ss[2], (B, H, T, DV), v_scale)
+    n = B * H * T * DK
+    if decay == "logsigmoid" or (isinstance(decay, tuple) and decay[0] == "logsigmoid"):
+        tau = 16.0 if decay == "logsigmoid" else float(decay[1])
+        x = _draw(ss[3], n, "normal32").astype(np.float64)
+        l = (-np.logaddexp(0.0, -x) / tau).astype(np.float32).reshape(B, H, T, DK)
+    elif isinstance(decay, tuple) and decay[0] == "const":
+        l = np.full((B, H, T, DK), decay[1], dtype=np.float32)
+    elif isinstance(decay, tuple) and decay[0] == "uniform":
+        l = _draw(ss[3], n, "uniform64", (decay[1], decay[2])).astype(np.float32)
+        l = l.reshape(B, H, T, DK)
     else:
         raise ValueError(f"unknown decay kind {decay!r}")
     S0 = None if S0_scale is None else _normal_f32(ss[4], (B, H, DK, DV), S0_scale)
