@@ -12,6 +12,10 @@ step of the computation runs in the library's HIP kernels.
     # training: the forward keeps the states the backward's segments start from
     o, S_T, saved = chunked_linear_attn(q, k, v, log_decay, S0, save_states=True)
     dq, dk, dv, dl, dS0 = chunked_linear_attn_bwd(q, k, v, log_decay, S0, dO, saved=saved)
+
+    # one log decay per key dimension (log_decay [B, H, T, DK])
+    o, ST              = gla(q, k, v, log_decay, S0=None)
+    dq, dk, dv, dl, dS0 = gla_bwd(q, k, v, log_decay, S0, dO, dST=None)
 """
 
 from ._lib import ClaError, lib  # noqa: F401
@@ -23,7 +27,11 @@ from .api import (  # noqa: F401
     scan_workspace_bytes,
     chunk_workspace_bytes,
     chunk_saved_bytes,
+    gla,
+    gla_bwd,
+    gla_workspace_bytes,
 )
 
 __all__ = ["scan", "scan_bwd", "chunked_linear_attn", "chunked_linear_attn_bwd",
-           "scan_workspace_bytes", "chunk_workspace_bytes", "chunk_saved_bytes", "ClaError"]
+           "scan_workspace_bytes", "chunk_workspace_bytes", "chunk_saved_bytes", "gla", "gla_bwd",
+           "gla_workspace_bytes", "ClaError"]

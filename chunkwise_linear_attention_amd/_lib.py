@@ -48,6 +48,9 @@ SIGNATURES = {
     "cla_chunk_saved_bytes": ([i64] * 6, sz),
     "cla_chunk_fwd_saved": ([p] * 8 + [sz] + [i64] * 6 + [p, sz, p], ctypes.c_int),
     "cla_chunk_bwd_saved": ([p] * 8 + [sz] + [p] * 5 + [i64] * 6 + [p, sz, p], ctypes.c_int),
+    "cla_gla_workspace_bytes": ([i64, i64, i64, i64, i64, i64, ctypes.c_int], sz),
+    "cla_gla_fwd": ([p] * 7 + [i64] * 6 + [p, sz, p], ctypes.c_int),
+    "cla_gla_bwd": ([p] * 12 + [i64] * 6 + [p, sz, p], ctypes.c_int),
     "cla_timing_enable": ([ctypes.c_int], ctypes.c_int),
     "cla_timing_read": ([p, p, p, ctypes.c_int], ctypes.c_int),
 }

@@ -193,3 +193,70 @@ def chunked_linear_attn_bwd(q, k, v, log_decay, S0, dO, dST=None, *, want_dS0=Tr
                                    _ptr(ws), wsb, _stream(dev))
         _lib.check("cla_chunk_bwd_saved", st)
     return dq, dk, dv, dl, dS0
+
+
+# ---------------------------------------------------------------------------
+# one decay per key dimension (gated linear attention)
+# ---------------------------------------------------------------------------
+
+
+def gla_workspace_bytes(B, H, T, DK, DV, backward=False, chunk=CHUNK) -> int:
+    return int(_lib.lib().cla_gla_workspace_bytes(B, H, T, DK, DV, chunk, int(backward)))
+
+
+def gla(q, k, v, log_decay, S0=None, *, want_final=True, chunk=CHUNK, workspace=None):
+    """S_t = diag(exp(l_t)) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t, chunkwise, with
+    one log decay per key dimension.  q, k: [B, H, T, DK] bf16; v: [B, H, T, DV]
+    bf16; log_decay: [B, H, T, DK] fp32; S0: [B, H, DK, DV] fp32 or None.
+    Returns (o bf16, S_T fp32 or None)."""
+    B, H, T, DK = q.shape
+    DV = v.shape[-1]
+    dev = q.device
+    _need(q, "q", torch.bfloat16, (B, H, T, DK), dev)
+    _need(k, "k", torch.bfloat16, (B, H, T, DK), dev)
+    _need(v, "v", torch.bfloat16, (B, H, T, DV), dev)
+    _need(log_decay, "log_decay", torch.float32, (B, H, T, DK), dev)
+    _opt(S0, "S0", torch.float32, (B, H, DK, DV), dev)
+    o = torch.empty((B, H, T, DV), dtype=torch.bfloat16, device=dev)
+    ST = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev) if want_final else None
+    L = _lib.lib()
+    nbytes = int(L.cla_gla_workspace_bytes(B, H, T, DK, DV, chunk, 0))
+    if workspace is None:
+        ws, wsb = _workspace(nbytes, dev)
+    else:
+        ws, wsb = workspace, workspace.numel() * workspace.element_size()
+    st = L.cla_gla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(S0), _ptr(o), _ptr(ST),
+                       B, H, T, DK, DV, chunk, _ptr(ws), wsb, _stream(dev))
+    _lib.check("cla_gla_fwd", st)
+    return o, ST
+
+
+def gla_bwd(q, k, v, log_decay, S0, dO, dST=None, *, want_dS0=True, chunk=CHUNK,
+            workspace=None):
+    """Backward of ``gla``: returns (dq, dk, dv, dlog_decay [B, H, T, DK], dS0)."""
+    B, H, T, DK = q.shape
+    DV = v.shape[-1]
+    dev = q.device
+    _need(q, "q", torch.bfloat16, (B, H, T, DK), dev)
+    _need(k, "k", torch.bfloat16, (B, H, T, DK), dev)
+    _need(v, "v", torch.bfloat16, (B, H, T, DV), dev)
+    _need(log_decay, "log_decay", torch.float32, (B, H, T, DK), dev)
+    _opt(S0, "S0", torch.float32, (B, H, DK, DV), dev)
+    _need(dO, "dO", torch.bfloat16, (B, H, T, DV), dev)
+    _opt(dST, "dST", torch.float32, (B, H, DK, DV), dev)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dl = torch.empty_like(log_decay)
+    dS0 = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev) if want_dS0 else None
+    L = _lib.lib()
+    nbytes = int(L.cla_gla_workspace_bytes(B, H, T, DK, DV, chunk, 1))
+    if workspace is None:
+        ws, wsb = _workspace(nbytes, dev)
+    else:
+        ws, wsb = workspace, workspace.numel() * workspace.element_size()
+    st = L.cla_gla_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(S0), _ptr(dO),
+                       _ptr(dST), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dl), _ptr(dS0),
+                       B, H, T, DK, DV, chunk, _ptr(ws), wsb, _stream(dev))
+    _lib.check("cla_gla_bwd", st)
+    return dq, dk, dv, dl, dS0

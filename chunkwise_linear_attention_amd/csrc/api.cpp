@@ -7,6 +7,7 @@
 #include <initializer_list>
 
 #include "../../include/cla.h"
+#include "gla_kernels.h"
 #include "internal.h"
 
 namespace {
@@ -250,6 +251,106 @@ int cla_chunk_bwd_saved(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   return chunk_bwd_impl(q, k, v, log_decay, S0, dO, dST, true, saved, saved_bytes, dq, dk, dv,
                         dlog_decay, dS0, B, H, T, DK, DV, chunk, workspace, workspace_bytes,
                         stream);
+}
+
+
+// ---- one decay per key dimension ----
+
+size_t cla_gla_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV,
+                               int64_t chunk, int backward) {
+  if (B < 0 || H < 0 || T < 0) return 0;
+  if (!supported_head_dim(DK) || !supported_head_dim(DV) || chunk != 64) return 0;
+  if (!backward || B == 0 || H == 0 || T == 0) return 0;
+  return cla::gla::gla_bwd_ws_bytes(B * H, T, DK, DV);
+}
+
+int cla_gla_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                const float *log_decay, const float *S0, uint16_t *o, float *ST, int64_t B,
+                int64_t H, int64_t T, int64_t DK, int64_t DV, int64_t chunk, void *workspace,
+                size_t workspace_bytes, cla_stream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (B < 0 || H < 0 || T < 0 || DK < 0 || DV < 0 || chunk < 0) return CLA_ERR_BAD_SHAPE;
+  if (!supported_head_dim(DK) || !supported_head_dim(DV) || chunk != 64)
+    return CLA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0) return CLA_OK;
+  const size_t nh = (size_t)B * (size_t)H;
+  if (nh > 0x7fffffffu) return CLA_ERR_UNSUPPORTED;
+  const size_t qk = nh * (size_t)T * (size_t)DK * 2, vv = nh * (size_t)T * (size_t)DV * 2;
+  const size_t ll = nh * (size_t)T * (size_t)DK * 4, ss = nh * (size_t)DK * (size_t)DV * 4;
+  if (T > 0 && (!q || !k || !v || !log_decay || !o)) return CLA_ERR_NULL_ARG;
+  if (T > 0 && !(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o) &&
+                 aligned16(log_decay)))
+    return CLA_ERR_UNSUPPORTED;
+  if (any_alias({{q, qk}, {k, qk}, {v, vv}, {log_decay, ll}, {S0, ss}}, {{o, vv}, {ST, ss}}))
+    return CLA_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0)
+    return ST ? hip_status(cla::launch_copy_or_zero(ST, S0, (int64_t)(nh * DK * DV), s))
+              : CLA_OK;
+  cla::gla::GlaFwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.l = log_decay;
+  a.S0 = S0;
+  a.o = o;
+  a.ST = ST;
+  a.nh = (int64_t)nh;
+  a.T = T;
+  return hip_status(cla::gla::gla_fwd_dispatch(a, (int)DK, (int)DV, s));
+}
+
+
+int cla_gla_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                const float *log_decay, const float *S0, const uint16_t *dO, const float *dST,
+                uint16_t *dq, uint16_t *dk, uint16_t *dv, float *dlog_decay, float *dS0,
+                int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV, int64_t chunk,
+                void *workspace, size_t workspace_bytes, cla_stream_t stream) {
+  if (B < 0 || H < 0 || T < 0 || DK < 0 || DV < 0 || chunk < 0) return CLA_ERR_BAD_SHAPE;
+  if (!supported_head_dim(DK) || !supported_head_dim(DV) || chunk != 64)
+    return CLA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0) return CLA_OK;
+  const size_t nh = (size_t)B * (size_t)H;
+  if (nh > 0x7fffffffu) return CLA_ERR_UNSUPPORTED;
+  const size_t qk = nh * (size_t)T * (size_t)DK * 2, vv = nh * (size_t)T * (size_t)DV * 2;
+  const size_t ll = nh * (size_t)T * (size_t)DK * 4, ss = nh * (size_t)DK * (size_t)DV * 4;
+  if (T > 0 && (!q || !k || !v || !log_decay || !dO || !dq || !dk || !dv || !dlog_decay))
+    return CLA_ERR_NULL_ARG;
+  if (T > 0 && !(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(dO) &&
+                 aligned16(dq) && aligned16(dk) && aligned16(dv) && aligned16(log_decay) &&
+                 aligned16(dlog_decay)))
+    return CLA_ERR_UNSUPPORTED;
+  const size_t need = T > 0 ? cla::gla::gla_bwd_ws_bytes((int64_t)nh, T, DK, DV) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return CLA_ERR_WORKSPACE;
+  const Range ws{need ? workspace : nullptr, need};
+  if (any_alias({{q, qk}, {k, qk}, {v, vv}, {log_decay, ll}, {S0, ss}, {dO, vv}, {dST, ss}},
+                {{dq, qk}, {dk, qk}, {dv, vv}, {dlog_decay, ll}, {dS0, ss}, ws}))
+    return CLA_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0)
+    return dS0 ? hip_status(cla::launch_copy_or_zero(dS0, dST, (int64_t)(nh * DK * DV), s))
+               : CLA_OK;
+  const size_t r1_bytes = ((size_t)nh * T * DK * sizeof(float) + 255) & ~(size_t)255;
+  cla::gla::GlaBwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dO = dO;
+  a.l = log_decay;
+  a.S0 = S0;
+  a.dST = dST;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dl = dlog_decay;
+  a.dS0 = dS0;
+  a.r1 = static_cast<float *>(workspace);
+  a.Sseg = reinterpret_cast<float *>(static_cast<char *>(workspace) + r1_bytes);
+  a.nh = (int64_t)nh;
+  a.T = T;
+  return hip_status(cla::gla::gla_bwd_dispatch(a, (int)DK, (int)DV, s));
 }
 
 }  // extern "C"

@@ -1,0 +1,437 @@
+// Chunkwise linear attention with one decay per key dimension (gated linear
+// attention), forward pass, for gfx950.
+//
+// Citations (page title, then section):
+//   ZTF = "Parallel scan" (zerotofrontier.app, ssm/parallel-scan)
+//
+// Recurrence (ZTF "The chunkwise algorithm", the GLA form): row d of the
+// state decays by its own a_t[d] = exp(l_t[d]),
+//   S_t = diag(a_t) S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t.
+// Chunks of 64 tokens; inside a chunk c_r[d] = l_1[d] + .. + l_r[d] is summed
+// in fp32 over the chunk's own logs only (ZTF "Long products without
+// underflow": short windows, no long cumulative sums).  The three segment
+// products become per-dimension:
+//   scores   A[r, s] = sum_d q_r[d] k_s[d] exp(c_r[d] - c_s[d])   (s <= r)
+//   read     O_r    += sum_d q_r[d] exp(c_r[d]) S[d, :]
+//   update   S[d, :] = exp(c_n[d]) S[d, :] + sum_s k_s[d] exp(c_n[d] - c_s[d]) v_s
+// The scores no longer factor through one matrix product with an elementwise
+// mask, and exp(c_r) exp(-c_s) overflows for strong decays.  The chunk is cut
+// into four sub-blocks of 16 tokens; with cb_R / ce_R the cumulative logs at
+// the start / end of block R (cb_0 = 0, cb_R = ce_{R-1}):
+//   Qh[r, d] = q_r[d] exp(c_r[d] - cb_R[d])     (r in block R; factor <= 1)
+//   Kh[s, d] = k_s[d] exp(ce_S[d] - c_s[d])     (s in block S; factor <= 1)
+// For S < R,  A[r, s] = sum_d Qh[r, d] Kh[s, d] exp(cb_R[d] - ce_S[d]), where
+// the last factor (the decay between the two blocks) is <= 1 as well: every
+// factor lies in (0, 1], so nothing overflows and a factor that underflows
+// only drops a product that is itself below fp32 range.  For S = R the middle
+// factor is exp(cb_R - ce_R) >= 1, the inverse of the block's own decay; while
+// that decay stays above exp(-60) in every dimension the same product form is
+// used (all factors within exp(+-60)); a block whose decay falls below it in
+// some dimension has its diagonal scores computed elementwise, exactly, from
+// the raw q and k rows.  The read and the update use
+//   QL[r, d] = Qh[r, d] exp(cb_R[d]),   KG[s, d] = Kh[s, d] exp(c_n[d] - ce_S[d]),
+// both products of factors <= 1.
+//
+// Workgroup = 4 waves on one (batch*head); wave w owns value columns
+// [w DV/4, (w+1) DV/4) of the state, held in MFMA accumulators.  LDS holds the
+// chunk's Q, K, V (bf16, swizzled rows) and its log decays (fp32, then the
+// cumulative logs), 80 KB at DK = DV = 128, so two workgroups share a CU.
+#include "chunk_common.h"
+#include "gla_kernels.h"
+#include "internal.h"
+
+namespace cla {
+namespace gla {
+
+using namespace cla::chunk;
+
+namespace {
+
+// Sub-block whose own decay is below exp(-kBadLog) in some dimension: its
+// diagonal scores are computed elementwise.
+constexpr float kBadLog = 60.f;
+
+// DMA of a [64 x D] fp32 tile, rows plain (unswizzled): 1 KB blocks of RPB
+// rows; rows past the chunk re-read row n - 1.
+template <int D>
+__device__ __forceinline__ void dma_f32_block(const float *chunk_src, int n, unsigned char *tile,
+                                              int block, int lane) {
+  constexpr int PPR = D / 4;     // 16-byte pieces per row
+  constexpr int RPB = 64 / PPR;  // rows per 1 KB block
+  const int row = block * RPB + lane / PPR;
+  const int grow = min(row, n - 1);
+  __builtin_amdgcn_global_load_lds(chunk_src + (int64_t)grow * D + (lane % PPR) * 4,
+                                   (lds_void *)(tile + block * 1024), 16, 0, 0);
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
+  constexpr int NJ = DV / 64;   // 16-column tiles of the state per wave
+  constexpr int NDT = DK / 16;  // 16-row tiles of the state
+  constexpr int NCK = DK / 8, NCV = DV / 8;
+  constexpr int B_KS = 64 * DK * 2;
+  constexpr int B_VS = B_KS + 64 * DK * 2;
+  constexpr int B_CS = B_VS + 64 * DV * 2;
+  constexpr int BUF = B_CS + 64 * DK * 4;
+  constexpr int NBQ = DK / 8, NBV = DV / 8, NBL = DK / 4;
+  constexpr int NBLK = 2 * NBQ + NBV + NBL;
+  // Once the scores are formed, the score tile P [64][64] bf16 (8 KB) reuses
+  // the first rows of the cumulative logs and the per-block factors the rest
+  // of the chunk needs go to rows 50..58 (interior rows of block 3).
+  constexpr int P_ROWS = 8192 / (DK * 4);  // rows of the logs P covers
+  static_assert(P_ROWS <= 32 && BUF <= 80 * 1024, "LDS layout");
+  constexpr int R_FQ = 50, R_FK = 54, R_AL = 58;
+  __shared__ __attribute__((aligned(1024))) unsigned char buf[BUF];
+  unsigned char *QS = buf;
+  unsigned char *KS = buf + B_KS;
+  unsigned char *VS = buf + B_VS;
+  float *CS = reinterpret_cast<float *>(buf + B_CS);
+  unsigned char *PS = buf + B_CS;
+
+  const int tid0 = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+  // Lane coordinates are re-derived behind an empty asm at the start of each
+  // phase, so that the compiler forms LDS addresses next to their use instead
+  // of hoisting them all out of the chunk loop (which exhausts registers).
+  int tid = tid0, lane = tid0 & 63, li = lane & 15, lg = lane >> 4;
+#define FRESH_LANE()             \
+  do {                           \
+    int t_ = tid0;               \
+    asm volatile("" : "+v"(t_)); \
+    tid = t_;                    \
+    lane = t_ & 63;              \
+    li = lane & 15;              \
+    lg = lane >> 4;              \
+  } while (0)
+  const int64_t bh = blockIdx.x;
+  const int64_t T = a.T;
+  const int64_t nchunks = (T + TC - 1) / TC;
+  const int j0 = w * (DV / 4);
+  const uint16_t *qh = a.q + bh * T * DK;
+  const uint16_t *kh = a.k + bh * T * DK;
+  const uint16_t *vh = a.v + bh * T * DV;
+  const float *lh = a.l + bh * T * DK;
+
+  // S_acc[dt][jt][i] = S[16 dt + 4 lg + i][j0 + 16 jt + li]
+  f32x4 S_acc[NDT][NJ];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) S_acc[dt][jt] = zero4();
+  if (a.S0) {
+    const float *src = a.S0 + bh * DK * DV;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          S_acc[dt][jt][i] = src[(16 * dt + 4 * lg + i) * DV + j0 + 16 * jt + li];
+  }
+
+  for (int64_t ci = 0; ci < nchunks; ++ci) {
+    const int64_t t0 = ci * TC;
+    const int n = (int)min<int64_t>(TC, T - t0);
+
+    // ---- stage: Q, K, V, l of the chunk into LDS ----
+    lds_barrier();  // the previous chunk's LDS reads are done
+    FRESH_LANE();
+    for (int b = w; b < NBLK; b += NWAVE) {
+      if (b < NBQ)
+        dma_block<DK>(qh + t0 * DK, n, QS, b, lane);
+      else if (b < 2 * NBQ)
+        dma_block<DK>(kh + t0 * DK, n, KS, b - NBQ, lane);
+      else if (b < 2 * NBQ + NBV)
+        dma_block<DV>(vh + t0 * DV, n, VS, b - 2 * NBQ, lane);
+      else
+        dma_f32_block<DK>(lh + t0 * DK, n, buf + B_CS, b - 2 * NBQ - NBV, lane);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+
+    // ---- cumulative logs, in place: NP parts of RP rows per dimension ----
+    {
+      FRESH_LANE();
+      constexpr int NP = NTHR / DK, RP = 64 / NP;
+      const int d = tid % DK, part = tid / DK;
+      float run = 0.f;
+#pragma unroll
+      for (int i = 0; i < RP; ++i) {
+        const int r = part * RP + i;
+        run += r < n ? CS[r * DK + d] : 0.f;  // rows past the chunk: no decay
+        CS[r * DK + d] = run;
+      }
+      lds_barrier();
+      float off = 0.f;
+      for (int p = 0; p < part; ++p) off += CS[(p * RP + RP - 1) * DK + d];
+      lds_barrier();
+      if (part > 0) {
+#pragma unroll
+        for (int i = 0; i < RP; ++i) CS[(part * RP + i) * DK + d] += off;
+      }
+      lds_barrier();
+    }
+
+    // ---- Qh, Kh in place (8 elements per step) ----
+    FRESH_LANE();
+    for (int g = tid; g < 64 * NCK; g += NTHR) {
+      const int r = g / NCK, c8 = g % NCK;
+      const int B = r >> 4;
+      const int off = swz_off<NCK>(r, c8);
+      const float *cr = CS + r * DK + 8 * c8;
+      const float *ce = CS + (16 * B + 15) * DK + 8 * c8;
+      const float *cb = CS + (16 * B - 1) * DK + 8 * c8;  // read only when B > 0
+      bf16x8 qv = *reinterpret_cast<const bf16x8 *>(QS + off);
+      bf16x8 kv = *reinterpret_cast<const bf16x8 *>(KS + off);
+      float yq[8], yk[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float cbe = B > 0 ? cb[e] : 0.f;
+        yq[e] = tof(qv[e]) * __expf(cr[e] - cbe);
+        yk[e] = r < n ? tof(kv[e]) * __expf(ce[e] - cr[e]) : 0.f;
+      }
+      *reinterpret_cast<bf16x8 *>(QS + off) = cvt8(yq);
+      *reinterpret_cast<bf16x8 *>(KS + off) = cvt8(yk);
+    }
+    lds_barrier();
+
+    // ---- scores: tile (R, S), S <= R, as acc[i] = A[16R + li][16S + 4lg + i] ----
+    // wave w: the diagonal tile (w, w) and the off-diagonal tiles w, w + 4 of
+    // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+    f32x4 sc[3];
+    int tR[3], tS[3];
+    int ntile = 0;
+    {
+      const int offR = 0x122333, offS = 0x001012;  // packed (R, S) of the six
+      tR[0] = w;
+      tS[0] = w;
+      ntile = 1;
+      for (int t = w; t < 6; t += NWAVE) {
+        tR[ntile] = (offR >> (4 * (5 - t))) & 15;
+        tS[ntile] = (offS >> (4 * (5 - t))) & 15;
+        ++ntile;
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      if (x >= ntile) break;
+      FRESH_LANE();
+      const int R = tR[x], S = tS[x];
+      f32x4 acc = zero4();
+      // a diagonal block whose decay falls below exp(-kBadLog) in some
+      // dimension is done elementwise (wave-uniform decision)
+      bool exact = false;
+      if (R == S) {
+        bool bad = false;
+        for (int d = lane; d < DK; d += 64) {
+          const float cbd = R > 0 ? CS[(16 * R - 1) * DK + d] : 0.f;
+          bad |= cbd - CS[(16 * R + 15) * DK + d] > kBadLog;
+        }
+        exact = __ballot(bad) != 0;
+      }
+      if (!exact) {
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+          const int d0 = 32 * kk + 8 * lg;  // this lane's 8 dimensions
+          const float *cbR = CS + (16 * R - 1) * DK + d0;
+          const float *ceS = CS + (16 * S + 15) * DK + d0;
+          const bf16x8 kv = lds_frag<NCK>(KS, 16 * S + li, 4 * kk + lg);
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            y[e] = tof(kv[e]) * __expf((R > 0 ? cbR[e] : 0.f) - ceS[e]);
+          acc = mfma(cvt8(y), lds_frag<NCK>(QS, 16 * R + li, 4 * kk + lg), acc);
+        }
+      } else {
+        // exact: sum_d q_r[d] k_s[d] exp(c_r[d] - c_s[d]) from the raw rows
+        const int r = 16 * R + li;
+        const int rr = min(r, n - 1);
+        const uint16_t *qrow = qh + (t0 + rr) * DK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * R + 4 * lg + i;
+          const uint16_t *krow = kh + (t0 + min(s, n - 1)) * DK;
+          float sum = 0.f;
+          if (s <= r) {
+            for (int d0 = 0; d0 < DK; d0 += 8) {
+              const bf16x8 qv = *reinterpret_cast<const bf16x8 *>(qrow + d0);
+              const bf16x8 kv = *reinterpret_cast<const bf16x8 *>(krow + d0);
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                sum += tof(qv[e]) * tof(kv[e]) *
+                       __expf(CS[r * DK + d0 + e] - CS[s * DK + d0 + e]);
+            }
+          }
+          acc[i] = sum;
+        }
+      }
+      // causal and chunk-length masks
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * R + li, s = 16 * S + 4 * lg + i;
+        if (s > r || s >= n || r >= n) acc[i] = 0.f;
+      }
+      sc[x] = acc;
+    }
+    lds_barrier();  // every read of the cumulative logs' interior rows is done
+
+    // ---- per-block factors (from the block-end rows, before P covers them) ----
+    FRESH_LANE();
+    for (int d = tid; d < DK; d += NTHR) {
+      float ce[4];
+#pragma unroll
+      for (int B = 0; B < 4; ++B) ce[B] = CS[(16 * B + 15) * DK + d];
+      const float cl = ce[3];  // the chunk's last cumulative log (rows past n add 0)
+#pragma unroll
+      for (int B = 0; B < 4; ++B) {
+        CS[(R_FQ + B) * DK + d] = B > 0 ? __expf(ce[B - 1]) : 1.f;  // exp(cb_B)
+        CS[(R_FK + B) * DK + d] = __expf(cl - ce[B]);
+      }
+      CS[R_AL * DK + d] = __expf(cl);
+    }
+    lds_barrier();
+    // ---- P[r][s] (bf16) over the first rows of the logs ----
+    FRESH_LANE();
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      if (x >= ntile) break;
+      const int R = tR[x], S = tS[x];
+      bf16x4 pv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[i] = tobf(sc[x][i]);
+      // P row r = 16R + li, columns 16S + 4lg .. + 3
+      *reinterpret_cast<bf16x4 *>(PS + swz_off<8>(16 * R + li, 2 * S + (lg >> 1)) + (lg & 1) * 8) =
+          pv;
+    }
+    // the output reads P in 32-column steps up to the diagonal, which covers
+    // the two tiles (0, 1) and (2, 3) above it: they hold zeros
+    if (w >= 2) {
+      const int R = w == 2 ? 0 : 2;
+      const bf16x4 z = {tobf(0.f), tobf(0.f), tobf(0.f), tobf(0.f)};
+      *reinterpret_cast<bf16x4 *>(PS + swz_off<8>(16 * R + li, 2 * (R + 1) + (lg >> 1)) +
+                                  (lg & 1) * 8) = z;
+    }
+    lds_barrier();
+
+    // ---- output: O^T[j][r] = (V^T P^T)[j][r] + (S^T QL^T)[j][r] ----
+    {
+      FRESH_LANE();
+      bf16x8 vfrag[NJ][2];
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) vfrag[jt][kb] = tr_frag<NCV>(VS, 32 * kb, j0 + 16 * jt, li, lg);
+      bf16x8 sfrag[DK / 32][NJ];
+#pragma unroll
+      for (int kk = 0; kk < DK / 32; ++kk)
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) sfrag[kk][jt] = cvt8(S_acc[2 * kk][jt], S_acc[2 * kk + 1][jt]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int rr = 16 * rt + li;
+        const float *fq = CS + (R_FQ + rt) * DK;
+        bf16x8 qfrag[DK / 32];  // QL^T B operands, k = {32kk + 4lg + 0..3, +16}
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+          const int da = 32 * kk + 4 * lg, db = da + 16;
+          const bf16x4 lo = lds_half<NCK>(QS, rr, da);
+          const bf16x4 hi = lds_half<NCK>(QS, rr, db);
+          const f32x4 fa = *reinterpret_cast<const f32x4 *>(fq + da);
+          const f32x4 fb = *reinterpret_cast<const f32x4 *>(fq + db);
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            y[e] = tof(lo[e]) * fa[e];
+            y[e + 4] = tof(hi[e]) * fb[e];
+          }
+          qfrag[kk] = cvt8(y);
+        }
+        bf16x8 pfrag[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) pfrag[kb] = lds_frag<8>(PS, rr, 4 * kb + lg);
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int kk = 0; kk < DK / 32; ++kk) acc = mfma(sfrag[kk][jt], qfrag[kk], acc);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            if (kb <= (rt >> 1)) acc = mfma(vfrag[jt][kb], pfrag[kb], acc);
+          if (rr < n) {
+            bf16x4 ov;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ov[i] = tobf(acc[i]);
+            *reinterpret_cast<bf16x4 *>(a.o + (bh * T + t0 + rr) * DV + j0 + 16 * jt + 4 * lg) = ov;
+          }
+        }
+      }
+    }
+
+    // ---- state update: S <- diag(alpha) S + KG^T V ----
+    {
+      FRESH_LANE();
+      const float *al = CS + R_AL * DK;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const f32x4 av = *reinterpret_cast<const f32x4 *>(al + 16 * dt + 4 * lg);
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S_acc[dt][jt][i] *= av[i];
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 vb[NJ];  // V B operands: k = s, column j
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) vb[jt] = tr_frag<NCV>(VS, 32 * kb, j0 + 16 * jt, li, lg);
+        const int Sblk = 2 * kb + (lg >> 1);  // block of this lane's 8 rows s
+        const float *fk = CS + (R_FK + Sblk) * DK;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const bf16x8 kx = tr_frag<NCK>(KS, 32 * kb, 16 * dt, li, lg);  // Kh^T: row d, k = s
+          const float f = fk[16 * dt + li];
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = tof(kx[e]) * f;
+          const bf16x8 ka = cvt8(y);
+#pragma unroll
+          for (int jt = 0; jt < NJ; ++jt) S_acc[dt][jt] = mfma(ka, vb[jt], S_acc[dt][jt]);
+        }
+      }
+    }
+  }
+
+  FRESH_LANE();
+  if (a.ST) {
+    float *dst = a.ST + bh * DK * DV;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dst[(16 * dt + 4 * lg + i) * DV + j0 + 16 * jt + li] = S_acc[dt][jt][i];
+  }
+}
+
+#undef FRESH_LANE
+
+template <int DK, int DV>
+hipError_t gla_fwd_impl(const GlaFwdArgs &args, hipStream_t stream) {
+  CLA_LAUNCH("gla_fwd", (gla_fwd_kernel<DK, DV>), dim3((unsigned)args.nh), dim3(NTHR), stream,
+             args);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t gla_fwd_dispatch(const GlaFwdArgs &args, int DK, int DV, hipStream_t stream) {
+  if (DK == 64 && DV == 64) return gla_fwd_impl<64, 64>(args, stream);
+  if (DK == 64 && DV == 128) return gla_fwd_impl<64, 128>(args, stream);
+  if (DK == 128 && DV == 64) return gla_fwd_impl<128, 64>(args, stream);
+  if (DK == 128 && DV == 128) return gla_fwd_impl<128, 128>(args, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gla
+}  // namespace cla

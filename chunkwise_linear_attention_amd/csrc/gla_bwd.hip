@@ -1,0 +1,860 @@
+// Chunkwise linear attention with one decay per key dimension, backward pass,
+// for gfx950.
+//
+// Citations (page title, then section):
+//   ZTF = "Parallel scan" (zerotofrontier.app, ssm/parallel-scan)
+//
+// ZTF "The backward pass of linear attention" with the diagonal decay: the
+// adjoint obeys Sbar_t = q_t dO_t^T + diag(a_{t+1}) Sbar_{t+1}; a query's
+// gradient needs the forward state (a sweep in time order), a key's, value's
+// and decay's the adjoint (a sweep in reverse).  Chunkwise, with the in-chunk
+// cumulative logs c and the sub-block factors of the forward (gla.hip):
+//   dq_r[d] = sum_{s <= r} B[r, s] k_s[d] exp(c_r[d] - c_s[d])
+//             + exp(c_r[d]) (S dO_r)[d],                B[r, s] = dO_r . v_s
+//   dk_s[d] = sum_{r >= s} B[r, s] q_r[d] exp(c_r[d] - c_s[d])
+//             + exp(c_n[d] - c_s[d]) (G v_s)[d]
+//   dv_s    = sum_{r >= s} A[r, s] dO_r + sum_d k_s[d] exp(c_n[d] - c_s[d]) G[d, :]
+//   G      <- diag(exp(c_n)) G + (q (.) exp(c))^T dO    (state gradient entering the chunk)
+// with A the forward's decayed scores and G the gradient of the state after
+// the chunk.  The decay gradient is the closed form of ZTF for a vector of
+// decays (Yang et al. 2023, Section 4.3), per key dimension:
+//   dl_u[d] = sum_{t >= u} (q_t[d] dq_t[d] - k_t[d] dk_t[d]) + paths past the end,
+// evaluated in segments of 16 chunks: the suffix sums run inside a segment
+// only and start from the exact term <S[d, :], G[d, :]> of the two fp32 states
+// at the segment's end (the dQ pass saves S there), so no long sum of
+// cancelling terms builds up.  Inside a chunk, most paths do not cross a given
+// step and must cancel between the two sums; both passes therefore form the
+// in-chunk contributions to q dq and k dk from the same rounded operands: one
+// 16-deep MFMA per pair of 16-token blocks (Qh^T B or Kh^T B^T), the block
+// factor applied in fp32 after it, and q dq = Qh (.) that, k dk = Kh (.) that.
+//
+// dQ pass: 4 waves; wave w owns dq columns d in [w DK/4, (w+1) DK/4) and the
+// same columns of the state, kept transposed (S^T) in MFMA accumulators.
+// dK/dV pass: 8 waves; waves 0-3 own value columns of G (for dv), waves 4-7
+// key columns of G^T (for dk and the decay gradient); both copies are updated
+// every chunk, as in the scalar kernel.  One workgroup per sequence-head, one
+// per CU (LDS ~124 KB and ~150 KB at DK = DV = 128).
+#include "chunk_common.h"
+#include "gla_kernels.h"
+#include "internal.h"
+
+namespace cla {
+namespace gla {
+
+using namespace cla::chunk;
+
+namespace {
+
+constexpr float kBadLog = 60.f;  // as in the forward
+constexpr int BTHR = 512;
+
+// v_mfma_f32_16x16x16_bf16: lane 16 lg + li holds A row li and B column li,
+// k-values 4 lg .. 4 lg + 3; C as for the 32-deep instruction.
+typedef short __attribute__((ext_vector_type(4))) s16x4;
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// One path of the in-chunk score product, write s -> read t through key
+// dimension d: both passes form it with this same expression, so that the
+// decay gradient's two sums hold the same numbers and the paths that do not
+// cross a step cancel in it up to fp32 summation order.
+__device__ __forceinline__ float path_term(float b, float q, float k, float ct, float cs) {
+  return ((b * q) * k) * __expf(ct - cs);
+}
+
+template <int D>
+__device__ __forceinline__ void dma_f32_rows(const float *chunk_src, int n, unsigned char *tile,
+                                             int block, int lane) {
+  constexpr int PPR = D / 4;
+  constexpr int RPB = 64 / PPR;
+  const int row = block * RPB + lane / PPR;
+  const int grow = min(row, n - 1);
+  __builtin_amdgcn_global_load_lds(chunk_src + (int64_t)grow * D + (lane % PPR) * 4,
+                                   (lds_void *)(tile + block * 1024), 16, 0, 0);
+}
+
+// In-chunk cumulative logs, in place, with NTH threads (rows past n: no decay).
+template <int DK, int NTH>
+__device__ __forceinline__ void cumsum_rows(float *CS, int n, int tid) {
+  constexpr int NP = NTH / DK, RP = 64 / NP;
+  const int d = tid % DK, part = tid / DK;
+  float run = 0.f;
+#pragma unroll
+  for (int i = 0; i < RP; ++i) {
+    const int r = part * RP + i;
+    run += r < n ? CS[r * DK + d] : 0.f;
+    CS[r * DK + d] = run;
+  }
+  lds_barrier();
+  float off = 0.f;
+  for (int p = 0; p < part; ++p) off += CS[(p * RP + RP - 1) * DK + d];
+  lds_barrier();
+  if (part > 0) {
+#pragma unroll
+    for (int i = 0; i < RP; ++i) CS[(part * RP + i) * DK + d] += off;
+  }
+  lds_barrier();
+}
+
+// Scaled copies: Qh = q exp(c - cb_R) (if QH), Kh = k exp(ce_S - c), both 0 on
+// rows past the chunk (which hold copies of its last row), and the per-block
+// factor rows FQ[R] = exp(cb_R), FK[S] =
+// exp(c_n - ce_S), AL = exp(c_n).
+template <int DK, int NTH>
+__device__ __forceinline__ void prep_scaled(const unsigned char *QS, const unsigned char *KS,
+                                            unsigned char *QH, unsigned char *KH, const float *CS,
+                                            float *FQ, float *FK, float *AL, int n, int tid) {
+  constexpr int NCK = DK / 8;
+  for (int g = tid; g < 64 * NCK; g += NTH) {
+    const int r = g / NCK, c8 = g % NCK;
+    const int B = r >> 4;
+    const int off = swz_off<NCK>(r, c8);
+    const float *cr = CS + r * DK + 8 * c8;
+    const float *ce = CS + (16 * B + 15) * DK + 8 * c8;
+    const float *cb = CS + (16 * B - 1) * DK + 8 * c8;
+    const bf16x8 kv = *reinterpret_cast<const bf16x8 *>(KS + off);
+    float yk[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) yk[e] = r < n ? tof(kv[e]) * __expf(ce[e] - cr[e]) : 0.f;
+    *reinterpret_cast<bf16x8 *>(KH + off) = cvt8(yk);
+    if (QH) {
+      const bf16x8 qv = *reinterpret_cast<const bf16x8 *>(QS + off);
+      float yq[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        yq[e] = r < n ? tof(qv[e]) * __expf(cr[e] - (B > 0 ? cb[e] : 0.f)) : 0.f;
+      *reinterpret_cast<bf16x8 *>(QH + off) = cvt8(yq);
+    }
+  }
+  for (int d = tid; d < DK; d += NTH) {
+    float ce[4];
+#pragma unroll
+    for (int B = 0; B < 4; ++B) ce[B] = CS[(16 * B + 15) * DK + d];
+#pragma unroll
+    for (int B = 0; B < 4; ++B) {
+      FQ[B * DK + d] = B > 0 ? __expf(ce[B - 1]) : 1.f;
+      FK[B * DK + d] = __expf(ce[3] - ce[B]);
+    }
+    AL[d] = __expf(ce[3]);
+  }
+}
+
+// decay factor between blocks for the score products:
+//   R > S : exp(cb_R - ce_S) (<= 1);  R == S and a good block: exp(cb_R - ce_R);
+//   otherwise 0 (a bad diagonal block is done elementwise; R < S is masked)
+__device__ __forceinline__ float block_factor(const float *CS, int DK, int R, int S, int d,
+                                              bool good) {
+  if (R < S || (R == S && !good)) return 0.f;
+  const float cb = R > 0 ? CS[(16 * R - 1) * DK + d] : 0.f;
+  return __expf(cb - CS[(16 * S + 15) * DK + d]);
+}
+
+// does block R decay below exp(-kBadLog) in some dimension? (wave-uniform)
+template <int DK>
+__device__ __forceinline__ bool block_bad(const float *CS, int R, int lane) {
+  bool bad = false;
+  for (int d = lane; d < DK; d += 64) {
+    const float cb = R > 0 ? CS[(16 * R - 1) * DK + d] : 0.f;
+    bad |= cb - CS[(16 * R + 15) * DK + d] > kBadLog;
+  }
+  return __ballot(bad) != 0;
+}
+
+// ===========================================================================
+// dQ pass
+// ===========================================================================
+
+template <int DK, int DV>
+__global__ __launch_bounds__(NTHR, 1) void gla_dq_kernel(GlaBwdArgs a) {
+  constexpr int NCK = DK / 8, NCV = DV / 8;
+  constexpr int NDT = DK / 64;  // 16-column d tiles per wave
+  constexpr int NJT = DV / 16;  // 16-row j tiles of S^T
+  constexpr int B_KS = 64 * DK * 2, B_QH = 2 * B_KS, B_KH = 3 * B_KS, B_VS = 4 * B_KS;
+  constexpr int B_DO = B_VS + 64 * DV * 2, B_CS = B_DO + 64 * DV * 2;
+  constexpr int B_BS = B_CS + 64 * DK * 4, B_FQ = B_BS + 64 * 64 * 2;
+  constexpr int B_FK = B_FQ + 4 * DK * 4, B_AL = B_FK + 4 * DK * 4;
+  constexpr int BUF = B_AL + DK * 4;
+  static_assert(BUF <= 160 * 1024, "LDS");
+  constexpr int NBQ = DK / 8, NBV = DV / 8, NBL = DK / 4;
+  constexpr int NBLK = 2 * NBQ + 2 * NBV + NBL;
+  __shared__ __attribute__((aligned(1024))) unsigned char buf[BUF];
+  unsigned char *QS = buf, *KS = buf + B_KS, *QH = buf + B_QH, *KH = buf + B_KH;
+  unsigned char *VS = buf + B_VS;
+  unsigned char *DOS = buf + B_DO, *BS = buf + B_BS;
+  float *CS = reinterpret_cast<float *>(buf + B_CS);
+  float *FQ = reinterpret_cast<float *>(buf + B_FQ);
+  float *FK = reinterpret_cast<float *>(buf + B_FK);
+  float *AL = reinterpret_cast<float *>(buf + B_AL);
+
+  const int tid0 = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+  int tid = tid0, lane = tid0 & 63, li = lane & 15, lg = lane >> 4;
+#define FRESH_LANE()             \
+  do {                           \
+    int t_ = tid0;               \
+    asm volatile("" : "+v"(t_)); \
+    tid = t_;                    \
+    lane = t_ & 63;              \
+    li = lane & 15;              \
+    lg = lane >> 4;              \
+  } while (0)
+  const int64_t bh = blockIdx.x;
+  const int64_t T = a.T;
+  const int64_t nchunks = (T + TC - 1) / TC;
+  const int d0 = w * (DK / 4);
+  const uint16_t *qh = a.q + bh * T * DK;
+  const uint16_t *kh = a.k + bh * T * DK;
+  const uint16_t *vh = a.v + bh * T * DV;
+  const uint16_t *doh = a.dO + bh * T * DV;
+  const float *lh = a.l + bh * T * DK;
+
+  // ST_acc[jt][dt][i] = S^T[16 jt + 4 lg + i][d0 + 16 dt + li] = S[d][j]
+  f32x4 ST_acc[NJT][NDT];
+#pragma unroll
+  for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      ST_acc[jt][dt] = zero4();
+      if (a.S0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ST_acc[jt][dt][i] = a.S0[(bh * DK + d0 + 16 * dt + li) * DV + 16 * jt + 4 * lg + i];
+      }
+    }
+
+  for (int64_t ci = 0; ci < nchunks; ++ci) {
+    const int64_t t0 = ci * TC;
+    const int n = (int)min<int64_t>(TC, T - t0);
+
+    lds_barrier();
+    FRESH_LANE();
+    for (int b = w; b < NBLK; b += NWAVE) {
+      if (b < NBQ)
+        dma_block<DK>(qh + t0 * DK, n, QS, b, lane);
+      else if (b < 2 * NBQ)
+        dma_block<DK>(kh + t0 * DK, n, KS, b - NBQ, lane);
+      else if (b < 2 * NBQ + NBV)
+        dma_block<DV>(vh + t0 * DV, n, VS, b - 2 * NBQ, lane);
+      else if (b < 2 * NBQ + 2 * NBV)
+        dma_block<DV>(doh + t0 * DV, n, DOS, b - 2 * NBQ - NBV, lane);
+      else
+        dma_f32_rows<DK>(lh + t0 * DK, n, buf + B_CS, b - 2 * NBQ - 2 * NBV, lane);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+    FRESH_LANE();
+    cumsum_rows<DK, NTHR>(CS, n, tid);
+    FRESH_LANE();
+    prep_scaled<DK, NTHR>(QS, KS, QH, KH, CS, FQ, FK, AL, n, tid);
+
+    // ---- B[r][s] = dO_r . v_s (masked), stored [r][s]; the 32-column steps
+    // read up to the diagonal also cover tiles (0,1) and (2,3): zeros ----
+    FRESH_LANE();
+    for (int t = w; t < 12; t += NWAVE) {
+      const int R = tile_rt(t), S = tile_st(t);
+      f32x4 acc = zero4();
+      if (S <= R) {
+#pragma unroll
+        for (int kk = 0; kk < DV / 32; ++kk)
+          acc = mfma(lds_frag<NCV>(VS, 16 * S + li, 4 * kk + lg),
+                     lds_frag<NCV>(DOS, 16 * R + li, 4 * kk + lg), acc);
+      }
+      bf16x4 pv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * R + li, s = 16 * S + 4 * lg + i;
+        pv[i] = tobf(s <= r && s < n && r < n ? acc[i] : 0.f);
+      }
+      *reinterpret_cast<bf16x4 *>(BS + swz_off<8>(16 * R + li, 2 * S + (lg >> 1)) + (lg & 1) * 8) =
+          pv;
+    }
+    lds_barrier();
+
+    // ---- dq^T[d][r] for this wave's columns d ----
+    {
+      FRESH_LANE();
+      bf16x8 sfrag[DV / 32][NDT];  // S as A operands: row d, k = j (permuted)
+#pragma unroll
+      for (int kk = 0; kk < DV / 32; ++kk)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) sfrag[kk][dt] = cvt8(ST_acc[2 * kk][dt], ST_acc[2 * kk + 1][dt]);
+      for (int R = 0; R < 4; ++R) {
+        const bool good = !block_bad<DK>(CS, R, lane);
+        const int r = 16 * R + li;
+        bf16x8 dofrag[DV / 32];  // dO^T B operands: k = j (same permutation), n = r
+#pragma unroll
+        for (int kk = 0; kk < DV / 32; ++kk)
+          dofrag[kk] = cat8(lds_half<NCV>(DOS, r, 32 * kk + 4 * lg),
+                            lds_half<NCV>(DOS, r, 32 * kk + 16 + 4 * lg));
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int dc = d0 + 16 * dt + 4 * lg;  // this lane's 4 output d's
+          // in-chunk part: sum over blocks S <= R of F_RS (Kh_S^T B_RS^T), one
+          // 16-deep product per block, the factor applied after it
+          f32x4 accI = zero4();
+          for (int S = 0; S <= R; ++S) {
+            f32x4 P = zero4();
+            P = mfma16(tr_read4<NCK>(KH, 16 * S + 4 * lg, d0 + 16 * dt, li),  // Kh^T: row d, k = s
+                       lds_half<8>(BS, r, 16 * S + 4 * lg), P);                // B: k = s, col t
+#pragma unroll
+            for (int i = 0; i < 4; ++i) accI[i] += block_factor(CS, DK, R, S, dc + i, good) * P[i];
+          }
+          f32x4 acc2 = zero4();
+#pragma unroll
+          for (int kk = 0; kk < DV / 32; ++kk) acc2 = mfma(sfrag[kk][dt], dofrag[kk], acc2);
+          // accI[i], acc2[i] at d = dc + i, row t = r
+          const bf16x4 qv = lds_half<NCK>(QS, min(r, 63), dc);
+          const bf16x4 qhv = lds_half<NCK>(QH, r, dc);
+          float out[4], r1v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d = dc + i;
+            const float cb = R > 0 ? CS[(16 * R - 1) * DK + d] : 0.f;
+            const float u = __expf(CS[r * DK + d] - cb);
+            const float inter = FQ[R * DK + d] * acc2[i] * u;
+            float v = accI[i] * u + inter;
+            float rv = tof(qhv[i]) * accI[i] + tof(qv[i]) * inter;
+            if (!good) {
+              // the block's own tokens, elementwise
+              const float qd = tof(qv[i]);
+              const int sr = min(r, n - 1);
+              for (int s2 = 16 * R; s2 <= sr; ++s2) {
+                const float bsc = tof(*reinterpret_cast<const __bf16 *>(
+                    BS + swz_off<8>(r, s2 >> 3) + (s2 & 7) * 2));
+                const float kd = tof(*reinterpret_cast<const __bf16 *>(
+                    KS + swz_off<NCK>(s2, d >> 3) + (d & 7) * 2));
+                v += (bsc * kd) * __expf(CS[r * DK + d] - CS[s2 * DK + d]);
+                rv += path_term(bsc, qd, kd, CS[r * DK + d], CS[s2 * DK + d]);
+              }
+            }
+            out[i] = v;
+            r1v[i] = rv;
+          }
+          if (r < n) {
+            bf16x4 ov;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ov[i] = tobf(out[i]);
+            *reinterpret_cast<bf16x4 *>(a.dq + (bh * T + t0 + r) * DK + dc) = ov;
+            f32x4 r1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r1[i] = r1v[i];
+            *reinterpret_cast<f32x4 *>(a.r1 + (bh * T + t0 + r) * DK + dc) = r1;
+          }
+        }
+      }
+    }
+
+    // ---- state update: S^T <- S^T diag(alpha) + V^T KG, KG = k e^{c_n - c_s}
+    // formed in fp32 and applied as two bf16 parts (hi + lo), so that the
+    // state at a segment's end holds the chunk's paths to fp32-level accuracy:
+    // the decay gradient pairs it with the same paths summed from k.dk ----
+    {
+      FRESH_LANE();
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const float al = AL[d0 + 16 * dt + li];
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ST_acc[jt][dt][i] *= al;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 kg[NDT], kl[NDT];  // KG B operands (hi, lo): k = s, column d
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int d = d0 + 16 * dt + li;
+          const bf16x8 x = tr_frag<NCK>(KS, 32 * kb, d0 + 16 * dt, li, lg);
+          const float cn = CS[63 * DK + d];
+          float y[8], z[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int s = 32 * kb + 8 * lg + e;
+            y[e] = s < n ? tof(x[e]) * __expf(cn - CS[s * DK + d]) : 0.f;
+          }
+          kg[dt] = cvt8(y);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) z[e] = y[e] - tof(kg[dt][e]);
+          kl[dt] = cvt8(z);
+        }
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) {
+          const bf16x8 va = tr_frag<NCV>(VS, 32 * kb, 16 * jt, li, lg);  // V^T: row j, k = s
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            ST_acc[jt][dt] = mfma(va, kg[dt], ST_acc[jt][dt]);
+            ST_acc[jt][dt] = mfma(va, kl[dt], ST_acc[jt][dt]);
+          }
+        }
+      }
+    }
+
+    // ---- the state at the end of each segment (and of the sequence) ----
+    if ((ci + 1) % kSegChunks == 0 || ci + 1 == nchunks) {
+      FRESH_LANE();
+      float *dst = a.Sseg + ((ci / kSegChunks) * a.nh + bh) * DK * DV;
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          *reinterpret_cast<f32x4 *>(dst + (d0 + 16 * dt + li) * DV + 16 * jt + 4 * lg) =
+              ST_acc[jt][dt];
+    }
+  }
+}
+#undef FRESH_LANE
+
+// ===========================================================================
+// dK/dV pass
+// ===========================================================================
+
+template <int DK, int DV>
+__global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
+  constexpr int NCK = DK / 8, NCV = DV / 8;
+  constexpr int NJ = DV / 64;   // side 0: 16-column j tiles per wave
+  constexpr int NI = DK / 64;   // side 1: 16-column d tiles per wave
+  constexpr int NG = DK * DV / 1024;
+  constexpr int B_KS = 64 * DK * 2, B_QH = 2 * B_KS, B_KH = 3 * B_KS, B_VS = 4 * B_KS;
+  constexpr int B_DO = B_VS + 64 * DV * 2, B_CS = B_DO + 64 * DV * 2;
+  constexpr int B_AS = B_CS + 64 * DK * 4, B_BS = B_AS + 8192;
+  constexpr int B_FQ = B_BS + 8192, B_FK = B_FQ + 4 * DK * 4, B_AL = B_FK + 4 * DK * 4;
+  constexpr int B_RED = B_AL + DK * 4;
+  constexpr int BUF = B_RED + 4 * DK * 4;
+  constexpr int NBQ = DK / 8, NBV = DV / 8, NBL = DK / 4;
+  constexpr int NBLK = 2 * NBQ + 2 * NBV + NBL;
+  static_assert(BUF <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) unsigned char buf[BUF];
+  unsigned char *QS = buf, *KS = buf + B_KS, *QH = buf + B_QH, *KH = buf + B_KH;
+  unsigned char *VS = buf + B_VS, *DOS = buf + B_DO, *AS = buf + B_AS, *BS = buf + B_BS;
+  float *CS = reinterpret_cast<float *>(buf + B_CS);
+  float *FQ = reinterpret_cast<float *>(buf + B_FQ);
+  float *FK = reinterpret_cast<float *>(buf + B_FK);
+  float *AL = reinterpret_cast<float *>(buf + B_AL);
+  float *RED = reinterpret_cast<float *>(buf + B_RED);
+
+  const int tid0 = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+  const int side = w >> 2, wv = w & 3;
+  int tid = tid0, lane = tid0 & 63, li = lane & 15, lg = lane >> 4;
+#define FRESH_LANE()             \
+  do {                           \
+    int t_ = tid0;               \
+    asm volatile("" : "+v"(t_)); \
+    tid = t_;                    \
+    lane = t_ & 63;              \
+    li = lane & 15;              \
+    lg = lane >> 4;              \
+  } while (0)
+  const int64_t bh = blockIdx.x;
+  const int64_t T = a.T;
+  const int64_t nchunks = (T + TC - 1) / TC;
+  const int j0 = wv * (DV / 4);  // side 0
+  const int d0 = wv * (DK / 4);  // side 1
+  const uint16_t *qh = a.q + bh * T * DK;
+  const uint16_t *kh = a.k + bh * T * DK;
+  const uint16_t *vh = a.v + bh * T * DV;
+  const uint16_t *doh = a.dO + bh * T * DV;
+  const float *lh = a.l + bh * T * DK;
+
+  // side 0: Gs[dt * NJ + jt][i] = G[16 dt + 4 lg + i][j0 + 16 jt + li]
+  // side 1: Gs[jt * NI + it][i] = G^T[16 jt + 4 lg + i][d0 + 16 it + li]
+  f32x4 Gs[NG];
+#define G0(dt, jt) Gs[(dt) * NJ + (jt)]
+#define G1(jt, it) Gs[(jt) * NI + (it)]
+#pragma unroll
+  for (int x = 0; x < NG; ++x) Gs[x] = zero4();
+  if (a.dST) {
+    const float *src = a.dST + bh * DK * DV;
+    if (side == 0) {
+#pragma unroll
+      for (int dt = 0; dt < DK / 16; ++dt)
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            G0(dt, jt)[i] = src[(16 * dt + 4 * lg + i) * DV + j0 + 16 * jt + li];
+    } else {
+#pragma unroll
+      for (int jt = 0; jt < DV / 16; ++jt)
+#pragma unroll
+        for (int it = 0; it < NI; ++it)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            G1(jt, it)[i] = src[(d0 + 16 * it + li) * DV + 16 * jt + 4 * lg + i];
+    }
+  }
+  // side 1: the running suffix sum of q.dq - k.dk for its dimensions
+  // d0 + 16 it + 4 lg + i (the same in every lane of a 16-lane row)
+  float carry[NI][4];
+#pragma unroll
+  for (int it = 0; it < NI; ++it)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) carry[it][i] = 0.f;
+
+  for (int64_t ci = nchunks - 1; ci >= 0; --ci) {
+    const int64_t t0 = ci * TC;
+    const int n = (int)min<int64_t>(TC, T - t0);
+
+    // ---- at a segment's end: carry = <S[d, :], G[d, :]> (side 0 sums), with
+    // G rounded to bf16 as the dK product below takes it: the paths from this
+    // chunk past the segment end then cancel against k.dk term by term ----
+    if ((ci + 1) % kSegChunks == 0 || ci + 1 == nchunks) {
+      FRESH_LANE();
+      if (side == 0) {
+        const float *Sg = a.Sseg + ((ci / kSegChunks) * a.nh + bh) * DK * DV;
+#pragma unroll
+        for (int dt = 0; dt < DK / 16; ++dt) {
+          f32x4 p;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float s = 0.f;
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt)
+              s += tof(tobf(G0(dt, jt)[i])) * Sg[(16 * dt + 4 * lg + i) * DV + j0 + 16 * jt + li];
+            // sum over the 16 lanes of this row group (the columns li)
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
+            p[i] = s;
+          }
+          if (li == 0) *reinterpret_cast<f32x4 *>(RED + wv * DK + 16 * dt + 4 * lg) = p;
+        }
+      }
+      lds_barrier();
+      if (side == 1) {
+#pragma unroll
+        for (int it = 0; it < NI; ++it)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d = d0 + 16 * it + 4 * lg + i;
+            carry[it][i] = RED[d] + RED[DK + d] + RED[2 * DK + d] + RED[3 * DK + d];
+          }
+      }
+    }
+
+    lds_barrier();
+    FRESH_LANE();
+    for (int b = w; b < NBLK; b += BTHR / 64) {
+      if (b < NBQ)
+        dma_block<DK>(qh + t0 * DK, n, QS, b, lane);
+      else if (b < 2 * NBQ)
+        dma_block<DK>(kh + t0 * DK, n, KS, b - NBQ, lane);
+      else if (b < 2 * NBQ + NBV)
+        dma_block<DV>(vh + t0 * DV, n, VS, b - 2 * NBQ, lane);
+      else if (b < 2 * NBQ + 2 * NBV)
+        dma_block<DV>(doh + t0 * DV, n, DOS, b - 2 * NBQ - NBV, lane);
+      else
+        dma_f32_rows<DK>(lh + t0 * DK, n, buf + B_CS, b - 2 * NBQ - 2 * NBV, lane);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+    FRESH_LANE();
+    cumsum_rows<DK, BTHR>(CS, n, tid);
+    FRESH_LANE();
+    prep_scaled<DK, BTHR>(QS, KS, QH, KH, CS, FQ, FK, AL, n, tid);
+    lds_barrier();
+
+    // ---- scores, stored transposed [s][r]: side 0 the decayed A, side 1 B ----
+    {
+      FRESH_LANE();
+      unsigned char *PT = side == 0 ? AS : BS;
+      for (int t = wv; t < 12; t += 4) {
+        // the tiles (rows s in block S, columns r in block R) that the
+        // 32-column steps over r >= s read: S <= (R | 1); those with R < S
+        // are zero
+        const int R = tile_rt(t), S = tile_st(t);
+        f32x4 acc = zero4();
+        // acc[i] = X[r = 16R + 4lg + i][s = 16S + li]
+        if (S <= R) {
+          if (side == 0) {
+            const bool good = R != S || !block_bad<DK>(CS, R, lane);
+            if (good) {
+#pragma unroll
+              for (int kk = 0; kk < DK / 32; ++kk) {
+                const int dd = 32 * kk + 8 * lg;
+                const bf16x8 kv = lds_frag<NCK>(KH, 16 * S + li, 4 * kk + lg);
+                const float *cbR = CS + (16 * R - 1) * DK + dd;
+                const float *ceS = CS + (16 * S + 15) * DK + dd;
+                float y[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                  y[e] = tof(kv[e]) * __expf((R > 0 ? cbR[e] : 0.f) - ceS[e]);
+                acc = mfma(lds_frag<NCK>(QH, 16 * R + li, 4 * kk + lg), cvt8(y), acc);
+              }
+            } else {
+              const int s = 16 * S + li;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int r = 16 * R + 4 * lg + i;
+                float sum = 0.f;
+                if (s <= r) {
+                  for (int dd = 0; dd < DK; dd += 8) {
+                    const bf16x8 qv = lds_frag<NCK>(QS, r, dd >> 3);
+                    const bf16x8 kv = lds_frag<NCK>(KS, s, dd >> 3);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                      sum += tof(qv[e]) * tof(kv[e]) *
+                             __expf(CS[r * DK + dd + e] - CS[s * DK + dd + e]);
+                  }
+                }
+                acc[i] = sum;
+              }
+            }
+          } else {
+#pragma unroll
+            for (int kk = 0; kk < DV / 32; ++kk)
+              acc = mfma(lds_frag<NCV>(DOS, 16 * R + li, 4 * kk + lg),
+                         lds_frag<NCV>(VS, 16 * S + li, 4 * kk + lg), acc);
+          }
+        }
+        bf16x4 pv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * R + 4 * lg + i, s = 16 * S + li;
+          pv[i] = tobf(s <= r && s < n && r < n ? acc[i] : 0.f);
+        }
+        *reinterpret_cast<bf16x4 *>(PT + swz_off<8>(16 * S + li, 2 * R + (lg >> 1)) + (lg & 1) * 8) =
+            pv;
+      }
+    }
+    lds_barrier();
+
+    if (side == 0) {
+      // ---- dV^T[j][s] = (dO^T A^T)[j][s] + (G^T KG^T)[j][s] ----
+      FRESH_LANE();
+      bf16x8 gfrag[DK / 32][NJ];  // G^T A operands: row j, k = d (permuted)
+#pragma unroll
+      for (int kk = 0; kk < DK / 32; ++kk)
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) gfrag[kk][jt] = cvt8(G0(2 * kk, jt), G0(2 * kk + 1, jt));
+      for (int S = 0; S < 4; ++S) {
+        const int s = 16 * S + li;
+        bf16x8 kgf[DK / 32];  // KG^T B operands: k = d (same permutation), n = s
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+          const int da = 32 * kk + 4 * lg, db = da + 16;
+          const bf16x4 lo = lds_half<NCK>(KH, s, da);
+          const bf16x4 hi = lds_half<NCK>(KH, s, db);
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            y[e] = tof(lo[e]) * FK[S * DK + da + e];
+            y[e + 4] = tof(hi[e]) * FK[S * DK + db + e];
+          }
+          kgf[kk] = cvt8(y);
+        }
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int kk = 0; kk < DK / 32; ++kk) acc = mfma(gfrag[kk][jt], kgf[kk], acc);
+          for (int kb = S >> 1; kb < 2; ++kb)
+            acc = mfma(tr_frag<NCV>(DOS, 32 * kb, j0 + 16 * jt, li, lg),
+                       lds_frag<8>(AS, s, 4 * kb + lg), acc);
+          // acc[i] = dV[s][j0 + 16 jt + 4 lg + i]
+          if (s < n) {
+            bf16x4 ov;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ov[i] = tobf(acc[i]);
+            *reinterpret_cast<bf16x4 *>(a.dv + (bh * T + t0 + s) * DV + j0 + 16 * jt + 4 * lg) =
+                ov;
+          }
+        }
+      }
+    } else {
+      // ---- dK^T[d][s], r2 = k dk, and the decay gradient ----
+      FRESH_LANE();
+      bf16x8 gfrag[DV / 32][NI];  // G A operands: row d, k = j (permuted)
+#pragma unroll
+      for (int kk = 0; kk < DV / 32; ++kk)
+#pragma unroll
+        for (int it = 0; it < NI; ++it) gfrag[kk][it] = cvt8(G1(2 * kk, it), G1(2 * kk + 1, it));
+      // blocks last to first: the suffix sums of x = q.dq - k.dk over s run
+      // through `carry` (later rows of this segment plus its boundary term)
+      for (int S = 3; S >= 0; --S) {
+        const int s = 16 * S + li;
+        const bool good = !block_bad<DK>(CS, S, lane);
+        bf16x8 vfr[DV / 32];  // V^T B operands: k = j (same permutation), n = s
+#pragma unroll
+        for (int kk = 0; kk < DV / 32; ++kk)
+          vfr[kk] = cat8(lds_half<NCV>(VS, s, 32 * kk + 4 * lg),
+                         lds_half<NCV>(VS, s, 32 * kk + 16 + 4 * lg));
+#pragma unroll
+        for (int it = 0; it < NI; ++it) {
+          const int dc = d0 + 16 * it + 4 * lg;  // this lane's 4 output d's
+          // in-chunk part: sum over blocks R >= S of F_RS (Qh_R^T B_RS), one
+          // 16-deep product per block, the factor applied after it
+          f32x4 accI = zero4();
+          for (int R = S; R < 4; ++R) {
+            f32x4 P = zero4();
+            P = mfma16(tr_read4<NCK>(QH, 16 * R + 4 * lg, d0 + 16 * it, li),  // Qh^T: row d, k = t
+                       lds_half<8>(BS, s, 16 * R + 4 * lg), P);                // B^T: k = t, col s
+#pragma unroll
+            for (int i = 0; i < 4; ++i) accI[i] += block_factor(CS, DK, R, S, dc + i, good) * P[i];
+          }
+          f32x4 acc2 = zero4();
+#pragma unroll
+          for (int kk = 0; kk < DV / 32; ++kk) acc2 = mfma(gfrag[kk][it], vfr[kk], acc2);
+          const bf16x4 kv = lds_half<NCK>(KS, s, dc);
+          const bf16x4 khv = lds_half<NCK>(KH, s, dc);
+          float out[4], r2v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d = dc + i;
+            const float csd = CS[s * DK + d];
+            const float ue = __expf(CS[(16 * S + 15) * DK + d] - csd);
+            const float inter = FK[S * DK + d] * acc2[i] * ue;
+            float v = accI[i] * ue + inter;
+            float rv = tof(khv[i]) * accI[i] + tof(kv[i]) * inter;
+            if (!good) {
+              const float kd = tof(kv[i]);
+              for (int r = s; r < min(16 * S + 16, n); ++r) {
+                const float bsc = tof(*reinterpret_cast<const __bf16 *>(
+                    BS + swz_off<8>(s, r >> 3) + (r & 7) * 2));
+                const float qd = tof(*reinterpret_cast<const __bf16 *>(
+                    QS + swz_off<NCK>(r, d >> 3) + (d & 7) * 2));
+                v += (bsc * qd) * __expf(CS[r * DK + d] - csd);
+                rv += path_term(bsc, qd, kd, CS[r * DK + d], csd);
+              }
+            }
+            out[i] = v;
+            r2v[i] = rv;
+          }
+          f32x4 r1 = zero4();
+          if (s < n) {
+            bf16x4 ov;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ov[i] = tobf(out[i]);
+            *reinterpret_cast<bf16x4 *>(a.dk + (bh * T + t0 + s) * DK + dc) = ov;
+            r1 = *reinterpret_cast<const f32x4 *>(a.r1 + (bh * T + t0 + s) * DK + dc);
+          }
+          f32x4 dl4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // inclusive suffix sum over the 16 rows li of block S
+            float x = s < n ? r1[i] - r2v[i] : 0.f;
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) {
+              const float y = __shfl_down(x, o, 16);
+              if (li + o < 16) x += y;
+            }
+            const float tot = __shfl(x, lane & 0x30, 64);  // li = 0: the block's total
+            dl4[i] = x + carry[it][i];
+            carry[it][i] += tot;
+          }
+          if (s < n)
+            *reinterpret_cast<f32x4 *>(a.dl + (bh * T + t0 + s) * DK + dc) = dl4;
+        }
+      }
+    }
+
+    // ---- G <- diag(alpha) G + QL^T dO (both copies) ----
+    {
+      FRESH_LANE();
+      if (side == 0) {
+#pragma unroll
+        for (int dt = 0; dt < DK / 16; ++dt) {
+          const f32x4 av = *reinterpret_cast<const f32x4 *>(AL + 16 * dt + 4 * lg);
+#pragma unroll
+          for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) G0(dt, jt)[i] *= av[i];
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int R = 2 * kb + (lg >> 1);
+          bf16x8 db[NJ];  // dO B operands: k = r, column j
+#pragma unroll
+          for (int jt = 0; jt < NJ; ++jt) db[jt] = tr_frag<NCV>(DOS, 32 * kb, j0 + 16 * jt, li, lg);
+#pragma unroll
+          for (int dt = 0; dt < DK / 16; ++dt) {
+            const bf16x8 x = tr_frag<NCK>(QH, 32 * kb, 16 * dt, li, lg);  // Qh^T: row d, k = r
+            const float f = FQ[R * DK + 16 * dt + li];
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = tof(x[e]) * f;
+            const bf16x8 qa = cvt8(y);
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt) G0(dt, jt) = mfma(qa, db[jt], G0(dt, jt));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int it = 0; it < NI; ++it) {
+          const float al = AL[d0 + 16 * it + li];
+#pragma unroll
+          for (int jt = 0; jt < DV / 16; ++jt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) G1(jt, it)[i] *= al;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int R = 2 * kb + (lg >> 1);
+          bf16x8 qb[NI];  // QL B operands: k = r, column d
+#pragma unroll
+          for (int it = 0; it < NI; ++it) {
+            const bf16x8 x = tr_frag<NCK>(QH, 32 * kb, d0 + 16 * it, li, lg);
+            const float f = FQ[R * DK + d0 + 16 * it + li];
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = tof(x[e]) * f;
+            qb[it] = cvt8(y);
+          }
+#pragma unroll
+          for (int jt = 0; jt < DV / 16; ++jt) {
+            const bf16x8 da = tr_frag<NCV>(DOS, 32 * kb, 16 * jt, li, lg);  // dO^T: row j, k = r
+#pragma unroll
+            for (int it = 0; it < NI; ++it) G1(jt, it) = mfma(da, qb[it], G1(jt, it));
+          }
+        }
+      }
+    }
+  }
+
+  FRESH_LANE();
+  if (a.dS0 && side == 0) {
+    float *dst = a.dS0 + bh * DK * DV;
+#pragma unroll
+    for (int dt = 0; dt < DK / 16; ++dt)
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dst[(16 * dt + 4 * lg + i) * DV + j0 + 16 * jt + li] = G0(dt, jt)[i];
+  }
+}
+#undef G0
+#undef G1
+#undef FRESH_LANE
+
+template <int DK, int DV>
+hipError_t gla_bwd_impl(const GlaBwdArgs &args, hipStream_t stream) {
+  CLA_LAUNCH("gla_dq", (gla_dq_kernel<DK, DV>), dim3((unsigned)args.nh), dim3(NTHR), stream,
+             args);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  CLA_LAUNCH("gla_dkdv", (gla_dkdv_kernel<DK, DV>), dim3((unsigned)args.nh), dim3(BTHR), stream,
+             args);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t gla_bwd_ws_bytes(int64_t nh, int64_t T, int64_t DK, int64_t DV) {
+  const int64_t nchunks = (T + TC - 1) / TC;
+  const int64_t nseg = (nchunks + kSegChunks - 1) / kSegChunks;
+  const size_t r1 = ((size_t)nh * T * DK * sizeof(float) + 255) & ~(size_t)255;
+  return r1 + (size_t)nseg * nh * DK * DV * sizeof(float);
+}
+
+hipError_t gla_bwd_dispatch(const GlaBwdArgs &args, int DK, int DV, hipStream_t stream) {
+  if (DK == 64 && DV == 64) return gla_bwd_impl<64, 64>(args, stream);
+  if (DK == 64 && DV == 128) return gla_bwd_impl<64, 128>(args, stream);
+  if (DK == 128 && DV == 64) return gla_bwd_impl<128, 64>(args, stream);
+  if (DK == 128 && DV == 128) return gla_bwd_impl<128, 128>(args, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gla
+}  // namespace cla

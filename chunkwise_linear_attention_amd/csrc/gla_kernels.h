@@ -1,0 +1,48 @@
+// Argument blocks and launchers of the kernels with one decay per key
+// dimension (gla.hip, gla_bwd.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cla {
+namespace gla {
+
+struct GlaFwdArgs {
+  const uint16_t *q, *k;  // [nh, T, DK] bf16
+  const uint16_t *v;      // [nh, T, DV] bf16
+  const float *l;         // [nh, T, DK] log decays
+  const float *S0;        // [nh, DK, DV] or NULL (zeros)
+  uint16_t *o;            // [nh, T, DV] bf16
+  float *ST;              // [nh, DK, DV] or NULL (not written)
+  int64_t nh, T;
+};
+
+hipError_t gla_fwd_dispatch(const GlaFwdArgs &args, int DK, int DV, hipStream_t stream);
+
+// The backward's decay gradient sums q.dq - k.dk backwards inside segments of
+// this many chunks, each started from the exact boundary term <S, G>.
+constexpr int64_t kSegChunks = 16;
+
+struct GlaBwdArgs {
+  const uint16_t *q, *k;  // [nh, T, DK] bf16
+  const uint16_t *v, *dO; // [nh, T, DV] bf16
+  const float *l;         // [nh, T, DK] log decays
+  const float *S0;        // [nh, DK, DV] or NULL
+  const float *dST;       // [nh, DK, DV] or NULL
+  uint16_t *dq, *dk;      // [nh, T, DK] bf16
+  uint16_t *dv;           // [nh, T, DV] bf16
+  float *dl;              // [nh, T, DK]
+  float *dS0;             // [nh, DK, DV] or NULL
+  float *r1;              // workspace [nh, T, DK]: q (.) dq (fp32, from the dQ pass)
+  float *Sseg;            // workspace [nseg, nh, DK, DV]: S at the end of each segment
+  int64_t nh, T;
+};
+
+// Workspace of the backward: r1, then Sseg (each 256-byte aligned).
+size_t gla_bwd_ws_bytes(int64_t nh, int64_t T, int64_t DK, int64_t DV);
+
+hipError_t gla_bwd_dispatch(const GlaBwdArgs &args, int DK, int DV, hipStream_t stream);
+
+}  // namespace gla
+}  // namespace cla

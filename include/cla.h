@@ -232,6 +232,62 @@ int cla_timing_enable(int enable);
  */
 int cla_timing_read(const char **names, double *total_ms, int64_t *counts, int max);
 
+/*
+ * One decay per key dimension (gated linear attention).  "Parallel scan",
+ * sections "Scans over vector and matrix states" (the diagonal transition,
+ * one decay per state entry) and "The chunkwise algorithm" (the GLA form
+ * S_t = G_t (.) S_{t-1} + k_t^T v_t): row d of the state decays by
+ * a_t[d] = exp(l_t[d]),
+ *   S_t = diag(a_t) S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t.
+ *   q, k      : [B, H, T, DK] bf16;  v, o : [B, H, T, DV] bf16.
+ *   log_decay : [B, H, T, DK] fp32, finite and <= 0 (decays in (0, 1]; not
+ *               checked), 16-byte aligned.
+ *   S0, ST    : [B, H, DK, DV] fp32 (S0 NULL = zeros; ST NULL = not written).
+ *   DK, DV in {64, 128}; chunk must be 64; the bf16 tensors and log_decay
+ *   must be 16-byte aligned (CLA_ERR_UNSUPPORTED otherwise).
+ * Inside a chunk the cumulative logs are summed over the chunk's own steps
+ * ("Long products without underflow"); the in-chunk products are formed
+ * from factors that never exceed 1, with an exact elementwise path for any
+ * 16-step block whose decay falls below exp(-60) in some dimension.
+ * The forward needs no workspace (cla_gla_workspace_bytes returns 0 for it;
+ * workspace may be NULL).  One workgroup runs each sequence-head from its
+ * first chunk to its last (no split of the sequence across workgroups).
+ */
+size_t cla_gla_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t DK,
+                               int64_t DV, int64_t chunk, int backward);
+
+int cla_gla_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                const float *log_decay, const float *S0, uint16_t *o, float *ST,
+                int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV,
+                int64_t chunk, void *workspace, size_t workspace_bytes,
+                cla_stream_t stream);
+
+/*
+ * Backward of cla_gla_fwd.  "Parallel scan", section "The backward pass of
+ * linear attention", with the diagonal decay: the adjoint state decays by row,
+ * and the decay gradient is the closed form for a vector of decays per step
+ * (Yang et al. 2023, Section 4.3, as the page cites it), per key dimension:
+ *   dl_u[d] = sum_{t >= u} q_t[d] dq_t[d] - sum_{s >= u} k_s[d] dk_s[d]
+ *             (+ <S_T[d, :], dS_T[d, :]> when dS_T is given).
+ * It is evaluated in segments of 16 chunks, each started from the exact
+ * boundary term <S[d, :], G[d, :]> of the fp32 states at the segment's end.
+ *   q, k, v, log_decay, S0 : as in cla_gla_fwd.
+ *   dO        : [B, H, T, DV] bf16 gradient at o.
+ *   dST       : [B, H, DK, DV] fp32 gradient at S_T, or NULL.
+ *   dq, dk    : [B, H, T, DK] bf16;  dv : [B, H, T, DV] bf16.
+ *   dlog_decay: [B, H, T, DK] fp32, 16-byte aligned.
+ *   dS0       : [B, H, DK, DV] fp32, or NULL (not written).
+ *   workspace : cla_gla_workspace_bytes(..., backward = 1) bytes, 16-byte
+ *               aligned (B*H*T*DK fp32 products q dq, plus one fp32 state per
+ *               segment of 16 chunks per sequence-head).
+ */
+int cla_gla_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                const float *log_decay, const float *S0, const uint16_t *dO,
+                const float *dST, uint16_t *dq, uint16_t *dk, uint16_t *dv,
+                float *dlog_decay, float *dS0, int64_t B, int64_t H, int64_t T,
+                int64_t DK, int64_t DV, int64_t chunk, void *workspace,
+                size_t workspace_bytes, cla_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
