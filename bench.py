@@ -6,9 +6,10 @@ cores beside it.
 
 One step is the forward and the backward call over one batch of the
 workload's synthetic inputs, already resident in HBM.  The default workload
-is the diagonal scan B=8, T=16384, D=4096 (fp32).  The chunkwise workloads
-(la_const, la_gated, la_long_T*) are selected with --workload.  Prints ONE
-JSON line.
+is the diagonal scan B=8, T=16384, D=4096 (fp32); the same run also times
+the chunkwise workloads (la_const, la_gated, la_long_T*) and the per-key-
+dimension decay workload (gla_T4096) and reports them under "extra".  Any of
+them can be the headline with --workload.  Prints ONE JSON line.
 """
 
 from __future__ import annotations
@@ -320,7 +321,125 @@ def cpu_baseline_chunk(ci, nheads):
                       "head fraction"}
 
 
+def bench_gla(args, torch, cla, wl, steps, warmup, cpu_heads=0):
+    """One decay per key dimension: cla_gla_fwd + cla_gla_bwd per step."""
+    from chunkwise_linear_attention_amd import _lib
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    ci = wl.make()
+    log(f"[bench] inputs for {wl.name} drawn in {time.time() - t0:.1f}s")
+    B, H, T, DK, DV = (wl.shape[x] for x in ("B", "H", "T", "DK", "DV"))
+
+    def up(x):
+        if x is None:
+            return None
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    q, k, v, l, S0, dO, dST = (up(x) for x in (ci.q, ci.k, ci.v, ci.l, ci.S0, ci.dO, ci.dST))
+    o = torch.empty_like(v)
+    ST = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dl = torch.empty_like(l)
+    dS0 = torch.empty_like(ST)
+    L = cla.lib()
+    wsb = int(L.cla_gla_workspace_bytes(B, H, T, DK, DV, 64, 1))
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    P = lambda t: None if t is None else t.data_ptr()
+
+    def fwd():
+        st = L.cla_gla_fwd(P(q), P(k), P(v), P(l), P(S0), P(o), P(ST), B, H, T, DK, DV, 64,
+                           None, 0, stream)
+        if st:
+            raise RuntimeError(L.cla_status_string(st))
+
+    def bwd():
+        st = L.cla_gla_bwd(P(q), P(k), P(v), P(l), P(S0), P(dO), P(dST), P(dq), P(dk), P(dv),
+                           P(dl), P(dS0), B, H, T, DK, DV, 64, P(ws), ws.numel(), stream)
+        if st:
+            raise RuntimeError(L.cla_status_string(st))
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        fwd()
+        bwd()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / steps
+    _lib.timing_enable(True)
+    for _ in range(steps):
+        fwd()
+        bwd()
+    table = _lib.timing_read()
+    _lib.timing_enable(False)
+    units = B * H * T
+    kernels = {}
+    total = sum(x[0] for x in table.values())
+    for name, (tot, cnt) in table.items():
+        avg = tot / cnt
+        ent = {"avg_ms": round(avg, 5), "launches_per_step": cnt // steps,
+               "share": round(tot / total, 4)}
+        if name in ("gla_fwd", "gla_dq", "gla_dkdv"):
+            per = pm.gla_kernel_bytes(name, DK, DV)
+            ent["algorithmic_bytes_per_launch"] = per * units
+            ent["GBps"] = round(per * units / (avg * 1e-3) / 1e9, 1)
+        kernels[name] = ent
+    main = {n: e for n, e in kernels.items() if "GBps" in e}
+    dom = max(main, key=lambda n: main[n]["avg_ms"] * main[n]["launches_per_step"])
+    d = kernels[dom]
+    path_bytes = pm.gla_bytes_per_token_head(DK, DV, "fwdbwd") * units
+    path_flops = pm.gla_flops_per_token_head(64, DK, DV, "fwdbwd") * units
+    t_roof = pm.roofline_seconds(path_bytes, path_flops)
+    roof = {"kernel": dom, "bound": "hbm", "achieved": d["GBps"], "peak": pm.PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(d["GBps"] / pm.PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic(dom, wl.name, "gla.hip" if dom == "gla_fwd" else "gla_bwd.hip"),
+            "avg_launch_ms": d["avg_ms"],
+            "algorithmic_bytes_per_launch": d["algorithmic_bytes_per_launch"]}
+    res = {"value": B * T / (ms_step * 1e-3), "ms_per_step": ms_step, "dtype": "bf16",
+           "config": {"workload": wl.name, "B": B, "H": H, "T": T, "DK": DK, "DV": DV,
+                      "chunk": 64, "tokens_per_step": B * T, "decay": "per key dimension"},
+           "roofline": roof,
+           "extra": {"kernels": kernels,
+                     "path_algorithmic_bytes": path_bytes, "path_algorithmic_flops": path_flops,
+                     "path_roofline_frac": round(t_roof / (ms_step * 1e-3), 4),
+                     "mfma_util": round(path_flops / (ms_step * 1e-3) / (pm.PEAK_BF16_TFLOPS * 1e12), 4),
+                     "hbm_GBps_path": round(path_bytes / (ms_step * 1e-3) / 1e9, 1),
+                     "workspace_bytes": wsb, "path": "cla_gla_fwd + cla_gla_bwd"}}
+    res["cpu_baseline"] = cpu_baseline_gla(ci, cpu_heads) if cpu_heads else None
+    del q, k, v, l, S0, dO, dST, o, ST, dq, dk, dv, dl, dS0, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline_gla(ci, nheads):
+    """The C oracle for one decay per key dimension, forward then backward, on
+    the first `nheads` (batch, head) sequences at full length."""
+    from oracle import cref
+    cref.build()
+    B, H, T, DK = ci.q.shape
+    heads = np.arange(min(nheads, B * H), dtype=np.int64)
+    t0 = time.time()
+    cref.gla_fwd(ci.q, ci.k, ci.v, ci.l, ci.S0, heads=heads)
+    cref.gla_bwd(ci.q, ci.k, ci.v, ci.l, ci.S0, ci.dO, ci.dST, heads=heads)
+    secs = time.time() - t0
+    frac = len(heads) / (B * H)
+    return {"value": round(B * T * frac / secs, 1), "unit": "tokens/s",
+            "cores": cref.num_threads(), "kind": "oracle",
+            "sample": f"{len(heads)} of {B * H} (batch, head) sequences at full length "
+                      f"T={T}, forward+backward, {secs:.2f} s; tokens/s scaled by the "
+                      "head fraction"}
+
+
 CHUNK_EXTRAS = ("la_const", "la_gated") + tuple(f"la_long_T{t}" for t in syn.LONG_T)
+GLA_EXTRAS = ("gla_T4096",)
 
 
 def main():
@@ -368,7 +487,21 @@ def main():
                 log(f"[bench] {name}: {r['ms_per_step']:.3f} ms/step")
             longs = [chunk[f"la_long_T{t}"]["tokens_per_s"] for t in syn.LONG_T]
             res["extra"]["chunkwise"] = chunk
+            for name in GLA_EXTRAS:
+                r = bench_gla(args, torch, cla, syn.WORKLOADS[name], max(3, args.steps // 2),
+                              args.warmup)
+                res["extra"].setdefault("gla", {})[name] = {
+                    "tokens_per_s": round(r["value"], 1),
+                    "ms_per_step": round(r["ms_per_step"], 4),
+                    "roofline": r["roofline"],
+                    "path_roofline_frac": r["extra"]["path_roofline_frac"],
+                    "mfma_util": r["extra"]["mfma_util"],
+                    "kernels": {n: e["avg_ms"] for n, e in r["extra"]["kernels"].items()}}
+                log(f"[bench] {name}: {r['ms_per_step']:.3f} ms/step")
             res["extra"]["la_long_T_flatness_min_over_max"] = round(min(longs) / max(longs), 4)
+    elif wl.kind == "gla":
+        res = bench_gla(args, torch, cla, wl, args.steps, args.warmup,
+                        cpu_heads=args.cpu_heads if args.cpu_baseline else 0)
     else:
         res = bench_chunk(args, torch, cla, wl, args.steps, args.warmup,
                           cpu_heads=args.cpu_heads if args.cpu_baseline else 0)

@@ -118,3 +118,35 @@ def chunk_kernel_bytes(name: str, dk: int, dv: int) -> int:
         "chunk_dq_segments": 2 * dv + 2 * dk + 4,
     }
     return table[name]
+
+
+# --------------------------------------------------------------------------
+# one decay per key dimension (gated linear attention): l is [.., T, dk] fp32
+# --------------------------------------------------------------------------
+
+
+def gla_bytes_per_token_head(dk: int, dv: int, direction: str = "fwdbwd") -> int:
+    """Forward reads q, k, v and the dk log decays and writes o; backward
+    reads q, k, v, dO, l and writes dq, dk, dv and the dk decay gradients."""
+    fwd = 2 * dk + 2 * dk + 2 * dv + 4 * dk + 2 * dv
+    bwd = (2 * dk + 2 * dk + 2 * dv + 2 * dv + 4 * dk) + (2 * dk + 2 * dk + 2 * dv + 4 * dk)
+    return {"fwd": fwd, "bwd": bwd, "fwdbwd": fwd + bwd}[direction]
+
+
+def gla_flops_per_token_head(Tc: int, dk: int, dv: int, direction: str = "fwdbwd") -> int:
+    """The same products as the scalar-decay chunkwise form (the decay enters
+    as scaling of the operands, which is not counted)."""
+    return chunk_flops_per_token_head(Tc, dk, dv, direction)
+
+
+def gla_kernel_bytes(name: str, dk: int, dv: int) -> int:
+    """gla_fwd  : q, k, v, l in; o out.
+    gla_dq   : q, k, v, dO, l in; dq and the fp32 products q.dq out (plus one
+               fp32 state per segment of 16 chunks, not per token).
+    gla_dkdv : q, k, v, dO, l, q.dq in; dk, dv, dl out."""
+    table = {
+        "gla_fwd": gla_bytes_per_token_head(dk, dv, "fwd"),
+        "gla_dq": 2 * dk + 2 * dk + 2 * dv + 2 * dv + 4 * dk + 2 * dk + 4 * dk,
+        "gla_dkdv": 2 * dk + 2 * dk + 2 * dv + 2 * dv + 4 * dk + 4 * dk + 2 * dk + 2 * dv + 4 * dk,
+    }
+    return table[name]

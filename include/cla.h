@@ -269,8 +269,11 @@ int cla_gla_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
  * (Yang et al. 2023, Section 4.3, as the page cites it), per key dimension:
  *   dl_u[d] = sum_{t >= u} q_t[d] dq_t[d] - sum_{s >= u} k_s[d] dk_s[d]
  *             (+ <S_T[d, :], dS_T[d, :]> when dS_T is given).
- * It is evaluated in segments of 16 chunks, each started from the exact
- * boundary term <S[d, :], G[d, :]> of the fp32 states at the segment's end.
+ * It is evaluated in segments of 16 chunks, each started from the boundary
+ * term <S[d, :], G[d, :]> of the states at the segment's end (S in fp32, G as
+ * the dk product rounds it), and both sums take their in-chunk terms from the
+ * same rounded block products, so paths that do not cross step u cancel to
+ * fp32 accuracy.
  *   q, k, v, log_decay, S0 : as in cla_gla_fwd.
  *   dO        : [B, H, T, DV] bf16 gradient at o.
  *   dST       : [B, H, DK, DV] fp32 gradient at S_T, or NULL.

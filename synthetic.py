@@ -24,6 +24,9 @@ Workloads (sizes as used by the bench and the full-size tests):
 * ``la_long_T``   -- H=16, dk=dv=128, T in {1024, 4096, 16384, 65536, 98304},
   B = 98304 // T, q, k ~ N(0,1)/sqrt(128), v ~ N(0,1), log a = -1e-5 or -5 with
   probability 1/2 each (i.i.d.), dO ~ N(0,1).
+* ``gla_T4096``   -- one decay per key dimension, B=32, H=16, T=4096,
+  dk=dv=128, q, k ~ N(0,1)/sqrt(128), v ~ N(0,1), log a[d] = logsigmoid(x)/16
+  with x ~ N(0,1) per (token, dimension), S0 = none, dO ~ N(0,1).
 """
 
 from __future__ import annotations
@@ -43,12 +46,37 @@ _THREADS = 8
 # ---------------------------------------------------------------------------
 
 
-def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to bf16 (nearest, ties to even); return the uint16
-    bit patterns.  Inputs must be finite."""
+def _elementwise(fn, x: np.ndarray, dtype) -> np.ndarray:
+    """fn applied to blocks of the flattened x by a thread pool (numpy's
+    ufuncs release the GIL); the result does not depend on the split."""
+    x = np.ascontiguousarray(x)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, dtype=dtype)
+    n = flat.size
+    nblocks = max(1, (n + _BLOCK - 1) // _BLOCK)
+
+    def work(i):
+        lo, hi = i * _BLOCK, min(n, (i + 1) * _BLOCK)
+        out[lo:hi] = fn(flat[lo:hi])
+
+    if nblocks == 1:
+        work(0)
+    else:
+        with ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(work, range(nblocks)))
+    return out.reshape(x.shape)
+
+
+def _bf16_round_bits(x: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
     return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); return the uint16
+    bit patterns.  Inputs must be finite."""
+    return _elementwise(_bf16_round_bits, np.asarray(x, dtype=np.float32), np.uint16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -211,8 +239,9 @@ def gla_inputs(B, H, T, DK, DV, seed, qk_scale=None, v_scale=1.0,
     n = B * H * T * DK
     if decay == "logsigmoid" or (isinstance(decay, tuple) and decay[0] == "logsigmoid"):
         tau = 16.0 if decay == "logsigmoid" else float(decay[1])
-        x = _draw(ss[3], n, "normal32").astype(np.float64)
-        l = (-np.logaddexp(0.0, -x) / tau).astype(np.float32).reshape(B, H, T, DK)
+        x = _draw(ss[3], n, "normal32")
+        l = _elementwise(lambda y: (-np.logaddexp(0.0, -y.astype(np.float64)) / tau)
+                         .astype(np.float32), x, np.float32).reshape(B, H, T, DK)
     elif isinstance(decay, tuple) and decay[0] == "const":
         l = np.full((B, H, T, DK), decay[1], dtype=np.float32)
     elif isinstance(decay, tuple) and decay[0] == "uniform":
@@ -271,6 +300,10 @@ def _la_long(T):
                         qk_scale=1 / math.sqrt(128), decay="mix")
 
 
+def _gla_train():
+    return gla_inputs(32, 16, 4096, 128, 128, 1060, decay="logsigmoid")
+
+
 WORKLOADS = {
     "scan_small": Workload("scan_small", "scan", dict(B=1, T=4096, D=64), _scan_small),
     "scan_large": Workload("scan_large", "scan", dict(B=8, T=16384, D=4096), _scan_large),
@@ -279,6 +312,8 @@ WORKLOADS = {
     "la_gated": Workload("la_gated", "chunk",
                          dict(B=2, H=32, T=32768, DK=128, DV=64), _la_gated),
 }
+WORKLOADS["gla_T4096"] = Workload("gla_T4096", "gla",
+                                  dict(B=32, H=16, T=4096, DK=128, DV=128), _gla_train)
 for _T in LONG_T:
     WORKLOADS[f"la_long_T{_T}"] = Workload(
         f"la_long_T{_T}", "chunk", dict(B=98304 // _T, H=16, T=_T, DK=128, DV=128),

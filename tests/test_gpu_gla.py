@@ -194,3 +194,38 @@ def test_gla_bwd_equal_decays_match_scalar_kernel():
     for i in (0, 1, 2, 4):
         assert rel_l2(to_np(gv[i]), to_np(gs[i])) <= 1e-2, i
     assert rel_l2(to_np(gv[3]).sum(-1), to_np(gs[3])) <= 2e-2
+
+
+@pytest.mark.parametrize("variant", ["plain", "S0_dST"])
+def test_gla_workload_sampled_heads(coracle, variant):
+    """The bench's GLA workload (B=32, H=16, T=4096, dk=dv=128) at full size, in
+    the launch configuration the bench times, against the oracle on sampled
+    sequences; every output finite.  The second variant adds S0 and dS_T."""
+    import torch
+    from gpu_util import rel_l2, say, to_np
+    if variant == "plain":
+        ci = syn.WORKLOADS["gla_T4096"].make()
+    else:
+        ci = syn.gla_inputs(32, 16, 4096, 128, 128, 1061, S0_scale=0.1, dST_scale=0.1)
+    B, H = ci.q.shape[:2]
+    heads = np.array(sorted({0, (B * H) // 2 + 1, B * H - 1}), dtype=np.int64)
+    say(f"[gla workload] {variant} shape={ci.q.shape} heads={heads.tolist()}")
+    o, ST = _gla_fwd(ci)
+    g = _gla_bwd(ci)
+    torch.cuda.synchronize()
+    out = (o, ST) + tuple(g)
+    names = ("o", "ST") + BWD_NAMES
+    for name, t in zip(names, out):
+        assert bool(torch.isfinite(t.float()).all()), name
+    o_r, ST_r = coracle.gla_fwd(ci.q, ci.k, ci.v, ci.l, ci.S0, heads=heads)
+    refs = (o_r, ST_r) + tuple(coracle.gla_bwd(ci.q, ci.k, ci.v, ci.l, ci.S0, ci.dO, ci.dST,
+                                               heads=heads))
+    errs = {}
+    for name, t, r in zip(names, out, refs):
+        if t is None:
+            continue
+        got = to_np(t.reshape(B * H, *t.shape[2:])[torch.from_numpy(heads).to(t.device)])
+        errs[name] = rel_l2(got.reshape(r.shape), r)
+    say(f"[gla workload] {variant} rel-L2: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= TOL}
+    assert not bad, errs
