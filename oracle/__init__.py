@@ -25,6 +25,9 @@ Modules:
 * ``oracle.gla``   -- the same with one decay per key dimension (gated linear
   attention), S_t = diag(a_t) S_{t-1} + k_t v_t^T: loop, matrix mode,
   chunkwise form, adjoint backward and the closed-form vector decay gradient.
+* ``oracle.sscan`` -- the selective scan with N state entries per channel
+  (Mamba-1's recurrence): decay exp(delta A), input delta B x, output C.h;
+  loop, path-sum form, and the reverse-time backward with the chain rule.
 * ``oracle.cref``  -- ctypes wrapper over ``oracle/ref.c``, the same loops in
   C (float64, OpenMP over independent channels / heads) for full-size samples
   and for the CPU baseline timing.
@@ -34,6 +37,6 @@ against values printed on the pages, closed forms, brute force on tiny inputs
 or finite differences; none is "parity unpinned".
 """
 
-from . import scan, attn, gla  # noqa: F401
+from . import scan, attn, gla, sscan  # noqa: F401
 
-__all__ = ["scan", "attn", "gla"]
+__all__ = ["scan", "attn", "gla", "sscan"]

@@ -46,6 +46,8 @@ def _load():
         lib.oracle_la_bwd.argtypes = [p] * 12 + [i64, i64, i64, p, i64]
         lib.oracle_gla_fwd.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, p, i64]
         lib.oracle_gla_bwd.argtypes = [p] * 12 + [i64, i64, i64, p, i64]
+        lib.oracle_sscan_fwd.argtypes = [p] * 6 + [i64] * 4 + [p, i64, p, p]
+        lib.oracle_sscan_bwd.argtypes = [p] * 8 + [i64] * 4 + [p, i64] + [p] * 6
         _lib = lib
     return _lib
 
@@ -184,3 +186,49 @@ def gla_bwd(q, k, v, l, S0, dO, dST=None, heads=None):
                        _ptr(dST), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dl),
                        _ptr(dS0), T, DK, DV, _ptr(hs), n)
     return dq, dk, dv, dl, dS0
+
+
+def _chans(chans, Bt, D):
+    if chans is None:
+        return np.arange(Bt * D, dtype=np.int64)
+    return np.ascontiguousarray(chans, dtype=np.int64)
+
+
+def sscan_fwd(x, delta, A, Bm, Cm, h0=None, chans=None):
+    """Selective scan forward on the (batch, channel) units chans (b * D + d;
+    default all).  x, delta [Bt, T, D], A [D, N], B, C [Bt, T, N], h0 [Bt, D, N]
+    or None, all fp32.  Returns y [nch, T] and hT [nch, N]."""
+    lib = _load()
+    x, delta, A, Bm, Cm = (_c(v, np.float32) for v in (x, delta, A, Bm, Cm))
+    h0 = _c(h0, np.float32)
+    Bt, T, D = x.shape
+    N = A.shape[1]
+    ch = _chans(chans, Bt, D)
+    y = np.empty((len(ch), T))
+    hT = np.empty((len(ch), N))
+    lib.oracle_sscan_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(h0),
+                         Bt, T, D, N, _ptr(ch), len(ch), _ptr(y), _ptr(hT))
+    return y, hT
+
+
+def sscan_bwd(x, delta, A, Bm, Cm, h0, dy, dhT=None, chans=None):
+    """Backward of ``sscan_fwd`` on the units chans.  Returns dx, ddelta
+    [nch, T], dA [nch, N] (each unit's own sum over t), dB, dC [Bt, T, N]
+    (sums over the listed units), dh0 [nch, N]."""
+    lib = _load()
+    x, delta, A, Bm, Cm, dy = (_c(v, np.float32) for v in (x, delta, A, Bm, Cm, dy))
+    h0, dhT = _c(h0, np.float32), _c(dhT, np.float32)
+    Bt, T, D = x.shape
+    N = A.shape[1]
+    ch = _chans(chans, Bt, D)
+    n = len(ch)
+    dx = np.empty((n, T))
+    dd = np.empty((n, T))
+    dA = np.empty((n, N))
+    dB = np.empty((Bt, T, N))
+    dC = np.empty((Bt, T, N))
+    dh0 = np.empty((n, N))
+    lib.oracle_sscan_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(h0),
+                         _ptr(dy), _ptr(dhT), Bt, T, D, N, _ptr(ch), n, _ptr(dx), _ptr(dd),
+                         _ptr(dA), _ptr(dB), _ptr(dC), _ptr(dh0))
+    return dx, dd, dA, dB, dC, dh0

@@ -1,7 +1,8 @@
 /*
  * Float64 CPU oracle loops -- TEST INFRASTRUCTURE ONLY.
  *
- * The same definitions as oracle/scan.py and oracle/attn.py, written as plain
+ * The same definitions as oracle/scan.py, oracle/attn.py, oracle/gla.py and
+ * oracle/sscan.py, written as plain
  * sequential loops in C so that full-size samples and the CPU baseline run in
  * seconds.  OpenMP spreads independent units (channels, heads) over the host
  * cores; each unit runs strictly in time order.  Nothing in the GPU library
@@ -371,5 +372,116 @@ void oracle_gla_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     free(Sb);
     free(blk);
     free(cp);
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * Selective scan with N state entries per channel (Mamba-1's recurrence):
+ *   a_t[d,n] = exp(delta_t[d] A[d,n]),  b_t[d,n] = delta_t[d] B_t[n] x_t[d],
+ *   h_t = a_t h_{t-1} + b_t,  y_t[d] = sum_n C_t[n] h_t[d,n]
+ * (ZTF "Scans over vector and matrix states"; "What limits a recurrent
+ * layer" for the decay exp(delta A)).  Layouts: x, delta, dy [Bt, T, D];
+ * A [D, N]; B, C [Bt, T, N]; h0, dhT [Bt, D, N].  chans lists the (batch,
+ * channel) units to run, as b * D + d; per-unit outputs are indexed by the
+ * position in that list.
+ * ------------------------------------------------------------------------ */
+
+void oracle_sscan_fwd(const float *x, const float *delta, const float *A, const float *Bm,
+                      const float *Cm, const float *h0, int64_t Bt, int64_t T, int64_t D,
+                      int64_t N, const int64_t *chans, int64_t nch, double *y, double *hT) {
+  (void)Bt;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t c = 0; c < nch; ++c) {
+    const int64_t b = chans[c] / D, d = chans[c] % D;
+    double *h = (double *)malloc(sizeof(double) * (size_t)N);
+    for (int64_t n = 0; n < N; ++n) h[n] = h0 ? (double)h0[(b * D + d) * N + n] : 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      const double dl = delta[(b * T + t) * D + d], xv = x[(b * T + t) * D + d];
+      double acc = 0.0;
+      for (int64_t n = 0; n < N; ++n) {
+        const double a = exp(dl * (double)A[d * N + n]);
+        h[n] = a * h[n] + dl * (double)Bm[(b * T + t) * N + n] * xv;
+        acc += (double)Cm[(b * T + t) * N + n] * h[n];
+      }
+      y[c * T + t] = acc;
+    }
+    for (int64_t n = 0; n < N; ++n) hT[c * N + n] = h[n];
+    free(h);
+  }
+}
+
+/* Backward: the reverse-time adjoint per entry, hbar_t = C_t dy_t + a_{t+1}
+ * hbar_{t+1} (+ dhT at the end), dL/da_t = hbar_t h_{t-1}, dL/db_t = hbar_t,
+ * dh0 = a_1 hbar_1 (ZTF "The backward pass is a scan in reverse"), then the
+ * chain rule through a = exp(delta A) and b = delta B x.  Per unit: dx,
+ * ddelta [nch, T], dA [nch, N] (this unit's sum over t), dh0 [nch, N].  dB and
+ * dC [Bt, T, N] receive the sums over the listed units (they are zeroed
+ * here first). */
+void oracle_sscan_bwd(const float *x, const float *delta, const float *A, const float *Bm,
+                      const float *Cm, const float *h0, const float *dy, const float *dhT,
+                      int64_t Bt, int64_t T, int64_t D, int64_t N, const int64_t *chans,
+                      int64_t nch, double *dx, double *ddelta, double *dA, double *dB,
+                      double *dC, double *dh0) {
+  const size_t nbtn = (size_t)(Bt * T * N);
+  memset(dB, 0, sizeof(double) * nbtn);
+  memset(dC, 0, sizeof(double) * nbtn);
+#pragma omp parallel
+  {
+    double *pB = (double *)calloc(nbtn, sizeof(double));
+    double *pC = (double *)calloc(nbtn, sizeof(double));
+    double *hs = (double *)malloc(sizeof(double) * (size_t)((T + 1) * N));
+    double *hbar = (double *)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t c = 0; c < nch; ++c) {
+      const int64_t b = chans[c] / D, d = chans[c] % D;
+      /* hs[t] = h_{t-1} for t = 0..T (hs[0] = h0, hs[T] = h_T) */
+      for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? (double)h0[(b * D + d) * N + n] : 0.0;
+      for (int64_t t = 0; t < T; ++t) {
+        const double dl = delta[(b * T + t) * D + d], xv = x[(b * T + t) * D + d];
+        for (int64_t n = 0; n < N; ++n) {
+          const double a = exp(dl * (double)A[d * N + n]);
+          hs[(t + 1) * N + n] = a * hs[t * N + n] + dl * (double)Bm[(b * T + t) * N + n] * xv;
+        }
+      }
+      for (int64_t n = 0; n < N; ++n) {
+        hbar[n] = dhT ? (double)dhT[(b * D + d) * N + n] : 0.0;
+        dA[c * N + n] = 0.0;
+      }
+      for (int64_t t = T - 1; t >= 0; --t) {
+        const double dl = delta[(b * T + t) * D + d], xv = x[(b * T + t) * D + d];
+        const double g = dy[(b * T + t) * D + d];
+        const double dl_next = t + 1 < T ? delta[(b * T + t + 1) * D + d] : 0.0;
+        double dd = 0.0, sb = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          const double An = A[d * N + n];
+          if (t + 1 < T) hbar[n] *= exp(dl_next * An);
+          hbar[n] += (double)Cm[(b * T + t) * N + n] * g;
+          const double a = exp(dl * An);
+          const double da = hbar[n] * hs[t * N + n];
+          dd += da * a * An;
+          dA[c * N + n] += da * a * dl;
+          sb += hbar[n] * (double)Bm[(b * T + t) * N + n];
+          pB[(b * T + t) * N + n] += hbar[n] * dl * xv;
+          pC[(b * T + t) * N + n] += g * hs[(t + 1) * N + n];
+        }
+        ddelta[c * T + t] = dd + sb * xv;
+        dx[c * T + t] = dl * sb;
+      }
+      for (int64_t n = 0; n < N; ++n) {
+        const double a1 = T > 0 ? exp((double)delta[(b * T) * D + d] * (double)A[d * N + n]) : 1.0;
+        dh0[c * N + n] = a1 * hbar[n];
+      }
+    }
+#pragma omp critical
+    {
+      for (size_t i = 0; i < nbtn; ++i) {
+        dB[i] += pB[i];
+        dC[i] += pC[i];
+      }
+    }
+    free(pB);
+    free(pC);
+    free(hs);
+    free(hbar);
   }
 }

@@ -24,6 +24,10 @@ Workloads (sizes as used by the bench and the full-size tests):
 * ``la_long_T``   -- H=16, dk=dv=128, T in {1024, 4096, 16384, 65536, 98304},
   B = 98304 // T, q, k ~ N(0,1)/sqrt(128), v ~ N(0,1), log a = -1e-5 or -5 with
   probability 1/2 each (i.i.d.), dO ~ N(0,1).
+* ``sscan_mamba`` -- selective scan with N state entries per channel, at the
+  size of one Mamba-2.8B layer on 8 sequences: B=8, T=4096 (32,768 tokens),
+  D=5120 channels, N=16; x, B, C, dy ~ N(0,1), delta log-uniform in
+  [1e-3, 1e-1], A[d, n] = -(n + 1), no h0.
 * ``gla_T4096``   -- one decay per key dimension, B=32, H=16, T=4096,
   dk=dv=128, q, k ~ N(0,1)/sqrt(128), v ~ N(0,1), log a[d] = logsigmoid(x)/16
   with x ~ N(0,1) per (token, dimension), S0 = none, dO ~ N(0,1).
@@ -255,6 +259,51 @@ def gla_inputs(B, H, T, DK, DV, seed, qk_scale=None, v_scale=1.0,
     return ChunkInputs(q, k, v, l, S0, dO, dST)
 
 
+@dataclass
+class SScanInputs:
+    x: np.ndarray            # [B, T, D] float32
+    delta: np.ndarray        # [B, T, D] float32 (step sizes, > 0)
+    A: np.ndarray            # [D, N] float32
+    Bm: np.ndarray           # [B, T, N] float32
+    Cm: np.ndarray           # [B, T, N] float32
+    h0: np.ndarray | None    # [B, D, N] float32
+    dy: np.ndarray           # [B, T, D] float32 (upstream gradient of y)
+    dhT: np.ndarray | None   # [B, D, N] float32 (upstream gradient of h_T)
+
+
+def sscan_inputs(B, T, D, N, seed, delta=("loguniform", 1e-3, 1e-1), A="s4d",
+                 h0_scale=None, dhT_scale=None) -> SScanInputs:
+    """Selective-scan inputs.  x, B, C, dy ~ N(0,1).  delta: ('loguniform', lo,
+    hi) -> exp(U(log lo, log hi)) per (batch, token, channel).  A: 's4d' ->
+    A[d, n] = -(n + 1) (the real diagonal initialisation Mamba-1 starts from);
+    ('uniform', lo, hi) -> U(lo, hi) per (channel, entry); ('const', c).
+    h0, dhT ~ N(0,1) * scale when a scale is given."""
+    ss = np.random.SeedSequence(seed).spawn(8)
+    n = B * T * D
+    x = _normal_f32(ss[0], (B, T, D))
+    if delta[0] == "loguniform":
+        u = _draw(ss[1], n, "uniform64", (math.log(delta[1]), math.log(delta[2])))
+        dl = _elementwise(lambda v: np.exp(v).astype(np.float32), u, np.float32)
+        dl = dl.reshape(B, T, D)
+        del u
+    else:
+        raise ValueError(f"unknown delta kind {delta!r}")
+    if A == "s4d":
+        Am = np.tile(-np.arange(1, N + 1, dtype=np.float32), (D, 1))
+    elif A[0] == "uniform":
+        Am = _draw(ss[2], D * N, "uniform64", (A[1], A[2])).astype(np.float32).reshape(D, N)
+    elif A[0] == "const":
+        Am = np.full((D, N), A[1], dtype=np.float32)
+    else:
+        raise ValueError(f"unknown A kind {A!r}")
+    Bm = _normal_f32(ss[3], (B, T, N))
+    Cm = _normal_f32(ss[4], (B, T, N))
+    h0 = None if h0_scale is None else _normal_f32(ss[5], (B, D, N), h0_scale)
+    dy = _normal_f32(ss[6], (B, T, D))
+    dhT = None if dhT_scale is None else _normal_f32(ss[7], (B, D, N), dhT_scale)
+    return SScanInputs(x, dl, Am, Bm, Cm, h0, dy, dhT)
+
+
 # ---------------------------------------------------------------------------
 # the named workloads
 # ---------------------------------------------------------------------------
@@ -300,6 +349,10 @@ def _la_long(T):
                         qk_scale=1 / math.sqrt(128), decay="mix")
 
 
+def _sscan_mamba():
+    return sscan_inputs(8, 4096, 5120, 16, 1070)
+
+
 def _gla_train():
     return gla_inputs(32, 16, 4096, 128, 128, 1060, decay="logsigmoid")
 
@@ -312,6 +365,8 @@ WORKLOADS = {
     "la_gated": Workload("la_gated", "chunk",
                          dict(B=2, H=32, T=32768, DK=128, DV=64), _la_gated),
 }
+WORKLOADS["sscan_mamba"] = Workload("sscan_mamba", "sscan",
+                                    dict(B=8, T=4096, D=5120, N=16), _sscan_mamba)
 WORKLOADS["gla_T4096"] = Workload("gla_T4096", "gla",
                                   dict(B=32, H=16, T=4096, DK=128, DV=128), _gla_train)
 for _T in LONG_T:
