@@ -16,6 +16,10 @@ step of the computation runs in the library's HIP kernels.
     # one log decay per key dimension (log_decay [B, H, T, DK])
     o, ST              = gla(q, k, v, log_decay, S0=None)
     dq, dk, dv, dl, dS0 = gla_bwd(q, k, v, log_decay, S0, dO, dST=None)
+
+    # selective scan, N state entries per channel (fp32)
+    y, hT, ckpt        = selective_scan(x, delta, A, Bm, Cm, h0=None, save_ckpt=True)
+    dx, ddelta, dA, dB, dC, dh0 = selective_scan_bwd(x, delta, A, Bm, Cm, h0, dy, ckpt=ckpt)
 """
 
 from ._lib import ClaError, lib  # noqa: F401
@@ -30,8 +34,13 @@ from .api import (  # noqa: F401
     gla,
     gla_bwd,
     gla_workspace_bytes,
+    selective_scan,
+    selective_scan_bwd,
+    sscan_ckpt_bytes,
+    sscan_workspace_bytes,
 )
 
 __all__ = ["scan", "scan_bwd", "chunked_linear_attn", "chunked_linear_attn_bwd",
            "scan_workspace_bytes", "chunk_workspace_bytes", "chunk_saved_bytes", "gla", "gla_bwd",
-           "gla_workspace_bytes", "ClaError"]
+           "gla_workspace_bytes", "selective_scan", "selective_scan_bwd", "sscan_ckpt_bytes",
+           "sscan_workspace_bytes", "ClaError"]

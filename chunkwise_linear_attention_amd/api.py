@@ -260,3 +260,78 @@ def gla_bwd(q, k, v, log_decay, S0, dO, dST=None, *, want_dS0=True, chunk=CHUNK,
                        B, H, T, DK, DV, chunk, _ptr(ws), wsb, _stream(dev))
     _lib.check("cla_gla_bwd", st)
     return dq, dk, dv, dl, dS0
+
+
+# ---------------------------------------------------------------------------
+# selective scan with N state entries per channel
+# ---------------------------------------------------------------------------
+
+
+def sscan_ckpt_bytes(B: int, T: int, D: int, N: int) -> int:
+    return int(_lib.lib().cla_sscan_ckpt_bytes(B, T, D, N))
+
+
+def sscan_workspace_bytes(B: int, T: int, D: int, N: int, have_ckpt: bool = True) -> int:
+    return int(_lib.lib().cla_sscan_workspace_bytes(B, T, D, N, 1 if have_ckpt else 0))
+
+
+def selective_scan(x, delta, A, Bm, Cm, h0=None, *, want_final=True, save_ckpt=False):
+    """h_t[d,n] = exp(delta_t[d] A[d,n]) h_{t-1}[d,n] + delta_t[d] B_t[n] x_t[d],
+    y_t[d] = sum_n C_t[n] h_t[d,n].  x, delta: [B, T, D] fp32; A: [D, N];
+    Bm, Cm: [B, T, N]; h0: [B, D, N] or None.  Returns (y, h_T or None) and,
+    with save_ckpt, the checkpoints for ``selective_scan_bwd`` as a third item."""
+    B, T, D = x.shape
+    N = A.shape[1]
+    dev = x.device
+    _need(x, "x", torch.float32, (B, T, D), dev)
+    _need(delta, "delta", torch.float32, (B, T, D), dev)
+    _need(A, "A", torch.float32, (D, N), dev)
+    _need(Bm, "Bm", torch.float32, (B, T, N), dev)
+    _need(Cm, "Cm", torch.float32, (B, T, N), dev)
+    _opt(h0, "h0", torch.float32, (B, D, N), dev)
+    y = torch.empty((B, T, D), dtype=torch.float32, device=dev)
+    hT = torch.empty((B, D, N), dtype=torch.float32, device=dev) if want_final else None
+    L = _lib.lib()
+    ck = None
+    if save_ckpt:
+        nb = int(L.cla_sscan_ckpt_bytes(B, T, D, N))
+        ck = torch.empty(max(nb // 4, 1), dtype=torch.float32, device=dev)
+    st = L.cla_sscan_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(h0), _ptr(y),
+                         _ptr(hT), _ptr(ck), B, T, D, N, _stream(dev))
+    _lib.check("cla_sscan_fwd", st)
+    return (y, hT, ck) if save_ckpt else (y, hT)
+
+
+def selective_scan_bwd(x, delta, A, Bm, Cm, h0, dy, dhT=None, *, ckpt=None, want_dh0=True,
+                       workspace=None):
+    """Backward of ``selective_scan``: returns (dx, ddelta, dA, dB, dC, dh0).
+    ``ckpt`` is the forward's checkpoints (save_ckpt=True) or None (the call
+    then recomputes them)."""
+    B, T, D = x.shape
+    N = A.shape[1]
+    dev = x.device
+    _need(x, "x", torch.float32, (B, T, D), dev)
+    _need(delta, "delta", torch.float32, (B, T, D), dev)
+    _need(A, "A", torch.float32, (D, N), dev)
+    _need(Bm, "Bm", torch.float32, (B, T, N), dev)
+    _need(Cm, "Cm", torch.float32, (B, T, N), dev)
+    _opt(h0, "h0", torch.float32, (B, D, N), dev)
+    _need(dy, "dy", torch.float32, (B, T, D), dev)
+    _opt(dhT, "dhT", torch.float32, (B, D, N), dev)
+    dx = torch.empty_like(x)
+    dd = torch.empty_like(delta)
+    dA = torch.empty((D, N), dtype=torch.float32, device=dev)
+    dB = torch.empty((B, T, N), dtype=torch.float32, device=dev)
+    dC = torch.empty((B, T, N), dtype=torch.float32, device=dev)
+    dh0 = torch.empty((B, D, N), dtype=torch.float32, device=dev) if want_dh0 else None
+    L = _lib.lib()
+    nbytes = int(L.cla_sscan_workspace_bytes(B, T, D, N, 0 if ckpt is None else 1))
+    if workspace is None:
+        ws, wsb = _workspace(nbytes, dev)
+    else:
+        ws, wsb = workspace, workspace.numel() * workspace.element_size()
+    st = L.cla_sscan_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(h0), _ptr(ckpt),
+                         _ptr(dy), _ptr(dhT), _ptr(dx), _ptr(dd), _ptr(dA), _ptr(dB), _ptr(dC),
+                         _ptr(dh0), B, T, D, N, _ptr(ws), wsb, _stream(dev))
+    _lib.check("cla_sscan_bwd", st)
+    return dx, dd, dA, dB, dC, dh0

@@ -9,6 +9,7 @@
 #include "../../include/cla.h"
 #include "gla_kernels.h"
 #include "internal.h"
+#include "sscan_kernels.h"
 
 namespace {
 
@@ -52,7 +53,7 @@ const char *cla_status_string(int status) {
     case CLA_OK: return "CLA_OK";
     case CLA_ERR_NULL_ARG: return "CLA_ERR_NULL_ARG: a required pointer is NULL";
     case CLA_ERR_BAD_SHAPE: return "CLA_ERR_BAD_SHAPE: a size is negative";
-    case CLA_ERR_UNSUPPORTED: return "CLA_ERR_UNSUPPORTED: head size or chunk length not supported";
+    case CLA_ERR_UNSUPPORTED: return "CLA_ERR_UNSUPPORTED: a size, alignment or option is not supported";
     case CLA_ERR_WORKSPACE: return "CLA_ERR_WORKSPACE: workspace missing or too small";
     case CLA_ERR_ALIAS: return "CLA_ERR_ALIAS: an output overlaps an input or another output";
     case CLA_ERR_HIP: return "CLA_ERR_HIP: a HIP launch failed";
@@ -351,6 +352,102 @@ int cla_gla_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   a.nh = (int64_t)nh;
   a.T = T;
   return hip_status(cla::gla::gla_bwd_dispatch(a, (int)DK, (int)DV, s));
+}
+
+// ---------------------------------------------------------------------------
+// selective scan (N state entries per channel)
+// ---------------------------------------------------------------------------
+
+static bool sscan_shape_ok(int64_t B, int64_t T, int64_t D, int64_t N) {
+  return B >= 0 && T >= 0 && D >= 0 && N >= 0;
+}
+
+static bool sscan_supported(int64_t B, int64_t D, int64_t N) {
+  return (N == 4 || N == 8 || N == 16) && D % 4 == 0 && D <= 0x7fffffc0 && B <= 65535;
+}
+
+size_t cla_sscan_ckpt_bytes(int64_t B, int64_t T, int64_t D, int64_t N) {
+  if (!sscan_shape_ok(B, T, D, N) || !sscan_supported(B, D, N)) return 0;
+  return cla::sscan::ckpt_bytes(B, T, D, N);
+}
+
+size_t cla_sscan_workspace_bytes(int64_t B, int64_t T, int64_t D, int64_t N, int have_ckpt) {
+  if (!sscan_shape_ok(B, T, D, N) || !sscan_supported(B, D, N)) return 0;
+  if (B == 0 || T == 0 || D == 0) return 0;
+  return cla::sscan::bwd_ws_bytes(B, T, D, N, !have_ckpt);
+}
+
+int cla_sscan_fwd(const float *x, const float *delta, const float *A, const float *Bm,
+                  const float *Cm, const float *h0, float *y, float *hT, float *ckpt, int64_t B,
+                  int64_t T, int64_t D, int64_t N, cla_stream_t stream) {
+  if (!sscan_shape_ok(B, T, D, N)) return CLA_ERR_BAD_SHAPE;
+  if (!sscan_supported(B, D, N)) return CLA_ERR_UNSUPPORTED;
+  if (B == 0 || D == 0) return CLA_OK;
+  const size_t full = (size_t)(B * T * D) * 4, bn = (size_t)(B * T * N) * 4;
+  const size_t st = (size_t)(B * D * N) * 4, an = (size_t)(D * N) * 4;
+  const size_t ck = cla::sscan::ckpt_bytes(B, T, D, N);
+  if (!A || (T > 0 && (!x || !delta || !Bm || !Cm || !y))) return CLA_ERR_NULL_ARG;
+  if (!(aligned16(x) && aligned16(delta) && aligned16(Bm) && aligned16(Cm) && aligned16(y) &&
+        aligned16(ckpt)))
+    return CLA_ERR_UNSUPPORTED;
+  if (any_alias({{x, full}, {delta, full}, {A, an}, {Bm, bn}, {Cm, bn}, {h0, st}},
+                {{y, full}, {hT, st}, {ckpt, ck}}))
+    return CLA_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0)
+    return hT ? hip_status(cla::launch_copy_or_zero(hT, h0, B * D * N, s)) : CLA_OK;
+  cla::sscan::FwdArgs a{x, delta, A, Bm, Cm, h0, y, hT, ckpt, B, T, D, N};
+  return hip_status(cla::sscan::fwd_dispatch(a, s));
+}
+
+int cla_sscan_bwd(const float *x, const float *delta, const float *A, const float *Bm,
+                  const float *Cm, const float *h0, const float *ckpt, const float *dy,
+                  const float *dhT, float *dx, float *ddelta, float *dA, float *dB, float *dC,
+                  float *dh0, int64_t B, int64_t T, int64_t D, int64_t N, void *workspace,
+                  size_t workspace_bytes, cla_stream_t stream) {
+  if (!sscan_shape_ok(B, T, D, N)) return CLA_ERR_BAD_SHAPE;
+  if (!sscan_supported(B, D, N)) return CLA_ERR_UNSUPPORTED;
+  if (D == 0) return CLA_OK;
+  const size_t full = (size_t)(B * T * D) * 4, bn = (size_t)(B * T * N) * 4;
+  const size_t st = (size_t)(B * D * N) * 4, an = (size_t)(D * N) * 4;
+  const size_t ck = cla::sscan::ckpt_bytes(B, T, D, N);
+  if (!A || !dA || (B > 0 && T > 0 && (!x || !delta || !Bm || !Cm || !dy || !dx || !ddelta ||
+                                       !dB || !dC)))
+    return CLA_ERR_NULL_ARG;
+  if (!(aligned16(x) && aligned16(delta) && aligned16(Bm) && aligned16(Cm) && aligned16(dy) &&
+        aligned16(dx) && aligned16(ddelta) && aligned16(dB) && aligned16(dC) &&
+        aligned16(ckpt)))
+    return CLA_ERR_UNSUPPORTED;
+  const size_t need = (B > 0 && T > 0) ? cla::sscan::bwd_ws_bytes(B, T, D, N, !ckpt) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return CLA_ERR_WORKSPACE;
+  const Range ws{need ? workspace : nullptr, need};
+  if (any_alias({{x, full}, {delta, full}, {A, an}, {Bm, bn}, {Cm, bn}, {h0, st}, {ckpt, ck},
+                 {dy, full}, {dhT, st}},
+                {{dx, full}, {ddelta, full}, {dA, an}, {dB, bn}, {dC, bn}, {dh0, st}, ws}))
+    return CLA_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (B == 0 || T == 0) {
+    hipError_t e = cla::launch_copy_or_zero(dA, nullptr, D * N, s);
+    if (e == hipSuccess && dh0 && B > 0) e = cla::launch_copy_or_zero(dh0, dhT, B * D * N, s);
+    return hip_status(e);
+  }
+  char *w = static_cast<char *>(workspace);
+  float *part = reinterpret_cast<float *>(w);
+  w += cla::sscan::round256(cla::sscan::part_bytes(B, T, D, N));
+  float *dAp = reinterpret_cast<float *>(w);
+  w += cla::sscan::round256((size_t)(B * D * N) * sizeof(float));
+  if (!ckpt) {
+    // no checkpoints from the forward: write them here first
+    float *ck_ws = reinterpret_cast<float *>(w);
+    cla::sscan::FwdArgs f{x, delta, A, Bm, Cm, h0, nullptr, nullptr, ck_ws, B, T, D, N};
+    const hipError_t e = cla::sscan::fwd_dispatch(f, s);
+    if (e != hipSuccess) return hip_status(e);
+    ckpt = ck_ws;
+  }
+  cla::sscan::BwdArgs a{x, delta, A, Bm, Cm, ckpt, dy, dhT, dx, ddelta, dA, dB, dC, dh0,
+                        part, dAp, B, T, D, N};
+  return hip_status(cla::sscan::bwd_dispatch(a, s));
 }
 
 }  // extern "C"

@@ -291,6 +291,58 @@ int cla_gla_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                 int64_t DK, int64_t DV, int64_t chunk, void *workspace,
                 size_t workspace_bytes, cla_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Selective scan with N state entries per channel (Mamba-1's recurrence).
+ * "Parallel scan", sections "Scans over vector and matrix states" (each
+ * channel keeps N state numbers with their own decays; the input is written
+ * into the state) and "What limits a recurrent layer" (the decay
+ * exp(delta_{t,d} A_{d,n}) and the fused kernel that keeps the state on chip
+ * and contracts it with C):
+ *   h_t[d,n] = exp(delta_t[d] A[d,n]) h_{t-1}[d,n] + delta_t[d] B_t[n] x_t[d]
+ *   y_t[d]   = sum_n C_t[n] h_t[d,n],   t = 1..T, h_0 = h0 (zeros if NULL).
+ * All tensors fp32; x, delta, y, Bm, Cm, ckpt 16-byte aligned
+ * (CLA_ERR_UNSUPPORTED otherwise):
+ *   x, delta, y : [B, T, D]  (delta is the step size, used as given)
+ *   A           : [D, N]
+ *   Bm, Cm      : [B, T, N]  (one B_t and C_t per token, shared by channels)
+ *   h0, hT      : [B, D, N]; h0 NULL means zeros, hT NULL is not written
+ *   ckpt        : [B, ceil(T/32), D, N] (cla_sscan_ckpt_bytes bytes) or NULL:
+ *                 the state at the start of every 32-step tile, kept for the
+ *                 backward, which recomputes the states inside a tile from
+ *                 it (the page: Mamba recomputes its states in the backward).
+ * Supported: N in {4, 8, 16}; D a multiple of 4 (at most 2^31 - 64);
+ * B <= 65535 (CLA_ERR_UNSUPPORTED otherwise).  The [B, T, D, N] state tensor
+ * is never written.  No workspace.
+ */
+size_t cla_sscan_ckpt_bytes(int64_t B, int64_t T, int64_t D, int64_t N);
+
+int cla_sscan_fwd(const float *x, const float *delta, const float *A, const float *Bm,
+                  const float *Cm, const float *h0, float *y, float *hT, float *ckpt,
+                  int64_t B, int64_t T, int64_t D, int64_t N, cla_stream_t stream);
+
+/*
+ * Backward of cla_sscan_fwd ("Parallel scan", section "The backward pass is
+ * a scan in reverse", per (channel, entry), then the chain rule through
+ * exp(delta A) and delta B x):  hbar_t = C_t dy_t + a_{t+1} hbar_{t+1}, with
+ * dhT added at the last step.
+ *   ckpt      : the forward's checkpoints, or NULL (this call then runs the
+ *               forward's checkpoint pass itself, into the workspace).
+ *   dy        : [B, T, D] gradient at y;  dhT : [B, D, N] or NULL.
+ *   dx, ddelta: [B, T, D];  dA : [D, N] (summed over the batch);
+ *   dB, dC    : [B, T, N] (summed over channels);  dh0 : [B, D, N] or NULL.
+ *   workspace : cla_sscan_workspace_bytes(B, T, D, N, ckpt != NULL) bytes,
+ *               16-byte aligned (per-workgroup partial sums for dB and dC,
+ *               per-sequence dA, and the checkpoints when not given).
+ * Sums run in a fixed order, so results are bit-identical from run to run.
+ */
+size_t cla_sscan_workspace_bytes(int64_t B, int64_t T, int64_t D, int64_t N, int have_ckpt);
+
+int cla_sscan_bwd(const float *x, const float *delta, const float *A, const float *Bm,
+                  const float *Cm, const float *h0, const float *ckpt, const float *dy,
+                  const float *dhT, float *dx, float *ddelta, float *dA, float *dB, float *dC,
+                  float *dh0, int64_t B, int64_t T, int64_t D, int64_t N, void *workspace,
+                  size_t workspace_bytes, cla_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
