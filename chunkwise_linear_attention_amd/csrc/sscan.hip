@@ -16,7 +16,7 @@
 // independent recurrences the GPU is full without a scan over time.
 //
 // Layout: x, delta, y, dy, dx, ddelta [B, T, D]; A [D, N]; B, C [B, T, N];
-// h0, hT, dhT, dh0 [B, D, N]; checkpoints [B, tiles, D, N]; all fp32.
+// h0, hT, dhT, dh0 [B, D, N]; checkpoints [B, ceil(T/16), D, N]; all fp32.
 // A workgroup is 4 waves = 64 channels of one sequence; lane 4c + q of a wave
 // (c = its channel among the wave's 16) holds entries q NPT .. q NPT + NPT - 1,
 // so y's sum over entries is two quad DPP adds.  Time runs in tiles of 32
@@ -24,13 +24,14 @@
 // and C rows of N entries).
 //
 // Backward (ZTF "The backward pass is a scan in reverse", per entry): the
-// forward writes the state at every tile start; the backward walks the tiles
-// last to first, recomputes the tile's 32 states into registers from that
-// checkpoint (Mamba recomputes its states rather than storing them, the same
+// forward writes the state before every 16th step; the backward walks
+// 16-step tiles last to first, recomputes a tile's 16 states into registers
+// from its checkpoint (Mamba recomputes its states rather than storing them, the same
 // section says), then runs hbar_t = C_t dy_t + a_{t+1} hbar_{t+1} in reverse
 // with the chain rule through exp(delta A) and delta B x.  The sums over
-// channels that dB and dC need pass through LDS in blocks of 4 steps to one
-// partial per workgroup; a small last kernel adds the partials, and dA over
+// channels that dB and dC need are taken over each 16-lane row's 4 channels
+// with DPP, then through LDS in blocks of 8 steps to one partial per
+// workgroup; a small last kernel adds the partials, and dA over
 // the batch, in a fixed order, so every result is deterministic.
 #include "chunk_common.h"
 #include "internal.h"
@@ -62,15 +63,25 @@ __device__ __forceinline__ float quad_sum(float v) {
   return v;
 }
 
-// Stage TT rows of a fp32 array (row r at src + r * ld; rows past nrows
+// sum over the 4 lanes of a 16-lane row that are 4 apart (lane 4c + q: the
+// row's 4 channels at one q); every lane gets the sum of its residue class
+__device__ __forceinline__ float row_channel_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124,
+                                                             0xF, 0xF, true));  // row_ror:4
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128,
+                                                             0xF, 0xF, true));  // row_ror:8
+  return v;
+}
+
+// Stage ROWS rows of a fp32 array (row r at src + r * ld; rows past nrows
 // re-read row nrows - 1; 16-byte pieces past column maxcol4 re-read that
-// piece) into a row-major [TT][W] LDS tile, W a multiple of 4.  Lane i of a
+// piece) into a row-major [ROWS][W] LDS tile, W a multiple of 4.  Lane i of a
 // wave's DMA writes bytes 16 i .. 16 i + 15 of the wave's 1 KB destination.
-template <int W>
+template <int ROWS, int W>
 __device__ __forceinline__ void dma_rows(const float *src, int64_t ld, int nrows, int col0,
                                          int maxcol4, float *tile, int tid) {
   constexpr int PPR = W / 4;
-  constexpr int NP = TT * PPR;
+  constexpr int NP = ROWS * PPR;
   const int lane = tid & 63, w = tid >> 6;
   for (int base = w * 64; base < NP; base += NTH) {
     const int p = base + lane;
@@ -83,10 +94,11 @@ __device__ __forceinline__ void dma_rows(const float *src, int64_t ld, int nrows
   }
 }
 
-// Store rows r < nt, channels d0 + k < D of a [TT][CH] LDS tile (16 bytes a lane).
+// Store rows r < nt, channels d0 + k < D of a [ROWS][CH] LDS tile (16 bytes a lane).
+template <int ROWS>
 __device__ __forceinline__ void store_rows(float *dst, int64_t ld, int nt, int d0, int64_t D,
                                            const float *tile, int tid) {
-  for (int p = tid; p < TT * CH / 4; p += NTH) {
+  for (int p = tid; p < ROWS * CH / 4; p += NTH) {
     const int r = p / (CH / 4), k = 4 * (p % (CH / 4));
     if (r < nt && d0 + k < D)
       *reinterpret_cast<float4 *>(dst + (int64_t)r * ld + d0 + k) =
@@ -117,35 +129,40 @@ __global__ __launch_bounds__(NTH) void sscan_fwd_kernel(FwdArgs a) {
     A2[j] = a.A[(int64_t)dc * N + e0 + j] * kLog2e;
     h[j] = a.h0 ? a.h0[(b * D + dc) * N + e0 + j] : 0.f;
   }
-  const int64_t ntiles = num_tiles(T);
+  const int64_t ntiles = num_tiles(T), nck = num_ckpts(T);
+  const bool save = a.ckpt && valid;
   for (int64_t s = 0; s < ntiles; ++s) {
     const int64_t t0 = s * TT;
     const int nt = (int)min<int64_t>(TT, T - t0);
-    if (a.ckpt && valid) {
-      float *dst = a.ckpt + ((b * ntiles + s) * D + d) * N + e0;
-#pragma unroll
-      for (int j = 0; j < NPT; ++j) dst[j] = h[j];
-    }
-    dma_rows<CH>(a.x + (b * T + t0) * D, D, nt, d0, (int)D - 4, XS, tid);
-    dma_rows<CH>(a.delta + (b * T + t0) * D, D, nt, d0, (int)D - 4, DS, tid);
-    dma_rows<N>(a.Bm + (b * T + t0) * N, N, nt, 0, N - 4, BS, tid);
-    dma_rows<N>(a.Cm + (b * T + t0) * N, N, nt, 0, N - 4, CS, tid);
+    dma_rows<TT, CH>(a.x + (b * T + t0) * D, D, nt, d0, (int)D - 4, XS, tid);
+    dma_rows<TT, CH>(a.delta + (b * T + t0) * D, D, nt, d0, (int)D - 4, DS, tid);
+    dma_rows<TT, N>(a.Bm + (b * T + t0) * N, N, nt, 0, N - 4, BS, tid);
+    dma_rows<TT, N>(a.Cm + (b * T + t0) * N, N, nt, 0, N - 4, CS, tid);
     __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
-    for (int t = 0; t < nt; ++t) {
-      const float xv = XS[t * CH + c], dv = DS[t * CH + c];
-      const float dx = dv * xv;
-      float yp = 0.f;
+    for (int th = 0; th < nt; th += kCkpt) {
+      if (save) {
+        // the state before step t0 + th, for the backward
+        float *dst = a.ckpt + ((b * nck + (t0 + th) / kCkpt) * D + d) * N + e0;
 #pragma unroll
-      for (int j = 0; j < NPT; ++j) {
-        h[j] = fmaf(decay(dv, A2[j]), h[j], dx * BS[t * N + e0 + j]);
-        yp = fmaf(CS[t * N + e0 + j], h[j], yp);
+        for (int j = 0; j < NPT; ++j) dst[j] = h[j];
       }
-      const float yv = quad_sum(yp);
-      if (q == 0) YS[t * CH + c] = yv;
+      const int te = min(th + kCkpt, nt);
+      for (int t = th; t < te; ++t) {
+        const float xv = XS[t * CH + c], dv = DS[t * CH + c];
+        const float dx = dv * xv;
+        float yp = 0.f;
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) {
+          h[j] = fmaf(decay(dv, A2[j]), h[j], dx * BS[t * N + e0 + j]);
+          yp = fmaf(CS[t * N + e0 + j], h[j], yp);
+        }
+        const float yv = quad_sum(yp);
+        if (q == 0) YS[t * CH + c] = yv;
+      }
     }
     lds_barrier();
-    if (a.y) store_rows(a.y + (b * T + t0) * D, D, nt, d0, D, YS, tid);
+    if (a.y) store_rows<TT>(a.y + (b * T + t0) * D, D, nt, d0, D, YS, tid);
   }
   if (a.hT && valid) {
 #pragma unroll
@@ -154,17 +171,19 @@ __global__ __launch_bounds__(NTH) void sscan_fwd_kernel(FwdArgs a) {
 }
 
 template <int NPT>
-__global__ __launch_bounds__(NTH, 2) void sscan_bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NTH, 3) void sscan_bwd_kernel(BwdArgs a) {
   constexpr int N = 4 * NPT;
-  constexpr int RS = 4;       // steps per block of the channel sums
-  constexpr int PC = CH + 4;  // padded row of the channel-sum area (no bank conflicts)
-  __shared__ __attribute__((aligned(16))) float XS[TT * CH];
-  __shared__ __attribute__((aligned(16))) float DS[TT * CH];
-  __shared__ __attribute__((aligned(16))) float GS[TT * CH];  // dy
-  __shared__ __attribute__((aligned(16))) float OX[TT * CH];  // dx out
-  __shared__ __attribute__((aligned(16))) float OD[TT * CH];  // ddelta out
-  __shared__ __attribute__((aligned(16))) float BS[TT * N];
-  __shared__ __attribute__((aligned(16))) float CS[TT * N];
+  constexpr int TB = kCkpt;   // steps per tile: one checkpoint each
+  constexpr int RS = 8;       // steps per block of the channel sums
+  constexpr int NG = CH / 4;  // channel groups: the 4 channels of a 16-lane row
+  constexpr int PC = NG + 4;  // padded row of the channel-sum area (no bank conflicts)
+  __shared__ __attribute__((aligned(16))) float XS[TB * CH];
+  __shared__ __attribute__((aligned(16))) float DS[TB * CH];
+  __shared__ __attribute__((aligned(16))) float GS[TB * CH];  // dy
+  __shared__ __attribute__((aligned(16))) float OX[TB * CH];  // dx out
+  __shared__ __attribute__((aligned(16))) float OD[TB * CH];  // ddelta out
+  __shared__ __attribute__((aligned(16))) float BS[TB * N];
+  __shared__ __attribute__((aligned(16))) float CS[TB * N];
   __shared__ __attribute__((aligned(16))) float PR[RS * 2 * N * PC];
   const int tid = threadIdx.x;
   const int c = tid >> 2, q = tid & 3;
@@ -185,27 +204,27 @@ __global__ __launch_bounds__(NTH, 2) void sscan_bwd_kernel(BwdArgs a) {
     an[j] = 1.f;  // a_{t+1}; none after the last step
     dAacc[j] = 0.f;
   }
-  const int64_t ntiles = num_tiles(T);
-  for (int64_t s = ntiles - 1; s >= 0; --s) {
-    const int64_t t0 = s * TT;
-    const int nt = (int)min<int64_t>(TT, T - t0);
-    float hs[TT][NPT];  // hs[t] = the state before step t of the tile
+  const int64_t nck = num_ckpts(T);
+  for (int64_t s = nck - 1; s >= 0; --s) {
+    const int64_t t0 = s * TB;
+    const int nt = (int)min<int64_t>(TB, T - t0);
+    float hs[TB][NPT];  // hs[t] = the state before step t of the tile
     float he[NPT];
     {
-      const float *src = a.ckpt + ((b * ntiles + s) * D + dc) * N + e0;
+      const float *src = a.ckpt + ((b * nck + s) * D + dc) * N + e0;
 #pragma unroll
       for (int j = 0; j < NPT; ++j) he[j] = src[j];
     }
-    dma_rows<CH>(a.x + (b * T + t0) * D, D, nt, d0, (int)D - 4, XS, tid);
-    dma_rows<CH>(a.delta + (b * T + t0) * D, D, nt, d0, (int)D - 4, DS, tid);
-    dma_rows<CH>(a.dy + (b * T + t0) * D, D, nt, d0, (int)D - 4, GS, tid);
-    dma_rows<N>(a.Bm + (b * T + t0) * N, N, nt, 0, N - 4, BS, tid);
-    dma_rows<N>(a.Cm + (b * T + t0) * N, N, nt, 0, N - 4, CS, tid);
+    dma_rows<TB, CH>(a.x + (b * T + t0) * D, D, nt, d0, (int)D - 4, XS, tid);
+    dma_rows<TB, CH>(a.delta + (b * T + t0) * D, D, nt, d0, (int)D - 4, DS, tid);
+    dma_rows<TB, CH>(a.dy + (b * T + t0) * D, D, nt, d0, (int)D - 4, GS, tid);
+    dma_rows<TB, N>(a.Bm + (b * T + t0) * N, N, nt, 0, N - 4, BS, tid);
+    dma_rows<TB, N>(a.Cm + (b * T + t0) * N, N, nt, 0, N - 4, CS, tid);
     __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
     // the tile's states, recomputed from its checkpoint
 #pragma unroll
-    for (int t = 0; t < TT; ++t) {
+    for (int t = 0; t < TB; ++t) {
 #pragma unroll
       for (int j = 0; j < NPT; ++j) hs[t][j] = he[j];
       if (t < nt) {
@@ -218,7 +237,7 @@ __global__ __launch_bounds__(NTH, 2) void sscan_bwd_kernel(BwdArgs a) {
     }
     // he = the state after the tile's last step
 #pragma unroll
-    for (int t = TT - 1; t >= 0; --t) {
+    for (int t = TB - 1; t >= 0; --t) {
       const int tl = t & (RS - 1);
       float pb[NPT], pc[NPT];
 #pragma unroll
@@ -231,7 +250,7 @@ __global__ __launch_bounds__(NTH, 2) void sscan_bwd_kernel(BwdArgs a) {
         for (int j = 0; j < NPT; ++j) {
           const float av = decay(dv, A2[j]);
           hbar[j] = fmaf(hbar[j], an[j], CS[t * N + e0 + j] * gv);
-          const float ht = t + 1 < nt ? hs[t + 1 < TT ? t + 1 : TT - 1][j] : he[j];
+          const float ht = t + 1 < nt ? hs[t + 1 < TB ? t + 1 : TB - 1][j] : he[j];
           const float daa = hbar[j] * hs[t][j] * av;  // dL/da_t times a_t
           ddp = fmaf(daa, Av[j], ddp);
           dAacc[j] = fmaf(daa, dv, dAacc[j]);
@@ -246,32 +265,42 @@ __global__ __launch_bounds__(NTH, 2) void sscan_bwd_kernel(BwdArgs a) {
           OD[t * CH + c] = fmaf(sb, xv, dd);
         }
       }
+      // dB, dC terms summed over the row's 4 channels in registers; the
+      // row's first quad stores them for the workgroup's sum below
 #pragma unroll
       for (int j = 0; j < NPT; ++j) {
-        PR[(tl * 2 * N + e0 + j) * PC + c] = pb[j];
-        PR[(tl * 2 * N + N + e0 + j) * PC + c] = pc[j];
+        pb[j] = row_channel_sum(pb[j]);
+        pc[j] = row_channel_sum(pc[j]);
+      }
+      if ((tid & 12) == 0) {
+        const int gi = (tid >> 4);  // the row: 4 channels
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) {
+          PR[(tl * 2 * N + e0 + j) * PC + gi] = pb[j];
+          PR[(tl * 2 * N + N + e0 + j) * PC + gi] = pc[j];
+        }
       }
       if (tl == 0) {
-        // sums over the workgroup's 64 channels: one thread per (step, row)
+        // sums over the workgroup's 16 rows: one thread per (step, entry row)
         lds_barrier();
-        if (tid < RS * 2 * N) {
-          const int tt = tid / (2 * N), row = tid % (2 * N);
+        for (int o = tid; o < RS * 2 * N; o += NTH) {
+          const int tt = o / (2 * N), row = o % (2 * N);
           if (t + tt < nt) {
             const float *pr = PR + (tt * 2 * N + row) * PC;
-            float sum = 0.f;
-#pragma unroll
-            for (int k = 0; k < CH; k += 4) {
-              const float4 v = *reinterpret_cast<const float4 *>(pr + k);
-              sum += (v.x + v.y) + (v.z + v.w);
-            }
+            const float4 v0 = *reinterpret_cast<const float4 *>(pr);
+            const float4 v1 = *reinterpret_cast<const float4 *>(pr + 4);
+            const float4 v2 = *reinterpret_cast<const float4 *>(pr + 8);
+            const float4 v3 = *reinterpret_cast<const float4 *>(pr + 12);
+            const float sum = (((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w))) +
+                              (((v2.x + v2.y) + (v2.z + v2.w)) + ((v3.x + v3.y) + (v3.z + v3.w)));
             a.part[((b * G + blockIdx.x) * T + t0 + t + tt) * 2 * N + row] = sum;
           }
         }
         lds_barrier();
       }
     }
-    store_rows(a.dx + (b * T + t0) * D, D, nt, d0, D, OX, tid);
-    store_rows(a.ddelta + (b * T + t0) * D, D, nt, d0, D, OD, tid);
+    store_rows<TB>(a.dx + (b * T + t0) * D, D, nt, d0, D, OX, tid);
+    store_rows<TB>(a.ddelta + (b * T + t0) * D, D, nt, d0, D, OD, tid);
   }
   if (valid) {
 #pragma unroll

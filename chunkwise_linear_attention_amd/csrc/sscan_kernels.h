@@ -9,14 +9,16 @@ namespace cla {
 namespace sscan {
 
 constexpr int kChannels = 64;  // channels per workgroup
-constexpr int kTile = 32;      // steps per time tile = checkpoint interval
+constexpr int kTile = 32;      // steps per time tile of the forward
+constexpr int kCkpt = 16;      // checkpoint interval = steps per tile of the backward
 
 __host__ __device__ inline int64_t num_tiles(int64_t T) { return (T + kTile - 1) / kTile; }
+__host__ __device__ inline int64_t num_ckpts(int64_t T) { return (T + kCkpt - 1) / kCkpt; }
 __host__ __device__ inline int64_t num_groups(int64_t D) { return (D + kChannels - 1) / kChannels; }
 
-// fp32 states at every tile start, [B, tiles, D, N]
+// fp32 states before every 16th step, [B, ceil(T/16), D, N]
 inline size_t ckpt_bytes(int64_t B, int64_t T, int64_t D, int64_t N) {
-  return (size_t)(B * num_tiles(T) * D * N) * sizeof(float);
+  return (size_t)(B * num_ckpts(T) * D * N) * sizeof(float);
 }
 
 struct FwdArgs {

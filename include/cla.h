@@ -306,9 +306,9 @@ int cla_gla_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
  *   A           : [D, N]
  *   Bm, Cm      : [B, T, N]  (one B_t and C_t per token, shared by channels)
  *   h0, hT      : [B, D, N]; h0 NULL means zeros, hT NULL is not written
- *   ckpt        : [B, ceil(T/32), D, N] (cla_sscan_ckpt_bytes bytes) or NULL:
- *                 the state at the start of every 32-step tile, kept for the
- *                 backward, which recomputes the states inside a tile from
+ *   ckpt        : [B, ceil(T/16), D, N] (cla_sscan_ckpt_bytes bytes) or NULL:
+ *                 the state before every 16th step, kept for the
+ *                 backward, which recomputes the 16 states after each from
  *                 it (the page: Mamba recomputes its states in the backward).
  * Supported: N in {4, 8, 16}; D a multiple of 4 (at most 2^31 - 64);
  * B <= 65535 (CLA_ERR_UNSUPPORTED otherwise).  The [B, T, D, N] state tensor
