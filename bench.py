@@ -7,8 +7,9 @@ cores beside it.
 One step is the forward and the backward call over one batch of the
 workload's synthetic inputs, already resident in HBM.  The default workload
 is the diagonal scan B=8, T=16384, D=4096 (fp32); the same run also times
-the chunkwise workloads (la_const, la_gated, la_long_T*) and the per-key-
-dimension decay workload (gla_T4096) and reports them under "extra".  Any of
+the chunkwise workloads (la_const, la_gated, la_long_T*), the selective scan
+(sscan_mamba) and the per-key-dimension decay workload (gla_T4096) and
+reports them under "extra".  Any of
 them can be the headline with --workload.  Prints ONE JSON line.
 """
 
@@ -438,6 +439,126 @@ def cpu_baseline_gla(ci, nheads):
                       "head fraction"}
 
 
+def bench_sscan(args, torch, cla, wl, steps, warmup, cpu_channels=0):
+    """Selective scan, N entries per channel: cla_sscan_fwd (with checkpoints)
+    + cla_sscan_bwd per step."""
+    from chunkwise_linear_attention_amd import _lib
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    ci = wl.make()
+    log(f"[bench] inputs for {wl.name} drawn in {time.time() - t0:.1f}s")
+    B, T, D, N = (wl.shape[k] for k in ("B", "T", "D", "N"))
+    up = lambda v: None if v is None else torch.from_numpy(v).to(dev)
+    x, dl, A, Bm, Cm, h0, dy, dhT = (up(v) for v in (ci.x, ci.delta, ci.A, ci.Bm, ci.Cm, ci.h0,
+                                                     ci.dy, ci.dhT))
+    y = torch.empty_like(x)
+    hT = torch.empty((B, D, N), dtype=torch.float32, device=dev)
+    dx, dd = torch.empty_like(x), torch.empty_like(x)
+    dA = torch.empty((D, N), dtype=torch.float32, device=dev)
+    dB, dC = torch.empty_like(Bm), torch.empty_like(Cm)
+    dh0 = torch.empty_like(hT)
+    L = cla.lib()
+    ck = torch.empty(int(L.cla_sscan_ckpt_bytes(B, T, D, N)) // 4, dtype=torch.float32,
+                     device=dev)
+    wsb = int(L.cla_sscan_workspace_bytes(B, T, D, N, 1))
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    P = lambda t: None if t is None else t.data_ptr()
+
+    def fwd():
+        st = L.cla_sscan_fwd(P(x), P(dl), P(A), P(Bm), P(Cm), P(h0), P(y), P(hT), P(ck),
+                             B, T, D, N, stream)
+        if st:
+            raise RuntimeError(L.cla_status_string(st))
+
+    def bwd():
+        st = L.cla_sscan_bwd(P(x), P(dl), P(A), P(Bm), P(Cm), P(h0), P(ck), P(dy), P(dhT), P(dx),
+                             P(dd), P(dA), P(dB), P(dC), P(dh0), B, T, D, N, P(ws), wsb, stream)
+        if st:
+            raise RuntimeError(L.cla_status_string(st))
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        fwd()
+        bwd()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / steps
+    _lib.timing_enable(True)
+    for _ in range(steps):
+        fwd()
+        bwd()
+    table = _lib.timing_read()
+    _lib.timing_enable(False)
+    elems = B * T * D * N
+    kernels = {}
+    total = sum(x_[0] for x_ in table.values())
+    for name, (tot, cnt) in table.items():
+        avg = tot / cnt
+        ent = {"avg_ms": round(avg, 5), "launches_per_step": cnt // steps,
+               "share": round(tot / total, 4)}
+        if name in ("sscan_fwd", "sscan_bwd"):
+            dirn = "fwd" if name == "sscan_fwd" else "bwd"
+            ops = pm.sscan_ops_per_element(dirn) * elems
+            by = pm.sscan_bytes(B, T, D, N, dirn)
+            ent["algorithmic_ops_per_launch"] = ops
+            ent["Tops"] = round(ops / (avg * 1e-3) / 1e12, 3)
+            ent["algorithmic_bytes_per_launch"] = by
+            ent["GBps"] = round(by / (avg * 1e-3) / 1e9, 1)
+        kernels[name] = ent
+    main = {n: e for n, e in kernels.items() if "Tops" in e}
+    dom = max(main, key=lambda n: main[n]["avg_ms"])
+    d = kernels[dom]
+    path_ops = pm.sscan_ops_per_element("fwdbwd") * elems
+    path_bytes = pm.sscan_bytes(B, T, D, N, "fwdbwd")
+    t_roof = max(path_ops / (pm.PEAK_VALU_TOPS * 1e12), path_bytes / (pm.PEAK_HBM_GBS * 1e9))
+    roof = {"kernel": dom, "bound": "alu", "achieved": d["Tops"], "peak": round(pm.PEAK_VALU_TOPS, 2),
+            "unit": "Top/s (fp32 VALU lane-ops, exp = 4)", "frac": round(d["Tops"] / pm.PEAK_VALU_TOPS, 4),
+            "traffic": measured_traffic(dom, wl.name, "sscan.hip"),
+            "avg_launch_ms": d["avg_ms"],
+            "algorithmic_ops_per_launch": d["algorithmic_ops_per_launch"]}
+    res = {"value": B * T / (ms_step * 1e-3), "ms_per_step": ms_step, "dtype": "f32",
+           "config": {"workload": wl.name, "B": B, "T": T, "D": D, "N": N,
+                      "tokens_per_step": B * T},
+           "roofline": roof,
+           "extra": {"kernels": kernels, "path_algorithmic_ops": path_ops,
+                     "path_algorithmic_bytes": path_bytes,
+                     "path_roofline_frac": round(t_roof / (ms_step * 1e-3), 4),
+                     "hbm_GBps_path": round(path_bytes / (ms_step * 1e-3) / 1e9, 1),
+                     "checkpoint_bytes": ck.numel() * 4, "workspace_bytes": wsb,
+                     "path": "cla_sscan_fwd (checkpoints) + cla_sscan_bwd"}}
+    res["cpu_baseline"] = cpu_baseline_sscan(ci, cpu_channels) if cpu_channels else None
+    del x, dl, A, Bm, Cm, dy, y, hT, dx, dd, dA, dB, dC, dh0, ck, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline_sscan(ci, nch):
+    """The C oracle (float64 loops, OpenMP over channels), forward then
+    backward, on the first `nch` channels of the first sequence at full
+    length."""
+    from oracle import cref
+    cref.build()
+    B, T, D = ci.x.shape
+    chans = np.arange(min(nch, B * D), dtype=np.int64)
+    t0 = time.time()
+    cref.sscan_fwd(ci.x, ci.delta, ci.A, ci.Bm, ci.Cm, ci.h0, chans=chans)
+    cref.sscan_bwd(ci.x, ci.delta, ci.A, ci.Bm, ci.Cm, ci.h0, ci.dy, ci.dhT, chans=chans)
+    secs = time.time() - t0
+    frac = len(chans) / (B * D)
+    return {"value": round(B * T * frac / secs, 1), "unit": "tokens/s",
+            "cores": cref.num_threads(), "kind": "oracle",
+            "sample": f"{len(chans)} of {B * D} (sequence, channel) units at full length "
+                      f"T={T}, N={ci.A.shape[1]}, forward+backward, {secs:.2f} s; tokens/s "
+                      "scaled by the channel fraction"}
+
+
 CHUNK_EXTRAS = ("la_const", "la_gated") + tuple(f"la_long_T{t}" for t in syn.LONG_T)
 GLA_EXTRAS = ("gla_T4096",)
 
@@ -487,6 +608,15 @@ def main():
                 log(f"[bench] {name}: {r['ms_per_step']:.3f} ms/step")
             longs = [chunk[f"la_long_T{t}"]["tokens_per_s"] for t in syn.LONG_T]
             res["extra"]["chunkwise"] = chunk
+            r = bench_sscan(args, torch, cla, syn.WORKLOADS["sscan_mamba"],
+                            max(3, args.steps // 2), args.warmup)
+            res["extra"]["selective_scan"] = {
+                "sscan_mamba": {"tokens_per_s": round(r["value"], 1),
+                                "ms_per_step": round(r["ms_per_step"], 4),
+                                "roofline": r["roofline"],
+                                "path_roofline_frac": r["extra"]["path_roofline_frac"],
+                                "kernels": {n: e["avg_ms"] for n, e in r["extra"]["kernels"].items()}}}
+            log(f"[bench] sscan_mamba: {r['ms_per_step']:.3f} ms/step")
             for name in GLA_EXTRAS:
                 r = bench_gla(args, torch, cla, syn.WORKLOADS[name], max(3, args.steps // 2),
                               args.warmup)
@@ -499,6 +629,10 @@ def main():
                     "kernels": {n: e["avg_ms"] for n, e in r["extra"]["kernels"].items()}}
                 log(f"[bench] {name}: {r['ms_per_step']:.3f} ms/step")
             res["extra"]["la_long_T_flatness_min_over_max"] = round(min(longs) / max(longs), 4)
+    elif wl.kind == "sscan":
+        # the oracle runs the whole workload (every channel): a few seconds
+        res = bench_sscan(args, torch, cla, wl, args.steps, args.warmup,
+                          cpu_channels=wl.shape["B"] * wl.shape["D"] if args.cpu_baseline else 0)
     elif wl.kind == "gla":
         res = bench_gla(args, torch, cla, wl, args.steps, args.warmup,
                         cpu_heads=args.cpu_heads if args.cpu_baseline else 0)

@@ -150,3 +150,34 @@ def gla_kernel_bytes(name: str, dk: int, dv: int) -> int:
         "gla_dkdv": 2 * dk + 2 * dk + 2 * dv + 2 * dv + 4 * dk + 4 * dk + 2 * dk + 2 * dv + 4 * dk,
     }
     return table[name]
+
+
+# --------------------------------------------------------------------------
+# selective scan with N state entries per channel: bound by VALU issue
+# --------------------------------------------------------------------------
+
+# One fp32 VALU operation per lane per cycle: 256 CUs x 4 SIMDs x 16 lanes x
+# 2.4 GHz.  (The 157.3 TFLOP/s fp32 figure counts an FMA as 2 flops and
+# packed two-wide math; the kernels here issue unpacked ops.)
+PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12   # 39.32 T lane-ops/s
+EXP_SLOTS = 4                                   # v_exp_f32 issues at quarter rate
+
+
+def sscan_bytes(B: int, T: int, D: int, N: int, direction: str = "fwdbwd") -> int:
+    """Forward reads x, delta (per token and channel), B, C (per token), A,
+    and writes y; backward reads x, delta, dy, B, C, A and writes dx, ddelta,
+    dB, dC, dA.  The [B, T, D, N] states are never moved."""
+    fwd = B * T * (4 * D * 3 + 4 * N * 2) + 4 * D * N
+    bwd = B * T * (4 * D * 5 + 4 * N * 4) + 4 * D * N * 2
+    return {"fwd": fwd, "bwd": bwd, "fwdbwd": fwd + bwd}[direction]
+
+
+def sscan_ops_per_element(direction: str = "fwdbwd") -> int:
+    """VALU lane-operations per (token, channel, entry), an exp counted as
+    EXP_SLOTS.  Forward: delta*A, exp, (delta x)*B, the state FMA, the output
+    FMA.  Backward: the state recomputed (4 ops and an exp), the decay again
+    (1 op and an exp), the adjoint FMA and C*dy, dL/da*a (2), the delta and A
+    gradients (2 FMAs), the B sum, and the dB and dC terms (2)."""
+    fwd = 4 + EXP_SLOTS
+    bwd = (3 + EXP_SLOTS) + (1 + EXP_SLOTS) + 2 + 2 + 2 + 1 + 2
+    return {"fwd": fwd, "bwd": bwd, "fwdbwd": fwd + bwd}[direction]
