@@ -141,14 +141,21 @@ __device__ __forceinline__ void prep_scaled(const unsigned char *QS, const unsig
   }
 }
 
-// decay factor between blocks for the score products:
-//   R > S : exp(cb_R - ce_S) (<= 1);  R == S and a good block: exp(cb_R - ce_R);
-//   otherwise 0 (a bad diagonal block is done elementwise; R < S is masked)
-__device__ __forceinline__ float block_factor(const float *CS, int DK, int R, int S, int d,
-                                              bool good) {
-  if (R < S || (R == S && !good)) return 0.f;
-  const float cb = R > 0 ? CS[(16 * R - 1) * DK + d] : 0.f;
-  return __expf(cb - CS[(16 * S + 15) * DK + d]);
+// index of the block pair (R, S), S <= R, in 0..9
+__device__ __forceinline__ int pair_index(int R, int S) { return R * (R + 1) / 2 + S; }
+
+// The block factors exp(cb_R - ce_S) of the 10 pairs S <= R for every key
+// dimension, FT[pair][d], formed once per chunk for all lanes (a diagonal
+// block past the decay limit is skipped by its users, not zeroed here).
+template <int DK, int NTH>
+__device__ __forceinline__ void block_factors(const float *CS, float *FT, int tid) {
+  for (int g = tid; g < 10 * DK; g += NTH) {
+    const int p = g / DK, d = g % DK;
+    const int R = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0;
+    const int S = p - R * (R + 1) / 2;
+    const float cb = R > 0 ? CS[(16 * R - 1) * DK + d] : 0.f;
+    FT[g] = __expf(cb - CS[(16 * S + 15) * DK + d]);
+  }
 }
 
 // does block R decay below exp(-kBadLog) in some dimension? (wave-uniform)
@@ -175,7 +182,8 @@ __global__ __launch_bounds__(NTHR, 1) void gla_dq_kernel(GlaBwdArgs a) {
   constexpr int B_DO = B_VS + 64 * DV * 2, B_CS = B_DO + 64 * DV * 2;
   constexpr int B_BS = B_CS + 64 * DK * 4, B_FQ = B_BS + 64 * 64 * 2;
   constexpr int B_FK = B_FQ + 4 * DK * 4, B_AL = B_FK + 4 * DK * 4;
-  constexpr int BUF = B_AL + DK * 4;
+  constexpr int B_FT = B_AL + DK * 4;
+  constexpr int BUF = B_FT + 10 * DK * 4;
   static_assert(BUF <= 160 * 1024, "LDS");
   constexpr int NBQ = DK / 8, NBV = DV / 8, NBL = DK / 4;
   constexpr int NBLK = 2 * NBQ + 2 * NBV + NBL;
@@ -187,6 +195,7 @@ __global__ __launch_bounds__(NTHR, 1) void gla_dq_kernel(GlaBwdArgs a) {
   float *FQ = reinterpret_cast<float *>(buf + B_FQ);
   float *FK = reinterpret_cast<float *>(buf + B_FK);
   float *AL = reinterpret_cast<float *>(buf + B_AL);
+  float *FT = reinterpret_cast<float *>(buf + B_FT);
 
   const int tid0 = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
@@ -248,6 +257,7 @@ __global__ __launch_bounds__(NTHR, 1) void gla_dq_kernel(GlaBwdArgs a) {
     cumsum_rows<DK, NTHR>(CS, n, tid);
     FRESH_LANE();
     prep_scaled<DK, NTHR>(QS, KS, QH, KH, CS, FQ, FK, AL, n, tid);
+    block_factors<DK, NTHR>(CS, FT, tid);
 
     // ---- B[r][s] = dO_r . v_s (masked), stored [r][s]; the 32-column steps
     // read up to the diagonal also cover tiles (0,1) and (2,3): zeros ----
@@ -280,6 +290,7 @@ __global__ __launch_bounds__(NTHR, 1) void gla_dq_kernel(GlaBwdArgs a) {
       for (int kk = 0; kk < DV / 32; ++kk)
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) sfrag[kk][dt] = cvt8(ST_acc[2 * kk][dt], ST_acc[2 * kk + 1][dt]);
+#pragma unroll
       for (int R = 0; R < 4; ++R) {
         const bool good = !block_bad<DK>(CS, R, lane);
         const int r = 16 * R + li;
@@ -294,12 +305,15 @@ __global__ __launch_bounds__(NTHR, 1) void gla_dq_kernel(GlaBwdArgs a) {
           // in-chunk part: sum over blocks S <= R of F_RS (Kh_S^T B_RS^T), one
           // 16-deep product per block, the factor applied after it
           f32x4 accI = zero4();
+#pragma unroll
           for (int S = 0; S <= R; ++S) {
+            if (S == R && !good) break;  // done elementwise below
             f32x4 P = zero4();
             P = mfma16(tr_read4<NCK>(KH, 16 * S + 4 * lg, d0 + 16 * dt, li),  // Kh^T: row d, k = s
                        lds_half<8>(BS, r, 16 * S + 4 * lg), P);                // B: k = s, col t
+            const f32x4 F = *reinterpret_cast<const f32x4 *>(FT + pair_index(R, S) * DK + dc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) accI[i] += block_factor(CS, DK, R, S, dc + i, good) * P[i];
+            for (int i = 0; i < 4; ++i) accI[i] += F[i] * P[i];
           }
           f32x4 acc2 = zero4();
 #pragma unroll
@@ -421,7 +435,8 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
   constexpr int B_AS = B_CS + 64 * DK * 4, B_BS = B_AS + 8192;
   constexpr int B_FQ = B_BS + 8192, B_FK = B_FQ + 4 * DK * 4, B_AL = B_FK + 4 * DK * 4;
   constexpr int B_RED = B_AL + DK * 4;
-  constexpr int BUF = B_RED + 4 * DK * 4;
+  constexpr int B_FT = B_RED + 4 * DK * 4;
+  constexpr int BUF = B_FT + 10 * DK * 4;
   constexpr int NBQ = DK / 8, NBV = DV / 8, NBL = DK / 4;
   constexpr int NBLK = 2 * NBQ + 2 * NBV + NBL;
   static_assert(BUF <= 160 * 1024, "LDS");
@@ -433,6 +448,7 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
   float *FK = reinterpret_cast<float *>(buf + B_FK);
   float *AL = reinterpret_cast<float *>(buf + B_AL);
   float *RED = reinterpret_cast<float *>(buf + B_RED);
+  float *FT = reinterpret_cast<float *>(buf + B_FT);
 
   const int tid0 = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
@@ -553,6 +569,7 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
     cumsum_rows<DK, BTHR>(CS, n, tid);
     FRESH_LANE();
     prep_scaled<DK, BTHR>(QS, KS, QH, KH, CS, FQ, FK, AL, n, tid);
+    block_factors<DK, BTHR>(CS, FT, tid);
     lds_barrier();
 
     // ---- scores, stored transposed [s][r]: side 0 the decayed A, side 1 B ----
@@ -574,12 +591,15 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
               for (int kk = 0; kk < DK / 32; ++kk) {
                 const int dd = 32 * kk + 8 * lg;
                 const bf16x8 kv = lds_frag<NCK>(KH, 16 * S + li, 4 * kk + lg);
-                const float *cbR = CS + (16 * R - 1) * DK + dd;
-                const float *ceS = CS + (16 * S + 15) * DK + dd;
+                const float *ft = FT + pair_index(R, S) * DK + dd;
+                const f32x4 f0 = *reinterpret_cast<const f32x4 *>(ft);
+                const f32x4 f1 = *reinterpret_cast<const f32x4 *>(ft + 4);
                 float y[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                  y[e] = tof(kv[e]) * __expf((R > 0 ? cbR[e] : 0.f) - ceS[e]);
+                for (int e = 0; e < 4; ++e) {
+                  y[e] = tof(kv[e]) * f0[e];
+                  y[e + 4] = tof(kv[e + 4]) * f1[e];
+                }
                 acc = mfma(lds_frag<NCK>(QH, 16 * R + li, 4 * kk + lg), cvt8(y), acc);
               }
             } else {
@@ -670,6 +690,20 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
       for (int kk = 0; kk < DV / 32; ++kk)
 #pragma unroll
         for (int it = 0; it < NI; ++it) gfrag[kk][it] = cvt8(G1(2 * kk, it), G1(2 * kk + 1, it));
+      // q.dq of this lane's rows and dimensions, loaded two blocks ahead of
+      // their use so that the load latency overlaps the block products
+      f32x4 r1c[NI], r1n[NI];  // block S's rows, block S - 1's rows
+      auto load_r1 = [&](int S, f32x4 (&dst)[NI]) {
+#pragma unroll
+        for (int it = 0; it < NI; ++it) {
+          const int s = 16 * S + li;
+          dst[it] = s < n ? *reinterpret_cast<const f32x4 *>(
+                                a.r1 + (bh * T + t0 + s) * DK + d0 + 16 * it + 4 * lg)
+                          : zero4();
+        }
+      };
+      load_r1(3, r1c);
+      load_r1(2, r1n);
       // blocks last to first: the suffix sums of x = q.dq - k.dk over s run
       // through `carry` (later rows of this segment plus its boundary term)
       for (int S = 3; S >= 0; --S) {
@@ -686,12 +720,15 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
           // in-chunk part: sum over blocks R >= S of F_RS (Qh_R^T B_RS), one
           // 16-deep product per block, the factor applied after it
           f32x4 accI = zero4();
+#pragma unroll
           for (int R = S; R < 4; ++R) {
+            if (R == S && !good) continue;  // done elementwise below
             f32x4 P = zero4();
             P = mfma16(tr_read4<NCK>(QH, 16 * R + 4 * lg, d0 + 16 * it, li),  // Qh^T: row d, k = t
                        lds_half<8>(BS, s, 16 * R + 4 * lg), P);                // B^T: k = t, col s
+            const f32x4 F = *reinterpret_cast<const f32x4 *>(FT + pair_index(R, S) * DK + dc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) accI[i] += block_factor(CS, DK, R, S, dc + i, good) * P[i];
+            for (int i = 0; i < 4; ++i) accI[i] += F[i] * P[i];
           }
           f32x4 acc2 = zero4();
 #pragma unroll
@@ -721,13 +758,12 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
             out[i] = v;
             r2v[i] = rv;
           }
-          f32x4 r1 = zero4();
+          const f32x4 r1 = r1c[it];
           if (s < n) {
             bf16x4 ov;
 #pragma unroll
             for (int i = 0; i < 4; ++i) ov[i] = tobf(out[i]);
             *reinterpret_cast<bf16x4 *>(a.dk + (bh * T + t0 + s) * DK + dc) = ov;
-            r1 = *reinterpret_cast<const f32x4 *>(a.r1 + (bh * T + t0 + s) * DK + dc);
           }
           f32x4 dl4;
 #pragma unroll
@@ -746,6 +782,9 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
           if (s < n)
             *reinterpret_cast<f32x4 *>(a.dl + (bh * T + t0 + s) * DK + dc) = dl4;
         }
+#pragma unroll
+        for (int it = 0; it < NI; ++it) r1c[it] = r1n[it];
+        if (S >= 2) load_r1(S - 2, r1n);
       }
     }
 
