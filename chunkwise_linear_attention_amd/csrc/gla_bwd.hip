@@ -56,6 +56,15 @@ __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
+// Lane exchange within 16-lane rows (DPP, no LDS).  row_shl:n: lane i reads
+// lane i + n of its row, 0 past the row's end; row_newbcast:0: every lane
+// reads its row's lane 0.
+template <int CTRL>
+__device__ __forceinline__ float row_dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
 // One path of the in-chunk score product, write s -> read t through key
 // dimension d: both passes form it with this same expression, so that the
 // decay gradient's two sums hold the same numbers and the paths that do not
@@ -770,12 +779,11 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
           for (int i = 0; i < 4; ++i) {
             // inclusive suffix sum over the 16 rows li of block S
             float x = s < n ? r1[i] - r2v[i] : 0.f;
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) {
-              const float y = __shfl_down(x, o, 16);
-              if (li + o < 16) x += y;
-            }
-            const float tot = __shfl(x, lane & 0x30, 64);  // li = 0: the block's total
+            x += row_dpp<0x101>(x);  // row_shl:1
+            x += row_dpp<0x102>(x);  // row_shl:2
+            x += row_dpp<0x104>(x);  // row_shl:4
+            x += row_dpp<0x108>(x);  // row_shl:8
+            const float tot = row_dpp<0x150>(x);  // row_newbcast:0 -- the block's total
             dl4[i] = x + carry[it][i];
             carry[it][i] += tot;
           }
