@@ -145,3 +145,70 @@ def test_chunk_length_limit(lib):
     assert fw(A, B_, C, D_, None, E, None, 1, 1, tmax, 64, 64, 64, None, 0, None) == WS
     assert bw(A, B_, C, D_, None, E, None, G, H_, I, J, None, 1, 1, tmax, 64, 64, 64,
               None, 0, None) == WS
+
+
+def test_gla_validation(lib):
+    ws = lib.cla_gla_workspace_bytes
+    assert ws(1, 1, 64, 64, 64, 64, 0) == 0                 # the forward needs none
+    assert ws(1, 1, 64, 64, 64, 64, 1) > 0
+    assert ws(1, 1, 64, 32, 64, 64, 1) == 0                 # unsupported head size
+    fw = lib.cla_gla_fwd
+    shp = (1, 1, 64, 64, 64, 64)
+    assert fw(A, B_, C, D_, None, E, None, -1, 1, 64, 64, 64, 64, None, 0, None) == SHAPE
+    assert fw(A, B_, C, D_, None, E, None, 1, 1, 64, 64, 64, 32, None, 0, None) == UNSUP
+    assert fw(A, B_, C, D_ + 4, None, E, None, *shp, None, 0, None) == UNSUP  # log decay misaligned
+    assert fw(A, B_, C, None, None, E, None, *shp, None, 0, None) == NULL
+    assert fw(A, B_, C, D_, None, A, None, *shp, None, 0, None) == ALIAS
+    bw = lib.cla_gla_bwd
+    need = ws(*shp, 1)
+    args = [A, B_, C, D_, None, E, None, F, G, H_, I, None]
+    assert bw(*args, *shp, None, 0, None) == WS
+    assert bw(*args, *shp, J, need - 16, None) == WS
+    for idx in (0, 1, 2, 3, 5, 7, 8, 9, 10):
+        a2 = list(args)
+        a2[idx] = None
+        assert bw(*a2, *shp, J, need, None) == NULL, idx
+    a2 = list(args)
+    a2[10] = D_  # dlog_decay aliases log_decay
+    assert bw(*a2, *shp, J, need, None) == ALIAS
+    assert bw(*args, *shp, F, need, None) == ALIAS  # workspace overlaps dq
+
+
+def test_sscan_validation(lib):
+    ck = lib.cla_sscan_ckpt_bytes
+    ws = lib.cla_sscan_workspace_bytes
+    # checkpoints: the state before every 16th step
+    assert ck(2, 100, 64, 16) == 2 * 7 * 64 * 16 * 4
+    assert ck(1, 4, 64, 5) == 0 and ck(1, 4, 66, 16) == 0   # N or D unsupported
+    # backward workspace: per-workgroup dB/dC partials and per-sequence dA,
+    # plus the checkpoints when the forward's are not given
+    with_ck = ws(2, 100, 64, 16, 1)
+    without = ws(2, 100, 64, 16, 0)
+    assert with_ck >= 2 * 1 * 100 * 32 * 4 + 2 * 64 * 16 * 4
+    assert without >= with_ck + ck(2, 100, 64, 16)
+    assert ws(2, 0, 64, 16, 1) == 0
+    fw = lib.cla_sscan_fwd
+    shp = (2, 100, 64, 16)
+    assert fw(A, B_, C, D_, E, None, F, None, None, -1, 100, 64, 16, None) == SHAPE
+    assert fw(A, B_, C, D_, E, None, F, None, None, 2, 100, 64, 12, None) == UNSUP
+    assert fw(A, B_, C, D_, E, None, F, None, None, 2, 100, 62, 16, None) == UNSUP
+    assert fw(A + 4, B_, C, D_, E, None, F, None, None, *shp, None) == UNSUP  # misaligned x
+    for idx in (0, 1, 2, 3, 4, 6):
+        a2 = [A, B_, C, D_, E, None, F, None, None]
+        a2[idx] = None
+        assert fw(*a2, *shp, None) == NULL, idx
+    assert fw(A, B_, C, D_, E, None, A, None, None, *shp, None) == ALIAS        # y over x
+    assert fw(A, B_, C, D_, E, None, F, None, F + 64, *shp, None) == ALIAS      # ckpt over y
+    assert fw(None, None, C, None, None, None, None, None, None, 2, 0, 64, 16, None) == OK
+    bw = lib.cla_sscan_bwd
+    args = [A, B_, C, D_, E, None, None, F, None, G, H_, I, J, K, None]
+    assert bw(*args, *shp, None, 0, None) == WS
+    assert bw(*args, *shp, L, without - 16, None) == WS
+    for idx in (0, 1, 2, 3, 4, 7, 9, 10, 11, 12, 13):
+        a2 = list(args)
+        a2[idx] = None
+        assert bw(*a2, *shp, L, without, None) == NULL, idx
+    a2 = list(args)
+    a2[9] = F  # dx aliases dy
+    assert bw(*a2, *shp, L, without, None) == ALIAS
+    assert bw(*args, *shp, G, without, None) == ALIAS  # workspace overlaps dx
