@@ -64,6 +64,20 @@ __device__ __forceinline__ void dma_f32_block(const float *chunk_src, int n, uns
                                    (lds_void *)(tile + block * 1024), 16, 0, 0);
 }
 
+// value of lane n of this lane's 16-lane row (DPP row_newbcast; n must be a
+// compile-time constant once the caller's loops are unrolled)
+__device__ __forceinline__ float row_bcast(float v, int n) {
+  switch (n) {
+#define CLA_RB(N) \
+  case N:         \
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + N, 0xF, 0xF, false));
+    CLA_RB(0) CLA_RB(1) CLA_RB(2) CLA_RB(3) CLA_RB(4) CLA_RB(5) CLA_RB(6) CLA_RB(7)
+    CLA_RB(8) CLA_RB(9) CLA_RB(10) CLA_RB(11) CLA_RB(12) CLA_RB(13) CLA_RB(14) CLA_RB(15)
+#undef CLA_RB
+  }
+  return v;
+}
+
 template <int DK, int DV>
 __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
   constexpr int NJ = DV / 64;   // 16-column tiles of the state per wave
@@ -230,16 +244,28 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
         exact = __ballot(bad) != 0;
       }
       if (!exact) {
+        // The 16 lanes of a row use the same DK / 2 factors exp(cb_R - ce_S)
+        // (dimensions 32 kk + 8 lg + e): each lane forms two of them and the
+        // row shares them by DPP broadcast.
+        float fpair[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int idx = 2 * li + h;  // (kk, e) = (idx / 8, idx % 8)
+          const int d = 32 * (idx >> 3) + 8 * lg + (idx & 7);
+          if (idx < DK / 4) {
+            const float cb = R > 0 ? CS[(16 * R - 1) * DK + d] : 0.f;
+            fpair[h] = __expf(cb - CS[(16 * S + 15) * DK + d]);
+          } else {
+            fpair[h] = 0.f;
+          }
+        }
 #pragma unroll
         for (int kk = 0; kk < DK / 32; ++kk) {
-          const int d0 = 32 * kk + 8 * lg;  // this lane's 8 dimensions
-          const float *cbR = CS + (16 * R - 1) * DK + d0;
-          const float *ceS = CS + (16 * S + 15) * DK + d0;
           const bf16x8 kv = lds_frag<NCK>(KS, 16 * S + li, 4 * kk + lg);
           float y[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            y[e] = tof(kv[e]) * __expf((R > 0 ? cbR[e] : 0.f) - ceS[e]);
+            y[e] = tof(kv[e]) * row_bcast((8 * kk + e) & 1 ? fpair[1] : fpair[0], (8 * kk + e) >> 1);
           acc = mfma(cvt8(y), lds_frag<NCK>(QS, 16 * R + li, 4 * kk + lg), acc);
         }
       } else {
