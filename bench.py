@@ -345,14 +345,15 @@ def bench_gla(args, torch, cla, wl, steps, warmup, cpu_heads=0):
     dl = torch.empty_like(l)
     dS0 = torch.empty_like(ST)
     L = cla.lib()
+    wsf = int(L.cla_gla_workspace_bytes(B, H, T, DK, DV, 64, 0))
     wsb = int(L.cla_gla_workspace_bytes(B, H, T, DK, DV, 64, 1))
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(wsf, wsb, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     P = lambda t: None if t is None else t.data_ptr()
 
     def fwd():
         st = L.cla_gla_fwd(P(q), P(k), P(v), P(l), P(S0), P(o), P(ST), B, H, T, DK, DV, 64,
-                           None, 0, stream)
+                           P(ws), ws.numel(), stream)
         if st:
             raise RuntimeError(L.cla_status_string(st))
 
@@ -413,7 +414,7 @@ def bench_gla(args, torch, cla, wl, steps, warmup, cpu_heads=0):
                      "path_roofline_frac": round(t_roof / (ms_step * 1e-3), 4),
                      "mfma_util": round(path_flops / (ms_step * 1e-3) / (pm.PEAK_BF16_TFLOPS * 1e12), 4),
                      "hbm_GBps_path": round(path_bytes / (ms_step * 1e-3) / 1e9, 1),
-                     "workspace_bytes": wsb, "path": "cla_gla_fwd + cla_gla_bwd"}}
+                     "workspace_bytes": [wsf, wsb], "path": "cla_gla_fwd + cla_gla_bwd"}}
     res["cpu_baseline"] = cpu_baseline_gla(ci, cpu_heads) if cpu_heads else None
     del q, k, v, l, S0, dO, dST, o, ST, dq, dk, dv, dl, dS0, ws
     torch.cuda.empty_cache()

@@ -261,16 +261,15 @@ size_t cla_gla_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t DK, int6
                                int64_t chunk, int backward) {
   if (B < 0 || H < 0 || T < 0) return 0;
   if (!supported_head_dim(DK) || !supported_head_dim(DV) || chunk != 64) return 0;
-  if (!backward || B == 0 || H == 0 || T == 0) return 0;
-  return cla::gla::gla_bwd_ws_bytes(B * H, T, DK, DV);
+  if (B == 0 || H == 0 || T == 0) return 0;
+  return backward ? cla::gla::gla_bwd_ws_bytes(B * H, T, DK, DV)
+                  : cla::gla::gla_fwd_ws_bytes(B * H, T, DK, DV);
 }
 
 int cla_gla_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                 const float *log_decay, const float *S0, uint16_t *o, float *ST, int64_t B,
                 int64_t H, int64_t T, int64_t DK, int64_t DV, int64_t chunk, void *workspace,
                 size_t workspace_bytes, cla_stream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (B < 0 || H < 0 || T < 0 || DK < 0 || DV < 0 || chunk < 0) return CLA_ERR_BAD_SHAPE;
   if (!supported_head_dim(DK) || !supported_head_dim(DV) || chunk != 64)
     return CLA_ERR_UNSUPPORTED;
@@ -283,13 +282,26 @@ int cla_gla_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   if (T > 0 && !(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o) &&
                  aligned16(log_decay)))
     return CLA_ERR_UNSUPPORTED;
-  if (any_alias({{q, qk}, {k, qk}, {v, vv}, {log_decay, ll}, {S0, ss}}, {{o, vv}, {ST, ss}}))
+  const cla::gla::GlaPlan plan = cla::gla::plan_gla((int64_t)nh, T);
+  if (plan.P > 65535) return CLA_ERR_UNSUPPORTED;
+  const size_t need = T > 0 ? cla::gla::gla_fwd_ws_bytes((int64_t)nh, T, DK, DV) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return CLA_ERR_WORKSPACE;
+  const Range ws{need ? workspace : nullptr, need};
+  if (any_alias({{q, qk}, {k, qk}, {v, vv}, {log_decay, ll}, {S0, ss}}, {{o, vv}, {ST, ss}, ws}))
     return CLA_ERR_ALIAS;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (T == 0)
     return ST ? hip_status(cla::launch_copy_or_zero(ST, S0, (int64_t)(nh * DK * DV), s))
               : CLA_OK;
   cla::gla::GlaFwdArgs a{};
+  a.P = plan.P;
+  a.seg_chunks = plan.seg_chunks;
+  if (plan.P > 1) {
+    const size_t sl = (((size_t)(plan.P - 1) * nh * DK * DV * sizeof(float)) + 255) & ~(size_t)255;
+    a.Sloc = static_cast<float *>(workspace);
+    a.Aseg = reinterpret_cast<float *>(static_cast<char *>(workspace) + sl);
+  }
   a.q = q;
   a.k = k;
   a.v = v;

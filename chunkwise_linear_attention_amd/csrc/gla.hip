@@ -78,7 +78,11 @@ __device__ __forceinline__ float row_bcast(float v, int n) {
   return v;
 }
 
-template <int DK, int DV>
+// OUT: the full forward over segment blockIdx.y of the plan, from S0 or the
+// scanned state of the segments before it.  !OUT: the state pass -- segment
+// blockIdx.y (of the first P - 1) from a zero state, writing its local state
+// and total decay for the scan across segments.
+template <int DK, int DV, bool OUT>
 __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
   constexpr int NJ = DV / 64;   // 16-column tiles of the state per wave
   constexpr int NDT = DK / 16;  // 16-row tiles of the state
@@ -118,8 +122,11 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
     lg = lane >> 4;              \
   } while (0)
   const int64_t bh = blockIdx.x;
+  const int64_t seg = blockIdx.y;
   const int64_t T = a.T;
   const int64_t nchunks = (T + TC - 1) / TC;
+  const int64_t c_begin = seg * a.seg_chunks;
+  const int64_t c_end = min(nchunks, c_begin + a.seg_chunks);
   const int j0 = w * (DV / 4);
   const uint16_t *qh = a.q + bh * T * DK;
   const uint16_t *kh = a.k + bh * T * DK;
@@ -132,8 +139,10 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) S_acc[dt][jt] = zero4();
-  if (a.S0) {
-    const float *src = a.S0 + bh * DK * DV;
+  const float *src = !OUT ? nullptr
+                     : seg == 0 ? (a.S0 ? a.S0 + bh * DK * DV : nullptr)
+                                : a.Sloc + ((seg - 1) * a.nh + bh) * DK * DV;
+  if (src) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -143,7 +152,9 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
           S_acc[dt][jt][i] = src[(16 * dt + 4 * lg + i) * DV + j0 + 16 * jt + li];
   }
 
-  for (int64_t ci = 0; ci < nchunks; ++ci) {
+  float lsum = 0.f;  // state pass: the segment's summed log decay of dimension tid
+
+  for (int64_t ci = c_begin; ci < c_end; ++ci) {
     const int64_t t0 = ci * TC;
     const int n = (int)min<int64_t>(TC, T - t0);
 
@@ -209,12 +220,13 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
     }
     lds_barrier();
 
-    // ---- scores: tile (R, S), S <= R, as acc[i] = A[16R + li][16S + 4lg + i] ----
-    // wave w: the diagonal tile (w, w) and the off-diagonal tiles w, w + 4 of
-    // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
     f32x4 sc[3];
     int tR[3], tS[3];
     int ntile = 0;
+    if constexpr (OUT) {
+    // ---- scores: tile (R, S), S <= R, as acc[i] = A[16R + li][16S + 4lg + i] ----
+    // wave w: the diagonal tile (w, w) and the off-diagonal tiles w, w + 4 of
+    // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
     {
       const int offR = 0x122333, offS = 0x001012;  // packed (R, S) of the six
       tR[0] = w;
@@ -299,6 +311,7 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
       }
       sc[x] = acc;
     }
+    }
     lds_barrier();  // every read of the cumulative logs' interior rows is done
 
     // ---- per-block factors (from the block-end rows, before P covers them) ----
@@ -308,6 +321,7 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
 #pragma unroll
       for (int B = 0; B < 4; ++B) ce[B] = CS[(16 * B + 15) * DK + d];
       const float cl = ce[3];  // the chunk's last cumulative log (rows past n add 0)
+      if (!OUT) lsum += cl;
 #pragma unroll
       for (int B = 0; B < 4; ++B) {
         CS[(R_FQ + B) * DK + d] = B > 0 ? __expf(ce[B - 1]) : 1.f;  // exp(cb_B)
@@ -316,6 +330,7 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
       CS[R_AL * DK + d] = __expf(cl);
     }
     lds_barrier();
+    if constexpr (OUT) {
     // ---- P[r][s] (bf16) over the first rows of the logs ----
     FRESH_LANE();
 #pragma unroll
@@ -393,6 +408,8 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
       }
     }
 
+    }
+
     // ---- state update: S <- diag(alpha) S + KG^T V ----
     {
       FRESH_LANE();
@@ -428,7 +445,17 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
   }
 
   FRESH_LANE();
-  if (a.ST) {
+  if (!OUT) {
+    float *dst = a.Sloc + (seg * a.nh + bh) * DK * DV;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dst[(16 * dt + 4 * lg + i) * DV + j0 + 16 * jt + li] = S_acc[dt][jt][i];
+    if (tid < DK) a.Aseg[(seg * a.nh + bh) * DK + tid] = __expf(lsum);
+  } else if (a.ST && seg == a.P - 1) {
     float *dst = a.ST + bh * DK * DV;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -442,14 +469,63 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
 
 #undef FRESH_LANE
 
+// The state each segment starts from (ZTF "Splitting one sequence across
+// devices", with a decay per key dimension): S_in(0) = S0 and
+// S_in(p) = diag(A(p-1)) S_in(p-1) + S_loc(p-1), one thread per state entry,
+// written over S_loc(p-1) once read.
+__global__ __launch_bounds__(256) void gla_segment_scan_kernel(const float *S0, float *Sloc,
+                                                               const float *Aseg, int64_t nh,
+                                                               int64_t DK, int64_t DV, int64_t P) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= nh * DK * DV) return;
+  const int64_t bh = e / (DK * DV), d = (e / DV) % DK;
+  float s = S0 ? S0[e] : 0.f;
+  for (int64_t p = 1; p < P; ++p) {
+    float *slot = Sloc + (p - 1) * nh * DK * DV + e;
+    s = Aseg[((p - 1) * nh + bh) * DK + d] * s + *slot;
+    *slot = s;
+  }
+}
+
 template <int DK, int DV>
 hipError_t gla_fwd_impl(const GlaFwdArgs &args, hipStream_t stream) {
-  CLA_LAUNCH("gla_fwd", (gla_fwd_kernel<DK, DV>), dim3((unsigned)args.nh), dim3(NTHR), stream,
-             args);
+  if (args.P > 1) {
+    CLA_LAUNCH("gla_fwd_segments", (gla_fwd_kernel<DK, DV, false>),
+               dim3((unsigned)args.nh, (unsigned)(args.P - 1)), dim3(NTHR), stream, args);
+    const int64_t n = args.nh * DK * DV;
+    CLA_LAUNCH("gla_segment_scan", gla_segment_scan_kernel, dim3((unsigned)((n + 255) / 256)),
+               dim3(256), stream, args.S0, args.Sloc, args.Aseg, args.nh, (int64_t)DK, (int64_t)DV,
+               args.P);
+  }
+  CLA_LAUNCH("gla_fwd", (gla_fwd_kernel<DK, DV, true>),
+             dim3((unsigned)args.nh, (unsigned)args.P), dim3(NTHR), stream, args);
   return hipGetLastError();
 }
 
 }  // namespace
+
+GlaPlan plan_gla(int64_t nh, int64_t T) {
+  // enough segments to give the GPU about 512 workgroups (two per CU), each
+  // a whole number of 16-chunk blocks
+  const int64_t nchunks = (T + TC - 1) / TC;
+  GlaPlan p{1, nchunks > 0 ? nchunks : 1};
+  if (nh >= 512 || nchunks <= kSegChunks) return p;
+  const int64_t want = (512 + nh - 1) / nh;
+  int64_t seg = (nchunks + want - 1) / want;
+  seg = ((seg + kSegChunks - 1) / kSegChunks) * kSegChunks;
+  p.seg_chunks = seg;
+  p.P = (nchunks + seg - 1) / seg;
+  return p;
+}
+
+static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t gla_fwd_ws_bytes(int64_t nh, int64_t T, int64_t DK, int64_t DV) {
+  const GlaPlan p = plan_gla(nh, T);
+  if (p.P <= 1) return 0;
+  return round256((size_t)((p.P - 1) * nh * DK * DV) * sizeof(float)) +
+         round256((size_t)((p.P - 1) * nh * DK) * sizeof(float));
+}
 
 hipError_t gla_fwd_dispatch(const GlaFwdArgs &args, int DK, int DV, hipStream_t stream) {
   if (DK == 64 && DV == 64) return gla_fwd_impl<64, 64>(args, stream);

@@ -8,6 +8,18 @@
 namespace cla {
 namespace gla {
 
+// The backward's decay gradient sums q.dq - k.dk backwards inside blocks of
+// this many chunks, each started from the boundary term <S, G>.  Segments of
+// the sequence that run on separate workgroups are whole multiples of it.
+constexpr int64_t kSegChunks = 16;
+
+// How a sequence is split over workgroups: P segments of seg_chunks chunks
+// (the last one shorter).  P = 1 when B*H alone fills the GPU.
+struct GlaPlan {
+  int64_t P, seg_chunks;
+};
+GlaPlan plan_gla(int64_t nh, int64_t T);
+
 struct GlaFwdArgs {
   const uint16_t *q, *k;  // [nh, T, DK] bf16
   const uint16_t *v;      // [nh, T, DV] bf16
@@ -16,13 +28,17 @@ struct GlaFwdArgs {
   uint16_t *o;            // [nh, T, DV] bf16
   float *ST;              // [nh, DK, DV] or NULL (not written)
   int64_t nh, T;
+  int64_t P, seg_chunks;  // the plan
+  // P > 1: each segment's local state from zero (Sloc [P-1, nh, DK, DV]) and
+  // total decay (Aseg [P-1, nh, DK]), then, scanned in place, the state each
+  // segment starts from (segment p >= 1 reads slot p - 1)
+  float *Sloc, *Aseg;
 };
 
-hipError_t gla_fwd_dispatch(const GlaFwdArgs &args, int DK, int DV, hipStream_t stream);
+// Workspace of the forward: Sloc and Aseg (256-byte aligned), 0 when P = 1.
+size_t gla_fwd_ws_bytes(int64_t nh, int64_t T, int64_t DK, int64_t DV);
 
-// The backward's decay gradient sums q.dq - k.dk backwards inside segments of
-// this many chunks, each started from the exact boundary term <S, G>.
-constexpr int64_t kSegChunks = 16;
+hipError_t gla_fwd_dispatch(const GlaFwdArgs &args, int DK, int DV, hipStream_t stream);
 
 struct GlaBwdArgs {
   const uint16_t *q, *k;  // [nh, T, DK] bf16

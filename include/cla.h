@@ -249,9 +249,14 @@ int cla_timing_read(const char **names, double *total_ms, int64_t *counts, int m
  * ("Long products without underflow"); the in-chunk products are formed
  * from factors that never exceed 1, with an exact elementwise path for any
  * 16-step block whose decay falls below exp(-60) in some dimension.
- * The forward needs no workspace (cla_gla_workspace_bytes returns 0 for it;
- * workspace may be NULL).  One workgroup runs each sequence-head from its
- * first chunk to its last (no split of the sequence across workgroups).
+ * When B*H alone gives fewer than 512 workgroups, each sequence is cut into
+ * segments of whole 16-chunk blocks that run on separate workgroups: a state
+ * pass gives each segment's local state and total decay, a scan over the
+ * segments the state each one starts from ("Splitting one sequence across
+ * devices", applied inside one GPU).  The forward's workspace
+ * (cla_gla_workspace_bytes(..., backward = 0), 16-byte aligned) holds those
+ * states; it is 0 bytes, and workspace may be NULL, when the sequence is not
+ * split.
  */
 size_t cla_gla_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t DK,
                                int64_t DV, int64_t chunk, int backward);

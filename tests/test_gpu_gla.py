@@ -50,6 +50,11 @@ FWD_CASES = [
     (1, 1, 200, 128, 128, ("const", -5.0), True, 8),         # every block exact
     (2, 2, 333, 128, 64, ("uniform", -0.02, 0.0), True, 9),  # weak decays
     (1, 2, 130, 64, 128, ("const", 0.0), False, 10),         # no decay
+    # few sequence-heads, long sequences: split into segments of 16-chunk blocks
+    (1, 2, 3000, 64, 64, "logsigmoid", True, 11),            # 3 segments
+    (1, 1, 5000, 128, 128, ("uniform", -0.05, 0.0), True, 12),  # 5 segments, weak decays
+    (2, 1, 2100, 128, 64, ("logsigmoid", 1.0), False, 13),   # ragged last segment
+    (1, 1, 4200, 64, 64, ("uniform", -8.0, 0.0), True, 14),  # exact blocks across segments
 ]
 
 
