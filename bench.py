@@ -561,7 +561,7 @@ def cpu_baseline_sscan(ci, nch):
 
 
 CHUNK_EXTRAS = ("la_const", "la_gated") + tuple(f"la_long_T{t}" for t in syn.LONG_T)
-GLA_EXTRAS = ("gla_T4096",)
+GLA_EXTRAS = ("gla_T4096", "gla_long_T98304")
 
 
 def main():

@@ -334,6 +334,7 @@ int cla_gla_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                  aligned16(dq) && aligned16(dk) && aligned16(dv) && aligned16(log_decay) &&
                  aligned16(dlog_decay)))
     return CLA_ERR_UNSUPPORTED;
+  if (cla::gla::plan_gla((int64_t)nh, T).P > 65535) return CLA_ERR_UNSUPPORTED;
   const size_t need = T > 0 ? cla::gla::gla_bwd_ws_bytes((int64_t)nh, T, DK, DV) : 0;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return CLA_ERR_WORKSPACE;
@@ -345,8 +346,35 @@ int cla_gla_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   if (T == 0)
     return dS0 ? hip_status(cla::launch_copy_or_zero(dS0, dST, (int64_t)(nh * DK * DV), s))
                : CLA_OK;
-  const size_t r1_bytes = ((size_t)nh * T * DK * sizeof(float) + 255) & ~(size_t)255;
+  const cla::gla::GlaPlan plan = cla::gla::plan_gla((int64_t)nh, T);
+  auto r256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t r1_bytes = r256((size_t)nh * T * DK * sizeof(float));
+  const int64_t nblk = ((T + 63) / 64 + cla::gla::kSegChunks - 1) / cla::gla::kSegChunks;
+  char *wp = static_cast<char *>(workspace) + r1_bytes + r256((size_t)nblk * nh * DK * DV * 4);
   cla::gla::GlaBwdArgs a{};
+  a.P = plan.P;
+  a.seg_chunks = plan.seg_chunks;
+  if (plan.P > 1) {
+    // the state each segment starts from: the forward's state pass and scan
+    cla::gla::GlaFwdArgs f{};
+    f.q = q;
+    f.k = k;
+    f.v = v;
+    f.l = log_decay;
+    f.S0 = S0;
+    f.nh = (int64_t)nh;
+    f.T = T;
+    f.P = plan.P;
+    f.seg_chunks = plan.seg_chunks;
+    f.Sloc = reinterpret_cast<float *>(wp);
+    f.Aseg = reinterpret_cast<float *>(wp + r256((size_t)(plan.P - 1) * nh * DK * DV * 4));
+    const hipError_t e = cla::gla::gla_states_dispatch(f, (int)DK, (int)DV, s);
+    if (e != hipSuccess) return hip_status(e);
+    a.Sin = f.Sloc;
+    wp += cla::gla::gla_fwd_ws_bytes((int64_t)nh, T, DK, DV);
+    a.Gloc = reinterpret_cast<float *>(wp);
+    a.Aq = reinterpret_cast<float *>(wp + r256((size_t)plan.P * nh * DK * DV * 4));
+  }
   a.q = q;
   a.k = k;
   a.v = v;

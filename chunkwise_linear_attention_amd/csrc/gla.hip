@@ -161,7 +161,7 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
     // ---- stage: Q, K, V, l of the chunk into LDS ----
     lds_barrier();  // the previous chunk's LDS reads are done
     FRESH_LANE();
-    for (int b = w; b < NBLK; b += NWAVE) {
+    for (int b = OUT ? w : NBQ + w; b < NBLK; b += NWAVE) {  // the state pass needs no q
       if (b < NBQ)
         dma_block<DK>(qh + t0 * DK, n, QS, b, lane);
       else if (b < 2 * NBQ)
@@ -206,17 +206,18 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
       const float *cr = CS + r * DK + 8 * c8;
       const float *ce = CS + (16 * B + 15) * DK + 8 * c8;
       const float *cb = CS + (16 * B - 1) * DK + 8 * c8;  // read only when B > 0
-      bf16x8 qv = *reinterpret_cast<const bf16x8 *>(QS + off);
       bf16x8 kv = *reinterpret_cast<const bf16x8 *>(KS + off);
-      float yq[8], yk[8];
+      float yk[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float cbe = B > 0 ? cb[e] : 0.f;
-        yq[e] = tof(qv[e]) * __expf(cr[e] - cbe);
-        yk[e] = r < n ? tof(kv[e]) * __expf(ce[e] - cr[e]) : 0.f;
-      }
-      *reinterpret_cast<bf16x8 *>(QS + off) = cvt8(yq);
+      for (int e = 0; e < 8; ++e) yk[e] = r < n ? tof(kv[e]) * __expf(ce[e] - cr[e]) : 0.f;
       *reinterpret_cast<bf16x8 *>(KS + off) = cvt8(yk);
+      if (OUT) {
+        bf16x8 qv = *reinterpret_cast<const bf16x8 *>(QS + off);
+        float yq[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) yq[e] = tof(qv[e]) * __expf(cr[e] - (B > 0 ? cb[e] : 0.f));
+        *reinterpret_cast<bf16x8 *>(QS + off) = cvt8(yq);
+      }
     }
     lds_barrier();
 
@@ -488,14 +489,21 @@ __global__ __launch_bounds__(256) void gla_segment_scan_kernel(const float *S0, 
 }
 
 template <int DK, int DV>
+hipError_t gla_states_impl(const GlaFwdArgs &args, hipStream_t stream) {
+  CLA_LAUNCH("gla_fwd_segments", (gla_fwd_kernel<DK, DV, false>),
+             dim3((unsigned)args.nh, (unsigned)(args.P - 1)), dim3(NTHR), stream, args);
+  const int64_t n = args.nh * DK * DV;
+  CLA_LAUNCH("gla_segment_scan", gla_segment_scan_kernel, dim3((unsigned)((n + 255) / 256)),
+             dim3(256), stream, args.S0, args.Sloc, args.Aseg, args.nh, (int64_t)DK, (int64_t)DV,
+             args.P);
+  return hipGetLastError();
+}
+
+template <int DK, int DV>
 hipError_t gla_fwd_impl(const GlaFwdArgs &args, hipStream_t stream) {
   if (args.P > 1) {
-    CLA_LAUNCH("gla_fwd_segments", (gla_fwd_kernel<DK, DV, false>),
-               dim3((unsigned)args.nh, (unsigned)(args.P - 1)), dim3(NTHR), stream, args);
-    const int64_t n = args.nh * DK * DV;
-    CLA_LAUNCH("gla_segment_scan", gla_segment_scan_kernel, dim3((unsigned)((n + 255) / 256)),
-               dim3(256), stream, args.S0, args.Sloc, args.Aseg, args.nh, (int64_t)DK, (int64_t)DV,
-               args.P);
+    const hipError_t e = gla_states_impl<DK, DV>(args, stream);
+    if (e != hipSuccess) return e;
   }
   CLA_LAUNCH("gla_fwd", (gla_fwd_kernel<DK, DV, true>),
              dim3((unsigned)args.nh, (unsigned)args.P), dim3(NTHR), stream, args);
@@ -532,6 +540,20 @@ hipError_t gla_fwd_dispatch(const GlaFwdArgs &args, int DK, int DV, hipStream_t 
   if (DK == 64 && DV == 128) return gla_fwd_impl<64, 128>(args, stream);
   if (DK == 128 && DV == 64) return gla_fwd_impl<128, 64>(args, stream);
   if (DK == 128 && DV == 128) return gla_fwd_impl<128, 128>(args, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gla
+}  // namespace cla
+
+namespace cla {
+namespace gla {
+
+hipError_t gla_states_dispatch(const GlaFwdArgs &args, int DK, int DV, hipStream_t stream) {
+  if (DK == 64 && DV == 64) return gla_states_impl<64, 64>(args, stream);
+  if (DK == 64 && DV == 128) return gla_states_impl<64, 128>(args, stream);
+  if (DK == 128 && DV == 64) return gla_states_impl<128, 64>(args, stream);
+  if (DK == 128 && DV == 128) return gla_states_impl<128, 128>(args, stream);
   return hipErrorInvalidValue;
 }
 

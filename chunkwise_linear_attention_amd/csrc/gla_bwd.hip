@@ -219,8 +219,11 @@ __global__ __launch_bounds__(NTHR, 1) void gla_dq_kernel(GlaBwdArgs a) {
     lg = lane >> 4;              \
   } while (0)
   const int64_t bh = blockIdx.x;
+  const int64_t seg = blockIdx.y;
   const int64_t T = a.T;
   const int64_t nchunks = (T + TC - 1) / TC;
+  const int64_t c_begin = seg * a.seg_chunks;
+  const int64_t c_end = min(nchunks, c_begin + a.seg_chunks);
   const int d0 = w * (DK / 4);
   const uint16_t *qh = a.q + bh * T * DK;
   const uint16_t *kh = a.k + bh * T * DK;
@@ -235,14 +238,29 @@ __global__ __launch_bounds__(NTHR, 1) void gla_dq_kernel(GlaBwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       ST_acc[jt][dt] = zero4();
-      if (a.S0) {
+      // the state this segment starts from: S0, or the scanned segment state
+      const float *src = seg == 0 ? (a.S0 ? a.S0 + bh * DK * DV : nullptr)
+                                  : a.Sin + ((seg - 1) * a.nh + bh) * DK * DV;
+      if (src) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          ST_acc[jt][dt][i] = a.S0[(bh * DK + d0 + 16 * dt + li) * DV + 16 * jt + 4 * lg + i];
+          ST_acc[jt][dt][i] = src[(d0 + 16 * dt + li) * DV + 16 * jt + 4 * lg + i];
       }
     }
+  // segments after the first: the local adjoint state sum_t diag(A_t) q_t dO_t^T
+  // (A_t the decay from the segment's start through step t), laid out as
+  // ST_acc, and the running decay from the segment's start to the chunk
+  const bool gsum = a.P > 1 && seg > 0;
+  f32x4 G_acc[NJT][NDT];
+  float apre[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    apre[dt] = 1.f;
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt) G_acc[jt][dt] = zero4();
+  }
 
-  for (int64_t ci = 0; ci < nchunks; ++ci) {
+  for (int64_t ci = c_begin; ci < c_end; ++ci) {
     const int64_t t0 = ci * TC;
     const int n = (int)min<int64_t>(TC, T - t0);
 
@@ -414,7 +432,36 @@ __global__ __launch_bounds__(NTHR, 1) void gla_dq_kernel(GlaBwdArgs a) {
       }
     }
 
-    // ---- the state at the end of each segment (and of the sequence) ----
+    // ---- the segment's local adjoint state: G^T += dO^T (A (.) Q) ----
+    if (gsum) {
+      FRESH_LANE();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 qa[NDT];  // (A (.) Q) B operands: k = t, column d
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int d = d0 + 16 * dt + li;
+          const bf16x8 x = tr_frag<NCK>(QS, 32 * kb, d0 + 16 * dt, li, lg);
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int t = 32 * kb + 8 * lg + e;
+            y[e] = t < n ? tof(x[e]) * (apre[dt] * __expf(CS[t * DK + d])) : 0.f;
+          }
+          qa[dt] = cvt8(y);
+        }
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) {
+          const bf16x8 da = tr_frag<NCV>(DOS, 32 * kb, 16 * jt, li, lg);  // dO^T: row j, k = t
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) G_acc[jt][dt] = mfma(da, qa[dt], G_acc[jt][dt]);
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) apre[dt] *= AL[d0 + 16 * dt + li];
+    }
+
+    // ---- the state at the end of each 16-chunk block (and of the sequence) ----
     if ((ci + 1) % kSegChunks == 0 || ci + 1 == nchunks) {
       FRESH_LANE();
       float *dst = a.Sseg + ((ci / kSegChunks) * a.nh + bh) * DK * DV;
@@ -424,6 +471,20 @@ __global__ __launch_bounds__(NTHR, 1) void gla_dq_kernel(GlaBwdArgs a) {
         for (int dt = 0; dt < NDT; ++dt)
           *reinterpret_cast<f32x4 *>(dst + (d0 + 16 * dt + li) * DV + 16 * jt + 4 * lg) =
               ST_acc[jt][dt];
+    }
+  }
+  if (gsum) {
+    FRESH_LANE();
+    float *dst = a.Gloc + (seg * a.nh + bh) * DK * DV;
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f32x4 *>(dst + (d0 + 16 * dt + li) * DV + 16 * jt + 4 * lg) =
+            G_acc[jt][dt];
+    if (lg == 0) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) a.Aq[(seg * a.nh + bh) * DK + d0 + 16 * dt + li] = apre[dt];
     }
   }
 }
@@ -473,8 +534,11 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
     lg = lane >> 4;              \
   } while (0)
   const int64_t bh = blockIdx.x;
+  const int64_t seg = blockIdx.y;
   const int64_t T = a.T;
   const int64_t nchunks = (T + TC - 1) / TC;
+  const int64_t c_begin = seg * a.seg_chunks;
+  const int64_t c_end = min(nchunks, c_begin + a.seg_chunks);
   const int j0 = wv * (DV / 4);  // side 0
   const int d0 = wv * (DK / 4);  // side 1
   const uint16_t *qh = a.q + bh * T * DK;
@@ -490,8 +554,11 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
 #define G1(jt, it) Gs[(jt) * NI + (it)]
 #pragma unroll
   for (int x = 0; x < NG; ++x) Gs[x] = zero4();
-  if (a.dST) {
-    const float *src = a.dST + bh * DK * DV;
+  // the adjoint state at this segment's end: dS_T, or the reverse scan's
+  const float *gsrc = seg == a.P - 1 ? (a.dST ? a.dST + bh * DK * DV : nullptr)
+                                     : a.Gloc + ((seg + 1) * a.nh + bh) * DK * DV;
+  if (gsrc) {
+    const float *src = gsrc;
     if (side == 0) {
 #pragma unroll
       for (int dt = 0; dt < DK / 16; ++dt)
@@ -518,7 +585,7 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) carry[it][i] = 0.f;
 
-  for (int64_t ci = nchunks - 1; ci >= 0; --ci) {
+  for (int64_t ci = c_end - 1; ci >= c_begin; --ci) {
     const int64_t t0 = ci * TC;
     const int n = (int)min<int64_t>(TC, T - t0);
 
@@ -860,7 +927,7 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
   }
 
   FRESH_LANE();
-  if (a.dS0 && side == 0) {
+  if (a.dS0 && side == 0 && seg == 0) {
     float *dst = a.dS0 + bh * DK * DV;
 #pragma unroll
     for (int dt = 0; dt < DK / 16; ++dt)
@@ -875,24 +942,53 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
 #undef G1
 #undef FRESH_LANE
 
+// The adjoint state at each segment's end, right to left (the backward's
+// mirror of the forward's scan): G_end(P-1) = dS_T and
+// G_end(p - 1) = diag(A(p)) G_end(p) + G_loc(p), one thread per entry,
+// written over G_loc(p) once read.
+__global__ __launch_bounds__(256) void gla_grad_scan_kernel(const float *dST, float *Gloc,
+                                                            const float *Aq, int64_t nh,
+                                                            int64_t DK, int64_t DV, int64_t P) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= nh * DK * DV) return;
+  const int64_t bh = e / (DK * DV), d = (e / DV) % DK;
+  float g = dST ? dST[e] : 0.f;
+  for (int64_t p = P - 1; p >= 1; --p) {
+    float *slot = Gloc + p * nh * DK * DV + e;
+    g = Aq[(p * nh + bh) * DK + d] * g + *slot;
+    *slot = g;
+  }
+}
+
 template <int DK, int DV>
 hipError_t gla_bwd_impl(const GlaBwdArgs &args, hipStream_t stream) {
-  CLA_LAUNCH("gla_dq", (gla_dq_kernel<DK, DV>), dim3((unsigned)args.nh), dim3(NTHR), stream,
-             args);
+  const dim3 grid((unsigned)args.nh, (unsigned)args.P);
+  CLA_LAUNCH("gla_dq", (gla_dq_kernel<DK, DV>), grid, dim3(NTHR), stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  CLA_LAUNCH("gla_dkdv", (gla_dkdv_kernel<DK, DV>), dim3((unsigned)args.nh), dim3(BTHR), stream,
-             args);
+  if (args.P > 1) {
+    const int64_t n = args.nh * DK * DV;
+    CLA_LAUNCH("gla_grad_scan", gla_grad_scan_kernel, dim3((unsigned)((n + 255) / 256)),
+               dim3(256), stream, args.dST, args.Gloc, args.Aq, args.nh, (int64_t)DK, (int64_t)DV,
+               args.P);
+  }
+  CLA_LAUNCH("gla_dkdv", (gla_dkdv_kernel<DK, DV>), grid, dim3(BTHR), stream, args);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t gla_bwd_ws_bytes(int64_t nh, int64_t T, int64_t DK, int64_t DV) {
+  auto r256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const int64_t nchunks = (T + TC - 1) / TC;
-  const int64_t nseg = (nchunks + kSegChunks - 1) / kSegChunks;
-  const size_t r1 = ((size_t)nh * T * DK * sizeof(float) + 255) & ~(size_t)255;
-  return r1 + (size_t)nseg * nh * DK * DV * sizeof(float);
+  const int64_t nblk = (nchunks + kSegChunks - 1) / kSegChunks;
+  size_t b = r256((size_t)nh * T * DK * sizeof(float)) +
+             r256((size_t)nblk * nh * DK * DV * sizeof(float));
+  const GlaPlan p = plan_gla(nh, T);
+  if (p.P > 1)
+    b += gla_fwd_ws_bytes(nh, T, DK, DV) + r256((size_t)(p.P * nh * DK * DV) * sizeof(float)) +
+         r256((size_t)(p.P * nh * DK) * sizeof(float));
+  return b;
 }
 
 hipError_t gla_bwd_dispatch(const GlaBwdArgs &args, int DK, int DV, hipStream_t stream) {

@@ -51,12 +51,26 @@ struct GlaBwdArgs {
   float *dl;              // [nh, T, DK]
   float *dS0;             // [nh, DK, DV] or NULL
   float *r1;              // workspace [nh, T, DK]: q (.) dq (fp32, from the dQ pass)
-  float *Sseg;            // workspace [nseg, nh, DK, DV]: S at the end of each segment
+  float *Sseg;            // workspace [nblk, nh, DK, DV]: S at the end of each 16-chunk block
   int64_t nh, T;
+  int64_t P, seg_chunks;  // the plan (segments on separate workgroups)
+  // P > 1, workspace: the state each segment starts from (slot p - 1 for
+  // segment p, from the state pass and its scan); per segment p >= 1 its
+  // local adjoint state sum_t diag(A_t) q_t dO_t^T (A_t the decay from the
+  // segment's start) and total decay, from the dQ pass, which the reverse
+  // scan turns into the adjoint state at each segment's end (slot p + 1 for
+  // segment p; the last segment starts from dS_T)
+  const float *Sin;
+  float *Gloc, *Aq;
 };
 
-// Workspace of the backward: r1, then Sseg (each 256-byte aligned).
+// Workspace of the backward: r1, Sseg and, for P > 1, the state pass's
+// buffers (as the forward's), Gloc [P, nh, DK, DV] and Aq [P, nh, DK], each
+// 256-byte aligned.
 size_t gla_bwd_ws_bytes(int64_t nh, int64_t T, int64_t DK, int64_t DV);
+
+// The forward's state pass and scan alone (args.Sloc, args.Aseg filled).
+hipError_t gla_states_dispatch(const GlaFwdArgs &args, int DK, int DV, hipStream_t stream);
 
 hipError_t gla_bwd_dispatch(const GlaBwdArgs &args, int DK, int DV, hipStream_t stream);
 

@@ -286,8 +286,14 @@ int cla_gla_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
  *   dlog_decay: [B, H, T, DK] fp32, 16-byte aligned.
  *   dS0       : [B, H, DK, DV] fp32, or NULL (not written).
  *   workspace : cla_gla_workspace_bytes(..., backward = 1) bytes, 16-byte
- *               aligned (B*H*T*DK fp32 products q dq, plus one fp32 state per
- *               segment of 16 chunks per sequence-head).
+ *               aligned (B*H*T*DK fp32 products q dq, one fp32 state per
+ *               block of 16 chunks per sequence-head, and, when the sequence
+ *               is split into segments as in the forward, each segment's
+ *               starting state, local adjoint state and total decay).
+ * With the sequence split, the backward runs the forward's state pass and
+ * scan, its dQ pass per segment (also summing each segment's local adjoint
+ * state), a reverse scan of the adjoint state over the segments, and its
+ * dK/dV pass per segment.
  */
 int cla_gla_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                 const float *log_decay, const float *S0, const uint16_t *dO,

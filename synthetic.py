@@ -31,6 +31,8 @@ Workloads (sizes as used by the bench and the full-size tests):
 * ``gla_T4096``   -- one decay per key dimension, B=32, H=16, T=4096,
   dk=dv=128, q, k ~ N(0,1)/sqrt(128), v ~ N(0,1), log a[d] = logsigmoid(x)/16
   with x ~ N(0,1) per (token, dimension), S0 = none, dO ~ N(0,1).
+* ``gla_long_T98304`` -- the same draws at B=1, H=16, T=98304 (16
+  sequence-heads: the sequence is split into segments).
 """
 
 from __future__ import annotations
@@ -357,6 +359,10 @@ def _gla_train():
     return gla_inputs(32, 16, 4096, 128, 128, 1060, decay="logsigmoid")
 
 
+def _gla_long():
+    return gla_inputs(1, 16, 98304, 128, 128, 1061, decay="logsigmoid")
+
+
 WORKLOADS = {
     "scan_small": Workload("scan_small", "scan", dict(B=1, T=4096, D=64), _scan_small),
     "scan_large": Workload("scan_large", "scan", dict(B=8, T=16384, D=4096), _scan_large),
@@ -369,6 +375,8 @@ WORKLOADS["sscan_mamba"] = Workload("sscan_mamba", "sscan",
                                     dict(B=8, T=4096, D=5120, N=16), _sscan_mamba)
 WORKLOADS["gla_T4096"] = Workload("gla_T4096", "gla",
                                   dict(B=32, H=16, T=4096, DK=128, DV=128), _gla_train)
+WORKLOADS["gla_long_T98304"] = Workload("gla_long_T98304", "gla",
+                                        dict(B=1, H=16, T=98304, DK=128, DV=128), _gla_long)
 for _T in LONG_T:
     WORKLOADS[f"la_long_T{_T}"] = Workload(
         f"la_long_T{_T}", "chunk", dict(B=98304 // _T, H=16, T=_T, DK=128, DV=128),

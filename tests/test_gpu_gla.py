@@ -130,6 +130,10 @@ BWD_CASES = [
     (1, 1, 200, 128, 128, ("const", -5.0), True, True, 29),          # every block exact
     (1, 2, 700, 128, 128, ("logsigmoid", 1.0), True, False, 30),
     (1, 2, 130, 64, 128, ("const", 0.0), False, True, 31),           # no decay
+    # few sequence-heads, long sequences: split into segments of 16-chunk blocks
+    (1, 2, 16384, 128, 128, "logsigmoid", True, True, 32),            # 16 segments
+    (1, 1, 4200, 64, 64, ("uniform", -8.0, 0.0), True, True, 33),     # exact blocks, 5 segments
+    (2, 1, 2100, 128, 64, ("logsigmoid", 1.0), False, True, 34),      # ragged last segment
 ]
 
 
