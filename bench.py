@@ -461,14 +461,15 @@ def bench_sscan(args, torch, cla, wl, steps, warmup, cpu_channels=0):
     L = cla.lib()
     ck = torch.empty(int(L.cla_sscan_ckpt_bytes(B, T, D, N)) // 4, dtype=torch.float32,
                      device=dev)
-    wsb = int(L.cla_sscan_workspace_bytes(B, T, D, N, 1))
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    wsf = int(L.cla_sscan_workspace_bytes(B, T, D, N, 0, 0))
+    wsb = int(L.cla_sscan_workspace_bytes(B, T, D, N, 1, 1))
+    ws = torch.empty(max(wsf, wsb, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     P = lambda t: None if t is None else t.data_ptr()
 
     def fwd():
         st = L.cla_sscan_fwd(P(x), P(dl), P(A), P(Bm), P(Cm), P(h0), P(y), P(hT), P(ck),
-                             B, T, D, N, stream)
+                             B, T, D, N, P(ws), ws.numel(), stream)
         if st:
             raise RuntimeError(L.cla_status_string(st))
 
@@ -532,7 +533,7 @@ def bench_sscan(args, torch, cla, wl, steps, warmup, cpu_channels=0):
                      "path_algorithmic_bytes": path_bytes,
                      "path_roofline_frac": round(t_roof / (ms_step * 1e-3), 4),
                      "hbm_GBps_path": round(path_bytes / (ms_step * 1e-3) / 1e9, 1),
-                     "checkpoint_bytes": ck.numel() * 4, "workspace_bytes": wsb,
+                     "checkpoint_bytes": ck.numel() * 4, "workspace_bytes": [wsf, wsb],
                      "path": "cla_sscan_fwd (checkpoints) + cla_sscan_bwd"}}
     res["cpu_baseline"] = cpu_baseline_sscan(ci, cpu_channels) if cpu_channels else None
     del x, dl, A, Bm, Cm, dy, y, hT, dx, dd, dA, dB, dC, dh0, ck, ws
@@ -562,6 +563,7 @@ def cpu_baseline_sscan(ci, nch):
 
 CHUNK_EXTRAS = ("la_const", "la_gated") + tuple(f"la_long_T{t}" for t in syn.LONG_T)
 GLA_EXTRAS = ("gla_T4096", "gla_long_T98304")
+SSCAN_EXTRAS = ("sscan_mamba", "sscan_b1")
 
 
 def main():
@@ -609,15 +611,16 @@ def main():
                 log(f"[bench] {name}: {r['ms_per_step']:.3f} ms/step")
             longs = [chunk[f"la_long_T{t}"]["tokens_per_s"] for t in syn.LONG_T]
             res["extra"]["chunkwise"] = chunk
-            r = bench_sscan(args, torch, cla, syn.WORKLOADS["sscan_mamba"],
-                            max(3, args.steps // 2), args.warmup)
-            res["extra"]["selective_scan"] = {
-                "sscan_mamba": {"tokens_per_s": round(r["value"], 1),
-                                "ms_per_step": round(r["ms_per_step"], 4),
-                                "roofline": r["roofline"],
-                                "path_roofline_frac": r["extra"]["path_roofline_frac"],
-                                "kernels": {n: e["avg_ms"] for n, e in r["extra"]["kernels"].items()}}}
-            log(f"[bench] sscan_mamba: {r['ms_per_step']:.3f} ms/step")
+            for name in SSCAN_EXTRAS:
+                r = bench_sscan(args, torch, cla, syn.WORKLOADS[name], max(3, args.steps // 2),
+                                args.warmup)
+                res["extra"].setdefault("selective_scan", {})[name] = {
+                    "tokens_per_s": round(r["value"], 1),
+                    "ms_per_step": round(r["ms_per_step"], 4),
+                    "roofline": r["roofline"],
+                    "path_roofline_frac": r["extra"]["path_roofline_frac"],
+                    "kernels": {n: e["avg_ms"] for n, e in r["extra"]["kernels"].items()}}
+                log(f"[bench] {name}: {r['ms_per_step']:.3f} ms/step")
             for name in GLA_EXTRAS:
                 r = bench_gla(args, torch, cla, syn.WORKLOADS[name], max(3, args.steps // 2),
                               args.warmup)

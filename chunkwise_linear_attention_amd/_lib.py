@@ -52,8 +52,8 @@ SIGNATURES = {
     "cla_gla_fwd": ([p] * 7 + [i64] * 6 + [p, sz, p], ctypes.c_int),
     "cla_gla_bwd": ([p] * 12 + [i64] * 6 + [p, sz, p], ctypes.c_int),
     "cla_sscan_ckpt_bytes": ([i64] * 4, sz),
-    "cla_sscan_workspace_bytes": ([i64] * 4 + [ctypes.c_int], sz),
-    "cla_sscan_fwd": ([p] * 9 + [i64] * 4 + [p], ctypes.c_int),
+    "cla_sscan_workspace_bytes": ([i64] * 4 + [ctypes.c_int] * 2, sz),
+    "cla_sscan_fwd": ([p] * 9 + [i64] * 4 + [p, sz, p], ctypes.c_int),
     "cla_sscan_bwd": ([p] * 15 + [i64] * 4 + [p, sz, p], ctypes.c_int),
     "cla_timing_enable": ([ctypes.c_int], ctypes.c_int),
     "cla_timing_read": ([p, p, p, ctypes.c_int], ctypes.c_int),

@@ -271,8 +271,10 @@ def sscan_ckpt_bytes(B: int, T: int, D: int, N: int) -> int:
     return int(_lib.lib().cla_sscan_ckpt_bytes(B, T, D, N))
 
 
-def sscan_workspace_bytes(B: int, T: int, D: int, N: int, have_ckpt: bool = True) -> int:
-    return int(_lib.lib().cla_sscan_workspace_bytes(B, T, D, N, 1 if have_ckpt else 0))
+def sscan_workspace_bytes(B: int, T: int, D: int, N: int, backward: bool = True,
+                          have_ckpt: bool = True) -> int:
+    return int(_lib.lib().cla_sscan_workspace_bytes(B, T, D, N, 1 if backward else 0,
+                                                    1 if have_ckpt else 0))
 
 
 def selective_scan(x, delta, A, Bm, Cm, h0=None, *, want_final=True, save_ckpt=False):
@@ -296,8 +298,9 @@ def selective_scan(x, delta, A, Bm, Cm, h0=None, *, want_final=True, save_ckpt=F
     if save_ckpt:
         nb = int(L.cla_sscan_ckpt_bytes(B, T, D, N))
         ck = torch.empty(max(nb // 4, 1), dtype=torch.float32, device=dev)
+    ws, wsb = _workspace(int(L.cla_sscan_workspace_bytes(B, T, D, N, 0, 0)), dev)
     st = L.cla_sscan_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(h0), _ptr(y),
-                         _ptr(hT), _ptr(ck), B, T, D, N, _stream(dev))
+                         _ptr(hT), _ptr(ck), B, T, D, N, _ptr(ws), wsb, _stream(dev))
     _lib.check("cla_sscan_fwd", st)
     return (y, hT, ck) if save_ckpt else (y, hT)
 
@@ -325,7 +328,7 @@ def selective_scan_bwd(x, delta, A, Bm, Cm, h0, dy, dhT=None, *, ckpt=None, want
     dC = torch.empty((B, T, N), dtype=torch.float32, device=dev)
     dh0 = torch.empty((B, D, N), dtype=torch.float32, device=dev) if want_dh0 else None
     L = _lib.lib()
-    nbytes = int(L.cla_sscan_workspace_bytes(B, T, D, N, 0 if ckpt is None else 1))
+    nbytes = int(L.cla_sscan_workspace_bytes(B, T, D, N, 1, 0 if ckpt is None else 1))
     if workspace is None:
         ws, wsb = _workspace(nbytes, dev)
     else:

@@ -411,15 +411,18 @@ size_t cla_sscan_ckpt_bytes(int64_t B, int64_t T, int64_t D, int64_t N) {
   return cla::sscan::ckpt_bytes(B, T, D, N);
 }
 
-size_t cla_sscan_workspace_bytes(int64_t B, int64_t T, int64_t D, int64_t N, int have_ckpt) {
+size_t cla_sscan_workspace_bytes(int64_t B, int64_t T, int64_t D, int64_t N, int backward,
+                                 int have_ckpt) {
   if (!sscan_shape_ok(B, T, D, N) || !sscan_supported(B, D, N)) return 0;
   if (B == 0 || T == 0 || D == 0) return 0;
-  return cla::sscan::bwd_ws_bytes(B, T, D, N, !have_ckpt);
+  return backward ? cla::sscan::bwd_ws_bytes(B, T, D, N, !have_ckpt)
+                  : cla::sscan::fwd_ws_bytes(B, T, D, N);
 }
 
 int cla_sscan_fwd(const float *x, const float *delta, const float *A, const float *Bm,
                   const float *Cm, const float *h0, float *y, float *hT, float *ckpt, int64_t B,
-                  int64_t T, int64_t D, int64_t N, cla_stream_t stream) {
+                  int64_t T, int64_t D, int64_t N, void *workspace, size_t workspace_bytes,
+                  cla_stream_t stream) {
   if (!sscan_shape_ok(B, T, D, N)) return CLA_ERR_BAD_SHAPE;
   if (!sscan_supported(B, D, N)) return CLA_ERR_UNSUPPORTED;
   if (B == 0 || D == 0) return CLA_OK;
@@ -430,13 +433,25 @@ int cla_sscan_fwd(const float *x, const float *delta, const float *A, const floa
   if (!(aligned16(x) && aligned16(delta) && aligned16(Bm) && aligned16(Cm) && aligned16(y) &&
         aligned16(ckpt)))
     return CLA_ERR_UNSUPPORTED;
+  const cla::sscan::Plan plan = cla::sscan::plan(B, T, D);
+  if (plan.P > 65535) return CLA_ERR_UNSUPPORTED;
+  const size_t need = T > 0 ? cla::sscan::fwd_ws_bytes(B, T, D, N) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return CLA_ERR_WORKSPACE;
+  const Range ws{need ? workspace : nullptr, need};
   if (any_alias({{x, full}, {delta, full}, {A, an}, {Bm, bn}, {Cm, bn}, {h0, st}},
-                {{y, full}, {hT, st}, {ckpt, ck}}))
+                {{y, full}, {hT, st}, {ckpt, ck}, ws}))
     return CLA_ERR_ALIAS;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (T == 0)
     return hT ? hip_status(cla::launch_copy_or_zero(hT, h0, B * D * N, s)) : CLA_OK;
-  cla::sscan::FwdArgs a{x, delta, A, Bm, Cm, h0, y, hT, ckpt, B, T, D, N};
+  cla::sscan::FwdArgs a{x, delta, A, Bm, Cm, h0, y, hT, ckpt, B, T, D, N, plan.P,
+                        plan.seg_tiles, nullptr, nullptr};
+  if (plan.P > 1) {
+    a.Hloc = static_cast<float *>(workspace);
+    a.Aprod = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                        cla::sscan::fwd_ws_bytes(B, T, D, N) / 2);
+  }
   return hip_status(cla::sscan::fwd_dispatch(a, s));
 }
 
@@ -458,6 +473,8 @@ int cla_sscan_bwd(const float *x, const float *delta, const float *A, const floa
         aligned16(dx) && aligned16(ddelta) && aligned16(dB) && aligned16(dC) &&
         aligned16(ckpt)))
     return CLA_ERR_UNSUPPORTED;
+  const cla::sscan::Plan plan = cla::sscan::plan(B, T, D);
+  if (plan.P > 65535) return CLA_ERR_UNSUPPORTED;
   const size_t need = (B > 0 && T > 0) ? cla::sscan::bwd_ws_bytes(B, T, D, N, !ckpt) : 0;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return CLA_ERR_WORKSPACE;
@@ -472,21 +489,35 @@ int cla_sscan_bwd(const float *x, const float *delta, const float *A, const floa
     if (e == hipSuccess && dh0 && B > 0) e = cla::launch_copy_or_zero(dh0, dhT, B * D * N, s);
     return hip_status(e);
   }
+  const size_t bdn = (size_t)(B * D * N) * sizeof(float);
   char *w = static_cast<char *>(workspace);
   float *part = reinterpret_cast<float *>(w);
   w += cla::sscan::round256(cla::sscan::part_bytes(B, T, D, N));
   float *dAp = reinterpret_cast<float *>(w);
-  w += cla::sscan::round256((size_t)(B * D * N) * sizeof(float));
+  w += cla::sscan::round256(plan.P * bdn);
+  float *Gloc = nullptr, *Aprod = nullptr;
+  if (plan.P > 1) {
+    Gloc = reinterpret_cast<float *>(w);
+    w += cla::sscan::round256(plan.P * bdn);
+    Aprod = reinterpret_cast<float *>(w);
+    w += cla::sscan::round256(plan.P * bdn);
+  }
   if (!ckpt) {
     // no checkpoints from the forward: write them here first
     float *ck_ws = reinterpret_cast<float *>(w);
-    cla::sscan::FwdArgs f{x, delta, A, Bm, Cm, h0, nullptr, nullptr, ck_ws, B, T, D, N};
+    w += cla::sscan::round256(cla::sscan::ckpt_bytes(B, T, D, N));
+    cla::sscan::FwdArgs f{x, delta, A, Bm, Cm, h0, nullptr, nullptr, ck_ws, B, T, D, N, plan.P,
+                          plan.seg_tiles, nullptr, nullptr};
+    if (plan.P > 1) {
+      f.Hloc = reinterpret_cast<float *>(w);
+      f.Aprod = reinterpret_cast<float *>(w + cla::sscan::fwd_ws_bytes(B, T, D, N) / 2);
+    }
     const hipError_t e = cla::sscan::fwd_dispatch(f, s);
     if (e != hipSuccess) return hip_status(e);
     ckpt = ck_ws;
   }
   cla::sscan::BwdArgs a{x, delta, A, Bm, Cm, ckpt, dy, dhT, dx, ddelta, dA, dB, dC, dh0,
-                        part, dAp, B, T, D, N};
+                        part, dAp, B, T, D, N, plan.P, plan.seg_tiles, Gloc, Aprod};
   return hip_status(cla::sscan::bwd_dispatch(a, s));
 }
 

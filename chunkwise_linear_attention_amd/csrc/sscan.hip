@@ -106,7 +106,11 @@ __device__ __forceinline__ void store_rows(float *dst, int64_t ld, int nt, int d
   }
 }
 
-template <int NPT>
+// AGG = false: the forward over time segment blockIdx.z (from h0 or the
+// scanned state of the segments before it).  AGG = true: segment blockIdx.z
+// of the first P - 1 from a zero state, writing its local state and its
+// product of decays for the scan across segments.
+template <int NPT, bool AGG>
 __global__ __launch_bounds__(NTH) void sscan_fwd_kernel(FwdArgs a) {
   constexpr int N = 4 * NPT;
   __shared__ __attribute__((aligned(16))) float XS[TT * CH];
@@ -116,30 +120,51 @@ __global__ __launch_bounds__(NTH) void sscan_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) float CS[TT * N];
   const int tid = threadIdx.x;
   const int c = tid >> 2, q = tid & 3;
-  const int64_t b = blockIdx.y;
+  const int64_t b = blockIdx.y, seg = blockIdx.z;
   const int64_t T = a.T, D = a.D;
   const int d0 = (int)blockIdx.x * CH;
   const int d = d0 + c;
   const bool valid = d < D;
   const int dc = min(d, (int)D - 1);
   const int e0 = q * NPT;  // this lane's first entry
-  float A2[NPT], h[NPT];
+  const int64_t bdn = a.B * D * N;
+  // the state this segment starts from
+  const float *hsrc = AGG ? nullptr
+                          : seg == 0 ? (a.h0 ? a.h0 + (b * D + dc) * N + e0 : nullptr)
+                                     : a.Hloc + (seg - 1) * bdn + (b * D + dc) * N + e0;
+  float A2[NPT], h[NPT], ap[NPT];
 #pragma unroll
   for (int j = 0; j < NPT; ++j) {
     A2[j] = a.A[(int64_t)dc * N + e0 + j] * kLog2e;
-    h[j] = a.h0 ? a.h0[(b * D + dc) * N + e0 + j] : 0.f;
+    h[j] = hsrc ? hsrc[j] : 0.f;
+    ap[j] = 1.f;
   }
   const int64_t ntiles = num_tiles(T), nck = num_ckpts(T);
-  const bool save = a.ckpt && valid;
-  for (int64_t s = 0; s < ntiles; ++s) {
+  const int64_t s_begin = seg * a.seg_tiles, s_end = min(ntiles, s_begin + a.seg_tiles);
+  const bool save = !AGG && a.ckpt && valid;
+  for (int64_t s = s_begin; s < s_end; ++s) {
     const int64_t t0 = s * TT;
     const int nt = (int)min<int64_t>(TT, T - t0);
     dma_rows<TT, CH>(a.x + (b * T + t0) * D, D, nt, d0, (int)D - 4, XS, tid);
     dma_rows<TT, CH>(a.delta + (b * T + t0) * D, D, nt, d0, (int)D - 4, DS, tid);
     dma_rows<TT, N>(a.Bm + (b * T + t0) * N, N, nt, 0, N - 4, BS, tid);
-    dma_rows<TT, N>(a.Cm + (b * T + t0) * N, N, nt, 0, N - 4, CS, tid);
+    if (!AGG) dma_rows<TT, N>(a.Cm + (b * T + t0) * N, N, nt, 0, N - 4, CS, tid);
     __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
+    if (AGG) {
+      for (int t = 0; t < nt; ++t) {
+        const float dv = DS[t * CH + c];
+        const float dx = dv * XS[t * CH + c];
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) {
+          const float av = decay(dv, A2[j]);
+          h[j] = fmaf(av, h[j], dx * BS[t * N + e0 + j]);
+          ap[j] *= av;
+        }
+      }
+      lds_barrier();
+      continue;
+    }
     for (int th = 0; th < nt; th += kCkpt) {
       if (save) {
         // the state before step t0 + th, for the backward
@@ -164,9 +189,105 @@ __global__ __launch_bounds__(NTH) void sscan_fwd_kernel(FwdArgs a) {
     lds_barrier();
     if (a.y) store_rows<TT>(a.y + (b * T + t0) * D, D, nt, d0, D, YS, tid);
   }
-  if (a.hT && valid) {
+  if (AGG) {
+    if (valid) {
+#pragma unroll
+      for (int j = 0; j < NPT; ++j) {
+        a.Hloc[seg * bdn + (b * D + d) * N + e0 + j] = h[j];
+        a.Aprod[seg * bdn + (b * D + d) * N + e0 + j] = ap[j];
+      }
+    }
+  } else if (a.hT && valid && seg == a.P - 1) {
 #pragma unroll
     for (int j = 0; j < NPT; ++j) a.hT[(b * D + d) * N + e0 + j] = h[j];
+  }
+}
+
+// The state each time segment starts from (ZTF "Splitting one sequence
+// across devices", per (channel, entry)): H_in(0) = h0,
+// H_in(p) = Aprod(p-1) H_in(p-1) + Hloc(p-1), written over Hloc(p-1).
+__global__ __launch_bounds__(256) void sscan_fwd_scan_kernel(FwdArgs a) {
+  const int64_t bdn = a.B * a.D * a.N;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= bdn) return;
+  float h = a.h0 ? a.h0[e] : 0.f;
+  for (int64_t p = 1; p < a.P; ++p) {
+    const int64_t slot = (p - 1) * bdn + e;
+    h = a.Aprod[slot] * h + a.Hloc[slot];
+    a.Hloc[slot] = h;
+  }
+}
+
+// The adjoint each time segment starts from on its right, from its end back
+// over the later segments: X(P-1) = dhT, X(q-1) = Aprod(q) X(q) + Gloc(q),
+// written over Gloc(q).
+__global__ __launch_bounds__(256) void sscan_bwd_scan_kernel(BwdArgs a) {
+  const int64_t bdn = a.B * a.D * a.N;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= bdn) return;
+  float x = a.dhT ? a.dhT[e] : 0.f;
+  for (int64_t p = a.P - 1; p >= 1; --p) {
+    const int64_t slot = p * bdn + e;
+    x = a.Aprod[slot] * x + a.Gloc[slot];
+    a.Gloc[slot] = x;
+  }
+}
+
+// Time segment q = 1 + blockIdx.z, last step to first, from a zero adjoint:
+// the segment's own contribution to the adjoint at its first step, times that
+// step's decay (what it hands to the segment before it), and its product of
+// decays.  Only the decays, C and dy are needed, not the states.
+template <int NPT>
+__global__ __launch_bounds__(NTH) void sscan_bwd_agg_kernel(BwdArgs a) {
+  constexpr int N = 4 * NPT;
+  __shared__ __attribute__((aligned(16))) float DS[TT * CH];
+  __shared__ __attribute__((aligned(16))) float GS[TT * CH];
+  __shared__ __attribute__((aligned(16))) float CS[TT * N];
+  const int tid = threadIdx.x;
+  const int c = tid >> 2, q = tid & 3;
+  const int64_t b = blockIdx.y, seg = 1 + blockIdx.z;
+  const int64_t T = a.T, D = a.D;
+  const int d0 = (int)blockIdx.x * CH;
+  const int d = d0 + c;
+  const int dc = min(d, (int)D - 1);
+  const int e0 = q * NPT;
+  const int64_t bdn = a.B * D * N;
+  float A2[NPT], hb[NPT], an[NPT], ap[NPT];
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) {
+    A2[j] = a.A[(int64_t)dc * N + e0 + j] * kLog2e;
+    hb[j] = 0.f;
+    an[j] = 1.f;
+    ap[j] = 1.f;
+  }
+  const int64_t ntiles = num_tiles(T);
+  const int64_t s_begin = seg * a.seg_tiles, s_end = min(ntiles, s_begin + a.seg_tiles);
+  for (int64_t s = s_end - 1; s >= s_begin; --s) {
+    const int64_t t0 = s * TT;
+    const int nt = (int)min<int64_t>(TT, T - t0);
+    dma_rows<TT, CH>(a.delta + (b * T + t0) * D, D, nt, d0, (int)D - 4, DS, tid);
+    dma_rows<TT, CH>(a.dy + (b * T + t0) * D, D, nt, d0, (int)D - 4, GS, tid);
+    dma_rows<TT, N>(a.Cm + (b * T + t0) * N, N, nt, 0, N - 4, CS, tid);
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+    for (int t = nt - 1; t >= 0; --t) {
+      const float dv = DS[t * CH + c], gv = GS[t * CH + c];
+#pragma unroll
+      for (int j = 0; j < NPT; ++j) {
+        const float av = decay(dv, A2[j]);
+        hb[j] = fmaf(hb[j], an[j], CS[t * N + e0 + j] * gv);
+        an[j] = av;
+        ap[j] *= av;
+      }
+    }
+    lds_barrier();
+  }
+  if (d < D) {
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      a.Gloc[seg * bdn + (b * D + d) * N + e0 + j] = an[j] * hb[j];
+      a.Aprod[seg * bdn + (b * D + d) * N + e0 + j] = ap[j];
+    }
   }
 }
 
@@ -187,7 +308,7 @@ __global__ __launch_bounds__(NTH, 3) void sscan_bwd_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float PR[RS * 2 * N * PC];
   const int tid = threadIdx.x;
   const int c = tid >> 2, q = tid & 3;
-  const int64_t b = blockIdx.y;
+  const int64_t b = blockIdx.y, seg = blockIdx.z;
   const int64_t T = a.T, D = a.D;
   const int64_t G = num_groups(D);
   const int d0 = (int)blockIdx.x * CH;
@@ -200,12 +321,18 @@ __global__ __launch_bounds__(NTH, 3) void sscan_bwd_kernel(BwdArgs a) {
   for (int j = 0; j < NPT; ++j) {
     Av[j] = a.A[(int64_t)dc * N + e0 + j];
     A2[j] = Av[j] * kLog2e;
-    hbar[j] = a.dhT ? a.dhT[(b * D + dc) * N + e0 + j] : 0.f;
+    // the adjoint from the steps after this segment: dhT, or the scan's
+    const float *gsrc = seg == a.P - 1 ? (a.dhT ? a.dhT + (b * D + dc) * N : nullptr)
+                                       : a.Gloc + (seg + 1) * a.B * D * N + (b * D + dc) * N;
+    hbar[j] = gsrc ? gsrc[e0 + j] : 0.f;
     an[j] = 1.f;  // a_{t+1}; none after the last step
     dAacc[j] = 0.f;
   }
   const int64_t nck = num_ckpts(T);
-  for (int64_t s = nck - 1; s >= 0; --s) {
+  // this segment's 16-step tiles (its 32-step tiles, two each)
+  const int64_t s_begin = seg * a.seg_tiles * (TT / TB);
+  const int64_t s_end = min(nck, s_begin + a.seg_tiles * (TT / TB));
+  for (int64_t s = s_end - 1; s >= s_begin; --s) {
     const int64_t t0 = s * TB;
     const int nt = (int)min<int64_t>(TB, T - t0);
     float hs[TB][NPT];  // hs[t] = the state before step t of the tile
@@ -305,8 +432,8 @@ __global__ __launch_bounds__(NTH, 3) void sscan_bwd_kernel(BwdArgs a) {
   if (valid) {
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
-      a.dAp[(b * D + d) * N + e0 + j] = dAacc[j];
-      if (a.dh0) a.dh0[(b * D + d) * N + e0 + j] = an[j] * hbar[j];
+      a.dAp[seg * a.B * D * N + (b * D + d) * N + e0 + j] = dAacc[j];
+      if (a.dh0 && seg == 0) a.dh0[(b * D + d) * N + e0 + j] = an[j] * hbar[j];
     }
   }
 }
@@ -331,21 +458,37 @@ __global__ __launch_bounds__(256) void sscan_reduce_kernel(BwdArgs a) {
   } else if (i < nbt + D * N) {
     const int64_t k = i - nbt;
     float s = 0.f;
-    for (int64_t bb = 0; bb < B; ++bb) s += a.dAp[bb * D * N + k];
+    for (int64_t pb = 0; pb < a.P * B; ++pb) s += a.dAp[pb * D * N + k];
     a.dA[k] = s;
   }
 }
 
 template <int NPT>
 hipError_t fwd_impl(const FwdArgs &a, hipStream_t stream) {
-  const dim3 grid((unsigned)num_groups(a.D), (unsigned)a.B);
-  CLA_LAUNCH("sscan_fwd", sscan_fwd_kernel<NPT>, grid, dim3(NTH), stream, a);
+  const unsigned G = (unsigned)num_groups(a.D), Bu = (unsigned)a.B;
+  if (a.P > 1) {
+    CLA_LAUNCH("sscan_fwd_segments", (sscan_fwd_kernel<NPT, true>), dim3(G, Bu, (unsigned)(a.P - 1)),
+               dim3(NTH), stream, a);
+    const int64_t n = a.B * a.D * a.N;
+    CLA_LAUNCH("sscan_segment_scan", sscan_fwd_scan_kernel, dim3((unsigned)((n + 255) / 256)),
+               dim3(256), stream, a);
+  }
+  CLA_LAUNCH("sscan_fwd", (sscan_fwd_kernel<NPT, false>), dim3(G, Bu, (unsigned)a.P), dim3(NTH),
+             stream, a);
   return hipGetLastError();
 }
 
 template <int NPT>
 hipError_t bwd_impl(const BwdArgs &a, hipStream_t stream) {
-  const dim3 grid((unsigned)num_groups(a.D), (unsigned)a.B);
+  const unsigned G = (unsigned)num_groups(a.D), Bu = (unsigned)a.B;
+  if (a.P > 1) {
+    CLA_LAUNCH("sscan_bwd_segments", sscan_bwd_agg_kernel<NPT>, dim3(G, Bu, (unsigned)(a.P - 1)),
+               dim3(NTH), stream, a);
+    const int64_t n = a.B * a.D * a.N;
+    CLA_LAUNCH("sscan_grad_scan", sscan_bwd_scan_kernel, dim3((unsigned)((n + 255) / 256)),
+               dim3(256), stream, a);
+  }
+  const dim3 grid(G, Bu, (unsigned)a.P);
   CLA_LAUNCH("sscan_bwd", sscan_bwd_kernel<NPT>, grid, dim3(NTH), stream, a);
   const int64_t n = a.B * a.T * a.N + a.D * a.N;
   CLA_LAUNCH("sscan_reduce", sscan_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256),

@@ -323,13 +323,22 @@ int cla_gla_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
  *                 it (the page: Mamba recomputes its states in the backward).
  * Supported: N in {4, 8, 16}; D a multiple of 4 (at most 2^31 - 64);
  * B <= 65535 (CLA_ERR_UNSUPPORTED otherwise).  The [B, T, D, N] state tensor
- * is never written.  No workspace.
+ * is never written.
+ * When B * ceil(D / 64) alone gives fewer than 512 workgroups, time is cut
+ * into segments of whole 32-step tiles that run on separate workgroups: a
+ * first pass gives each segment's local state and product of decays, a scan
+ * over the segments the state each one starts from ("Splitting one sequence
+ * across devices", per channel and entry).  The workspace
+ * (cla_sscan_workspace_bytes(..., backward = 0, 0) bytes, 16-byte aligned)
+ * holds those states; it is 0 bytes, and workspace may be NULL, when time is
+ * not split.
  */
 size_t cla_sscan_ckpt_bytes(int64_t B, int64_t T, int64_t D, int64_t N);
 
 int cla_sscan_fwd(const float *x, const float *delta, const float *A, const float *Bm,
                   const float *Cm, const float *h0, float *y, float *hT, float *ckpt,
-                  int64_t B, int64_t T, int64_t D, int64_t N, cla_stream_t stream);
+                  int64_t B, int64_t T, int64_t D, int64_t N, void *workspace,
+                  size_t workspace_bytes, cla_stream_t stream);
 
 /*
  * Backward of cla_sscan_fwd ("Parallel scan", section "The backward pass is
@@ -341,12 +350,19 @@ int cla_sscan_fwd(const float *x, const float *delta, const float *A, const floa
  *   dy        : [B, T, D] gradient at y;  dhT : [B, D, N] or NULL.
  *   dx, ddelta: [B, T, D];  dA : [D, N] (summed over the batch);
  *   dB, dC    : [B, T, N] (summed over channels);  dh0 : [B, D, N] or NULL.
- *   workspace : cla_sscan_workspace_bytes(B, T, D, N, ckpt != NULL) bytes,
+ *   workspace : cla_sscan_workspace_bytes(B, T, D, N, 1, ckpt != NULL) bytes,
  *               16-byte aligned (per-workgroup partial sums for dB and dC,
- *               per-sequence dA, and the checkpoints when not given).
- * Sums run in a fixed order, so results are bit-identical from run to run.
+ *               dA per segment and sequence, when time is split each
+ *               segment's own adjoint and product of decays, and the
+ *               checkpoints and the forward's workspace when not given).
+ * With time split as in the forward, a first pass runs each later segment
+ * backwards from a zero adjoint (decays, C and dy only), a reverse scan gives
+ * the adjoint each segment receives from the steps after it, and the main
+ * pass runs per segment.  Sums run in a fixed order, so results are
+ * bit-identical from run to run.
  */
-size_t cla_sscan_workspace_bytes(int64_t B, int64_t T, int64_t D, int64_t N, int have_ckpt);
+size_t cla_sscan_workspace_bytes(int64_t B, int64_t T, int64_t D, int64_t N, int backward,
+                                 int have_ckpt);
 
 int cla_sscan_bwd(const float *x, const float *delta, const float *A, const float *Bm,
                   const float *Cm, const float *h0, const float *ckpt, const float *dy,

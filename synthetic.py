@@ -28,6 +28,8 @@ Workloads (sizes as used by the bench and the full-size tests):
   size of one Mamba-2.8B layer on 8 sequences: B=8, T=4096 (32,768 tokens),
   D=5120 channels, N=16; x, B, C, dy ~ N(0,1), delta log-uniform in
   [1e-3, 1e-1], A[d, n] = -(n + 1), no h0.
+* ``sscan_b1``    -- the same draws for one sequence of 32,768 tokens and
+  D=2048 channels (32 channel groups: time is split into segments).
 * ``gla_T4096``   -- one decay per key dimension, B=32, H=16, T=4096,
   dk=dv=128, q, k ~ N(0,1)/sqrt(128), v ~ N(0,1), log a[d] = logsigmoid(x)/16
   with x ~ N(0,1) per (token, dimension), S0 = none, dO ~ N(0,1).
@@ -355,6 +357,10 @@ def _sscan_mamba():
     return sscan_inputs(8, 4096, 5120, 16, 1070)
 
 
+def _sscan_b1():
+    return sscan_inputs(1, 32768, 2048, 16, 1071)
+
+
 def _gla_train():
     return gla_inputs(32, 16, 4096, 128, 128, 1060, decay="logsigmoid")
 
@@ -373,6 +379,8 @@ WORKLOADS = {
 }
 WORKLOADS["sscan_mamba"] = Workload("sscan_mamba", "sscan",
                                     dict(B=8, T=4096, D=5120, N=16), _sscan_mamba)
+WORKLOADS["sscan_b1"] = Workload("sscan_b1", "sscan",
+                                 dict(B=1, T=32768, D=2048, N=16), _sscan_b1)
 WORKLOADS["gla_T4096"] = Workload("gla_T4096", "gla",
                                   dict(B=32, H=16, T=4096, DK=128, DV=128), _gla_train)
 WORKLOADS["gla_long_T98304"] = Workload("gla_long_T98304", "gla",

@@ -180,27 +180,41 @@ def test_sscan_validation(lib):
     # checkpoints: the state before every 16th step
     assert ck(2, 100, 64, 16) == 2 * 7 * 64 * 16 * 4
     assert ck(1, 4, 64, 5) == 0 and ck(1, 4, 66, 16) == 0   # N or D unsupported
-    # backward workspace: per-workgroup dB/dC partials and per-sequence dA,
-    # plus the checkpoints when the forward's are not given
-    with_ck = ws(2, 100, 64, 16, 1)
-    without = ws(2, 100, 64, 16, 0)
-    assert with_ck >= 2 * 1 * 100 * 32 * 4 + 2 * 64 * 16 * 4
-    assert without >= with_ck + ck(2, 100, 64, 16)
-    assert ws(2, 0, 64, 16, 1) == 0
+    # enough (sequence, 64-channel group) units: no time split, no forward workspace
+    assert ws(8, 4096, 4096, 16, 0, 0) == 0
+    # few units: time is split (4 segments of one 32-step tile here), and the
+    # forward keeps each segment's state and decay product
+    bdn = 2 * 64 * 16 * 4
+    assert ws(2, 100, 64, 16, 0, 0) == 2 * 3 * bdn
+    # backward: per-workgroup dB/dC partials, dA per (segment, sequence), and
+    # each segment's adjoint and decay product, plus checkpoints and the
+    # forward's workspace when the forward's checkpoints are not given
+    with_ck = ws(2, 100, 64, 16, 1, 1)
+    assert with_ck == 2 * 1 * 100 * 32 * 4 + 4 * bdn + 2 * 4 * bdn
+    assert ws(2, 100, 64, 16, 1, 0) == with_ck + ck(2, 100, 64, 16) + 2 * 3 * bdn
+    assert ws(2, 0, 64, 16, 1, 1) == 0
     fw = lib.cla_sscan_fwd
-    shp = (2, 100, 64, 16)
-    assert fw(A, B_, C, D_, E, None, F, None, None, -1, 100, 64, 16, None) == SHAPE
-    assert fw(A, B_, C, D_, E, None, F, None, None, 2, 100, 64, 12, None) == UNSUP
-    assert fw(A, B_, C, D_, E, None, F, None, None, 2, 100, 62, 16, None) == UNSUP
-    assert fw(A + 4, B_, C, D_, E, None, F, None, None, *shp, None) == UNSUP  # misaligned x
+    shp = (8, 64, 4096, 16)  # no split
+    nows = (None, 0, None)
+    assert fw(A, B_, C, D_, E, None, F, None, None, -1, 64, 64, 16, *nows) == SHAPE
+    assert fw(A, B_, C, D_, E, None, F, None, None, 8, 64, 4096, 12, *nows) == UNSUP
+    assert fw(A, B_, C, D_, E, None, F, None, None, 8, 64, 4094, 16, *nows) == UNSUP
+    assert fw(A + 4, B_, C, D_, E, None, F, None, None, *shp, *nows) == UNSUP  # misaligned x
     for idx in (0, 1, 2, 3, 4, 6):
         a2 = [A, B_, C, D_, E, None, F, None, None]
         a2[idx] = None
-        assert fw(*a2, *shp, None) == NULL, idx
-    assert fw(A, B_, C, D_, E, None, A, None, None, *shp, None) == ALIAS        # y over x
-    assert fw(A, B_, C, D_, E, None, F, None, F + 64, *shp, None) == ALIAS      # ckpt over y
-    assert fw(None, None, C, None, None, None, None, None, None, 2, 0, 64, 16, None) == OK
+        assert fw(*a2, *shp, *nows) == NULL, idx
+    assert fw(A, B_, C, D_, E, None, A, None, None, *shp, *nows) == ALIAS        # y over x
+    assert fw(A, B_, C, D_, E, None, F, None, F + 64, *shp, *nows) == ALIAS      # ckpt over y
+    assert fw(None, None, C, None, None, None, None, None, None, 2, 0, 64, 16, *nows) == OK
+    # split: the workspace is required, and may not overlap an output
+    need = ws(2, 100, 64, 16, 0, 0)
+    assert fw(A, B_, C, D_, E, None, F, None, None, 2, 100, 64, 16, None, 0, None) == WS
+    assert fw(A, B_, C, D_, E, None, F, None, None, 2, 100, 64, 16, G, need - 16, None) == WS
+    assert fw(A, B_, C, D_, E, None, F, None, None, 2, 100, 64, 16, F, need, None) == ALIAS
     bw = lib.cla_sscan_bwd
+    shp = (2, 100, 64, 16)
+    without = ws(*shp, 1, 0)
     args = [A, B_, C, D_, E, None, None, F, None, G, H_, I, J, K, None]
     assert bw(*args, *shp, None, 0, None) == WS
     assert bw(*args, *shp, L, without - 16, None) == WS

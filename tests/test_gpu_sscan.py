@@ -7,7 +7,9 @@ ragged T (not a multiple of the 32-step tile), D not a multiple of the
 64-channel workgroup, N in {4, 8, 16}, strong and weak decays, no decay
 (A = 0), initial state and final-state gradient present or absent, T = 0,
 stitched pieces, the backward with and without the forward's checkpoints,
-bit-identical repeats, and the full-size workload on sampled channels.
+bit-identical repeats, and the full-size workload on sampled channels.  Every
+case with few (sequence, 64-channel group) units and T > 96 runs with time
+split into segments (up to 94 here); the large cases run unsplit.
 """
 
 import numpy as np
@@ -67,6 +69,12 @@ CASES = [
     (1, 300, 64, 16, ("loguniform", 1e-4, 1e-2), ("const", 0.0), True, True, 8),   # no decay
     (1, 77, 64, 16, ("loguniform", 0.5, 5.0), "s4d", True, True, 9),               # strong decays
     (4, 2048, 320, 16, ("loguniform", 1e-3, 1e-1), "s4d", False, False, 10),
+    # few (sequence, channel group) units: time split into segments of whole
+    # 32-step tiles (every case above with T > 96 is split as well)
+    (1, 3000, 64, 16, ("loguniform", 1e-3, 1e-1), ("uniform", -2.0, -0.1), True, True, 11),
+    (2, 1000, 64, 8, ("loguniform", 1e-2, 1.0), "s4d", True, True, 12),
+    # enough units: no split
+    (8, 200, 4096, 4, ("loguniform", 1e-3, 1e-1), "s4d", True, True, 13),
 ]
 
 
