@@ -20,8 +20,12 @@ step of the computation runs in the library's HIP kernels.
     # selective scan, N state entries per channel (fp32)
     y, hT, ckpt        = selective_scan(x, delta, A, Bm, Cm, h0=None, save_ckpt=True)
     dx, ddelta, dA, dB, dC, dh0 = selective_scan_bwd(x, delta, A, Bm, Cm, h0, dy, ckpt=ckpt)
+
+    # autograd: chunkwise_linear_attention_amd.autograd.{scan_fn,
+    # chunked_linear_attn_fn, gla_fn, selective_scan_fn}
 """
 
+from . import autograd  # noqa: F401
 from ._lib import ClaError, lib  # noqa: F401
 from .api import (  # noqa: F401
     chunked_linear_attn,
