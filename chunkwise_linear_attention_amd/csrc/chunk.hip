@@ -224,6 +224,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     const int fl = fresh(lane);
     const ChunkDecay dc = chunk_decay(fl < n ? LC[fl] : 0.f, fl);
     const float c_l = dc.c;
+    const float c2_l = c_l * kLog2e;  // base-2 cumulative log
     const float lam_l = dc.k == 0 ? expf(c_l) : 0.f;
     const float gam_l = lane < n && dc.k == dc.k_last ? expf(dc.c_last - c_l) : 0.f;
     const float alpha = dc.k_last == 0 ? expf(dc.c_last) : 0.f;
@@ -231,7 +232,13 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     {
       // ---- masked transposed score tiles -> P[r][s] (bf16) ----
       FRESH_LANE();
-      for (int t = w; t < 12; t += NWAVE) {
+      // A whole chunk without resets needs no mask below the diagonal tiles
+      // (s < r there); the decay factor is exp2 of a difference of base-2
+      // cumulative logs.
+      const bool plain = n == TC && !dc.any;
+#pragma unroll
+      for (int tt = 0; tt < 12 / NWAVE; ++tt) {
+        const int t = w + NWAVE * tt;
         const int rt = tile_rt(t), st = tile_st(t);
         const int r = 16 * rt + li;
         f32x4 acc = zero4();
@@ -242,17 +249,23 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
                        lds_frag<NCK>(QS, r, 4 * kk + lg), acc);
         }
         // acc[i] = (K Q^T)[s = 16 st + 4 lg + i][r]; keys past the chunk are masked
-        const float cr = __shfl(c_l, r, 64);
-        const int kr = dc.any ? __shfl(dc.k, r, 64) : 0;
+        const float cr = __shfl(c2_l, r, 64);
         bf16x4 pv;
+        if (plain && st < rt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = 16 * st + 4 * lg + i;
-          const float cs = __shfl(c_l, s, 64);
-          const bool sep = dc.any && __shfl(dc.k, s, 64) != kr;  // a reset in (s, r]
-          float p = 0.f;
-          if (s <= r && s < n && !sep) p = acc[i] * __expf(cr - cs);
-          pv[i] = tobf(p);
+          for (int i = 0; i < 4; ++i)
+            pv[i] = tobf(acc[i] * __builtin_amdgcn_exp2f(cr - __shfl(c2_l, 16 * st + 4 * lg + i, 64)));
+        } else {
+          const int kr = dc.any ? __shfl(dc.k, r, 64) : 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int s = 16 * st + 4 * lg + i;
+            const float cs = __shfl(c2_l, s, 64);
+            const bool sep = dc.any && __shfl(dc.k, s, 64) != kr;  // a reset in (s, r]
+            float p = 0.f;
+            if (s <= r && s < n && !sep) p = acc[i] * __builtin_amdgcn_exp2f(cr - cs);
+            pv[i] = tobf(p);
+          }
         }
         *reinterpret_cast<bf16x4 *>(PS + swz_off<8>(r, 2 * st + (lg >> 1)) + (lg & 1) * 8) = pv;
       }

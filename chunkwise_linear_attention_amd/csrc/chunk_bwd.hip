@@ -231,6 +231,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     // decay, and lambda = 0 so that they add nothing to the state gradient.
     const ChunkDecay dc = chunk_decay(lane < n ? LC[lane] : 0.f, lane);
     const float c_l = dc.c;
+    const float c2_l = c_l * kLog2e;  // base-2 cumulative log
     const float lam_l = lane < n && dc.k == 0 ? expf(c_l) : 0.f;
     const float gam_l = dc.k == dc.k_last ? expf(dc.c_last - c_l) : 0.f;
     const float alpha = dc.k_last == 0 ? expf(dc.c_last) : 0.f;
@@ -240,7 +241,13 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
       FRESH_LANE();
       {
         unsigned char *PT = side == 0 ? P1 : P2;
-        for (int t = wv; t < 12; t += 4) {
+        // A whole chunk without resets needs no mask below the diagonal
+        // tiles (r > s there); the decay factor is exp2 of a difference of
+        // base-2 cumulative logs.
+        const bool plain = n == TC && !dc.any;
+#pragma unroll
+        for (int tt = 0; tt < 3; ++tt) {
+          const int t = wv + 4 * tt;
           const int rt = tile_rt(t), st = tile_st(t);
           const int s = 16 * st + li;
           f32x4 acc = zero4();
@@ -258,17 +265,23 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
             }
           }
           // acc[i] = X[r = 16 rt + 4 lg + i][s]; rows past the chunk are masked
-          const float cs = __shfl(c_l, s, 64);
-          const int ks = dc.any ? __shfl(dc.k, s, 64) : 0;
+          const float cs = __shfl(c2_l, s, 64);
           bf16x4 pv;
+          if (plain && rt > st) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * rt + 4 * lg + i;
-            float p = 0.f;
-            const float cr = __shfl(c_l, r, 64);
-            const bool sep = dc.any && __shfl(dc.k, r, 64) != ks;  // a reset in (s, r]
-            if (r >= s && r < n && !sep) p = acc[i] * __expf(cr - cs);
-            pv[i] = tobf(p);
+            for (int i = 0; i < 4; ++i)
+              pv[i] = tobf(acc[i] * __builtin_amdgcn_exp2f(__shfl(c2_l, 16 * rt + 4 * lg + i, 64) - cs));
+          } else {
+            const int ks = dc.any ? __shfl(dc.k, s, 64) : 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 16 * rt + 4 * lg + i;
+              float p = 0.f;
+              const float cr = __shfl(c2_l, r, 64);
+              const bool sep = dc.any && __shfl(dc.k, r, 64) != ks;  // a reset in (s, r]
+              if (r >= s && r < n && !sep) p = acc[i] * __builtin_amdgcn_exp2f(cr - cs);
+              pv[i] = tobf(p);
+            }
           }
           *reinterpret_cast<bf16x4 *>(PT + swz_off<8>(s, 2 * rt + (lg >> 1)) + (lg & 1) * 8) = pv;
         }

@@ -47,6 +47,9 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
 // fp32 -> bf16, round to nearest even (hardware conversion on gfx950)
 __device__ __forceinline__ __bf16 tobf(float x) { return (__bf16)x; }
 
+// log2(e) in fp32: exp(x) = exp2(x * kLog2e)
+constexpr float kLog2e = 1.44269504088896341f;
+
 __device__ __forceinline__ float tof(__bf16 x) { return (float)x; }
 
 __device__ __forceinline__ bf16x8 cvt8(const float (&x)[8]) {
