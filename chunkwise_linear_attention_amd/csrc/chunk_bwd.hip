@@ -49,15 +49,15 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
   constexpr int NI = DK / 64;   // dK side: 16-col tiles of G^T per wave
   constexpr int NCK = DK / 8, NCV = DV / 8;
   constexpr int RK = 64 * DK * 2, RV = 64 * DV * 2;  // row-major tile bytes
-  // Two staging buffers, each [Q | dO | K | V | l]:
+  // Two staging buffers, each [Q | dO | K | V] (the log decays go to
+  // registers):
   // the next chunk streams into one by DMA while the other is being used.
   // They are separate arrays so that the compiler can tell the DMA target
   // from the buffer being read and does not wait for the DMA before reads.
   constexpr int B_DOS = RK;
   constexpr int B_KS = B_DOS + RV;
   constexpr int B_VS = B_KS + RK;
-  constexpr int B_L = B_VS + RV;
-  constexpr int BUF = B_L + 64 * 4;
+  constexpr int BUF = B_VS + RV;
   // 1 KB DMA blocks per chunk
   constexpr int NBQ = DK / 8, NBD = DV / 8;
   constexpr int NBK = DK / 8, NBV = DV / 8;
@@ -67,7 +67,19 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
   // P1[s][r] = D_rs (q_r . k_s), P2[s][r] = D_rs (dO_r . v_s)
   __shared__ __attribute__((aligned(1024))) unsigned char P1[64 * 128];
   __shared__ __attribute__((aligned(1024))) unsigned char P2[64 * 128];
-  __shared__ float R2P[4 * 64];
+  // The per-wave k.dk partials of a chunk, R2P[u][s] (u = dK-side wave),
+  // live in score-tile pieces that no tile uses: rows s >= 32 of P2, logical
+  // pieces 0-3 (the tiles (r, s) with r < 32 <= s are structurally zero and
+  // neither written nor read).  With the decays in registers this keeps
+  // DK = DV = 64 at 80 KB of LDS, two workgroups per CU.
+  auto r2p_at = [&](int u, int s_) __attribute__((always_inline)) -> float * {
+    const int idx = u * 64 + s_;  // 0..255: 16-byte piece idx / 4, word idx % 4
+    const int q = idx >> 2;
+    return reinterpret_cast<float *>(P2 + swz_off<8>(32 + (q >> 2), q & 3) + 4 * (idx & 3));
+  };
+  auto r2p_sum = [&](int s_) __attribute__((always_inline)) -> float {
+    return *r2p_at(0, s_) + *r2p_at(1, s_) + *r2p_at(2, s_) + *r2p_at(3, s_);
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -173,7 +185,8 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
-    __shared__ double bred[8];
+    // (P1 holds no score tile before the chunk loop)
+    double *bred = reinterpret_cast<double *>(P1);
     if (lane == 0) bred[w] = part;
     __syncthreads();
     if (tid == 0) {
@@ -182,11 +195,13 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
       a.Bnd[seg * a.nh + bh] = (float)b;
     }
   }
-  int64_t r2_t0 = -1;  // chunk whose k.dk partials sit in R2P
+  int64_t r2_t0 = -1;  // chunk whose k.dk partials sit in the P2 spare pieces
   int r2_n = 0;
 
   // DMA of chunk cj into a staging buffer: 1 KB row blocks spread over the
-  // waves, the 64 log decays (rows clamped to the chunk) by wave 0.
+  // waves; every wave loads the chunk's log decays, one per lane, into a
+  // register for the step that computes the chunk.
+  float l_next = 0.f;
   auto stage = [&](int64_t cj, unsigned char *buf) __attribute__((always_inline)) {
     const int64_t tj = cj * TC;
     const int nj = (int)min<int64_t>(TC, T - tj);
@@ -201,9 +216,9 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
         dma_block<DV>(vh + tj * DV, nj, buf + B_VS, b - NBQ - NBD - NBK, lane);
       }
     }
-    if (w == 0)
-      __builtin_amdgcn_global_load_lds(lh + tj + min(lane, nj - 1), (lds_void *)(buf + B_L), 4, 0,
-                                       0);
+    // this lane's log decay, used when the chunk is computed (rows past the
+    // chunk read l = 0 there)
+    l_next = lane < nj ? lh[tj + lane] : 0.f;
   };
 
   // One chunk from staging buffer `cur`, while the chunk before it streams
@@ -216,7 +231,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     unsigned char *DOS = cur + B_DOS;
     unsigned char *KS = cur + B_KS;
     unsigned char *VS = cur + B_VS;
-    const float *LC = reinterpret_cast<const float *>(cur + B_L);
+    const float l_cur = l_next;
 
     if (ci > c_begin) stage(ci - 1, nxt);
     // the previous chunk's k.dk sums, stored at the end of this step (a store
@@ -225,11 +240,11 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     const int64_t r2_row = r2_t0;
     const int r2_prev_n = r2_n;
     if (r2_t0 >= 0 && tid < r2_n)
-      r2_sum = R2P[tid] + R2P[64 + tid] + R2P[128 + tid] + R2P[192 + tid];
+      r2_sum = r2p_sum(tid);
     // In-chunk decays, one token per lane, computed by every wave (lanes
     // are then read with cross-lane shuffles).  Rows past the chunk: no
     // decay, and lambda = 0 so that they add nothing to the state gradient.
-    const ChunkDecay dc = chunk_decay(lane < n ? LC[lane] : 0.f, lane);
+    const ChunkDecay dc = chunk_decay(l_cur, lane);
     const float c_l = dc.c;
     const float c2_l = c_l * kLog2e;  // base-2 cumulative log
     const float lam_l = lane < n && dc.k == 0 ? expf(c_l) : 0.f;
@@ -245,7 +260,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
         // tiles (r > s there); the decay factor is exp2 of a difference of
         // base-2 cumulative logs.
         const bool plain = n == TC && !dc.any;
-#pragma unroll
+#pragma unroll 1
         for (int tt = 0; tt < 3; ++tt) {
           const int t = wv + 4 * tt;
           const int rt = tile_rt(t), st = tile_st(t);
@@ -382,7 +397,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
           }
           r2p += __shfl_xor(r2p, 16, 64);
           r2p += __shfl_xor(r2p, 32, 64);
-          if (lg == 0) R2P[wv * 64 + s] = r2p;
+          if (lg == 0) *r2p_at(wv, s) = r2p;
         }
       }
     }
@@ -456,7 +471,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     if (ci - 1 >= c_begin) step(ci - 1, buf1, buf0);
   }
   if (r2_t0 >= 0 && tid < r2_n)
-    a.r2[bh * T + r2_t0 + tid] = R2P[tid] + R2P[64 + tid] + R2P[128 + tid] + R2P[192 + tid];
+    a.r2[bh * T + r2_t0 + tid] = r2p_sum(tid);
 
   // ---- segment outputs ----
   if (seg == 0 && a.dS0 && side == 0) {
