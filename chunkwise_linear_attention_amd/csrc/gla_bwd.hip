@@ -182,10 +182,19 @@ __device__ __forceinline__ bool block_bad(const float *CS, int R, int lane) {
 // dQ pass
 // ===========================================================================
 
+// One wave per 16 key dimensions (DK = 128: 8 waves, two per SIMD, which
+// hides the latency of each phase better than one wave per SIMD).
+template <int DK>
+constexpr int dq_threads() {
+  return 4 * DK;
+}
+
 template <int DK, int DV>
-__global__ __launch_bounds__(NTHR, 1) void gla_dq_kernel(GlaBwdArgs a) {
+__global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs a) {
   constexpr int NCK = DK / 8, NCV = DV / 8;
-  constexpr int NDT = DK / 64;  // 16-column d tiles per wave
+  constexpr int NT = dq_threads<DK>(), NW = NT / 64;
+  constexpr int NDT = DK / (16 * NW);  // 16-column d tiles per wave
+  static_assert(NDT == 1, "one d tile per wave");
   constexpr int NJT = DV / 16;  // 16-row j tiles of S^T
   constexpr int B_KS = 64 * DK * 2, B_QH = 2 * B_KS, B_KH = 3 * B_KS, B_VS = 4 * B_KS;
   constexpr int B_DO = B_VS + 64 * DV * 2, B_CS = B_DO + 64 * DV * 2;
@@ -224,7 +233,7 @@ __global__ __launch_bounds__(NTHR, 1) void gla_dq_kernel(GlaBwdArgs a) {
   const int64_t nchunks = (T + TC - 1) / TC;
   const int64_t c_begin = seg * a.seg_chunks;
   const int64_t c_end = min(nchunks, c_begin + a.seg_chunks);
-  const int d0 = w * (DK / 4);
+  const int d0 = w * (DK / NW);
   const uint16_t *qh = a.q + bh * T * DK;
   const uint16_t *kh = a.k + bh * T * DK;
   const uint16_t *vh = a.v + bh * T * DV;
@@ -266,7 +275,7 @@ __global__ __launch_bounds__(NTHR, 1) void gla_dq_kernel(GlaBwdArgs a) {
 
     lds_barrier();
     FRESH_LANE();
-    for (int b = w; b < NBLK; b += NWAVE) {
+    for (int b = w; b < NBLK; b += NW) {
       if (b < NBQ)
         dma_block<DK>(qh + t0 * DK, n, QS, b, lane);
       else if (b < 2 * NBQ)
@@ -281,15 +290,15 @@ __global__ __launch_bounds__(NTHR, 1) void gla_dq_kernel(GlaBwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
     FRESH_LANE();
-    cumsum_rows<DK, NTHR>(CS, n, tid);
+    cumsum_rows<DK, NT>(CS, n, tid);
     FRESH_LANE();
-    prep_scaled<DK, NTHR>(QS, KS, QH, KH, CS, FQ, FK, AL, n, tid);
-    block_factors<DK, NTHR>(CS, FT, tid);
+    prep_scaled<DK, NT>(QS, KS, QH, KH, CS, FQ, FK, AL, n, tid);
+    block_factors<DK, NT>(CS, FT, tid);
 
     // ---- B[r][s] = dO_r . v_s (masked), stored [r][s]; the 32-column steps
     // read up to the diagonal also cover tiles (0,1) and (2,3): zeros ----
     FRESH_LANE();
-    for (int t = w; t < 12; t += NWAVE) {
+    for (int t = w; t < 12; t += NW) {
       const int R = tile_rt(t), S = tile_st(t);
       f32x4 acc = zero4();
       if (S <= R) {
@@ -963,7 +972,7 @@ __global__ __launch_bounds__(256) void gla_grad_scan_kernel(const float *dST, fl
 template <int DK, int DV>
 hipError_t gla_bwd_impl(const GlaBwdArgs &args, hipStream_t stream) {
   const dim3 grid((unsigned)args.nh, (unsigned)args.P);
-  CLA_LAUNCH("gla_dq", (gla_dq_kernel<DK, DV>), grid, dim3(NTHR), stream, args);
+  CLA_LAUNCH("gla_dq", (gla_dq_kernel<DK, DV>), grid, dim3(dq_threads<DK>()), stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (args.P > 1) {
