@@ -154,7 +154,14 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(ScanArgs p) {
   const int s = lane >> 4;
   const int slot = w * 4 + s;
 
-  const int64_t g = blockIdx.x;
+  // Workgroups are dispatched to the 8 XCDs round-robin by their linear id.
+  // Give each XCD a contiguous range of channel groups (at 8 batch rows of 64
+  // groups: one batch row per XCD), so that the rows an XCD streams at a time
+  // step are one contiguous span (scan_large: forward 1.27 -> 1.19 ms,
+  // backward 2.05 -> 2.01 ms against the plain order).
+  const int64_t ng = gridDim.x;
+  const int64_t g = ng % 8 == 0 ? (int64_t)(blockIdx.x % 8) * (ng / 8) + blockIdx.x / 8
+                                : (int64_t)blockIdx.x;
   const int64_t seg = blockIdx.y;
   const int64_t bb = g / p.groups_per_batch;
   const int64_t c = (g % p.groups_per_batch) * CG + cq * VEC;
