@@ -56,6 +56,12 @@ namespace {
 #ifndef CLA_SCAN_NT
 #define CLA_SCAN_NT 1
 #endif
+#ifndef CLA_SCAN_NT_LD
+#define CLA_SCAN_NT_LD CLA_SCAN_NT
+#endif
+#ifndef CLA_SCAN_NT_ST
+#define CLA_SCAN_NT_ST CLA_SCAN_NT
+#endif
 #ifndef CLA_SCAN_TARGET_GROUPS
 #define CLA_SCAN_TARGET_GROUPS 512
 #endif
@@ -79,7 +85,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 template <int VEC>
 __device__ __forceinline__ void ldv(const float *p, float (&x)[VEC]) {
   if constexpr (VEC == 4) {
-#if CLA_SCAN_NT
+#if CLA_SCAN_NT_LD
     const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
 #else
     const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
@@ -89,7 +95,7 @@ __device__ __forceinline__ void ldv(const float *p, float (&x)[VEC]) {
     x[2] = v.z;
     x[3] = v.w;
   } else {
-#if CLA_SCAN_NT
+#if CLA_SCAN_NT_LD
     x[0] = __builtin_nontemporal_load(p);
 #else
     x[0] = *p;
@@ -101,13 +107,13 @@ template <int VEC>
 __device__ __forceinline__ void stv(float *p, const float (&x)[VEC]) {
   if constexpr (VEC == 4) {
     const f32x4 v = {x[0], x[1], x[2], x[3]};
-#if CLA_SCAN_NT
+#if CLA_SCAN_NT_ST
     __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
 #else
     *reinterpret_cast<f32x4 *>(p) = v;
 #endif
   } else {
-#if CLA_SCAN_NT
+#if CLA_SCAN_NT_ST
     __builtin_nontemporal_store(x[0], p);
 #else
     *p = x[0];
