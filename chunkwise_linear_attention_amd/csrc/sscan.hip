@@ -110,6 +110,16 @@ __device__ __forceinline__ void store_rows(float *dst, int64_t ld, int nt, int d
 // scanned state of the segments before it).  AGG = true: segment blockIdx.z
 // of the first P - 1 from a zero state, writing its local state and its
 // product of decays for the scan across segments.
+// The channel group of this workgroup.  Workgroups are dispatched to the 8
+// XCDs round-robin by linear id (x fastest); with a multiple of 8 groups this
+// gives each XCD a contiguous range of channel groups, so that the rows an
+// XCD streams at a time step are one contiguous span (results are the same
+// for any order).
+__device__ __forceinline__ int xcd_group() {
+  const unsigned G = gridDim.x;
+  return G % 8 == 0 ? (int)((blockIdx.x % 8) * (G / 8) + blockIdx.x / 8) : (int)blockIdx.x;
+}
+
 template <int NPT, bool AGG>
 __global__ __launch_bounds__(NTH) void sscan_fwd_kernel(FwdArgs a) {
   constexpr int N = 4 * NPT;
@@ -122,7 +132,8 @@ __global__ __launch_bounds__(NTH) void sscan_fwd_kernel(FwdArgs a) {
   const int c = tid >> 2, q = tid & 3;
   const int64_t b = blockIdx.y, seg = blockIdx.z;
   const int64_t T = a.T, D = a.D;
-  const int d0 = (int)blockIdx.x * CH;
+  const int gx = xcd_group();
+  const int d0 = gx * CH;
   const int d = d0 + c;
   const bool valid = d < D;
   const int dc = min(d, (int)D - 1);
@@ -247,7 +258,8 @@ __global__ __launch_bounds__(NTH) void sscan_bwd_agg_kernel(BwdArgs a) {
   const int c = tid >> 2, q = tid & 3;
   const int64_t b = blockIdx.y, seg = 1 + blockIdx.z;
   const int64_t T = a.T, D = a.D;
-  const int d0 = (int)blockIdx.x * CH;
+  const int gx = xcd_group();
+  const int d0 = gx * CH;
   const int d = d0 + c;
   const int dc = min(d, (int)D - 1);
   const int e0 = q * NPT;
@@ -311,7 +323,8 @@ __global__ __launch_bounds__(NTH, 3) void sscan_bwd_kernel(BwdArgs a) {
   const int64_t b = blockIdx.y, seg = blockIdx.z;
   const int64_t T = a.T, D = a.D;
   const int64_t G = num_groups(D);
-  const int d0 = (int)blockIdx.x * CH;
+  const int gx = xcd_group();
+  const int d0 = gx * CH;
   const int d = d0 + c;
   const bool valid = d < D;
   const int dc = min(d, (int)D - 1);
@@ -420,7 +433,7 @@ __global__ __launch_bounds__(NTH, 3) void sscan_bwd_kernel(BwdArgs a) {
             const float4 v3 = *reinterpret_cast<const float4 *>(pr + 12);
             const float sum = (((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w))) +
                               (((v2.x + v2.y) + (v2.z + v2.w)) + ((v3.x + v3.y) + (v3.z + v3.w)));
-            a.part[((b * G + blockIdx.x) * T + t0 + t + tt) * 2 * N + row] = sum;
+            a.part[((b * G + gx) * T + t0 + t + tt) * 2 * N + row] = sum;
           }
         }
         lds_barrier();
