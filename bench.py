@@ -323,7 +323,9 @@ def cpu_baseline_chunk(ci, nheads):
 
 
 def bench_gla(args, torch, cla, wl, steps, warmup, cpu_heads=0):
-    """One decay per key dimension: cla_gla_fwd + cla_gla_bwd per step."""
+    """One decay per key dimension: cla_gla_fwd_saved + cla_gla_bwd_saved per
+    step (the training path: the backward starts its segments from the
+    forward's saved states; bit-identical to the plain calls)."""
     from chunkwise_linear_attention_amd import _lib
     dev = torch.device("cuda:0")
     t0 = time.time()
@@ -348,18 +350,21 @@ def bench_gla(args, torch, cla, wl, steps, warmup, cpu_heads=0):
     wsf = int(L.cla_gla_workspace_bytes(B, H, T, DK, DV, 64, 0))
     wsb = int(L.cla_gla_workspace_bytes(B, H, T, DK, DV, 64, 1))
     ws = torch.empty(max(wsf, wsb, 1), dtype=torch.uint8, device=dev)
+    svb = int(L.cla_gla_saved_bytes(B, H, T, DK, DV, 64))
+    saved = torch.empty(max(svb, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     P = lambda t: None if t is None else t.data_ptr()
 
     def fwd():
-        st = L.cla_gla_fwd(P(q), P(k), P(v), P(l), P(S0), P(o), P(ST), B, H, T, DK, DV, 64,
-                           P(ws), ws.numel(), stream)
+        st = L.cla_gla_fwd_saved(P(q), P(k), P(v), P(l), P(S0), P(o), P(ST), P(saved),
+                                 saved.numel(), B, H, T, DK, DV, 64, P(ws), ws.numel(), stream)
         if st:
             raise RuntimeError(L.cla_status_string(st))
 
     def bwd():
-        st = L.cla_gla_bwd(P(q), P(k), P(v), P(l), P(S0), P(dO), P(dST), P(dq), P(dk), P(dv),
-                           P(dl), P(dS0), B, H, T, DK, DV, 64, P(ws), ws.numel(), stream)
+        st = L.cla_gla_bwd_saved(P(q), P(k), P(v), P(l), P(S0), P(dO), P(dST), P(saved),
+                                 saved.numel(), P(dq), P(dk), P(dv), P(dl), P(dS0), B, H, T, DK,
+                                 DV, 64, P(ws), ws.numel(), stream)
         if st:
             raise RuntimeError(L.cla_status_string(st))
 
@@ -414,9 +419,10 @@ def bench_gla(args, torch, cla, wl, steps, warmup, cpu_heads=0):
                      "path_roofline_frac": round(t_roof / (ms_step * 1e-3), 4),
                      "mfma_util": round(path_flops / (ms_step * 1e-3) / (pm.PEAK_BF16_TFLOPS * 1e12), 4),
                      "hbm_GBps_path": round(path_bytes / (ms_step * 1e-3) / 1e9, 1),
-                     "workspace_bytes": [wsf, wsb], "path": "cla_gla_fwd + cla_gla_bwd"}}
+                     "workspace_bytes": [wsf, wsb], "saved_bytes": svb,
+                     "path": "cla_gla_fwd_saved + cla_gla_bwd_saved"}}
     res["cpu_baseline"] = cpu_baseline_gla(ci, cpu_heads) if cpu_heads else None
-    del q, k, v, l, S0, dO, dST, o, ST, dq, dk, dv, dl, dS0, ws
+    del q, k, v, l, S0, dO, dST, o, ST, dq, dk, dv, dl, dS0, ws, saved
     torch.cuda.empty_cache()
     return res
 

@@ -37,6 +37,7 @@ from .api import (  # noqa: F401
     chunk_saved_bytes,
     gla,
     gla_bwd,
+    gla_saved_bytes,
     gla_workspace_bytes,
     selective_scan,
     selective_scan_bwd,
@@ -45,6 +46,6 @@ from .api import (  # noqa: F401
 )
 
 __all__ = ["scan", "scan_bwd", "chunked_linear_attn", "chunked_linear_attn_bwd",
-           "scan_workspace_bytes", "chunk_workspace_bytes", "chunk_saved_bytes", "gla", "gla_bwd",
+           "scan_workspace_bytes", "chunk_workspace_bytes", "chunk_saved_bytes", "gla", "gla_bwd", "gla_saved_bytes",
            "gla_workspace_bytes", "selective_scan", "selective_scan_bwd", "sscan_ckpt_bytes",
            "sscan_workspace_bytes", "ClaError"]

@@ -51,6 +51,9 @@ SIGNATURES = {
     "cla_gla_workspace_bytes": ([i64, i64, i64, i64, i64, i64, ctypes.c_int], sz),
     "cla_gla_fwd": ([p] * 7 + [i64] * 6 + [p, sz, p], ctypes.c_int),
     "cla_gla_bwd": ([p] * 12 + [i64] * 6 + [p, sz, p], ctypes.c_int),
+    "cla_gla_saved_bytes": ([i64] * 6, sz),
+    "cla_gla_fwd_saved": ([p] * 8 + [sz] + [i64] * 6 + [p, sz, p], ctypes.c_int),
+    "cla_gla_bwd_saved": ([p] * 8 + [sz] + [p] * 5 + [i64] * 6 + [p, sz, p], ctypes.c_int),
     "cla_sscan_ckpt_bytes": ([i64] * 4, sz),
     "cla_sscan_workspace_bytes": ([i64] * 4 + [ctypes.c_int] * 2, sz),
     "cla_sscan_fwd": ([p] * 9 + [i64] * 4 + [p, sz, p], ctypes.c_int),

@@ -204,11 +204,18 @@ def gla_workspace_bytes(B, H, T, DK, DV, backward=False, chunk=CHUNK) -> int:
     return int(_lib.lib().cla_gla_workspace_bytes(B, H, T, DK, DV, chunk, int(backward)))
 
 
-def gla(q, k, v, log_decay, S0=None, *, want_final=True, chunk=CHUNK, workspace=None):
+def gla_saved_bytes(B, H, T, DK, DV, chunk=CHUNK) -> int:
+    return int(_lib.lib().cla_gla_saved_bytes(B, H, T, DK, DV, chunk))
+
+
+def gla(q, k, v, log_decay, S0=None, *, want_final=True, chunk=CHUNK, workspace=None,
+        save_states=False):
     """S_t = diag(exp(l_t)) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t, chunkwise, with
     one log decay per key dimension.  q, k: [B, H, T, DK] bf16; v: [B, H, T, DV]
     bf16; log_decay: [B, H, T, DK] fp32; S0: [B, H, DK, DV] fp32 or None.
-    Returns (o bf16, S_T fp32 or None)."""
+    Returns (o bf16, S_T fp32 or None), and with save_states=True also the
+    saved segment start states for ``gla_bwd(..., saved=...)``
+    (cla_gla_fwd_saved)."""
     B, H, T, DK = q.shape
     DV = v.shape[-1]
     dev = q.device
@@ -225,15 +232,25 @@ def gla(q, k, v, log_decay, S0=None, *, want_final=True, chunk=CHUNK, workspace=
         ws, wsb = _workspace(nbytes, dev)
     else:
         ws, wsb = workspace, workspace.numel() * workspace.element_size()
-    st = L.cla_gla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(S0), _ptr(o), _ptr(ST),
-                       B, H, T, DK, DV, chunk, _ptr(ws), wsb, _stream(dev))
-    _lib.check("cla_gla_fwd", st)
-    return o, ST
+    if not save_states:
+        st = L.cla_gla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(S0), _ptr(o),
+                           _ptr(ST), B, H, T, DK, DV, chunk, _ptr(ws), wsb, _stream(dev))
+        _lib.check("cla_gla_fwd", st)
+        return o, ST
+    sb = int(L.cla_gla_saved_bytes(B, H, T, DK, DV, chunk))
+    saved = torch.empty(max(sb, 1), dtype=torch.uint8, device=dev)
+    st = L.cla_gla_fwd_saved(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(S0), _ptr(o),
+                             _ptr(ST), _ptr(saved), saved.numel(), B, H, T, DK, DV, chunk,
+                             _ptr(ws), wsb, _stream(dev))
+    _lib.check("cla_gla_fwd_saved", st)
+    return o, ST, saved
 
 
 def gla_bwd(q, k, v, log_decay, S0, dO, dST=None, *, want_dS0=True, chunk=CHUNK,
-            workspace=None):
-    """Backward of ``gla``: returns (dq, dk, dv, dlog_decay [B, H, T, DK], dS0)."""
+            workspace=None, saved=None):
+    """Backward of ``gla``: returns (dq, dk, dv, dlog_decay [B, H, T, DK], dS0).
+    ``saved``: the states returned by the forward with save_states=True
+    (cla_gla_bwd_saved), or None (cla_gla_bwd)."""
     B, H, T, DK = q.shape
     DV = v.shape[-1]
     dev = q.device
@@ -255,10 +272,20 @@ def gla_bwd(q, k, v, log_decay, S0, dO, dST=None, *, want_dS0=True, chunk=CHUNK,
         ws, wsb = _workspace(nbytes, dev)
     else:
         ws, wsb = workspace, workspace.numel() * workspace.element_size()
-    st = L.cla_gla_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(S0), _ptr(dO),
-                       _ptr(dST), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dl), _ptr(dS0),
-                       B, H, T, DK, DV, chunk, _ptr(ws), wsb, _stream(dev))
-    _lib.check("cla_gla_bwd", st)
+    if saved is None:
+        st = L.cla_gla_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(S0), _ptr(dO),
+                           _ptr(dST), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dl), _ptr(dS0),
+                           B, H, T, DK, DV, chunk, _ptr(ws), wsb, _stream(dev))
+        _lib.check("cla_gla_bwd", st)
+    else:
+        if saved.device != dev:
+            raise ValueError("saved must be on the same device as q")
+        st = L.cla_gla_bwd_saved(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(S0),
+                                 _ptr(dO), _ptr(dST), _ptr(saved),
+                                 saved.numel() * saved.element_size(), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), _ptr(dl), _ptr(dS0), B, H, T, DK, DV, chunk,
+                                 _ptr(ws), wsb, _stream(dev))
+        _lib.check("cla_gla_bwd_saved", st)
     return dq, dk, dv, dl, dS0
 
 

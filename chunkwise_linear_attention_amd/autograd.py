@@ -64,21 +64,22 @@ class ChunkedLinearAttnFn(torch.autograd.Function):
 
 
 class GLAFn(torch.autograd.Function):
-    """The same with one decay per key dimension (cla_gla_fwd / cla_gla_bwd)."""
+    """The same with one decay per key dimension (cla_gla_fwd_saved /
+    cla_gla_bwd_saved)."""
 
     @staticmethod
     def forward(ctx, q, k, v, log_decay, S0):
-        o, ST = api.gla(q, k, v, log_decay, S0)
-        ctx.save_for_backward(q, k, v, log_decay, S0)
+        o, ST, saved = api.gla(q, k, v, log_decay, S0, save_states=True)
+        ctx.save_for_backward(q, k, v, log_decay, S0, saved)
         ctx.has_S0 = S0 is not None
         return o, ST
 
     @staticmethod
     def backward(ctx, dO, dST):
-        q, k, v, l, S0 = ctx.saved_tensors
+        q, k, v, l, S0, saved = ctx.saved_tensors
         dq, dk, dv, dl, dS0 = api.gla_bwd(q, k, v, l, S0, _zeros_if_none(dO, v),
                                           None if dST is None else dST.contiguous(),
-                                          want_dS0=ctx.has_S0)
+                                          want_dS0=ctx.has_S0, saved=saved)
         return dq, dk, dv, dl, dS0
 
 

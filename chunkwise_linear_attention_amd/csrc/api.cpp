@@ -266,10 +266,24 @@ size_t cla_gla_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t DK, int6
                   : cla::gla::gla_fwd_ws_bytes(B * H, T, DK, DV);
 }
 
-int cla_gla_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                const float *log_decay, const float *S0, uint16_t *o, float *ST, int64_t B,
-                int64_t H, int64_t T, int64_t DK, int64_t DV, int64_t chunk, void *workspace,
-                size_t workspace_bytes, cla_stream_t stream) {
+size_t cla_gla_saved_bytes(int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV,
+                           int64_t chunk) {
+  if (B < 0 || H < 0 || T < 0) return 0;
+  if (!supported_head_dim(DK) || !supported_head_dim(DV) || chunk != 64) return 0;
+  if (B == 0 || H == 0 || T == 0) return 0;
+  const cla::gla::GlaPlan plan = cla::gla::plan_gla(B * H, T);
+  return plan.P > 1 ? (size_t)(plan.P - 1) * (size_t)(B * H) * DK * DV * sizeof(float) : 0;
+}
+
+namespace {
+
+// saved != NULL or use_saved: the forward's segment start states go to
+// `saved` (cla_gla_fwd_saved) instead of the workspace.
+int gla_fwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                 const float *log_decay, const float *S0, uint16_t *o, float *ST, bool use_saved,
+                 float *saved, size_t saved_bytes, int64_t B, int64_t H, int64_t T, int64_t DK,
+                 int64_t DV, int64_t chunk, void *workspace, size_t workspace_bytes,
+                 cla_stream_t stream) {
   if (B < 0 || H < 0 || T < 0 || DK < 0 || DV < 0 || chunk < 0) return CLA_ERR_BAD_SHAPE;
   if (!supported_head_dim(DK) || !supported_head_dim(DV) || chunk != 64)
     return CLA_ERR_UNSUPPORTED;
@@ -287,8 +301,13 @@ int cla_gla_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   const size_t need = T > 0 ? cla::gla::gla_fwd_ws_bytes((int64_t)nh, T, DK, DV) : 0;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return CLA_ERR_WORKSPACE;
+  const size_t sneed = use_saved && T > 0 ? cla_gla_saved_bytes(B, H, T, DK, DV, chunk) : 0;
+  if (sneed > 0 && (!saved || saved_bytes < sneed || !aligned16(saved)))
+    return CLA_ERR_WORKSPACE;
   const Range ws{need ? workspace : nullptr, need};
-  if (any_alias({{q, qk}, {k, qk}, {v, vv}, {log_decay, ll}, {S0, ss}}, {{o, vv}, {ST, ss}, ws}))
+  const Range sv{sneed ? saved : nullptr, sneed};
+  if (any_alias({{q, qk}, {k, qk}, {v, vv}, {log_decay, ll}, {S0, ss}},
+                {{o, vv}, {ST, ss}, ws, sv}))
     return CLA_ERR_ALIAS;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (T == 0)
@@ -299,7 +318,7 @@ int cla_gla_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   a.seg_chunks = plan.seg_chunks;
   if (plan.P > 1) {
     const size_t sl = (((size_t)(plan.P - 1) * nh * DK * DV * sizeof(float)) + 255) & ~(size_t)255;
-    a.Sloc = static_cast<float *>(workspace);
+    a.Sloc = sneed ? saved : static_cast<float *>(workspace);
     a.Aseg = reinterpret_cast<float *>(static_cast<char *>(workspace) + sl);
   }
   a.q = q;
@@ -315,11 +334,13 @@ int cla_gla_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 }
 
 
-int cla_gla_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                const float *log_decay, const float *S0, const uint16_t *dO, const float *dST,
-                uint16_t *dq, uint16_t *dk, uint16_t *dv, float *dlog_decay, float *dS0,
-                int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV, int64_t chunk,
-                void *workspace, size_t workspace_bytes, cla_stream_t stream) {
+// use_saved: the segments start from the forward's saved states (no state pass).
+int gla_bwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                 const float *log_decay, const float *S0, const uint16_t *dO, const float *dST,
+                 bool use_saved, const float *saved, size_t saved_bytes, uint16_t *dq,
+                 uint16_t *dk, uint16_t *dv, float *dlog_decay, float *dS0, int64_t B, int64_t H,
+                 int64_t T, int64_t DK, int64_t DV, int64_t chunk, void *workspace,
+                 size_t workspace_bytes, cla_stream_t stream) {
   if (B < 0 || H < 0 || T < 0 || DK < 0 || DV < 0 || chunk < 0) return CLA_ERR_BAD_SHAPE;
   if (!supported_head_dim(DK) || !supported_head_dim(DV) || chunk != 64)
     return CLA_ERR_UNSUPPORTED;
@@ -338,8 +359,12 @@ int cla_gla_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   const size_t need = T > 0 ? cla::gla::gla_bwd_ws_bytes((int64_t)nh, T, DK, DV) : 0;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return CLA_ERR_WORKSPACE;
+  const size_t sneed = use_saved && T > 0 ? cla_gla_saved_bytes(B, H, T, DK, DV, chunk) : 0;
+  if (sneed > 0 && (!saved || saved_bytes < sneed || !aligned16(saved)))
+    return CLA_ERR_WORKSPACE;
   const Range ws{need ? workspace : nullptr, need};
-  if (any_alias({{q, qk}, {k, qk}, {v, vv}, {log_decay, ll}, {S0, ss}, {dO, vv}, {dST, ss}},
+  if (any_alias({{q, qk}, {k, qk}, {v, vv}, {log_decay, ll}, {S0, ss}, {dO, vv}, {dST, ss},
+                 {saved, sneed}},
                 {{dq, qk}, {dk, qk}, {dv, vv}, {dlog_decay, ll}, {dS0, ss}, ws}))
     return CLA_ERR_ALIAS;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -354,7 +379,13 @@ int cla_gla_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   cla::gla::GlaBwdArgs a{};
   a.P = plan.P;
   a.seg_chunks = plan.seg_chunks;
-  if (plan.P > 1) {
+  if (plan.P > 1 && sneed) {
+    // the state each segment starts from, saved by the forward
+    a.Sin = saved;
+    wp += cla::gla::gla_fwd_ws_bytes((int64_t)nh, T, DK, DV);
+    a.Gloc = reinterpret_cast<float *>(wp);
+    a.Aq = reinterpret_cast<float *>(wp + r256((size_t)plan.P * nh * DK * DV * 4));
+  } else if (plan.P > 1) {
     // the state each segment starts from: the forward's state pass and scan
     cla::gla::GlaFwdArgs f{};
     f.q = q;
@@ -392,6 +423,44 @@ int cla_gla_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   a.nh = (int64_t)nh;
   a.T = T;
   return hip_status(cla::gla::gla_bwd_dispatch(a, (int)DK, (int)DV, s));
+}
+
+}  // namespace
+
+int cla_gla_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                const float *log_decay, const float *S0, uint16_t *o, float *ST, int64_t B,
+                int64_t H, int64_t T, int64_t DK, int64_t DV, int64_t chunk, void *workspace,
+                size_t workspace_bytes, cla_stream_t stream) {
+  return gla_fwd_impl(q, k, v, log_decay, S0, o, ST, false, nullptr, 0, B, H, T, DK, DV, chunk,
+                      workspace, workspace_bytes, stream);
+}
+
+int cla_gla_fwd_saved(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                      const float *log_decay, const float *S0, uint16_t *o, float *ST,
+                      float *saved, size_t saved_bytes, int64_t B, int64_t H, int64_t T,
+                      int64_t DK, int64_t DV, int64_t chunk, void *workspace,
+                      size_t workspace_bytes, cla_stream_t stream) {
+  return gla_fwd_impl(q, k, v, log_decay, S0, o, ST, true, saved, saved_bytes, B, H, T, DK, DV,
+                      chunk, workspace, workspace_bytes, stream);
+}
+
+int cla_gla_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                const float *log_decay, const float *S0, const uint16_t *dO, const float *dST,
+                uint16_t *dq, uint16_t *dk, uint16_t *dv, float *dlog_decay, float *dS0,
+                int64_t B, int64_t H, int64_t T, int64_t DK, int64_t DV, int64_t chunk,
+                void *workspace, size_t workspace_bytes, cla_stream_t stream) {
+  return gla_bwd_impl(q, k, v, log_decay, S0, dO, dST, false, nullptr, 0, dq, dk, dv,
+                      dlog_decay, dS0, B, H, T, DK, DV, chunk, workspace, workspace_bytes, stream);
+}
+
+int cla_gla_bwd_saved(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                      const float *log_decay, const float *S0, const uint16_t *dO,
+                      const float *dST, const float *saved, size_t saved_bytes, uint16_t *dq,
+                      uint16_t *dk, uint16_t *dv, float *dlog_decay, float *dS0, int64_t B,
+                      int64_t H, int64_t T, int64_t DK, int64_t DV, int64_t chunk,
+                      void *workspace, size_t workspace_bytes, cla_stream_t stream) {
+  return gla_bwd_impl(q, k, v, log_decay, S0, dO, dST, true, saved, saved_bytes, dq, dk, dv,
+                      dlog_decay, dS0, B, H, T, DK, DV, chunk, workspace, workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -302,6 +302,44 @@ int cla_gla_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                 int64_t DK, int64_t DV, int64_t chunk, void *workspace,
                 size_t workspace_bytes, cla_stream_t stream);
 
+/*
+ * Training path that keeps the forward's segment start states for the
+ * backward (the same decomposition as above: "Parallel scan", section
+ * "Splitting one sequence across devices", with a decay per key dimension).
+ * When a sequence is split into P > 1 segments, cla_gla_fwd_saved writes the
+ * state each segment p = 1 .. P-1 starts from (the state pass and scan the
+ * forward runs anyway) into `saved`, and cla_gla_bwd_saved starts the dQ
+ * pass's segments from them instead of running that state pass again.
+ * Results are bit-identical to cla_gla_fwd / cla_gla_bwd.
+ * cla_gla_saved_bytes: bytes of the saved states at this shape (0 when the
+ * sequence is not split, or for an invalid shape); layout [P-1, B*H, DK, DV]
+ * fp32, private to the library (pass it from cla_gla_fwd_saved to
+ * cla_gla_bwd_saved unchanged, same shape and inputs).
+ * saved: device buffer of at least cla_gla_saved_bytes bytes (may be NULL when
+ * that is 0), 16-byte aligned, owned by the caller.  Too small, misaligned or
+ * NULL when needed -> CLA_ERR_WORKSPACE; overlapping another argument ->
+ * CLA_ERR_ALIAS.  Every other argument and check is that of cla_gla_fwd /
+ * cla_gla_bwd.
+ */
+size_t cla_gla_saved_bytes(int64_t B, int64_t H, int64_t T, int64_t DK,
+                           int64_t DV, int64_t chunk);
+
+int cla_gla_fwd_saved(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                      const float *log_decay, const float *S0, uint16_t *o,
+                      float *ST, float *saved, size_t saved_bytes, int64_t B,
+                      int64_t H, int64_t T, int64_t DK, int64_t DV,
+                      int64_t chunk, void *workspace, size_t workspace_bytes,
+                      cla_stream_t stream);
+
+int cla_gla_bwd_saved(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                      const float *log_decay, const float *S0,
+                      const uint16_t *dO, const float *dST, const float *saved,
+                      size_t saved_bytes, uint16_t *dq, uint16_t *dk,
+                      uint16_t *dv, float *dlog_decay, float *dS0, int64_t B,
+                      int64_t H, int64_t T, int64_t DK, int64_t DV,
+                      int64_t chunk, void *workspace, size_t workspace_bytes,
+                      cla_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * Selective scan with N state entries per channel (Mamba-1's recurrence).
  * "Parallel scan", sections "Scans over vector and matrix states" (each

@@ -174,6 +174,39 @@ def test_gla_validation(lib):
     assert bw(*args, *shp, F, need, None) == ALIAS  # workspace overlaps dq
 
 
+def test_gla_saved_validation(lib):
+    # 16 heads of 98304 tokens: 32 segments of 3 blocks of 16 chunks
+    nb = lib.cla_gla_saved_bytes(1, 16, 98304, 128, 128, 64)
+    assert nb == 31 * 16 * 128 * 128 * 4
+    # 512 sequence-heads fill the GPU without splitting: nothing to save
+    assert lib.cla_gla_saved_bytes(32, 16, 4096, 128, 128, 64) == 0
+    assert lib.cla_gla_saved_bytes(1, 16, 98304, 96, 128, 64) == 0
+    assert lib.cla_gla_saved_bytes(-1, 16, 98304, 128, 128, 64) == 0
+    args = (1, 16, 98304, 128, 128, 64)
+    wf = lib.cla_gla_workspace_bytes(*args, 0)
+    f = lib.cla_gla_fwd_saved
+    # saved missing, too small or misaligned
+    assert f(A, B_, C, D_, None, E, None, None, 0, *args, F, wf, None) == WS
+    assert f(A, B_, C, D_, None, E, None, G, nb - 16, *args, F, wf, None) == WS
+    assert f(A, B_, C, D_, None, E, None, G + 4, nb, *args, F, wf, None) == WS
+    # saved overlapping an input, the output or the workspace
+    assert f(A, B_, C, D_, None, E, None, A, nb, *args, F, wf, None) == ALIAS
+    assert f(A, B_, C, D_, None, E, None, E + 64, nb, *args, F, wf, None) == ALIAS
+    assert f(A, B_, C, D_, None, E, None, F, nb, *args, F, wf, None) == ALIAS
+    wb = lib.cla_gla_workspace_bytes(*args, 1)
+    b = lib.cla_gla_bwd_saved
+    out = (H_, I, J, K, None)
+    assert b(A, B_, C, D_, None, E, None, None, 0, *out, *args, F, wb, None) == WS
+    assert b(A, B_, C, D_, None, E, None, G, nb - 16, *out, *args, F, wb, None) == WS
+    # saved states are an input of the backward: an output may not overlap them
+    assert b(A, B_, C, D_, None, E, None, H_, nb, *out, *args, F, wb, None) == ALIAS
+    assert b(A, B_, C, D_, None, E, None, G, nb, *out, 1, 16, 98304, 96, 128, 64,
+             F, wb, None) == UNSUP
+    # no split: no saved states needed (NULL accepted)
+    assert lib.cla_gla_fwd_saved(A, B_, C, D_, None, E, None, None, 0, 1, 1, 0, 64, 64, 64,
+                                 None, 0, None) == OK
+
+
 def test_sscan_validation(lib):
     ck = lib.cla_sscan_ckpt_bytes
     ws = lib.cla_sscan_workspace_bytes

@@ -238,3 +238,30 @@ def test_gla_workload_sampled_heads(coracle, variant):
     say(f"[gla workload] {variant} rel-L2: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if not v <= TOL}
     assert not bad, errs
+
+
+@pytest.mark.parametrize("B,H,T,DK,DV,S0,dST,seed", [
+    (1, 2, 4100, 128, 128, True, True, 41),    # 5 segments
+    (1, 1, 3000, 64, 64, False, True, 42),     # 3 segments, ragged tail
+    (2, 1, 200, 64, 128, True, False, 43),     # not split: nothing saved
+])
+def test_gla_saved_states_bit_identical(B, H, T, DK, DV, S0, dST, seed):
+    """cla_gla_fwd_saved then cla_gla_bwd_saved (the backward's segments start
+    from the forward's saved states) give exactly the outputs of the plain
+    calls, which rerun the state pass."""
+    import torch
+    import chunkwise_linear_attention_amd as cla
+    from gpu_util import say, to_dev
+    say(f"[gla saved] B={B} H={H} T={T} DK={DK} DV={DV} S0={S0} dST={dST}")
+    gi = syn.gla_inputs(B, H, T, DK, DV, seed, S0_scale=0.1 if S0 else None,
+                        dST_scale=0.1 if dST else None)
+    q, k, v, l, S0d, dO, dSTd = (to_dev(x) for x in (gi.q, gi.k, gi.v, gi.l, gi.S0, gi.dO, gi.dST))
+    o1, ST1 = cla.gla(q, k, v, l, S0d)
+    g1 = cla.gla_bwd(q, k, v, l, S0d, dO, dSTd)
+    o2, ST2, saved = cla.gla(q, k, v, l, S0d, save_states=True)
+    assert saved.numel() == max(1, cla.gla_saved_bytes(B, H, T, DK, DV))
+    g2 = cla.gla_bwd(q, k, v, l, S0d, dO, dSTd, saved=saved)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(ST1, ST2)
+    for x, y in zip(g1, g2):
+        assert (x is None and y is None) or torch.equal(x, y)
