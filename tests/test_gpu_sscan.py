@@ -140,23 +140,26 @@ def test_sscan_empty_and_stitched(coracle):
     assert all(v <= TOL for v in errs.values()), errs
 
 
-def test_sscan_workload_sampled(coracle):
-    """The bench workload (B=8, T=4096, D=5120, N=16) at full size, in the
-    launch configuration the bench times: y, h_T, dx, ddelta and dh0 on
-    sampled channels, dA on sampled channels summed over the batch, dB and dC
-    for one whole sequence; every output finite."""
+@pytest.mark.parametrize("wl", ["sscan_mamba", "sscan_b1"])
+def test_sscan_workload_sampled(coracle, wl):
+    """The bench workloads (B=8, T=4096, D=5120, N=16; B=1, T=32768, D=2048,
+    N=16 with time split into 16 segments) at full size, in the launch
+    configuration the bench times: y, h_T, dx, ddelta and dh0 on sampled
+    channels, dA on sampled channels summed over the batch, dB and dC for one
+    whole sequence; every output finite."""
     import torch
     from gpu_util import rel_l2, say, to_np
-    ci = syn.WORKLOADS["sscan_mamba"].make()
+    ci = syn.WORKLOADS[wl].make()
     Bt, T, D = ci.x.shape
     N = ci.A.shape[1]
-    say(f"[sscan workload] shape B={Bt} T={T} D={D} N={N}")
+    say(f"[sscan workload] {wl} shape B={Bt} T={T} D={D} N={N}")
     out = _run(ci)
     for name, t in zip(NAMES, out):
         if t is not None:
             assert bool(torch.isfinite(t).all()), name
-    ds = np.array([0, 1, 777, 2048, 4095, 5119])
-    chans = np.array([b * D + d for b in (0, 3, 7) for d in ds], dtype=np.int64)
+    ds = np.array(sorted({0, 1, D // 7, D // 2, D - 2, D - 1}))
+    bs = sorted({0, Bt // 2, Bt - 1})
+    chans = np.array([b * D + d for b in bs for d in ds], dtype=np.int64)
     y, hT = coracle.sscan_fwd(ci.x, ci.delta, ci.A, ci.Bm, ci.Cm, ci.h0, chans=chans)
     dx, dd, _, _, _, dh0 = coracle.sscan_bwd(ci.x, ci.delta, ci.A, ci.Bm, ci.Cm, ci.h0, ci.dy,
                                              ci.dhT, chans=chans)
@@ -174,11 +177,12 @@ def test_sscan_workload_sampled(coracle):
     rA = coracle.sscan_bwd(ci.x, ci.delta, ci.A, ci.Bm, ci.Cm, ci.h0, ci.dy, ci.dhT,
                            chans=chA)[2].reshape(len(ds), Bt, N).sum(axis=1)
     errs["dA"] = rel_l2(to_np(out[4])[ds], rA)
-    # dB, dC of sequence 5: every channel
-    b5 = np.arange(5 * D, 6 * D, dtype=np.int64)
+    # dB, dC of one sequence: every channel
+    sb = min(5, Bt - 1)
+    b5 = np.arange(sb * D, (sb + 1) * D, dtype=np.int64)
     rB, rC = coracle.sscan_bwd(ci.x, ci.delta, ci.A, ci.Bm, ci.Cm, ci.h0, ci.dy, ci.dhT,
                                chans=b5)[3:5]
-    errs["dB"] = rel_l2(to_np(out[5])[5], rB[5])
-    errs["dC"] = rel_l2(to_np(out[6])[5], rC[5])
-    say("[sscan workload] rel-L2 " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    errs["dB"] = rel_l2(to_np(out[5])[sb], rB[sb])
+    errs["dC"] = rel_l2(to_np(out[6])[sb], rC[sb])
+    say(f"[sscan workload] {wl} rel-L2 " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     assert all(v <= TOL for v in errs.values()), errs
