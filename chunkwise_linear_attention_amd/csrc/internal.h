@@ -12,13 +12,21 @@ namespace cla {
 namespace timing {
 void before(hipStream_t stream);
 void after(hipStream_t stream, const char *name);
+void cancel(hipStream_t stream);  // drop the start event of a failed launch
 }  // namespace timing
 
-// Launch a kernel between the timing hooks.
+// Launch a kernel between the timing hooks and return the launch error, if
+// any, from the enclosing function (which returns hipError_t) before anything
+// else is enqueued, so that no later call can hide it.
 #define CLA_LAUNCH(name, kernel, grid, block, stream, ...)                       \
   do {                                                                           \
     ::cla::timing::before(stream);                                               \
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, __VA_ARGS__);             \
+    const hipError_t cla_launch_err_ = hipGetLastError();                       \
+    if (cla_launch_err_ != hipSuccess) {                                         \
+      ::cla::timing::cancel(stream);                                             \
+      return cla_launch_err_;                                                    \
+    }                                                                            \
     ::cla::timing::after(stream, name);                                          \
   } while (0)
 

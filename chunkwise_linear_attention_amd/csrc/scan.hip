@@ -21,9 +21,10 @@
 // channels) -> a serial compose of kK steps in registers -> a Hillis-Steele
 // scan over the 4 slots of a wave with lane shuffles (WIKI code listing; ZTF
 // "The scan for one number of state") -> wave aggregates through LDS, folded
-// onto the pair carried from the previous block (WIKI: "carry one composed
-// pair across the chunk boundary") -> each lane recomputes its kK states from
-// its incoming state and stores them.  No intermediate state reaches HBM.
+// onto the pair carried from the previous block (one composed pair goes from
+// tile to tile and no intermediate state goes to HBM: WIKI, the closing
+// section on tiled, IO-aware kernels) -> each lane recomputes its kK states
+// from its incoming state and stores them.
 //
 // When B * D alone gives too few workgroups, the time axis is cut into P
 // segments: a first pass (AGG) writes each segment's composed pair, and the

@@ -2,13 +2,16 @@
 // library launches is bracketed by two HIP events recorded on the launch
 // stream; cla_timing_read() waits for them and reports the total time and the
 // launch count per kernel name.  Disabled by default: then the hooks cost one
-// branch per launch.
+// branch per launch.  A start event waits in a per-stream slot until its stop
+// event is recorded, so launches enqueued from several threads on different
+// streams pair their own events.
 #include <hip/hip_runtime.h>
 #include <string.h>
 
 #include <atomic>
 #include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/cla.h"
@@ -27,7 +30,9 @@ std::mutex mu;
 std::atomic<bool> enabled{false};
 std::vector<Rec> recs;
 std::vector<hipEvent_t> pool;
-hipEvent_t pending = nullptr;
+// start events recorded by before() and not yet closed by after(), one per
+// stream
+std::vector<std::pair<hipStream_t, hipEvent_t>> pending;
 
 hipEvent_t get_event() {
   if (!pool.empty()) {
@@ -42,22 +47,50 @@ hipEvent_t get_event() {
 
 }  // namespace
 
+// Removes and returns the open start event of `stream` (nullptr if none).
+hipEvent_t take_pending(hipStream_t stream) {
+  for (size_t i = 0; i < pending.size(); ++i) {
+    if (pending[i].first == stream) {
+      hipEvent_t e = pending[i].second;
+      pending.erase(pending.begin() + (ptrdiff_t)i);
+      return e;
+    }
+  }
+  return nullptr;
+}
+
 void before(hipStream_t stream) {
   if (!enabled) return;
   std::lock_guard<std::mutex> g(mu);
-  pending = get_event();
-  if (pending) (void)hipEventRecord(pending, stream);
+  hipEvent_t stale = take_pending(stream);
+  if (stale) pool.push_back(stale);
+  hipEvent_t start = get_event();
+  if (!start) return;
+  if (hipEventRecord(start, stream) != hipSuccess) {
+    pool.push_back(start);
+    return;
+  }
+  pending.push_back({stream, start});
 }
 
 void after(hipStream_t stream, const char *name) {
   if (!enabled) return;
   std::lock_guard<std::mutex> g(mu);
-  if (!pending) return;
+  hipEvent_t start = take_pending(stream);
+  if (!start) return;
   hipEvent_t stop = get_event();
-  if (!stop) return;
-  (void)hipEventRecord(stop, stream);
-  recs.push_back({name, pending, stop});
-  pending = nullptr;
+  if (!stop || hipEventRecord(stop, stream) != hipSuccess) {
+    pool.push_back(start);
+    if (stop) pool.push_back(stop);
+    return;
+  }
+  recs.push_back({name, start, stop});
+}
+
+void cancel(hipStream_t stream) {
+  std::lock_guard<std::mutex> g(mu);
+  hipEvent_t start = take_pending(stream);
+  if (start) pool.push_back(start);
 }
 
 }  // namespace timing

@@ -3,10 +3,18 @@
 The library must load, export every function include/cla.h declares, and
 reject bad arguments with the documented status codes before any launch.
 Fake non-NULL addresses are used for pointers the checks only compare; every
-call here returns before the library touches the device.
+call here is meant to return before the library touches the device.
+
+So that a regression in that validation can never hand a fake address to a
+real GPU, the checks run in a child process started with every GPU hidden
+(HIP_VISIBLE_DEVICES, ROCR_VISIBLE_DEVICES and CUDA_VISIBLE_DEVICES set
+empty), which confirms that it sees no device before it loads the library.
 """
 
 import ctypes
+import os
+import subprocess
+import sys
 
 import pytest
 
@@ -17,9 +25,36 @@ OK, NULL, SHAPE, UNSUP, WS, ALIAS = 0, 1, 2, 3, 4, 5
 # distinct fake device addresses, far apart so that ranges never overlap
 A, B_, C, D_, E, F, G, H_, I, J, K, L = (0x10_0000_0000 * (i + 1) for i in range(12))
 
+_CHILD_FLAG = "CLA_BOUNDARY_GPU_HIDDEN"
+IN_CHILD = os.environ.get(_CHILD_FLAG) == "1"
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_boundary_checks_in_gpu_free_child():
+    """Run every check below in a child process that sees no GPU."""
+    if IN_CHILD:
+        pytest.skip("this is the child")
+    env = dict(os.environ)
+    env.update({_CHILD_FLAG: "1", "HIP_VISIBLE_DEVICES": "", "ROCR_VISIBLE_DEVICES": "",
+                "CUDA_VISIBLE_DEVICES": ""})
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.abspath(__file__)], env=env, cwd=ROOT, capture_output=True,
+                       text=True, timeout=600)
+    print(r.stdout[-3000:])
+    assert r.returncode == 0, r.stdout[-4000:] + r.stderr[-2000:]
+    assert " passed" in r.stdout and "failed" not in r.stdout
+
 
 @pytest.fixture(scope="module")
 def lib():
+    if not IN_CHILD:
+        pytest.skip("runs in the GPU-free child process")
+    import torch
+    # counting devices does not initialise the GPU; with every device hidden
+    # the count must be 0 before any fake address reaches the library
+    n = torch.cuda.device_count()
+    if n != 0:
+        pytest.fail(f"{n} GPU(s) visible in the child; refusing to pass fake addresses")
     return _lib.lib()
 
 
