@@ -32,6 +32,7 @@ from .api import (  # noqa: F401
     chunked_linear_attn_bwd,
     scan,
     scan_bwd,
+    scan_fwd_noalloc,
     scan_workspace_bytes,
     chunk_workspace_bytes,
     chunk_saved_bytes,
@@ -45,7 +46,7 @@ from .api import (  # noqa: F401
     sscan_workspace_bytes,
 )
 
-__all__ = ["scan", "scan_bwd", "chunked_linear_attn", "chunked_linear_attn_bwd",
+__all__ = ["scan", "scan_bwd", "scan_fwd_noalloc", "chunked_linear_attn", "chunked_linear_attn_bwd",
            "scan_workspace_bytes", "chunk_workspace_bytes", "chunk_saved_bytes", "gla", "gla_bwd", "gla_saved_bytes",
            "gla_workspace_bytes", "selective_scan", "selective_scan_bwd", "sscan_ckpt_bytes",
            "sscan_workspace_bytes", "ClaError"]

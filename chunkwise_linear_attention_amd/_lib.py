@@ -40,6 +40,7 @@ SIGNATURES = {
     "cla_version": ([], ctypes.c_char_p),
     "cla_scan_workspace_bytes": ([i64, i64, i64], sz),
     "cla_scan_fwd": ([p, p, p, p, p, i64, i64, i64, p, sz, p], ctypes.c_int),
+    "cla_scan_fwd_noalloc": ([p, p, p, p, p, i64, i64, i64, p], ctypes.c_int),
     "cla_scan_bwd": ([p, p, p, p, p, p, p, p, i64, i64, i64, p, sz, p], ctypes.c_int),
     "cla_chunk_workspace_bytes": ([i64, i64, i64, i64, i64, i64, ctypes.c_int], sz),
     "cla_chunk_fwd": ([p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, p, sz, p],

@@ -78,6 +78,26 @@ def scan(a, b, h0=None, *, want_final=True, workspace=None):
     return h, hT
 
 
+def scan_fwd_noalloc(a, b, h0, h, hT=None):
+    """``scan`` for callers that cannot allocate: the outputs h [B, T, D] and
+    hT [B, D] (or None) are the caller's, and the library keeps the segment
+    pairs in its own fixed device array, so nothing is allocated here or in
+    the library.  Calls that may overlap on one GPU must be ordered."""
+    if a.dim() != 3:
+        raise ValueError("a must be [B, T, D]")
+    B, T, D = a.shape
+    dev = a.device
+    _need(a, "a", torch.float32, (B, T, D), dev)
+    _need(b, "b", torch.float32, (B, T, D), dev)
+    _opt(h0, "h0", torch.float32, (B, D), dev)
+    _need(h, "h", torch.float32, (B, T, D), dev)
+    _opt(hT, "hT", torch.float32, (B, D), dev)
+    st = _lib.lib().cla_scan_fwd_noalloc(_ptr(a), _ptr(b), _ptr(h0), _ptr(h), _ptr(hT),
+                                         B, T, D, _stream(dev))
+    _lib.check("cla_scan_fwd_noalloc", st)
+    return h, hT
+
+
 def scan_bwd(a, h, h0, dh, dhT=None, *, want_dh0=True, workspace=None):
     """Backward of ``scan``: returns (da, db, dh0)."""
     B, T, D = a.shape

@@ -91,6 +91,31 @@ int cla_scan_fwd(const float *a, const float *b, const float *h0, float *h,
   return hip_status(cla::launch_scan_fwd(a, b, h0, h, hT, B, T, D, plan, workspace, s));
 }
 
+int cla_scan_fwd_noalloc(const float *a, const float *b, const float *h0, float *h,
+                         float *hT, int64_t B, int64_t T, int64_t D, cla_stream_t stream) {
+  static_assert(cla::kScanNoAllocScratchBytes == CLA_SCAN_NOALLOC_SCRATCH_BYTES, "header");
+  if (B < 0 || T < 0 || D < 0) return CLA_ERR_BAD_SHAPE;
+  if (B == 0 || D == 0) return CLA_OK;
+  const size_t full = (size_t)B * (size_t)T * (size_t)D * sizeof(float);
+  const size_t row = (size_t)B * (size_t)D * sizeof(float);
+  if (T > 0 && (!a || !b || !h)) return CLA_ERR_NULL_ARG;
+  const cla::ScanPlan plan = cla::plan_scan(B, T, D);
+  if (plan.ws_bytes > cla::kScanNoAllocScratchBytes) return CLA_ERR_WORKSPACE;
+  if (any_alias({{a, full}, {b, full}, {h0, row}}, {{h, full}, {hT, row}}))
+    return CLA_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0) return hT ? hip_status(cla::launch_copy_or_zero(hT, h0, B * D, s)) : CLA_OK;
+  // the fixed array is looked up on the current device, so the stream must
+  // belong to it
+  if (s) {
+    int cur = -1, sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(s, &sdev) != hipSuccess)
+      return CLA_ERR_HIP;
+    if (cur != sdev) return CLA_ERR_UNSUPPORTED;
+  }
+  return hip_status(cla::launch_scan_fwd_noalloc(a, b, h0, h, hT, B, T, D, plan, s));
+}
+
 int cla_scan_bwd(const float *a, const float *h, const float *h0,
                  const float *dh, const float *dhT, float *da, float *db,
                  float *dh0, int64_t B, int64_t T, int64_t D, void *workspace,

@@ -57,6 +57,17 @@ hipError_t launch_scan_bwd(const float *a, const float *h, const float *h0,
                            int64_t D, const ScanPlan &plan, void *ws,
                            hipStream_t stream);
 
+// Bytes of the fixed device array behind launch_scan_fwd_noalloc (the
+// largest workspace plan_scan can ask for fits in it).
+constexpr size_t kScanNoAllocScratchBytes = 262144;
+
+// launch_scan_fwd with the segment pairs in the library's fixed device array
+// instead of a workspace (on the current device; no allocation).
+hipError_t launch_scan_fwd_noalloc(const float *a, const float *b, const float *h0,
+                                   float *h, float *hT, int64_t B, int64_t T,
+                                   int64_t D, const ScanPlan &plan,
+                                   hipStream_t stream);
+
 // dst[i] = src ? src[i] : 0 for i < n (empty-sequence final states).
 hipError_t launch_copy_or_zero(float *dst, const float *src, int64_t n,
                                hipStream_t stream);

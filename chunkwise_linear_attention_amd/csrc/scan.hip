@@ -30,6 +30,8 @@
 // segments: a first pass (AGG) writes each segment's composed pair, and the
 // main pass starts each segment from the fold of the earlier segments' pairs
 // (ZTF "Splitting one sequence across devices", done across workgroups).
+#include <mutex>
+
 #include "internal.h"
 
 namespace cla {
@@ -460,6 +462,55 @@ hipError_t launch_scan_bwd(const float *a, const float *h, const float *h0,
                   aligned16(da) && aligned16(db) && (!h0 || aligned16(h0)) &&
                   (!dhT || aligned16(dhT)) && (!dh0 || aligned16(dh0));
   return v4 ? run<4, 1>(args, plan, stream) : run<1, 1>(args, plan, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Forward scan without a caller workspace
+// ---------------------------------------------------------------------------
+// The segment pairs go to `scratch`, a fixed array that every GPU the library
+// runs on holds once, until the process ends.  The planner never needs more:
+// the time axis is split only when groups = B * ceil(D / 64) < kTargetGroups,
+// into P <= ceil(kTargetGroups / groups) segments, so (P - 1) * B * D <=
+// (kTargetGroups - 1) / groups * 64 * groups < 64 * kTargetGroups pairs.
+// Every pair the main pass reads is written by the segment pass of the same
+// call, so the array is never cleared; calls that overlap on one GPU share it
+// and race.
+namespace {
+
+constexpr int64_t kScratchPairs = (int64_t)(kScanNoAllocScratchBytes / sizeof(float2));
+static_assert(64 * kTargetGroups <= kScratchPairs, "scratch smaller than the largest plan");
+static __device__ __align__(256) float2 scratch[kScratchPairs];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+float2 *scratch_ptr[kMaxDevices] = {};  // device address of `scratch`, per device
+
+}  // namespace
+
+hipError_t launch_scan_fwd_noalloc(const float *a, const float *b, const float *h0,
+                                   float *h, float *hT, int64_t B, int64_t T,
+                                   int64_t D, const ScanPlan &plan,
+                                   hipStream_t stream) {
+  if (plan.ws_bytes > kScanNoAllocScratchBytes) return hipErrorInvalidValue;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float2 *ptr = nullptr;
+  {
+    std::lock_guard<std::mutex> g(scratch_mu);
+    if (!scratch_ptr[dev]) {
+      // once per device, with that device current: the host-side name of the
+      // array is not a device address, so kernels get this address instead
+      void *addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!addr) return hipErrorInvalidSymbol;
+      scratch_ptr[dev] = static_cast<float2 *>(addr);
+    }
+    ptr = scratch_ptr[dev];
+  }
+  return launch_scan_fwd(a, b, h0, h, hT, B, T, D, plan, ptr, stream);
 }
 
 hipError_t launch_copy_or_zero(float *dst, const float *src, int64_t n,

@@ -94,6 +94,27 @@ int cla_scan_fwd(const float *a, const float *b, const float *h0, float *h,
                  size_t workspace_bytes, cla_stream_t stream);
 
 /*
+ * cla_scan_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no workspace argument, and no allocation of any kind.  When the time axis
+ * is split into segments, their composed pairs go to a fixed device array of
+ * CLA_SCAN_NOALLOC_SCRATCH_BYTES that the library holds once per GPU until
+ * the process ends; every shape cla_scan_workspace_bytes accepts needs at
+ * most that much (a larger need returns CLA_ERR_WORKSPACE).  Arguments,
+ * results and every other check are those of cla_scan_fwd.
+ *   - The array is looked up (hipGetSymbolAddress) on the first call on each
+ *     device, with that device current; `stream` must belong to the current
+ *     device (CLA_ERR_UNSUPPORTED otherwise).
+ *   - Each call writes every entry it reads before reading it, so nothing is
+ *     cleared between calls.  All calls on one GPU share the array: calls
+ *     that may run at the same time on one GPU (different streams, or
+ *     threads) race and must be ordered by the caller.
+ */
+#define CLA_SCAN_NOALLOC_SCRATCH_BYTES 262144
+int cla_scan_fwd_noalloc(const float *a, const float *b, const float *h0, float *h,
+                         float *hT, int64_t B, int64_t T, int64_t D, cla_stream_t stream);
+
+/*
  * Backward of cla_scan_fwd.  "Parallel scan", section "The backward pass is a
  * scan in reverse": the adjoint hbar_t = dL/dh_t satisfies
  *   hbar_T = dh_T + dhT,  hbar_t = dh_t + a_{t+1} hbar_{t+1},

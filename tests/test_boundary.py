@@ -101,6 +101,33 @@ def test_scan_fwd_validation(lib):
     assert f(None, None, None, None, None, 3, 4, 0, None, 0, None) == OK
 
 
+def test_scan_fwd_noalloc_validation(lib):
+    f = lib.cla_scan_fwd_noalloc
+    assert f(A, B_, None, C, None, -1, 4, 4, None) == SHAPE
+    assert f(A, B_, None, C, None, 1, 4, -4, None) == SHAPE
+    assert f(None, B_, None, C, None, 1, 4, 4, None) == NULL
+    assert f(A, None, None, C, None, 1, 4, 4, None) == NULL
+    assert f(A, B_, None, None, None, 1, 4, 4, None) == NULL
+    assert f(A, B_, None, A, None, 1, 4096, 64, None) == ALIAS
+    assert f(A, B_, None, C, B_ + 16, 1, 4096, 64, None) == ALIAS
+    assert f(A, B_, D_, C, D_, 1, 4096, 64, None) == ALIAS
+    assert f(None, None, None, None, None, 0, 4, 4, None) == OK
+    assert f(None, None, None, None, None, 3, 4, 0, None) == OK
+
+
+def test_noalloc_array_covers_every_plan(lib):
+    """The fixed array behind cla_scan_fwd_noalloc (256 KiB) holds the largest
+    workspace the scan planner asks for: the time axis is split only when
+    B * ceil(D / 64) < 512 groups, into at most ceil(512 / groups) segments."""
+    worst = 0
+    for B in (1, 2, 3, 5, 7, 8):
+        for D in (1, 3, 4, 63, 64, 65, 128, 191, 192, 1000, 4096, 32704):
+            for T in (1, 127, 128, 129, 4096, 65535, 65536, 1 << 20, 1 << 24):
+                worst = max(worst, lib.cla_scan_workspace_bytes(B, T, D))
+    assert 0 < worst <= 262144
+    assert lib.cla_scan_workspace_bytes(1, 65536, 64) == 511 * 64 * 8
+
+
 def test_scan_bwd_validation(lib):
     f = lib.cla_scan_bwd
     assert f(A, B_, None, C, None, D_, E, None, 1, -1, 4, None, 0, None) == SHAPE
