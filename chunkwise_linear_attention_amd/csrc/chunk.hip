@@ -49,15 +49,22 @@ constexpr int64_t kFwdSlots = 512;
 constexpr int64_t kBwdSlots = 256;
 constexpr int64_t kMinSegChunks = 4;
 // The backward's decay gradient sums q.dq - k.dk backwards only inside one
-// segment, starting from the exact boundary term <S, G> of the two segment
-// states.  Inter-chunk paths reach q.dq through the bf16-rounded state S and
-// k.dk through the bf16-rounded gradient G, so the two sums do not cancel
-// exactly and their difference gathers rounding noise that grows with the
-// summed length; backward segments therefore hold at most 16 chunks (1024
-// tokens).
+// segment, starting from the boundary term <S, G> of the two segment states.
+// The sum telescopes: over a chunk, the inter-chunk parts of q.dq add up to
+// <S_[j-1], dG_j> and those of k.dk to <dS_j, G_j>, where dG_j and dS_j are
+// the chunk's contributions to the two states as the kernels accumulate them
+// (from (lambda q) and (gamma k) rounded to bf16).  The kernels form q.dq and
+// k.dk from exactly those rounded operands and from both states split into
+// two bf16 parts (hi + lo), so the two sums cancel to fp32 accumulation
+// accuracy and no bf16 rounding noise gathers along the sum.  Backward
+// segments hold at most 16 chunks (1024 tokens).
 constexpr int64_t kMaxBwdSegChunks = 16;
 
-// Outputs o, S_T and the optional rdot of one segment.  With GSUM, also (in
+// Outputs o, S_T and (XD) rdot of one segment.  XD marks the backward's dQ
+// pass (see launch_chunk_bwd): there the inter-chunk product uses the state
+// split into two bf16 parts, rdot carries the correction that pairs it with
+// the rounded (lambda q) of the state-gradient update, and the state at the
+// end of each segment but the last is written to Send.  With GSUM, also (in
 // segments after the first) the segment-local sum Q^T diag(A) X over the
 // segment (gloc, galoc), A_t the decay from the segment start through token
 // t.  Run as the backward's dQ pass (Q = dO, X = q) this is the local G state
@@ -66,8 +73,9 @@ constexpr int64_t kMaxBwdSegChunks = 16;
 // reverse sweep (ZTF "The chunkwise algorithm", the inter-chunk term read
 // backwards).
 // Four waves; wave w owns value columns [w DV/4, (w+1) DV/4).
-template <int DK, int DV, bool GSUM>
+template <int DK, int DV, bool GSUM, bool XD>
 __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
+  static_assert(!GSUM || XD, "segment-local sums are formed in the dQ pass only");
   constexpr int NJ = DV / 64;          // 16-column tiles per wave
   constexpr int NDT = DK / 16;         // 16-row tiles of the state
   constexpr int NCK = DK / 8, NCV = DV / 8;  // 16-byte chunks per row
@@ -80,7 +88,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   constexpr int B_KS = QB;
   constexpr int B_VS = B_KS + QB;
   constexpr int B_XS = B_VS + VB;
-  constexpr int B_L = B_XS + VB;
+  constexpr int B_L = B_XS + (XD ? VB : 0);
   constexpr int BUF = B_L + 64 * 4;
   constexpr int PSB = 64 * 128;
   constexpr int RDB = NWAVE * 64;
@@ -120,7 +128,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   const int64_t c_begin = seg * a.seg_chunks;
   const int64_t c_end = min(nchunks, c_begin + a.seg_chunks);
   const int j0 = w * (DV / 4);  // first value column of this wave
-  const bool has_x = a.xdot != nullptr;
+  constexpr bool has_x = XD;
   const bool do_g = GSUM && seg > 0;  // wave-uniform
   const int nblk = NBQ + NBK + NBV + (has_x ? NBV : 0);
 
@@ -182,19 +190,22 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   auto stage = [&](int64_t cj, unsigned char *buf) __attribute__((always_inline)) {
     const int64_t tj = cj * TC;
     const int nj = (int)min<int64_t>(TC, T - tj);
+    // the per-lane DMA addresses are formed here, at each stage, instead of
+    // being kept live (one 64-bit pair per staged tensor) across the loop
+    const int ln = fresh(lane);
     for (int b = w; b < nblk; b += NWAVE) {
       if (b < NBQ) {
-        dma_block<DK>(qh + tj * DK, nj, buf, b, lane);
+        dma_block<DK>(qh + tj * DK, nj, buf, b, ln);
       } else if (b < NBQ + NBK) {
-        dma_block<DK>(kh + tj * DK, nj, buf + B_KS, b - NBQ, lane);
+        dma_block<DK>(kh + tj * DK, nj, buf + B_KS, b - NBQ, ln);
       } else if (b < NBQ + NBK + NBV) {
-        dma_block<DV>(vh + tj * DV, nj, buf + B_VS, b - NBQ - NBK, lane);
+        dma_block<DV>(vh + tj * DV, nj, buf + B_VS, b - NBQ - NBK, ln);
       } else {
-        dma_block<DV>(xh + tj * DV, nj, buf + B_XS, b - NBQ - NBK - NBV, lane);
+        dma_block<DV>(xh + tj * DV, nj, buf + B_XS, b - NBQ - NBK - NBV, ln);
       }
     }
     if (w == 0)
-      __builtin_amdgcn_global_load_lds(lh + tj + min(lane, nj - 1), (lds_void *)(buf + B_L), 4, 0,
+      __builtin_amdgcn_global_load_lds(lh + tj + min(ln, nj - 1), (lds_void *)(buf + B_L), 4, 0,
                                        0);
   };
 
@@ -271,66 +282,129 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
       }
       lds_barrier();
 
-      // ---- output: O^T[j][r] = lambda_r (S^T Q^T)[j][r] + (V^T P^T)[j][r] ----
-      FRESH_LANE();
-      bf16x8 vfrag[NJ][2];  // A operands V^T: row j, k = s
+      if constexpr (XD) {
+        // ---- dQ pass output: O^T[j][r] = lambda_r (S^T Q^T)[j][r] + (V^T P^T)[j][r] ----
+        // (here O = dq, Q = dO, V = k, X = q).  The inter-chunk product takes
+        // the state as S = hi + lo, two bf16 parts (hi = bf16(S), lo =
+        // bf16(S - hi), formed where used), so that S enters it to ~2^-16;
+        // rdot_r = x_r . o_r plus the correction
+        //   sum_j ((lambda_r x_r)_bf16 - lambda_r x_r)[j] (S^T Q^T)[j][r],
+        // which makes its inter-chunk part pair with the bf16-rounded
+        // (lambda q) rows that the dK/dV pass adds into its state gradient.
+        FRESH_LANE();
+        bf16x8 vfrag[NJ][2];  // A operands V^T: row j, k = s
 #pragma unroll
-      for (int jt = 0; jt < NJ; ++jt)
+        for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) vfrag[jt][kb] = tr_frag<NCV>(VS, 32 * kb, j0 + 16 * jt, li, lg);
-      // the state slice as bf16 A operands: row j, k-set
-      // {32kk + 4lg + 0..3, 32kk + 16 + 4lg + 0..3}
-      bf16x8 sfrag[DK / 32][NJ];
-#pragma unroll
-      for (int kk = 0; kk < DK / 32; ++kk)
-#pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) sfrag[kk][jt] = cvt8(S_acc[2 * kk][jt], S_acc[2 * kk + 1][jt]);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int rr = 16 * rt + li;
-        const float lam = __shfl(lam_l, rr, 64);
-        bf16x8 qfrag[DK / 32];  // Q^T B operands, same k permutation
+          for (int kb = 0; kb < 2; ++kb) vfrag[jt][kb] = tr_frag<NCV>(VS, 32 * kb, j0 + 16 * jt, li, lg);
+        bf16x8 sfrag[DK / 32][NJ];  // hi parts of the state slice
 #pragma unroll
         for (int kk = 0; kk < DK / 32; ++kk)
-          qfrag[kk] = cat8(lds_half<NCK>(QS, rr, 32 * kk + 4 * lg),
-                           lds_half<NCK>(QS, rr, 32 * kk + 16 + 4 * lg));
-        bf16x8 pfrag[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) pfrag[kb] = lds_frag<8>(PS, rr, 4 * kb + lg);
-        float rdp = 0.f;
+          for (int jt = 0; jt < NJ; ++jt) sfrag[kk][jt] = cvt8(S_acc[2 * kk][jt], S_acc[2 * kk + 1][jt]);
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) {
-          f32x4 acc = zero4();
+        for (int rt = 0; rt < 4; ++rt) {
+          const int rr = 16 * rt + li;
+          const float lam = __shfl(lam_l, rr, 64);
+          bf16x8 qfrag[DK / 32];  // Q^T B operands, same k permutation
 #pragma unroll
-          for (int kk = 0; kk < DK / 32; ++kk) acc = mfma(sfrag[kk][jt], qfrag[kk], acc);
+          for (int kk = 0; kk < DK / 32; ++kk)
+            qfrag[kk] = cat8(lds_half<NCK>(QS, rr, 32 * kk + 4 * lg),
+                             lds_half<NCK>(QS, rr, 32 * kk + 16 + 4 * lg));
+          bf16x8 pfrag[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] *= lam;
+          for (int kb = 0; kb < 2; ++kb) pfrag[kb] = lds_frag<8>(PS, rr, 4 * kb + lg);
+          float rdp = 0.f;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            if (kb <= (rt >> 1)) acc = mfma(vfrag[jt][kb], pfrag[kb], acc);
-          // acc[i] = O[row rr][col j0 + 16 jt + 4 lg + i]
-          const int jc = j0 + 16 * jt + 4 * lg;
-          if (rr < n) {
-            bf16x4 ov;
+          for (int jt = 0; jt < NJ; ++jt) {
+            f32x4 acc = zero4();
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ov[i] = tobf(acc[i]);
-            *reinterpret_cast<bf16x4 *>(a.o + (bh * T + t0 + rr) * DV + jc) = ov;
-          }
-          if (has_x) {
+            for (int kk = 0; kk < DK / 32; ++kk) acc = mfma(sfrag[kk][jt], qfrag[kk], acc);
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) {
+              f32x4 r0, r1;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                r0[e] = S_acc[2 * kk][jt][e] - tof(sfrag[kk][jt][e]);
+                r1[e] = S_acc[2 * kk + 1][jt][e] - tof(sfrag[kk][jt][e + 4]);
+              }
+              acc = mfma(cvt8(r0, r1), qfrag[kk], acc);
+            }
+            const int jc = j0 + 16 * jt + 4 * lg;
             const bf16x4 xv = lds_half<NCV>(XS, rr, jc);
+            float corr = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float xl = tof(xv[i]) * lam;
+              corr += (tof(tobf(xl)) - xl) * acc[i];
+              acc[i] *= lam;
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+              if (kb <= (rt >> 1)) acc = mfma(vfrag[jt][kb], pfrag[kb], acc);
+            if (rr < n) {
+              bf16x4 ov;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) ov[i] = tobf(acc[i]);
+              *reinterpret_cast<bf16x4 *>(a.o + (bh * T + t0 + rr) * DV + jc) = ov;
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) rdp += tof(xv[i]) * acc[i];
+            rdp += corr;
           }
-        }
-        if (has_x) {
           rdp += __shfl_xor(rdp, 16, 64);
           rdp += __shfl_xor(rdp, 32, 64);
           if (lg == 0) RD[w * 64 + rr] = rdp;
         }
-      }
-      if (has_x) {
         rd_t0 = t0;
         rd_n = n;
+      } else {
+        // ---- output: O^T[j][r] = lambda_r (S^T Q^T)[j][r] + (V^T P^T)[j][r] ----
+        FRESH_LANE();
+        bf16x8 vfrag[NJ][2];  // A operands V^T: row j, k = s
+  #pragma unroll
+        for (int jt = 0; jt < NJ; ++jt)
+  #pragma unroll
+          for (int kb = 0; kb < 2; ++kb) vfrag[jt][kb] = tr_frag<NCV>(VS, 32 * kb, j0 + 16 * jt, li, lg);
+        // the state slice as bf16 A operands: row j, k-set
+        // {32kk + 4lg + 0..3, 32kk + 16 + 4lg + 0..3}
+        bf16x8 sfrag[DK / 32][NJ];
+  #pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk)
+  #pragma unroll
+          for (int jt = 0; jt < NJ; ++jt) sfrag[kk][jt] = cvt8(S_acc[2 * kk][jt], S_acc[2 * kk + 1][jt]);
+  #pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const int rr = 16 * rt + li;
+          const float lam = __shfl(lam_l, rr, 64);
+          bf16x8 qfrag[DK / 32];  // Q^T B operands, same k permutation
+  #pragma unroll
+          for (int kk = 0; kk < DK / 32; ++kk)
+            qfrag[kk] = cat8(lds_half<NCK>(QS, rr, 32 * kk + 4 * lg),
+                             lds_half<NCK>(QS, rr, 32 * kk + 16 + 4 * lg));
+          bf16x8 pfrag[2];
+  #pragma unroll
+          for (int kb = 0; kb < 2; ++kb) pfrag[kb] = lds_frag<8>(PS, rr, 4 * kb + lg);
+  #pragma unroll
+          for (int jt = 0; jt < NJ; ++jt) {
+            f32x4 acc = zero4();
+  #pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) acc = mfma(sfrag[kk][jt], qfrag[kk], acc);
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] *= lam;
+  #pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+              if (kb <= (rt >> 1)) acc = mfma(vfrag[jt][kb], pfrag[kb], acc);
+            // acc[i] = O[row rr][col j0 + 16 jt + 4 lg + i]
+            const int jc = j0 + 16 * jt + 4 * lg;
+            if (rr < n) {
+              bf16x4 ov;
+  #pragma unroll
+              for (int i = 0; i < 4; ++i) ov[i] = tobf(acc[i]);
+              *reinterpret_cast<bf16x4 *>(a.o + (bh * T + t0 + rr) * DV + jc) = ov;
+            }
+          }
+        }
       }
     }
 
@@ -394,7 +468,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
       }
     }
     // the state the backward's segment ci / save_every starts from
-    if (!GSUM && a.saved && (ci + 1) % a.save_every == 0 && ci + 1 < nchunks) {
+    if (!XD && a.saved && (ci + 1) % a.save_every == 0 && ci + 1 < nchunks) {
       float *dst = a.saved + (((ci + 1) / a.save_every - 1) * a.nh + bh) * DK * DV;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
@@ -458,6 +532,18 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
             G_acc[dt][jt];
     if (tid == 0) a.galoc[(seg - 1) * a.nh + bh] = alpha_total;
   }
+  if (XD && a.Send && seg < a.P - 1) {
+    // this pass's own state at the segment's end, for the decay gradient's
+    // boundary term (row-major, coalesced 64-byte pieces)
+    float *dst = a.Send + (seg * a.nh + bh) * DK * DV;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dst[(16 * dt + 4 * lg + i) * DV + j0 + 16 * jt + li] = S_acc[dt][jt][i];
+  }
   if (seg == a.P - 1 && a.ST) {
     float *dst = a.ST + bh * DK * DV;
 #pragma unroll
@@ -483,7 +569,15 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
 // with l = -inf), every earlier chunk contributes exactly 0: the pass stops
 // there without reading them, and alpha_p = 0.  Only K, V and l are read.
 // Four waves; wave w owns columns [w DV/4, (w+1) DV/4); two staging buffers.
-template <int DK, int DV>
+//
+// GRAD: the mirror image, for the backward's dQ pass when its own
+// segment-local sums do not fit in its registers.  For every segment p >= 1,
+// the local state gradient G_p = sum_t A_t k_t v_t^T (run on k = q, v = dO),
+// A_t = the decay from the segment's start through token t; the chunks are
+// taken first to last with the product of the chunk decays carried, and the
+// pass stops once it is exactly 0 (every later token adds exactly 0).  Slot
+// p - 1 receives G_p, aloc[p - 1] its total decay.
+template <int DK, int DV, bool GRAD>
 __global__ __launch_bounds__(NTHR, 2) void chunk_state_kernel(FwdArgs a) {
   constexpr int NJ = DV / 64, NDT = DK / 16;
   constexpr int NCK = DK / 8, NCV = DV / 8;
@@ -497,7 +591,8 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_state_kernel(FwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int li = lane & 15, lg = lane >> 4;
   const int64_t bh = blockIdx.x;
-  const int64_t seg = blockIdx.y;
+  const int64_t seg = blockIdx.y + (GRAD ? 1 : 0);
+  const int64_t slot = GRAD ? seg - 1 : seg;
   const int64_t T = a.T;
   const int64_t nchunks = (T + TC - 1) / TC;
   const int64_t c_begin = seg * a.seg_chunks;
@@ -512,9 +607,10 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_state_kernel(FwdArgs a) {
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) S_acc[dt][jt] = zero4();
-  // decay from the end of the chunk being added to the segment's end; every
-  // wave forms it from the same data with the same instructions, so it is
-  // the same in all waves
+  // decay from the end of the chunk being added to the segment's end (GRAD:
+  // from the segment's start to the start of that chunk); every wave forms
+  // it from the same data with the same instructions, so it is the same in
+  // all waves
   float A = 1.f;
 
   auto stage = [&](int64_t cj, unsigned char *buf) __attribute__((always_inline)) {
@@ -542,8 +638,10 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_state_kernel(FwdArgs a) {
     li = l_ & 15;
     lg = l_ >> 4;
     const ChunkDecay dc = chunk_decay(l_ < n ? LC[l_] : 0.f, l_);
-    // weight of token s: its decay to the chunk end, times A
-    const float wt_l = l_ < n && dc.k == dc.k_last ? A * expf(dc.c_last - dc.c) : 0.f;
+    // weight of token s: its decay to the chunk end, times A (GRAD: the decay
+    // from the chunk start through s, times A)
+    const float wt_l = GRAD ? (l_ < n && dc.k == 0 ? A * expf(dc.c) : 0.f)
+                            : (l_ < n && dc.k == dc.k_last ? A * expf(dc.c_last - dc.c) : 0.f);
     const float alpha = dc.k_last == 0 ? expf(dc.c_last) : 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -569,26 +667,37 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_state_kernel(FwdArgs a) {
     A *= alpha;
   };
 
-  // Chunk ci from `cur` while chunk ci - 1 streams into `nxt`; returns false
-  // once the earlier chunks can add nothing.  Nothing is in flight on return.
+  // Chunk ci from `cur` while the next chunk to take (ci - 1; GRAD: ci + 1)
+  // streams into `nxt`; returns false once the chunks not yet taken can add
+  // nothing.  Nothing is in flight on return.
   auto step = [&](int64_t ci, const unsigned char *cur, unsigned char *nxt)
                   __attribute__((always_inline)) -> bool {
-    if (ci > c_begin) stage(ci - 1, nxt);
+    if (GRAD ? ci + 1 < c_end : ci > c_begin) stage(GRAD ? ci + 1 : ci - 1, nxt);
     compute(ci, cur);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // the next chunk has landed; this chunk's buffer is free
     return __builtin_amdgcn_readfirstlane(A != 0.f ? 1 : 0) != 0;
   };
 
-  stage(c_end - 1, st0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int64_t ci = c_end - 1; ci >= c_begin; ci -= 2) {
-    if (!step(ci, st0, st1)) break;
-    if (ci - 1 >= c_begin && !step(ci - 1, st1, st0)) break;
+  if constexpr (GRAD) {
+    stage(c_begin, st0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int64_t ci = c_begin; ci < c_end; ci += 2) {
+      if (!step(ci, st0, st1)) break;
+      if (ci + 1 < c_end && !step(ci + 1, st1, st0)) break;
+    }
+  } else {
+    stage(c_end - 1, st0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int64_t ci = c_end - 1; ci >= c_begin; ci -= 2) {
+      if (!step(ci, st0, st1)) break;
+      if (ci - 1 >= c_begin && !step(ci - 1, st1, st0)) break;
+    }
   }
 
-  float *dst = a.Sloc + (seg * a.nh + bh) * DK * DV;
+  float *dst = a.Sloc + (slot * a.nh + bh) * DK * DV;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -599,7 +708,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_state_kernel(FwdArgs a) {
         dst[a.slot_trans ? j * DK + d : d * DV + j] = S_acc[dt][jt][i];
       }
   // the product of every chunk decay of the segment (0 after an early stop)
-  if (tid == 0) a.aloc[seg * a.nh + bh] = A;
+  if (tid == 0) a.aloc[slot * a.nh + bh] = A;
 }
 
 // Incoming state of every segment from the segment pairs (alpha_p, S_p):
@@ -648,7 +757,7 @@ hipError_t fwd_impl(FwdArgs args, hipStream_t stream) {
   if (P > 1 && !args.sin_given) {
     dim3 g1((unsigned)args.nh, (unsigned)(P - 1));
     CLA_LAUNCH(args.xdot ? "chunk_dq_segments" : "chunk_fwd_segments",
-               (chunk_state_kernel<DK, DV>), g1, dim3(NTHR), stream, args);
+               (chunk_state_kernel<DK, DV, false>), g1, dim3(NTHR), stream, args);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // slots and S0 are combined elementwise; S0 is read transposed only when
@@ -659,11 +768,20 @@ hipError_t fwd_impl(FwdArgs args, hipStream_t stream) {
     args.Sin = args.Sloc;
   }
   dim3 g((unsigned)args.nh, (unsigned)P);
-  if (args.gloc && P > 1) {
-    CLA_LAUNCH("chunk_dq", (chunk_fwd_kernel<DK, DV, true>), g, dim3(NTHR), stream, args);
+  if (args.xdot && args.gloc && P > 1) {
+    // (at DK = DV = 128 the segment-local sums come from a separate pass)
+    if constexpr (DK * DV < 128 * 128) {
+      CLA_LAUNCH("chunk_dq", (chunk_fwd_kernel<DK, DV, true, true>), g, dim3(NTHR), stream,
+                 args);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (args.xdot) {
+    CLA_LAUNCH("chunk_dq", (chunk_fwd_kernel<DK, DV, false, true>), g, dim3(NTHR), stream,
+               args);
   } else {
-    CLA_LAUNCH(args.xdot ? "chunk_dq" : "chunk_fwd", (chunk_fwd_kernel<DK, DV, false>), g,
-               dim3(NTHR), stream, args);
+    CLA_LAUNCH("chunk_fwd", (chunk_fwd_kernel<DK, DV, false, false>), g, dim3(NTHR), stream,
+               args);
   }
   return hipGetLastError();
 }
@@ -677,6 +795,24 @@ hipError_t launch_segment_scan(float *slots, const float *aloc, const float *ini
   CLA_LAUNCH("chunk_segment_scan", segment_scan_kernel, dim3((unsigned)((n + 255) / 256)),
              dim3(256), stream, slots, aloc, init, init_trans, reverse, nh, P, DK, DV);
   return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t grad_state_impl(const FwdArgs &args, hipStream_t stream) {
+  CLA_LAUNCH("chunk_grad_segments", (chunk_state_kernel<DK, DV, true>),
+             dim3((unsigned)args.nh, (unsigned)(args.P - 1)), dim3(NTHR), stream, args);
+  return hipSuccess;
+}
+
+// The segment-local state gradients G_p (segments 1..P-1) by the GRAD state
+// pass; args.k = q, args.v = dO, args.Sloc / args.aloc receive them.
+hipError_t grad_state_dispatch(const FwdArgs &args, int DK, int DV, hipStream_t stream) {
+  if (args.P <= 1) return hipSuccess;
+  if (DK == 64 && DV == 64) return grad_state_impl<64, 64>(args, stream);
+  if (DK == 64 && DV == 128) return grad_state_impl<64, 128>(args, stream);
+  if (DK == 128 && DV == 64) return grad_state_impl<128, 64>(args, stream);
+  if (DK == 128 && DV == 128) return grad_state_impl<128, 128>(args, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t fwd_dispatch(FwdArgs args, int DK, int DV, hipStream_t stream) {
@@ -707,12 +843,14 @@ FwdWs fwd_ws(void *base, int64_t nh, int64_t P, int64_t DK, int64_t DV) {
   return w;
 }
 
-// backward workspace: the segment states of the dQ pass (S at segment ends)
-// and of the reverse pass (G at segment ends), q . dq and k . dk per token,
-// the final state S_T, and the boundary terms <S, G> per segment
+// backward workspace: the segment states of the dQ pass (the states its
+// segments start from, and the states it ends them with) and of the reverse
+// pass (G at segment ends), q . dq and k . dk per token, the final state S_T,
+// and the boundary terms <S, G> per segment
 struct BwdWs {
-  FwdWs seg;   // dQ pass: slots p = S^T at the end of segment p
+  FwdWs seg;   // dQ pass: slots p = S^T entering segment p + 1
   FwdWs gseg;  // reverse pass: slots p = G at the end of segment p
+  float *Send; // dQ pass: [P-1, nh] S^T at the end of segment p, as that pass held it
   float *r1, *r2, *ST, *Bnd;
   size_t bytes;
 };
@@ -728,6 +866,7 @@ BwdWs bwd_ws(void *base, int64_t nh, int64_t T, int64_t P, int64_t DK, int64_t D
     off += (bytes + 255) & ~(size_t)255;
     return p;
   };
+  w.Send = P > 1 ? carve((size_t)(P - 1) * nh * DK * DV * sizeof(float)) : nullptr;
   w.r1 = carve((size_t)nh * T * sizeof(float));
   w.r2 = carve((size_t)nh * T * sizeof(float));
   w.ST = carve((size_t)nh * DK * DV * sizeof(float));
@@ -836,11 +975,21 @@ hipError_t launch_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t
     fa.slot_trans = 1;
     fa.sin_given = 1;
   }
-  if (plan.P_b > 1) {
-    // the dK/dV pass's segment-local G states, from the dO and q rows this
-    // pass already stages
+  // The dK/dV pass's segment-local G states: formed by this pass from the dO
+  // and q rows it stages anyway, except at DK = DV = 128, where its state,
+  // the split state operands and a second set of accumulators do not fit in
+  // its registers; a separate pass over q and dO (which stops where the decay
+  // from the segment start reaches 0) forms them there.
+  const bool gsum_in_dq = DK * DV < 128 * 128;
+  if (plan.P_b > 1 && gsum_in_dq) {
     fa.gloc = w.gseg.Sloc;
     fa.galoc = w.gseg.aloc;
+  }
+  if (plan.P_b > 1) {
+    // the state each segment ends with, for the boundary terms of the decay
+    // gradient (the states the segments start from were formed apart from
+    // this pass, by the segment pass and scan or by the forward)
+    fa.Send = w.Send;
   }
   fa.nh = nh;
   fa.T = T;
@@ -848,6 +997,20 @@ hipError_t launch_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t
   fa.P = plan.P_b;
   hipError_t e = chunk::fwd_dispatch(fa, (int)DV, (int)DK, stream);
   if (e != hipSuccess) return e;
+  if (plan.P_b > 1 && !gsum_in_dq) {
+    chunk::FwdArgs ga{};
+    ga.k = q;
+    ga.v = dO;
+    ga.l = l;
+    ga.Sloc = w.gseg.Sloc;
+    ga.aloc = w.gseg.aloc;
+    ga.nh = nh;
+    ga.T = T;
+    ga.seg_chunks = plan.seg_chunks_b;
+    ga.P = plan.P_b;
+    e = chunk::grad_state_dispatch(ga, (int)DK, (int)DV, stream);
+    if (e != hipSuccess) return e;
+  }
   // dK/dV pass (reverse chunk order)
   chunk::BwdArgs ba{};
   ba.q = q;
@@ -862,8 +1025,7 @@ hipError_t launch_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t
   ba.dS0 = dS0;
   ba.Gloc = w.gseg.Sloc;
   ba.aloc = w.gseg.aloc;
-  ba.Sseg = saved ? saved : w.seg.Sloc;
-  ba.sseg_dkdv = saved ? 1 : 0;
+  ba.Sseg = w.Send;
   ba.STb = dST ? w.ST : nullptr;
   ba.Bnd = w.Bnd;
   ba.nh = nh;

@@ -43,8 +43,11 @@ constexpr int BTHR = 512;
 
 // dK, dV, r2 and dS0 of one segment, starting from the G at its end (dS_T
 // for the last segment; the segment-local G states come from the dQ pass).
+// At DK = DV = 64 two workgroups (16 waves) share a CU, four waves per SIMD:
+// the register budget is then 128 per lane.
 template <int DK, int DV>
-__global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bwd_kernel(
+    BwdArgs a) {
   constexpr int NJ = DV / 64;   // dV side: 16-col tiles of G per wave
   constexpr int NI = DK / 64;   // dK side: 16-col tiles of G^T per wave
   constexpr int NCK = DK / 8, NCV = DV / 8;
@@ -95,6 +98,13 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     li = l_ & 15;                      \
     lg = l_ >> 4;                      \
   } while (0)
+  // a lane-dependent value re-derived behind an empty asm, like FRESH_LANE,
+  // so that the 64-bit addresses built from it are formed at their use and
+  // not kept live (or spilled) across the chunk loop
+  auto fresh = [](int x) __attribute__((always_inline)) {
+    asm volatile("" : "+v"(x));
+    return x;
+  };
   const int side = w >> 2, wv = w & 3;   // side 0: dV / G;  side 1: dK / G^T
   // grid (nh, segments): both indices are workgroup ids, held in scalar
   // registers, so every pointer derived from them stays wave-uniform
@@ -153,34 +163,22 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
   }
   {
     // Boundary term of the decay gradient: <S, G> at this segment's end, from
-    // the fp32 state left at that boundary and the G just loaded; each read
-    // runs along rows (coalesced) through the wave side whose copy of G has
-    // the state's layout: S^T from the dQ pass against G^T, S itself (saved
-    // by the forward) against G.
+    // the fp32 state S^T that the dQ pass held at that boundary (S_T^T for
+    // the last segment) and the G just loaded; the read runs along rows
+    // (coalesced) through the G^T side, whose copy has the state's layout.
     const bool last = seg == a.P - 1;
     const float *St = last ? (a.STb ? a.STb + bh * DK * DV : nullptr)
                            : a.Sseg + (seg * a.nh + bh) * DK * DV;
-    const bool trans = last || !a.sseg_dkdv;  // St holds S^T
     double part = 0.0;
-    if (St && side == (trans ? 1 : 0)) {
+    if (St && side == 1) {
       float pf = 0.f;
-      if (trans) {
 #pragma unroll
-        for (int jt = 0; jt < DV / 16; ++jt)
+      for (int jt = 0; jt < DV / 16; ++jt)
 #pragma unroll
-          for (int it = 0; it < NI; ++it)
+        for (int it = 0; it < NI; ++it)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              pf += G1(jt, it)[i] * St[(16 * jt + 4 * lg + i) * DK + dw0 + 16 * it + li];
-      } else {
-#pragma unroll
-        for (int dt = 0; dt < DK / 16; ++dt)
-#pragma unroll
-          for (int jt = 0; jt < NJ; ++jt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              pf += G0(dt, jt)[i] * St[(16 * dt + 4 * lg + i) * DV + jw0 + 16 * jt + li];
-      }
+          for (int i = 0; i < 4; ++i)
+            pf += G1(jt, it)[i] * St[(16 * jt + 4 * lg + i) * DK + dw0 + 16 * it + li];
       part = pf;
     }
 #pragma unroll
@@ -205,20 +203,23 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
   auto stage = [&](int64_t cj, unsigned char *buf) __attribute__((always_inline)) {
     const int64_t tj = cj * TC;
     const int nj = (int)min<int64_t>(TC, T - tj);
+    // the per-lane DMA addresses are formed here, at each stage, instead of
+    // being kept live (one 64-bit pair per staged tensor) across the loop
+    const int ln = fresh(lane);
     for (int b = w; b < NBLK; b += BTHR / 64) {
       if (b < NBQ) {
-        dma_block<DK>(qh + tj * DK, nj, buf, b, lane);
+        dma_block<DK>(qh + tj * DK, nj, buf, b, ln);
       } else if (b < NBQ + NBD) {
-        dma_block<DV>(doh + tj * DV, nj, buf + B_DOS, b - NBQ, lane);
+        dma_block<DV>(doh + tj * DV, nj, buf + B_DOS, b - NBQ, ln);
       } else if (b < NBQ + NBD + NBK) {
-        dma_block<DK>(kh + tj * DK, nj, buf + B_KS, b - NBQ - NBD, lane);
+        dma_block<DK>(kh + tj * DK, nj, buf + B_KS, b - NBQ - NBD, ln);
       } else {
-        dma_block<DV>(vh + tj * DV, nj, buf + B_VS, b - NBQ - NBD - NBK, lane);
+        dma_block<DV>(vh + tj * DV, nj, buf + B_VS, b - NBQ - NBD - NBK, ln);
       }
     }
     // this lane's log decay, used when the chunk is computed (rows past the
     // chunk read l = 0 there)
-    l_next = lane < nj ? lh[tj + lane] : 0.f;
+    l_next = ln < nj ? lh[tj + ln] : 0.f;
   };
 
   // One chunk from staging buffer `cur`, while the chunk before it streams
@@ -348,9 +349,15 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
           }
         }
       } else {
-        // ---- dK^T[d][s] = gamma_s (G V^T)[d][s] + (Q^T P2)[d][s] ; r2_s = k_s . dk_s ----
+        // ---- dK^T[d][s] = gamma_s (G V^T)[d][s] + (Q^T P2)[d][s] ; r2_s ----
+        // G enters the inter-chunk product as G = hi + lo, two bf16 parts
+        // (hi = bf16(G), lo = bf16(G - hi), formed where used), and
+        //   r2_s = k_s . dk_s + sum_d ((gamma_s k_s)_bf16 - gamma_s k_s)[d] (G v_s)[d],
+        // whose inter-chunk part then pairs with the bf16-rounded (gamma k)
+        // rows of the dQ pass's state update, so that the decay gradient's
+        // sums telescope exactly (see the segment length in chunk.hip).
         FRESH_LANE();
-        bf16x8 gfrag[DV / 32][NI];
+        bf16x8 gfrag[DV / 32][NI];  // hi parts
 #pragma unroll
         for (int kk = 0; kk < DV / 32; ++kk)
 #pragma unroll
@@ -364,7 +371,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
         for (int st = 0; st < 4; ++st) {
           const int s = 16 * st + li;
           const float gs = __shfl(gam_l, s, 64);
-          bf16x8 vfrag[DV / 32];
+          bf16x8 vfrag[DV / 32];  // V B operands: column s
 #pragma unroll
           for (int kk = 0; kk < DV / 32; ++kk)
             vfrag[kk] = cat8(lds_half<NCV>(VS, s, 32 * kk + 4 * lg),
@@ -379,13 +386,28 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
 #pragma unroll
             for (int kk = 0; kk < DV / 32; ++kk) acc = mfma(gfrag[kk][it], vfrag[kk], acc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] *= gs;
+            for (int kk = 0; kk < DV / 32; ++kk) {
+              f32x4 e0, e1;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                e0[e] = G1(2 * kk, it)[e] - tof(gfrag[kk][it][e]);
+                e1[e] = G1(2 * kk + 1, it)[e] - tof(gfrag[kk][it][e + 4]);
+              }
+              acc = mfma(cvt8(e0, e1), vfrag[kk], acc);
+            }
+            const int dc = dw0 + 16 * it + 4 * lg;
+            const bf16x4 kv = lds_half<NCK>(KS, s, dc);
+            float corr = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float kg = tof(kv[i]) * gs;
+              corr += (tof(tobf(kg)) - kg) * acc[i];
+              acc[i] *= gs;
+            }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
               if (2 * kb + 1 >= st) acc = mfma(qfrag[it][kb], pfrag[kb], acc);
-            // acc[i] = dK[s][dw0 + 16 it + 4 lg + i]
-            const int dc = dw0 + 16 * it + 4 * lg;
-            const bf16x4 kv = lds_half<NCK>(KS, s, dc);
+            r2p += corr;
 #pragma unroll
             for (int i = 0; i < 4; ++i) r2p += tof(kv[i]) * acc[i];
             if (s < n) {
@@ -457,7 +479,7 @@ __global__ __launch_bounds__(BTHR, 2) void chunk_bwd_kernel(BwdArgs a) {
     }
     r2_t0 = t0;
     r2_n = n;
-    if (r2_row >= 0 && tid < r2_prev_n) a.r2[bh * T + r2_row + tid] = r2_sum;
+    if (r2_row >= 0 && tid < r2_prev_n) a.r2[bh * T + r2_row + fresh(tid)] = r2_sum;
     // the next chunk has landed; this chunk's buffer is free
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

@@ -29,6 +29,8 @@ struct FwdArgs {
                            // start through t (needs xdot); in the dQ pass this is
                            // the dK/dV pass's local G state, stored as G
   float *galoc;            // with gloc: [P-1, nh] total decay of the segment
+  float *Send;             // optional (dQ pass): [P-1, nh, DK, DV] this pass's own state
+                           // at the end of segments 0..P-2, row-major in its orientation
   int64_t nh, T, seg_chunks, P, save_every;
   int s0_trans, st_trans;
   int slot_trans;          // segment slots (Sloc, Sin) hold this kernel's state transposed
@@ -48,15 +50,18 @@ struct BwdArgs {
                                     // scan turns it into Gin
   float *aloc;                      // [P-1, nh]: total decay of segment p in slot p-1
   const float *Sseg;                // [P-1, nh, DV, DK]: S^T at the end of segments 0..P-2
-                                    // ([P-1, nh, DK, DV], S itself, when sseg_dkdv)
+                                    // as the dQ pass held it
   const float *STb;                 // [nh, DV, DK]: S_T^T (NULL when there is no dS_T)
-  int sseg_dkdv;
   float *Bnd;                       // [P, nh]: <S, G> at the end of each segment
   int64_t nh, T, seg_chunks, P;
 };
 
 // Forward-type pass (segment state pass, segment scan, main pass).
 hipError_t fwd_dispatch(FwdArgs args, int DK, int DV, hipStream_t stream);
+
+// Segment-local state gradients of segments 1..P-1 (args.k = q, args.v = dO)
+// into args.Sloc / args.aloc slots 0..P-2, as the dQ pass's gloc / galoc.
+hipError_t grad_state_dispatch(const FwdArgs &args, int DK, int DV, hipStream_t stream);
 
 // Reverse dK/dV pass (reverse segment scan of Gloc, main pass).
 hipError_t bwd_kv_dispatch(const BwdArgs &args, int DK, int DV, hipStream_t stream);

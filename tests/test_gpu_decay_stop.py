@@ -7,8 +7,9 @@ pass adds them last to first and stops once that running product is 0, and
 the dQ pass stops adding to a segment's local state gradient once the decay
 from the segment start is 0.  Here a constant log decay makes the product
 vanish after a known number of chunks, inside the segments of both passes;
-every output is compared with the float64 oracle on sampled sequences, through
-the saved-state path and the plain calls.
+every output is compared with the float64 oracle on sampled sequences (the
+whole tensors and every 1024-token block of each), through the saved-state
+path and the plain calls.
 """
 
 import math
@@ -50,7 +51,7 @@ def _run(ci, saved):
 @pytest.mark.parametrize("B,H,T,DK,DV,lval,seed", CASES)
 def test_decay_product_reaches_zero(coracle, B, H, T, DK, DV, lval, seed, saved):
     import torch
-    from gpu_util import rel_l2, say, to_np
+    from gpu_util import CHUNK_BLOCKS, block_rel_l2, rel_l2, say, to_np
     say(f"[decay stop] B={B} H={H} T={T} DK={DK} DV={DV} l={lval} saved={saved}")
     ci = syn.chunk_inputs(B, H, T, DK, DV, seed, qk_scale=1 / math.sqrt(DK),
                           decay=("const", lval), S0_scale=0.1, dST_scale=0.1)
@@ -63,8 +64,9 @@ def test_decay_product_reaches_zero(coracle, B, H, T, DK, DV, lval, seed, saved)
     g_r = coracle.la_bwd(ci.q, ci.k, ci.v, ci.l, ci.S0, ci.dO, ci.dST, heads=heads)
     errs = {}
     for name, t, r in zip(NAMES, out, (o_r, ST_r) + tuple(g_r)):
-        got = to_np(t.reshape(nh, *t.shape[2:])[heads])
-        errs[name] = rel_l2(got.reshape(r.shape), r)
+        got = to_np(t.reshape(nh, *t.shape[2:])[heads]).reshape(r.shape)
+        errs[name] = rel_l2(got, r)
+        errs[name + "_blk"] = block_rel_l2(got, r, CHUNK_BLOCKS[name])[0]
     say("[decay stop] rel-L2 " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if not v <= TOL}
     assert not bad, errs

@@ -209,9 +209,10 @@ def test_gla_bwd_equal_decays_match_scalar_kernel():
 def test_gla_workload_sampled_heads(coracle, variant):
     """The bench's GLA workload (B=32, H=16, T=4096, dk=dv=128) at full size, in
     the launch configuration the bench times, against the oracle on sampled
-    sequences; every output finite.  The second variant adds S0 and dS_T."""
+    sequences (the whole tensors and every 1024-token block of each);
+    every output finite.  The second variant adds S0 and dS_T."""
     import torch
-    from gpu_util import rel_l2, say, to_np
+    from gpu_util import CHUNK_BLOCKS, block_rel_l2, rel_l2, say, to_np
     if variant == "plain":
         ci = syn.WORKLOADS["gla_T4096"].make()
     else:
@@ -234,7 +235,9 @@ def test_gla_workload_sampled_heads(coracle, variant):
         if t is None:
             continue
         got = to_np(t.reshape(B * H, *t.shape[2:])[torch.from_numpy(heads).to(t.device)])
-        errs[name] = rel_l2(got.reshape(r.shape), r)
+        got = got.reshape(r.shape)
+        errs[name] = rel_l2(got, r)
+        errs[name + "_blk"] = block_rel_l2(got, r, CHUNK_BLOCKS[name])[0]
     say(f"[gla workload] {variant} rel-L2: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if not v <= TOL}
     assert not bad, errs
@@ -267,17 +270,15 @@ def test_gla_saved_states_bit_identical(B, H, T, DK, DV, S0, dST, seed):
         assert (x is None and y is None) or torch.equal(x, y)
 
 
-def test_gla_long_workload_prefix_suffix(coracle):
+def test_gla_long_workload_full_heads(coracle):
     """The long GLA workload (B=1, H=16, T=98304: 32 segments) at full size,
-    through the saved-state path the bench times.  o_t and dq_t depend only on
-    the tokens up to t, and dk_t, dv_t only on the tokens from t on (no final
-    state gradient here), so the oracle run on the first 2048 tokens gives
-    exact o and dq there, and on the last 2048 tokens exact dk and dv there;
-    sampled heads.  The plain calls give bit-identical results; every output
-    is finite."""
+    through the saved-state path the bench times, against the oracle on two
+    whole sequence-heads: every output (o, S_T, dq, dk, dv, dl, dS0), the
+    whole tensors and every 1024-token block.  The plain calls give
+    bit-identical results; every output is finite."""
     import torch
     import chunkwise_linear_attention_amd as cla
-    from gpu_util import rel_l2, say, to_dev, to_np
+    from gpu_util import CHUNK_BLOCKS, block_rel_l2, rel_l2, say, to_dev, to_np
     ci = syn.WORKLOADS["gla_long_T98304"].make()
     B, H, T, DK = ci.q.shape
     heads = np.array([0, 9], dtype=np.int64)
@@ -291,19 +292,19 @@ def test_gla_long_workload_prefix_suffix(coracle):
     assert torch.equal(o, o2) and torch.equal(ST, ST2)
     for x, y in zip(g, g2):
         assert (x is None and y is None) or torch.equal(x, y)
-    for name, t in zip(("o", "ST", "dq", "dk", "dv", "dl"), (o, ST) + tuple(g[:4])):
+    out = (o, ST) + tuple(g)
+    names = ("o", "ST", "dq", "dk", "dv", "dl", "dS0")
+    for name, t in zip(names, out):
         assert bool(torch.isfinite(t.float()).all()), name
-    N = 2048
-    pre = lambda x: np.ascontiguousarray(x[:, :, :N])
-    suf = lambda x: np.ascontiguousarray(x[:, :, T - N:])
-    o_r, _ = coracle.gla_fwd(pre(ci.q), pre(ci.k), pre(ci.v), pre(ci.l), None, heads=heads)
-    dq_r = coracle.gla_bwd(pre(ci.q), pre(ci.k), pre(ci.v), pre(ci.l), None, pre(ci.dO), None,
-                           heads=heads)[0]
-    _, dk_r, dv_r, _, _ = coracle.gla_bwd(suf(ci.q), suf(ci.k), suf(ci.v), suf(ci.l), None,
-                                          suf(ci.dO), None, heads=heads)
-    sel = lambda t, lo, hi: to_np(t.reshape(B * H, T, -1)[torch.from_numpy(heads).to(t.device),
-                                                          lo:hi])
-    errs = {"o": rel_l2(sel(o, 0, N), o_r), "dq": rel_l2(sel(g[0], 0, N), dq_r),
-            "dk": rel_l2(sel(g[1], T - N, T), dk_r), "dv": rel_l2(sel(g[2], T - N, T), dv_r)}
+    say("[gla long workload] oracle on two whole heads")
+    o_r, ST_r = coracle.gla_fwd(ci.q, ci.k, ci.v, ci.l, None, heads=heads)
+    refs = (o_r, ST_r) + tuple(coracle.gla_bwd(ci.q, ci.k, ci.v, ci.l, None, ci.dO, None,
+                                               heads=heads))
+    hsel = torch.from_numpy(heads)
+    errs = {}
+    for name, t, r in zip(names, out, refs):
+        got = to_np(t.reshape(B * H, *t.shape[2:])[hsel.to(t.device)]).reshape(r.shape)
+        errs[name] = rel_l2(got, r)
+        errs[name + "_blk"] = block_rel_l2(got, r, CHUNK_BLOCKS[name])[0]
     say("[gla long workload] rel-L2 " + ", ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()))
     assert all(v_ <= TOL for v_ in errs.values()), errs

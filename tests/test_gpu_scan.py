@@ -25,17 +25,28 @@ def _run(inp, want_final=True):
     return h, hT, da, db, dh0
 
 
+# blocks of the error measure: each batch row, 1024 steps, 64 channels (one
+# workgroup's channel group); final states per batch row and channel group
+SEQ_BLOCKS = (1, 1024, 64)
+ROW_BLOCKS = (1, 64)
+
+
 def _check(inp, got, coracle):
-    from gpu_util import rel_l2, to_np
+    """Whole tensors and every block within the bar."""
+    from gpu_util import block_rel_l2, rel_l2, to_np
     h, hT, da, db, dh0 = got
     hr, hTr = coracle.scan_fwd(inp.a, inp.b, inp.h0)
     # the backward oracle reads the device forward output as its h input
     h32 = h.detach().cpu().numpy()
     dar, dbr, dh0r = coracle.scan_bwd(inp.a, h32, inp.h0, inp.dh, inp.dhT)
-    errs = {"h": rel_l2(to_np(h), hr), "da": rel_l2(to_np(da), dar),
-            "db": rel_l2(to_np(db), dbr), "dh0": rel_l2(to_np(dh0), dh0r)}
+    pairs = {"h": (to_np(h), hr, SEQ_BLOCKS), "da": (to_np(da), dar, SEQ_BLOCKS),
+             "db": (to_np(db), dbr, SEQ_BLOCKS), "dh0": (to_np(dh0), dh0r, ROW_BLOCKS)}
     if hT is not None:
-        errs["hT"] = rel_l2(to_np(hT), hTr)
+        pairs["hT"] = (to_np(hT), hTr, ROW_BLOCKS)
+    errs = {}
+    for k, (x, r, blk) in pairs.items():
+        errs[k] = rel_l2(x, r)
+        errs[k + "_blk"] = block_rel_l2(x, r, blk)[0]
     for k, e in errs.items():
         assert e <= TOL, (k, e, errs)
     return errs
@@ -81,11 +92,25 @@ def test_scan_special_decays(coracle, const):
         assert np.max(np.abs(h - ref)) < 1e-3
 
 
-def test_scan_small_workload_full(coracle):
+@pytest.mark.parametrize("h0", ["null", "zeros"])
+def test_scan_small_workload_full(coracle, h0):
+    """The small workload (B=1, T=4096, D=64: one channel group, time split
+    into 32 segments) with h0 given as NULL and as explicit zeros; both give
+    the same results, bit for bit."""
+    import torch
     from gpu_util import say
-    say("[scan workload] B=1 T=4096 D=64 (seed 1001)")
+    say(f"[scan workload] B=1 T=4096 D=64 (seed 1001) h0={h0}")
     inp = syn.WORKLOADS["scan_small"].make()
-    _check(inp, _run(inp), coracle)
+    if h0 == "zeros":
+        inp.h0 = np.zeros((1, 64), dtype=np.float32)
+    got = _run(inp)
+    errs = _check(inp, got, coracle)
+    say("[scan workload] rel-L2 " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    if h0 == "zeros":
+        inp.h0 = None
+        ref = _run(inp)
+        for x, y in zip(got, ref):
+            assert torch.equal(x, y)
 
 
 def test_scan_empty_sequence():
@@ -147,29 +172,41 @@ def test_scan_deterministic():
             assert torch.equal(x, y)
 
 
-def test_scan_large_workload_sampled(coracle):
-    """The B=8, T=16384, D=4096 workload in the bench's launch configuration;
-    outputs compared on sampled channel blocks (every batch row, three blocks
-    of 64 channels including the last) computed one by one by the oracle."""
+def test_scan_large_workload_full(coracle):
+    """The B=8, T=16384, D=4096 workload in the bench's launch configuration
+    (XCD-ordered workgroups), compared with the oracle on every channel, in
+    slabs of 512 channels: the whole slab and every block (batch row, 1024
+    steps, 64 channels) within the bar."""
     import torch
     import chunkwise_linear_attention_amd as cla
-    from gpu_util import rel_l2, say, to_dev
-    say("[scan large] B=8 T=16384 D=4096 (seed 1002), sampled channels")
+    from gpu_util import block_rel_l2, rel_l2, say, to_dev
+    say("[scan large] B=8 T=16384 D=4096 (seed 1002), every channel")
     inp = syn.WORKLOADS["scan_large"].make()
     a, b, dh = to_dev(inp.a), to_dev(inp.b), to_dev(inp.dh)
     h0 = to_dev(inp.h0)
     h, hT = cla.scan(a, b, h0)
     da, db, dh0 = cla.scan_bwd(a, h, h0, dh, None)
     torch.cuda.synchronize()
+    del a, b, dh
     h_full = h.cpu().numpy()
-    for d0 in (0, 2048 + 64, 4096 - 64):
-        sl = slice(d0, d0 + 64)
-        hr, hTr = coracle.scan_fwd(inp.a, inp.b, inp.h0, drange=(d0, d0 + 64))
-        hs = h[:, :, sl].cpu().numpy()
-        assert rel_l2(hs, hr) <= TOL
-        assert rel_l2(hT[:, sl].cpu().numpy(), hTr) <= TOL
+    worst = {}
+    for d0 in range(0, 4096, 512):
+        sl = slice(d0, d0 + 512)
+        hr, hTr = coracle.scan_fwd(inp.a, inp.b, inp.h0, drange=(d0, d0 + 512))
         dar, dbr, dh0r = coracle.scan_bwd(inp.a, h_full, inp.h0, inp.dh, None,
-                                          drange=(d0, d0 + 64))
-        assert rel_l2(da[:, :, sl].cpu().numpy(), dar) <= TOL
-        assert rel_l2(db[:, :, sl].cpu().numpy(), dbr) <= TOL
-        assert rel_l2(dh0[:, sl].cpu().numpy(), dh0r) <= TOL
+                                          drange=(d0, d0 + 512))
+        pairs = {"h": (h_full[:, :, sl], hr, SEQ_BLOCKS),
+                 "hT": (hT[:, sl].cpu().numpy(), hTr, ROW_BLOCKS),
+                 "da": (da[:, :, sl].cpu().numpy(), dar, SEQ_BLOCKS),
+                 "db": (db[:, :, sl].cpu().numpy(), dbr, SEQ_BLOCKS),
+                 "dh0": (dh0[:, sl].cpu().numpy(), dh0r, ROW_BLOCKS)}
+        for k, (x, r, blk) in pairs.items():
+            e = rel_l2(x, r)
+            eb, at = block_rel_l2(x, r, blk)
+            assert e <= TOL, (k, d0, e)
+            assert eb <= TOL, (k, d0, at, eb)
+            worst[k] = max(worst.get(k, 0.0), e)
+            worst[k + "_blk"] = max(worst.get(k + "_blk", 0.0), eb)
+        del hr, dar, dbr
+    say("[scan large] worst rel-L2 over slabs " +
+        ", ".join(f"{k}={v:.2e}" for k, v in worst.items()))

@@ -146,9 +146,10 @@ def test_sscan_workload_sampled(coracle, wl):
     N=16 with time split into 16 segments) at full size, in the launch
     configuration the bench times: y, h_T, dx, ddelta and dh0 on sampled
     channels, dA on sampled channels summed over the batch, dB and dC for one
-    whole sequence; every output finite."""
+    whole sequence; every output finite.  The bar holds for the whole sampled
+    tensors and for every 1024-step block of each sampled channel."""
     import torch
-    from gpu_util import rel_l2, say, to_np
+    from gpu_util import block_rel_l2, rel_l2, say, to_np
     ci = syn.WORKLOADS[wl].make()
     Bt, T, D = ci.x.shape
     N = ci.A.shape[1]
@@ -166,10 +167,13 @@ def test_sscan_workload_sampled(coracle, wl):
     gy, ghT, gdx, gdd = (to_np(t) for t in out[:2] + out[2:4])
     errs = {}
     bsel, dsel = chans // D, chans % D
-    errs["y"] = rel_l2(gy[bsel, :, dsel], y)
+    # whole sampled tensors, and every 1024-step block of each sampled channel
+    for nm, g, r in (("y", gy[bsel, :, dsel], y), ("dx", gdx[bsel, :, dsel], dx),
+                     ("ddelta", gdd[bsel, :, dsel], dd)):
+        errs[nm] = rel_l2(g, r)
+        errs[nm + "_blk"] = block_rel_l2(g, r, (1, 1024))[0]
     errs["hT"] = rel_l2(ghT[bsel, dsel], hT)
-    errs["dx"] = rel_l2(gdx[bsel, :, dsel], dx)
-    errs["ddelta"] = rel_l2(gdd[bsel, :, dsel], dd)
+    errs["hT_blk"] = block_rel_l2(ghT[bsel, dsel], hT, (1,))[0]
     if out[7] is not None:
         errs["dh0"] = rel_l2(to_np(out[7])[bsel, dsel], dh0)
     # dA on sampled channels: all sequences
@@ -184,5 +188,7 @@ def test_sscan_workload_sampled(coracle, wl):
                                chans=b5)[3:5]
     errs["dB"] = rel_l2(to_np(out[5])[sb], rB[sb])
     errs["dC"] = rel_l2(to_np(out[6])[sb], rC[sb])
+    errs["dB_blk"] = block_rel_l2(to_np(out[5])[sb], rB[sb], (1024,))[0]
+    errs["dC_blk"] = block_rel_l2(to_np(out[6])[sb], rC[sb], (1024,))[0]
     say(f"[sscan workload] {wl} rel-L2 " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     assert all(v <= TOL for v in errs.values()), errs
