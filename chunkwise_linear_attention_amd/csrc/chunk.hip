@@ -182,6 +182,14 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     }
   }
   float alpha_total = 1.f;
+  // saved states: the next one is slot save_slot - 1, taken after chunk
+  // save_at - 1 (a counter, so that the chunk loop does no 64-bit division)
+  int64_t save_slot = 0, save_at = -1;
+  if (!XD && a.saved) {
+    save_slot = c_begin / a.save_every + 1;
+    save_at = save_slot * a.save_every;
+    if (save_at >= nchunks) save_at = -1;  // no state is saved after the last chunk
+  }
   int64_t rd_t0 = -1;  // chunk whose xdot partials sit in RD
   int rd_n = 0;
 
@@ -286,7 +294,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
         // ---- dQ pass output: O^T[j][r] = lambda_r (S^T Q^T)[j][r] + (V^T P^T)[j][r] ----
         // (here O = dq, Q = dO, V = k, X = q).  The inter-chunk product takes
         // the state as S = hi + lo, two bf16 parts (hi = bf16(S), lo =
-        // bf16(S - hi), formed where used), so that S enters it to ~2^-16;
+        // bf16(S - hi), both formed once per chunk), so that S enters it to ~2^-16;
         // rdot_r = x_r . o_r plus the correction
         //   sum_j ((lambda_r x_r)_bf16 - lambda_r x_r)[j] (S^T Q^T)[j][r],
         // which makes its inter-chunk part pair with the bf16-rounded
@@ -297,11 +305,12 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
         for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) vfrag[jt][kb] = tr_frag<NCV>(VS, 32 * kb, j0 + 16 * jt, li, lg);
-        bf16x8 sfrag[DK / 32][NJ];  // hi parts of the state slice
+        bf16x8 shi[DK / 32][NJ], slo[DK / 32][NJ];  // the state slice as hi + lo
 #pragma unroll
         for (int kk = 0; kk < DK / 32; ++kk)
 #pragma unroll
-          for (int jt = 0; jt < NJ; ++jt) sfrag[kk][jt] = cvt8(S_acc[2 * kk][jt], S_acc[2 * kk + 1][jt]);
+          for (int jt = 0; jt < NJ; ++jt)
+            split8(S_acc[2 * kk][jt], S_acc[2 * kk + 1][jt], shi[kk][jt], slo[kk][jt]);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
           const int rr = 16 * rt + li;
@@ -319,17 +328,9 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
           for (int jt = 0; jt < NJ; ++jt) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) acc = mfma(sfrag[kk][jt], qfrag[kk], acc);
+            for (int kk = 0; kk < DK / 32; ++kk) acc = mfma(shi[kk][jt], qfrag[kk], acc);
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-              f32x4 r0, r1;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                r0[e] = S_acc[2 * kk][jt][e] - tof(sfrag[kk][jt][e]);
-                r1[e] = S_acc[2 * kk + 1][jt][e] - tof(sfrag[kk][jt][e + 4]);
-              }
-              acc = mfma(cvt8(r0, r1), qfrag[kk], acc);
-            }
+            for (int kk = 0; kk < DK / 32; ++kk) acc = mfma(slo[kk][jt], qfrag[kk], acc);
             const int jc = j0 + 16 * jt + 4 * lg;
             const bf16x4 xv = lds_half<NCV>(XS, rr, jc);
             float corr = 0.f;
@@ -467,9 +468,11 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
         for (int jt = 0; jt < NJ; ++jt) S_acc[dt][jt] = mfma(ka, vb[jt], S_acc[dt][jt]);
       }
     }
-    // the state the backward's segment ci / save_every starts from
-    if (!XD && a.saved && (ci + 1) % a.save_every == 0 && ci + 1 < nchunks) {
-      float *dst = a.saved + (((ci + 1) / a.save_every - 1) * a.nh + bh) * DK * DV;
+    // the state the backward's segment save_slot starts from
+    if (!XD && ci + 1 == save_at) {
+      float *dst = a.saved + ((save_slot - 1) * a.nh + bh) * DK * DV;
+      ++save_slot;
+      save_at = ci + 1 + a.save_every < nchunks ? ci + 1 + a.save_every : -1;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll

@@ -351,17 +351,18 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
       } else {
         // ---- dK^T[d][s] = gamma_s (G V^T)[d][s] + (Q^T P2)[d][s] ; r2_s ----
         // G enters the inter-chunk product as G = hi + lo, two bf16 parts
-        // (hi = bf16(G), lo = bf16(G - hi), formed where used), and
+        // (hi = bf16(G), lo = bf16(G - hi), both formed once per chunk), and
         //   r2_s = k_s . dk_s + sum_d ((gamma_s k_s)_bf16 - gamma_s k_s)[d] (G v_s)[d],
         // whose inter-chunk part then pairs with the bf16-rounded (gamma k)
         // rows of the dQ pass's state update, so that the decay gradient's
         // sums telescope exactly (see the segment length in chunk.hip).
         FRESH_LANE();
-        bf16x8 gfrag[DV / 32][NI];  // hi parts
+        bf16x8 ghi[DV / 32][NI], glo[DV / 32][NI];
 #pragma unroll
         for (int kk = 0; kk < DV / 32; ++kk)
 #pragma unroll
-          for (int it = 0; it < NI; ++it) gfrag[kk][it] = cvt8(G1(2 * kk, it), G1(2 * kk + 1, it));
+          for (int it = 0; it < NI; ++it)
+            split8(G1(2 * kk, it), G1(2 * kk + 1, it), ghi[kk][it], glo[kk][it]);
         bf16x8 qfrag[NI][2];  // Q^T A operands: row d, k = r
 #pragma unroll
         for (int it = 0; it < NI; ++it)
@@ -384,17 +385,9 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
           for (int it = 0; it < NI; ++it) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < DV / 32; ++kk) acc = mfma(gfrag[kk][it], vfrag[kk], acc);
+            for (int kk = 0; kk < DV / 32; ++kk) acc = mfma(ghi[kk][it], vfrag[kk], acc);
 #pragma unroll
-            for (int kk = 0; kk < DV / 32; ++kk) {
-              f32x4 e0, e1;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                e0[e] = G1(2 * kk, it)[e] - tof(gfrag[kk][it][e]);
-                e1[e] = G1(2 * kk + 1, it)[e] - tof(gfrag[kk][it][e + 4]);
-              }
-              acc = mfma(cvt8(e0, e1), vfrag[kk], acc);
-            }
+            for (int kk = 0; kk < DV / 32; ++kk) acc = mfma(glo[kk][it], vfrag[kk], acc);
             const int dc = dw0 + 16 * it + 4 * lg;
             const bf16x4 kv = lds_half<NCK>(KS, s, dc);
             float corr = 0.f;

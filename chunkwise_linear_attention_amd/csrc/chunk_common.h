@@ -150,6 +150,25 @@ __device__ __forceinline__ ChunkDecay chunk_decay(float l, int lane) {
 __device__ __forceinline__ int tile_rt(int t) { return (0x8FFA94u >> (2 * t)) & 3; }
 __device__ __forceinline__ int tile_st(int t) { return (0xDE4910u >> (2 * t)) & 3; }
 
+// x = hi + lo to about 2^-16 relative: hi = bf16(x) (round to nearest even),
+// lo = bf16(x - hi).  The fp32 value of each hi element is read back from its
+// packed pair (a shift or a mask) rather than converted a second time.
+__device__ __forceinline__ void split8(f32x4 a, f32x4 b, bf16x8 &hi, bf16x8 &lo) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  hi = cvt8(a, b);
+  const u32x4 hw = __builtin_bit_cast(u32x4, hi);
+  float r[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float x0 = w < 2 ? a[2 * w] : b[2 * w - 4];
+    const float x1 = w < 2 ? a[2 * w + 1] : b[2 * w - 3];
+    r[2 * w] = x0 - __builtin_bit_cast(float, hw[w] << 16);
+    r[2 * w + 1] = x1 - __builtin_bit_cast(float, hw[w] & 0xffff0000u);
+  }
+  lo = cvt8(r);
+}
+
+// ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
 // Asynchronous staging: global -> LDS copies that bypass registers
 // (global_load_lds, 16 bytes per lane; lane i of a wave writes bytes
