@@ -73,6 +73,8 @@ __device__ __forceinline__ float path_term(float b, float q, float k, float ct, 
   return ((b * q) * k) * __expf(ct - cs);
 }
 
+// DMA of a [64 x D] fp32 tile, rows plain (unswizzled): 1 KB blocks of RPB
+// rows; rows past the chunk re-read row n - 1.
 template <int D>
 __device__ __forceinline__ void dma_f32_rows(const float *chunk_src, int n, unsigned char *tile,
                                              int block, int lane) {
@@ -83,6 +85,89 @@ __device__ __forceinline__ void dma_f32_rows(const float *chunk_src, int n, unsi
   __builtin_amdgcn_global_load_lds(chunk_src + (int64_t)grow * D + (lane % PPR) * 4,
                                    (lds_void *)(tile + block * 1024), 16, 0, 0);
 }
+
+// ---------------------------------------------------------------------------
+// Register staging of a chunk's inputs.  A workgroup's LDS holds one chunk
+// (there is no room for a second), so the next chunk is fetched into
+// registers while the current one is worked on and written to LDS between
+// the two.  The LDS layout is the 1 KB-block layout of the DMA staging of the
+// scalar kernels (lane i holds bytes 16 i .. 16 i + 15 of its block): q, k,
+// v, dO as swizzled bf16 tiles, then the [64 x DK] fp32 log rows, plain.
+// Wave w holds blocks w, w + NW, ...; each tensor's block count is a multiple
+// of NW, so the tensor of every held block is known at compile time.  Rows
+// past the chunk's n tokens re-read row n - 1 (finite data, masked later).
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ uint4 fetch_bf16_block(const uint16_t *chunk_src, int n, int block,
+                                                  int lane) {
+  constexpr int NCH = D / 8;
+  constexpr int RPB = 64 / NCH;
+  const int row = block * RPB + lane / NCH;
+  const int c = (lane % NCH) ^ swz_pat(row);
+  const int grow = min(row, n - 1);
+  return *reinterpret_cast<const uint4 *>(chunk_src + (int64_t)grow * D + c * 8);
+}
+
+template <int D>
+__device__ __forceinline__ uint4 fetch_f32_block(const float *chunk_src, int n, int block,
+                                                 int lane) {
+  constexpr int PPR = D / 4;     // 16-byte pieces per row
+  constexpr int RPB = 64 / PPR;  // rows per 1 KB block
+  const int row = block * RPB + lane / PPR;
+  const int grow = min(row, n - 1);
+  return *reinterpret_cast<const uint4 *>(chunk_src + (int64_t)grow * D + (lane % PPR) * 4);
+}
+
+template <int DK, int DV, int NW>
+struct ChunkRegs {
+  static constexpr int NBQ = DK / 8, NBV = DV / 8, NBL = DK / 4;
+  static_assert(NBQ % NW == 0 && NBV % NW == 0 && NBL % NW == 0, "whole rounds per tensor");
+  static constexpr int NPF = (2 * NBQ + 2 * NBV + NBL) / NW;
+  uint4 r[NPF];
+
+  // tokens [t0, t0 + n) of one sequence-head (pointers at its first token)
+  __device__ __forceinline__ void fetch(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                        const uint16_t *dO, const float *l, int64_t t0, int n,
+                                        int w, int lane) {
+#pragma unroll
+    for (int x = 0; x < NPF; ++x) {
+      const int r0 = NW * x;  // first block of this round
+      const int b = w + r0;
+      if (r0 < NBQ)
+        r[x] = fetch_bf16_block<DK>(q + t0 * DK, n, b, lane);
+      else if (r0 < 2 * NBQ)
+        r[x] = fetch_bf16_block<DK>(k + t0 * DK, n, b - NBQ, lane);
+      else if (r0 < 2 * NBQ + NBV)
+        r[x] = fetch_bf16_block<DV>(v + t0 * DV, n, b - 2 * NBQ, lane);
+      else if (r0 < 2 * NBQ + 2 * NBV)
+        r[x] = fetch_bf16_block<DV>(dO + t0 * DV, n, b - 2 * NBQ - NBV, lane);
+      else
+        r[x] = fetch_f32_block<DK>(l + t0 * DK, n, b - 2 * NBQ - 2 * NBV, lane);
+    }
+  }
+
+  __device__ __forceinline__ void store(unsigned char *QS, unsigned char *KS, unsigned char *VS,
+                                        unsigned char *DOS, unsigned char *CS, int w,
+                                        int lane) const {
+#pragma unroll
+    for (int x = 0; x < NPF; ++x) {
+      const int r0 = NW * x;
+      const int b = w + r0;
+      unsigned char *dst;
+      if (r0 < NBQ)
+        dst = QS + b * 1024;
+      else if (r0 < 2 * NBQ)
+        dst = KS + (b - NBQ) * 1024;
+      else if (r0 < 2 * NBQ + NBV)
+        dst = VS + (b - 2 * NBQ) * 1024;
+      else if (r0 < 2 * NBQ + 2 * NBV)
+        dst = DOS + (b - 2 * NBQ - NBV) * 1024;
+      else
+        dst = CS + (b - 2 * NBQ - 2 * NBV) * 1024;
+      *reinterpret_cast<uint4 *>(dst + lane * 16) = r[x];
+    }
+  }
+};
 
 // In-chunk cumulative logs, in place, with NTH threads (rows past n: no decay).
 template <int DK, int NTH>
@@ -203,8 +288,6 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
   constexpr int B_FT = B_AL + DK * 4;
   constexpr int BUF = B_FT + 10 * DK * 4;
   static_assert(BUF <= 160 * 1024, "LDS");
-  constexpr int NBQ = DK / 8, NBV = DV / 8, NBL = DK / 4;
-  constexpr int NBLK = 2 * NBQ + 2 * NBV + NBL;
   __shared__ __attribute__((aligned(1024))) unsigned char buf[BUF];
   unsigned char *QS = buf, *KS = buf + B_KS, *QH = buf + B_QH, *KH = buf + B_KH;
   unsigned char *VS = buf + B_VS;
@@ -269,25 +352,18 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
     for (int jt = 0; jt < NJT; ++jt) G_acc[jt][dt] = zero4();
   }
 
+  // the first chunk's inputs; every step then fetches the next one
+  ChunkRegs<DK, DV, NW> stage;
+  stage.fetch(qh, kh, vh, doh, lh, c_begin * TC, (int)min<int64_t>(TC, T - c_begin * TC), w, lane);
   for (int64_t ci = c_begin; ci < c_end; ++ci) {
     const int64_t t0 = ci * TC;
     const int n = (int)min<int64_t>(TC, T - t0);
 
-    lds_barrier();
+    lds_barrier();  // the previous chunk's LDS reads are done
     FRESH_LANE();
-    for (int b = w; b < NBLK; b += NW) {
-      if (b < NBQ)
-        dma_block<DK>(qh + t0 * DK, n, QS, b, lane);
-      else if (b < 2 * NBQ)
-        dma_block<DK>(kh + t0 * DK, n, KS, b - NBQ, lane);
-      else if (b < 2 * NBQ + NBV)
-        dma_block<DV>(vh + t0 * DV, n, VS, b - 2 * NBQ, lane);
-      else if (b < 2 * NBQ + 2 * NBV)
-        dma_block<DV>(doh + t0 * DV, n, DOS, b - 2 * NBQ - NBV, lane);
-      else
-        dma_f32_rows<DK>(lh + t0 * DK, n, buf + B_CS, b - 2 * NBQ - 2 * NBV, lane);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
+    stage.store(QS, KS, VS, DOS, buf + B_CS, w, lane);
+    if (ci + 1 < c_end)
+      stage.fetch(qh, kh, vh, doh, lh, t0 + TC, (int)min<int64_t>(TC, T - t0 - TC), w, lane);
     lds_barrier();
     FRESH_LANE();
     cumsum_rows<DK, NT>(CS, n, tid);
