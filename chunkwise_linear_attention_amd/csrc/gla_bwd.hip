@@ -48,6 +48,17 @@ namespace {
 constexpr float kBadLog = 60.f;  // as in the forward
 constexpr int BTHR = 512;
 
+// The [64 x DK] fp32 cumulative logs in LDS: row r's 16-byte pieces are
+// XOR-swizzled by r & 15 (piece p held at p ^ (r & 15)), so that the 16 rows
+// a 16-lane group reads at one column fall in different banks (the plain
+// layout put all of them, 512 bytes apart, in the same bank).  Index of
+// element (r, d):
+template <int DK>
+__device__ __forceinline__ int csx(int r, int d) {
+  static_assert(DK >= 64, "at least 16 pieces per row");
+  return r * DK + ((((d >> 2) ^ (r & 15)) << 2) | (d & 3));
+}
+
 // v_mfma_f32_16x16x16_bf16: lane 16 lg + li holds A row li and B column li,
 // k-values 4 lg .. 4 lg + 3; C as for the 32-deep instruction.
 typedef short __attribute__((ext_vector_type(4))) s16x4;
@@ -73,8 +84,8 @@ __device__ __forceinline__ float path_term(float b, float q, float k, float ct, 
   return ((b * q) * k) * __expf(ct - cs);
 }
 
-// DMA of a [64 x D] fp32 tile, rows plain (unswizzled): 1 KB blocks of RPB
-// rows; rows past the chunk re-read row n - 1.
+// DMA of the [64 x D] fp32 log tile in the swizzled layout of csx: 1 KB
+// blocks of RPB rows; rows past the chunk re-read row n - 1.
 template <int D>
 __device__ __forceinline__ void dma_f32_rows(const float *chunk_src, int n, unsigned char *tile,
                                              int block, int lane) {
@@ -82,7 +93,9 @@ __device__ __forceinline__ void dma_f32_rows(const float *chunk_src, int n, unsi
   constexpr int RPB = 64 / PPR;
   const int row = block * RPB + lane / PPR;
   const int grow = min(row, n - 1);
-  __builtin_amdgcn_global_load_lds(chunk_src + (int64_t)grow * D + (lane % PPR) * 4,
+  // this lane lands at piece lane % PPR of the row: it fetches the piece the
+  // row's swizzle puts there
+  __builtin_amdgcn_global_load_lds(chunk_src + (int64_t)grow * D + (((lane % PPR) ^ (row & 15)) * 4),
                                    (lds_void *)(tile + block * 1024), 16, 0, 0);
 }
 
@@ -92,7 +105,8 @@ __device__ __forceinline__ void dma_f32_rows(const float *chunk_src, int n, unsi
 // registers while the current one is worked on and written to LDS between
 // the two.  The LDS layout is the 1 KB-block layout of the DMA staging of the
 // scalar kernels (lane i holds bytes 16 i .. 16 i + 15 of its block): q, k,
-// v, dO as swizzled bf16 tiles, then the [64 x DK] fp32 log rows, plain.
+// v, dO as swizzled bf16 tiles, then the [64 x DK] fp32 log rows (swizzled as
+// csx describes).
 // Wave w holds blocks w, w + NW, ...; each tensor's block count is a multiple
 // of NW, so the tensor of every held block is known at compile time.  Rows
 // past the chunk's n tokens re-read row n - 1 (finite data, masked later).
@@ -115,7 +129,8 @@ __device__ __forceinline__ uint4 fetch_f32_block(const float *chunk_src, int n, 
   constexpr int RPB = 64 / PPR;  // rows per 1 KB block
   const int row = block * RPB + lane / PPR;
   const int grow = min(row, n - 1);
-  return *reinterpret_cast<const uint4 *>(chunk_src + (int64_t)grow * D + (lane % PPR) * 4);
+  return *reinterpret_cast<const uint4 *>(chunk_src + (int64_t)grow * D +
+                                          (((lane % PPR) ^ (row & 15)) * 4));
 }
 
 template <int DK, int DV, int NW>
@@ -178,16 +193,16 @@ __device__ __forceinline__ void cumsum_rows(float *CS, int n, int tid) {
 #pragma unroll
   for (int i = 0; i < RP; ++i) {
     const int r = part * RP + i;
-    run += r < n ? CS[r * DK + d] : 0.f;
-    CS[r * DK + d] = run;
+    run += r < n ? CS[csx<DK>(r, d)] : 0.f;
+    CS[csx<DK>(r, d)] = run;
   }
   lds_barrier();
   float off = 0.f;
-  for (int p = 0; p < part; ++p) off += CS[(p * RP + RP - 1) * DK + d];
+  for (int p = 0; p < part; ++p) off += CS[csx<DK>(p * RP + RP - 1, d)];
   lds_barrier();
   if (part > 0) {
 #pragma unroll
-    for (int i = 0; i < RP; ++i) CS[(part * RP + i) * DK + d] += off;
+    for (int i = 0; i < RP; ++i) CS[csx<DK>(part * RP + i, d)] += off;
   }
   lds_barrier();
 }
@@ -205,27 +220,27 @@ __device__ __forceinline__ void prep_scaled(const unsigned char *QS, const unsig
     const int r = g / NCK, c8 = g % NCK;
     const int B = r >> 4;
     const int off = swz_off<NCK>(r, c8);
-    const float *cr = CS + r * DK + 8 * c8;
-    const float *ce = CS + (16 * B + 15) * DK + 8 * c8;
-    const float *cb = CS + (16 * B - 1) * DK + 8 * c8;
+    const int re = 16 * B + 15, rb = 16 * B - 1;
     const bf16x8 kv = *reinterpret_cast<const bf16x8 *>(KS + off);
     float yk[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) yk[e] = r < n ? tof(kv[e]) * __expf(ce[e] - cr[e]) : 0.f;
+    for (int e = 0; e < 8; ++e) yk[e] = r < n ? tof(kv[e]) * __expf(CS[csx<DK>(re, 8 * c8 + e)] - CS[csx<DK>(r, 8 * c8 + e)]) : 0.f;
     *reinterpret_cast<bf16x8 *>(KH + off) = cvt8(yk);
     if (QH) {
       const bf16x8 qv = *reinterpret_cast<const bf16x8 *>(QS + off);
       float yq[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        yq[e] = r < n ? tof(qv[e]) * __expf(cr[e] - (B > 0 ? cb[e] : 0.f)) : 0.f;
+        yq[e] = r < n ? tof(qv[e]) * __expf(CS[csx<DK>(r, 8 * c8 + e)] -
+                                            (B > 0 ? CS[csx<DK>(rb, 8 * c8 + e)] : 0.f))
+                      : 0.f;
       *reinterpret_cast<bf16x8 *>(QH + off) = cvt8(yq);
     }
   }
   for (int d = tid; d < DK; d += NTH) {
     float ce[4];
 #pragma unroll
-    for (int B = 0; B < 4; ++B) ce[B] = CS[(16 * B + 15) * DK + d];
+    for (int B = 0; B < 4; ++B) ce[B] = CS[csx<DK>(16 * B + 15, d)];
 #pragma unroll
     for (int B = 0; B < 4; ++B) {
       FQ[B * DK + d] = B > 0 ? __expf(ce[B - 1]) : 1.f;
@@ -247,8 +262,8 @@ __device__ __forceinline__ void block_factors(const float *CS, float *FT, int ti
     const int p = g / DK, d = g % DK;
     const int R = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0;
     const int S = p - R * (R + 1) / 2;
-    const float cb = R > 0 ? CS[(16 * R - 1) * DK + d] : 0.f;
-    FT[g] = __expf(cb - CS[(16 * S + 15) * DK + d]);
+    const float cb = R > 0 ? CS[csx<DK>(16 * R - 1, d)] : 0.f;
+    FT[g] = __expf(cb - CS[csx<DK>(16 * S + 15, d)]);
   }
 }
 
@@ -257,8 +272,8 @@ template <int DK>
 __device__ __forceinline__ bool block_bad(const float *CS, int R, int lane) {
   bool bad = false;
   for (int d = lane; d < DK; d += 64) {
-    const float cb = R > 0 ? CS[(16 * R - 1) * DK + d] : 0.f;
-    bad |= cb - CS[(16 * R + 15) * DK + d] > kBadLog;
+    const float cb = R > 0 ? CS[csx<DK>(16 * R - 1, d)] : 0.f;
+    bad |= cb - CS[csx<DK>(16 * R + 15, d)] > kBadLog;
   }
   return __ballot(bad) != 0;
 }
@@ -437,8 +452,8 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int d = dc + i;
-            const float cb = R > 0 ? CS[(16 * R - 1) * DK + d] : 0.f;
-            const float u = __expf(CS[r * DK + d] - cb);
+            const float cb = R > 0 ? CS[csx<DK>(16 * R - 1, d)] : 0.f;
+            const float u = __expf(CS[csx<DK>(r, d)] - cb);
             const float inter = FQ[R * DK + d] * acc2[i] * u;
             float v = accI[i] * u + inter;
             float rv = tof(qhv[i]) * accI[i] + tof(qv[i]) * inter;
@@ -451,8 +466,8 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
                     BS + swz_off<8>(r, s2 >> 3) + (s2 & 7) * 2));
                 const float kd = tof(*reinterpret_cast<const __bf16 *>(
                     KS + swz_off<NCK>(s2, d >> 3) + (d & 7) * 2));
-                v += (bsc * kd) * __expf(CS[r * DK + d] - CS[s2 * DK + d]);
-                rv += path_term(bsc, qd, kd, CS[r * DK + d], CS[s2 * DK + d]);
+                v += (bsc * kd) * __expf(CS[csx<DK>(r, d)] - CS[csx<DK>(s2, d)]);
+                rv += path_term(bsc, qd, kd, CS[csx<DK>(r, d)], CS[csx<DK>(s2, d)]);
               }
             }
             out[i] = v;
@@ -493,12 +508,12 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
         for (int dt = 0; dt < NDT; ++dt) {
           const int d = d0 + 16 * dt + li;
           const bf16x8 x = tr_frag<NCK>(KS, 32 * kb, d0 + 16 * dt, li, lg);
-          const float cn = CS[63 * DK + d];
+          const float cn = CS[csx<DK>(63, d)];
           float y[8], z[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int s = 32 * kb + 8 * lg + e;
-            y[e] = s < n ? tof(x[e]) * __expf(cn - CS[s * DK + d]) : 0.f;
+            y[e] = s < n ? tof(x[e]) * __expf(cn - CS[csx<DK>(s, d)]) : 0.f;
           }
           kg[dt] = cvt8(y);
 #pragma unroll
@@ -531,7 +546,7 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int t = 32 * kb + 8 * lg + e;
-            y[e] = t < n ? tof(x[e]) * (apre[dt] * __expf(CS[t * DK + d])) : 0.f;
+            y[e] = t < n ? tof(x[e]) * (apre[dt] * __expf(CS[csx<DK>(t, d)])) : 0.f;
           }
           qa[dt] = cvt8(y);
         }
@@ -776,7 +791,7 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                       sum += tof(qv[e]) * tof(kv[e]) *
-                             __expf(CS[r * DK + dd + e] - CS[s * DK + dd + e]);
+                             __expf(CS[csx<DK>(r, dd + e)] - CS[csx<DK>(s, dd + e)]);
                   }
                 }
                 acc[i] = sum;
@@ -900,8 +915,8 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int d = dc + i;
-            const float csd = CS[s * DK + d];
-            const float ue = __expf(CS[(16 * S + 15) * DK + d] - csd);
+            const float csd = CS[csx<DK>(s, d)];
+            const float ue = __expf(CS[csx<DK>(16 * S + 15, d)] - csd);
             const float inter = FK[S * DK + d] * acc2[i] * ue;
             float v = accI[i] * ue + inter;
             float rv = tof(khv[i]) * accI[i] + tof(kv[i]) * inter;
@@ -912,8 +927,8 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
                     BS + swz_off<8>(s, r >> 3) + (r & 7) * 2));
                 const float qd = tof(*reinterpret_cast<const __bf16 *>(
                     QS + swz_off<NCK>(r, d >> 3) + (d & 7) * 2));
-                v += (bsc * qd) * __expf(CS[r * DK + d] - csd);
-                rv += path_term(bsc, qd, kd, CS[r * DK + d], csd);
+                v += (bsc * qd) * __expf(CS[csx<DK>(r, d)] - csd);
+                rv += path_term(bsc, qd, kd, CS[csx<DK>(r, d)], csd);
               }
             }
             out[i] = v;
