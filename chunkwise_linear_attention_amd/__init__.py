@@ -21,6 +21,11 @@ step of the computation runs in the library's HIP kernels.
     y, hT, ckpt        = selective_scan(x, delta, A, Bm, Cm, h0=None, save_ckpt=True)
     dx, ddelta, dA, dB, dC, dh0 = selective_scan_bwd(x, delta, A, Bm, Cm, h0, dy, ckpt=ckpt)
 
+    # decays the chunkwise calls do not accept (NaN, +inf; for gla also > 0
+    # and -inf), counted on the device; set_input_checks(True) runs the check
+    # at the start of chunked_linear_attn[_bwd] and gla[_bwd]
+    check_log_decay(log_decay, kind="scalar" | "gla")
+
     # autograd: chunkwise_linear_attention_amd.autograd.{scan_fn,
     # chunked_linear_attn_fn, gla_fn, selective_scan_fn}
 """
@@ -28,6 +33,9 @@ step of the computation runs in the library's HIP kernels.
 from . import autograd  # noqa: F401
 from ._lib import ClaError, lib  # noqa: F401
 from .api import (  # noqa: F401
+    check_log_decay,
+    log_decay_counts,
+    set_input_checks,
     chunked_linear_attn,
     chunked_linear_attn_bwd,
     scan,
@@ -49,4 +57,5 @@ from .api import (  # noqa: F401
 __all__ = ["scan", "scan_bwd", "scan_fwd_noalloc", "chunked_linear_attn", "chunked_linear_attn_bwd",
            "scan_workspace_bytes", "chunk_workspace_bytes", "chunk_saved_bytes", "gla", "gla_bwd", "gla_saved_bytes",
            "gla_workspace_bytes", "selective_scan", "selective_scan_bwd", "sscan_ckpt_bytes",
-           "sscan_workspace_bytes", "ClaError"]
+           "sscan_workspace_bytes", "check_log_decay", "log_decay_counts", "set_input_checks",
+           "ClaError"]

@@ -38,6 +38,7 @@ sz = ctypes.c_size_t
 SIGNATURES = {
     "cla_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "cla_version": ([], ctypes.c_char_p),
+    "cla_check_log_decay": ([p, i64, p, p], ctypes.c_int),
     "cla_scan_workspace_bytes": ([i64, i64, i64], sz),
     "cla_scan_fwd": ([p, p, p, p, p, i64, i64, i64, p, sz, p], ctypes.c_int),
     "cla_scan_fwd_noalloc": ([p, p, p, p, p, i64, i64, i64, p], ctypes.c_int),

@@ -46,6 +46,53 @@ def _workspace(nbytes, device):
 
 
 # ---------------------------------------------------------------------------
+# log-decay checks
+# ---------------------------------------------------------------------------
+
+_CHECK_INPUTS = False
+
+
+def set_input_checks(on: bool) -> bool:
+    """With on=True, chunked_linear_attn[_bwd] and gla[_bwd] first run
+    check_log_decay on their log decays (a pass over the tensor and a
+    synchronization; off by default).  Returns the previous setting."""
+    global _CHECK_INPUTS
+    prev, _CHECK_INPUTS = _CHECK_INPUTS, bool(on)
+    return prev
+
+
+def log_decay_counts(log_decay) -> dict:
+    """Numbers of NaN, +inf, finite positive and -inf values in a fp32 device
+    tensor, counted on the device (cla_check_log_decay)."""
+    if not isinstance(log_decay, torch.Tensor) or log_decay.dtype != torch.float32:
+        raise TypeError("log_decay must be a float32 torch.Tensor")
+    if not log_decay.is_contiguous():
+        raise ValueError("log_decay must be contiguous")
+    dev = log_decay.device
+    counts = torch.empty(4, dtype=torch.int32, device=dev)
+    st = _lib.lib().cla_check_log_decay(_ptr(log_decay), log_decay.numel(), _ptr(counts),
+                                        _stream(dev))
+    _lib.check("cla_check_log_decay", st)
+    c = [int(x) & 0xFFFFFFFF for x in counts.cpu().tolist()]
+    return {"nan": c[0], "posinf": c[1], "positive": c[2], "neginf": c[3]}
+
+
+def check_log_decay(log_decay, kind: str = "scalar") -> None:
+    """Raise ValueError if log_decay holds values the chunkwise calls do not
+    accept: NaN or +inf for the scalar decay (kind="scalar"); anything but
+    finite values <= 0 for one decay per key dimension (kind="gla")."""
+    if kind not in ("scalar", "gla"):
+        raise ValueError("kind must be 'scalar' or 'gla'")
+    c = log_decay_counts(log_decay)
+    bad = ("nan", "posinf") if kind == "scalar" else ("nan", "posinf", "positive", "neginf")
+    found = {k: c[k] for k in bad if c[k]}
+    if found:
+        rule = ("finite or -inf" if kind == "scalar" else "finite and <= 0")
+        raise ValueError(f"log_decay must be {rule}; found " +
+                         ", ".join(f"{v} {k}" for k, v in found.items()))
+
+
+# ---------------------------------------------------------------------------
 # diagonal scan
 # ---------------------------------------------------------------------------
 
@@ -149,6 +196,8 @@ def chunked_linear_attn(q, k, v, log_decay, S0=None, *, want_final=True,
     _need(k, "k", torch.bfloat16, (B, H, T, DK), dev)
     _need(v, "v", torch.bfloat16, (B, H, T, DV), dev)
     _need(log_decay, "log_decay", torch.float32, (B, H, T), dev)
+    if _CHECK_INPUTS:
+        check_log_decay(log_decay, "scalar")
     _opt(S0, "S0", torch.float32, (B, H, DK, DV), dev)
     o = torch.empty((B, H, T, DV), dtype=torch.bfloat16, device=dev)
     ST = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev) if want_final else None
@@ -184,6 +233,8 @@ def chunked_linear_attn_bwd(q, k, v, log_decay, S0, dO, dST=None, *, want_dS0=Tr
     _need(k, "k", torch.bfloat16, (B, H, T, DK), dev)
     _need(v, "v", torch.bfloat16, (B, H, T, DV), dev)
     _need(log_decay, "log_decay", torch.float32, (B, H, T), dev)
+    if _CHECK_INPUTS:
+        check_log_decay(log_decay, "scalar")
     _opt(S0, "S0", torch.float32, (B, H, DK, DV), dev)
     _need(dO, "dO", torch.bfloat16, (B, H, T, DV), dev)
     _opt(dST, "dST", torch.float32, (B, H, DK, DV), dev)
@@ -243,6 +294,8 @@ def gla(q, k, v, log_decay, S0=None, *, want_final=True, chunk=CHUNK, workspace=
     _need(k, "k", torch.bfloat16, (B, H, T, DK), dev)
     _need(v, "v", torch.bfloat16, (B, H, T, DV), dev)
     _need(log_decay, "log_decay", torch.float32, (B, H, T, DK), dev)
+    if _CHECK_INPUTS:
+        check_log_decay(log_decay, "gla")
     _opt(S0, "S0", torch.float32, (B, H, DK, DV), dev)
     o = torch.empty((B, H, T, DV), dtype=torch.bfloat16, device=dev)
     ST = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev) if want_final else None
@@ -278,6 +331,8 @@ def gla_bwd(q, k, v, log_decay, S0, dO, dST=None, *, want_dS0=True, chunk=CHUNK,
     _need(k, "k", torch.bfloat16, (B, H, T, DK), dev)
     _need(v, "v", torch.bfloat16, (B, H, T, DV), dev)
     _need(log_decay, "log_decay", torch.float32, (B, H, T, DK), dev)
+    if _CHECK_INPUTS:
+        check_log_decay(log_decay, "gla")
     _opt(S0, "S0", torch.float32, (B, H, DK, DV), dev)
     _need(dO, "dO", torch.bfloat16, (B, H, T, DV), dev)
     _opt(dST, "dST", torch.float32, (B, H, DK, DV), dev)

@@ -63,6 +63,17 @@ const char *cla_status_string(int status) {
 
 const char *cla_version(void) { return "cla 0.1 gfx950"; }
 
+int cla_check_log_decay(const float *log_decay, int64_t n, uint32_t *counts,
+                        cla_stream_t stream) {
+  if (n < 0) return CLA_ERR_BAD_SHAPE;
+  if (!counts || (n > 0 && !log_decay)) return CLA_ERR_NULL_ARG;
+  if ((reinterpret_cast<uintptr_t>(counts) & 3) != 0) return CLA_ERR_UNSUPPORTED;
+  if (any_alias({{log_decay, (size_t)n * sizeof(float)}}, {{counts, 4 * sizeof(uint32_t)}}))
+    return CLA_ERR_ALIAS;
+  return hip_status(
+      cla::launch_check_log_decay(log_decay, n, counts, reinterpret_cast<hipStream_t>(stream)));
+}
+
 // ---------------------------------------------------------------------------
 // diagonal scan
 // ---------------------------------------------------------------------------

@@ -68,6 +68,11 @@ hipError_t launch_scan_fwd_noalloc(const float *a, const float *b, const float *
                                    int64_t D, const ScanPlan &plan,
                                    hipStream_t stream);
 
+// counts[0..3] = the numbers of NaN, +inf, finite positive and -inf values
+// among l[0..n) (counts zeroed by a kernel of its own first).
+hipError_t launch_check_log_decay(const float *l, int64_t n, uint32_t *counts,
+                                  hipStream_t stream);
+
 // dst[i] = src ? src[i] : 0 for i < n (empty-sequence final states).
 hipError_t launch_copy_or_zero(float *dst, const float *src, int64_t n,
                                hipStream_t stream);

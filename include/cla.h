@@ -66,6 +66,32 @@ const char *cla_status_string(int status);
 /* Library version string, e.g. "cla 0.1 gfx950". */
 const char *cla_version(void);
 
+/*
+ * Counts, on the device, the log-decay values that the chunkwise entry points
+ * do not accept; those calls do not check their decays (a check would cost a
+ * pass over the tensor and a synchronization in every call), and such values
+ * give wrong results without an error.  In the chunkwise forms the in-chunk
+ * decay products are exponentials of differences of cumulative log decays
+ * ("Parallel scan", section "The chunkwise algorithm"; "Lightning
+ * Attention-2", Eq. 10): one NaN or +inf spoils every later token of its
+ * chunk and state.
+ *   log_decay : n fp32 values (device), any layout.
+ *   counts    : 4 uint32 (device, 4-byte aligned), overwritten with the
+ *               numbers of NaN, +inf, finite > 0, and -inf values, in that
+ *               order (each wraps past 2^32 - 1).
+ * Scalar decays (cla_chunk_*) need counts[0] = counts[1] = 0 (-inf is an
+ * exact reset, finite l > 0 a growth factor, both computed exactly).  One
+ * decay per key dimension (cla_gla_*) needs all four 0: finite l <= 0, since
+ * its 16-token block factors exp(c) and exp(-c) stay bounded only for decays
+ * at most 1, and it has no reset.  Asynchronous like every call: counts are
+ * valid once the stream reaches this point.  Errors: n < 0 ->
+ * CLA_ERR_BAD_SHAPE; counts NULL, or log_decay NULL with n > 0 ->
+ * CLA_ERR_NULL_ARG; counts misaligned -> CLA_ERR_UNSUPPORTED; counts inside
+ * log_decay -> CLA_ERR_ALIAS.
+ */
+int cla_check_log_decay(const float *log_decay, int64_t n, uint32_t *counts,
+                        cla_stream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Diagonal state                                                            */
 /* ------------------------------------------------------------------------ */
@@ -158,7 +184,8 @@ size_t cla_chunk_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t DK,
  *               the in-chunk decays are formed from finite partial sums and
  *               a count of resets, the additions-only segment sums of
  *               "Parallel scan", section "Long products without underflow").
- *               NaN and +inf are not allowed (not checked).
+ *               NaN and +inf are not allowed (not checked here;
+ *               cla_check_log_decay counts them).
  *   S0        : [B, H, DK, DV] fp32 initial state, or NULL for zeros.
  *   o         : [B, H, T, DV] bf16 output.
  *   ST        : [B, H, DK, DV] fp32 final state, or NULL to skip.
@@ -262,7 +289,8 @@ int cla_timing_read(const char **names, double *total_ms, int64_t *counts, int m
  *   S_t = diag(a_t) S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t.
  *   q, k      : [B, H, T, DK] bf16;  v, o : [B, H, T, DV] bf16.
  *   log_decay : [B, H, T, DK] fp32, finite and <= 0 (decays in (0, 1]; not
- *               checked), 16-byte aligned.
+ *               checked here: cla_check_log_decay counts the values outside
+ *               that range), 16-byte aligned.
  *   S0, ST    : [B, H, DK, DV] fp32 (S0 NULL = zeros; ST NULL = not written).
  *   DK, DV in {64, 128}; chunk must be 64; the bf16 tensors and log_decay
  *   must be 16-byte aligned (CLA_ERR_UNSUPPORTED otherwise).

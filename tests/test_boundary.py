@@ -101,6 +101,16 @@ def test_scan_fwd_validation(lib):
     assert f(None, None, None, None, None, 3, 4, 0, None, 0, None) == OK
 
 
+def test_check_log_decay_validation(lib):
+    f = lib.cla_check_log_decay
+    assert f(A, -1, B_, None) == SHAPE
+    assert f(A, 16, None, None) == NULL
+    assert f(None, 16, B_, None) == NULL
+    assert f(A, 16, B_ + 2, None) == UNSUP        # counts not 4-byte aligned
+    assert f(A, 16, A + 8, None) == ALIAS         # counts inside the decays
+    assert f(A, 16, A + 60, None) == ALIAS        # overlapping the last value
+
+
 def test_scan_fwd_noalloc_validation(lib):
     f = lib.cla_scan_fwd_noalloc
     assert f(A, B_, None, C, None, -1, 4, 4, None) == SHAPE
