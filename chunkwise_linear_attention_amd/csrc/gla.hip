@@ -51,8 +51,8 @@ namespace {
 // diagonal scores are computed elementwise.
 constexpr float kBadLog = 60.f;
 
-// DMA of a [64 x D] fp32 tile, rows plain (unswizzled): 1 KB blocks of RPB
-// rows; rows past the chunk re-read row n - 1.
+// DMA of the [64 x D] fp32 log tile in the swizzled layout of csx: 1 KB
+// blocks of RPB rows; rows past the chunk re-read row n - 1.
 template <int D>
 __device__ __forceinline__ void dma_f32_block(const float *chunk_src, int n, unsigned char *tile,
                                               int block, int lane) {
@@ -60,7 +60,9 @@ __device__ __forceinline__ void dma_f32_block(const float *chunk_src, int n, uns
   constexpr int RPB = 64 / PPR;  // rows per 1 KB block
   const int row = block * RPB + lane / PPR;
   const int grow = min(row, n - 1);
-  __builtin_amdgcn_global_load_lds(chunk_src + (int64_t)grow * D + (lane % PPR) * 4,
+  // this lane lands at piece lane % PPR of the row: it fetches the piece the
+  // row's swizzle (csx) puts there
+  __builtin_amdgcn_global_load_lds(chunk_src + (int64_t)grow * D + (((lane % PPR) ^ (row & 15)) * 4),
                                    (lds_void *)(tile + block * 1024), 16, 0, 0);
 }
 
@@ -183,16 +185,16 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
 #pragma unroll
       for (int i = 0; i < RP; ++i) {
         const int r = part * RP + i;
-        run += r < n ? CS[r * DK + d] : 0.f;  // rows past the chunk: no decay
-        CS[r * DK + d] = run;
+        run += r < n ? CS[csx<DK>(r, d)] : 0.f;  // rows past the chunk: no decay
+        CS[csx<DK>(r, d)] = run;
       }
       lds_barrier();
       float off = 0.f;
-      for (int p = 0; p < part; ++p) off += CS[(p * RP + RP - 1) * DK + d];
+      for (int p = 0; p < part; ++p) off += CS[csx<DK>(p * RP + RP - 1, d)];
       lds_barrier();
       if (part > 0) {
 #pragma unroll
-        for (int i = 0; i < RP; ++i) CS[(part * RP + i) * DK + d] += off;
+        for (int i = 0; i < RP; ++i) CS[csx<DK>(part * RP + i, d)] += off;
       }
       lds_barrier();
     }
@@ -203,19 +205,19 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
       const int r = g / NCK, c8 = g % NCK;
       const int B = r >> 4;
       const int off = swz_off<NCK>(r, c8);
-      const float *cr = CS + r * DK + 8 * c8;
-      const float *ce = CS + (16 * B + 15) * DK + 8 * c8;
-      const float *cb = CS + (16 * B - 1) * DK + 8 * c8;  // read only when B > 0
+      const int re = 16 * B + 15, rb = 16 * B - 1;  // rb read only when B > 0
       bf16x8 kv = *reinterpret_cast<const bf16x8 *>(KS + off);
       float yk[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) yk[e] = r < n ? tof(kv[e]) * __expf(ce[e] - cr[e]) : 0.f;
+      for (int e = 0; e < 8; ++e)
+        yk[e] = r < n ? tof(kv[e]) * __expf(CS[csx<DK>(re, 8 * c8 + e)] - CS[csx<DK>(r, 8 * c8 + e)]) : 0.f;
       *reinterpret_cast<bf16x8 *>(KS + off) = cvt8(yk);
       if (OUT) {
         bf16x8 qv = *reinterpret_cast<const bf16x8 *>(QS + off);
         float yq[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) yq[e] = tof(qv[e]) * __expf(cr[e] - (B > 0 ? cb[e] : 0.f));
+        for (int e = 0; e < 8; ++e)
+          yq[e] = tof(qv[e]) * __expf(CS[csx<DK>(r, 8 * c8 + e)] - (B > 0 ? CS[csx<DK>(rb, 8 * c8 + e)] : 0.f));
         *reinterpret_cast<bf16x8 *>(QS + off) = cvt8(yq);
       }
     }
@@ -251,8 +253,8 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
       if (R == S) {
         bool bad = false;
         for (int d = lane; d < DK; d += 64) {
-          const float cbd = R > 0 ? CS[(16 * R - 1) * DK + d] : 0.f;
-          bad |= cbd - CS[(16 * R + 15) * DK + d] > kBadLog;
+          const float cbd = R > 0 ? CS[csx<DK>(16 * R - 1, d)] : 0.f;
+          bad |= cbd - CS[csx<DK>(16 * R + 15, d)] > kBadLog;
         }
         exact = __ballot(bad) != 0;
       }
@@ -266,8 +268,8 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
           const int idx = 2 * li + h;  // (kk, e) = (idx / 8, idx % 8)
           const int d = 32 * (idx >> 3) + 8 * lg + (idx & 7);
           if (idx < DK / 4) {
-            const float cb = R > 0 ? CS[(16 * R - 1) * DK + d] : 0.f;
-            fpair[h] = __expf(cb - CS[(16 * S + 15) * DK + d]);
+            const float cb = R > 0 ? CS[csx<DK>(16 * R - 1, d)] : 0.f;
+            fpair[h] = __expf(cb - CS[csx<DK>(16 * S + 15, d)]);
           } else {
             fpair[h] = 0.f;
           }
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
 #pragma unroll
               for (int e = 0; e < 8; ++e)
                 sum += tof(qv[e]) * tof(kv[e]) *
-                       __expf(CS[r * DK + d0 + e] - CS[s * DK + d0 + e]);
+                       __expf(CS[csx<DK>(r, d0 + e)] - CS[csx<DK>(s, d0 + e)]);
             }
           }
           acc[i] = sum;
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
     for (int d = tid; d < DK; d += NTHR) {
       float ce[4];
 #pragma unroll
-      for (int B = 0; B < 4; ++B) ce[B] = CS[(16 * B + 15) * DK + d];
+      for (int B = 0; B < 4; ++B) ce[B] = CS[csx<DK>(16 * B + 15, d)];
       const float cl = ce[3];  // the chunk's last cumulative log (rows past n add 0)
       if (!OUT) lsum += cl;
 #pragma unroll

@@ -48,17 +48,6 @@ namespace {
 constexpr float kBadLog = 60.f;  // as in the forward
 constexpr int BTHR = 512;
 
-// The [64 x DK] fp32 cumulative logs in LDS: row r's 16-byte pieces are
-// XOR-swizzled by r & 15 (piece p held at p ^ (r & 15)), so that the 16 rows
-// a 16-lane group reads at one column fall in different banks (the plain
-// layout put all of them, 512 bytes apart, in the same bank).  Index of
-// element (r, d):
-template <int DK>
-__device__ __forceinline__ int csx(int r, int d) {
-  static_assert(DK >= 64, "at least 16 pieces per row");
-  return r * DK + ((((d >> 2) ^ (r & 15)) << 2) | (d & 3));
-}
-
 // v_mfma_f32_16x16x16_bf16: lane 16 lg + li holds A row li and B column li,
 // k-values 4 lg .. 4 lg + 3; C as for the 32-deep instruction.
 typedef short __attribute__((ext_vector_type(4))) s16x4;

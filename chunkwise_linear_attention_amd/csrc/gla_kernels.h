@@ -8,6 +8,17 @@
 namespace cla {
 namespace gla {
 
+// The [64 x DK] fp32 cumulative logs in LDS: row r's 16-byte pieces are
+// XOR-swizzled by r & 15 (piece p held at p ^ (r & 15)), so that the 16 rows
+// a 16-lane group reads at one column fall in different banks (the plain
+// layout put all of them, 512 bytes apart, in the same bank).  Index of
+// element (r, d):
+template <int DK>
+__host__ __device__ __forceinline__ int csx(int r, int d) {
+  static_assert(DK >= 64, "at least 16 pieces per row");
+  return r * DK + ((((d >> 2) ^ (r & 15)) << 2) | (d & 3));
+}
+
 // The backward's decay gradient sums q.dq - k.dk backwards inside blocks of
 // this many chunks, each started from the boundary term <S, G>.  Segments of
 // the sequence that run on separate workgroups are whole multiples of it.
