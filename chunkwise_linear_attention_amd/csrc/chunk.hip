@@ -201,12 +201,17 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     // the per-lane DMA addresses are formed here, at each stage, instead of
     // being kept live (one 64-bit pair per staged tensor) across the loop
     const int ln = fresh(lane);
-    for (int b = w; b < nblk; b += NWAVE) {
-      if (b < NBQ) {
+    // wave w takes blocks w, w + NWAVE, ...; every tensor's block count is a
+    // multiple of NWAVE, so the tensor of each round is known at compile time
+    static_assert(NBQ % NWAVE == 0 && NBK % NWAVE == 0 && NBV % NWAVE == 0, "rounds");
+#pragma unroll
+    for (int r0 = 0; r0 < NBQ + NBK + NBV + (XD ? NBV : 0); r0 += NWAVE) {
+      const int b = w + r0;
+      if (r0 < NBQ) {
         dma_block<DK>(qh + tj * DK, nj, buf, b, ln);
-      } else if (b < NBQ + NBK) {
+      } else if (r0 < NBQ + NBK) {
         dma_block<DK>(kh + tj * DK, nj, buf + B_KS, b - NBQ, ln);
-      } else if (b < NBQ + NBK + NBV) {
+      } else if (r0 < NBQ + NBK + NBV) {
         dma_block<DV>(vh + tj * DV, nj, buf + B_VS, b - NBQ - NBK, ln);
       } else {
         dma_block<DV>(xh + tj * DV, nj, buf + B_XS, b - NBQ - NBK - NBV, ln);
@@ -619,8 +624,11 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_state_kernel(FwdArgs a) {
   auto stage = [&](int64_t cj, unsigned char *buf) __attribute__((always_inline)) {
     const int64_t tj = cj * TC;
     const int nj = (int)min<int64_t>(TC, T - tj);
-    for (int b = w; b < NBLK; b += NWAVE) {
-      if (b < NBK)
+    static_assert(NBK % NWAVE == 0 && NBV % NWAVE == 0, "rounds");
+#pragma unroll
+    for (int r0 = 0; r0 < NBLK; r0 += NWAVE) {
+      const int b = w + r0;
+      if (r0 < NBK)
         dma_block<DK>(kh + tj * DK, nj, buf, b, lane);
       else
         dma_block<DV>(vh + tj * DV, nj, buf + B_VS, b - NBK, lane);

@@ -206,12 +206,18 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
     // the per-lane DMA addresses are formed here, at each stage, instead of
     // being kept live (one 64-bit pair per staged tensor) across the loop
     const int ln = fresh(lane);
-    for (int b = w; b < NBLK; b += BTHR / 64) {
-      if (b < NBQ) {
+    // wave w takes blocks w, w + 8, ...; every tensor's block count is a
+    // multiple of 8, so the tensor of each round is known at compile time
+    constexpr int NW = BTHR / 64;
+    static_assert(NBQ % NW == 0 && NBD % NW == 0 && NBK % NW == 0 && NBV % NW == 0, "rounds");
+#pragma unroll
+    for (int r0 = 0; r0 < NBLK; r0 += NW) {
+      const int b = w + r0;
+      if (r0 < NBQ) {
         dma_block<DK>(qh + tj * DK, nj, buf, b, ln);
-      } else if (b < NBQ + NBD) {
+      } else if (r0 < NBQ + NBD) {
         dma_block<DV>(doh + tj * DV, nj, buf + B_DOS, b - NBQ, ln);
-      } else if (b < NBQ + NBD + NBK) {
+      } else if (r0 < NBQ + NBD + NBK) {
         dma_block<DK>(kh + tj * DK, nj, buf + B_KS, b - NBQ - NBD, ln);
       } else {
         dma_block<DV>(vh + tj * DV, nj, buf + B_VS, b - NBQ - NBD - NBK, ln);
