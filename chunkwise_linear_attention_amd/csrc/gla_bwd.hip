@@ -205,7 +205,10 @@ __device__ __forceinline__ void prep_scaled(const unsigned char *QS, const unsig
                                             unsigned char *QH, unsigned char *KH, const float *CS,
                                             float *FQ, float *FK, float *AL, int n, int tid) {
   constexpr int NCK = DK / 8;
-  for (int g = tid; g < 64 * NCK; g += NTH) {
+  static_assert((64 * NCK) % NTH == 0, "whole rounds");
+#pragma unroll
+  for (int g0 = 0; g0 < 64 * NCK; g0 += NTH) {
+    const int g = g0 + tid;
     const int r = g / NCK, c8 = g % NCK;
     const int B = r >> 4;
     const int off = swz_off<NCK>(r, c8);
