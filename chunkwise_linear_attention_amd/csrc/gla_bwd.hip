@@ -28,12 +28,14 @@
 // 16-deep MFMA per pair of 16-token blocks (Qh^T B or Kh^T B^T), the block
 // factor applied in fp32 after it, and q dq = Qh (.) that, k dk = Kh (.) that.
 //
-// dQ pass: 4 waves; wave w owns dq columns d in [w DK/4, (w+1) DK/4) and the
-// same columns of the state, kept transposed (S^T) in MFMA accumulators.
-// dK/dV pass: 8 waves; waves 0-3 own value columns of G (for dv), waves 4-7
-// key columns of G^T (for dk and the decay gradient); both copies are updated
-// every chunk, as in the scalar kernel.  One workgroup per sequence-head, one
-// per CU (LDS ~124 KB and ~150 KB at DK = DV = 128).
+// dQ pass: one wave per 16 key dimensions; wave w owns dq columns d in
+// [16 w, 16 w + 16) and the same columns of the state, kept transposed (S^T)
+// in MFMA accumulators.
+// dK/dV pass: 8 waves holding value columns of G (for dv) and key columns of
+// G^T (for dk and the decay gradient): at DK = DV = 128 each wave 16 of both,
+// otherwise waves 0-3 the value columns and waves 4-7 the key columns.  Both
+// copies are updated every chunk, as in the scalar kernel.  One workgroup per
+// sequence-head, one per CU (LDS ~146 KB and ~158 KB at DK = DV = 128).
 #include "chunk_common.h"
 #include "gla_kernels.h"
 #include "internal.h"
@@ -589,15 +591,22 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
 template <int DK, int DV>
 __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
   constexpr int NCK = DK / 8, NCV = DV / 8;
-  constexpr int NJ = DV / 64;   // side 0: 16-column j tiles per wave
-  constexpr int NI = DK / 64;   // side 1: 16-column d tiles per wave
-  constexpr int NG = DK * DV / 1024;
+  // At DK = DV = 128 every wave takes one 16-column tile of each product:
+  // value columns j0 = 16 w of dv and key dimensions d0 = 16 w of dk (the dk
+  // side's per-element work, the larger, is then spread over all eight waves).
+  // Otherwise waves 0-3 take dv and waves 4-7 dk.
+  constexpr bool MIX = DK == 128 && DV == 128;
+  constexpr int NJ = MIX ? 1 : DV / 64;  // dv: 16-column j tiles per wave
+  constexpr int NI = MIX ? 1 : DK / 64;  // dk: 16-column d tiles per wave
+  constexpr int NG0 = DK / 16 * NJ;       // tiles of G held for dv
+  constexpr int NG = MIX ? NG0 + DV / 16 * NI : NG0;
+  constexpr int NRED = MIX ? 8 : 4;       // partial sums of the boundary term per d
   constexpr int B_KS = 64 * DK * 2, B_QH = 2 * B_KS, B_KH = 3 * B_KS, B_VS = 4 * B_KS;
   constexpr int B_DO = B_VS + 64 * DV * 2, B_CS = B_DO + 64 * DV * 2;
   constexpr int B_AS = B_CS + 64 * DK * 4, B_BS = B_AS + 8192;
   constexpr int B_FQ = B_BS + 8192, B_FK = B_FQ + 4 * DK * 4, B_AL = B_FK + 4 * DK * 4;
   constexpr int B_RED = B_AL + DK * 4;
-  constexpr int B_FT = B_RED + 4 * DK * 4;
+  constexpr int B_FT = B_RED + NRED * DK * 4;
   constexpr int BUF = B_FT + 10 * DK * 4;
   constexpr int NBQ = DK / 8, NBV = DV / 8, NBL = DK / 4;
   constexpr int NBLK = 2 * NBQ + 2 * NBV + NBL;
@@ -615,6 +624,8 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
   const int tid0 = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
   const int side = w >> 2, wv = w & 3;
+  const bool do_dv = MIX || side == 0, do_dk = MIX || side == 1;
+  const int rw = MIX ? w : wv;  // this wave's row of boundary-term partials
   int tid = tid0, lane = tid0 & 63, li = lane & 15, lg = lane >> 4;
 #define FRESH_LANE()             \
   do {                           \
@@ -631,19 +642,19 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
   const int64_t nchunks = (T + TC - 1) / TC;
   const int64_t c_begin = seg * a.seg_chunks;
   const int64_t c_end = min(nchunks, c_begin + a.seg_chunks);
-  const int j0 = wv * (DV / 4);  // side 0
-  const int d0 = wv * (DK / 4);  // side 1
+  const int j0 = MIX ? 16 * w : wv * (DV / 4);  // dv columns
+  const int d0 = MIX ? 16 * w : wv * (DK / 4);  // dk dimensions
   const uint16_t *qh = a.q + bh * T * DK;
   const uint16_t *kh = a.k + bh * T * DK;
   const uint16_t *vh = a.v + bh * T * DV;
   const uint16_t *doh = a.dO + bh * T * DV;
   const float *lh = a.l + bh * T * DK;
 
-  // side 0: Gs[dt * NJ + jt][i] = G[16 dt + 4 lg + i][j0 + 16 jt + li]
-  // side 1: Gs[jt * NI + it][i] = G^T[16 jt + 4 lg + i][d0 + 16 it + li]
+  // dv: G0(dt, jt)[i] = G[16 dt + 4 lg + i][j0 + 16 jt + li]
+  // dk: G1(jt, it)[i] = G^T[16 jt + 4 lg + i][d0 + 16 it + li]
   f32x4 Gs[NG];
 #define G0(dt, jt) Gs[(dt) * NJ + (jt)]
-#define G1(jt, it) Gs[(jt) * NI + (it)]
+#define G1(jt, it) Gs[(MIX ? NG0 : 0) + (jt) * NI + (it)]
 #pragma unroll
   for (int x = 0; x < NG; ++x) Gs[x] = zero4();
   // the adjoint state at this segment's end: dS_T, or the reverse scan's
@@ -651,7 +662,7 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
                                      : a.Gloc + ((seg + 1) * a.nh + bh) * DK * DV;
   if (gsrc) {
     const float *src = gsrc;
-    if (side == 0) {
+    if (do_dv) {
 #pragma unroll
       for (int dt = 0; dt < DK / 16; ++dt)
 #pragma unroll
@@ -659,7 +670,8 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             G0(dt, jt)[i] = src[(16 * dt + 4 * lg + i) * DV + j0 + 16 * jt + li];
-    } else {
+    }
+    if (do_dk) {
 #pragma unroll
       for (int jt = 0; jt < DV / 16; ++jt)
 #pragma unroll
@@ -669,7 +681,7 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
             G1(jt, it)[i] = src[(d0 + 16 * it + li) * DV + 16 * jt + 4 * lg + i];
     }
   }
-  // side 1: the running suffix sum of q.dq - k.dk for its dimensions
+  // dk: the running suffix sum of q.dq - k.dk for its dimensions
   // d0 + 16 it + 4 lg + i (the same in every lane of a 16-lane row)
   float carry[NI][4];
 #pragma unroll
@@ -681,12 +693,12 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
     const int64_t t0 = ci * TC;
     const int n = (int)min<int64_t>(TC, T - t0);
 
-    // ---- at a segment's end: carry = <S[d, :], G[d, :]> (side 0 sums), with
+    // ---- at a segment's end: carry = <S[d, :], G[d, :]> (dv waves' sums), with
     // G rounded to bf16 as the dK product below takes it: the paths from this
     // chunk past the segment end then cancel against k.dk term by term ----
     if ((ci + 1) % kSegChunks == 0 || ci + 1 == nchunks) {
       FRESH_LANE();
-      if (side == 0) {
+      if (do_dv) {
         const float *Sg = a.Sseg + ((ci / kSegChunks) * a.nh + bh) * DK * DV;
 #pragma unroll
         for (int dt = 0; dt < DK / 16; ++dt) {
@@ -702,17 +714,20 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
             for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
             p[i] = s;
           }
-          if (li == 0) *reinterpret_cast<f32x4 *>(RED + wv * DK + 16 * dt + 4 * lg) = p;
+          if (li == 0) *reinterpret_cast<f32x4 *>(RED + rw * DK + 16 * dt + 4 * lg) = p;
         }
       }
       lds_barrier();
-      if (side == 1) {
+      if (do_dk) {
 #pragma unroll
         for (int it = 0; it < NI; ++it)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int d = d0 + 16 * it + 4 * lg + i;
-            carry[it][i] = RED[d] + RED[DK + d] + RED[2 * DK + d] + RED[3 * DK + d];
+            float c = RED[d];
+#pragma unroll
+            for (int u = 1; u < NRED; ++u) c += RED[u * DK + d];
+            carry[it][i] = c;
           }
       }
     }
@@ -808,7 +823,7 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
     }
     lds_barrier();
 
-    if (side == 0) {
+    if (do_dv) {
       // ---- dV^T[j][s] = (dO^T A^T)[j][s] + (G^T KG^T)[j][s] ----
       FRESH_LANE();
       bf16x8 gfrag[DK / 32][NJ];  // G^T A operands: row j, k = d (permuted)
@@ -850,7 +865,8 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
           }
         }
       }
-    } else {
+    }
+    if (do_dk) {
       // ---- dK^T[d][s], r2 = k dk, and the decay gradient ----
       FRESH_LANE();
       bf16x8 gfrag[DV / 32][NI];  // G A operands: row d, k = j (permuted)
@@ -958,7 +974,7 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
     // ---- G <- diag(alpha) G + QL^T dO (both copies) ----
     {
       FRESH_LANE();
-      if (side == 0) {
+      if (do_dv) {
 #pragma unroll
         for (int dt = 0; dt < DK / 16; ++dt) {
           const f32x4 av = *reinterpret_cast<const f32x4 *>(AL + 16 * dt + 4 * lg);
@@ -985,7 +1001,8 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
             for (int jt = 0; jt < NJ; ++jt) G0(dt, jt) = mfma(qa, db[jt], G0(dt, jt));
           }
         }
-      } else {
+      }
+      if (do_dk) {
 #pragma unroll
         for (int it = 0; it < NI; ++it) {
           const float al = AL[d0 + 16 * it + li];
@@ -1019,7 +1036,7 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
   }
 
   FRESH_LANE();
-  if (a.dS0 && side == 0 && seg == 0) {
+  if (a.dS0 && do_dv && seg == 0) {
     float *dst = a.dS0 + bh * DK * DV;
 #pragma unroll
     for (int dt = 0; dt < DK / 16; ++dt)
