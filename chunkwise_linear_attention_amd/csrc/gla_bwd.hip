@@ -588,6 +588,32 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
 // dK/dV pass
 // ===========================================================================
 
+// dst[r][d] = src[r][d] * F[r / 16][d] over a swizzled [64 x DK] bf16 tile
+// (dst may be src), formed once per chunk by all threads for operands every
+// wave reads.
+template <int DK, int NTH>
+__device__ __forceinline__ void scale_rows_by_block(const unsigned char *src, unsigned char *dst,
+                                                    const float *F, int tid) {
+  constexpr int NCK = DK / 8;
+  static_assert((64 * NCK) % NTH == 0, "whole rounds");
+#pragma unroll
+  for (int g0 = 0; g0 < 64 * NCK; g0 += NTH) {
+    const int g = g0 + tid;
+    const int r = g / NCK, c8 = g % NCK;
+    const int off = swz_off<NCK>(r, c8);
+    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(src + off);
+    const f32x4 f0 = *reinterpret_cast<const f32x4 *>(F + (r >> 4) * DK + 8 * c8);
+    const f32x4 f1 = *reinterpret_cast<const f32x4 *>(F + (r >> 4) * DK + 8 * c8 + 4);
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y[e] = tof(x[e]) * f0[e];
+      y[e + 4] = tof(x[e + 4]) * f1[e];
+    }
+    *reinterpret_cast<bf16x8 *>(dst + off) = cvt8(y);
+  }
+}
+
 template <int DK, int DV>
 __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
   constexpr int NCK = DK / 8, NCV = DV / 8;
@@ -822,6 +848,12 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
       }
     }
     lds_barrier();
+    // KH -> KG = KH (.) FK[S] in place: the dv product's operand, which every
+    // wave reads, formed once here instead of by each wave.  The dk side
+    // re-forms the K-hat values it needs from k and the factor it computes.
+    FRESH_LANE();
+    scale_rows_by_block<DK, BTHR>(KH, KH, FK, tid);
+    lds_barrier();
 
     if (do_dv) {
       // ---- dV^T[j][s] = (dO^T A^T)[j][s] + (G^T KG^T)[j][s] ----
@@ -837,15 +869,7 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
 #pragma unroll
         for (int kk = 0; kk < DK / 32; ++kk) {
           const int da = 32 * kk + 4 * lg, db = da + 16;
-          const bf16x4 lo = lds_half<NCK>(KH, s, da);
-          const bf16x4 hi = lds_half<NCK>(KH, s, db);
-          float y[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            y[e] = tof(lo[e]) * FK[S * DK + da + e];
-            y[e + 4] = tof(hi[e]) * FK[S * DK + db + e];
-          }
-          kgf[kk] = cvt8(y);
+          kgf[kk] = cat8(lds_half<NCK>(KH, s, da), lds_half<NCK>(KH, s, db));
         }
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt) {
@@ -918,16 +942,18 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
 #pragma unroll
           for (int kk = 0; kk < DV / 32; ++kk) acc2 = mfma(gfrag[kk][it], vfr[kk], acc2);
           const bf16x4 kv = lds_half<NCK>(KS, s, dc);
-          const bf16x4 khv = lds_half<NCK>(KH, s, dc);
           float out[4], r2v[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int d = dc + i;
             const float csd = CS[csx<DK>(s, d)];
             const float ue = __expf(CS[csx<DK>(16 * S + 15, d)] - csd);
+            // K-hat exactly as the scaled copy formed it (same factor, same
+            // rounding), so the in-chunk paths still cancel against q.dq
+            const float khd = tof(tobf(tof(kv[i]) * ue));
             const float inter = FK[S * DK + d] * acc2[i] * ue;
             float v = accI[i] * ue + inter;
-            float rv = tof(khv[i]) * accI[i] + tof(kv[i]) * inter;
+            float rv = khd * accI[i] + tof(kv[i]) * inter;
             if (!good) {
               const float kd = tof(kv[i]);
               for (int r = s; r < min(16 * S + 16, n); ++r) {
@@ -972,6 +998,12 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
     }
 
     // ---- G <- diag(alpha) G + QL^T dO (both copies) ----
+    // QL = Qh (.) FQ[R] over the raw q tile (no longer read), formed once
+    // for every wave
+    lds_barrier();
+    FRESH_LANE();
+    scale_rows_by_block<DK, BTHR>(QH, QS, FQ, tid);
+    lds_barrier();
     {
       FRESH_LANE();
       if (do_dv) {
@@ -985,18 +1017,12 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const int R = 2 * kb + (lg >> 1);
           bf16x8 db[NJ];  // dO B operands: k = r, column j
 #pragma unroll
           for (int jt = 0; jt < NJ; ++jt) db[jt] = tr_frag<NCV>(DOS, 32 * kb, j0 + 16 * jt, li, lg);
 #pragma unroll
           for (int dt = 0; dt < DK / 16; ++dt) {
-            const bf16x8 x = tr_frag<NCK>(QH, 32 * kb, 16 * dt, li, lg);  // Qh^T: row d, k = r
-            const float f = FQ[R * DK + 16 * dt + li];
-            float y[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = tof(x[e]) * f;
-            const bf16x8 qa = cvt8(y);
+            const bf16x8 qa = tr_frag<NCK>(QS, 32 * kb, 16 * dt, li, lg);  // QL^T: row d, k = r
 #pragma unroll
             for (int jt = 0; jt < NJ; ++jt) G0(dt, jt) = mfma(qa, db[jt], G0(dt, jt));
           }
@@ -1013,17 +1039,9 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const int R = 2 * kb + (lg >> 1);
           bf16x8 qb[NI];  // QL B operands: k = r, column d
 #pragma unroll
-          for (int it = 0; it < NI; ++it) {
-            const bf16x8 x = tr_frag<NCK>(QH, 32 * kb, d0 + 16 * it, li, lg);
-            const float f = FQ[R * DK + d0 + 16 * it + li];
-            float y[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = tof(x[e]) * f;
-            qb[it] = cvt8(y);
-          }
+          for (int it = 0; it < NI; ++it) qb[it] = tr_frag<NCK>(QS, 32 * kb, d0 + 16 * it, li, lg);
 #pragma unroll
           for (int jt = 0; jt < DV / 16; ++jt) {
             const bf16x8 da = tr_frag<NCV>(DOS, 32 * kb, 16 * jt, li, lg);  // dO^T: row j, k = r
