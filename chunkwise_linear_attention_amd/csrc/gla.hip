@@ -333,6 +333,12 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
       CS[R_AL * DK + d] = __expf(cl);
     }
     lds_barrier();
+    // KG = Kh (.) exp(c_n - ce_S) and QL = Qh (.) exp(cb_R) in place: the
+    // update's and the output's operands, which every wave reads in full
+    FRESH_LANE();
+    scale_rows_by_block<DK, NTHR>(KS, KS, CS + R_FK * DK, tid);
+    if constexpr (OUT) scale_rows_by_block<DK, NTHR>(QS, QS, CS + R_FQ * DK, tid);
+    if constexpr (!OUT) lds_barrier();
     if constexpr (OUT) {
     // ---- P[r][s] (bf16) over the first rows of the logs ----
     FRESH_LANE();
@@ -373,22 +379,11 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const int rr = 16 * rt + li;
-        const float *fq = CS + (R_FQ + rt) * DK;
         bf16x8 qfrag[DK / 32];  // QL^T B operands, k = {32kk + 4lg + 0..3, +16}
 #pragma unroll
         for (int kk = 0; kk < DK / 32; ++kk) {
           const int da = 32 * kk + 4 * lg, db = da + 16;
-          const bf16x4 lo = lds_half<NCK>(QS, rr, da);
-          const bf16x4 hi = lds_half<NCK>(QS, rr, db);
-          const f32x4 fa = *reinterpret_cast<const f32x4 *>(fq + da);
-          const f32x4 fb = *reinterpret_cast<const f32x4 *>(fq + db);
-          float y[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            y[e] = tof(lo[e]) * fa[e];
-            y[e + 4] = tof(hi[e]) * fb[e];
-          }
-          qfrag[kk] = cvt8(y);
+          qfrag[kk] = cat8(lds_half<NCK>(QS, rr, da), lds_half<NCK>(QS, rr, db));
         }
         bf16x8 pfrag[2];
 #pragma unroll
@@ -430,16 +425,9 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
         bf16x8 vb[NJ];  // V B operands: k = s, column j
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt) vb[jt] = tr_frag<NCV>(VS, 32 * kb, j0 + 16 * jt, li, lg);
-        const int Sblk = 2 * kb + (lg >> 1);  // block of this lane's 8 rows s
-        const float *fk = CS + (R_FK + Sblk) * DK;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const bf16x8 kx = tr_frag<NCK>(KS, 32 * kb, 16 * dt, li, lg);  // Kh^T: row d, k = s
-          const float f = fk[16 * dt + li];
-          float y[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] = tof(kx[e]) * f;
-          const bf16x8 ka = cvt8(y);
+          const bf16x8 ka = tr_frag<NCK>(KS, 32 * kb, 16 * dt, li, lg);  // KG^T: row d, k = s
 #pragma unroll
           for (int jt = 0; jt < NJ; ++jt) S_acc[dt][jt] = mfma(ka, vb[jt], S_acc[dt][jt]);
         }

@@ -588,32 +588,6 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
 // dK/dV pass
 // ===========================================================================
 
-// dst[r][d] = src[r][d] * F[r / 16][d] over a swizzled [64 x DK] bf16 tile
-// (dst may be src), formed once per chunk by all threads for operands every
-// wave reads.
-template <int DK, int NTH>
-__device__ __forceinline__ void scale_rows_by_block(const unsigned char *src, unsigned char *dst,
-                                                    const float *F, int tid) {
-  constexpr int NCK = DK / 8;
-  static_assert((64 * NCK) % NTH == 0, "whole rounds");
-#pragma unroll
-  for (int g0 = 0; g0 < 64 * NCK; g0 += NTH) {
-    const int g = g0 + tid;
-    const int r = g / NCK, c8 = g % NCK;
-    const int off = swz_off<NCK>(r, c8);
-    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(src + off);
-    const f32x4 f0 = *reinterpret_cast<const f32x4 *>(F + (r >> 4) * DK + 8 * c8);
-    const f32x4 f1 = *reinterpret_cast<const f32x4 *>(F + (r >> 4) * DK + 8 * c8 + 4);
-    float y[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      y[e] = tof(x[e]) * f0[e];
-      y[e + 4] = tof(x[e + 4]) * f1[e];
-    }
-    *reinterpret_cast<bf16x8 *>(dst + off) = cvt8(y);
-  }
-}
-
 template <int DK, int DV>
 __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
   constexpr int NCK = DK / 8, NCV = DV / 8;

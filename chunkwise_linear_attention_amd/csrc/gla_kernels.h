@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "chunk_common.h"
+
 namespace cla {
 namespace gla {
 
@@ -17,6 +19,34 @@ template <int DK>
 __host__ __device__ __forceinline__ int csx(int r, int d) {
   static_assert(DK >= 64, "at least 16 pieces per row");
   return r * DK + ((((d >> 2) ^ (r & 15)) << 2) | (d & 3));
+}
+
+// dst[r][d] = src[r][d] * F[r / 16][d] over a swizzled [64 x DK] bf16 tile
+// (dst may be src; F: 4 rows of DK fp32 factors, one per 16-token block), by
+// all NTH threads of a workgroup: operands that every wave reads, formed once
+// instead of by each wave.
+template <int DK, int NTH>
+__device__ __forceinline__ void scale_rows_by_block(const unsigned char *src, unsigned char *dst,
+                                                    const float *F, int tid) {
+  using namespace cla::chunk;
+  constexpr int NCK = DK / 8;
+  static_assert((64 * NCK) % NTH == 0, "whole rounds");
+#pragma unroll
+  for (int g0 = 0; g0 < 64 * NCK; g0 += NTH) {
+    const int g = g0 + tid;
+    const int r = g / NCK, c8 = g % NCK;
+    const int off = swz_off<NCK>(r, c8);
+    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(src + off);
+    const f32x4 f0 = *reinterpret_cast<const f32x4 *>(F + (r >> 4) * DK + 8 * c8);
+    const f32x4 f1 = *reinterpret_cast<const f32x4 *>(F + (r >> 4) * DK + 8 * c8 + 4);
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y[e] = tof(x[e]) * f0[e];
+      y[e + 4] = tof(x[e + 4]) * f1[e];
+    }
+    *reinterpret_cast<bf16x8 *>(dst + off) = cvt8(y);
+  }
 }
 
 // The backward's decay gradient sums q.dq - k.dk backwards inside blocks of
