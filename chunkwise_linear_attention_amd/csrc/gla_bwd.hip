@@ -290,7 +290,7 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
   constexpr int NDT = DK / (16 * NW);  // 16-column d tiles per wave
   static_assert(NDT == 1, "one d tile per wave");
   constexpr int NJT = DV / 16;  // 16-row j tiles of S^T
-  constexpr int B_KS = 64 * DK * 2, B_QH = 2 * B_KS, B_KH = 3 * B_KS, B_VS = 4 * B_KS;
+  constexpr int B_KS = 64 * DK * 2, B_KH = 2 * B_KS, B_VS = 3 * B_KS;
   constexpr int B_DO = B_VS + 64 * DV * 2, B_CS = B_DO + 64 * DV * 2;
   constexpr int B_BS = B_CS + 64 * DK * 4, B_FQ = B_BS + 64 * 64 * 2;
   constexpr int B_FK = B_FQ + 4 * DK * 4, B_AL = B_FK + 4 * DK * 4;
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
   constexpr int BUF = B_FT + 10 * DK * 4;
   static_assert(BUF <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) unsigned char buf[BUF];
-  unsigned char *QS = buf, *KS = buf + B_KS, *QH = buf + B_QH, *KH = buf + B_KH;
+  unsigned char *QS = buf, *KS = buf + B_KS, *KH = buf + B_KH;
   unsigned char *VS = buf + B_VS;
   unsigned char *DOS = buf + B_DO, *BS = buf + B_BS;
   float *CS = reinterpret_cast<float *>(buf + B_CS);
@@ -377,7 +377,9 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
     FRESH_LANE();
     cumsum_rows<DK, NT>(CS, n, tid);
     FRESH_LANE();
-    prep_scaled<DK, NT>(QS, KS, QH, KH, CS, FQ, FK, AL, n, tid);
+    // (no Qh copy: this pass needs only this lane's few Qh values, re-formed
+    // where they are used)
+    prep_scaled<DK, NT>(QS, KS, nullptr, KH, CS, FQ, FK, AL, n, tid);
     block_factors<DK, NT>(CS, FT, tid);
 
     // ---- B[r][s] = dO_r . v_s (masked), stored [r][s]; the 32-column steps
@@ -441,16 +443,19 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
           for (int kk = 0; kk < DV / 32; ++kk) acc2 = mfma(sfrag[kk][dt], dofrag[kk], acc2);
           // accI[i], acc2[i] at d = dc + i, row t = r
           const bf16x4 qv = lds_half<NCK>(QS, min(r, 63), dc);
-          const bf16x4 qhv = lds_half<NCK>(QH, r, dc);
           float out[4], r1v[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int d = dc + i;
             const float cb = R > 0 ? CS[csx<DK>(16 * R - 1, d)] : 0.f;
             const float u = __expf(CS[csx<DK>(r, d)] - cb);
+            // Q-hat exactly as the scaled copy of the dK/dV pass forms it
+            // (same factor, same rounding), so the in-chunk paths cancel
+            // against k.dk there
+            const float qhd = tof(tobf(tof(qv[i]) * u));
             const float inter = FQ[R * DK + d] * acc2[i] * u;
             float v = accI[i] * u + inter;
-            float rv = tof(qhv[i]) * accI[i] + tof(qv[i]) * inter;
+            float rv = qhd * accI[i] + tof(qv[i]) * inter;
             if (!good) {
               // the block's own tokens, elementwise
               const float qd = tof(qv[i]);
