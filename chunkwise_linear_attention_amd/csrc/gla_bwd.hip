@@ -77,16 +77,50 @@ __device__ __forceinline__ float path_term(float b, float q, float k, float ct, 
 
 // DMA of the [64 x D] fp32 log tile in the swizzled layout of csx: 1 KB
 // blocks of RPB rows; rows past the chunk re-read row n - 1.
+// the global address of the 16 bytes lane `lane` copies for block `block` of a
+// bf16 tile (as dma_block fetches it)
 template <int D>
-__device__ __forceinline__ void dma_f32_rows(const float *chunk_src, int n, unsigned char *tile,
-                                             int block, int lane) {
+__device__ __forceinline__ const uint16_t *bf16_block_src(const uint16_t *chunk_src, int n,
+                                                          int block, int lane) {
+  constexpr int NCH = D / 8;
+  constexpr int RPB = 64 / NCH;
+  const int row = block * RPB + lane / NCH;
+  const int c = (lane % NCH) ^ swz_pat(row);
+  const int grow = min(row, n - 1);
+  return chunk_src + (int64_t)grow * D + c * 8;
+}
+
+// The same copy as global_load_lds (16 bytes per lane into a 1 KB LDS
+// block), issued from inline assembly with the block's LDS address passed in
+// M0.  The compiler does not see this load, so it inserts no wait for it: not
+// in front of LDS reads it cannot tell apart from the target (where the
+// builtin gets a vmcnt(0) that holds all later work until the copy lands),
+// nor anywhere else.  The caller waits (vmcnt(0)) and synchronizes the
+// workgroup before any lane reads the target.  Loads the compiler does track
+// stay correctly waited for: vector loads complete in issue order, so a load
+// it does not count only makes its counted waits (vmcnt(N)) wait longer.
+__device__ __forceinline__ void lds_copy16_untracked(const void *src, unsigned char *lds_block) {
+  const uint32_t m0v =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds_block);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0v) : "memory");
+}
+
+template <int D>
+__device__ __forceinline__ const float *dma_f32_rows_src(const float *chunk_src, int n, int block,
+                                                         int lane) {
   constexpr int PPR = D / 4;
   constexpr int RPB = 64 / PPR;
   const int row = block * RPB + lane / PPR;
   const int grow = min(row, n - 1);
   // this lane lands at piece lane % PPR of the row: it fetches the piece the
   // row's swizzle puts there
-  __builtin_amdgcn_global_load_lds(chunk_src + (int64_t)grow * D + (((lane % PPR) ^ (row & 15)) * 4),
+  return chunk_src + (int64_t)grow * D + (((lane % PPR) ^ (row & 15)) * 4);
+}
+
+template <int D>
+__device__ __forceinline__ void dma_f32_rows(const float *chunk_src, int n, unsigned char *tile,
+                                             int block, int lane) {
+  __builtin_amdgcn_global_load_lds(dma_f32_rows_src<D>(chunk_src, n, block, lane),
                                    (lds_void *)(tile + block * 1024), 16, 0, 0);
 }
 
@@ -694,6 +728,28 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) carry[it][i] = 0.f;
 
+  // Staging: k, v and the logs of a chunk are copied during the previous
+  // chunk's state update (which reads none of them), q and dO (which it
+  // reads) at the chunk's start; all by untracked copies, waited for at the
+  // chunk's start.
+  auto stage_kvl = [&](int64_t cj) __attribute__((always_inline)) {
+    const int64_t tj = cj * TC;
+    const int nj = (int)min<int64_t>(TC, T - tj);
+    for (int b = w; b < NBQ + NBV + NBL; b += BTHR / 64) {
+      if (b < NBQ)
+        lds_copy16_untracked(bf16_block_src<DK>(kh + tj * DK, nj, b, lane), KS + b * 1024);
+      else if (b < NBQ + NBV)
+        lds_copy16_untracked(bf16_block_src<DV>(vh + tj * DV, nj, b - NBQ, lane),
+                             VS + (b - NBQ) * 1024);
+      else
+        lds_copy16_untracked(dma_f32_rows_src<DK>(lh + tj * DK, nj, b - NBQ - NBV, lane),
+                             buf + B_CS + (b - NBQ - NBV) * 1024);
+    }
+  };
+  if (c_end > c_begin) {
+    FRESH_LANE();
+    stage_kvl(c_end - 1);
+  }
   for (int64_t ci = c_end - 1; ci >= c_begin; --ci) {
     const int64_t t0 = ci * TC;
     const int n = (int)min<int64_t>(TC, T - t0);
@@ -739,17 +795,12 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
 
     lds_barrier();
     FRESH_LANE();
-    for (int b = w; b < NBLK; b += BTHR / 64) {
+    for (int b = w; b < NBQ + NBV; b += BTHR / 64) {
       if (b < NBQ)
-        dma_block<DK>(qh + t0 * DK, n, QS, b, lane);
-      else if (b < 2 * NBQ)
-        dma_block<DK>(kh + t0 * DK, n, KS, b - NBQ, lane);
-      else if (b < 2 * NBQ + NBV)
-        dma_block<DV>(vh + t0 * DV, n, VS, b - 2 * NBQ, lane);
-      else if (b < 2 * NBQ + 2 * NBV)
-        dma_block<DV>(doh + t0 * DV, n, DOS, b - 2 * NBQ - NBV, lane);
+        lds_copy16_untracked(bf16_block_src<DK>(qh + t0 * DK, n, b, lane), QS + b * 1024);
       else
-        dma_f32_rows<DK>(lh + t0 * DK, n, buf + B_CS, b - 2 * NBQ - 2 * NBV, lane);
+        lds_copy16_untracked(bf16_block_src<DV>(doh + t0 * DV, n, b - NBQ, lane),
+                             DOS + (b - NBQ) * 1024);
     }
     __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
@@ -978,8 +1029,10 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
 
     // ---- G <- diag(alpha) G + QL^T dO (both copies) ----
     // QL = Qh (.) FQ[R] over the raw q tile (no longer read), formed once
-    // for every wave
+    // for every wave; the next chunk's k, v and logs start streaming in
     lds_barrier();
+    FRESH_LANE();
+    if (ci > c_begin) stage_kvl(ci - 1);
     FRESH_LANE();
     scale_rows_by_block<DK, BTHR>(QH, QS, FQ, tid);
     lds_barrier();
