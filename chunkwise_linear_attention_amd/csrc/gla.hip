@@ -201,7 +201,10 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
 
     // ---- Qh, Kh in place (8 elements per step) ----
     FRESH_LANE();
-    for (int g = tid; g < 64 * NCK; g += NTHR) {
+    static_assert((64 * NCK) % NTHR == 0, "whole rounds");
+#pragma unroll
+    for (int g0 = 0; g0 < 64 * NCK; g0 += NTHR) {
+      const int g = g0 + tid;
       const int r = g / NCK, c8 = g % NCK;
       const int B = r >> 4;
       const int off = swz_off<NCK>(r, c8);
