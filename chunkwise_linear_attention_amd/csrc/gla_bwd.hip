@@ -627,6 +627,14 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
 // dK/dV pass
 // ===========================================================================
 
+// Score tiles of the dK/dV pass per wave, one byte per job (0xFF: none):
+// tile t (tile_rt / tile_st) of the decayed A (t) or of B (16 + t).  An A
+// tile scales its K-hat operand by the block factors, about twice a B tile's
+// work; waves 0-1 take two A tiles, waves 2-7 one A and two B tiles, and the
+// two structurally zero tiles of each kind (t = 10, 11) go to waves 6 and 7.
+__constant__ uint32_t kScoreJobs[8] = {0xFFFF0100u, 0xFFFF0302u, 0xFF111004u, 0xFF131205u,
+                                       0xFF151406u, 0xFF171607u, 0x1A0A1808u, 0x1B0B1909u};
+
 template <int DK, int DV>
 __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
   constexpr int NCK = DK / 8, NCV = DV / 8;
@@ -811,11 +819,16 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
     block_factors<DK, BTHR>(CS, FT, tid);
     lds_barrier();
 
-    // ---- scores, stored transposed [s][r]: side 0 the decayed A, side 1 B ----
+    // ---- scores, stored transposed [s][r]: the decayed A and B ----
     {
       FRESH_LANE();
-      unsigned char *PT = side == 0 ? AS : BS;
-      for (int t = wv; t < 12; t += 4) {
+      const uint32_t jobs = kScoreJobs[w];
+      for (int slot = 0; slot < 4; ++slot) {
+        const uint32_t job = (jobs >> (8 * slot)) & 0xFFu;
+        if (job == 0xFFu) break;
+        const bool is_a = job < 16;
+        const int t = job & 15;
+        unsigned char *PT = is_a ? AS : BS;
         // the tiles (rows s in block S, columns r in block R) that the
         // 32-column steps over r >= s read: S <= (R | 1); those with R < S
         // are zero
@@ -823,7 +836,7 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
         f32x4 acc = zero4();
         // acc[i] = X[r = 16R + 4lg + i][s = 16S + li]
         if (S <= R) {
-          if (side == 0) {
+          if (is_a) {
             const bool good = R != S || !block_bad<DK>(CS, R, lane);
             if (good) {
 #pragma unroll
