@@ -176,28 +176,9 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
 
-    // ---- cumulative logs, in place: NP parts of RP rows per dimension ----
-    {
-      FRESH_LANE();
-      constexpr int NP = NTHR / DK, RP = 64 / NP;
-      const int d = tid % DK, part = tid / DK;
-      float run = 0.f;
-#pragma unroll
-      for (int i = 0; i < RP; ++i) {
-        const int r = part * RP + i;
-        run += r < n ? CS[csx<DK>(r, d)] : 0.f;  // rows past the chunk: no decay
-        CS[csx<DK>(r, d)] = run;
-      }
-      lds_barrier();
-      float off = 0.f;
-      for (int p = 0; p < part; ++p) off += CS[csx<DK>(p * RP + RP - 1, d)];
-      lds_barrier();
-      if (part > 0) {
-#pragma unroll
-        for (int i = 0; i < RP; ++i) CS[csx<DK>(part * RP + i, d)] += off;
-      }
-      lds_barrier();
-    }
+    // ---- cumulative logs, in place ----
+    cumsum_rows_dpp<DK, NTHR>(CS, n, tid);
+    lds_barrier();
 
     // ---- Qh, Kh in place (8 elements per step) ----
     FRESH_LANE();

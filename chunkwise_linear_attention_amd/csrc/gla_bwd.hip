@@ -212,23 +212,7 @@ struct ChunkRegs {
 // In-chunk cumulative logs, in place, with NTH threads (rows past n: no decay).
 template <int DK, int NTH>
 __device__ __forceinline__ void cumsum_rows(float *CS, int n, int tid) {
-  constexpr int NP = NTH / DK, RP = 64 / NP;
-  const int d = tid % DK, part = tid / DK;
-  float run = 0.f;
-#pragma unroll
-  for (int i = 0; i < RP; ++i) {
-    const int r = part * RP + i;
-    run += r < n ? CS[csx<DK>(r, d)] : 0.f;
-    CS[csx<DK>(r, d)] = run;
-  }
-  lds_barrier();
-  float off = 0.f;
-  for (int p = 0; p < part; ++p) off += CS[csx<DK>(p * RP + RP - 1, d)];
-  lds_barrier();
-  if (part > 0) {
-#pragma unroll
-    for (int i = 0; i < RP; ++i) CS[csx<DK>(part * RP + i, d)] += off;
-  }
+  cumsum_rows_dpp<DK, NTH>(CS, n, tid);
   lds_barrier();
 }
 

@@ -49,6 +49,57 @@ __device__ __forceinline__ void scale_rows_by_block(const unsigned char *src, un
   }
 }
 
+// x + (x of the lane DPP control CTRL selects), rows outside ROW_MASK and
+// sources outside the row adding 0
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, true));
+}
+
+// The in-chunk cumulative logs, in place in the [64 x DK] fp32 tile (csx
+// layout): c_r[d] = sum of l_t[d] over t <= r, t < n (rows past the chunk's
+// n tokens repeat its total).  One lane per row: wave w takes the columns
+// [w CPW, (w + 1) CPW), reads its row's pieces of them, forms each column's
+// inclusive prefix sum across the 64 lanes by DPP (within every 16-lane row by
+// shifts of 1, 2, 4 and 8 lanes, then across rows by the broadcasts of lanes 15
+// and 31: the cross-lane scan of AMD's GCN documentation), and writes them
+// back.  The caller synchronizes the workgroup before and after.
+template <int DK, int NTH>
+__device__ __forceinline__ void cumsum_rows_dpp(float *CS, int n, int tid) {
+  using namespace cla::chunk;
+  constexpr int NW = NTH / 64, CPW = DK / NW;  // columns per wave
+  static_assert(CPW % 4 == 0 && NW * CPW == DK, "whole 16-byte pieces per wave");
+  const int r = tid & 63;
+  const int c0 = __builtin_amdgcn_readfirstlane(tid >> 6) * CPW;
+  float x[CPW];
+#pragma unroll
+  for (int p = 0; p < CPW / 4; ++p) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(CS + csx<DK>(r, c0 + 4 * p));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[4 * p + e] = r < n ? v[e] : 0.f;
+  }
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) x[c] = dpp_add<0x111, 0xF>(x[c]);  // row_shr:1
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) x[c] = dpp_add<0x112, 0xF>(x[c]);  // row_shr:2
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) x[c] = dpp_add<0x114, 0xF>(x[c]);  // row_shr:4
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) x[c] = dpp_add<0x118, 0xF>(x[c]);  // row_shr:8
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) x[c] = dpp_add<0x142, 0xA>(x[c]);  // row_bcast:15 into rows 1, 3
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) x[c] = dpp_add<0x143, 0xC>(x[c]);  // row_bcast:31 into rows 2, 3
+#pragma unroll
+  for (int p = 0; p < CPW / 4; ++p) {
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = x[4 * p + e];
+    *reinterpret_cast<f32x4 *>(CS + csx<DK>(r, c0 + 4 * p)) = v;
+  }
+}
+
 // The backward's decay gradient sums q.dq - k.dk backwards inside blocks of
 // this many chunks, each started from the boundary term <S, G>.  Segments of
 // the sequence that run on separate workgroups are whole multiples of it.
