@@ -47,9 +47,10 @@ using namespace cla::chunk;
 
 namespace {
 
-// Sub-block whose own decay is below exp(-kBadLog) in some dimension: its
-// diagonal scores are computed elementwise.
-constexpr float kBadLog = 60.f;
+// Sub-block whose own decay is below e^-60 in some dimension: its diagonal
+// scores are computed elementwise.  (The threshold is in the base-2 units the
+// cumulative logs are kept in.)
+constexpr float kBadLog = 60.f * kLog2e;
 
 // DMA of the [64 x D] fp32 log tile in the swizzled layout of csx: 1 KB
 // blocks of RPB rows; rows past the chunk re-read row n - 1.
@@ -194,14 +195,14 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
       float yk[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        yk[e] = r < n ? tof(kv[e]) * __expf(CS[csx<DK>(re, 8 * c8 + e)] - CS[csx<DK>(r, 8 * c8 + e)]) : 0.f;
+        yk[e] = r < n ? tof(kv[e]) * exp_c(CS[csx<DK>(re, 8 * c8 + e)] - CS[csx<DK>(r, 8 * c8 + e)]) : 0.f;
       *reinterpret_cast<bf16x8 *>(KS + off) = cvt8(yk);
       if (OUT) {
         bf16x8 qv = *reinterpret_cast<const bf16x8 *>(QS + off);
         float yq[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          yq[e] = tof(qv[e]) * __expf(CS[csx<DK>(r, 8 * c8 + e)] - (B > 0 ? CS[csx<DK>(rb, 8 * c8 + e)] : 0.f));
+          yq[e] = tof(qv[e]) * exp_c(CS[csx<DK>(r, 8 * c8 + e)] - (B > 0 ? CS[csx<DK>(rb, 8 * c8 + e)] : 0.f));
         *reinterpret_cast<bf16x8 *>(QS + off) = cvt8(yq);
       }
     }
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
       FRESH_LANE();
       const int R = tR[x], S = tS[x];
       f32x4 acc = zero4();
-      // a diagonal block whose decay falls below exp(-kBadLog) in some
+      // a diagonal block whose decay falls below e^-60 in some
       // dimension is done elementwise (wave-uniform decision)
       bool exact = false;
       if (R == S) {
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
           const int d = 32 * (idx >> 3) + 8 * lg + (idx & 7);
           if (idx < DK / 4) {
             const float cb = R > 0 ? CS[csx<DK>(16 * R - 1, d)] : 0.f;
-            fpair[h] = __expf(cb - CS[csx<DK>(16 * S + 15, d)]);
+            fpair[h] = exp_c(cb - CS[csx<DK>(16 * S + 15, d)]);
           } else {
             fpair[h] = 0.f;
           }
@@ -284,7 +285,7 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
 #pragma unroll
               for (int e = 0; e < 8; ++e)
                 sum += tof(qv[e]) * tof(kv[e]) *
-                       __expf(CS[csx<DK>(r, d0 + e)] - CS[csx<DK>(s, d0 + e)]);
+                       exp_c(CS[csx<DK>(r, d0 + e)] - CS[csx<DK>(s, d0 + e)]);
             }
           }
           acc[i] = sum;
@@ -311,10 +312,10 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
       if (!OUT) lsum += cl;
 #pragma unroll
       for (int B = 0; B < 4; ++B) {
-        CS[(R_FQ + B) * DK + d] = B > 0 ? __expf(ce[B - 1]) : 1.f;  // exp(cb_B)
-        CS[(R_FK + B) * DK + d] = __expf(cl - ce[B]);
+        CS[(R_FQ + B) * DK + d] = B > 0 ? exp_c(ce[B - 1]) : 1.f;  // exp(cb_B)
+        CS[(R_FK + B) * DK + d] = exp_c(cl - ce[B]);
       }
-      CS[R_AL * DK + d] = __expf(cl);
+      CS[R_AL * DK + d] = exp_c(cl);
     }
     lds_barrier();
     // KG = Kh (.) exp(c_n - ce_S) and QL = Qh (.) exp(cb_R) in place: the
@@ -429,7 +430,7 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           dst[(16 * dt + 4 * lg + i) * DV + j0 + 16 * jt + li] = S_acc[dt][jt][i];
-    if (tid < DK) a.Aseg[(seg * a.nh + bh) * DK + tid] = __expf(lsum);
+    if (tid < DK) a.Aseg[(seg * a.nh + bh) * DK + tid] = exp_c(lsum);
   } else if (a.ST && seg == a.P - 1) {
     float *dst = a.ST + bh * DK * DV;
 #pragma unroll

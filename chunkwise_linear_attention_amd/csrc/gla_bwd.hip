@@ -47,7 +47,7 @@ using namespace cla::chunk;
 
 namespace {
 
-constexpr float kBadLog = 60.f;  // as in the forward
+constexpr float kBadLog = 60.f * kLog2e;  // e^-60, as in the forward (base-2 units)
 constexpr int BTHR = 512;
 
 // v_mfma_f32_16x16x16_bf16: lane 16 lg + li holds A row li and B column li,
@@ -72,7 +72,7 @@ __device__ __forceinline__ float row_dpp(float v) {
 // decay gradient's two sums hold the same numbers and the paths that do not
 // cross a step cancel in it up to fp32 summation order.
 __device__ __forceinline__ float path_term(float b, float q, float k, float ct, float cs) {
-  return ((b * q) * k) * __expf(ct - cs);
+  return ((b * q) * k) * exp_c(ct - cs);
 }
 
 // DMA of the [64 x D] fp32 log tile in the swizzled layout of csx: 1 KB
@@ -236,14 +236,14 @@ __device__ __forceinline__ void prep_scaled(const unsigned char *QS, const unsig
     const bf16x8 kv = *reinterpret_cast<const bf16x8 *>(KS + off);
     float yk[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) yk[e] = r < n ? tof(kv[e]) * __expf(CS[csx<DK>(re, 8 * c8 + e)] - CS[csx<DK>(r, 8 * c8 + e)]) : 0.f;
+    for (int e = 0; e < 8; ++e) yk[e] = r < n ? tof(kv[e]) * exp_c(CS[csx<DK>(re, 8 * c8 + e)] - CS[csx<DK>(r, 8 * c8 + e)]) : 0.f;
     *reinterpret_cast<bf16x8 *>(KH + off) = cvt8(yk);
     if (QH) {
       const bf16x8 qv = *reinterpret_cast<const bf16x8 *>(QS + off);
       float yq[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        yq[e] = r < n ? tof(qv[e]) * __expf(CS[csx<DK>(r, 8 * c8 + e)] -
+        yq[e] = r < n ? tof(qv[e]) * exp_c(CS[csx<DK>(r, 8 * c8 + e)] -
                                             (B > 0 ? CS[csx<DK>(rb, 8 * c8 + e)] : 0.f))
                       : 0.f;
       *reinterpret_cast<bf16x8 *>(QH + off) = cvt8(yq);
@@ -255,10 +255,10 @@ __device__ __forceinline__ void prep_scaled(const unsigned char *QS, const unsig
     for (int B = 0; B < 4; ++B) ce[B] = CS[csx<DK>(16 * B + 15, d)];
 #pragma unroll
     for (int B = 0; B < 4; ++B) {
-      FQ[B * DK + d] = B > 0 ? __expf(ce[B - 1]) : 1.f;
-      FK[B * DK + d] = __expf(ce[3] - ce[B]);
+      FQ[B * DK + d] = B > 0 ? exp_c(ce[B - 1]) : 1.f;
+      FK[B * DK + d] = exp_c(ce[3] - ce[B]);
     }
-    AL[d] = __expf(ce[3]);
+    AL[d] = exp_c(ce[3]);
   }
 }
 
@@ -275,11 +275,11 @@ __device__ __forceinline__ void block_factors(const float *CS, float *FT, int ti
     const int R = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0;
     const int S = p - R * (R + 1) / 2;
     const float cb = R > 0 ? CS[csx<DK>(16 * R - 1, d)] : 0.f;
-    FT[g] = __expf(cb - CS[csx<DK>(16 * S + 15, d)]);
+    FT[g] = exp_c(cb - CS[csx<DK>(16 * S + 15, d)]);
   }
 }
 
-// does block R decay below exp(-kBadLog) in some dimension? (wave-uniform)
+// does block R decay below e^-60 in some dimension? (wave-uniform)
 template <int DK>
 __device__ __forceinline__ bool block_bad(const float *CS, int R, int lane) {
   bool bad = false;
@@ -466,7 +466,7 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
           for (int i = 0; i < 4; ++i) {
             const int d = dc + i;
             const float cb = R > 0 ? CS[csx<DK>(16 * R - 1, d)] : 0.f;
-            const float u = __expf(CS[csx<DK>(r, d)] - cb);
+            const float u = exp_c(CS[csx<DK>(r, d)] - cb);
             // Q-hat exactly as the scaled copy of the dK/dV pass forms it
             // (same factor, same rounding), so the in-chunk paths cancel
             // against k.dk there
@@ -483,7 +483,7 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
                     BS + swz_off<8>(r, s2 >> 3) + (s2 & 7) * 2));
                 const float kd = tof(*reinterpret_cast<const __bf16 *>(
                     KS + swz_off<NCK>(s2, d >> 3) + (d & 7) * 2));
-                v += (bsc * kd) * __expf(CS[csx<DK>(r, d)] - CS[csx<DK>(s2, d)]);
+                v += (bsc * kd) * exp_c(CS[csx<DK>(r, d)] - CS[csx<DK>(s2, d)]);
                 rv += path_term(bsc, qd, kd, CS[csx<DK>(r, d)], CS[csx<DK>(s2, d)]);
               }
             }
@@ -530,7 +530,7 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int s = 32 * kb + 8 * lg + e;
-            y[e] = s < n ? tof(x[e]) * __expf(cn - CS[csx<DK>(s, d)]) : 0.f;
+            y[e] = s < n ? tof(x[e]) * exp_c(cn - CS[csx<DK>(s, d)]) : 0.f;
           }
           kg[dt] = cvt8(y);
 #pragma unroll
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int t = 32 * kb + 8 * lg + e;
-            y[e] = t < n ? tof(x[e]) * (apre[dt] * __expf(CS[csx<DK>(t, d)])) : 0.f;
+            y[e] = t < n ? tof(x[e]) * (apre[dt] * exp_c(CS[csx<DK>(t, d)])) : 0.f;
           }
           qa[dt] = cvt8(y);
         }
@@ -851,7 +851,7 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                       sum += tof(qv[e]) * tof(kv[e]) *
-                             __expf(CS[csx<DK>(r, dd + e)] - CS[csx<DK>(s, dd + e)]);
+                             exp_c(CS[csx<DK>(r, dd + e)] - CS[csx<DK>(s, dd + e)]);
                   }
                 }
                 acc[i] = sum;
@@ -974,7 +974,7 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
           for (int i = 0; i < 4; ++i) {
             const int d = dc + i;
             const float csd = CS[csx<DK>(s, d)];
-            const float ue = __expf(CS[csx<DK>(16 * S + 15, d)] - csd);
+            const float ue = exp_c(CS[csx<DK>(16 * S + 15, d)] - csd);
             // K-hat exactly as the scaled copy formed it (same factor, same
             // rounding), so the in-chunk paths still cancel against q.dq
             const float khd = tof(tobf(tof(kv[i]) * ue));
@@ -988,7 +988,7 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
                     BS + swz_off<8>(s, r >> 3) + (r & 7) * 2));
                 const float qd = tof(*reinterpret_cast<const __bf16 *>(
                     QS + swz_off<NCK>(r, d >> 3) + (d & 7) * 2));
-                v += (bsc * qd) * __expf(CS[csx<DK>(r, d)] - csd);
+                v += (bsc * qd) * exp_c(CS[csx<DK>(r, d)] - csd);
                 rv += path_term(bsc, qd, kd, CS[csx<DK>(r, d)], csd);
               }
             }

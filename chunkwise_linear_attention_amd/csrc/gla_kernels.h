@@ -57,9 +57,13 @@ __device__ __forceinline__ float dpp_add(float x) {
                                            0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, true));
 }
 
+// exp of a difference of cumulative logs, which the kernels keep in base-2
+// units (c log2 e): a single v_exp_f32
+__device__ __forceinline__ float exp_c(float x2) { return __builtin_amdgcn_exp2f(x2); }
+
 // The in-chunk cumulative logs, in place in the [64 x DK] fp32 tile (csx
-// layout): c_r[d] = sum of l_t[d] over t <= r, t < n (rows past the chunk's
-// n tokens repeat its total).  One lane per row: wave w takes the columns
+// layout), in base-2 units: c_r[d] = log2(e) * (sum of l_t[d] over t <= r,
+// t < n) (rows past the chunk's n tokens repeat its total).  One lane per row: wave w takes the columns
 // [w CPW, (w + 1) CPW), reads its row's pieces of them, forms each column's
 // inclusive prefix sum across the 64 lanes by DPP (within every 16-lane row by
 // shifts of 1, 2, 4 and 8 lanes, then across rows by the broadcasts of lanes 15
@@ -95,7 +99,7 @@ __device__ __forceinline__ void cumsum_rows_dpp(float *CS, int n, int tid) {
   for (int p = 0; p < CPW / 4; ++p) {
     f32x4 v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = x[4 * p + e];
+    for (int e = 0; e < 4; ++e) v[e] = x[4 * p + e] * kLog2e;  // base-2 units
     *reinterpret_cast<f32x4 *>(CS + csx<DK>(r, c0 + 4 * p)) = v;
   }
 }
