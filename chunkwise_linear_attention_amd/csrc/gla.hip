@@ -183,27 +183,37 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
 
     // ---- Qh, Kh in place (8 elements per step) ----
     FRESH_LANE();
-    static_assert((64 * NCK) % NTHR == 0, "whole rounds");
-#pragma unroll
-    for (int g0 = 0; g0 < 64 * NCK; g0 += NTHR) {
-      const int g = g0 + tid;
-      const int r = g / NCK, c8 = g % NCK;
-      const int B = r >> 4;
-      const int off = swz_off<NCK>(r, c8);
+    // each thread takes RPT rows of one 16-row block (one 8-column group), so
+    // it reads the block's boundary logs once
+    {
+      constexpr int RPT = 64 * NCK / NTHR, SPB = 16 / RPT;
+      static_assert(RPT * NTHR == 64 * NCK && SPB * RPT == 16, "whole rounds in one block");
+      const int c8 = tid % NCK, q = tid / NCK;
+      const int B = q / SPB, i0 = q % SPB;
       const int re = 16 * B + 15, rb = 16 * B - 1;  // rb read only when B > 0
-      bf16x8 kv = *reinterpret_cast<const bf16x8 *>(KS + off);
-      float yk[8];
+      float ce8[8], cb8[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        yk[e] = r < n ? tof(kv[e]) * exp_c(CS[csx<DK>(re, 8 * c8 + e)] - CS[csx<DK>(r, 8 * c8 + e)]) : 0.f;
-      *reinterpret_cast<bf16x8 *>(KS + off) = cvt8(yk);
-      if (OUT) {
-        bf16x8 qv = *reinterpret_cast<const bf16x8 *>(QS + off);
-        float yq[8];
+      for (int e = 0; e < 8; ++e) {
+        ce8[e] = CS[csx<DK>(re, 8 * c8 + e)];
+        cb8[e] = B > 0 ? CS[csx<DK>(rb, 8 * c8 + e)] : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) {
+        const int r = 16 * B + i0 + k * SPB;
+        const int off = swz_off<NCK>(r, c8);
+        bf16x8 kv = *reinterpret_cast<const bf16x8 *>(KS + off);
+        float yk[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          yq[e] = tof(qv[e]) * exp_c(CS[csx<DK>(r, 8 * c8 + e)] - (B > 0 ? CS[csx<DK>(rb, 8 * c8 + e)] : 0.f));
-        *reinterpret_cast<bf16x8 *>(QS + off) = cvt8(yq);
+          yk[e] = r < n ? tof(kv[e]) * exp_c(ce8[e] - CS[csx<DK>(r, 8 * c8 + e)]) : 0.f;
+        *reinterpret_cast<bf16x8 *>(KS + off) = cvt8(yk);
+        if (OUT) {
+          bf16x8 qv = *reinterpret_cast<const bf16x8 *>(QS + off);
+          float yq[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) yq[e] = tof(qv[e]) * exp_c(CS[csx<DK>(r, 8 * c8 + e)] - cb8[e]);
+          *reinterpret_cast<bf16x8 *>(QS + off) = cvt8(yq);
+        }
       }
     }
     lds_barrier();
