@@ -289,15 +289,23 @@ __device__ __forceinline__ void block_factors(const float *CS, float *FT, int ti
   }
 }
 
-// does block R decay below e^-60 in some dimension? (wave-uniform)
+// Bit R set: block R of the chunk decays below e^-60 in some dimension
+// (wave-uniform; formed once per chunk from the four block-end rows)
 template <int DK>
-__device__ __forceinline__ bool block_bad(const float *CS, int R, int lane) {
-  bool bad = false;
-  for (int d = lane; d < DK; d += 64) {
-    const float cb = R > 0 ? CS[csx<DK>(16 * R - 1, d)] : 0.f;
-    bad |= cb - CS[csx<DK>(16 * R + 15, d)] > kBadLog;
+__device__ __forceinline__ uint32_t bad_blocks(const float *CS, int lane) {
+  uint32_t mask = 0;
+#pragma unroll
+  for (int R = 0; R < 4; ++R) {
+    bool bad = false;
+#pragma unroll
+    for (int d0 = 0; d0 < DK; d0 += 64) {
+      const int d = d0 + lane;
+      const float cb = R > 0 ? CS[csx<DK>(16 * R - 1, d)] : 0.f;
+      bad |= cb - CS[csx<DK>(16 * R + 15, d)] > kBadLog;
+    }
+    if (__ballot(bad) != 0) mask |= 1u << R;
   }
-  return __ballot(bad) != 0;
+  return mask;
 }
 
 // ===========================================================================
@@ -404,6 +412,7 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
     lds_barrier();
     FRESH_LANE();
     cumsum_rows<DK, NT>(CS, n, tid);
+    const uint32_t bad_mask = bad_blocks<DK>(CS, lane);
     FRESH_LANE();
     // (no Qh copy: this pass needs only this lane's few Qh values, re-formed
     // where they are used)
@@ -443,7 +452,7 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
         for (int dt = 0; dt < NDT; ++dt) sfrag[kk][dt] = cvt8(ST_acc[2 * kk][dt], ST_acc[2 * kk + 1][dt]);
 #pragma unroll
       for (int R = 0; R < 4; ++R) {
-        const bool good = !block_bad<DK>(CS, R, lane);
+        const bool good = !((bad_mask >> R) & 1u);
         const int r = 16 * R + li;
         bf16x8 dofrag[DV / 32];  // dO^T B operands: k = j (same permutation), n = r
 #pragma unroll
@@ -808,6 +817,7 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
     lds_barrier();
     FRESH_LANE();
     cumsum_rows<DK, BTHR>(CS, n, tid);
+    const uint32_t bad_mask = bad_blocks<DK>(CS, lane);
     FRESH_LANE();
     prep_scaled<DK, BTHR>(QS, KS, QH, KH, CS, FQ, FK, AL, n, tid);
     block_factors<DK, BTHR>(CS, FT, tid);
@@ -831,7 +841,7 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
         // acc[i] = X[r = 16R + 4lg + i][s = 16S + li]
         if (S <= R) {
           if (is_a) {
-            const bool good = R != S || !block_bad<DK>(CS, R, lane);
+            const bool good = R != S || !((bad_mask >> R) & 1u);
             if (good) {
 #pragma unroll
               for (int kk = 0; kk < DK / 32; ++kk) {
@@ -953,7 +963,7 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
       // through `carry` (later rows of this segment plus its boundary term)
       for (int S = 3; S >= 0; --S) {
         const int s = 16 * S + li;
-        const bool good = !block_bad<DK>(CS, S, lane);
+        const bool good = !((bad_mask >> S) & 1u);
         bf16x8 vfr[DV / 32];  // V^T B operands: k = j (same permutation), n = s
 #pragma unroll
         for (int kk = 0; kk < DV / 32; ++kk)
