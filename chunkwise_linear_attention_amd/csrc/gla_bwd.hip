@@ -815,6 +815,21 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
+    // this lane's q.dq (rows s = 16 S + li, its 4 dimensions of each d tile),
+    // loaded here so that the phases before the dk side hide their latency
+    f32x4 r1b[4][NI];
+    if (do_dk) {
+      FRESH_LANE();
+#pragma unroll
+      for (int S = 0; S < 4; ++S)
+#pragma unroll
+        for (int it = 0; it < NI; ++it) {
+          const int s = 16 * S + li;
+          r1b[S][it] = s < n ? *reinterpret_cast<const f32x4 *>(
+                                   a.r1 + (bh * T + t0 + s) * DK + d0 + 16 * it + 4 * lg)
+                             : zero4();
+        }
+    }
     FRESH_LANE();
     cumsum_rows<DK, BTHR>(CS, n, tid);
     const uint32_t bad_mask = bad_blocks<DK>(CS, lane);
@@ -945,20 +960,6 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
       for (int kk = 0; kk < DV / 32; ++kk)
 #pragma unroll
         for (int it = 0; it < NI; ++it) gfrag[kk][it] = cvt8(G1(2 * kk, it), G1(2 * kk + 1, it));
-      // q.dq of this lane's rows and dimensions, loaded two blocks ahead of
-      // their use so that the load latency overlaps the block products
-      f32x4 r1c[NI], r1n[NI];  // block S's rows, block S - 1's rows
-      auto load_r1 = [&](int S, f32x4 (&dst)[NI]) {
-#pragma unroll
-        for (int it = 0; it < NI; ++it) {
-          const int s = 16 * S + li;
-          dst[it] = s < n ? *reinterpret_cast<const f32x4 *>(
-                                a.r1 + (bh * T + t0 + s) * DK + d0 + 16 * it + 4 * lg)
-                          : zero4();
-        }
-      };
-      load_r1(3, r1c);
-      load_r1(2, r1n);
       // blocks last to first: the suffix sums of x = q.dq - k.dk over s run
       // through `carry` (later rows of this segment plus its boundary term)
       for (int S = 3; S >= 0; --S) {
@@ -1015,13 +1016,9 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
             out[i] = v;
             r2v[i] = rv;
           }
-          const f32x4 r1 = r1c[it];
-          if (s < n) {
-            bf16x4 ov;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ov[i] = tobf(out[i]);
-            *reinterpret_cast<bf16x4 *>(a.dk + (bh * T + t0 + s) * DK + dc) = ov;
-          }
+          const f32x4 r1 = r1b[S][it];
+          // (the decay gradient first: its q.dq loads are then waited for
+          // before this block's stores are issued, not after them)
           f32x4 dl4;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -1035,12 +1032,14 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
             dl4[i] = x + carry[it][i];
             carry[it][i] += tot;
           }
-          if (s < n)
-            *reinterpret_cast<f32x4 *>(a.dl + (bh * T + t0 + s) * DK + dc) = dl4;
-        }
+          if (s < n) {
+            bf16x4 ov;
 #pragma unroll
-        for (int it = 0; it < NI; ++it) r1c[it] = r1n[it];
-        if (S >= 2) load_r1(S - 2, r1n);
+            for (int i = 0; i < 4; ++i) ov[i] = tobf(out[i]);
+            *reinterpret_cast<bf16x4 *>(a.dk + (bh * T + t0 + s) * DK + dc) = ov;
+            *reinterpret_cast<f32x4 *>(a.dl + (bh * T + t0 + s) * DK + dc) = dl4;
+          }
+        }
       }
     }
 
