@@ -910,11 +910,14 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
       }
     }
     lds_barrier();
-    // KH -> KG = KH (.) FK[S] in place: the dv product's operand, which every
-    // wave reads, formed once here instead of by each wave.  The dk side
-    // re-forms the K-hat values it needs from k and the factor it computes.
+    // KH -> KG = KH (.) FK[S] in place, the dv product's operand, and QL =
+    // Qh (.) FQ[R] over the raw q tile, the state update's: every wave reads
+    // them in full, so they are formed once here instead of by each wave.
+    // The dk side re-forms the K-hat values it needs from k and the factor
+    // it computes, and its exact path reads raw q from global memory.
     FRESH_LANE();
     scale_rows_by_block<DK, BTHR>(KH, KH, FK, tid);
+    scale_rows_by_block<DK, BTHR>(QH, QS, FQ, tid);
     lds_barrier();
 
     if (do_dv) {
@@ -1007,8 +1010,8 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
               for (int r = s; r < min(16 * S + 16, n); ++r) {
                 const float bsc = tof(*reinterpret_cast<const __bf16 *>(
                     BS + swz_off<8>(s, r >> 3) + (r & 7) * 2));
-                const float qd = tof(*reinterpret_cast<const __bf16 *>(
-                    QS + swz_off<NCK>(r, d >> 3) + (d & 7) * 2));
+                // (raw q from global memory: its LDS tile holds QL by now)
+                const float qd = tof(*reinterpret_cast<const __bf16 *>(qh + (t0 + r) * DK + d));
                 v += (bsc * qd) * exp_c(CS[csx<DK>(r, d)] - csd);
                 rv += path_term(bsc, qd, kd, CS[csx<DK>(r, d)], csd);
               }
@@ -1044,14 +1047,11 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
     }
 
     // ---- G <- diag(alpha) G + QL^T dO (both copies) ----
-    // QL = Qh (.) FQ[R] over the raw q tile (no longer read), formed once
-    // for every wave; the next chunk's k, v and logs start streaming in
+    // the next chunk's k, v and logs start streaming in (every read of them
+    // in this chunk is done)
     lds_barrier();
     FRESH_LANE();
     if (ci > c_begin) stage_kvl(ci - 1);
-    FRESH_LANE();
-    scale_rows_by_block<DK, BTHR>(QH, QS, FQ, tid);
-    lds_barrier();
     {
       FRESH_LANE();
       if (do_dv) {
