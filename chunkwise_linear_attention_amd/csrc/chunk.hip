@@ -82,9 +82,10 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   constexpr int QB = 64 * DK * 2, VB = 64 * DV * 2;
   // Staging buffer [Q | K | V | X | l] (X: the optional xdot rows).  It is
   // double-buffered (the next chunk streams in by DMA while this one is used)
-  // when two workgroups per CU still fit in LDS; the two buffers are separate
-  // arrays so that the compiler can tell the DMA target from the buffer being
-  // read.
+  // when two workgroups per CU still fit in LDS.  The copies are issued
+  // untracked (the compiler had waited for them in front of LDS reads it could
+  // not tell apart from their target); each staged chunk is waited for
+  // explicitly before it is read.
   constexpr int B_KS = QB;
   constexpr int B_VS = B_KS + QB;
   constexpr int B_XS = B_VS + VB;
@@ -201,25 +202,28 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     // the per-lane DMA addresses are formed here, at each stage, instead of
     // being kept live (one 64-bit pair per staged tensor) across the loop
     const int ln = fresh(lane);
+    const uint32_t lb = staging_base(buf);
     // wave w takes blocks w, w + NWAVE, ...; every tensor's block count is a
     // multiple of NWAVE, so the tensor of each round is known at compile time
     static_assert(NBQ % NWAVE == 0 && NBK % NWAVE == 0 && NBV % NWAVE == 0, "rounds");
 #pragma unroll
     for (int r0 = 0; r0 < NBQ + NBK + NBV + (XD ? NBV : 0); r0 += NWAVE) {
       const int b = w + r0;
+      // (untracked copies: every staged chunk is waited for explicitly)
       if (r0 < NBQ) {
-        dma_block<DK>(qh + tj * DK, nj, buf, b, ln);
+        lds_copy16_untracked(bf16_block_src<DK>(qh + tj * DK, nj, b, ln), lb + b * 1024);
       } else if (r0 < NBQ + NBK) {
-        dma_block<DK>(kh + tj * DK, nj, buf + B_KS, b - NBQ, ln);
+        lds_copy16_untracked(bf16_block_src<DK>(kh + tj * DK, nj, b - NBQ, ln),
+                             lb + B_KS + (b - NBQ) * 1024);
       } else if (r0 < NBQ + NBK + NBV) {
-        dma_block<DV>(vh + tj * DV, nj, buf + B_VS, b - NBQ - NBK, ln);
+        lds_copy16_untracked(bf16_block_src<DV>(vh + tj * DV, nj, b - NBQ - NBK, ln),
+                             lb + B_VS + (b - NBQ - NBK) * 1024);
       } else {
-        dma_block<DV>(xh + tj * DV, nj, buf + B_XS, b - NBQ - NBK - NBV, ln);
+        lds_copy16_untracked(bf16_block_src<DV>(xh + tj * DV, nj, b - NBQ - NBK - NBV, ln),
+                             lb + B_XS + (b - NBQ - NBK - NBV) * 1024);
       }
     }
-    if (w == 0)
-      __builtin_amdgcn_global_load_lds(lh + tj + min(ln, nj - 1), (lds_void *)(buf + B_L), 4, 0,
-                                       0);
+    if (w == 0) lds_copy4_untracked(lh + tj + min(ln, nj - 1), lb + B_L);
   };
 
   // the xdot sums of the previous chunk, from RD
@@ -625,17 +629,18 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_state_kernel(FwdArgs a) {
     const int64_t tj = cj * TC;
     const int nj = (int)min<int64_t>(TC, T - tj);
     static_assert(NBK % NWAVE == 0 && NBV % NWAVE == 0, "rounds");
+    const uint32_t lb = staging_base(buf);
 #pragma unroll
     for (int r0 = 0; r0 < NBLK; r0 += NWAVE) {
       const int b = w + r0;
+      // (untracked copies: every staged chunk is waited for explicitly)
       if (r0 < NBK)
-        dma_block<DK>(kh + tj * DK, nj, buf, b, lane);
+        lds_copy16_untracked(bf16_block_src<DK>(kh + tj * DK, nj, b, lane), lb + b * 1024);
       else
-        dma_block<DV>(vh + tj * DV, nj, buf + B_VS, b - NBK, lane);
+        lds_copy16_untracked(bf16_block_src<DV>(vh + tj * DV, nj, b - NBK, lane),
+                             lb + B_VS + (b - NBK) * 1024);
     }
-    if (w == 0)
-      __builtin_amdgcn_global_load_lds(lh + tj + min(lane, nj - 1), (lds_void *)(buf + B_L), 4, 0,
-                                       0);
+    if (w == 0) lds_copy4_untracked(lh + tj + min(lane, nj - 1), lb + B_L);
   };
 
   auto compute = [&](int64_t ci, const unsigned char *cur) __attribute__((always_inline)) {

@@ -55,8 +55,9 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
   // Two staging buffers, each [Q | dO | K | V] (the log decays go to
   // registers):
   // the next chunk streams into one by DMA while the other is being used.
-  // They are separate arrays so that the compiler can tell the DMA target
-  // from the buffer being read and does not wait for the DMA before reads.
+  // The copies are issued untracked: with the builtin the compiler waited for
+  // the whole DMA at the first score-tile write (it cannot tell the score
+  // tiles from the DMA target); the step waits for it at its end instead.
   constexpr int B_DOS = RK;
   constexpr int B_KS = B_DOS + RV;
   constexpr int B_VS = B_KS + RK;
@@ -206,6 +207,7 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
     // the per-lane DMA addresses are formed here, at each stage, instead of
     // being kept live (one 64-bit pair per staged tensor) across the loop
     const int ln = fresh(lane);
+    const uint32_t lb = staging_base(buf);
     // wave w takes blocks w, w + 8, ...; every tensor's block count is a
     // multiple of 8, so the tensor of each round is known at compile time
     constexpr int NW = BTHR / 64;
@@ -213,14 +215,18 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
 #pragma unroll
     for (int r0 = 0; r0 < NBLK; r0 += NW) {
       const int b = w + r0;
+      // (untracked copies: the step waits for them at its end)
       if (r0 < NBQ) {
-        dma_block<DK>(qh + tj * DK, nj, buf, b, ln);
+        lds_copy16_untracked(bf16_block_src<DK>(qh + tj * DK, nj, b, ln), lb + b * 1024);
       } else if (r0 < NBQ + NBD) {
-        dma_block<DV>(doh + tj * DV, nj, buf + B_DOS, b - NBQ, ln);
+        lds_copy16_untracked(bf16_block_src<DV>(doh + tj * DV, nj, b - NBQ, ln),
+                             lb + B_DOS + (b - NBQ) * 1024);
       } else if (r0 < NBQ + NBD + NBK) {
-        dma_block<DK>(kh + tj * DK, nj, buf + B_KS, b - NBQ - NBD, ln);
+        lds_copy16_untracked(bf16_block_src<DK>(kh + tj * DK, nj, b - NBQ - NBD, ln),
+                             lb + B_KS + (b - NBQ - NBD) * 1024);
       } else {
-        dma_block<DV>(vh + tj * DV, nj, buf + B_VS, b - NBQ - NBD - NBK, ln);
+        lds_copy16_untracked(bf16_block_src<DV>(vh + tj * DV, nj, b - NBQ - NBD - NBK, ln),
+                             lb + B_VS + (b - NBQ - NBD - NBK) * 1024);
       }
     }
     // this lane's log decay, used when the chunk is computed (rows past the

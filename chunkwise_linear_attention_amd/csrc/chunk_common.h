@@ -193,6 +193,55 @@ __device__ __forceinline__ void dma_block(const uint16_t *chunk_src, int n, unsi
                                    (lds_void *)(tile + block * 1024), 16, 0, 0);
 }
 
+// The global address of the 16 bytes lane `lane` copies for block `block`
+// of such a tile (the address dma_block fetches).
+template <int D>
+__device__ __forceinline__ const uint16_t *bf16_block_src(const uint16_t *chunk_src, int n,
+                                                          int block, int lane) {
+  constexpr int NCH = D / 8;
+  constexpr int RPB = 64 / NCH;
+  const int row = block * RPB + lane / NCH;
+  const int c = (lane % NCH) ^ swz_pat(row);
+  const int grow = min(row, n - 1);
+  return chunk_src + (int64_t)grow * D + c * 8;
+}
+
+// The same copies as global_load_lds (16 or 4 bytes per lane into an LDS
+// block, lane i at byte offset i times the size), issued from inline assembly
+// with the block's LDS address passed in M0.  The compiler does not see these
+// loads, so it inserts no wait for them: not in front of LDS accesses it
+// cannot tell apart from the target (where the builtin gets a vmcnt(0) that
+// holds all later work until the copy lands), nor anywhere else.  The caller
+// waits (vmcnt(0)) and synchronizes the workgroup before any lane touches the
+// target.  Loads the compiler does track stay correctly waited for: vector
+// memory operations complete in issue order, so one it does not count only
+// makes its counted waits (vmcnt(N)) wait longer.
+// (M0 takes the LDS byte address of the block, a wave-uniform value.)
+__device__ __forceinline__ void lds_copy16_untracked(const void *src, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_addr)
+               : "memory");
+}
+
+__device__ __forceinline__ void lds_copy4_untracked(const void *src, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(src), "{m0}"(lds_addr)
+               : "memory");
+}
+
+__device__ __forceinline__ void lds_copy16_untracked(const void *src, unsigned char *lds_block) {
+  lds_copy16_untracked(
+      src, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds_block));
+}
+
+// The LDS byte address of a staging buffer, re-derived behind an empty asm at
+// each staging call: the block addresses added to it are then formed next to
+// their copies instead of being computed once and kept live (in SGPRs, which
+// then spill) across the chunk loop.
+__device__ __forceinline__ uint32_t staging_base(const unsigned char *buf) {
+  uint32_t x = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void *)buf);
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
 // ---------------------------------------------------------------------------
 // Transposed fragment reads (ds_read_b64_tr_b16).  Within each 16-lane group
 // the hardware returns result[i][e] = src[4 e + i / 4][i % 4], where src[j] is

@@ -77,34 +77,6 @@ __device__ __forceinline__ float path_term(float b, float q, float k, float ct, 
 
 // DMA of the [64 x D] fp32 log tile in the swizzled layout of csx: 1 KB
 // blocks of RPB rows; rows past the chunk re-read row n - 1.
-// the global address of the 16 bytes lane `lane` copies for block `block` of a
-// bf16 tile (as dma_block fetches it)
-template <int D>
-__device__ __forceinline__ const uint16_t *bf16_block_src(const uint16_t *chunk_src, int n,
-                                                          int block, int lane) {
-  constexpr int NCH = D / 8;
-  constexpr int RPB = 64 / NCH;
-  const int row = block * RPB + lane / NCH;
-  const int c = (lane % NCH) ^ swz_pat(row);
-  const int grow = min(row, n - 1);
-  return chunk_src + (int64_t)grow * D + c * 8;
-}
-
-// The same copy as global_load_lds (16 bytes per lane into a 1 KB LDS
-// block), issued from inline assembly with the block's LDS address passed in
-// M0.  The compiler does not see this load, so it inserts no wait for it: not
-// in front of LDS reads it cannot tell apart from the target (where the
-// builtin gets a vmcnt(0) that holds all later work until the copy lands),
-// nor anywhere else.  The caller waits (vmcnt(0)) and synchronizes the
-// workgroup before any lane reads the target.  Loads the compiler does track
-// stay correctly waited for: vector loads complete in issue order, so a load
-// it does not count only makes its counted waits (vmcnt(N)) wait longer.
-__device__ __forceinline__ void lds_copy16_untracked(const void *src, unsigned char *lds_block) {
-  const uint32_t m0v =
-      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds_block);
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0v) : "memory");
-}
-
 template <int D>
 __device__ __forceinline__ const float *dma_f32_rows_src(const float *chunk_src, int n, int block,
                                                          int lane) {
