@@ -369,7 +369,7 @@ def bench_chunk(args, torch, cla, wl, steps, warmup, cpu_heads=0):
         avg = tot / cnt
         ent = {"avg_ms": round(avg, 5), "launches_per_step": cnt // steps,
                "share": round(tot / sum(x[0] for x in table.values()), 4)}
-        if name in ("chunk_fwd", "chunk_dq", "chunk_dkdv", "chunk_dlog"):
+        if name in ("chunk_fwd", "chunk_dq", "chunk_dkdv"):
             # every token-head once per launch (segment passes cover a
             # fraction and are reported by time only)
             per = pm.chunk_kernel_bytes(name, DK, DV)

@@ -867,7 +867,7 @@ struct BwdWs {
   FwdWs seg;   // dQ pass: slots p = S^T entering segment p + 1
   FwdWs gseg;  // reverse pass: slots p = G at the end of segment p
   float *Send; // dQ pass: [P-1, nh] S^T at the end of segment p, as that pass held it
-  float *r1, *r2, *ST, *Bnd;
+  float *r1, *ST;
   size_t bytes;
 };
 
@@ -884,9 +884,7 @@ BwdWs bwd_ws(void *base, int64_t nh, int64_t T, int64_t P, int64_t DK, int64_t D
   };
   w.Send = P > 1 ? carve((size_t)(P - 1) * nh * DK * DV * sizeof(float)) : nullptr;
   w.r1 = carve((size_t)nh * T * sizeof(float));
-  w.r2 = carve((size_t)nh * T * sizeof(float));
   w.ST = carve((size_t)nh * DK * DV * sizeof(float));
-  w.Bnd = carve((size_t)P * nh * sizeof(float));
   w.bytes = off;
   return w;
 }
@@ -1037,21 +1035,20 @@ hipError_t launch_chunk_bwd(const uint16_t *q, const uint16_t *k, const uint16_t
   ba.dST = dST;
   ba.dk = dk;
   ba.dv = dv;
-  ba.r2 = w.r2;
+  ba.r1 = w.r1;
+  ba.dl = dl;
   ba.dS0 = dS0;
   ba.Gloc = w.gseg.Sloc;
   ba.aloc = w.gseg.aloc;
   ba.Sseg = w.Send;
   ba.STb = dST ? w.ST : nullptr;
-  ba.Bnd = w.Bnd;
   ba.nh = nh;
   ba.T = T;
   ba.seg_chunks = plan.seg_chunks_b;
   ba.P = plan.P_b;
   e = chunk::bwd_kv_dispatch(ba, (int)DK, (int)DV, stream);
   if (e != hipSuccess) return e;
-  return chunk::launch_dlog(w.r1, w.r2, w.Bnd, dl, nh, T, plan.seg_chunks_b * chunk::TC,
-                            plan.P_b, stream);
+  return hipSuccess;
 }
 
 }  // namespace cla

@@ -1,5 +1,5 @@
-// Chunkwise linear attention, backward pass: the reverse-order dK/dV kernel
-// and the decay-gradient kernel, for gfx950.  The dQ pass is the forward
+// Chunkwise linear attention, backward pass: the reverse-order dK/dV kernel,
+// which also forms the decay gradient, for gfx950.  The dQ pass is the forward
 // kernel run on (dO, V, K) (chunk.hip).
 //
 // Citations (page title, then section / equation):
@@ -41,7 +41,7 @@ namespace {
 
 constexpr int BTHR = 512;
 
-// dK, dV, r2 and dS0 of one segment, starting from the G at its end (dS_T
+// dK, dV, the decay gradient and dS0 of one segment, starting from the G at its end (dS_T
 // for the last segment; the segment-local G states come from the dQ pass).
 // At DK = DV = 64 two workgroups (16 waves) share a CU, four waves per SIMD:
 // the register budget is then 128 per lane.
@@ -162,6 +162,7 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
       }
     }
   }
+  double dl_carry = 0.0;  // wave 0: the decay gradient's running suffix sum
   {
     // Boundary term of the decay gradient: <S, G> at this segment's end, from
     // the fp32 state S^T that the dQ pass held at that boundary (S_T^T for
@@ -188,14 +189,34 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
     double *bred = reinterpret_cast<double *>(P1);
     if (lane == 0) bred[w] = part;
     __syncthreads();
-    if (tid == 0) {
-      double b = 0.0;
-      for (int u = 0; u < 8; ++u) b += bred[u];
-      a.Bnd[seg * a.nh + bh] = (float)b;
+    if (w == 0) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) dl_carry += bred[u];
     }
   }
   int64_t r2_t0 = -1;  // chunk whose k.dk partials sit in the P2 spare pieces
   int r2_n = 0;
+  // wave 0: q.dq of the staged chunk (one token per lane), and of the chunk
+  // whose decay gradient is formed next
+  float r1_next = 0.f, r1_prev = 0.f;
+
+  // Decay gradient of one chunk by wave 0, token t on lane t:
+  //   dl_t = carry + sum_{u >= t in the chunk} (r1_u - r2_u),
+  // r1 = q.dq (the dQ pass), r2 = k.dk (this pass); the chunk's total then
+  // joins the carry, which starts at <S, G> at the segment's end (the sum over
+  // all paths that cross it) and runs backwards through the segment's chunks.
+  // fp64 accumulation throughout.
+  auto chunk_dl = [&](float r1, float r2, int nrows) __attribute__((always_inline)) -> float {
+    double sfx = lane < nrows ? (double)r1 - (double)r2 : 0.0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double y = __shfl_down(sfx, o, 64);
+      if (lane + o < 64) sfx += y;
+    }
+    const float out = (float)(dl_carry + sfx);
+    dl_carry += __shfl(sfx, 0, 64);
+    return out;
+  };
 
   // DMA of chunk cj into a staging buffer: 1 KB row blocks spread over the
   // waves; every wave loads the chunk's log decays, one per lane, into a
@@ -232,6 +253,7 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
     // this lane's log decay, used when the chunk is computed (rows past the
     // chunk read l = 0 there)
     l_next = ln < nj ? lh[tj + ln] : 0.f;
+    if (w == 0) r1_next = ln < nj ? a.r1[bh * T + tj + ln] : 0.f;
   };
 
   // One chunk from staging buffer `cur`, while the chunk before it streams
@@ -245,15 +267,16 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
     unsigned char *KS = cur + B_KS;
     unsigned char *VS = cur + B_VS;
     const float l_cur = l_next;
+    const float r1_cur = r1_next;
 
     if (ci > c_begin) stage(ci - 1, nxt);
-    // the previous chunk's k.dk sums, stored at the end of this step (a store
-    // issued here would hold its data register while the DMA is in flight)
-    float r2_sum = 0.f;
-    const int64_t r2_row = r2_t0;
-    const int r2_prev_n = r2_n;
-    if (r2_t0 >= 0 && tid < r2_n)
-      r2_sum = r2p_sum(tid);
+    // the previous chunk's k.dk sums (complete; this step overwrites them):
+    // its decay gradient is formed and stored at the end of the step, where
+    // wave 0's side waits for the other (a store issued here would also hold
+    // its data register while the DMA is in flight)
+    const int64_t dl_row = r2_t0;
+    const int dl_n = r2_n;
+    const float r2_prev = w == 0 && r2_t0 >= 0 && lane < r2_n ? r2p_sum(lane) : 0.f;
     // In-chunk decays, one token per lane, computed by every wave (lanes
     // are then read with cross-lane shuffles).  Rows past the chunk: no
     // decay, and lambda = 0 so that they add nothing to the state gradient.
@@ -484,7 +507,11 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
     }
     r2_t0 = t0;
     r2_n = n;
-    if (r2_row >= 0 && tid < r2_prev_n) a.r2[bh * T + r2_row + fresh(tid)] = r2_sum;
+    if (w == 0 && dl_row >= 0) {
+      const float dl_val = chunk_dl(r1_prev, r2_prev, dl_n);
+      if (lane < dl_n) a.dl[bh * T + dl_row + fresh(lane)] = dl_val;
+    }
+    r1_prev = r1_cur;
     // the next chunk has landed; this chunk's buffer is free
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -497,8 +524,10 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
     step(ci, buf0, buf1);
     if (ci - 1 >= c_begin) step(ci - 1, buf1, buf0);
   }
-  if (r2_t0 >= 0 && tid < r2_n)
-    a.r2[bh * T + r2_t0 + tid] = r2p_sum(tid);
+  if (w == 0 && r2_t0 >= 0) {
+    const float v = chunk_dl(r1_prev, lane < r2_n ? r2p_sum(lane) : 0.f, r2_n);
+    if (lane < r2_n) a.dl[bh * T + r2_t0 + lane] = v;
+  }
 
   // ---- segment outputs ----
   if (seg == 0 && a.dS0 && side == 0) {
@@ -516,50 +545,6 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
 #undef G0
 #undef G1
 #undef FRESH_LANE
-
-// Decay gradient of one segment of one sequence (one workgroup each):
-//   dl_u = B + sum_{t >= u, t in segment} (r1_t - r2_t),
-// B = the sum over all paths that cross the segment's end, i.e. <S, G> at
-// that boundary (computed exactly from the two fp32 states by the dK/dV
-// pass).  fp64 accumulation throughout.
-constexpr int DL_THR = 256;
-constexpr int DL_PER = 16;  // tokens per thread; segments hold <= 4096 tokens
-
-__global__ __launch_bounds__(DL_THR) void dlog_kernel(const float *r1, const float *r2,
-                                                      const float *Bnd, float *dl, int64_t nh,
-                                                      int64_t T, int64_t seg_len) {
-  __shared__ double red[DL_THR];
-  const int64_t bh = blockIdx.x % nh;
-  const int64_t seg = blockIdx.x / nh;
-  const int tid = threadIdx.x;
-  const double B = (double)Bnd[seg * nh + bh];
-  const int64_t s0 = seg * seg_len, s1 = min(T, s0 + seg_len);
-  const int64_t lo = min(s1, s0 + (int64_t)tid * DL_PER), hi = min(s1, lo + DL_PER);
-  const float *x1 = r1 + bh * T, *x2 = r2 + bh * T;
-  double x[DL_PER];
-  double local = 0.0;
-#pragma unroll
-  for (int i = 0; i < DL_PER; ++i) {
-    x[i] = (lo + i < hi) ? (double)x1[lo + i] - (double)x2[lo + i] : 0.0;
-    local += x[i];
-  }
-  red[tid] = local;
-  __syncthreads();
-  // suffix sums over threads (Hillis-Steele from the right)
-  for (int o = 1; o < DL_THR; o <<= 1) {
-    const double add = (tid + o < DL_THR) ? red[tid + o] : 0.0;
-    __syncthreads();
-    red[tid] += add;
-    __syncthreads();
-  }
-  double acc = B + (tid + 1 < DL_THR ? red[tid + 1] : 0.0);
-  float *out = dl + bh * T;
-#pragma unroll
-  for (int i = DL_PER - 1; i >= 0; --i) {
-    acc += x[i];
-    if (lo + i < hi) out[lo + i] = (float)acc;
-  }
-}
 
 template <int DK, int DV>
 hipError_t bwd_kv_impl(BwdArgs args, hipStream_t stream) {
@@ -586,14 +571,6 @@ hipError_t bwd_kv_dispatch(const BwdArgs &args, int DK, int DV, hipStream_t stre
   if (DK == 128 && DV == 64) return bwd_kv_impl<128, 64>(args, stream);
   if (DK == 128 && DV == 128) return bwd_kv_impl<128, 128>(args, stream);
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_dlog(const float *r1, const float *r2, const float *Bnd, float *dl, int64_t nh,
-                       int64_t T, int64_t seg_len, int64_t P, hipStream_t stream) {
-  if (seg_len > (int64_t)DL_THR * DL_PER) return hipErrorInvalidValue;
-  CLA_LAUNCH("chunk_dlog", dlog_kernel, dim3((unsigned)(nh * P)), dim3(DL_THR), stream, r1, r2,
-             Bnd, dl, nh, T, seg_len);
-  return hipGetLastError();
 }
 
 }  // namespace chunk

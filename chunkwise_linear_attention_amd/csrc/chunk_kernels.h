@@ -43,7 +43,8 @@ struct BwdArgs {
   const float *dST;                 // [nh, DK, DV] or NULL
   const float *Gin;                 // [P-1, nh, DK, DV]: G at the end of segments 0..P-2
   uint16_t *dk, *dv;                // [nh, T, DK|DV]
-  float *r2;                        // [nh, T]  k . dk
+  const float *r1;                  // [nh, T]  q . dq (from the dQ pass)
+  float *dl;                        // [nh, T]  the decay gradient
   float *dS0;                       // [nh, DK, DV] or NULL
   float *Gloc;                      // [P-1, nh, DK, DV]: segment p's local G state in slot
                                     // p-1 (written by the dQ pass); the reverse segment
@@ -52,7 +53,6 @@ struct BwdArgs {
   const float *Sseg;                // [P-1, nh, DV, DK]: S^T at the end of segments 0..P-2
                                     // as the dQ pass held it
   const float *STb;                 // [nh, DV, DK]: S_T^T (NULL when there is no dS_T)
-  float *Bnd;                       // [P, nh]: <S, G> at the end of each segment
   int64_t nh, T, seg_chunks, P;
 };
 
@@ -74,11 +74,6 @@ hipError_t bwd_kv_dispatch(const BwdArgs &args, int DK, int DV, hipStream_t stre
 hipError_t launch_segment_scan(float *slots, const float *aloc, const float *init,
                                int init_trans, int reverse, int64_t nh, int64_t P,
                                int DK, int DV, hipStream_t stream);
-
-// dl_u for u in segment p = Bnd[p] + sum_{t >= u, t in segment p} (r1_t - r2_t),
-// with Bnd[p] = <S, G> at the end of segment p (computed by the dK/dV pass).
-hipError_t launch_dlog(const float *r1, const float *r2, const float *Bnd, float *dl, int64_t nh,
-                       int64_t T, int64_t seg_len, int64_t P, hipStream_t stream);
 
 }  // namespace chunk
 }  // namespace cla

@@ -106,14 +106,13 @@ def chunk_kernel_bytes(name: str, dk: int, dv: int) -> int:
     """chunk_fwd : q, k, v, l in; o out (the forward per-unit figure).
     chunk_dq    : dO, v, k, l, q in; dq, q.dq out (plus, with segments, one
                   fp32 state per segment, not per token).
-    chunk_dkdv  : q, k, v, dO, l in; dk, dv, k.dk out.
-    chunk_dlog  : q.dq, k.dk in; dl out.
+    chunk_dkdv  : q, k, v, dO, l, q.dq in; dk, dv, dl out (the decay
+                  gradient's suffix sums are formed in this pass).
     *_segments  : the inputs of the state recurrence only (k, v, l)."""
     table = {
         "chunk_fwd": chunk_bytes_per_token_head(dk, dv, "fwd"),
         "chunk_dq": 2 * dv + 2 * dv + 2 * dk + 4 + 2 * dk + 2 * dk + 4,
-        "chunk_dkdv": 2 * dk + 2 * dk + 2 * dv + 2 * dv + 4 + 2 * dk + 2 * dv + 4,
-        "chunk_dlog": 12,
+        "chunk_dkdv": 2 * dk + 2 * dk + 2 * dv + 2 * dv + 4 + 4 + 2 * dk + 2 * dv + 4,
         "chunk_fwd_segments": 2 * dk + 2 * dv + 4,
         "chunk_dq_segments": 2 * dv + 2 * dk + 4,
     }
