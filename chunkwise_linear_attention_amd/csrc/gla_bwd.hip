@@ -452,17 +452,22 @@ __global__ __launch_bounds__(dq_threads<DK>(), 1) void gla_dq_kernel(GlaBwdArgs 
           for (int kk = 0; kk < DV / 32; ++kk) acc2 = mfma(sfrag[kk][dt], dofrag[kk], acc2);
           // accI[i], acc2[i] at d = dc + i, row t = r
           const bf16x4 qv = lds_half<NCK>(QS, min(r, 63), dc);
+          // this lane's 4 dimensions are one 16-byte piece of each row (dc is
+          // a multiple of 4): read as such, not as 4 separate words
+          const f32x4 cbv = R > 0 ? *reinterpret_cast<const f32x4 *>(CS + csx<DK>(16 * R - 1, dc))
+                                  : zero4();
+          const f32x4 crv = *reinterpret_cast<const f32x4 *>(CS + csx<DK>(r, dc));
+          const f32x4 fqv = *reinterpret_cast<const f32x4 *>(FQ + R * DK + dc);
           float out[4], r1v[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int d = dc + i;
-            const float cb = R > 0 ? CS[csx<DK>(16 * R - 1, d)] : 0.f;
-            const float u = exp_c(CS[csx<DK>(r, d)] - cb);
+            const float u = exp_c(crv[i] - cbv[i]);
             // Q-hat exactly as the scaled copy of the dK/dV pass forms it
             // (same factor, same rounding), so the in-chunk paths cancel
             // against k.dk there
             const float qhd = tof(tobf(tof(qv[i]) * u));
-            const float inter = FQ[R * DK + d] * acc2[i] * u;
+            const float inter = fqv[i] * acc2[i] * u;
             float v = accI[i] * u + inter;
             float rv = qhd * accI[i] + tof(qv[i]) * inter;
             if (!good) {
@@ -965,16 +970,21 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
 #pragma unroll
           for (int kk = 0; kk < DV / 32; ++kk) acc2 = mfma(gfrag[kk][it], vfr[kk], acc2);
           const bf16x4 kv = lds_half<NCK>(KS, s, dc);
+          // this lane's 4 dimensions are one 16-byte piece of each row (dc is
+          // a multiple of 4): read as such, not as 4 separate words
+          const f32x4 csv = *reinterpret_cast<const f32x4 *>(CS + csx<DK>(s, dc));
+          const f32x4 cev = *reinterpret_cast<const f32x4 *>(CS + csx<DK>(16 * S + 15, dc));
+          const f32x4 fkv = *reinterpret_cast<const f32x4 *>(FK + S * DK + dc);
           float out[4], r2v[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int d = dc + i;
-            const float csd = CS[csx<DK>(s, d)];
-            const float ue = exp_c(CS[csx<DK>(16 * S + 15, d)] - csd);
+            const float csd = csv[i];
+            const float ue = exp_c(cev[i] - csd);
             // K-hat exactly as the scaled copy formed it (same factor, same
             // rounding), so the in-chunk paths still cancel against q.dq
             const float khd = tof(tobf(tof(kv[i]) * ue));
-            const float inter = FK[S * DK + d] * acc2[i] * ue;
+            const float inter = fkv[i] * acc2[i] * ue;
             float v = accI[i] * ue + inter;
             float rv = khd * accI[i] + tof(kv[i]) * inter;
             if (!good) {
