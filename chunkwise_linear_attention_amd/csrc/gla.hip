@@ -192,26 +192,29 @@ __global__ __launch_bounds__(NTHR, 2) void gla_fwd_kernel(GlaFwdArgs a) {
       const int B = q / SPB, i0 = q % SPB;
       const int re = 16 * B + 15, rb = 16 * B - 1;  // rb read only when B > 0
       float ce8[8], cb8[8];
+      cs_read8<DK>(CS, re, c8, ce8);
+      if (B > 0) {
+        cs_read8<DK>(CS, rb, c8, cb8);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        ce8[e] = CS[csx<DK>(re, 8 * c8 + e)];
-        cb8[e] = B > 0 ? CS[csx<DK>(rb, 8 * c8 + e)] : 0.f;
+        for (int e = 0; e < 8; ++e) cb8[e] = 0.f;
       }
 #pragma unroll
       for (int k = 0; k < RPT; ++k) {
         const int r = 16 * B + i0 + k * SPB;
         const int off = swz_off<NCK>(r, c8);
+        float cr8[8];
+        cs_read8<DK>(CS, r, c8, cr8);
         bf16x8 kv = *reinterpret_cast<const bf16x8 *>(KS + off);
         float yk[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          yk[e] = r < n ? tof(kv[e]) * exp_c(ce8[e] - CS[csx<DK>(r, 8 * c8 + e)]) : 0.f;
+        for (int e = 0; e < 8; ++e) yk[e] = r < n ? tof(kv[e]) * exp_c(ce8[e] - cr8[e]) : 0.f;
         *reinterpret_cast<bf16x8 *>(KS + off) = cvt8(yk);
         if (OUT) {
           bf16x8 qv = *reinterpret_cast<const bf16x8 *>(QS + off);
           float yq[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) yq[e] = tof(qv[e]) * exp_c(CS[csx<DK>(r, 8 * c8 + e)] - cb8[e]);
+          for (int e = 0; e < 8; ++e) yq[e] = tof(qv[e]) * exp_c(cr8[e] - cb8[e]);
           *reinterpret_cast<bf16x8 *>(QS + off) = cvt8(yq);
         }
       }

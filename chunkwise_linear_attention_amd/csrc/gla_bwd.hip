@@ -206,27 +206,29 @@ __device__ __forceinline__ void prep_scaled(const unsigned char *QS, const unsig
     const int B = q / SPB, i0 = q % SPB;
     const int re = 16 * B + 15, rb = 16 * B - 1;
     float ce8[8], cb8[8];
+    cs_read8<DK>(CS, re, c8, ce8);
+    if (B > 0) {
+      cs_read8<DK>(CS, rb, c8, cb8);
+    } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      ce8[e] = CS[csx<DK>(re, 8 * c8 + e)];
-      cb8[e] = B > 0 ? CS[csx<DK>(rb, 8 * c8 + e)] : 0.f;
+      for (int e = 0; e < 8; ++e) cb8[e] = 0.f;
     }
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       const int r = 16 * B + i0 + k * SPB;
       const int off = swz_off<NCK>(r, c8);
+      float cr8[8];
+      cs_read8<DK>(CS, r, c8, cr8);
       const bf16x8 kv = *reinterpret_cast<const bf16x8 *>(KS + off);
       float yk[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        yk[e] = r < n ? tof(kv[e]) * exp_c(ce8[e] - CS[csx<DK>(r, 8 * c8 + e)]) : 0.f;
+      for (int e = 0; e < 8; ++e) yk[e] = r < n ? tof(kv[e]) * exp_c(ce8[e] - cr8[e]) : 0.f;
       *reinterpret_cast<bf16x8 *>(KH + off) = cvt8(yk);
       if (QH) {
         const bf16x8 qv = *reinterpret_cast<const bf16x8 *>(QS + off);
         float yq[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          yq[e] = r < n ? tof(qv[e]) * exp_c(CS[csx<DK>(r, 8 * c8 + e)] - cb8[e]) : 0.f;
+        for (int e = 0; e < 8; ++e) yq[e] = r < n ? tof(qv[e]) * exp_c(cr8[e] - cb8[e]) : 0.f;
         *reinterpret_cast<bf16x8 *>(QH + off) = cvt8(yq);
       }
     }

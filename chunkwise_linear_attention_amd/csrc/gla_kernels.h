@@ -104,6 +104,21 @@ __device__ __forceinline__ void cumsum_rows_dpp(float *CS, int n, int tid) {
   }
 }
 
+// x[e] = the log tile's element (r, 8 c8 + e), e < 8: two 16-byte pieces of
+// row r, read as such (the compiler does not see through csx's XOR that each
+// group of 4 columns is contiguous, and would read single words)
+template <int DK>
+__device__ __forceinline__ void cs_read8(const float *CS, int r, int c8, float (&x)[8]) {
+  using namespace cla::chunk;
+  const f32x4 lo = *reinterpret_cast<const f32x4 *>(CS + csx<DK>(r, 8 * c8));
+  const f32x4 hi = *reinterpret_cast<const f32x4 *>(CS + csx<DK>(r, 8 * c8 + 4));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = lo[e];
+    x[e + 4] = hi[e];
+  }
+}
+
 // The backward's decay gradient sums q.dq - k.dk backwards inside blocks of
 // this many chunks, each started from the boundary term <S, G>.  Segments of
 // the sequence that run on separate workgroups are whole multiples of it.
