@@ -84,6 +84,16 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
   auto r2p_sum = [&](int s_) __attribute__((always_inline)) -> float {
     return *r2p_at(0, s_) + *r2p_at(1, s_) + *r2p_at(2, s_) + *r2p_at(3, s_);
   };
+  // The same pieces of P1 (never written by a score tile either) hold the
+  // chunk's per-token values TOK[u][t] (u = 0: base-2 cumulative log, 1:
+  // lambda), written by every wave (the same values) at the start of a step,
+  // so that lanes needing 4 or 8 consecutive tokens read them as 16-byte
+  // pieces instead of one cross-lane shuffle per token.
+  auto tok_at = [&](int u, int t_) __attribute__((always_inline)) -> float * {
+    const int idx = u * 64 + t_;
+    const int q = idx >> 2;
+    return reinterpret_cast<float *>(P1 + swz_off<8>(32 + (q >> 2), q & 3) + 4 * (idx & 3));
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -286,6 +296,8 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
     const float lam_l = lane < n && dc.k == 0 ? expf(c_l) : 0.f;
     const float gam_l = dc.k == dc.k_last ? expf(dc.c_last - c_l) : 0.f;
     const float alpha = dc.k_last == 0 ? expf(dc.c_last) : 0.f;
+    *tok_at(0, lane) = c2_l;
+    *tok_at(1, lane) = lam_l;
 
     {
       // ---- masked score tiles, stored transposed: P[s][r] ----
@@ -317,18 +329,20 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
           }
           // acc[i] = X[r = 16 rt + 4 lg + i][s]; rows past the chunk are masked
           const float cs = __shfl(c2_l, s, 64);
+          // base-2 cumulative logs of this lane's 4 rows r = 16 rt + 4 lg + i
+          const f32x4 c2r = *reinterpret_cast<const f32x4 *>(tok_at(0, 16 * rt + 4 * lg));
           bf16x4 pv;
           if (plain && rt > st) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              pv[i] = tobf(acc[i] * __builtin_amdgcn_exp2f(__shfl(c2_l, 16 * rt + 4 * lg + i, 64) - cs));
+              pv[i] = tobf(acc[i] * __builtin_amdgcn_exp2f(c2r[i] - cs));
           } else {
             const int ks = dc.any ? __shfl(dc.k, s, 64) : 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int r = 16 * rt + 4 * lg + i;
               float p = 0.f;
-              const float cr = __shfl(c2_l, r, 64);
+              const float cr = c2r[i];
               const bool sep = dc.any && __shfl(dc.k, r, 64) != ks;  // a reset in (s, r]
               if (r >= s && r < n && !sep) p = acc[i] * __builtin_amdgcn_exp2f(cr - cs);
               pv[i] = tobf(p);
@@ -464,7 +478,11 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
       for (int kb = 0; kb < 2; ++kb) {
         float lam[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) lam[e] = __shfl(lam_l, 32 * kb + 8 * lg + e, 64);
+        for (int e = 0; e < 8; e += 4) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4 *>(tok_at(1, 32 * kb + 8 * lg + e));
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) lam[e + e2] = l4[e2];
+        }
         bf16x8 db[NJ];  // (lambda dO) B operands: k = r, column j
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt) {
@@ -487,7 +505,11 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
       for (int kb = 0; kb < 2; ++kb) {
         float lam[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) lam[e] = __shfl(lam_l, 32 * kb + 8 * lg + e, 64);
+        for (int e = 0; e < 8; e += 4) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4 *>(tok_at(1, 32 * kb + 8 * lg + e));
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) lam[e + e2] = l4[e2];
+        }
         bf16x8 qb[NI];  // (lambda Q) B operands: k = r, column d
 #pragma unroll
         for (int it = 0; it < NI; ++it) {
