@@ -99,6 +99,17 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char buf1[DB ? BUF : 16];
   __shared__ __attribute__((aligned(1024))) unsigned char PS[PSB];
   __shared__ float RD[RDB];  // xdot partial sums [w][row]
+  // The output reads P in 32-column steps up to the diagonal, so rows 0-31,
+  // columns 32-63 of P are never written or read: they hold the chunk's
+  // per-token values TOK[u][t] (u = 0: base-2 cumulative log, 1: gamma, 2:
+  // the segment sums' weight), written by every wave (the same values), so
+  // that lanes needing 4 or 8 consecutive tokens read them as 16-byte pieces
+  // instead of one cross-lane shuffle per token.
+  auto tok_at = [&](int u, int t_) __attribute__((always_inline)) -> float * {
+    const int idx = u * 64 + t_;
+    const int q = idx >> 2;
+    return reinterpret_cast<float *>(PS + swz_off<8>(q >> 2, 4 + (q & 3)) + 4 * (idx & 3));
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -256,6 +267,8 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     const float lam_l = dc.k == 0 ? expf(c_l) : 0.f;
     const float gam_l = lane < n && dc.k == dc.k_last ? expf(dc.c_last - c_l) : 0.f;
     const float alpha = dc.k_last == 0 ? expf(dc.c_last) : 0.f;
+    *tok_at(0, lane) = c2_l;
+    *tok_at(1, lane) = gam_l;
 
     {
       // ---- masked transposed score tiles -> P[r][s] (bf16) ----
@@ -278,17 +291,18 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
         }
         // acc[i] = (K Q^T)[s = 16 st + 4 lg + i][r]; keys past the chunk are masked
         const float cr = __shfl(c2_l, r, 64);
+        // base-2 cumulative logs of this lane's 4 keys s = 16 st + 4 lg + i
+        const f32x4 c2s = *reinterpret_cast<const f32x4 *>(tok_at(0, 16 * st + 4 * lg));
         bf16x4 pv;
         if (plain && st < rt) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            pv[i] = tobf(acc[i] * __builtin_amdgcn_exp2f(cr - __shfl(c2_l, 16 * st + 4 * lg + i, 64)));
+          for (int i = 0; i < 4; ++i) pv[i] = tobf(acc[i] * __builtin_amdgcn_exp2f(cr - c2s[i]));
         } else {
           const int kr = dc.any ? __shfl(dc.k, r, 64) : 0;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int s = 16 * st + 4 * lg + i;
-            const float cs = __shfl(c2_l, s, 64);
+            const float cs = c2s[i];
             const bool sep = dc.any && __shfl(dc.k, s, 64) != kr;  // a reset in (s, r]
             float p = 0.f;
             if (s <= r && s < n && !sep) p = acc[i] * __builtin_amdgcn_exp2f(cr - cs);
@@ -423,12 +437,16 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     // adds exactly 0)
     if (GSUM && do_g && __builtin_amdgcn_readfirstlane(alpha_total != 0.f ? 1 : 0)) {
       FRESH_LANE();
-      const float wg_l = lane < n ? alpha_total * lam_l : 0.f;
+      *tok_at(2, lane) = lane < n ? alpha_total * lam_l : 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float wg[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wg[e] = __shfl(wg_l, 32 * kb + 8 * lg + e, 64);
+        for (int e = 0; e < 8; e += 4) {
+          const f32x4 w4 = *reinterpret_cast<const f32x4 *>(tok_at(2, 32 * kb + 8 * lg + e));
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) wg[e + e2] = w4[e2];
+        }
         bf16x8 xb[NJ];  // (A X) B operands: k = s, column j
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt) {
@@ -460,7 +478,11 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
       float gam[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gam[e] = __shfl(gam_l, 32 * kb + 8 * lg + e, 64);
+      for (int e = 0; e < 8; e += 4) {
+        const f32x4 g4 = *reinterpret_cast<const f32x4 *>(tok_at(1, 32 * kb + 8 * lg + e));
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) gam[e + e2] = g4[e2];
+      }
       bf16x8 vb[NJ];  // (gamma V) B operands: k = s, column j
 #pragma unroll
       for (int jt = 0; jt < NJ; ++jt) {
