@@ -116,28 +116,48 @@ struct ChunkDecay {
   bool any;         // the chunk holds a reset (wave-uniform)
 };
 
+// x + (the x of the lane DPP control CTRL selects), rows outside ROW_MASK and
+// sources outside the row adding 0
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_addf(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, true));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_addi(int x) {
+  return x + __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, true);
+}
+
+// Inclusive prefix sum across the 64 lanes by DPP: within every 16-lane row
+// by shifts of 1, 2, 4 and 8 lanes, then across rows by the broadcasts of
+// lanes 15 and 31 (the cross-lane scan of AMD's GCN documentation); no LDS.
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  x = dpp_addf<0x111, 0xF>(x);  // row_shr:1
+  x = dpp_addf<0x112, 0xF>(x);  // row_shr:2
+  x = dpp_addf<0x114, 0xF>(x);  // row_shr:4
+  x = dpp_addf<0x118, 0xF>(x);  // row_shr:8
+  x = dpp_addf<0x142, 0xA>(x);  // row_bcast:15 into rows 1, 3
+  return dpp_addf<0x143, 0xC>(x);  // row_bcast:31 into rows 2, 3
+}
+__device__ __forceinline__ int wave_prefix_sum(int x) {
+  x = dpp_addi<0x111, 0xF>(x);
+  x = dpp_addi<0x112, 0xF>(x);
+  x = dpp_addi<0x114, 0xF>(x);
+  x = dpp_addi<0x118, 0xF>(x);
+  x = dpp_addi<0x142, 0xA>(x);
+  return dpp_addi<0x143, 0xC>(x);
+}
+
 __device__ __forceinline__ ChunkDecay chunk_decay(float l, int lane) {
   ChunkDecay d;
   const bool rst = l < -3.0e38f;  // -inf
   d.any = __ballot(rst) != 0;
-  float c = rst ? 0.f : l;
-#pragma unroll
-  for (int sh = 1; sh < 64; sh <<= 1) {
-    const float p = __shfl_up(c, sh, 64);
-    if (lane >= sh) c += p;
-  }
-  int k = rst ? 1 : 0;
-  if (d.any) {
-#pragma unroll
-    for (int sh = 1; sh < 64; sh <<= 1) {
-      const int p = __shfl_up(k, sh, 64);
-      if (lane >= sh) k += p;
-    }
-  }
+  const float c = wave_prefix_sum(rst ? 0.f : l);
+  const int k = d.any ? wave_prefix_sum(rst ? 1 : 0) : 0;
   d.c = c;
   d.k = k;
-  d.c_last = __shfl(c, 63, 64);
-  d.k_last = d.any ? __shfl(k, 63, 64) : 0;
+  d.c_last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c), 63));
+  d.k_last = d.any ? __builtin_amdgcn_readlane(k, 63) : 0;
   return d;
 }
 
