@@ -142,7 +142,6 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   const int j0 = w * (DV / 4);  // first value column of this wave
   constexpr bool has_x = XD;
   const bool do_g = GSUM && seg > 0;  // wave-uniform
-  const int nblk = NBQ + NBK + NBV + (has_x ? NBV : 0);
 
   const uint16_t *qh = a.q + bh * T * DK;
   const uint16_t *kh = a.k + bh * T * DK;

@@ -638,7 +638,6 @@ __global__ __launch_bounds__(BTHR, 1) void gla_dkdv_kernel(GlaBwdArgs a) {
   constexpr int B_FT = B_RED + NRED * DK * 4;
   constexpr int BUF = B_FT + 10 * DK * 4;
   constexpr int NBQ = DK / 8, NBV = DV / 8, NBL = DK / 4;
-  constexpr int NBLK = 2 * NBQ + 2 * NBV + NBL;
   static_assert(BUF <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) unsigned char buf[BUF];
   unsigned char *QS = buf, *KS = buf + B_KS, *QH = buf + B_QH, *KH = buf + B_KH;
