@@ -882,8 +882,7 @@ FwdWs fwd_ws(void *base, int64_t nh, int64_t P, int64_t DK, int64_t DV) {
 
 // backward workspace: the segment states of the dQ pass (the states its
 // segments start from, and the states it ends them with) and of the reverse
-// pass (G at segment ends), q . dq and k . dk per token, the final state S_T,
-// and the boundary terms <S, G> per segment
+// pass (G at segment ends), q . dq per token and the final state S_T
 struct BwdWs {
   FwdWs seg;   // dQ pass: slots p = S^T entering segment p + 1
   FwdWs gseg;  // reverse pass: slots p = G at the end of segment p
