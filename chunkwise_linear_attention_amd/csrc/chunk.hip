@@ -319,8 +319,10 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
         // bf16(S - hi), both formed once per chunk), so that S enters it to ~2^-16;
         // rdot_r = x_r . o_r plus the correction
         //   sum_j ((lambda_r x_r)_bf16 - lambda_r x_r)[j] (S^T Q^T)[j][r],
-        // which makes its inter-chunk part pair with the bf16-rounded
-        // (lambda q) rows that the dK/dV pass adds into its state gradient.
+        // evaluated as (lambda_r x_r)_bf16 . (S^T Q^T)[:, r] + x_r . (V^T P^T)[:, r]
+        // (the in-chunk product on its own accumulator), which makes its
+        // inter-chunk part pair with the bf16-rounded (lambda q) rows that the
+        // dK/dV pass adds into its state gradient.
         FRESH_LANE();
         bf16x8 vfrag[NJ][2];  // A operands V^T: row j, k = s
 #pragma unroll
@@ -353,27 +355,34 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
             for (int kk = 0; kk < DK / 32; ++kk) acc = mfma(shi[kk][jt], qfrag[kk], acc);
 #pragma unroll
             for (int kk = 0; kk < DK / 32; ++kk) acc = mfma(slo[kk][jt], qfrag[kk], acc);
-            const int jc = j0 + 16 * jt + 4 * lg;
-            const bf16x4 xv = lds_half<NCV>(XS, rr, jc);
-            float corr = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float xl = tof(xv[i]) * lam;
-              corr += (tof(tobf(xl)) - xl) * acc[i];
-              acc[i] *= lam;
-            }
+            // in-chunk part on its own accumulator (no wait for the above)
+            f32x4 ai = zero4();
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
-              if (kb <= (rt >> 1)) acc = mfma(vfrag[jt][kb], pfrag[kb], acc);
+              if (kb <= (rt >> 1)) ai = mfma(vfrag[jt][kb], pfrag[kb], ai);
+            const int jc = j0 + 16 * jt + 4 * lg;
+            const bf16x4 xv = lds_half<NCV>(XS, rr, jc);
+            float xf[4];
+            bf16x4 xlb;  // bf16(lambda_r x_r), as the dK/dV pass's state update rounds it
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              xf[i] = tof(xv[i]);
+              xlb[i] = tobf(xf[i] * lam);
+            }
+            // rdot_r = bf16(lambda x) . (S^T q) + x . (in-chunk part), and
+            // o = lambda (S^T q) + in-chunk part
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              rdp += tof(xlb[i]) * acc[i];
+              rdp += xf[i] * ai[i];
+              acc[i] = __builtin_fmaf(lam, acc[i], ai[i]);
+            }
             if (rr < n) {
               bf16x4 ov;
 #pragma unroll
               for (int i = 0; i < 4; ++i) ov[i] = tobf(acc[i]);
               *reinterpret_cast<bf16x4 *>(a.o + (bh * T + t0 + rr) * DV + jc) = ov;
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) rdp += tof(xv[i]) * acc[i];
-            rdp += corr;
           }
           rdp += __shfl_xor(rdp, 16, 64);
           rdp += __shfl_xor(rdp, 32, 64);

@@ -401,10 +401,13 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
         // ---- dK^T[d][s] = gamma_s (G V^T)[d][s] + (Q^T P2)[d][s] ; r2_s ----
         // G enters the inter-chunk product as G = hi + lo, two bf16 parts
         // (hi = bf16(G), lo = bf16(G - hi), both formed once per chunk), and
-        //   r2_s = k_s . dk_s + sum_d ((gamma_s k_s)_bf16 - gamma_s k_s)[d] (G v_s)[d],
-        // whose inter-chunk part then pairs with the bf16-rounded (gamma k)
-        // rows of the dQ pass's state update, so that the decay gradient's
-        // sums telescope exactly (see the segment length in chunk.hip).
+        //   r2_s = k_s . dk_s + sum_d ((gamma_s k_s)_bf16 - gamma_s k_s)[d] (G v_s)[d]
+        //        = (gamma_s k_s)_bf16 . (G v_s) + k_s . (Q^T P2)[:, s],
+        // evaluated in the second form (the in-chunk product on its own
+        // accumulator); its inter-chunk part pairs with the bf16-rounded
+        // (gamma k) rows of the dQ pass's state update, so that the decay
+        // gradient's sums telescope exactly (see the segment length in
+        // chunk.hip).
         FRESH_LANE();
         bf16x8 ghi[DV / 32][NI], glo[DV / 32][NI];
 #pragma unroll
@@ -437,21 +440,28 @@ __global__ __launch_bounds__(BTHR, (DK == 64 && DV == 64) ? 4 : 2) void chunk_bw
             for (int kk = 0; kk < DV / 32; ++kk) acc = mfma(ghi[kk][it], vfrag[kk], acc);
 #pragma unroll
             for (int kk = 0; kk < DV / 32; ++kk) acc = mfma(glo[kk][it], vfrag[kk], acc);
-            const int dc = dw0 + 16 * it + 4 * lg;
-            const bf16x4 kv = lds_half<NCK>(KS, s, dc);
-            float corr = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float kg = tof(kv[i]) * gs;
-              corr += (tof(tobf(kg)) - kg) * acc[i];
-              acc[i] *= gs;
-            }
+            // in-chunk part on its own accumulator (no wait for the above)
+            f32x4 ai = zero4();
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
-              if (2 * kb + 1 >= st) acc = mfma(qfrag[it][kb], pfrag[kb], acc);
-            r2p += corr;
+              if (2 * kb + 1 >= st) ai = mfma(qfrag[it][kb], pfrag[kb], ai);
+            const int dc = dw0 + 16 * it + 4 * lg;
+            const bf16x4 kv = lds_half<NCK>(KS, s, dc);
+            float kf[4];
+            bf16x4 kgb;  // bf16(gamma_s k_s), as the dQ pass's state update rounds it
 #pragma unroll
-            for (int i = 0; i < 4; ++i) r2p += tof(kv[i]) * acc[i];
+            for (int i = 0; i < 4; ++i) {
+              kf[i] = tof(kv[i]);
+              kgb[i] = tobf(kf[i] * gs);
+            }
+            // r2_s = bf16(gamma k) . (G v) + k . (in-chunk part), and
+            // dk = gamma (G v) + in-chunk part
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              r2p += tof(kgb[i]) * acc[i];
+              r2p += kf[i] * ai[i];
+              acc[i] = __builtin_fmaf(gs, acc[i], ai[i]);
+            }
             if (s < n) {
               bf16x4 ov;
 #pragma unroll
