@@ -205,8 +205,9 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   int rd_n = 0;
 
   // DMA of chunk cj into a staging buffer: 1 KB row blocks spread over the
-  // waves, the 64 log decays (rows clamped to the chunk) by wave 0.
-  auto stage = [&](int64_t cj, unsigned char *buf) __attribute__((always_inline)) {
+  // waves, the 64 log decays (rows clamped to the chunk) by wave 0.  part 0:
+  // everything; 1: Q, X and the log decays; 2: K and V.
+  auto stage = [&](int64_t cj, unsigned char *buf, int part = 0) __attribute__((always_inline)) {
     const int64_t tj = cj * TC;
     const int nj = (int)min<int64_t>(TC, T - tj);
     // the per-lane DMA addresses are formed here, at each stage, instead of
@@ -219,6 +220,8 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int r0 = 0; r0 < NBQ + NBK + NBV + (XD ? NBV : 0); r0 += NWAVE) {
       const int b = w + r0;
+      const bool early = r0 < NBQ || r0 >= NBQ + NBK + NBV;  // Q or X
+      if ((part == 1 && !early) || (part == 2 && early)) continue;
       // (untracked copies: every staged chunk is waited for explicitly)
       if (r0 < NBQ) {
         lds_copy16_untracked(bf16_block_src<DK>(qh + tj * DK, nj, b, ln), lb + b * 1024);
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
                              lb + B_XS + (b - NBQ - NBK - NBV) * 1024);
       }
     }
-    if (w == 0) lds_copy4_untracked(lh + tj + min(ln, nj - 1), lb + B_L);
+    if (w == 0 && part != 2) lds_copy4_untracked(lh + tj + min(ln, nj - 1), lb + B_L);
   };
 
   // the xdot sums of the previous chunk, from RD
@@ -247,7 +250,8 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
   };
 
   // The work on one staged chunk.
-  auto compute = [&](int64_t ci, const unsigned char *cur) __attribute__((always_inline)) {
+  auto compute = [&](int64_t ci, const unsigned char *cur, auto before_update)
+                     __attribute__((always_inline)) {
     const int64_t t0 = ci * TC;
     const int n = (int)min<int64_t>(TC, T - t0);
     const unsigned char *QS = cur;
@@ -473,6 +477,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
       }
     }
 
+    before_update();
     // ---- state update: S <- alpha S + K^T (gamma V) ----
     FRESH_LANE();
     alpha_total *= alpha;
@@ -533,7 +538,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
       const float rs = rd_sum();
       const int64_t rs_t0 = rd_t0;
       const int rs_n = rd_n;
-      compute(ci, cur);
+      compute(ci, cur, [] {});
       if (rs_t0 >= 0 && tid < rs_n) a.rdot[bh * T + rs_t0 + fresh(tid)] = rs;
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // the next chunk has landed; this chunk's buffer is free
@@ -546,14 +551,23 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(FwdArgs a) {
       if (ci + 1 < c_end) step(ci + 1, buf1, buf0);
     }
   } else {
+    // One buffer: Q, X and the log decays of the next chunk are copied while
+    // the state update runs (it reads none of them), K and V once it is done.
+    stage(c_begin, buf0, 1);
     for (int64_t ci = c_begin; ci < c_end; ++ci) {
       lds_barrier();  // the previous chunk's LDS reads (and RD writes) are done
       const float rs = rd_sum();
-      if (rd_t0 >= 0 && tid < rd_n) a.rdot[bh * T + rd_t0 + fresh(tid)] = rs;
-      stage(ci, buf0);
+      const int64_t rs_t0 = rd_t0;
+      const int rs_n = rd_n;
+      stage(ci, buf0, 2);
       __builtin_amdgcn_s_waitcnt(0);
       lds_barrier();  // every wave's DMA has landed
-      compute(ci, buf0);
+      // (stored with nothing in flight)
+      if (rs_t0 >= 0 && tid < rs_n) a.rdot[bh * T + rs_t0 + fresh(tid)] = rs;
+      compute(ci, buf0, [&] {
+        lds_barrier();  // every wave is done with Q and X
+        if (ci + 1 < c_end) stage(ci + 1, buf0, 1);
+      });
     }
     lds_barrier();
   }
