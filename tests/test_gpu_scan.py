@@ -36,9 +36,9 @@ def _check(inp, got, coracle):
     from gpu_util import block_rel_l2, rel_l2, to_np
     h, hT, da, db, dh0 = got
     hr, hTr = coracle.scan_fwd(inp.a, inp.b, inp.h0)
-    # the backward oracle reads the device forward output as its h input
-    h32 = h.detach().cpu().numpy()
-    dar, dbr, dh0r = coracle.scan_bwd(inp.a, h32, inp.h0, inp.dh, inp.dhT)
+    # the backward oracle's h input is the oracle's own forward output, stored
+    # in fp32 as the library stores h (never the device's h)
+    dar, dbr, dh0r = coracle.scan_bwd(inp.a, hr.astype(np.float32), inp.h0, inp.dh, inp.dhT)
     pairs = {"h": (to_np(h), hr, SEQ_BLOCKS), "da": (to_np(da), dar, SEQ_BLOCKS),
              "db": (to_np(db), dbr, SEQ_BLOCKS), "dh0": (to_np(dh0), dh0r, ROW_BLOCKS)}
     if hT is not None:
@@ -149,7 +149,7 @@ def test_scan_stitched_pieces(coracle):
     da1, db1, dh0 = cla.scan_bwd(a1, h1, h0, dh[:, :s].contiguous(), dmid)
     hr, hTr = osc.scan_loop(inp.a, inp.b, inp.h0)
     hcat = torch.cat([h1, h2], 1)
-    dar, dbr, dh0r = osc.scan_bwd_loop(inp.a, to_np(hcat), inp.h0, inp.dh, inp.dhT)
+    dar, dbr, dh0r = osc.scan_bwd_loop(inp.a, hr, inp.h0, inp.dh, inp.dhT)
     assert rel_l2(to_np(hcat), hr) <= TOL
     assert rel_l2(to_np(hT2), hTr) <= TOL
     assert rel_l2(to_np(torch.cat([da1, da2], 1)), dar) <= TOL
@@ -193,8 +193,10 @@ def test_scan_large_workload_full(coracle):
     for d0 in range(0, 4096, 512):
         sl = slice(d0, d0 + 512)
         hr, hTr = coracle.scan_fwd(inp.a, inp.b, inp.h0, drange=(d0, d0 + 512))
-        dar, dbr, dh0r = coracle.scan_bwd(inp.a, h_full, inp.h0, inp.dh, None,
-                                          drange=(d0, d0 + 512))
+        # the backward oracle runs on the slab with the oracle's own h (fp32)
+        dar, dbr, dh0r = coracle.scan_bwd(inp.a[:, :, sl], hr.astype(np.float32),
+                                          None if inp.h0 is None else inp.h0[:, sl],
+                                          inp.dh[:, :, sl], None)
         pairs = {"h": (h_full[:, :, sl], hr, SEQ_BLOCKS),
                  "hT": (hT[:, sl].cpu().numpy(), hTr, ROW_BLOCKS),
                  "da": (da[:, :, sl].cpu().numpy(), dar, SEQ_BLOCKS),
