@@ -303,8 +303,42 @@ def streaming_ceilings(torch):
     ms = float(np.median(timer.time(lambda: torch.add(a, b, out=c), 5)))
     out["two_reads_one_write_GBps"] = round(3 * a.numel() * 4 / (ms * 1e-3) / 1e9, 1)
     del a, b, c
+    out.update(scan_bwd_mix_ceiling(torch, timer))
     torch.cuda.empty_cache()
     return out
+
+
+def scan_bwd_mix_ceiling(torch, timer):
+    """The diagonal scan backward's traffic without its arithmetic: three
+    reads and two writes per element of [8, 16384, 4096] fp32 arrays, in the
+    scan kernels' workgroup and lane order (the streaming probe library built
+    beside libcla).  Bytes moved / median of 5 timings."""
+    import ctypes
+    from chunkwise_linear_attention_amd import build as cbuild
+    if not os.path.exists(cbuild.PROBE_LIB):
+        raise RuntimeError(f"{cbuild.PROBE_LIB} is missing: run the build first")
+    lib = ctypes.CDLL(cbuild.PROBE_LIB)
+    fn = lib.cla_probe_stream_3r2w
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 3 + [ctypes.c_void_p]
+    B, T, D = 8, 16384, 4096
+    xs = [torch.empty(B * T * D, dtype=torch.float32, device="cuda:0") for _ in range(5)]
+    for x in xs[:3]:
+        x.fill_(0.5)
+    st = torch.cuda.current_stream().cuda_stream
+    args = [x.data_ptr() for x in xs] + [B, T, D, st]
+
+    def run():
+        r = fn(*args)
+        if r != 0:
+            raise RuntimeError(f"cla_probe_stream_3r2w returned {r}")
+
+    run()
+    ms = float(np.median(timer.time(run, 5)))
+    del xs
+    return {"scan_bwd_mix_GBps": round(20 * B * T * D / (ms * 1e-3) / 1e9, 1),
+            "scan_bwd_mix": "3 reads + 2 writes of [8, 16384, 4096] fp32 in the scan "
+                            "kernels' order, no arithmetic dependence"}
 
 
 # ---------------------------------------------------------------------------
@@ -725,7 +759,11 @@ def main():
         res = bench_scan(args, torch, cla, wl, args.steps, args.warmup, cpu=args.cpu_baseline)
         if wl.name == "scan_large" and not args.no_chunk_extras:
             ex = res["extra"]
-            ex["streaming_ceilings"] = streaming_ceilings(torch)
+            ex["streaming_ceilings"] = sc = streaming_ceilings(torch)
+            # the headline kernel against the same traffic without arithmetic
+            if res["roofline"]["kernel"] == "scan_bwd":
+                sc["scan_bwd_over_mix_ceiling"] = round(
+                    res["roofline"]["achieved"] / sc["scan_bwd_mix_GBps"], 4)
             # the small scan (one channel group, time split into segments):
             # launch latency dominates, so more steps are timed
             r = bench_scan(args, torch, cla, syn.WORKLOADS["scan_small"], max(200, args.steps),

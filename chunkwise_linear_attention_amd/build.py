@@ -1,7 +1,8 @@
 """Build libcla.so, the HIP library behind the C ABI in include/cla.h.
 
 Compiles every source under csrc/ for gfx950 with hipcc (in parallel, one
-object per source) and links them into chunkwise_linear_attention_amd/libcla.so.
+object per source) and links them into chunkwise_linear_attention_amd/libcla.so;
+also builds the benchmark's streaming probe (probe/libstreamprobe.so).
 Always recompiles.  Usage: ``python -m chunkwise_linear_attention_amd.build``.
 """
 
@@ -42,6 +43,22 @@ def _compile(src):
     return obj, out
 
 
+PROBE_SRC = os.path.join(HERE, "probe", "stream_probe.hip")
+PROBE_LIB = os.path.join(HERE, "probe", "libstreamprobe.so")
+
+
+def build_probe() -> str:
+    """The benchmark's streaming probe (probe/stream_probe.hip), a library of
+    its own that only bench.py loads."""
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([HIPCC, *FLAGS, "-shared", PROBE_SRC, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
@@ -54,6 +71,7 @@ def build(verbose: bool = False) -> str:
            *[o for o, _ in results]]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    build_probe()
     return LIB
 
 

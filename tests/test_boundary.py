@@ -335,3 +335,20 @@ def test_sscan_validation(lib):
     a2[9] = F  # dx aliases dy
     assert bw(*a2, *shp, L, without, None) == ALIAS
     assert bw(*args, *shp, G, without, None) == ALIAS  # workspace overlaps dx
+
+
+def test_stream_probe_rejects_before_launch(lib):
+    """The benchmark's streaming probe (a library of its own) loads, exports
+    its one call and returns -1 for arguments it does not take, before any
+    launch."""
+    from chunkwise_linear_attention_amd import build as cbuild
+    probe = ctypes.CDLL(cbuild.PROBE_LIB)
+    f = probe.cla_probe_stream_3r2w
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 3 + [ctypes.c_void_p]
+    assert f(None, B_, C, D_, E, 8, 16, 4096, None) == -1          # NULL input
+    assert f(A, B_, C, D_, None, 8, 16, 4096, None) == -1          # NULL output
+    assert f(A, B_, C, D_, E, 8, 16, 4000, None) == -1             # D % 64
+    assert f(A, B_, C, D_, E, 1, 16, 64, None) == -1               # groups % 8
+    assert f(A, B_, C, D_, E, 0, 16, 4096, None) == -1             # empty
+    assert f(A + 4, B_, C, D_, E, 8, 16, 4096, None) == -1         # misaligned
