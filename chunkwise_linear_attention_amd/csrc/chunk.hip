@@ -45,15 +45,8 @@ namespace {
 // Concurrent workgroups: the forward-type kernel runs two per CU, the dK/dV
 // kernel one per CU, on 256 CUs.  Segment counts are chosen so that the
 // workgroups fill whole rounds of these slots.
-// (overridable for tuning builds)
-#ifndef CLA_CHUNK_FWD_SLOTS
-#define CLA_CHUNK_FWD_SLOTS 512
-#endif
-#ifndef CLA_CHUNK_BWD_SLOTS
-#define CLA_CHUNK_BWD_SLOTS 256
-#endif
-constexpr int64_t kFwdSlots = CLA_CHUNK_FWD_SLOTS;
-constexpr int64_t kBwdSlots = CLA_CHUNK_BWD_SLOTS;
+constexpr int64_t kFwdSlots = 512;
+constexpr int64_t kBwdSlots = 256;
 constexpr int64_t kMinSegChunks = 4;
 // The backward's decay gradient sums q.dq - k.dk backwards only inside one
 // segment, starting from the boundary term <S, G> of the two segment states.
